@@ -1,0 +1,125 @@
+/*
+ * wvd.h -- C ABI of the MI355X (gfx950) Wan-style causal video VAE decoder.
+ *
+ * The decoder turns latents [1, 48, T, h, w] into video
+ * [1, 3, 4T-3, 16h, 16w] for any T >= 1 (Wan2.2 VAE decoder page,
+ * introduction: 48 latent channels, 16x16 spatial and 4x temporal
+ * compression).  Weights are prepared once (layout and phase transforms;
+ * same page, "Use": the decoder prepares the weights once and its raw entry
+ * points are destination-passing on the current stream); decoding writes into
+ * a caller-owned video buffer on the caller's stream.  Arithmetic: bf16
+ * weights and activations, fp32 accumulation, fp32 RMS-norm statistics (same
+ * page, "Limits").  frames_per_pass latent frames are carried through the
+ * whole decoder per pass; it trades memory for speed and leaves the video
+ * bit-identical (same page, "Performance and memory").
+ *
+ * Memory ownership: the caller owns every device buffer (weights, prepared
+ * buffer, workspace, latents, video).  A plan refers to the prepared buffer
+ * but does not own it.  All device pointers are HIP device addresses on the
+ * device current at the call; all work is enqueued on `stream` (NULL = the
+ * default stream) and nothing synchronises the host.
+ *
+ * Errors: every entry point validates its arguments on the host before it
+ * enqueues anything; on an error it returns a negative wvd_status, enqueues
+ * nothing and leaves the output untouched.  A HIP launch failure returns
+ * WVD_EHIP (work enqueued before it may have run).  No C++ exception crosses
+ * this ABI.
+ */
+#ifndef WVD_H
+#define WVD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct wvd_plan wvd_plan; /* opaque; read-only after wvd_prepare */
+
+enum wvd_status {
+  WVD_OK = 0,
+  WVD_EINVAL = -1,      /* null pointer, bad count, T < 1, frames_per_pass < 1 */
+  WVD_ESHAPE = -2,      /* shape inconsistent with the plan */
+  WVD_ENOSPACE = -3,    /* prepared buffer or workspace smaller than required */
+  WVD_EUNSUPPORTED = -4,/* c not a positive multiple of 16, h or w out of range */
+  WVD_EHIP = -5         /* a HIP call failed */
+};
+
+/* Number of weight tensors in the canonical order (see wvd_prepare). */
+#define WVD_NUM_WEIGHTS 84
+
+/* Bytes of the prepared-weights buffer for base width c at latent size h x w.
+ * c: positive multiple of 16; 1 <= h, w <= 4096.  Writes *bytes. */
+int wvd_prepared_bytes(int c, int h, int w, size_t* bytes);
+
+/* One-time weight preparation (Wan2.2 VAE decoder page, "Use": layout and
+ * phase transforms of the weights, done once).
+ *   weights:  WVD_NUM_WEIGHTS device pointers to bf16 tensors, contiguous, in
+ *             the canonical order and PyTorch layouts: conv_in (weight
+ *             [4c,48,3,3,3], bias); mid.res0 (norm1.gamma, conv1.weight,
+ *             conv1.bias, norm2.gamma, conv2.weight, conv2.bias); mid.attn
+ *             (norm.gamma [4c], qkv.weight [12c,4c], qkv.bias, proj.weight
+ *             [4c,4c], proj.bias); mid.res1; then for stage s = 0..3 with
+ *             widths [4c,4c,2c,c]: res0 (+ shortcut.weight [Cs,Cprev,1,1,1],
+ *             shortcut.bias when the width changes), res1, time_conv (weight
+ *             [2Cs,Cs,3,1,1], bias; s < 2), up_conv (weight [Cs,Cs,3,3],
+ *             bias; s < 3); head (norm.gamma [c], conv.weight [12,c,3,3,3],
+ *             conv.bias).
+ *   prepared: caller-owned device buffer of wvd_prepared_bytes(c,h,w) bytes.
+ * The input weights may be freed once the enqueued work has completed.  On
+ * success *plan_out receives a host object to release with wvd_destroy. */
+int wvd_prepare(int c, int h, int w, const void* const* weights, int n_weights,
+                void* prepared, size_t prepared_bytes, void* stream,
+                wvd_plan** plan_out);
+
+/* Workspace bytes wvd_decode needs for T latent frames at frames_per_pass.
+ * Depends on min(T, frames_per_pass) only. */
+int wvd_workspace_bytes(const wvd_plan* plan, int T, int frames_per_pass, size_t* bytes);
+
+/* Decode latents into video (destination-passing, on `stream`).
+ *   z:   device bf16 [1, 48, T, h, w], contiguous (the plan's h, w).
+ *   out: device bf16 [1, 3, 4T-3, 16h, 16w], contiguous; every element is
+ *        written, finite and in [-1, 1].
+ *   workspace: device buffer of at least wvd_workspace_bytes(plan, T, P).
+ * The output is bit-identical for every frames_per_pass >= 1, and its first
+ * 4k-3 frames are bit-identical to the decode of the first k latent frames.
+ * Concurrent decodes with one plan need separate workspaces. */
+int wvd_decode(const wvd_plan* plan, const void* z, int T, int frames_per_pass,
+               void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Release a plan (host memory only; the prepared buffer stays the caller's).
+ * NULL is ignored. */
+void wvd_destroy(wvd_plan* plan);
+
+/* Static description of a status code. */
+const char* wvd_status_string(int status);
+
+/* Text naming the launch and HIP error behind the last WVD_EHIP returned on
+ * the calling thread ("" if none).  Valid until the next call on the thread. */
+const char* wvd_last_error(void);
+
+/* Host-validation mode for testing without a GPU: with on != 0, every entry
+ * point validates its arguments and walks the full launch schedule (all
+ * per-launch checks included) but enqueues no GPU work and dereferences no
+ * device pointer.  Process-wide; not for use while decodes are in flight. */
+void wvd_set_dry_run(int on);
+
+/* Kernel launches the last wvd_decode on this plan made (or would have made in
+ * dry-run mode); -1 for a null plan. */
+long long wvd_last_launch_count(const wvd_plan* plan);
+
+/* Enables (1) or disables (0) per-kernel HIP-event timing of wvd_decode's
+ * launches on the plan; wvd_profile_read then returns, per kernel class
+ * (0 conv 3x3x3, 1 conv other, 2 attention, 3 norm statistics, 4 copies),
+ * the summed milliseconds and algorithmic FLOPs of the last decode.  The
+ * timing synchronises the stream at the end of wvd_decode.  Returns
+ * WVD_EINVAL on a null plan. */
+int wvd_profile_enable(wvd_plan* plan, int on);
+int wvd_profile_read(const wvd_plan* plan, double* ms, double* flops, int n_classes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WVD_H */

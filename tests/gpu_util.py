@@ -1,0 +1,83 @@
+"""Shared helpers of the GPU tests: the seeded inputs, the oracle's video
+(cached on disk, keyed by the oracle's and the generator's source) and the
+GPU decode through the C ABI."""
+from __future__ import annotations
+
+import hashlib
+import os
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+
+from video_diffusion_vae_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CACHE = os.path.join(ROOT, ".oracle_cache")
+
+
+def gpu_available() -> bool:
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+def rel_l2(got: np.ndarray, ref: np.ndarray) -> float:
+    g = got.astype(np.float64)
+    r = ref.astype(np.float64)
+    return float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30))
+
+
+def _src_hash() -> str:
+    h = hashlib.sha256()
+    for p in ("oracle/decoder.py", "video_diffusion_vae_amd/synth.py"):
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def inputs(cfg: synth.Config, seed: int, T: Optional[int] = None):
+    T = cfg.T if T is None else T
+    W = synth.make_weights(cfg.c, seed=seed, bf16=cfg.weights_bf16)
+    z = synth.make_latents(T, cfg.h, cfg.w, seed=seed, bf16=cfg.weights_bf16)
+    return W, z
+
+
+def oracle_video(cfg: synth.Config, seed: int = 0, T: Optional[int] = None) -> np.ndarray:
+    from oracle import decoder as O
+    T = cfg.T if T is None else T
+    key = f"{cfg.name}_s{seed}_T{T}_{_src_hash()}.npy"
+    path = os.path.join(CACHE, key)
+    if os.path.exists(path):
+        return np.load(path)
+    W, z = inputs(cfg, seed, T)
+    v = O.decode(z, W, cfg.c)
+    os.makedirs(CACHE, exist_ok=True)
+    np.save(path + ".tmp.npy", v)
+    os.replace(path + ".tmp.npy", path)
+    return v
+
+
+_decoders: Dict[Tuple[int, int, int, int, bool], object] = {}
+
+
+def decoder_for(cfg: synth.Config, seed: int):
+    from video_diffusion_vae_amd import wvd
+    key = (cfg.c, cfg.h, cfg.w, seed, cfg.weights_bf16)
+    if key not in _decoders:
+        W, _ = inputs(cfg, seed, 1)
+        _decoders.clear()
+        _decoders[key] = wvd.Decoder(W, cfg.c, cfg.h, cfg.w)
+    return _decoders[key]
+
+
+def decode_gpu(cfg: synth.Config, seed: int = 0, frames_per_pass: int = 1, T: Optional[int] = None) -> np.ndarray:
+    import torch
+    T = cfg.T if T is None else T
+    dec = decoder_for(cfg, seed)
+    z = synth.make_latents(T, cfg.h, cfg.w, seed=seed, bf16=cfg.weights_bf16)
+    zt = torch.from_numpy(z).to("cuda").to(torch.bfloat16)
+    out = dec.decode(zt, frames_per_pass=frames_per_pass)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy()

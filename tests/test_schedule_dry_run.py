@@ -1,0 +1,70 @@
+"""The pass scheduler and every per-launch check, run on the host in the
+library's dry-run mode (no GPU work, no device pointer dereferenced)."""
+import pytest
+
+from video_diffusion_vae_amd import synth
+
+FAKE = 1 << 20  # a 256-byte aligned address that is never dereferenced
+
+
+@pytest.fixture
+def dry():
+    from video_diffusion_vae_amd import wvd
+    wvd.wvd_set_dry_run(True)
+    yield wvd
+    wvd.wvd_set_dry_run(False)
+
+
+def plan_for(wvd, c, h, w):
+    n = wvd.wvd_prepared_bytes(c, h, w)
+    return wvd.wvd_prepare(c, h, w, [FAKE] * 84, FAKE, n, 0)
+
+
+@pytest.mark.parametrize("cfg", synth.CONFIGS, ids=lambda c: c.name)
+def test_every_config_schedules(dry, cfg):
+    wvd = dry
+    plan = plan_for(wvd, cfg.c, cfg.h, cfg.w)
+    try:
+        counts = {}
+        for P in sorted(set(cfg.passes) | {1, cfg.T, cfg.T + 3}):
+            ws = wvd.wvd_workspace_bytes(plan, cfg.T, P)
+            wvd.wvd_decode(plan, FAKE, cfg.T, P, FAKE, FAKE, ws, 0)
+            counts[P] = wvd.wvd_last_launch_count(plan)
+            assert counts[P] > 0
+        # One pass per P latent frames; launches per pass do not depend on P
+        # except for pass 0 (no time_conv history) and the frame-0 copies.
+        assert counts[cfg.T] == counts[cfg.T + 3]
+        assert counts[1] >= counts[cfg.T]
+    finally:
+        wvd.wvd_destroy(plan)
+
+
+def test_workspace_depends_on_min_T_P(dry):
+    wvd = dry
+    plan = plan_for(wvd, 64, 22, 39)
+    try:
+        assert wvd.wvd_workspace_bytes(plan, 3, 5) == wvd.wvd_workspace_bytes(plan, 3, 3)
+        assert wvd.wvd_workspace_bytes(plan, 9, 1) < wvd.wvd_workspace_bytes(plan, 9, 2)
+        ws = wvd.wvd_workspace_bytes(plan, 3, 3)
+        with pytest.raises(wvd.WvdError) as e:
+            wvd.wvd_decode(plan, FAKE, 3, 3, FAKE, FAKE, ws - 1, 0)
+        assert e.value.status == wvd.WVD_ENOSPACE
+        for bad in ((0, 1), (3, 0)):
+            with pytest.raises(wvd.WvdError) as e:
+                wvd.wvd_decode(plan, FAKE, bad[0], bad[1], FAKE, FAKE, ws, 0)
+            assert e.value.status == wvd.WVD_EINVAL
+        with pytest.raises(wvd.WvdError) as e:
+            wvd.wvd_decode(plan, FAKE, 3, 3, FAKE, FAKE + 8, ws, 0)  # misaligned workspace
+        assert e.value.status == wvd.WVD_EINVAL
+    finally:
+        wvd.wvd_destroy(plan)
+
+
+def test_workspace_fits_288GB_at_the_largest_sweep_point(dry):
+    wvd = dry
+    plan = plan_for(wvd, 256, 44, 78)
+    try:
+        sizes = {P: wvd.wvd_workspace_bytes(plan, 121, P) for P in (2, 4, 8, 16)}
+        assert sizes[2] < sizes[4] < sizes[8] < sizes[16] < 200e9
+    finally:
+        wvd.wvd_destroy(plan)

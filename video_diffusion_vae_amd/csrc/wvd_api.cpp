@@ -1,0 +1,740 @@
+// Host side of the wvd library: the C ABI, the prepared-weight layout, the
+// workspace plan and the pass scheduler that walks the decoder frames_per_pass
+// latent frames at a time, carrying two history frames per causal conv in a
+// ring (the "temporal caching" of the TensorRT-LLM norm-SiLU issue; chunked
+// decoding that leaves the video unchanged, Wan2.2 VAE decoder page,
+// "Performance and memory").
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "wvd.h"
+#include "wvd_internal.h"
+
+using namespace wvd;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+enum ItemKind { K_CONV = 0, K_PHASE = 1, K_VEC = 2 };
+
+// One canonical weight tensor and where its prepared form lives.
+struct Item {
+  int kind;
+  int cout, cin, taps, cin_pad;  // conv: PyTorch [cout][cin][taps] -> [taps][cout][cin_pad]
+  int n;                          // vec length
+  float scale;                    // vec scale (sqrt(C) for gammas)
+  size_t off;                     // byte offset in the prepared buffer
+  size_t bytes;
+};
+
+// Indices of the canonical tensors of one ResBlock.
+struct RB {
+  int norm1, conv1w, conv1b, norm2, conv2w, conv2b, scw = -1, scb = -1;
+  int cin, cout;
+};
+
+struct Layout {
+  std::vector<Item> items;
+  int conv_in_w, conv_in_b;
+  RB mid0, mid1, up[4][2];
+  int attn_norm, qkv_w, qkv_b, proj_w, proj_b;
+  int tc_w[2], tc_b[2], upc_w[3], upc_b[3];
+  int head_norm, head_w, head_b;
+  size_t total = 0;
+};
+
+void add_conv(Layout& L, int cout, int cin, int taps, int cin_pad, int* wi, int* bi) {
+  Item w{K_CONV, cout, cin, taps, cin_pad, 0, 1.0f, 0, 0};
+  w.bytes = (size_t)taps * cout * cin_pad * 2;
+  *wi = (int)L.items.size();
+  L.items.push_back(w);
+  Item b{K_VEC, 0, 0, 0, 0, cout, 1.0f, 0, (size_t)cout * 4};
+  *bi = (int)L.items.size();
+  L.items.push_back(b);
+}
+int add_vec(Layout& L, int n, float scale) {
+  Item g{K_VEC, 0, 0, 0, 0, n, scale, 0, (size_t)n * 4};
+  L.items.push_back(g);
+  return (int)L.items.size() - 1;
+}
+RB add_rb(Layout& L, int cin, int cout) {
+  RB r;
+  r.cin = cin;
+  r.cout = cout;
+  r.norm1 = add_vec(L, cin, std::sqrt((float)cin));
+  add_conv(L, cout, cin, 27, cin, &r.conv1w, &r.conv1b);
+  r.norm2 = add_vec(L, cout, std::sqrt((float)cout));
+  add_conv(L, cout, cout, 27, cout, &r.conv2w, &r.conv2b);
+  if (cin != cout) add_conv(L, cout, cin, 1, cin, &r.scw, &r.scb);
+  return r;
+}
+
+Layout make_layout(int c) {
+  Layout L;
+  const int c4 = 4 * c;
+  const int widths[4] = {c4, c4, 2 * c, c};
+  add_conv(L, c4, 48, 27, 64, &L.conv_in_w, &L.conv_in_b);
+  L.mid0 = add_rb(L, c4, c4);
+  L.attn_norm = add_vec(L, c4, std::sqrt((float)c4));
+  add_conv(L, 3 * c4, c4, 1, c4, &L.qkv_w, &L.qkv_b);
+  add_conv(L, c4, c4, 1, c4, &L.proj_w, &L.proj_b);
+  L.mid1 = add_rb(L, c4, c4);
+  int prev = c4;
+  for (int s = 0; s < 4; ++s) {
+    const int cs = widths[s];
+    L.up[s][0] = add_rb(L, prev, cs);
+    L.up[s][1] = add_rb(L, cs, cs);
+    if (s < 2) add_conv(L, 2 * cs, cs, 3, cs, &L.tc_w[s], &L.tc_b[s]);
+    if (s < 3) {
+      add_conv(L, cs, cs, 9, cs, &L.upc_w[s], &L.upc_b[s]);
+      Item& it = L.items[L.upc_w[s]];
+      it.kind = K_PHASE;
+      it.taps = 16;  // 4 phases x 2x2 taps
+      it.bytes = (size_t)16 * cs * cs * 2;
+    }
+    prev = cs;
+  }
+  L.head_norm = add_vec(L, c, std::sqrt((float)c));
+  add_conv(L, 12, c, 27, c, &L.head_w, &L.head_b);
+  size_t off = 0;
+  for (auto& it : L.items) {
+    it.off = off;
+    off = align_up(off + it.bytes);
+  }
+  L.total = off;
+  return L;
+}
+
+// Workspace carve-up for a given maximum number of latent frames per pass.
+struct Work {
+  size_t X, H, Y, zt, rs, qkv, S, Pm, Vt, O;
+  std::vector<size_t> ring;  // 24 rings
+  size_t total;
+};
+
+struct RingInfo {
+  int cin;
+  int level;
+};
+
+enum RingId {
+  R_CONV_IN = 0, R_MID0_1, R_MID0_2, R_MID1_1, R_MID1_2,
+  R_UP00_1, R_UP00_2, R_UP01_1, R_UP01_2, R_TC0,
+  R_UP10_1, R_UP10_2, R_UP11_1, R_UP11_2, R_TC1,
+  R_UP20_1, R_UP20_2, R_UP21_1, R_UP21_2,
+  R_UP30_1, R_UP30_2, R_UP31_1, R_UP31_2,
+  R_HEAD, R_COUNT
+};
+
+RingInfo ring_info(int c, int id) {
+  const int c4 = 4 * c, c2 = 2 * c;
+  switch (id) {
+    case R_CONV_IN: return {64, 0};
+    case R_MID0_1: case R_MID0_2: case R_MID1_1: case R_MID1_2:
+    case R_UP00_1: case R_UP00_2: case R_UP01_1: case R_UP01_2: case R_TC0: return {c4, 0};
+    case R_UP10_1: case R_UP10_2: case R_UP11_1: case R_UP11_2: case R_TC1: return {c4, 1};
+    case R_UP20_1: return {c4, 2};
+    case R_UP20_2: case R_UP21_1: case R_UP21_2: return {c2, 2};
+    case R_UP30_1: return {c2, 3};
+    default: return {c, 3};  // R_UP30_2, R_UP31_*, R_HEAD
+  }
+}
+
+int lpad_of(int L) { return (L + 31) / 32 * 32; }
+
+Work make_work(int c, int h, int w, int P) {
+  Work W;
+  const long long r0 = (long long)h * w;
+  const long long res[4] = {r0, 4 * r0, 16 * r0, 64 * r0};
+  const long long c4 = 4 * c, c2 = 2 * c;
+  const long long F0 = P, F1 = 2LL * P, F2 = 4LL * P;
+  long long act = std::max({F0 * r0 * c4, F1 * res[1] * c4, F2 * res[2] * c4, F2 * res[3] * c2});
+  const long long L = r0, Lp = lpad_of((int)r0);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  W.X = take(act * 2);
+  W.H = take(act * 2);
+  W.Y = take(act * 2);
+  W.zt = take((size_t)F0 * r0 * 64 * 2);
+  W.rs = take((size_t)(F2 + 2) * res[3] * 4);
+  W.qkv = take((size_t)F0 * L * 3 * c4 * 2);
+  W.S = take((size_t)F0 * L * Lp * 4);
+  W.Pm = take((size_t)F0 * L * Lp * 2);
+  W.Vt = take((size_t)F0 * c4 * Lp * 2);
+  W.O = take((size_t)F0 * L * c4 * 2);
+  for (int i = 0; i < R_COUNT; ++i) {
+    RingInfo ri = ring_info(c, i);
+    W.ring.push_back(take((size_t)2 * res[ri.level] * ri.cin * 2));
+  }
+  W.total = off;
+  return W;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+struct ProfRec {
+  int cls;
+  double flops;
+  hipEvent_t e0, e1;
+};
+
+}  // namespace
+
+struct wvd_plan {
+  int c, h, w;
+  Layout L;
+  unsigned char* prep;
+  bool profile = false;
+  std::vector<ProfRec> recs;
+  std::vector<hipEvent_t> pool;
+  size_t pool_used = 0;
+  double acc_ms[5] = {0, 0, 0, 0, 0};
+  double acc_flops[5] = {0, 0, 0, 0, 0};
+  long long launches = 0;  // kernel launches of the last wvd_decode
+  int magic = 0x77766470;
+};
+
+namespace {
+
+bool plan_ok(const wvd_plan* p) { return p && p->magic == 0x77766470; }
+
+int check_dims(int c, int h, int w) {
+  if (c <= 0 || c % 16 != 0 || 4 * c > kMaxCin) return WVD_EUNSUPPORTED;
+  if (h < 1 || w < 1 || h > 4096 || w > 4096) return WVD_EUNSUPPORTED;
+  return WVD_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Decode-time scheduler
+// ---------------------------------------------------------------------------
+
+thread_local std::string g_last_error;
+
+void set_error(const char* what, hipError_t e) {
+  g_last_error = std::string(what) + ": " + hipGetErrorName(e) + " (" + hipGetErrorString(e) + ")";
+}
+
+struct Ctx {
+  wvd_plan* plan;
+  hipStream_t st;
+  unsigned char* ws;
+  const Work* W;
+  hipError_t err = hipSuccess;
+  const char* what = "";
+
+  template <typename T>
+  T* prep(int item) const { return reinterpret_cast<T*>(plan->prep + plan->L.items[item].off); }
+  template <typename T>
+  T* wsp(size_t off) const { return reinterpret_cast<T*>(ws + off); }
+
+  hipEvent_t ev() {
+    if (plan->pool_used == plan->pool.size()) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      plan->pool.push_back(e);
+    }
+    return plan->pool[plan->pool_used++];
+  }
+  template <typename F>
+  void run(int cls, double flops, F&& fn) {
+    if (err != hipSuccess) return;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (plan->profile) {
+      e0 = ev();
+      e1 = ev();
+      if (e0) hipEventRecord(e0, st);
+    }
+    err = fn();
+    if (err != hipSuccess) set_error(what, err);
+    ++plan->launches;
+    if (plan->profile && e0 && e1) {
+      hipEventRecord(e1, st);
+      plan->recs.push_back({cls, flops, e0, e1});
+    }
+  }
+};
+
+ConvSeg seg_basic(const bf16_t* x, long long x_fstride, int lda, int Cin, const bf16_t* w, int ldw,
+                  long long tap_stride, int KT, int KS) {
+  ConvSeg s;
+  std::memset(&s, 0, sizeof(s));
+  s.x = x;
+  s.x_fstride = x_fstride;
+  s.lda = lda;
+  s.Cin = Cin;
+  s.w = w;
+  s.ldw = ldw;
+  s.w_tap_stride = tap_stride;
+  s.KT = KT;
+  s.KS = KS;
+  s.prologue = PRO_RAW;
+  return s;
+}
+
+void set_grid(ConvArgs& a, int F, int H, int W, int TF) {
+  a.F = F;
+  a.H = H;
+  a.W = W;
+  a.TF = TF;
+  a.TH = kTileM / kTileW / TF;
+  a.tiles_x = (W + kTileW - 1) / kTileW;
+  a.tiles_y = (H + a.TH - 1) / a.TH;
+  a.tiles_f = (F + TF - 1) / TF;
+  if (a.nphase == 0) a.nphase = 1;
+  int nhv = 0;
+  for (int s = 0; s < a.nseg; ++s) {
+    const ConvSeg& g = a.seg[s];
+    const int hs = g.KS == 1 ? 0 : 1;
+    nhv = std::max(nhv, (TF + g.KT - 1) * (a.TH + 2 * hs) * (kTileW + 2 * hs));
+  }
+  a.nhv_max = nhv;
+}
+
+ConvArgs args_init() {
+  ConvArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.scale = 1.0f;
+  a.nphase = 1;
+  return a;
+}
+
+double conv_flops(const ConvArgs& a) {
+  double f = 0;
+  const double vox = (double)a.F * a.H * a.W * a.nphase;
+  for (int s = 0; s < a.nseg; ++s) {
+    const ConvSeg& g = a.seg[s];
+    const int k2 = g.KS == 3 ? 9 : (g.KS == 2 ? 4 : 1);
+    f += 2.0 * vox * a.Cout * (double)g.KT * k2 * g.Cin;
+  }
+  return f;
+}
+
+void conv(Ctx& cx, ConvArgs& a, int cls) {
+  const char* why = conv_check(a);
+  if (why && cx.err == hipSuccess) {
+    cx.err = hipErrorInvalidValue;
+    g_last_error = std::string("conv launch check: ") + why;
+    return;
+  }
+  cx.what = "conv";
+  cx.run(cls, conv_flops(a), [&] { return launch_conv(a, cx.st); });
+}
+
+struct Act {
+  bf16_t* p;
+  int C;      // channels (= voxel stride)
+  int F;      // frames in this pass
+  int H, W;
+  long long fstride() const { return (long long)H * W * C; }
+};
+
+void stats(Ctx& cx, const Act& x, const bf16_t* ring, int nh) {
+  float* rs = cx.wsp<float>(cx.W->rs);
+  cx.what = "rms_stats";
+  cx.run(3, 0, [&] { return launch_rms_stats(x.p, x.fstride(), x.C, ring, nh, x.C, x.F, x.H * x.W, rs, cx.st); });
+}
+
+void ring_update(Ctx& cx, bf16_t* ring, const Act& x) {
+  cx.what = "ring_update";
+  cx.run(4, 0, [&] { return launch_ring_update(ring, x.p, x.fstride(), x.C, x.C, x.F, x.H * x.W, cx.st); });
+}
+
+int tf_for(int KT, int F) { return (KT == 3 && F > 1) ? 2 : 1; }
+
+// Causal 3x3x3 conv with the fused RMSNorm+SiLU prologue.
+ConvArgs conv333(Ctx& cx, const Act& x, bf16_t* ring, int nh, int gamma_item, int w_item, int b_item, int Cout) {
+  ConvArgs a = args_init();
+  ConvSeg& s = a.seg[0];
+  s = seg_basic(x.p, x.fstride(), x.C, x.C, cx.prep<bf16_t>(w_item), x.C, (long long)Cout * x.C, 3, 3);
+  s.ring = ring;
+  s.n_hist = nh;
+  s.rs = cx.wsp<float>(cx.W->rs);
+  s.gamma = cx.prep<float>(gamma_item);
+  s.prologue = PRO_NORM_SILU;
+  a.nseg = 1;
+  a.Cout = Cout;
+  a.bias = cx.prep<float>(b_item);
+  return a;
+}
+
+// ResBlock: x -> x (in place) when widths match, else x -> out.
+Act resblock(Ctx& cx, const RB& rb, const Act& x, bf16_t* hbuf, bf16_t* obuf, int ring1, int ring2, int nh) {
+  bf16_t* r1 = cx.wsp<bf16_t>(cx.W->ring[ring1]);
+  bf16_t* r2 = cx.wsp<bf16_t>(cx.W->ring[ring2]);
+  stats(cx, x, r1, nh);
+  Act h{hbuf, rb.cout, x.F, x.H, x.W};
+  {
+    ConvArgs a = conv333(cx, x, r1, nh, rb.norm1, rb.conv1w, rb.conv1b, rb.cout);
+    a.out = h.p;
+    a.out_fstride = h.fstride();
+    a.ldo = h.C;
+    a.epi = EPI_BF16;
+    set_grid(a, x.F, x.H, x.W, tf_for(3, x.F));
+    conv(cx, a, 0);
+  }
+  ring_update(cx, r1, x);
+  stats(cx, h, r2, nh);
+  Act out{rb.cin == rb.cout ? x.p : obuf, rb.cout, x.F, x.H, x.W};
+  {
+    ConvArgs a = conv333(cx, h, r2, nh, rb.norm2, rb.conv2w, rb.conv2b, rb.cout);
+    if (rb.cin == rb.cout) {
+      a.res = x.p;
+      a.res_fstride = x.fstride();
+      a.ldr = x.C;
+    } else {
+      // 1x1x1 shortcut over the raw block input as a second K segment; its
+      // bias is pre-summed with conv2's into the shortcut bias slot.
+      a.seg[1] = seg_basic(x.p, x.fstride(), x.C, x.C, cx.prep<bf16_t>(rb.scw), x.C, 0, 1, 1);
+      a.nseg = 2;
+      a.bias = cx.prep<float>(rb.scb);
+    }
+    a.out = out.p;
+    a.out_fstride = out.fstride();
+    a.ldo = out.C;
+    a.epi = EPI_BF16;
+    set_grid(a, x.F, x.H, x.W, tf_for(3, x.F));
+    conv(cx, a, 0);
+  }
+  ring_update(cx, r2, h);
+  return out;
+}
+
+void attention(Ctx& cx, const Act& x) {
+  const Layout& L = cx.plan->L;
+  const int C = x.C, Lt = x.H * x.W, Lp = lpad_of(Lt);
+  bf16_t* qkv = cx.wsp<bf16_t>(cx.W->qkv);
+  float* S = cx.wsp<float>(cx.W->S);
+  bf16_t* Pm = cx.wsp<bf16_t>(cx.W->Pm);
+  bf16_t* Vt = cx.wsp<bf16_t>(cx.W->Vt);
+  bf16_t* O = cx.wsp<bf16_t>(cx.W->O);
+  stats(cx, x, nullptr, 0);
+  {  // qkv = Wqkv RMSNorm(x) + b
+    ConvArgs a = args_init();
+    a.seg[0] = seg_basic(x.p, x.fstride(), C, C, cx.prep<bf16_t>(L.qkv_w), C, 0, 1, 1);
+    a.seg[0].rs = cx.wsp<float>(cx.W->rs);
+    a.seg[0].gamma = cx.prep<float>(L.attn_norm);
+    a.seg[0].prologue = PRO_NORM;
+    a.nseg = 1;
+    a.Cout = 3 * C;
+    a.bias = cx.prep<float>(L.qkv_b);
+    a.out = qkv;
+    a.out_fstride = (long long)Lt * 3 * C;
+    a.ldo = 3 * C;
+    a.epi = EPI_BF16;
+    set_grid(a, x.F, x.H, x.W, 1);
+    conv(cx, a, 1);
+  }
+  {  // S = Q K^T / sqrt(C), per frame
+    ConvArgs a = args_init();
+    a.seg[0] = seg_basic(qkv, (long long)Lt * 3 * C, 3 * C, C, qkv + C, 3 * C, 0, 1, 1);
+    a.seg[0].w_frame_stride = (long long)Lt * 3 * C;
+    a.nseg = 1;
+    a.Cout = Lt;
+    a.scale = 1.0f / std::sqrt((float)C);
+    a.out = S;
+    a.out_fstride = (long long)Lt * Lp;
+    a.ldo = Lp;
+    a.epi = EPI_F32;
+    set_grid(a, x.F, x.H, x.W, 1);
+    conv(cx, a, 2);
+  }
+  cx.run(4, 0, [&] { return launch_softmax_rows(S, x.F * Lt, Lt, Lp, Pm, cx.st); });
+  cx.run(4, 0, [&] { return launch_transpose_v(qkv, x.F, Lt, C, Lp, Vt, cx.st); });
+  {  // O = P V
+    ConvArgs a = args_init();
+    a.seg[0] = seg_basic(Pm, (long long)Lt * Lp, Lp, Lp, Vt, Lp, 0, 1, 1);
+    a.seg[0].w_frame_stride = (long long)C * Lp;
+    a.nseg = 1;
+    a.Cout = C;
+    a.out = O;
+    a.out_fstride = (long long)Lt * C;
+    a.ldo = C;
+    a.epi = EPI_BF16;
+    set_grid(a, x.F, x.H, x.W, 1);
+    conv(cx, a, 2);
+  }
+  {  // x += Wp O + bp
+    ConvArgs a = args_init();
+    a.seg[0] = seg_basic(O, (long long)Lt * C, C, C, cx.prep<bf16_t>(L.proj_w), C, 0, 1, 1);
+    a.nseg = 1;
+    a.Cout = C;
+    a.bias = cx.prep<float>(L.proj_b);
+    a.res = x.p;
+    a.res_fstride = x.fstride();
+    a.ldr = C;
+    a.out = x.p;
+    a.out_fstride = x.fstride();
+    a.ldo = C;
+    a.epi = EPI_BF16;
+    set_grid(a, x.F, x.H, x.W, 1);
+    conv(cx, a, 1);
+  }
+}
+
+// time_conv: x (F frames, first global frame g) -> y (interleaved frames).
+Act time_upsample(Ctx& cx, int s, const Act& x, int g, bf16_t* ybuf, int ring_id) {
+  const Layout& L = cx.plan->L;
+  bf16_t* ring = cx.wsp<bf16_t>(cx.W->ring[ring_id]);
+  const bool first = g == 0;
+  Act y{ybuf, x.C, first ? 2 * x.F - 1 : 2 * x.F, x.H, x.W};
+  if (first) {
+    cx.run(4, 0, [&] { return launch_copy16(y.p, x.p, (size_t)x.fstride() * 2, cx.st); });
+  }
+  Act sx{first ? x.p + x.fstride() : x.p, x.C, first ? x.F - 1 : x.F, x.H, x.W};
+  if (sx.F == 0) return y;
+  const int nh = std::min(2, std::max(0, g - 1));
+  ConvArgs a = args_init();
+  a.seg[0] = seg_basic(sx.p, sx.fstride(), sx.C, sx.C, cx.prep<bf16_t>(L.tc_w[s]), sx.C, 2LL * sx.C * sx.C, 3, 1);
+  a.seg[0].ring = ring;
+  a.seg[0].n_hist = nh;
+  a.nseg = 1;
+  a.Cout = 2 * x.C;
+  a.bias = cx.prep<float>(L.tc_b[s]);
+  a.out = y.p;
+  a.out_fstride = y.fstride();
+  a.ldo = y.C;
+  a.epi = EPI_TIME;
+  a.out_base = first ? 1 : 0;
+  set_grid(a, sx.F, sx.H, sx.W, tf_for(3, sx.F));
+  conv(cx, a, 1);
+  ring_update(cx, ring, sx);
+  return y;
+}
+
+// Nearest-2x + Conv2d 3x3 in phase form: x [F][H][W][C] -> y [F][2H][2W][C].
+Act up_conv(Ctx& cx, int s, const Act& x, bf16_t* ybuf) {
+  const Layout& L = cx.plan->L;
+  Act y{ybuf, x.C, x.F, 2 * x.H, 2 * x.W};
+  ConvArgs a = args_init();
+  a.seg[0] = seg_basic(x.p, x.fstride(), x.C, x.C, cx.prep<bf16_t>(L.upc_w[s]), x.C, (long long)x.C * x.C, 1, 2);
+  a.nseg = 1;
+  a.nphase = 4;
+  a.Cout = x.C;
+  a.bias = cx.prep<float>(L.upc_b[s]);
+  a.out = y.p;
+  a.out_fstride = y.fstride();
+  a.ldo = y.C;
+  a.epi = EPI_PHASE;
+  set_grid(a, x.F, x.H, x.W, 1);
+  conv(cx, a, 1);
+  return y;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* wvd_status_string(int st) {
+  switch (st) {
+    case WVD_OK: return "ok";
+    case WVD_EINVAL: return "invalid argument";
+    case WVD_ESHAPE: return "shape inconsistent with the plan";
+    case WVD_ENOSPACE: return "buffer smaller than required";
+    case WVD_EUNSUPPORTED: return "unsupported configuration";
+    case WVD_EHIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+int wvd_prepared_bytes(int c, int h, int w, size_t* bytes) {
+  if (!bytes) return WVD_EINVAL;
+  int st = check_dims(c, h, w);
+  if (st) return st;
+  *bytes = make_layout(c).total;
+  return WVD_OK;
+}
+
+int wvd_prepare(int c, int h, int w, const void* const* weights, int n_weights, void* prepared,
+                size_t prepared_bytes, void* stream, wvd_plan** plan_out) {
+  if (!weights || !prepared || !plan_out) return WVD_EINVAL;
+  int st = check_dims(c, h, w);
+  if (st) return st;
+  if (n_weights != WVD_NUM_WEIGHTS) return WVD_EINVAL;
+  for (int i = 0; i < n_weights; ++i)
+    if (!weights[i]) return WVD_EINVAL;
+  if (!aligned16(prepared)) return WVD_EINVAL;
+  Layout L = make_layout(c);
+  if ((int)L.items.size() != WVD_NUM_WEIGHTS) return WVD_EINVAL;
+  if (prepared_bytes < L.total) return WVD_ENOSPACE;
+  wvd_plan* p = new (std::nothrow) wvd_plan();
+  if (!p) return WVD_EINVAL;
+  p->c = c;
+  p->h = h;
+  p->w = w;
+  p->L = L;
+  p->prep = static_cast<unsigned char*>(prepared);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  for (int i = 0; i < WVD_NUM_WEIGHTS && e == hipSuccess; ++i) {
+    const Item& it = L.items[i];
+    const bf16_t* src = static_cast<const bf16_t*>(weights[i]);
+    void* dst = p->prep + it.off;
+    if (it.kind == K_CONV)
+      e = launch_prep_permute(src, it.cout, it.cin, it.taps, it.cin_pad, static_cast<bf16_t*>(dst), s);
+    else if (it.kind == K_PHASE)
+      e = launch_prep_phase(src, it.cout, static_cast<bf16_t*>(dst), s);
+    else
+      e = launch_prep_vec(src, it.n, it.scale, static_cast<float*>(dst), s);
+  }
+  // Blocks with a shortcut add two biases; keep their sum in the shortcut slot.
+  const RB* sc_blocks[2] = {&L.up[2][0], &L.up[3][0]};
+  for (const RB* rb : sc_blocks) {
+    if (e != hipSuccess) break;
+    e = launch_prep_vec_add(static_cast<const bf16_t*>(weights[rb->conv2b]), static_cast<const bf16_t*>(weights[rb->scb]),
+                            rb->cout, reinterpret_cast<float*>(p->prep + L.items[rb->scb].off), s);
+  }
+  if (e != hipSuccess) {
+    set_error("wvd_prepare", e);
+    delete p;
+    return WVD_EHIP;
+  }
+  *plan_out = p;
+  return WVD_OK;
+}
+
+int wvd_workspace_bytes(const wvd_plan* plan, int T, int frames_per_pass, size_t* bytes) {
+  if (!plan_ok(plan) || !bytes || T < 1 || frames_per_pass < 1) return WVD_EINVAL;
+  const int P = std::min(T, frames_per_pass);
+  *bytes = make_work(plan->c, plan->h, plan->w, P).total;
+  return WVD_OK;
+}
+
+int wvd_decode(const wvd_plan* cplan, const void* z, int T, int frames_per_pass, void* out, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  if (!plan_ok(cplan) || !z || !out || !workspace || T < 1 || frames_per_pass < 1) return WVD_EINVAL;
+  if (!aligned16(workspace)) return WVD_EINVAL;
+  wvd_plan* plan = const_cast<wvd_plan*>(cplan);
+  const int c = plan->c, h = plan->h, w = plan->w;
+  const int P = std::min(T, frames_per_pass);
+  Work W = make_work(c, h, w, P);
+  if (workspace_bytes < W.total) return WVD_ENOSPACE;
+  const Layout& L = plan->L;
+  Ctx cx;
+  cx.plan = plan;
+  cx.st = static_cast<hipStream_t>(stream);
+  cx.ws = static_cast<unsigned char*>(workspace);
+  cx.W = &W;
+  plan->launches = 0;
+  const int c4 = 4 * c;
+  bf16_t* X = cx.wsp<bf16_t>(W.X);
+  bf16_t* Hb = cx.wsp<bf16_t>(W.H);
+  bf16_t* Y = cx.wsp<bf16_t>(W.Y);
+  bf16_t* zt = cx.wsp<bf16_t>(W.zt);
+  const int VT = 4 * T - 3;
+
+  for (int t0 = 0; t0 < T && cx.err == hipSuccess; t0 += P) {
+    const int F0 = std::min(P, T - t0);
+    const bool first = t0 == 0;
+    const int g0 = t0, g1 = first ? 0 : 2 * t0 - 1, g2 = first ? 0 : 4 * t0 - 3;
+    const int nh0 = std::min(2, g0), nh1 = std::min(2, g1), nh2 = std::min(2, g2);
+    // conv_in on the channels-last latents.
+    cx.run(4, 0, [&] { return launch_latent_to_cl(static_cast<const bf16_t*>(z), T, t0, F0, h * w, zt, cx.st); });
+    Act za{zt, 64, F0, h, w};
+    Act x{X, c4, F0, h, w};
+    {
+      bf16_t* ring = cx.wsp<bf16_t>(W.ring[R_CONV_IN]);
+      ConvArgs a = args_init();
+      a.seg[0] = seg_basic(zt, za.fstride(), 64, 64, cx.prep<bf16_t>(L.conv_in_w), 64, (long long)c4 * 64, 3, 3);
+      a.seg[0].ring = ring;
+      a.seg[0].n_hist = nh0;
+      a.nseg = 1;
+      a.Cout = c4;
+      a.bias = cx.prep<float>(L.conv_in_b);
+      a.out = x.p;
+      a.out_fstride = x.fstride();
+      a.ldo = c4;
+      a.epi = EPI_BF16;
+      set_grid(a, F0, h, w, tf_for(3, F0));
+      conv(cx, a, 0);
+      ring_update(cx, ring, za);
+    }
+    x = resblock(cx, L.mid0, x, Hb, nullptr, R_MID0_1, R_MID0_2, nh0);
+    attention(cx, x);
+    x = resblock(cx, L.mid1, x, Hb, nullptr, R_MID1_1, R_MID1_2, nh0);
+    // Stage 0 (h x w), time_conv, up-conv to 2h x 2w.
+    x = resblock(cx, L.up[0][0], x, Hb, nullptr, R_UP00_1, R_UP00_2, nh0);
+    x = resblock(cx, L.up[0][1], x, Hb, nullptr, R_UP01_1, R_UP01_2, nh0);
+    Act y = time_upsample(cx, 0, x, g0, Y, R_TC0);
+    x = up_conv(cx, 0, y, X);
+    // Stage 1 (2h x 2w).
+    x = resblock(cx, L.up[1][0], x, Hb, nullptr, R_UP10_1, R_UP10_2, nh1);
+    x = resblock(cx, L.up[1][1], x, Hb, nullptr, R_UP11_1, R_UP11_2, nh1);
+    y = time_upsample(cx, 1, x, g1, Y, R_TC1);
+    x = up_conv(cx, 1, y, X);
+    // Stage 2 (4h x 4w): 4c -> 2c.
+    x = resblock(cx, L.up[2][0], x, Hb, Y, R_UP20_1, R_UP20_2, nh2);
+    x = resblock(cx, L.up[2][1], x, Hb, nullptr, R_UP21_1, R_UP21_2, nh2);
+    x = up_conv(cx, 2, x, X);
+    // Stage 3 (8h x 8w): 2c -> c.
+    x = resblock(cx, L.up[3][0], x, Hb, Y, R_UP30_1, R_UP30_2, nh2);
+    x = resblock(cx, L.up[3][1], x, Hb, nullptr, R_UP31_1, R_UP31_2, nh2);
+    // Head: RMSNorm + SiLU + conv c -> 12, pixel shuffle, clamp, NCTHW video.
+    {
+      bf16_t* ring = cx.wsp<bf16_t>(W.ring[R_HEAD]);
+      stats(cx, x, ring, nh2);
+      ConvArgs a = conv333(cx, x, ring, nh2, L.head_norm, L.head_w, L.head_b, 12);
+      a.out = out;
+      a.epi = EPI_VIDEO;
+      a.out_base = g2;
+      a.video_T = VT;
+      set_grid(a, x.F, x.H, x.W, tf_for(3, x.F));
+      conv(cx, a, 0);
+      ring_update(cx, ring, x);
+    }
+  }
+  if (cx.err != hipSuccess) return WVD_EHIP;
+  return WVD_OK;
+}
+
+const char* wvd_last_error(void) { return g_last_error.c_str(); }
+
+void wvd_set_dry_run(int on) { g_dry_run = on != 0; }
+
+long long wvd_last_launch_count(const wvd_plan* plan) { return plan_ok(plan) ? plan->launches : -1; }
+
+void wvd_destroy(wvd_plan* plan) {
+  if (!plan_ok(plan)) return;
+  for (hipEvent_t e : plan->pool) hipEventDestroy(e);
+  plan->magic = 0;
+  delete plan;
+}
+
+int wvd_profile_enable(wvd_plan* plan, int on) {
+  if (!plan_ok(plan)) return WVD_EINVAL;
+  plan->profile = on != 0;
+  return WVD_OK;
+}
+
+int wvd_profile_read(const wvd_plan* cplan, double* ms, double* flops, int n_classes) {
+  if (!plan_ok(cplan) || !ms || !flops || n_classes < 1) return WVD_EINVAL;
+  wvd_plan* plan = const_cast<wvd_plan*>(cplan);
+  if (!plan->recs.empty() && hipEventSynchronize(plan->recs.back().e1) != hipSuccess) return WVD_EHIP;
+  double m[5] = {0, 0, 0, 0, 0}, f[5] = {0, 0, 0, 0, 0};
+  for (const ProfRec& r : plan->recs) {
+    float t = 0;
+    if (hipEventElapsedTime(&t, r.e0, r.e1) != hipSuccess) return WVD_EHIP;
+    m[r.cls] += t;
+    f[r.cls] += r.flops;
+  }
+  for (int i = 0; i < n_classes && i < 5; ++i) {
+    ms[i] = m[i];
+    flops[i] = f[i];
+  }
+  plan->recs.clear();
+  plan->pool_used = 0;
+  return WVD_OK;
+}
+
+}  // extern "C"

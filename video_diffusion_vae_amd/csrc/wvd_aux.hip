@@ -1,0 +1,290 @@
+// Memory-bound helper kernels of the wvd decoder: per-voxel RMS statistics,
+// temporal-cache ring updates, latent layout transform, frame copies, the
+// attention softmax and V transpose, and the one-time weight transforms.
+#include "wvd_internal.h"
+
+namespace wvd {
+
+bool g_dry_run = false;
+
+namespace {
+
+constexpr float kNormEps = 1e-12f;
+
+// rs[slot][pix] = 1 / max(||x_voxel||, eps) over the C channels of a voxel,
+// for slots 0,1 = the two history frames held in `ring` (only the last
+// n_hist are valid) and slots 2.. = the F frames of the pass.  G lanes share
+// a voxel; lane sums run over channel groups of 8 in increasing order, then a
+// fixed butterfly combines the G lanes, so the value of a voxel never depends
+// on where or when it is computed (fp32 statistics: Wan2.2 VAE decoder page,
+// "Limits").
+__global__ __launch_bounds__(256) void rms_stats_kernel(const bf16_t* __restrict__ x, long long x_fstride,
+                                                        int lda, const bf16_t* __restrict__ ring,
+                                                        int n_hist, int C, int F, int HW, int G,
+                                                        float* __restrict__ rs) {
+  const int lane = threadIdx.x & 63;
+  const int sub = lane % G;
+  const int vox_per_wave = 64 / G;
+  const long long gw = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const long long nw = ((long long)gridDim.x * blockDim.x) >> 6;
+  const int first_slot = 2 - n_hist;
+  const long long nvox = (long long)(F + n_hist) * HW;
+  const int ngroups = C >> 3;
+  for (long long base = gw * vox_per_wave; base < nvox; base += nw * vox_per_wave) {
+    const long long vv = base + lane / G;
+    float ss = 0.0f;
+    const bool ok = vv < nvox;
+    long long slot = 0, pix = 0;
+    if (ok) {
+      slot = vv / HW + first_slot;
+      pix = vv % HW;
+      const bf16_t* p = slot < 2 ? ring + (slot * HW + pix) * C : x + (slot - 2) * x_fstride + pix * lda;
+      for (int g = sub; g < ngroups; g += G) {
+        uint4 r = *reinterpret_cast<const uint4*>(p + g * 8);
+        float f[8];
+        unpack8(r, f);
+        float t = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) t += f[k] * f[k];
+        ss += t;
+      }
+    }
+    for (int off = 1; off < G; off <<= 1) ss += __shfl_xor(ss, off, 64);
+    if (ok && sub == 0) rs[slot * HW + pix] = 1.0f / fmaxf(sqrtf(ss), kNormEps);
+  }
+}
+
+// ring <- the last two frames of [ring[0], ring[1], x[0..F-1]] (F >= 1).
+__global__ __launch_bounds__(256) void ring_update_kernel(bf16_t* __restrict__ ring, const bf16_t* __restrict__ x,
+                                                          long long x_fstride, int lda, int C, int F, int HW) {
+  const int g8 = C >> 3;
+  const long long n = (long long)HW * g8;
+  const long long fs = (long long)HW * C;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+       e += (long long)gridDim.x * blockDim.x) {
+    const long long pix = e / g8;
+    const int g = (int)(e % g8);
+    const long long ro = pix * C + g * 8;
+    uint4 s1 = *reinterpret_cast<const uint4*>(x + (F - 1) * x_fstride + pix * lda + g * 8);
+    uint4 s0 = F >= 2 ? *reinterpret_cast<const uint4*>(x + (F - 2) * x_fstride + pix * lda + g * 8)
+                      : *reinterpret_cast<const uint4*>(ring + fs + ro);
+    *reinterpret_cast<uint4*>(ring + ro) = s0;
+    *reinterpret_cast<uint4*>(ring + fs + ro) = s1;
+  }
+}
+
+// z [48][T][HW] frames t0..t0+F-1 -> zt [F][HW][64] (channels 48..63 zero).
+__global__ __launch_bounds__(256) void latent_to_cl_kernel(const bf16_t* __restrict__ z, int T, int t0, int F,
+                                                           int HW, bf16_t* __restrict__ zt) {
+  const long long n = (long long)F * HW;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+       e += (long long)gridDim.x * blockDim.x) {
+    const long long f = e / HW, pix = e % HW;
+    uint32_t w[32];
+#pragma unroll
+    for (int c2 = 0; c2 < 32; ++c2) {
+      const int c = 2 * c2;
+      uint32_t lo = 0, hi = 0;
+      if (c < 48) {
+        lo = z[((long long)c * T + t0 + f) * HW + pix];
+        hi = z[((long long)(c + 1) * T + t0 + f) * HW + pix];
+      }
+      w[c2] = lo | (hi << 16);
+    }
+    uint4* dst = reinterpret_cast<uint4*>(zt + e * 64);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) dst[q] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+  }
+}
+
+__global__ __launch_bounds__(256) void copy16_kernel(uint4* __restrict__ dst, const uint4* __restrict__ src, long long n) {
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+       e += (long long)gridDim.x * blockDim.x)
+    dst[e] = src[e];
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// One wave per row: P = softmax(S) over the L valid columns (max-subtracted,
+// fp32), written as bf16 with zeros in columns L..Lpad-1.
+__global__ __launch_bounds__(256) void softmax_rows_kernel(const float* __restrict__ S, int rows, int L, int Lpad,
+                                                           bf16_t* __restrict__ P) {
+  const int lane = threadIdx.x & 63;
+  const long long row = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  if (row >= rows) return;
+  const float* s = S + row * Lpad;
+  float mx = -INFINITY;
+  for (int j = lane; j < L; j += 64) mx = fmaxf(mx, s[j]);
+  mx = wave_max(mx);
+  float sum = 0.0f;
+  for (int j = lane; j < L; j += 64) sum += __expf(s[j] - mx);
+  sum = wave_sum(sum);
+  const float inv = 1.0f / sum;
+  bf16_t* p = P + row * Lpad;
+  for (int j = lane; j < Lpad; j += 64) p[j] = j < L ? (bf16_t)f2bf(__expf(s[j] - mx) * inv) : (bf16_t)0;
+}
+
+// V^T per frame: vt[f][c][l] = qkv[f][l][2C + c], zero for l >= L.
+__global__ __launch_bounds__(256) void transpose_v_kernel(const bf16_t* __restrict__ qkv, int L, int C, int Lpad,
+                                                          bf16_t* __restrict__ vt) {
+  __shared__ bf16_t tile[64][65];
+  const int f = blockIdx.z;
+  const int l0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const bf16_t* src = qkv + (long long)f * L * 3 * C + 2 * C;
+  bf16_t* dst = vt + (long long)f * C * Lpad;
+  for (int k = threadIdx.x; k < 64 * 64; k += 256) {
+    const int r = k / 64, cc = k % 64;  // r: token, cc: channel
+    const int l = l0 + r, c = c0 + cc;
+    tile[r][cc] = (l < L && c < C) ? src[(long long)l * 3 * C + c] : (bf16_t)0;
+  }
+  __syncthreads();
+  for (int k = threadIdx.x; k < 64 * 64; k += 256) {
+    const int r = k / 64, ll = k % 64;  // r: channel, ll: token
+    const int c = c0 + r, l = l0 + ll;
+    if (c < C && l < Lpad) dst[(long long)c * Lpad + l] = tile[ll][r];
+  }
+}
+
+// out[tap][o][i] = w[o][i][tap] (i < cin), 0 for cin <= i < cin_pad.
+__global__ void prep_permute_kernel(const bf16_t* __restrict__ w, int cout, int cin, int taps, int cin_pad,
+                                    bf16_t* __restrict__ out) {
+  const long long n = (long long)taps * cout * cin_pad;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+       e += (long long)gridDim.x * blockDim.x) {
+    const int i = (int)(e % cin_pad);
+    const long long t2 = e / cin_pad;
+    const int o = (int)(t2 % cout);
+    const int tap = (int)(t2 / cout);
+    out[e] = i < cin ? w[((long long)o * cin + i) * taps + tap] : (bf16_t)0;
+  }
+}
+
+// Phase form of nearest-2x upsampling followed by a 3x3 conv (pad 1): output
+// pixel (2i+py, 2j+px) is a 2x2 conv of the low-resolution input at rows
+// i+py-1+a, cols j+px-1+b (a, b in {0,1}) whose weights are sums of the 3x3
+// weights: rows {0} / {1,2} for py = 0 and {0,1} / {2} for py = 1 (same for
+// columns).  Sums in fp32, rounded once to bf16.  out[ph][tap][o][i].
+__global__ void prep_phase_kernel(const bf16_t* __restrict__ w, int C, bf16_t* __restrict__ out) {
+  const long long n = 16LL * C * C;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+       e += (long long)gridDim.x * blockDim.x) {
+    const int i = (int)(e % C);
+    const long long t2 = e / C;
+    const int o = (int)(t2 % C);
+    const int tap = (int)((t2 / C) % 4);
+    const int ph = (int)(t2 / (4LL * C));
+    const int py = ph >> 1, px = ph & 1, ta = tap >> 1, tb = tap & 1;
+    const int ky0 = (py == 0) ? (ta == 0 ? 0 : 1) : (ta == 0 ? 0 : 2);
+    const int ky1 = (py == 0) ? (ta == 0 ? 0 : 2) : (ta == 0 ? 1 : 2);
+    const int kx0 = (px == 0) ? (tb == 0 ? 0 : 1) : (tb == 0 ? 0 : 2);
+    const int kx1 = (px == 0) ? (tb == 0 ? 0 : 2) : (tb == 0 ? 1 : 2);
+    float s = 0.0f;
+    const bf16_t* wp = w + ((long long)o * C + i) * 9;
+    for (int ky = ky0; ky <= ky1; ++ky)
+      for (int kx = kx0; kx <= kx1; ++kx) s += bf2f(wp[ky * 3 + kx]);
+    out[e] = (bf16_t)f2bf(s);
+  }
+}
+
+__global__ void prep_vec_kernel(const bf16_t* __restrict__ v, int n, float scale, float* __restrict__ out) {
+  for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < n; e += gridDim.x * blockDim.x)
+    out[e] = bf2f(v[e]) * scale;
+}
+
+__global__ void prep_vec_add_kernel(const bf16_t* __restrict__ a, const bf16_t* __restrict__ b, int n,
+                                    float* __restrict__ out) {
+  for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < n; e += gridDim.x * blockDim.x)
+    out[e] = bf2f(a[e]) + bf2f(b[e]);
+}
+
+unsigned grid_for(long long n, int per_block = 256, long long cap = 65536) {
+  long long g = (n + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  if (g > cap) g = cap;
+  return (unsigned)g;
+}
+
+}  // namespace
+
+hipError_t launch_rms_stats(const bf16_t* x, long long x_fstride, int lda, const bf16_t* ring, int n_hist,
+                            int C, int F, int HW, float* rs, hipStream_t s) {
+  if (g_dry_run) return hipSuccess;
+  int G = 1;
+  while (G < 64 && G * 2 <= C / 8) G *= 2;
+  const long long nvox = (long long)(F + n_hist) * HW;
+  const long long waves = (nvox + (64 / G) - 1) / (64 / G);
+  hipLaunchKernelGGL(rms_stats_kernel, dim3(grid_for(waves * 64, 256, 16384)), dim3(256), 0, s, x, x_fstride, lda,
+                     ring, n_hist, C, F, HW, G, rs);
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_update(bf16_t* ring, const bf16_t* x, long long x_fstride, int lda, int C, int F, int HW,
+                              hipStream_t s) {
+  if (g_dry_run) return hipSuccess;
+  const long long n = (long long)HW * (C / 8);
+  hipLaunchKernelGGL(ring_update_kernel, dim3(grid_for(n, 256, 16384)), dim3(256), 0, s, ring, x, x_fstride, lda, C,
+                     F, HW);
+  return hipGetLastError();
+}
+
+hipError_t launch_latent_to_cl(const bf16_t* z, int T, int t0, int F, int HW, bf16_t* zt, hipStream_t s) {
+  if (g_dry_run) return hipSuccess;
+  hipLaunchKernelGGL(latent_to_cl_kernel, dim3(grid_for((long long)F * HW)), dim3(256), 0, s, z, T, t0, F, HW, zt);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy16(void* dst, const void* src, size_t bytes, hipStream_t s) {
+  if (g_dry_run) return hipSuccess;
+  const long long n = (long long)(bytes / 16);
+  hipLaunchKernelGGL(copy16_kernel, dim3(grid_for(n, 256, 16384)), dim3(256), 0, s, static_cast<uint4*>(dst),
+                     static_cast<const uint4*>(src), n);
+  return hipGetLastError();
+}
+
+hipError_t launch_softmax_rows(const float* S, int rows, int L, int Lpad, bf16_t* P, hipStream_t s) {
+  if (g_dry_run) return hipSuccess;
+  hipLaunchKernelGGL(softmax_rows_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, S, rows, L, Lpad, P);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_v(const bf16_t* qkv, int F, int L, int C, int Lpad, bf16_t* vt, hipStream_t s) {
+  if (g_dry_run) return hipSuccess;
+  dim3 grid((unsigned)((Lpad + 63) / 64), (unsigned)((C + 63) / 64), (unsigned)F);
+  hipLaunchKernelGGL(transpose_v_kernel, grid, dim3(256), 0, s, qkv, L, C, Lpad, vt);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep_permute(const bf16_t* w, int cout, int cin, int taps, int cin_pad, bf16_t* out,
+                               hipStream_t s) {
+  if (g_dry_run) return hipSuccess;
+  hipLaunchKernelGGL(prep_permute_kernel, dim3(grid_for((long long)taps * cout * cin_pad)), dim3(256), 0, s, w, cout,
+                     cin, taps, cin_pad, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep_phase(const bf16_t* w, int C, bf16_t* out, hipStream_t s) {
+  if (g_dry_run) return hipSuccess;
+  hipLaunchKernelGGL(prep_phase_kernel, dim3(grid_for(16LL * C * C)), dim3(256), 0, s, w, C, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep_vec(const bf16_t* v, int n, float scale, float* out, hipStream_t s) {
+  if (g_dry_run) return hipSuccess;
+  hipLaunchKernelGGL(prep_vec_kernel, dim3(grid_for(n)), dim3(256), 0, s, v, n, scale, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep_vec_add(const bf16_t* a, const bf16_t* b, int n, float* out, hipStream_t s) {
+  if (g_dry_run) return hipSuccess;
+  hipLaunchKernelGGL(prep_vec_add_kernel, dim3(grid_for(n)), dim3(256), 0, s, a, b, n, out);
+  return hipGetLastError();
+}
+
+}  // namespace wvd

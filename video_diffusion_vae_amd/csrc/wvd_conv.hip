@@ -1,0 +1,408 @@
+// Implicit-GEMM causal convolution on bf16 MFMA (gfx950), with the channel
+// RMSNorm (+ SiLU) applied while the input tile is staged into LDS and the
+// bias / residual / frame-interleave / phase-scatter / pixel-shuffle work
+// done in the epilogue.
+//
+// GEMM view: M = output voxels (tile TF x TH x 16), N = output channels
+// (tile BN), K = taps x input channels.  The K loop runs segment by segment
+// (the main conv, then optionally a 1x1x1 shortcut over the raw block input),
+// input-channel chunk by chunk (BK channels), tap by tap.  For each chunk the
+// input halo of the tile -- (TF+KT-1) x (TH+2) x 18 voxels for a 3x3x3 conv --
+// sits in LDS once and every tap reads a shifted window of it, so the input
+// is fetched once per chunk instead of once per tap.  The next chunk's halo
+// and the next tap's weights are double-buffered in LDS.  The accumulation
+// order (segment, chunk, tap, k16 step) does not depend on where the tile
+// lies, which keeps every output bit-identical for any frames_per_pass.
+//
+// The conv definition (cross-correlation, causal in time with two history
+// frames, zero spatial padding) follows the decoder the Wan2.2 VAE decoder
+// page describes; normalisation is channel RMSNorm with affine scale and SiLU
+// as the TensorRT-LLM norm-SiLU issue describes for the decoder's residual
+// norms and norm_out, statistics in fp32 (Wan2.2 page, "Limits").
+#include "wvd_internal.h"
+
+namespace wvd {
+
+namespace {
+
+template <int NP>
+__device__ __forceinline__ int swz(int row) {
+  // XOR swizzle of the 16-byte parts of a row so that 8 consecutive rows
+  // reading the same part hit 8 different 16-byte bank groups.
+  if constexpr (NP == 4) return (row >> 1) & 3;
+  else return (row >> 2) & 1;
+}
+
+template <int BK, int BN, int WAVES_N>
+__global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
+  constexpr int NP = BK / 8;            // 16-byte parts per voxel row
+  constexpr int ROWB = BK * 2;          // bytes per LDS row
+  constexpr int WAVES_M = 4 / WAVES_N;
+  constexpr int WM = kTileM / WAVES_M;
+  constexpr int WN = BN / WAVES_N;
+  constexpr int MI = WM / 32;
+  constexpr int NJ = WN / 32;
+  constexpr int W_ITEMS = (BN * NP + 255) / 256;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wave_m = wave / WAVES_N;
+  const int wave_n = wave % WAVES_N;
+
+  // ---- LDS carve-up ----
+  const int halo_bytes = a.nhv_max * ROWB;
+  unsigned char* halo_s[2] = {smem, smem + halo_bytes};
+  unsigned char* wbuf_s[2] = {smem + 2 * halo_bytes, smem + 2 * halo_bytes + BN * ROWB};
+  const bf16_t** vptr_s = reinterpret_cast<const bf16_t**>(smem + 2 * halo_bytes + 2 * BN * ROWB);
+  float* rs_s = reinterpret_cast<float*>(vptr_s + a.nhv_max);
+  float* gamma_s = rs_s + a.nhv_max;
+
+  // ---- tile coordinates; consecutive logical tiles share an XCD ----
+  const int nM = a.tiles_x * a.tiles_y * a.tiles_f;
+  const int nN = (a.Cout + BN - 1) / BN;
+  const int total = nM * nN * a.nphase;
+  int logical;
+  {
+    const int id = blockIdx.x;
+    const int q = total >> 3, r = total & 7, xcd = id & 7, slot = id >> 3;
+    logical = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + slot;
+  }
+  const int nt = logical % nN;
+  const int ph = (logical / nN) % a.nphase;
+  const int mt = logical / (nN * a.nphase);
+  const int py = ph >> 1, px = ph & 1;
+  const int txi = mt % a.tiles_x;
+  const int tyi = (mt / a.tiles_x) % a.tiles_y;
+  const int tfi = mt / (a.tiles_x * a.tiles_y);
+  const int f0 = tfi * a.TF, y0 = tyi * a.TH, x0 = txi * kTileW;
+  const int n0 = nt * BN;
+  const int HW = a.H * a.W;
+
+  f32x16_t acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  const int kpart = lane >> 5;  // which 8-wide K group of a k16 step this lane feeds
+  const int lrow = lane & 31;
+
+  for (int s = 0; s < a.nseg; ++s) {
+    const ConvSeg& S = a.seg[s];
+    const int KT = S.KT;
+    const int hs = S.KS == 1 ? 0 : 1;
+    const int K2 = S.KS == 3 ? 3 : (S.KS == 2 ? 2 : 1);
+    const int HX = kTileW + 2 * hs;
+    const int HY = a.TH + 2 * hs;
+    const int HF = a.TF + KT - 1;
+    const int nhv = HF * HY * HX;
+    const int ntaps = KT * K2 * K2;
+    const int nchunks = S.Cin / BK;
+    const int nitems = nhv * NP;
+    const int ipt = (nitems + 255) >> 8;
+    const int per_tap = (ipt + ntaps - 1) / ntaps;
+    const bool norm = S.prologue != PRO_RAW;
+    const bool act = S.prologue == PRO_NORM_SILU;
+    const bf16_t* wseg = S.w + (long long)ph * ntaps * S.w_tap_stride + (long long)f0 * S.w_frame_stride;
+
+    __syncthreads();  // previous segment finished with the LDS tables
+    // Per-halo-voxel source pointer (null = zero padding) and norm scale.
+    for (int v = tid; v < nhv; v += 256) {
+      const int hx = v % HX;
+      const int t2 = v / HX;
+      const int hy = t2 % HY;
+      const int hf = t2 / HY;
+      const int fo = f0 + hf - (KT - 1);
+      const int y = y0 + hy - hs;
+      const int x = x0 + hx - hs;
+      const bf16_t* p = nullptr;
+      float rsv = 0.0f;
+      if (y >= 0 && y < a.H && x >= 0 && x < a.W && fo < a.F) {
+        const long long pix = (long long)y * a.W + x;
+        if (fo >= 0) {
+          p = S.x + fo * S.x_fstride + pix * S.lda;
+        } else if (fo + 2 >= 2 - S.n_hist) {
+          p = S.ring + (long long)(fo + 2) * HW * S.Cin + pix * S.Cin;
+        }
+        if (p && norm) rsv = S.rs[(long long)(fo + 2) * HW + pix];
+      }
+      vptr_s[v] = p;
+      rs_s[v] = rsv;
+    }
+    if (norm)
+      for (int c = tid; c < S.Cin; c += 256) gamma_s[c] = S.gamma[c];
+    __syncthreads();
+
+    // Halo voxel of each A row this lane feeds (tap (0,0,0) in halo coords).
+    int abase[MI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int m = wave_m * WM + 32 * i + lrow;
+      const int tx = m & (kTileW - 1);
+      const int t2 = m / kTileW;
+      const int ty = t2 % a.TH;
+      const int tf = t2 / a.TH;
+      abase[i] = (tf * HY + ty) * HX + tx;
+    }
+
+    auto load_item = [&](int idx, int chunk) -> uint4 {
+      uint4 r = make_uint4(0, 0, 0, 0);
+      if (idx < nitems) {
+        const bf16_t* p = vptr_s[idx / NP];
+        if (p) r = *reinterpret_cast<const uint4*>(p + chunk * BK + (idx % NP) * 8);
+      }
+      return r;
+    };
+    auto store_item = [&](int idx, int chunk, uint4 r, unsigned char* hbuf) {
+      if (idx >= nitems) return;
+      const int v = idx / NP;
+      const int p = idx % NP;
+      if (norm) {
+        float f[8];
+        unpack8(r, f);
+        const float sc = rs_s[v];
+        const float* g = gamma_s + chunk * BK + p * 8;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          float t = f[k] * sc * g[k];
+          f[k] = act ? silu(t) : t;
+        }
+        r = pack8(f);
+      }
+      *reinterpret_cast<uint4*>(hbuf + v * ROWB + 16 * (p ^ swz<NP>(v))) = r;
+    };
+    auto load_w = [&](int chunk, int tap, uint4* wr) {
+      const bf16_t* base = wseg + (long long)tap * S.w_tap_stride + chunk * BK;
+#pragma unroll
+      for (int k = 0; k < W_ITEMS; ++k) {
+        const int idx = tid + 256 * k;
+        uint4 r = make_uint4(0, 0, 0, 0);
+        if (idx < BN * NP) {
+          const int n = idx / NP;
+          if (n0 + n < a.Cout)
+            r = *reinterpret_cast<const uint4*>(base + (long long)(n0 + n) * S.ldw + (idx % NP) * 8);
+        }
+        wr[k] = r;
+      }
+    };
+    auto store_w = [&](const uint4* wr, unsigned char* wb) {
+#pragma unroll
+      for (int k = 0; k < W_ITEMS; ++k) {
+        const int idx = tid + 256 * k;
+        if (idx < BN * NP) {
+          const int n = idx / NP;
+          const int p = idx % NP;
+          *reinterpret_cast<uint4*>(wb + n * ROWB + 16 * (p ^ swz<NP>(n))) = wr[k];
+        }
+      }
+    };
+
+    // Chunk 0 halo and the first weight tile, synchronously.
+    for (int idx = tid; idx < nitems; idx += 256) store_item(idx, 0, load_item(idx, 0), halo_s[0]);
+    {
+      uint4 wr[W_ITEMS];
+      load_w(0, 0, wr);
+      store_w(wr, wbuf_s[0]);
+    }
+    __syncthreads();
+
+    int hb = 0, wb = 0;
+    for (int c = 0; c < nchunks; ++c) {
+      const bool hnext = c + 1 < nchunks;
+      for (int t = 0; t < ntaps; ++t) {
+        int cn = c, tn = t + 1;
+        if (tn == ntaps) { tn = 0; cn = c + 1; }
+        const bool wnext = cn < nchunks;
+        uint4 wr[W_ITEMS];
+        if (wnext) load_w(cn, tn, wr);
+        uint4 hr[kMaxHaloItemsPerTap];
+        const int j0 = t * per_tap;
+        if (hnext) {
+#pragma unroll
+          for (int k = 0; k < kMaxHaloItemsPerTap; ++k)
+            if (k < per_tap) hr[k] = load_item(tid + 256 * (j0 + k), c + 1);
+        }
+        // Tap offset inside the halo.
+        const int dt = t / (K2 * K2);
+        const int a2 = (t / K2) % K2;
+        const int b2 = t % K2;
+        const int dy = S.KS == 2 ? py + a2 : a2;
+        const int dx = S.KS == 2 ? px + b2 : b2;
+        const int toff = (dt * HY + dy) * HX + dx;
+        const unsigned char* hsrc = halo_s[hb];
+        const unsigned char* wsrc = wbuf_s[wb];
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+          const int part = kk * 2 + kpart;
+          bf16x8_t av[MI], bv[NJ];
+#pragma unroll
+          for (int i = 0; i < MI; ++i) {
+            const int v = abase[i] + toff;
+            av[i] = *reinterpret_cast<const bf16x8_t*>(hsrc + v * ROWB + 16 * (part ^ swz<NP>(v)));
+          }
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            const int n = wave_n * WN + 32 * j + lrow;
+            bv[j] = *reinterpret_cast<const bf16x8_t*>(wsrc + n * ROWB + 16 * (part ^ swz<NP>(n)));
+          }
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+        }
+        if (hnext) {
+#pragma unroll
+          for (int k = 0; k < kMaxHaloItemsPerTap; ++k)
+            if (k < per_tap) store_item(tid + 256 * (j0 + k), c + 1, hr[k], halo_s[hb ^ 1]);
+        }
+        if (wnext) store_w(wr, wbuf_s[wb ^ 1]);
+        __syncthreads();
+        wb ^= 1;
+      }
+      hb ^= 1;
+    }
+  }
+
+  // ---- epilogue ----
+  const int Chalf = a.Cout >> 1;
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+#pragma unroll
+      for (int e1 = 0; e1 < 4; ++e1) {
+        const int e = e4 * 4 + e1;
+        const int m = wave_m * WM + 32 * i + 8 * e4 + 4 * kpart + e1;
+        const int tx = m & (kTileW - 1);
+        const int t2 = m / kTileW;
+        const int ty = t2 % a.TH;
+        const int tf = t2 / a.TH;
+        const int f = f0 + tf, y = y0 + ty, x = x0 + tx;
+        if (f >= a.F || y >= a.H || x >= a.W) continue;
+        const long long pix = (long long)y * a.W + x;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int n = n0 + wave_n * WN + 32 * j + lrow;
+          if (n >= a.Cout) continue;
+          float v = acc[i][j][e] * a.scale;
+          if (a.bias) v += a.bias[n];
+          switch (a.epi) {
+            case EPI_BF16: {
+              if (a.res) v += bf2f(a.res[f * a.res_fstride + pix * a.ldr + n]);
+              static_cast<bf16_t*>(a.out)[f * a.out_fstride + pix * a.ldo + n] = (bf16_t)f2bf(v);
+              break;
+            }
+            case EPI_F32:
+              static_cast<float*>(a.out)[f * a.out_fstride + pix * a.ldo + n] = v;
+              break;
+            case EPI_TIME: {
+              const int half = n >= Chalf ? 1 : 0;
+              const int ch = n - half * Chalf;
+              const long long fr = a.out_base + 2 * f + half;
+              static_cast<bf16_t*>(a.out)[fr * a.out_fstride + pix * a.ldo + ch] = (bf16_t)f2bf(v);
+              break;
+            }
+            case EPI_PHASE: {
+              const long long op = (long long)(2 * y + py) * (2 * a.W) + (2 * x + px);
+              static_cast<bf16_t*>(a.out)[f * a.out_fstride + op * a.ldo + n] = (bf16_t)f2bf(v);
+              break;
+            }
+            default: {  // EPI_VIDEO
+              const int k = n >> 2, ddy = (n >> 1) & 1, ddx = n & 1;
+              v = fminf(fmaxf(v, -1.0f), 1.0f);
+              const long long row = ((long long)k * a.video_T + a.out_base + f) * (2 * a.H) + 2 * y + ddy;
+              static_cast<bf16_t*>(a.out)[row * (2 * a.W) + 2 * x + ddx] = (bf16_t)f2bf(v);
+              break;
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int BK, int BN, int WAVES_N>
+hipError_t launch_impl(const ConvArgs& a, hipStream_t stream) {
+  if (g_dry_run) return hipSuccess;
+  const size_t lds = conv_lds_bytes(a);
+  auto kern = conv_igemm<BK, BN, WAVES_N>;
+  static size_t attr_bytes = 0;
+  if (lds > attr_bytes) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_bytes = lds;
+  }
+  const int nM = a.tiles_x * a.tiles_y * a.tiles_f;
+  const int nN = (a.Cout + BN - 1) / BN;
+  const long long total = (long long)nM * nN * a.nphase;
+  if (total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3((unsigned)total), dim3(256), lds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t conv_lds_bytes(const ConvArgs& a) {
+  int bk = 32;
+  for (int s = 0; s < a.nseg; ++s)
+    if (a.seg[s].Cin % 32) bk = 16;
+  const int bn = a.Cout <= 32 ? 32 : 128;
+  int cin_max = 0;
+  for (int s = 0; s < a.nseg; ++s)
+    if (a.seg[s].prologue != PRO_RAW && a.seg[s].Cin > cin_max) cin_max = a.seg[s].Cin;
+  return (size_t)2 * a.nhv_max * bk * 2 + (size_t)2 * bn * bk * 2 + (size_t)a.nhv_max * (8 + 4) +
+         (size_t)cin_max * 4;
+}
+
+const char* conv_check(const ConvArgs& a) {
+  if (a.TF < 1 || a.TF * a.TH * kTileW != kTileM) return "tile TF*TH*16 != 256";
+  if (a.nseg < 1 || a.nseg > 2) return "segment count";
+  if (a.F < 1 || a.H < 1 || a.W < 1 || a.Cout < 1) return "empty output grid";
+  if (a.nphase != 1 && a.nphase != 4) return "phase count";
+  if (conv_lds_bytes(a) > 160 * 1024) return "LDS over 160 KiB";
+  // One BK for all segments: 16 when any segment's Cin is not a multiple of 32.
+  int bk = 32;
+  for (int s = 0; s < a.nseg; ++s)
+    if (a.seg[s].Cin % 32) bk = 16;
+  for (int s = 0; s < a.nseg; ++s) {
+    const ConvSeg& g = a.seg[s];
+    const int hs = g.KS == 1 ? 0 : 1;
+    const int k2 = g.KS == 3 ? 3 : (g.KS == 2 ? 2 : 1);
+    const int nhv = (a.TF + g.KT - 1) * (a.TH + 2 * hs) * (kTileW + 2 * hs);
+    const int ipt = (nhv * (bk / 8) + 255) / 256;
+    const int ntaps = g.KT * k2 * k2;
+    if (!g.x || !g.w) return "null operand";
+    if (g.KT != 1 && g.KT != 3) return "KT must be 1 or 3";
+    if (g.KS != 1 && g.KS != 2 && g.KS != 3) return "KS must be 1, 2 or 3";
+    if ((g.KS == 2) != (a.nphase == 4)) return "phase taps need 4 phases";
+    if (nhv > a.nhv_max) return "halo larger than nhv_max";
+    if ((ipt + ntaps - 1) / ntaps > kMaxHaloItemsPerTap) return "halo items per tap over the register budget";
+    if (g.Cin < 16 || g.Cin % 16) return "Cin must be a positive multiple of 16";
+    if (g.lda % 8 || g.ldw % 8 || g.lda < g.Cin) return "row strides must be multiples of 8 and >= Cin";
+    if (g.prologue != PRO_RAW && (g.Cin > kMaxCin || !g.rs || !g.gamma)) return "norm prologue operands";
+    if (g.n_hist < 0 || g.n_hist > 2 || (g.n_hist > 0 && (!g.ring || g.KT != 3))) return "history ring";
+    if (g.w_frame_stride && a.TF != 1) return "per-frame weights need TF == 1";
+  }
+  if (!a.out) return "null output";
+  return nullptr;
+}
+
+hipError_t launch_conv(const ConvArgs& a, hipStream_t stream) {
+  if (conv_check(a)) return hipErrorInvalidValue;
+  bool bk16 = false;
+  for (int s = 0; s < a.nseg; ++s)
+    if (a.seg[s].Cin % 32) bk16 = true;
+  const bool small_n = a.Cout <= 32;
+  if (!bk16 && !small_n) return launch_impl<32, 128, 2>(a, stream);
+  if (!bk16 && small_n) return launch_impl<32, 32, 1>(a, stream);
+  if (bk16 && !small_n) return launch_impl<16, 128, 2>(a, stream);
+  return launch_impl<16, 32, 1>(a, stream);
+}
+
+}  // namespace wvd

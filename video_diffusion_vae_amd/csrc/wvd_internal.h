@@ -1,0 +1,95 @@
+// Internal interfaces between the wvd host scheduler and its HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "wvd_common.h"
+
+namespace wvd {
+
+// Output tile: TF frames x TH rows x kTileW columns of output voxels (the M
+// dimension of the implicit GEMM); TF * TH * kTileW == kTileM.
+constexpr int kTileW = 16;
+constexpr int kTileM = 256;
+constexpr int kMaxHaloItemsPerTap = 4;  // 16-byte halo items per thread per tap
+constexpr int kMaxCin = 1024;           // largest norm input width kept in LDS
+
+enum Prologue { PRO_RAW = 0, PRO_NORM = 1, PRO_NORM_SILU = 2 };
+enum Epilogue {
+  EPI_BF16 = 0,    // channels-last bf16 (+ bias, + optional residual)
+  EPI_F32 = 1,     // fp32 (scaled), e.g. attention logits
+  EPI_TIME = 2,    // time_conv: channels [0,C) -> frame 2s+base, [C,2C) -> 2s+1+base
+  EPI_PHASE = 3,   // up-conv phase (py,px): voxel (y,x) -> (2y+py, 2x+px)
+  EPI_VIDEO = 4    // head: 2x2 pixel shuffle of 12 channels, clamp, NCTHW video
+};
+
+// One K segment of the implicit GEMM: a (possibly normalised) input tensor,
+// its temporal history and the weights that contract it.
+struct ConvSeg {
+  const bf16_t* x;          // input frame 0 of this pass, voxel stride lda
+  const bf16_t* ring;       // [2][H][W][Cin] previous input frames (raw) or null
+  const float* rs;          // [2+F][H][W] per-voxel 1/||x|| (slot 2+f = frame f)
+  const float* gamma;       // [Cin] gamma * sqrt(Cin) (norm prologues)
+  const bf16_t* w;          // [taps][rows][ldw] bf16, K contiguous
+  long long x_fstride;      // elements per input frame
+  long long w_tap_stride;   // elements per tap
+  long long w_frame_stride; // per-frame weight offset (attention GEMMs), else 0
+  int lda, ldw, Cin;
+  int KT;                   // temporal taps: 1 or 3 (causal, history frames first)
+  int KS;                   // spatial taps: 1 (1x1), 3 (3x3, pad 1), 2 (2x2 phase)
+  int n_hist;               // valid history frames in ring (0..2)
+  int prologue;             // Prologue
+};
+
+struct ConvArgs {
+  ConvSeg seg[2];
+  int nseg;
+  int F, H, W;              // output voxel grid (input grid for phase mode)
+  int TF, TH;               // tile frames / rows
+  int tiles_x, tiles_y, tiles_f;
+  int nphase;               // 4 for EPI_PHASE, else 1
+  int Cout;
+  const float* bias;        // [Cout] fp32 or null
+  float scale;
+  const bf16_t* res;        // residual on the output grid, or null
+  long long res_fstride;
+  int ldr;
+  void* out;
+  long long out_fstride;
+  int ldo;
+  int epi;
+  int out_base;             // EPI_TIME frame base; EPI_VIDEO first frame index
+  int video_T;              // EPI_VIDEO total frames of the video
+  int nhv_max;              // largest halo (voxels) over segments: LDS sizing
+};
+
+// Host-validation mode: every launcher checks its arguments and returns
+// without enqueuing GPU work (lets the whole schedule run without a GPU).
+extern bool g_dry_run;
+
+// nullptr when the launch of `a` satisfies what the kernel assumes, else the
+// violated condition.
+const char* conv_check(const ConvArgs& a);
+// Launches one implicit-GEMM convolution; returns hipSuccess or the error.
+hipError_t launch_conv(const ConvArgs& a, hipStream_t stream);
+// LDS bytes the launch of `a` needs (host-side check).
+size_t conv_lds_bytes(const ConvArgs& a);
+
+// Auxiliary kernels (wvd_aux.hip).
+hipError_t launch_rms_stats(const bf16_t* x, long long x_fstride, int lda, const bf16_t* ring,
+                            int n_hist, int C, int F, int HW, float* rs, hipStream_t s);
+hipError_t launch_ring_update(bf16_t* ring, const bf16_t* x, long long x_fstride, int lda, int C,
+                              int F, int HW, hipStream_t s);
+hipError_t launch_latent_to_cl(const bf16_t* z, int T, int t0, int F, int HW, bf16_t* zt, hipStream_t s);
+hipError_t launch_copy16(void* dst, const void* src, size_t bytes, hipStream_t s);
+hipError_t launch_softmax_rows(const float* S, int rows, int L, int Lpad, bf16_t* P, hipStream_t s);
+hipError_t launch_transpose_v(const bf16_t* qkv, int F, int L, int C, int Lpad, bf16_t* vt, hipStream_t s);
+// Prepare-time kernels.
+hipError_t launch_prep_permute(const bf16_t* w, int cout, int cin, int taps, int cin_pad, bf16_t* out,
+                               hipStream_t s);
+hipError_t launch_prep_phase(const bf16_t* w, int C, bf16_t* out, hipStream_t s);
+hipError_t launch_prep_vec(const bf16_t* v, int n, float scale, float* out, hipStream_t s);
+// out[i] = a[i] + b[i] in fp32 (the two biases of a block with a shortcut).
+hipError_t launch_prep_vec_add(const bf16_t* a, const bf16_t* b, int n, float* out, hipStream_t s);
+
+}  // namespace wvd

@@ -1,0 +1,203 @@
+"""ctypes binding of libwvd.so (the C ABI in include/wvd.h).
+
+Argument marshalling only: every step of the decoder runs in the HIP library.
+PyTorch provides device memory and the current stream.  Importing this module
+loads the library and raises if it has not been built
+(python -m video_diffusion_vae_amd.csrc.build).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, List, Optional, Sequence, Union
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwvd.so")
+
+WVD_OK = 0
+WVD_EINVAL = -1
+WVD_ESHAPE = -2
+WVD_ENOSPACE = -3
+WVD_EUNSUPPORTED = -4
+WVD_EHIP = -5
+NUM_WEIGHTS = 84
+PROFILE_CLASSES = ("conv3x3x3", "conv_other", "attention_gemm", "norm_stats", "copies")
+
+
+class WvdError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        detail = ""
+        if status == WVD_EHIP:
+            detail = " " + _lib.wvd_last_error().decode()
+        super().__init__(f"{where}: {status} ({status_string(status)}){detail}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run: python -m video_diffusion_vae_amd.csrc.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    sz = ctypes.c_size_t
+    vp = ctypes.c_void_p
+    i = ctypes.c_int
+    lib.wvd_prepared_bytes.argtypes = [i, i, i, ctypes.POINTER(sz)]
+    lib.wvd_prepared_bytes.restype = i
+    lib.wvd_prepare.argtypes = [i, i, i, ctypes.POINTER(vp), i, vp, sz, vp, ctypes.POINTER(vp)]
+    lib.wvd_prepare.restype = i
+    lib.wvd_workspace_bytes.argtypes = [vp, i, i, ctypes.POINTER(sz)]
+    lib.wvd_workspace_bytes.restype = i
+    lib.wvd_decode.argtypes = [vp, vp, i, i, vp, vp, sz, vp]
+    lib.wvd_decode.restype = i
+    lib.wvd_destroy.argtypes = [vp]
+    lib.wvd_destroy.restype = None
+    lib.wvd_status_string.argtypes = [i]
+    lib.wvd_status_string.restype = ctypes.c_char_p
+    lib.wvd_last_error.argtypes = []
+    lib.wvd_last_error.restype = ctypes.c_char_p
+    lib.wvd_set_dry_run.argtypes = [i]
+    lib.wvd_set_dry_run.restype = None
+    lib.wvd_last_launch_count.argtypes = [vp]
+    lib.wvd_last_launch_count.restype = ctypes.c_longlong
+    lib.wvd_profile_enable.argtypes = [vp, i]
+    lib.wvd_profile_enable.restype = i
+    lib.wvd_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), i]
+    lib.wvd_profile_read.restype = i
+    return lib
+
+
+_lib = _load()
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return _lib.wvd_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != WVD_OK:
+        raise WvdError(status, where)
+
+
+# ---- raw entry points (same names as the C ABI) ----
+
+def wvd_prepared_bytes(c: int, h: int, w: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.wvd_prepared_bytes(c, h, w, ctypes.byref(n)), "wvd_prepared_bytes")
+    return n.value
+
+
+def wvd_prepare(c: int, h: int, w: int, weight_ptrs: Sequence[int], prepared_ptr: int, prepared_bytes: int,
+                stream_ptr: int) -> int:
+    arr = (ctypes.c_void_p * len(weight_ptrs))(*weight_ptrs)
+    plan = ctypes.c_void_p(0)
+    _check(_lib.wvd_prepare(c, h, w, arr, len(weight_ptrs), prepared_ptr, prepared_bytes, stream_ptr,
+                            ctypes.byref(plan)), "wvd_prepare")
+    return plan.value
+
+
+def wvd_workspace_bytes(plan: int, T: int, frames_per_pass: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.wvd_workspace_bytes(plan, T, frames_per_pass, ctypes.byref(n)), "wvd_workspace_bytes")
+    return n.value
+
+
+def wvd_decode(plan: int, z_ptr: int, T: int, frames_per_pass: int, out_ptr: int, ws_ptr: int, ws_bytes: int,
+               stream_ptr: int) -> None:
+    _check(_lib.wvd_decode(plan, z_ptr, T, frames_per_pass, out_ptr, ws_ptr, ws_bytes, stream_ptr), "wvd_decode")
+
+
+def wvd_destroy(plan: int) -> None:
+    _lib.wvd_destroy(plan)
+
+
+def wvd_set_dry_run(on: bool) -> None:
+    _lib.wvd_set_dry_run(1 if on else 0)
+
+
+def wvd_last_launch_count(plan: int) -> int:
+    return int(_lib.wvd_last_launch_count(plan))
+
+
+def wvd_profile_enable(plan: int, on: bool) -> None:
+    _check(_lib.wvd_profile_enable(plan, 1 if on else 0), "wvd_profile_enable")
+
+
+def wvd_profile_read(plan: int) -> Dict[str, Dict[str, float]]:
+    n = len(PROFILE_CLASSES)
+    ms = (ctypes.c_double * n)()
+    fl = (ctypes.c_double * n)()
+    _check(_lib.wvd_profile_read(plan, ms, fl, n), "wvd_profile_read")
+    return {k: {"ms": ms[i], "flops": fl[i]} for i, k in enumerate(PROFILE_CLASSES)}
+
+
+# ---- torch-facing wrapper ----
+
+class Decoder:
+    """Prepared decoder for base width c at latent size h x w on the current
+    CUDA (HIP) device.  `weights` are the 84 tensors in canonical order (a
+    sequence, or a dict in that order), any float dtype; they are copied to
+    contiguous bf16 on the device for preparation and may be dropped after."""
+
+    def __init__(self, weights: Union[Sequence, Dict[str, object]], c: int, h: int, w: int, device=None):
+        import torch
+
+        self.torch = torch
+        self.c, self.h, self.w = int(c), int(h), int(w)
+        self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        ws = list(weights.values()) if isinstance(weights, dict) else list(weights)
+        if len(ws) != NUM_WEIGHTS:
+            raise WvdError(WVD_EINVAL, f"Decoder: expected {NUM_WEIGHTS} weights, got {len(ws)}")
+        dev_ws = []
+        for t in ws:
+            t = torch.as_tensor(t)
+            dev_ws.append(t.to(device=self.device, dtype=torch.bfloat16).contiguous())
+        nbytes = wvd_prepared_bytes(self.c, self.h, self.w)
+        self.prepared = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        stream = torch.cuda.current_stream(self.device)
+        self.plan = wvd_prepare(self.c, self.h, self.w, [t.data_ptr() for t in dev_ws], self.prepared.data_ptr(),
+                                nbytes, stream.cuda_stream)
+        stream.synchronize()  # the input copies may be freed after this
+        del dev_ws
+        self._ws = None
+
+    def workspace_bytes(self, T: int, frames_per_pass: int) -> int:
+        return wvd_workspace_bytes(self.plan, T, frames_per_pass)
+
+    def decode(self, z, frames_per_pass: int = 4, out=None, workspace=None):
+        torch = self.torch
+        if z.dim() != 5 or tuple(z.shape[:2]) != (1, 48) or tuple(z.shape[3:]) != (self.h, self.w):
+            raise WvdError(WVD_ESHAPE, f"decode: latents of shape {tuple(z.shape)}")
+        z = z.to(device=self.device, dtype=torch.bfloat16).contiguous()
+        T = int(z.shape[2])
+        shape = (1, 3, 4 * T - 3, 16 * self.h, 16 * self.w)
+        if out is None:
+            out = torch.empty(shape, dtype=torch.bfloat16, device=self.device)
+        elif tuple(out.shape) != shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
+            raise WvdError(WVD_ESHAPE, f"decode: out must be contiguous bf16 {shape}")
+        need = self.workspace_bytes(T, frames_per_pass)
+        if workspace is None:
+            if self._ws is None or self._ws.numel() < need:
+                self._ws = None
+                self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+            workspace = self._ws
+        stream = torch.cuda.current_stream(self.device)
+        wvd_decode(self.plan, z.data_ptr(), T, int(frames_per_pass), out.data_ptr(), workspace.data_ptr(),
+                   workspace.numel(), stream.cuda_stream)
+        return out
+
+    def release_workspace(self) -> None:
+        self._ws = None
+
+    def profile(self, on: bool = True) -> None:
+        wvd_profile_enable(self.plan, on)
+
+    def profile_read(self) -> Dict[str, Dict[str, float]]:
+        return wvd_profile_read(self.plan)
+
+    def __del__(self):
+        plan = getattr(self, "plan", None)
+        if plan:
+            wvd_destroy(plan)
+            self.plan = None
