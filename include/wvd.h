@@ -7,9 +7,13 @@
  * compression).  Weights are prepared once (layout and phase transforms;
  * same page, "Use": the decoder prepares the weights once and its raw entry
  * points are destination-passing on the current stream); decoding writes into
- * a caller-owned video buffer on the caller's stream.  Arithmetic: bf16
- * weights and activations, fp32 accumulation, fp32 RMS-norm statistics (same
- * page, "Limits").  frames_per_pass latent frames are carried through the
+ * a caller-owned bf16 video buffer on the caller's stream.  Arithmetic: the
+ * pages' kernel keeps bf16 weights and activations with fp32 accumulation and
+ * fp32 RMS-norm statistics (same page, "Limits"); this library keeps the same
+ * 2-byte storage and MFMA operand width but in fp16 (which gfx950 multiplies
+ * at the bf16 rate and into which every bf16 weight of normal range converts
+ * exactly), with fp32 accumulation and fp32 norm statistics; values beyond
+ * the fp16 range saturate.  frames_per_pass latent frames are carried through the
  * whole decoder per pass; it trades memory for speed and leaves the video
  * bit-identical (same page, "Performance and memory").
  *
@@ -49,13 +53,17 @@ enum wvd_status {
 /* Number of weight tensors in the canonical order (see wvd_prepare). */
 #define WVD_NUM_WEIGHTS 84
 
+/* Element type of the weights and latents handed to wvd_prepare/wvd_decode. */
+enum wvd_dtype { WVD_DTYPE_BF16 = 0, WVD_DTYPE_F32 = 1 };
+
 /* Bytes of the prepared-weights buffer for base width c at latent size h x w.
  * c: positive multiple of 16; 1 <= h, w <= 4096.  Writes *bytes. */
 int wvd_prepared_bytes(int c, int h, int w, size_t* bytes);
 
 /* One-time weight preparation (Wan2.2 VAE decoder page, "Use": layout and
  * phase transforms of the weights, done once).
- *   weights:  WVD_NUM_WEIGHTS device pointers to bf16 tensors, contiguous, in
+ *   weights:  WVD_NUM_WEIGHTS device pointers to tensors of weight_dtype
+ *             (WVD_DTYPE_BF16 or WVD_DTYPE_F32), contiguous, in
  *             the canonical order and PyTorch layouts: conv_in (weight
  *             [4c,48,3,3,3], bias); mid.res0 (norm1.gamma, conv1.weight,
  *             conv1.bias, norm2.gamma, conv2.weight, conv2.bias); mid.attn
@@ -70,7 +78,7 @@ int wvd_prepared_bytes(int c, int h, int w, size_t* bytes);
  * The input weights may be freed once the enqueued work has completed.  On
  * success *plan_out receives a host object to release with wvd_destroy. */
 int wvd_prepare(int c, int h, int w, const void* const* weights, int n_weights,
-                void* prepared, size_t prepared_bytes, void* stream,
+                int weight_dtype, void* prepared, size_t prepared_bytes, void* stream,
                 wvd_plan** plan_out);
 
 /* Workspace bytes wvd_decode needs for T latent frames at frames_per_pass.
@@ -78,14 +86,15 @@ int wvd_prepare(int c, int h, int w, const void* const* weights, int n_weights,
 int wvd_workspace_bytes(const wvd_plan* plan, int T, int frames_per_pass, size_t* bytes);
 
 /* Decode latents into video (destination-passing, on `stream`).
- *   z:   device bf16 [1, 48, T, h, w], contiguous (the plan's h, w).
+ *   z:   device [1, 48, T, h, w] of z_dtype (WVD_DTYPE_BF16 or WVD_DTYPE_F32),
+ *        contiguous (the plan's h, w).
  *   out: device bf16 [1, 3, 4T-3, 16h, 16w], contiguous; every element is
  *        written, finite and in [-1, 1].
  *   workspace: device buffer of at least wvd_workspace_bytes(plan, T, P).
  * The output is bit-identical for every frames_per_pass >= 1, and its first
  * 4k-3 frames are bit-identical to the decode of the first k latent frames.
  * Concurrent decodes with one plan need separate workspaces. */
-int wvd_decode(const wvd_plan* plan, const void* z, int T, int frames_per_pass,
+int wvd_decode(const wvd_plan* plan, const void* z, int z_dtype, int T, int frames_per_pass,
                void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Release a plan (host memory only; the prepared buffer stays the caller's).

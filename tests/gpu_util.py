@@ -66,8 +66,11 @@ def decoder_for(cfg: synth.Config, seed: int):
     from video_diffusion_vae_amd import wvd
     key = (cfg.c, cfg.h, cfg.w, seed, cfg.weights_bf16)
     if key not in _decoders:
+        import torch
         W, _ = inputs(cfg, seed, 1)
         _decoders.clear()
+        if cfg.weights_bf16:  # bf16-exact values: hand them over as bf16
+            W = {k: torch.from_numpy(v).to(torch.bfloat16) for k, v in W.items()}
         _decoders[key] = wvd.Decoder(W, cfg.c, cfg.h, cfg.w)
     return _decoders[key]
 
@@ -77,7 +80,9 @@ def decode_gpu(cfg: synth.Config, seed: int = 0, frames_per_pass: int = 1, T: Op
     T = cfg.T if T is None else T
     dec = decoder_for(cfg, seed)
     z = synth.make_latents(T, cfg.h, cfg.w, seed=seed, bf16=cfg.weights_bf16)
-    zt = torch.from_numpy(z).to("cuda").to(torch.bfloat16)
+    zt = torch.from_numpy(z).to("cuda")
+    if cfg.weights_bf16:
+        zt = zt.to(torch.bfloat16)
     out = dec.decode(zt, frames_per_pass=frames_per_pass)
     torch.cuda.synchronize()
     return out.float().cpu().numpy()

@@ -61,15 +61,17 @@ def test_prepare_rejects_bad_arguments_before_any_launch(wvd):
     plan = ctypes.c_void_p(0)
     ptrs = (ctypes.c_void_p * 84)(*([16] * 84))
     # null weights / prepared / plan_out
-    assert lib.wvd_prepare(16, 4, 6, None, 84, 16, 1 << 30, None, ctypes.byref(plan)) == wvd.WVD_EINVAL
-    assert lib.wvd_prepare(16, 4, 6, ptrs, 84, None, 1 << 30, None, ctypes.byref(plan)) == wvd.WVD_EINVAL
-    assert lib.wvd_prepare(16, 4, 6, ptrs, 84, 16, 1 << 30, None, None) == wvd.WVD_EINVAL
+    assert lib.wvd_prepare(16, 4, 6, None, 84, 0, 16, 1 << 30, None, ctypes.byref(plan)) == wvd.WVD_EINVAL
+    assert lib.wvd_prepare(16, 4, 6, ptrs, 84, 0, None, 1 << 30, None, ctypes.byref(plan)) == wvd.WVD_EINVAL
+    assert lib.wvd_prepare(16, 4, 6, ptrs, 84, 0, 16, 1 << 30, None, None) == wvd.WVD_EINVAL
     # wrong count, unsupported width, too small a buffer, a null weight
-    assert lib.wvd_prepare(16, 4, 6, ptrs, 83, 16, 1 << 30, None, ctypes.byref(plan)) == wvd.WVD_EINVAL
-    assert lib.wvd_prepare(20, 4, 6, ptrs, 84, 16, 1 << 30, None, ctypes.byref(plan)) == wvd.WVD_EUNSUPPORTED
-    assert lib.wvd_prepare(16, 4, 6, ptrs, 84, 16, 10, None, ctypes.byref(plan)) == wvd.WVD_ENOSPACE
+    assert lib.wvd_prepare(16, 4, 6, ptrs, 83, 0, 16, 1 << 30, None, ctypes.byref(plan)) == wvd.WVD_EINVAL
+    assert lib.wvd_prepare(20, 4, 6, ptrs, 84, 0, 16, 1 << 30, None, ctypes.byref(plan)) == wvd.WVD_EUNSUPPORTED
+    assert lib.wvd_prepare(16, 4, 6, ptrs, 84, 0, 16, 10, None, ctypes.byref(plan)) == wvd.WVD_ENOSPACE
     ptrs2 = (ctypes.c_void_p * 84)(*([16] * 83 + [None]))
-    assert lib.wvd_prepare(16, 4, 6, ptrs2, 84, 16, 1 << 30, None, ctypes.byref(plan)) == wvd.WVD_EINVAL
+    assert lib.wvd_prepare(16, 4, 6, ptrs2, 84, 0, 16, 1 << 30, None, ctypes.byref(plan)) == wvd.WVD_EINVAL
+    # unknown weight dtype
+    assert lib.wvd_prepare(16, 4, 6, ptrs, 84, 7, 16, 1 << 30, None, ctypes.byref(plan)) == wvd.WVD_EINVAL
     assert plan.value is None
 
 
@@ -77,6 +79,6 @@ def test_decode_and_workspace_reject_bad_plans(wvd):
     lib = wvd.lib()
     n = ctypes.c_size_t(0)
     assert lib.wvd_workspace_bytes(None, 3, 1, ctypes.byref(n)) == wvd.WVD_EINVAL
-    assert lib.wvd_decode(None, 16, 3, 1, 16, 16, 1 << 30, None) == wvd.WVD_EINVAL
+    assert lib.wvd_decode(None, 16, 0, 3, 1, 16, 16, 1 << 30, None) == wvd.WVD_EINVAL
     lib.wvd_destroy(None)  # ignored
     assert lib.wvd_profile_enable(None, 1) == wvd.WVD_EINVAL

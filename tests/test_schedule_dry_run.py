@@ -17,7 +17,7 @@ def dry():
 
 def plan_for(wvd, c, h, w):
     n = wvd.wvd_prepared_bytes(c, h, w)
-    return wvd.wvd_prepare(c, h, w, [FAKE] * 84, FAKE, n, 0)
+    return wvd.wvd_prepare(c, h, w, [FAKE] * 84, wvd.WVD_DTYPE_BF16, FAKE, n, 0)
 
 
 @pytest.mark.parametrize("cfg", synth.CONFIGS, ids=lambda c: c.name)
@@ -28,7 +28,7 @@ def test_every_config_schedules(dry, cfg):
         counts = {}
         for P in sorted(set(cfg.passes) | {1, cfg.T, cfg.T + 3}):
             ws = wvd.wvd_workspace_bytes(plan, cfg.T, P)
-            wvd.wvd_decode(plan, FAKE, cfg.T, P, FAKE, FAKE, ws, 0)
+            wvd.wvd_decode(plan, FAKE, wvd.WVD_DTYPE_BF16, cfg.T, P, FAKE, FAKE, ws, 0)
             counts[P] = wvd.wvd_last_launch_count(plan)
             assert counts[P] > 0
         # One pass per P latent frames; launches per pass do not depend on P
@@ -47,14 +47,17 @@ def test_workspace_depends_on_min_T_P(dry):
         assert wvd.wvd_workspace_bytes(plan, 9, 1) < wvd.wvd_workspace_bytes(plan, 9, 2)
         ws = wvd.wvd_workspace_bytes(plan, 3, 3)
         with pytest.raises(wvd.WvdError) as e:
-            wvd.wvd_decode(plan, FAKE, 3, 3, FAKE, FAKE, ws - 1, 0)
+            wvd.wvd_decode(plan, FAKE, 0, 3, 3, FAKE, FAKE, ws - 1, 0)
         assert e.value.status == wvd.WVD_ENOSPACE
+        with pytest.raises(wvd.WvdError) as e:
+            wvd.wvd_decode(plan, FAKE, 5, 3, 3, FAKE, FAKE, ws, 0)  # unknown latent dtype
+        assert e.value.status == wvd.WVD_EINVAL
         for bad in ((0, 1), (3, 0)):
             with pytest.raises(wvd.WvdError) as e:
-                wvd.wvd_decode(plan, FAKE, bad[0], bad[1], FAKE, FAKE, ws, 0)
+                wvd.wvd_decode(plan, FAKE, 0, bad[0], bad[1], FAKE, FAKE, ws, 0)
             assert e.value.status == wvd.WVD_EINVAL
         with pytest.raises(wvd.WvdError) as e:
-            wvd.wvd_decode(plan, FAKE, 3, 3, FAKE, FAKE + 8, ws, 0)  # misaligned workspace
+            wvd.wvd_decode(plan, FAKE, 0, 3, 3, FAKE, FAKE + 8, ws, 0)  # misaligned workspace
         assert e.value.status == wvd.WVD_EINVAL
     finally:
         wvd.wvd_destroy(plan)

@@ -266,7 +266,7 @@ struct Ctx {
   }
 };
 
-ConvSeg seg_basic(const bf16_t* x, long long x_fstride, int lda, int Cin, const bf16_t* w, int ldw,
+ConvSeg seg_basic(const h16_t* x, long long x_fstride, int lda, int Cin, const h16_t* w, int ldw,
                   long long tap_stride, int KT, int KS) {
   ConvSeg s;
   std::memset(&s, 0, sizeof(s));
@@ -333,20 +333,20 @@ void conv(Ctx& cx, ConvArgs& a, int cls) {
 }
 
 struct Act {
-  bf16_t* p;
+  h16_t* p;
   int C;      // channels (= voxel stride)
   int F;      // frames in this pass
   int H, W;
   long long fstride() const { return (long long)H * W * C; }
 };
 
-void stats(Ctx& cx, const Act& x, const bf16_t* ring, int nh) {
+void stats(Ctx& cx, const Act& x, const h16_t* ring, int nh) {
   float* rs = cx.wsp<float>(cx.W->rs);
   cx.what = "rms_stats";
   cx.run(3, 0, [&] { return launch_rms_stats(x.p, x.fstride(), x.C, ring, nh, x.C, x.F, x.H * x.W, rs, cx.st); });
 }
 
-void ring_update(Ctx& cx, bf16_t* ring, const Act& x) {
+void ring_update(Ctx& cx, h16_t* ring, const Act& x) {
   cx.what = "ring_update";
   cx.run(4, 0, [&] { return launch_ring_update(ring, x.p, x.fstride(), x.C, x.C, x.F, x.H * x.W, cx.st); });
 }
@@ -354,10 +354,10 @@ void ring_update(Ctx& cx, bf16_t* ring, const Act& x) {
 int tf_for(int KT, int F) { return (KT == 3 && F > 1) ? 2 : 1; }
 
 // Causal 3x3x3 conv with the fused RMSNorm+SiLU prologue.
-ConvArgs conv333(Ctx& cx, const Act& x, bf16_t* ring, int nh, int gamma_item, int w_item, int b_item, int Cout) {
+ConvArgs conv333(Ctx& cx, const Act& x, h16_t* ring, int nh, int gamma_item, int w_item, int b_item, int Cout) {
   ConvArgs a = args_init();
   ConvSeg& s = a.seg[0];
-  s = seg_basic(x.p, x.fstride(), x.C, x.C, cx.prep<bf16_t>(w_item), x.C, (long long)Cout * x.C, 3, 3);
+  s = seg_basic(x.p, x.fstride(), x.C, x.C, cx.prep<h16_t>(w_item), x.C, (long long)Cout * x.C, 3, 3);
   s.ring = ring;
   s.n_hist = nh;
   s.rs = cx.wsp<float>(cx.W->rs);
@@ -370,9 +370,9 @@ ConvArgs conv333(Ctx& cx, const Act& x, bf16_t* ring, int nh, int gamma_item, in
 }
 
 // ResBlock: x -> x (in place) when widths match, else x -> out.
-Act resblock(Ctx& cx, const RB& rb, const Act& x, bf16_t* hbuf, bf16_t* obuf, int ring1, int ring2, int nh) {
-  bf16_t* r1 = cx.wsp<bf16_t>(cx.W->ring[ring1]);
-  bf16_t* r2 = cx.wsp<bf16_t>(cx.W->ring[ring2]);
+Act resblock(Ctx& cx, const RB& rb, const Act& x, h16_t* hbuf, h16_t* obuf, int ring1, int ring2, int nh) {
+  h16_t* r1 = cx.wsp<h16_t>(cx.W->ring[ring1]);
+  h16_t* r2 = cx.wsp<h16_t>(cx.W->ring[ring2]);
   stats(cx, x, r1, nh);
   Act h{hbuf, rb.cout, x.F, x.H, x.W};
   {
@@ -380,7 +380,7 @@ Act resblock(Ctx& cx, const RB& rb, const Act& x, bf16_t* hbuf, bf16_t* obuf, in
     a.out = h.p;
     a.out_fstride = h.fstride();
     a.ldo = h.C;
-    a.epi = EPI_BF16;
+    a.epi = EPI_H16;
     set_grid(a, x.F, x.H, x.W, tf_for(3, x.F));
     conv(cx, a, 0);
   }
@@ -396,14 +396,14 @@ Act resblock(Ctx& cx, const RB& rb, const Act& x, bf16_t* hbuf, bf16_t* obuf, in
     } else {
       // 1x1x1 shortcut over the raw block input as a second K segment; its
       // bias is pre-summed with conv2's into the shortcut bias slot.
-      a.seg[1] = seg_basic(x.p, x.fstride(), x.C, x.C, cx.prep<bf16_t>(rb.scw), x.C, 0, 1, 1);
+      a.seg[1] = seg_basic(x.p, x.fstride(), x.C, x.C, cx.prep<h16_t>(rb.scw), x.C, 0, 1, 1);
       a.nseg = 2;
       a.bias = cx.prep<float>(rb.scb);
     }
     a.out = out.p;
     a.out_fstride = out.fstride();
     a.ldo = out.C;
-    a.epi = EPI_BF16;
+    a.epi = EPI_H16;
     set_grid(a, x.F, x.H, x.W, tf_for(3, x.F));
     conv(cx, a, 0);
   }
@@ -414,15 +414,15 @@ Act resblock(Ctx& cx, const RB& rb, const Act& x, bf16_t* hbuf, bf16_t* obuf, in
 void attention(Ctx& cx, const Act& x) {
   const Layout& L = cx.plan->L;
   const int C = x.C, Lt = x.H * x.W, Lp = lpad_of(Lt);
-  bf16_t* qkv = cx.wsp<bf16_t>(cx.W->qkv);
+  h16_t* qkv = cx.wsp<h16_t>(cx.W->qkv);
   float* S = cx.wsp<float>(cx.W->S);
-  bf16_t* Pm = cx.wsp<bf16_t>(cx.W->Pm);
-  bf16_t* Vt = cx.wsp<bf16_t>(cx.W->Vt);
-  bf16_t* O = cx.wsp<bf16_t>(cx.W->O);
+  h16_t* Pm = cx.wsp<h16_t>(cx.W->Pm);
+  h16_t* Vt = cx.wsp<h16_t>(cx.W->Vt);
+  h16_t* O = cx.wsp<h16_t>(cx.W->O);
   stats(cx, x, nullptr, 0);
   {  // qkv = Wqkv RMSNorm(x) + b
     ConvArgs a = args_init();
-    a.seg[0] = seg_basic(x.p, x.fstride(), C, C, cx.prep<bf16_t>(L.qkv_w), C, 0, 1, 1);
+    a.seg[0] = seg_basic(x.p, x.fstride(), C, C, cx.prep<h16_t>(L.qkv_w), C, 0, 1, 1);
     a.seg[0].rs = cx.wsp<float>(cx.W->rs);
     a.seg[0].gamma = cx.prep<float>(L.attn_norm);
     a.seg[0].prologue = PRO_NORM;
@@ -432,7 +432,7 @@ void attention(Ctx& cx, const Act& x) {
     a.out = qkv;
     a.out_fstride = (long long)Lt * 3 * C;
     a.ldo = 3 * C;
-    a.epi = EPI_BF16;
+    a.epi = EPI_H16;
     set_grid(a, x.F, x.H, x.W, 1);
     conv(cx, a, 1);
   }
@@ -461,13 +461,13 @@ void attention(Ctx& cx, const Act& x) {
     a.out = O;
     a.out_fstride = (long long)Lt * C;
     a.ldo = C;
-    a.epi = EPI_BF16;
+    a.epi = EPI_H16;
     set_grid(a, x.F, x.H, x.W, 1);
     conv(cx, a, 2);
   }
   {  // x += Wp O + bp
     ConvArgs a = args_init();
-    a.seg[0] = seg_basic(O, (long long)Lt * C, C, C, cx.prep<bf16_t>(L.proj_w), C, 0, 1, 1);
+    a.seg[0] = seg_basic(O, (long long)Lt * C, C, C, cx.prep<h16_t>(L.proj_w), C, 0, 1, 1);
     a.nseg = 1;
     a.Cout = C;
     a.bias = cx.prep<float>(L.proj_b);
@@ -477,16 +477,16 @@ void attention(Ctx& cx, const Act& x) {
     a.out = x.p;
     a.out_fstride = x.fstride();
     a.ldo = C;
-    a.epi = EPI_BF16;
+    a.epi = EPI_H16;
     set_grid(a, x.F, x.H, x.W, 1);
     conv(cx, a, 1);
   }
 }
 
 // time_conv: x (F frames, first global frame g) -> y (interleaved frames).
-Act time_upsample(Ctx& cx, int s, const Act& x, int g, bf16_t* ybuf, int ring_id) {
+Act time_upsample(Ctx& cx, int s, const Act& x, int g, h16_t* ybuf, int ring_id) {
   const Layout& L = cx.plan->L;
-  bf16_t* ring = cx.wsp<bf16_t>(cx.W->ring[ring_id]);
+  h16_t* ring = cx.wsp<h16_t>(cx.W->ring[ring_id]);
   const bool first = g == 0;
   Act y{ybuf, x.C, first ? 2 * x.F - 1 : 2 * x.F, x.H, x.W};
   if (first) {
@@ -496,7 +496,7 @@ Act time_upsample(Ctx& cx, int s, const Act& x, int g, bf16_t* ybuf, int ring_id
   if (sx.F == 0) return y;
   const int nh = std::min(2, std::max(0, g - 1));
   ConvArgs a = args_init();
-  a.seg[0] = seg_basic(sx.p, sx.fstride(), sx.C, sx.C, cx.prep<bf16_t>(L.tc_w[s]), sx.C, 2LL * sx.C * sx.C, 3, 1);
+  a.seg[0] = seg_basic(sx.p, sx.fstride(), sx.C, sx.C, cx.prep<h16_t>(L.tc_w[s]), sx.C, 2LL * sx.C * sx.C, 3, 1);
   a.seg[0].ring = ring;
   a.seg[0].n_hist = nh;
   a.nseg = 1;
@@ -514,11 +514,11 @@ Act time_upsample(Ctx& cx, int s, const Act& x, int g, bf16_t* ybuf, int ring_id
 }
 
 // Nearest-2x + Conv2d 3x3 in phase form: x [F][H][W][C] -> y [F][2H][2W][C].
-Act up_conv(Ctx& cx, int s, const Act& x, bf16_t* ybuf) {
+Act up_conv(Ctx& cx, int s, const Act& x, h16_t* ybuf) {
   const Layout& L = cx.plan->L;
   Act y{ybuf, x.C, x.F, 2 * x.H, 2 * x.W};
   ConvArgs a = args_init();
-  a.seg[0] = seg_basic(x.p, x.fstride(), x.C, x.C, cx.prep<bf16_t>(L.upc_w[s]), x.C, (long long)x.C * x.C, 1, 2);
+  a.seg[0] = seg_basic(x.p, x.fstride(), x.C, x.C, cx.prep<h16_t>(L.upc_w[s]), x.C, (long long)x.C * x.C, 1, 2);
   a.nseg = 1;
   a.nphase = 4;
   a.Cout = x.C;
@@ -556,9 +556,10 @@ int wvd_prepared_bytes(int c, int h, int w, size_t* bytes) {
   return WVD_OK;
 }
 
-int wvd_prepare(int c, int h, int w, const void* const* weights, int n_weights, void* prepared,
+int wvd_prepare(int c, int h, int w, const void* const* weights, int n_weights, int weight_dtype, void* prepared,
                 size_t prepared_bytes, void* stream, wvd_plan** plan_out) {
   if (!weights || !prepared || !plan_out) return WVD_EINVAL;
+  if (weight_dtype != WVD_DTYPE_BF16 && weight_dtype != WVD_DTYPE_F32) return WVD_EINVAL;
   int st = check_dims(c, h, w);
   if (st) return st;
   if (n_weights != WVD_NUM_WEIGHTS) return WVD_EINVAL;
@@ -579,21 +580,21 @@ int wvd_prepare(int c, int h, int w, const void* const* weights, int n_weights, 
   hipError_t e = hipSuccess;
   for (int i = 0; i < WVD_NUM_WEIGHTS && e == hipSuccess; ++i) {
     const Item& it = L.items[i];
-    const bf16_t* src = static_cast<const bf16_t*>(weights[i]);
+    const void* src = weights[i];
     void* dst = p->prep + it.off;
     if (it.kind == K_CONV)
-      e = launch_prep_permute(src, it.cout, it.cin, it.taps, it.cin_pad, static_cast<bf16_t*>(dst), s);
+      e = launch_prep_permute(src, weight_dtype, it.cout, it.cin, it.taps, it.cin_pad, static_cast<h16_t*>(dst), s);
     else if (it.kind == K_PHASE)
-      e = launch_prep_phase(src, it.cout, static_cast<bf16_t*>(dst), s);
+      e = launch_prep_phase(src, weight_dtype, it.cout, static_cast<h16_t*>(dst), s);
     else
-      e = launch_prep_vec(src, it.n, it.scale, static_cast<float*>(dst), s);
+      e = launch_prep_vec(src, weight_dtype, it.n, it.scale, static_cast<float*>(dst), s);
   }
   // Blocks with a shortcut add two biases; keep their sum in the shortcut slot.
   const RB* sc_blocks[2] = {&L.up[2][0], &L.up[3][0]};
   for (const RB* rb : sc_blocks) {
     if (e != hipSuccess) break;
-    e = launch_prep_vec_add(static_cast<const bf16_t*>(weights[rb->conv2b]), static_cast<const bf16_t*>(weights[rb->scb]),
-                            rb->cout, reinterpret_cast<float*>(p->prep + L.items[rb->scb].off), s);
+    e = launch_prep_vec_add(weights[rb->conv2b], weights[rb->scb], weight_dtype, rb->cout,
+                            reinterpret_cast<float*>(p->prep + L.items[rb->scb].off), s);
   }
   if (e != hipSuccess) {
     set_error("wvd_prepare", e);
@@ -611,9 +612,10 @@ int wvd_workspace_bytes(const wvd_plan* plan, int T, int frames_per_pass, size_t
   return WVD_OK;
 }
 
-int wvd_decode(const wvd_plan* cplan, const void* z, int T, int frames_per_pass, void* out, void* workspace,
-               size_t workspace_bytes, void* stream) {
+int wvd_decode(const wvd_plan* cplan, const void* z, int z_dtype, int T, int frames_per_pass, void* out,
+               void* workspace, size_t workspace_bytes, void* stream) {
   if (!plan_ok(cplan) || !z || !out || !workspace || T < 1 || frames_per_pass < 1) return WVD_EINVAL;
+  if (z_dtype != WVD_DTYPE_BF16 && z_dtype != WVD_DTYPE_F32) return WVD_EINVAL;
   if (!aligned16(workspace)) return WVD_EINVAL;
   wvd_plan* plan = const_cast<wvd_plan*>(cplan);
   const int c = plan->c, h = plan->h, w = plan->w;
@@ -628,10 +630,10 @@ int wvd_decode(const wvd_plan* cplan, const void* z, int T, int frames_per_pass,
   cx.W = &W;
   plan->launches = 0;
   const int c4 = 4 * c;
-  bf16_t* X = cx.wsp<bf16_t>(W.X);
-  bf16_t* Hb = cx.wsp<bf16_t>(W.H);
-  bf16_t* Y = cx.wsp<bf16_t>(W.Y);
-  bf16_t* zt = cx.wsp<bf16_t>(W.zt);
+  h16_t* X = cx.wsp<h16_t>(W.X);
+  h16_t* Hb = cx.wsp<h16_t>(W.H);
+  h16_t* Y = cx.wsp<h16_t>(W.Y);
+  h16_t* zt = cx.wsp<h16_t>(W.zt);
   const int VT = 4 * T - 3;
 
   for (int t0 = 0; t0 < T && cx.err == hipSuccess; t0 += P) {
@@ -640,13 +642,14 @@ int wvd_decode(const wvd_plan* cplan, const void* z, int T, int frames_per_pass,
     const int g0 = t0, g1 = first ? 0 : 2 * t0 - 1, g2 = first ? 0 : 4 * t0 - 3;
     const int nh0 = std::min(2, g0), nh1 = std::min(2, g1), nh2 = std::min(2, g2);
     // conv_in on the channels-last latents.
-    cx.run(4, 0, [&] { return launch_latent_to_cl(static_cast<const bf16_t*>(z), T, t0, F0, h * w, zt, cx.st); });
+    cx.what = "latent_to_cl";
+    cx.run(4, 0, [&] { return launch_latent_to_cl(z, z_dtype, T, t0, F0, h * w, zt, cx.st); });
     Act za{zt, 64, F0, h, w};
     Act x{X, c4, F0, h, w};
     {
-      bf16_t* ring = cx.wsp<bf16_t>(W.ring[R_CONV_IN]);
+      h16_t* ring = cx.wsp<h16_t>(W.ring[R_CONV_IN]);
       ConvArgs a = args_init();
-      a.seg[0] = seg_basic(zt, za.fstride(), 64, 64, cx.prep<bf16_t>(L.conv_in_w), 64, (long long)c4 * 64, 3, 3);
+      a.seg[0] = seg_basic(zt, za.fstride(), 64, 64, cx.prep<h16_t>(L.conv_in_w), 64, (long long)c4 * 64, 3, 3);
       a.seg[0].ring = ring;
       a.seg[0].n_hist = nh0;
       a.nseg = 1;
@@ -655,7 +658,7 @@ int wvd_decode(const wvd_plan* cplan, const void* z, int T, int frames_per_pass,
       a.out = x.p;
       a.out_fstride = x.fstride();
       a.ldo = c4;
-      a.epi = EPI_BF16;
+      a.epi = EPI_H16;
       set_grid(a, F0, h, w, tf_for(3, F0));
       conv(cx, a, 0);
       ring_update(cx, ring, za);
@@ -682,7 +685,7 @@ int wvd_decode(const wvd_plan* cplan, const void* z, int T, int frames_per_pass,
     x = resblock(cx, L.up[3][1], x, Hb, nullptr, R_UP31_1, R_UP31_2, nh2);
     // Head: RMSNorm + SiLU + conv c -> 12, pixel shuffle, clamp, NCTHW video.
     {
-      bf16_t* ring = cx.wsp<bf16_t>(W.ring[R_HEAD]);
+      h16_t* ring = cx.wsp<h16_t>(W.ring[R_HEAD]);
       stats(cx, x, ring, nh2);
       ConvArgs a = conv333(cx, x, ring, nh2, L.head_norm, L.head_w, L.head_b, 12);
       a.out = out;

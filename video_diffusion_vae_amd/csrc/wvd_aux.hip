@@ -18,8 +18,8 @@ constexpr float kNormEps = 1e-12f;
 // fixed butterfly combines the G lanes, so the value of a voxel never depends
 // on where or when it is computed (fp32 statistics: Wan2.2 VAE decoder page,
 // "Limits").
-__global__ __launch_bounds__(256) void rms_stats_kernel(const bf16_t* __restrict__ x, long long x_fstride,
-                                                        int lda, const bf16_t* __restrict__ ring,
+__global__ __launch_bounds__(256) void rms_stats_kernel(const h16_t* __restrict__ x, long long x_fstride,
+                                                        int lda, const h16_t* __restrict__ ring,
                                                         int n_hist, int C, int F, int HW, int G,
                                                         float* __restrict__ rs) {
   const int lane = threadIdx.x & 63;
@@ -38,11 +38,11 @@ __global__ __launch_bounds__(256) void rms_stats_kernel(const bf16_t* __restrict
     if (ok) {
       slot = vv / HW + first_slot;
       pix = vv % HW;
-      const bf16_t* p = slot < 2 ? ring + (slot * HW + pix) * C : x + (slot - 2) * x_fstride + pix * lda;
+      const h16_t* p = slot < 2 ? ring + (slot * HW + pix) * C : x + (slot - 2) * x_fstride + pix * lda;
       for (int g = sub; g < ngroups; g += G) {
         uint4 r = *reinterpret_cast<const uint4*>(p + g * 8);
         float f[8];
-        unpack8(r, f);
+        unpack8h(r, f);
         float t = 0.0f;
 #pragma unroll
         for (int k = 0; k < 8; ++k) t += f[k] * f[k];
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void rms_stats_kernel(const bf16_t* __restrict
 }
 
 // ring <- the last two frames of [ring[0], ring[1], x[0..F-1]] (F >= 1).
-__global__ __launch_bounds__(256) void ring_update_kernel(bf16_t* __restrict__ ring, const bf16_t* __restrict__ x,
+__global__ __launch_bounds__(256) void ring_update_kernel(h16_t* __restrict__ ring, const h16_t* __restrict__ x,
                                                           long long x_fstride, int lda, int C, int F, int HW) {
   const int g8 = C >> 3;
   const long long n = (long long)HW * g8;
@@ -73,9 +73,10 @@ __global__ __launch_bounds__(256) void ring_update_kernel(bf16_t* __restrict__ r
   }
 }
 
-// z [48][T][HW] frames t0..t0+F-1 -> zt [F][HW][64] (channels 48..63 zero).
-__global__ __launch_bounds__(256) void latent_to_cl_kernel(const bf16_t* __restrict__ z, int T, int t0, int F,
-                                                           int HW, bf16_t* __restrict__ zt) {
+// z [48][T][HW] (bf16 or fp32) frames t0..t0+F-1 -> zt [F][HW][64] fp16
+// (channels 48..63 zero).
+__global__ __launch_bounds__(256) void latent_to_cl_kernel(const void* __restrict__ z, int dtype, int T, int t0,
+                                                           int F, int HW, h16_t* __restrict__ zt) {
   const long long n = (long long)F * HW;
   for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n;
        e += (long long)gridDim.x * blockDim.x) {
@@ -86,8 +87,8 @@ __global__ __launch_bounds__(256) void latent_to_cl_kernel(const bf16_t* __restr
       const int c = 2 * c2;
       uint32_t lo = 0, hi = 0;
       if (c < 48) {
-        lo = z[((long long)c * T + t0 + f) * HW + pix];
-        hi = z[((long long)(c + 1) * T + t0 + f) * HW + pix];
+        lo = f2h(load_in(z, ((long long)c * T + t0 + f) * HW + pix, dtype));
+        hi = f2h(load_in(z, ((long long)(c + 1) * T + t0 + f) * HW + pix, dtype));
       }
       w[c2] = lo | (hi << 16);
     }
@@ -113,9 +114,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // One wave per row: P = softmax(S) over the L valid columns (max-subtracted,
-// fp32), written as bf16 with zeros in columns L..Lpad-1.
+// fp32), written as fp16 with zeros in columns L..Lpad-1.
 __global__ __launch_bounds__(256) void softmax_rows_kernel(const float* __restrict__ S, int rows, int L, int Lpad,
-                                                           bf16_t* __restrict__ P) {
+                                                           h16_t* __restrict__ P) {
   const int lane = threadIdx.x & 63;
   const long long row = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   if (row >= rows) return;
@@ -127,22 +128,22 @@ __global__ __launch_bounds__(256) void softmax_rows_kernel(const float* __restri
   for (int j = lane; j < L; j += 64) sum += __expf(s[j] - mx);
   sum = wave_sum(sum);
   const float inv = 1.0f / sum;
-  bf16_t* p = P + row * Lpad;
-  for (int j = lane; j < Lpad; j += 64) p[j] = j < L ? (bf16_t)f2bf(__expf(s[j] - mx) * inv) : (bf16_t)0;
+  h16_t* p = P + row * Lpad;
+  for (int j = lane; j < Lpad; j += 64) p[j] = j < L ? (h16_t)f2h(__expf(s[j] - mx) * inv) : (h16_t)0;
 }
 
 // V^T per frame: vt[f][c][l] = qkv[f][l][2C + c], zero for l >= L.
-__global__ __launch_bounds__(256) void transpose_v_kernel(const bf16_t* __restrict__ qkv, int L, int C, int Lpad,
-                                                          bf16_t* __restrict__ vt) {
-  __shared__ bf16_t tile[64][65];
+__global__ __launch_bounds__(256) void transpose_v_kernel(const h16_t* __restrict__ qkv, int L, int C, int Lpad,
+                                                          h16_t* __restrict__ vt) {
+  __shared__ h16_t tile[64][65];
   const int f = blockIdx.z;
   const int l0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
-  const bf16_t* src = qkv + (long long)f * L * 3 * C + 2 * C;
-  bf16_t* dst = vt + (long long)f * C * Lpad;
+  const h16_t* src = qkv + (long long)f * L * 3 * C + 2 * C;
+  h16_t* dst = vt + (long long)f * C * Lpad;
   for (int k = threadIdx.x; k < 64 * 64; k += 256) {
     const int r = k / 64, cc = k % 64;  // r: token, cc: channel
     const int l = l0 + r, c = c0 + cc;
-    tile[r][cc] = (l < L && c < C) ? src[(long long)l * 3 * C + c] : (bf16_t)0;
+    tile[r][cc] = (l < L && c < C) ? src[(long long)l * 3 * C + c] : (h16_t)0;
   }
   __syncthreads();
   for (int k = threadIdx.x; k < 64 * 64; k += 256) {
@@ -152,9 +153,9 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const bf16_t* __restri
   }
 }
 
-// out[tap][o][i] = w[o][i][tap] (i < cin), 0 for cin <= i < cin_pad.
-__global__ void prep_permute_kernel(const bf16_t* __restrict__ w, int cout, int cin, int taps, int cin_pad,
-                                    bf16_t* __restrict__ out) {
+// out[tap][o][i] = fp16(w[o][i][tap]) (i < cin), 0 for cin <= i < cin_pad.
+__global__ void prep_permute_kernel(const void* __restrict__ w, int dtype, int cout, int cin, int taps, int cin_pad,
+                                    h16_t* __restrict__ out) {
   const long long n = (long long)taps * cout * cin_pad;
   for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n;
        e += (long long)gridDim.x * blockDim.x) {
@@ -162,7 +163,7 @@ __global__ void prep_permute_kernel(const bf16_t* __restrict__ w, int cout, int 
     const long long t2 = e / cin_pad;
     const int o = (int)(t2 % cout);
     const int tap = (int)(t2 / cout);
-    out[e] = i < cin ? w[((long long)o * cin + i) * taps + tap] : (bf16_t)0;
+    out[e] = i < cin ? (h16_t)f2h(load_in(w, ((long long)o * cin + i) * taps + tap, dtype)) : (h16_t)0;
   }
 }
 
@@ -170,8 +171,8 @@ __global__ void prep_permute_kernel(const bf16_t* __restrict__ w, int cout, int 
 // pixel (2i+py, 2j+px) is a 2x2 conv of the low-resolution input at rows
 // i+py-1+a, cols j+px-1+b (a, b in {0,1}) whose weights are sums of the 3x3
 // weights: rows {0} / {1,2} for py = 0 and {0,1} / {2} for py = 1 (same for
-// columns).  Sums in fp32, rounded once to bf16.  out[ph][tap][o][i].
-__global__ void prep_phase_kernel(const bf16_t* __restrict__ w, int C, bf16_t* __restrict__ out) {
+// columns).  Sums in fp32, rounded once to fp16.  out[ph][tap][o][i].
+__global__ void prep_phase_kernel(const void* __restrict__ w, int dtype, int C, h16_t* __restrict__ out) {
   const long long n = 16LL * C * C;
   for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n;
        e += (long long)gridDim.x * blockDim.x) {
@@ -186,22 +187,22 @@ __global__ void prep_phase_kernel(const bf16_t* __restrict__ w, int C, bf16_t* _
     const int kx0 = (px == 0) ? (tb == 0 ? 0 : 1) : (tb == 0 ? 0 : 2);
     const int kx1 = (px == 0) ? (tb == 0 ? 0 : 2) : (tb == 0 ? 1 : 2);
     float s = 0.0f;
-    const bf16_t* wp = w + ((long long)o * C + i) * 9;
+    const long long wp = ((long long)o * C + i) * 9;
     for (int ky = ky0; ky <= ky1; ++ky)
-      for (int kx = kx0; kx <= kx1; ++kx) s += bf2f(wp[ky * 3 + kx]);
-    out[e] = (bf16_t)f2bf(s);
+      for (int kx = kx0; kx <= kx1; ++kx) s += load_in(w, wp + ky * 3 + kx, dtype);
+    out[e] = (h16_t)f2h(s);
   }
 }
 
-__global__ void prep_vec_kernel(const bf16_t* __restrict__ v, int n, float scale, float* __restrict__ out) {
+__global__ void prep_vec_kernel(const void* __restrict__ v, int dtype, int n, float scale, float* __restrict__ out) {
   for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < n; e += gridDim.x * blockDim.x)
-    out[e] = bf2f(v[e]) * scale;
+    out[e] = load_in(v, e, dtype) * scale;
 }
 
-__global__ void prep_vec_add_kernel(const bf16_t* __restrict__ a, const bf16_t* __restrict__ b, int n,
+__global__ void prep_vec_add_kernel(const void* __restrict__ a, const void* __restrict__ b, int dtype, int n,
                                     float* __restrict__ out) {
   for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < n; e += gridDim.x * blockDim.x)
-    out[e] = bf2f(a[e]) + bf2f(b[e]);
+    out[e] = load_in(a, e, dtype) + load_in(b, e, dtype);
 }
 
 unsigned grid_for(long long n, int per_block = 256, long long cap = 65536) {
@@ -213,7 +214,7 @@ unsigned grid_for(long long n, int per_block = 256, long long cap = 65536) {
 
 }  // namespace
 
-hipError_t launch_rms_stats(const bf16_t* x, long long x_fstride, int lda, const bf16_t* ring, int n_hist,
+hipError_t launch_rms_stats(const h16_t* x, long long x_fstride, int lda, const h16_t* ring, int n_hist,
                             int C, int F, int HW, float* rs, hipStream_t s) {
   if (g_dry_run) return hipSuccess;
   int G = 1;
@@ -225,7 +226,7 @@ hipError_t launch_rms_stats(const bf16_t* x, long long x_fstride, int lda, const
   return hipGetLastError();
 }
 
-hipError_t launch_ring_update(bf16_t* ring, const bf16_t* x, long long x_fstride, int lda, int C, int F, int HW,
+hipError_t launch_ring_update(h16_t* ring, const h16_t* x, long long x_fstride, int lda, int C, int F, int HW,
                               hipStream_t s) {
   if (g_dry_run) return hipSuccess;
   const long long n = (long long)HW * (C / 8);
@@ -234,9 +235,10 @@ hipError_t launch_ring_update(bf16_t* ring, const bf16_t* x, long long x_fstride
   return hipGetLastError();
 }
 
-hipError_t launch_latent_to_cl(const bf16_t* z, int T, int t0, int F, int HW, bf16_t* zt, hipStream_t s) {
+hipError_t launch_latent_to_cl(const void* z, int dtype, int T, int t0, int F, int HW, h16_t* zt, hipStream_t s) {
   if (g_dry_run) return hipSuccess;
-  hipLaunchKernelGGL(latent_to_cl_kernel, dim3(grid_for((long long)F * HW)), dim3(256), 0, s, z, T, t0, F, HW, zt);
+  hipLaunchKernelGGL(latent_to_cl_kernel, dim3(grid_for((long long)F * HW)), dim3(256), 0, s, z, dtype, T, t0, F, HW,
+                     zt);
   return hipGetLastError();
 }
 
@@ -248,42 +250,42 @@ hipError_t launch_copy16(void* dst, const void* src, size_t bytes, hipStream_t s
   return hipGetLastError();
 }
 
-hipError_t launch_softmax_rows(const float* S, int rows, int L, int Lpad, bf16_t* P, hipStream_t s) {
+hipError_t launch_softmax_rows(const float* S, int rows, int L, int Lpad, h16_t* P, hipStream_t s) {
   if (g_dry_run) return hipSuccess;
   hipLaunchKernelGGL(softmax_rows_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, S, rows, L, Lpad, P);
   return hipGetLastError();
 }
 
-hipError_t launch_transpose_v(const bf16_t* qkv, int F, int L, int C, int Lpad, bf16_t* vt, hipStream_t s) {
+hipError_t launch_transpose_v(const h16_t* qkv, int F, int L, int C, int Lpad, h16_t* vt, hipStream_t s) {
   if (g_dry_run) return hipSuccess;
   dim3 grid((unsigned)((Lpad + 63) / 64), (unsigned)((C + 63) / 64), (unsigned)F);
   hipLaunchKernelGGL(transpose_v_kernel, grid, dim3(256), 0, s, qkv, L, C, Lpad, vt);
   return hipGetLastError();
 }
 
-hipError_t launch_prep_permute(const bf16_t* w, int cout, int cin, int taps, int cin_pad, bf16_t* out,
+hipError_t launch_prep_permute(const void* w, int dtype, int cout, int cin, int taps, int cin_pad, h16_t* out,
                                hipStream_t s) {
   if (g_dry_run) return hipSuccess;
-  hipLaunchKernelGGL(prep_permute_kernel, dim3(grid_for((long long)taps * cout * cin_pad)), dim3(256), 0, s, w, cout,
-                     cin, taps, cin_pad, out);
+  hipLaunchKernelGGL(prep_permute_kernel, dim3(grid_for((long long)taps * cout * cin_pad)), dim3(256), 0, s, w, dtype,
+                     cout, cin, taps, cin_pad, out);
   return hipGetLastError();
 }
 
-hipError_t launch_prep_phase(const bf16_t* w, int C, bf16_t* out, hipStream_t s) {
+hipError_t launch_prep_phase(const void* w, int dtype, int C, h16_t* out, hipStream_t s) {
   if (g_dry_run) return hipSuccess;
-  hipLaunchKernelGGL(prep_phase_kernel, dim3(grid_for(16LL * C * C)), dim3(256), 0, s, w, C, out);
+  hipLaunchKernelGGL(prep_phase_kernel, dim3(grid_for(16LL * C * C)), dim3(256), 0, s, w, dtype, C, out);
   return hipGetLastError();
 }
 
-hipError_t launch_prep_vec(const bf16_t* v, int n, float scale, float* out, hipStream_t s) {
+hipError_t launch_prep_vec(const void* v, int dtype, int n, float scale, float* out, hipStream_t s) {
   if (g_dry_run) return hipSuccess;
-  hipLaunchKernelGGL(prep_vec_kernel, dim3(grid_for(n)), dim3(256), 0, s, v, n, scale, out);
+  hipLaunchKernelGGL(prep_vec_kernel, dim3(grid_for(n)), dim3(256), 0, s, v, dtype, n, scale, out);
   return hipGetLastError();
 }
 
-hipError_t launch_prep_vec_add(const bf16_t* a, const bf16_t* b, int n, float* out, hipStream_t s) {
+hipError_t launch_prep_vec_add(const void* a, const void* b, int dtype, int n, float* out, hipStream_t s) {
   if (g_dry_run) return hipSuccess;
-  hipLaunchKernelGGL(prep_vec_add_kernel, dim3(grid_for(n)), dim3(256), 0, s, a, b, n, out);
+  hipLaunchKernelGGL(prep_vec_add_kernel, dim3(grid_for(n)), dim3(256), 0, s, a, b, dtype, n, out);
   return hipGetLastError();
 }
 

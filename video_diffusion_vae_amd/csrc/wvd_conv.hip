@@ -1,4 +1,4 @@
-// Implicit-GEMM causal convolution on bf16 MFMA (gfx950), with the channel
+// Implicit-GEMM causal convolution on fp16 MFMA (gfx950), with the channel
 // RMSNorm (+ SiLU) applied while the input tile is staged into LDS and the
 // bias / residual / frame-interleave / phase-scatter / pixel-shuffle work
 // done in the epilogue.
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
   const int halo_bytes = a.nhv_max * ROWB;
   unsigned char* halo_s[2] = {smem, smem + halo_bytes};
   unsigned char* wbuf_s[2] = {smem + 2 * halo_bytes, smem + 2 * halo_bytes + BN * ROWB};
-  const bf16_t** vptr_s = reinterpret_cast<const bf16_t**>(smem + 2 * halo_bytes + 2 * BN * ROWB);
+  const h16_t** vptr_s = reinterpret_cast<const h16_t**>(smem + 2 * halo_bytes + 2 * BN * ROWB);
   float* rs_s = reinterpret_cast<float*>(vptr_s + a.nhv_max);
   float* gamma_s = rs_s + a.nhv_max;
 
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
     const int per_tap = (ipt + ntaps - 1) / ntaps;
     const bool norm = S.prologue != PRO_RAW;
     const bool act = S.prologue == PRO_NORM_SILU;
-    const bf16_t* wseg = S.w + (long long)ph * ntaps * S.w_tap_stride + (long long)f0 * S.w_frame_stride;
+    const h16_t* wseg = S.w + (long long)ph * ntaps * S.w_tap_stride + (long long)f0 * S.w_frame_stride;
 
     __syncthreads();  // previous segment finished with the LDS tables
     // Per-halo-voxel source pointer (null = zero padding) and norm scale.
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
       const int fo = f0 + hf - (KT - 1);
       const int y = y0 + hy - hs;
       const int x = x0 + hx - hs;
-      const bf16_t* p = nullptr;
+      const h16_t* p = nullptr;
       float rsv = 0.0f;
       if (y >= 0 && y < a.H && x >= 0 && x < a.W && fo < a.F) {
         const long long pix = (long long)y * a.W + x;
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
     auto load_item = [&](int idx, int chunk) -> uint4 {
       uint4 r = make_uint4(0, 0, 0, 0);
       if (idx < nitems) {
-        const bf16_t* p = vptr_s[idx / NP];
+        const h16_t* p = vptr_s[idx / NP];
         if (p) r = *reinterpret_cast<const uint4*>(p + chunk * BK + (idx % NP) * 8);
       }
       return r;
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
       const int p = idx % NP;
       if (norm) {
         float f[8];
-        unpack8(r, f);
+        unpack8h(r, f);
         const float sc = rs_s[v];
         const float* g = gamma_s + chunk * BK + p * 8;
 #pragma unroll
@@ -171,12 +171,12 @@ __global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
           float t = f[k] * sc * g[k];
           f[k] = act ? silu(t) : t;
         }
-        r = pack8(f);
+        r = pack8h(f);
       }
       *reinterpret_cast<uint4*>(hbuf + v * ROWB + 16 * (p ^ swz<NP>(v))) = r;
     };
     auto load_w = [&](int chunk, int tap, uint4* wr) {
-      const bf16_t* base = wseg + (long long)tap * S.w_tap_stride + chunk * BK;
+      const h16_t* base = wseg + (long long)tap * S.w_tap_stride + chunk * BK;
 #pragma unroll
       for (int k = 0; k < W_ITEMS; ++k) {
         const int idx = tid + 256 * k;
@@ -238,22 +238,22 @@ __global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
           const int part = kk * 2 + kpart;
-          bf16x8_t av[MI], bv[NJ];
+          f16x8_t av[MI], bv[NJ];
 #pragma unroll
           for (int i = 0; i < MI; ++i) {
             const int v = abase[i] + toff;
-            av[i] = *reinterpret_cast<const bf16x8_t*>(hsrc + v * ROWB + 16 * (part ^ swz<NP>(v)));
+            av[i] = *reinterpret_cast<const f16x8_t*>(hsrc + v * ROWB + 16 * (part ^ swz<NP>(v)));
           }
 #pragma unroll
           for (int j = 0; j < NJ; ++j) {
             const int n = wave_n * WN + 32 * j + lrow;
-            bv[j] = *reinterpret_cast<const bf16x8_t*>(wsrc + n * ROWB + 16 * (part ^ swz<NP>(n)));
+            bv[j] = *reinterpret_cast<const f16x8_t*>(wsrc + n * ROWB + 16 * (part ^ swz<NP>(n)));
           }
 #pragma unroll
           for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
         }
         if (hnext) {
 #pragma unroll
@@ -292,9 +292,9 @@ __global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
           float v = acc[i][j][e] * a.scale;
           if (a.bias) v += a.bias[n];
           switch (a.epi) {
-            case EPI_BF16: {
-              if (a.res) v += bf2f(a.res[f * a.res_fstride + pix * a.ldr + n]);
-              static_cast<bf16_t*>(a.out)[f * a.out_fstride + pix * a.ldo + n] = (bf16_t)f2bf(v);
+            case EPI_H16: {
+              if (a.res) v += h2f(a.res[f * a.res_fstride + pix * a.ldr + n]);
+              static_cast<h16_t*>(a.out)[f * a.out_fstride + pix * a.ldo + n] = (h16_t)f2h(v);
               break;
             }
             case EPI_F32:
@@ -304,12 +304,12 @@ __global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
               const int half = n >= Chalf ? 1 : 0;
               const int ch = n - half * Chalf;
               const long long fr = a.out_base + 2 * f + half;
-              static_cast<bf16_t*>(a.out)[fr * a.out_fstride + pix * a.ldo + ch] = (bf16_t)f2bf(v);
+              static_cast<h16_t*>(a.out)[fr * a.out_fstride + pix * a.ldo + ch] = (h16_t)f2h(v);
               break;
             }
             case EPI_PHASE: {
               const long long op = (long long)(2 * y + py) * (2 * a.W) + (2 * x + px);
-              static_cast<bf16_t*>(a.out)[f * a.out_fstride + op * a.ldo + n] = (bf16_t)f2bf(v);
+              static_cast<h16_t*>(a.out)[f * a.out_fstride + op * a.ldo + n] = (h16_t)f2h(v);
               break;
             }
             default: {  // EPI_VIDEO

@@ -16,7 +16,7 @@ constexpr int kMaxCin = 1024;           // largest norm input width kept in LDS
 
 enum Prologue { PRO_RAW = 0, PRO_NORM = 1, PRO_NORM_SILU = 2 };
 enum Epilogue {
-  EPI_BF16 = 0,    // channels-last bf16 (+ bias, + optional residual)
+  EPI_H16 = 0,     // channels-last fp16 (+ bias, + optional residual)
   EPI_F32 = 1,     // fp32 (scaled), e.g. attention logits
   EPI_TIME = 2,    // time_conv: channels [0,C) -> frame 2s+base, [C,2C) -> 2s+1+base
   EPI_PHASE = 3,   // up-conv phase (py,px): voxel (y,x) -> (2y+py, 2x+px)
@@ -26,11 +26,11 @@ enum Epilogue {
 // One K segment of the implicit GEMM: a (possibly normalised) input tensor,
 // its temporal history and the weights that contract it.
 struct ConvSeg {
-  const bf16_t* x;          // input frame 0 of this pass, voxel stride lda
-  const bf16_t* ring;       // [2][H][W][Cin] previous input frames (raw) or null
+  const h16_t* x;           // input frame 0 of this pass, voxel stride lda
+  const h16_t* ring;        // [2][H][W][Cin] previous input frames (raw) or null
   const float* rs;          // [2+F][H][W] per-voxel 1/||x|| (slot 2+f = frame f)
   const float* gamma;       // [Cin] gamma * sqrt(Cin) (norm prologues)
-  const bf16_t* w;          // [taps][rows][ldw] bf16, K contiguous
+  const h16_t* w;           // [taps][rows][ldw] fp16, K contiguous
   long long x_fstride;      // elements per input frame
   long long w_tap_stride;   // elements per tap
   long long w_frame_stride; // per-frame weight offset (attention GEMMs), else 0
@@ -51,7 +51,7 @@ struct ConvArgs {
   int Cout;
   const float* bias;        // [Cout] fp32 or null
   float scale;
-  const bf16_t* res;        // residual on the output grid, or null
+  const h16_t* res;         // fp16 residual on the output grid, or null
   long long res_fstride;
   int ldr;
   void* out;
@@ -76,20 +76,21 @@ hipError_t launch_conv(const ConvArgs& a, hipStream_t stream);
 size_t conv_lds_bytes(const ConvArgs& a);
 
 // Auxiliary kernels (wvd_aux.hip).
-hipError_t launch_rms_stats(const bf16_t* x, long long x_fstride, int lda, const bf16_t* ring,
+hipError_t launch_rms_stats(const h16_t* x, long long x_fstride, int lda, const h16_t* ring,
                             int n_hist, int C, int F, int HW, float* rs, hipStream_t s);
-hipError_t launch_ring_update(bf16_t* ring, const bf16_t* x, long long x_fstride, int lda, int C,
+hipError_t launch_ring_update(h16_t* ring, const h16_t* x, long long x_fstride, int lda, int C,
                               int F, int HW, hipStream_t s);
-hipError_t launch_latent_to_cl(const bf16_t* z, int T, int t0, int F, int HW, bf16_t* zt, hipStream_t s);
+hipError_t launch_latent_to_cl(const void* z, int dtype, int T, int t0, int F, int HW, h16_t* zt, hipStream_t s);
 hipError_t launch_copy16(void* dst, const void* src, size_t bytes, hipStream_t s);
-hipError_t launch_softmax_rows(const float* S, int rows, int L, int Lpad, bf16_t* P, hipStream_t s);
-hipError_t launch_transpose_v(const bf16_t* qkv, int F, int L, int C, int Lpad, bf16_t* vt, hipStream_t s);
+hipError_t launch_softmax_rows(const float* S, int rows, int L, int Lpad, h16_t* P, hipStream_t s);
+hipError_t launch_transpose_v(const h16_t* qkv, int F, int L, int C, int Lpad, h16_t* vt, hipStream_t s);
 // Prepare-time kernels.
-hipError_t launch_prep_permute(const bf16_t* w, int cout, int cin, int taps, int cin_pad, bf16_t* out,
+// Weights arrive as bf16 or fp32 (dtype); conv weights leave as fp16, vectors as fp32.
+hipError_t launch_prep_permute(const void* w, int dtype, int cout, int cin, int taps, int cin_pad, h16_t* out,
                                hipStream_t s);
-hipError_t launch_prep_phase(const bf16_t* w, int C, bf16_t* out, hipStream_t s);
-hipError_t launch_prep_vec(const bf16_t* v, int n, float scale, float* out, hipStream_t s);
+hipError_t launch_prep_phase(const void* w, int dtype, int C, h16_t* out, hipStream_t s);
+hipError_t launch_prep_vec(const void* v, int dtype, int n, float scale, float* out, hipStream_t s);
 // out[i] = a[i] + b[i] in fp32 (the two biases of a block with a shortcut).
-hipError_t launch_prep_vec_add(const bf16_t* a, const bf16_t* b, int n, float* out, hipStream_t s);
+hipError_t launch_prep_vec_add(const void* a, const void* b, int dtype, int n, float* out, hipStream_t s);
 
 }  // namespace wvd

@@ -20,6 +20,8 @@ WVD_ENOSPACE = -3
 WVD_EUNSUPPORTED = -4
 WVD_EHIP = -5
 NUM_WEIGHTS = 84
+WVD_DTYPE_BF16 = 0
+WVD_DTYPE_F32 = 1
 PROFILE_CLASSES = ("conv3x3x3", "conv_other", "attention_gemm", "norm_stats", "copies")
 
 
@@ -41,11 +43,11 @@ def _load() -> ctypes.CDLL:
     i = ctypes.c_int
     lib.wvd_prepared_bytes.argtypes = [i, i, i, ctypes.POINTER(sz)]
     lib.wvd_prepared_bytes.restype = i
-    lib.wvd_prepare.argtypes = [i, i, i, ctypes.POINTER(vp), i, vp, sz, vp, ctypes.POINTER(vp)]
+    lib.wvd_prepare.argtypes = [i, i, i, ctypes.POINTER(vp), i, i, vp, sz, vp, ctypes.POINTER(vp)]
     lib.wvd_prepare.restype = i
     lib.wvd_workspace_bytes.argtypes = [vp, i, i, ctypes.POINTER(sz)]
     lib.wvd_workspace_bytes.restype = i
-    lib.wvd_decode.argtypes = [vp, vp, i, i, vp, vp, sz, vp]
+    lib.wvd_decode.argtypes = [vp, vp, i, i, i, vp, vp, sz, vp]
     lib.wvd_decode.restype = i
     lib.wvd_destroy.argtypes = [vp]
     lib.wvd_destroy.restype = None
@@ -88,11 +90,11 @@ def wvd_prepared_bytes(c: int, h: int, w: int) -> int:
     return n.value
 
 
-def wvd_prepare(c: int, h: int, w: int, weight_ptrs: Sequence[int], prepared_ptr: int, prepared_bytes: int,
-                stream_ptr: int) -> int:
+def wvd_prepare(c: int, h: int, w: int, weight_ptrs: Sequence[int], weight_dtype: int, prepared_ptr: int,
+                prepared_bytes: int, stream_ptr: int) -> int:
     arr = (ctypes.c_void_p * len(weight_ptrs))(*weight_ptrs)
     plan = ctypes.c_void_p(0)
-    _check(_lib.wvd_prepare(c, h, w, arr, len(weight_ptrs), prepared_ptr, prepared_bytes, stream_ptr,
+    _check(_lib.wvd_prepare(c, h, w, arr, len(weight_ptrs), weight_dtype, prepared_ptr, prepared_bytes, stream_ptr,
                             ctypes.byref(plan)), "wvd_prepare")
     return plan.value
 
@@ -103,9 +105,10 @@ def wvd_workspace_bytes(plan: int, T: int, frames_per_pass: int) -> int:
     return n.value
 
 
-def wvd_decode(plan: int, z_ptr: int, T: int, frames_per_pass: int, out_ptr: int, ws_ptr: int, ws_bytes: int,
-               stream_ptr: int) -> None:
-    _check(_lib.wvd_decode(plan, z_ptr, T, frames_per_pass, out_ptr, ws_ptr, ws_bytes, stream_ptr), "wvd_decode")
+def wvd_decode(plan: int, z_ptr: int, z_dtype: int, T: int, frames_per_pass: int, out_ptr: int, ws_ptr: int,
+               ws_bytes: int, stream_ptr: int) -> None:
+    _check(_lib.wvd_decode(plan, z_ptr, z_dtype, T, frames_per_pass, out_ptr, ws_ptr, ws_bytes, stream_ptr),
+           "wvd_decode")
 
 
 def wvd_destroy(plan: int) -> None:
@@ -137,8 +140,9 @@ def wvd_profile_read(plan: int) -> Dict[str, Dict[str, float]]:
 class Decoder:
     """Prepared decoder for base width c at latent size h x w on the current
     CUDA (HIP) device.  `weights` are the 84 tensors in canonical order (a
-    sequence, or a dict in that order), any float dtype; they are copied to
-    contiguous bf16 on the device for preparation and may be dropped after."""
+    sequence, or a dict in that order), as numpy arrays or tensors; float32
+    weights are handed over as fp32 and any other float type as bf16.  They
+    are copied to the device for preparation and may be dropped after."""
 
     def __init__(self, weights: Union[Sequence, Dict[str, object]], c: int, h: int, w: int, device=None):
         import torch
@@ -149,15 +153,16 @@ class Decoder:
         ws = list(weights.values()) if isinstance(weights, dict) else list(weights)
         if len(ws) != NUM_WEIGHTS:
             raise WvdError(WVD_EINVAL, f"Decoder: expected {NUM_WEIGHTS} weights, got {len(ws)}")
-        dev_ws = []
-        for t in ws:
-            t = torch.as_tensor(t)
-            dev_ws.append(t.to(device=self.device, dtype=torch.bfloat16).contiguous())
+        ts = [torch.as_tensor(t) for t in ws]
+        f32 = all(t.dtype == torch.float32 for t in ts)
+        dt = torch.float32 if f32 else torch.bfloat16
+        self.weight_dtype = WVD_DTYPE_F32 if f32 else WVD_DTYPE_BF16
+        dev_ws = [t.to(device=self.device, dtype=dt).contiguous() for t in ts]
         nbytes = wvd_prepared_bytes(self.c, self.h, self.w)
         self.prepared = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         stream = torch.cuda.current_stream(self.device)
-        self.plan = wvd_prepare(self.c, self.h, self.w, [t.data_ptr() for t in dev_ws], self.prepared.data_ptr(),
-                                nbytes, stream.cuda_stream)
+        self.plan = wvd_prepare(self.c, self.h, self.w, [t.data_ptr() for t in dev_ws], self.weight_dtype,
+                                self.prepared.data_ptr(), nbytes, stream.cuda_stream)
         stream.synchronize()  # the input copies may be freed after this
         del dev_ws
         self._ws = None
@@ -169,7 +174,8 @@ class Decoder:
         torch = self.torch
         if z.dim() != 5 or tuple(z.shape[:2]) != (1, 48) or tuple(z.shape[3:]) != (self.h, self.w):
             raise WvdError(WVD_ESHAPE, f"decode: latents of shape {tuple(z.shape)}")
-        z = z.to(device=self.device, dtype=torch.bfloat16).contiguous()
+        zdt = torch.float32 if z.dtype == torch.float32 else torch.bfloat16
+        z = z.to(device=self.device, dtype=zdt).contiguous()
         T = int(z.shape[2])
         shape = (1, 3, 4 * T - 3, 16 * self.h, 16 * self.w)
         if out is None:
@@ -183,8 +189,9 @@ class Decoder:
                 self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
             workspace = self._ws
         stream = torch.cuda.current_stream(self.device)
-        wvd_decode(self.plan, z.data_ptr(), T, int(frames_per_pass), out.data_ptr(), workspace.data_ptr(),
-                   workspace.numel(), stream.cuda_stream)
+        wvd_decode(self.plan, z.data_ptr(), WVD_DTYPE_F32 if zdt == torch.float32 else WVD_DTYPE_BF16, T,
+                   int(frames_per_pass), out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                   stream.cuda_stream)
         return out
 
     def release_workspace(self) -> None:
