@@ -269,60 +269,90 @@ __global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
   }
 
   // ---- epilogue ----
-  const int Chalf = a.Cout >> 1;
+  // Each wave moves one 32-row block of its accumulators at a time through
+  // its own LDS region (compile-time register indices only), then every lane
+  // takes one output voxel and a contiguous run of CPL channels, so stores go
+  // out as 16-byte vectors along the channel axis.
+  constexpr int CPL = WN / 2;          // channels per lane in the store phase
+  constexpr int EROW = WN + 4;         // padded LDS row (floats)
+  __syncthreads();                     // all waves are done with the halo / weight tiles
+  float* ep = reinterpret_cast<float*>(smem) + wave * 32 * EROW;
+  const int er = lane >> 1;            // row of the block this lane stores
+  const int ec0 = (lane & 1) * CPL;    // first column of the block this lane stores
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
 #pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int e1 = 0; e1 < 4; ++e1) {
-        const int e = e4 * 4 + e1;
-        const int m = wave_m * WM + 32 * i + 8 * e4 + 4 * kpart + e1;
-        const int tx = m & (kTileW - 1);
-        const int t2 = m / kTileW;
-        const int ty = t2 % a.TH;
-        const int tf = t2 / a.TH;
-        const int f = f0 + tf, y = y0 + ty, x = x0 + tx;
-        if (f >= a.F || y >= a.H || x >= a.W) continue;
-        const long long pix = (long long)y * a.W + x;
+      for (int e = 0; e < 16; ++e)
+        ep[(8 * (e >> 2) + 4 * kpart + (e & 3)) * EROW + 32 * j + lrow] = acc[i][j][e];
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the block is in LDS
+    __builtin_amdgcn_wave_barrier();
+    const int m = wave_m * WM + 32 * i + er;
+    const int tx = m & (kTileW - 1);
+    const int t2 = m / kTileW;
+    const int f = f0 + t2 / a.TH, y = y0 + t2 % a.TH, x = x0 + tx;
+    const int nb = n0 + wave_n * WN + ec0;  // first output channel of this lane
+    if (f < a.F && y < a.H && x < a.W && nb < a.Cout) {
+      const long long pix = (long long)y * a.W + x;
+      const float* row = ep + er * EROW + ec0;
+      if (a.epi == EPI_VIDEO) {
+        for (int c = 0; c < CPL && nb + c < a.Cout; ++c) {
+          const int n = nb + c;
+          float v = row[c] * a.scale + (a.bias ? a.bias[n] : 0.0f);
+          v = fminf(fmaxf(v, -1.0f), 1.0f);
+          const int k = n >> 2, ddy = (n >> 1) & 1, ddx = n & 1;
+          const long long r2 = ((long long)k * a.video_T + a.out_base + f) * (2 * a.H) + 2 * y + ddy;
+          static_cast<bf16_t*>(a.out)[r2 * (2 * a.W) + 2 * x + ddx] = (bf16_t)f2bf(v);
+        }
+      } else if (a.epi == EPI_F32) {
+        float* o = static_cast<float*>(a.out) + f * a.out_fstride + pix * a.ldo;
+        for (int c = 0; c < CPL && nb + c < a.Cout; ++c)
+          o[nb + c] = row[c] * a.scale + (a.bias ? a.bias[nb + c] : 0.0f);
+      } else {
+        // fp16 channels-last destinations: plain, time-interleaved or phase.
+        h16_t* o;
+        int nc = nb;
+        if (a.epi == EPI_TIME) {
+          const int Chalf = a.Cout >> 1;
+          const int half = nb >= Chalf ? 1 : 0;
+          nc = nb - half * Chalf;
+          o = static_cast<h16_t*>(a.out) + (long long)(a.out_base + 2 * f + half) * a.out_fstride + pix * a.ldo;
+        } else if (a.epi == EPI_PHASE) {
+          const long long op = (long long)(2 * y + py) * (2 * a.W) + (2 * x + px);
+          o = static_cast<h16_t*>(a.out) + f * a.out_fstride + op * a.ldo;
+        } else {
+          o = static_cast<h16_t*>(a.out) + f * a.out_fstride + pix * a.ldo;
+        }
+        const h16_t* rp = a.res ? a.res + f * a.res_fstride + pix * a.ldr + nb : nullptr;
+        const bool full = nb + CPL <= a.Cout;
+        for (int c8 = 0; c8 < CPL; c8 += 8) {
+          float v[8];
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int n = n0 + wave_n * WN + 32 * j + lrow;
-          if (n >= a.Cout) continue;
-          float v = acc[i][j][e] * a.scale;
-          if (a.bias) v += a.bias[n];
-          switch (a.epi) {
-            case EPI_H16: {
-              if (a.res) v += h2f(a.res[f * a.res_fstride + pix * a.ldr + n]);
-              static_cast<h16_t*>(a.out)[f * a.out_fstride + pix * a.ldo + n] = (h16_t)f2h(v);
-              break;
+          for (int k = 0; k < 8; ++k) v[k] = row[c8 + k] * a.scale;
+          if (full) {
+            if (a.bias) {
+#pragma unroll
+              for (int k = 0; k < 8; ++k) v[k] += a.bias[nb + c8 + k];
             }
-            case EPI_F32:
-              static_cast<float*>(a.out)[f * a.out_fstride + pix * a.ldo + n] = v;
-              break;
-            case EPI_TIME: {
-              const int half = n >= Chalf ? 1 : 0;
-              const int ch = n - half * Chalf;
-              const long long fr = a.out_base + 2 * f + half;
-              static_cast<h16_t*>(a.out)[fr * a.out_fstride + pix * a.ldo + ch] = (h16_t)f2h(v);
-              break;
+            if (rp) {
+              float r[8];
+              unpack8h(*reinterpret_cast<const uint4*>(rp + c8), r);
+#pragma unroll
+              for (int k = 0; k < 8; ++k) v[k] += r[k];
             }
-            case EPI_PHASE: {
-              const long long op = (long long)(2 * y + py) * (2 * a.W) + (2 * x + px);
-              static_cast<h16_t*>(a.out)[f * a.out_fstride + op * a.ldo + n] = (h16_t)f2h(v);
-              break;
-            }
-            default: {  // EPI_VIDEO
-              const int k = n >> 2, ddy = (n >> 1) & 1, ddx = n & 1;
-              v = fminf(fmaxf(v, -1.0f), 1.0f);
-              const long long row = ((long long)k * a.video_T + a.out_base + f) * (2 * a.H) + 2 * y + ddy;
-              static_cast<bf16_t*>(a.out)[row * (2 * a.W) + 2 * x + ddx] = (bf16_t)f2bf(v);
-              break;
+            *reinterpret_cast<uint4*>(o + nc + c8) = pack8h(v);
+          } else {
+            for (int k = 0; k < 8 && nb + c8 + k < a.Cout; ++k) {
+              float t = v[k] + (a.bias ? a.bias[nb + c8 + k] : 0.0f);
+              if (rp) t += h2f(rp[c8 + k]);
+              o[nc + c8 + k] = (h16_t)f2h(t);
             }
           }
         }
       }
     }
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -356,8 +386,11 @@ size_t conv_lds_bytes(const ConvArgs& a) {
   int cin_max = 0;
   for (int s = 0; s < a.nseg; ++s)
     if (a.seg[s].prologue != PRO_RAW && a.seg[s].Cin > cin_max) cin_max = a.seg[s].Cin;
-  return (size_t)2 * a.nhv_max * bk * 2 + (size_t)2 * bn * bk * 2 + (size_t)a.nhv_max * (8 + 4) +
-         (size_t)cin_max * 4;
+  const size_t main_loop = (size_t)2 * a.nhv_max * bk * 2 + (size_t)2 * bn * bk * 2 + (size_t)a.nhv_max * (8 + 4) +
+                           (size_t)cin_max * 4;
+  const int wn = bn == 32 ? 32 : 64;  // wave tile width of the instantiation
+  const size_t epilogue = (size_t)4 * 32 * (wn + 4) * 4;
+  return main_loop > epilogue ? main_loop : epilogue;
 }
 
 const char* conv_check(const ConvArgs& a) {
