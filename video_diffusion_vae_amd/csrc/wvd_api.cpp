@@ -53,7 +53,7 @@ struct Layout {
 
 void add_conv(Layout& L, int cout, int cin, int taps, int cin_pad, int* wi, int* bi) {
   Item w{K_CONV, cout, cin, taps, cin_pad, 0, 1.0f, 0, 0};
-  w.bytes = (size_t)taps * cout * cin_pad * 2;
+  w.bytes = prep_frag_bytes(cout, cin_pad, taps);
   *wi = (int)L.items.size();
   L.items.push_back(w);
   Item b{K_VEC, 0, 0, 0, 0, cout, 1.0f, 0, (size_t)cout * 4};
@@ -98,7 +98,7 @@ Layout make_layout(int c) {
       Item& it = L.items[L.upc_w[s]];
       it.kind = K_PHASE;
       it.taps = 16;  // 4 phases x 2x2 taps
-      it.bytes = (size_t)16 * cs * cs * 2;
+      it.bytes = prep_frag_bytes(cs, cs, 16);
     }
     prev = cs;
   }
@@ -280,6 +280,7 @@ ConvSeg seg_basic(const h16_t* x, long long x_fstride, int lda, int Cin, const h
   s.KT = KT;
   s.KS = KS;
   s.prologue = PRO_RAW;
+  s.wfrag = 1;
   return s;
 }
 
@@ -351,7 +352,12 @@ void ring_update(Ctx& cx, h16_t* ring, const Act& x) {
   cx.run(4, 0, [&] { return launch_ring_update(ring, x.p, x.fstride(), x.C, x.C, x.F, x.H * x.W, cx.st); });
 }
 
-int tf_for(int KT, int F) { return (KT == 3 && F > 1) ? 2 : 1; }
+// Temporal-3 convs use 2-frame tiles (a single-frame pass masks the second
+// frame); the 1-frame, 16-row tile of a 3x3x3 conv would not fit in LDS.
+int tf_for(int KT, int F) {
+  (void)F;
+  return KT == 3 ? 2 : 1;
+}
 
 // Causal 3x3x3 conv with the fused RMSNorm+SiLU prologue.
 ConvArgs conv333(Ctx& cx, const Act& x, h16_t* ring, int nh, int gamma_item, int w_item, int b_item, int Cout) {
@@ -440,6 +446,7 @@ void attention(Ctx& cx, const Act& x) {
     ConvArgs a = args_init();
     a.seg[0] = seg_basic(qkv, (long long)Lt * 3 * C, 3 * C, C, qkv + C, 3 * C, 0, 1, 1);
     a.seg[0].w_frame_stride = (long long)Lt * 3 * C;
+    a.seg[0].wfrag = 0;  // K rows of the qkv activations
     a.nseg = 1;
     a.Cout = Lt;
     a.scale = 1.0f / std::sqrt((float)C);
@@ -456,6 +463,7 @@ void attention(Ctx& cx, const Act& x) {
     ConvArgs a = args_init();
     a.seg[0] = seg_basic(Pm, (long long)Lt * Lp, Lp, Lp, Vt, Lp, 0, 1, 1);
     a.seg[0].w_frame_stride = (long long)C * Lp;
+    a.seg[0].wfrag = 0;  // rows of V^T
     a.nseg = 1;
     a.Cout = C;
     a.out = O;
@@ -583,9 +591,9 @@ int wvd_prepare(int c, int h, int w, const void* const* weights, int n_weights, 
     const void* src = weights[i];
     void* dst = p->prep + it.off;
     if (it.kind == K_CONV)
-      e = launch_prep_permute(src, weight_dtype, it.cout, it.cin, it.taps, it.cin_pad, static_cast<h16_t*>(dst), s);
+      e = launch_prep_frag(src, weight_dtype, it.cout, it.cin, it.taps, it.cin_pad, static_cast<h16_t*>(dst), s);
     else if (it.kind == K_PHASE)
-      e = launch_prep_phase(src, weight_dtype, it.cout, static_cast<h16_t*>(dst), s);
+      e = launch_prep_phase_frag(src, weight_dtype, it.cout, static_cast<h16_t*>(dst), s);
     else
       e = launch_prep_vec(src, weight_dtype, it.n, it.scale, static_cast<float*>(dst), s);
   }

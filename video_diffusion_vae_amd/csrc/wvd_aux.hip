@@ -153,17 +153,23 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const h16_t* __restric
   }
 }
 
-// out[tap][o][i] = fp16(w[o][i][tap]) (i < cin), 0 for cin <= i < cin_pad.
-__global__ void prep_permute_kernel(const void* __restrict__ w, int dtype, int cout, int cin, int taps, int cin_pad,
-                                    h16_t* __restrict__ out) {
-  const long long n = (long long)taps * cout * cin_pad;
+// Fragment-order conv weights (layout in wvd_internal.h) from the PyTorch
+// layout w[o][i][tap] (taps flattened).
+__global__ void prep_frag_kernel(const void* __restrict__ w, int dtype, int cout, int cin, int taps, int cin_pad,
+                                 h16_t* __restrict__ out) {
+  const int NB = (cout + 31) / 32, U = cin_pad / 16;
+  const long long n = (long long)NB * U * taps * 512;
   for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n;
        e += (long long)gridDim.x * blockDim.x) {
-    const int i = (int)(e % cin_pad);
-    const long long t2 = e / cin_pad;
-    const int o = (int)(t2 % cout);
-    const int tap = (int)(t2 / cout);
-    out[e] = i < cin ? (h16_t)f2h(load_in(w, ((long long)o * cin + i) * taps + tap, dtype)) : (h16_t)0;
+    const int j = (int)(e & 7);
+    const int l = (int)((e >> 3) & 63);
+    const long long blk = e >> 9;
+    const int t = (int)(blk % taps);
+    const int u = (int)((blk / taps) % U);
+    const int nb = (int)(blk / ((long long)taps * U));
+    const int o = nb * 32 + (l & 31);
+    const int i = u * 16 + (l >> 5) * 8 + j;
+    out[e] = (o < cout && i < cin) ? (h16_t)f2h(load_in(w, ((long long)o * cin + i) * taps + t, dtype)) : (h16_t)0;
   }
 }
 
@@ -171,25 +177,33 @@ __global__ void prep_permute_kernel(const void* __restrict__ w, int dtype, int c
 // pixel (2i+py, 2j+px) is a 2x2 conv of the low-resolution input at rows
 // i+py-1+a, cols j+px-1+b (a, b in {0,1}) whose weights are sums of the 3x3
 // weights: rows {0} / {1,2} for py = 0 and {0,1} / {2} for py = 1 (same for
-// columns).  Sums in fp32, rounded once to fp16.  out[ph][tap][o][i].
-__global__ void prep_phase_kernel(const void* __restrict__ w, int dtype, int C, h16_t* __restrict__ out) {
-  const long long n = 16LL * C * C;
+// columns).  Sums in fp32, rounded once to fp16; fragment order with
+// tap = phase * 4 + a * 2 + b.
+__global__ void prep_phase_frag_kernel(const void* __restrict__ w, int dtype, int C, h16_t* __restrict__ out) {
+  const int NB = (C + 31) / 32, U = C / 16;
+  const long long n = (long long)NB * U * 16 * 512;
   for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n;
        e += (long long)gridDim.x * blockDim.x) {
-    const int i = (int)(e % C);
-    const long long t2 = e / C;
-    const int o = (int)(t2 % C);
-    const int tap = (int)((t2 / C) % 4);
-    const int ph = (int)(t2 / (4LL * C));
-    const int py = ph >> 1, px = ph & 1, ta = tap >> 1, tb = tap & 1;
-    const int ky0 = (py == 0) ? (ta == 0 ? 0 : 1) : (ta == 0 ? 0 : 2);
-    const int ky1 = (py == 0) ? (ta == 0 ? 0 : 2) : (ta == 0 ? 1 : 2);
-    const int kx0 = (px == 0) ? (tb == 0 ? 0 : 1) : (tb == 0 ? 0 : 2);
-    const int kx1 = (px == 0) ? (tb == 0 ? 0 : 2) : (tb == 0 ? 1 : 2);
+    const int j = (int)(e & 7);
+    const int l = (int)((e >> 3) & 63);
+    const long long blk = e >> 9;
+    const int t16 = (int)(blk % 16);
+    const int u = (int)((blk / 16) % U);
+    const int nb = (int)(blk / (16LL * U));
+    const int o = nb * 32 + (l & 31);
+    const int i = u * 16 + (l >> 5) * 8 + j;
     float s = 0.0f;
-    const long long wp = ((long long)o * C + i) * 9;
-    for (int ky = ky0; ky <= ky1; ++ky)
-      for (int kx = kx0; kx <= kx1; ++kx) s += load_in(w, wp + ky * 3 + kx, dtype);
+    if (o < C) {
+      const int ph = t16 >> 2, tap = t16 & 3;
+      const int py = ph >> 1, px = ph & 1, ta = tap >> 1, tb = tap & 1;
+      const int ky0 = (py == 0) ? (ta == 0 ? 0 : 1) : (ta == 0 ? 0 : 2);
+      const int ky1 = (py == 0) ? (ta == 0 ? 0 : 2) : (ta == 0 ? 1 : 2);
+      const int kx0 = (px == 0) ? (tb == 0 ? 0 : 1) : (tb == 0 ? 0 : 2);
+      const int kx1 = (px == 0) ? (tb == 0 ? 0 : 2) : (tb == 0 ? 1 : 2);
+      const long long wp = ((long long)o * C + i) * 9;
+      for (int ky = ky0; ky <= ky1; ++ky)
+        for (int kx = kx0; kx <= kx1; ++kx) s += load_in(w, wp + ky * 3 + kx, dtype);
+    }
     out[e] = (h16_t)f2h(s);
   }
 }
@@ -263,17 +277,22 @@ hipError_t launch_transpose_v(const h16_t* qkv, int F, int L, int C, int Lpad, h
   return hipGetLastError();
 }
 
-hipError_t launch_prep_permute(const void* w, int dtype, int cout, int cin, int taps, int cin_pad, h16_t* out,
-                               hipStream_t s) {
+size_t prep_frag_bytes(int cout, int cin_pad, int taps) {
+  return (size_t)((cout + 31) / 32) * 32 * cin_pad * taps * 2;
+}
+
+hipError_t launch_prep_frag(const void* w, int dtype, int cout, int cin, int taps, int cin_pad, h16_t* out,
+                            hipStream_t s) {
   if (g_dry_run) return hipSuccess;
-  hipLaunchKernelGGL(prep_permute_kernel, dim3(grid_for((long long)taps * cout * cin_pad)), dim3(256), 0, s, w, dtype,
-                     cout, cin, taps, cin_pad, out);
+  const long long n = (long long)prep_frag_bytes(cout, cin_pad, taps) / 2;
+  hipLaunchKernelGGL(prep_frag_kernel, dim3(grid_for(n)), dim3(256), 0, s, w, dtype, cout, cin, taps, cin_pad, out);
   return hipGetLastError();
 }
 
-hipError_t launch_prep_phase(const void* w, int dtype, int C, h16_t* out, hipStream_t s) {
+hipError_t launch_prep_phase_frag(const void* w, int dtype, int C, h16_t* out, hipStream_t s) {
   if (g_dry_run) return hipSuccess;
-  hipLaunchKernelGGL(prep_phase_kernel, dim3(grid_for(16LL * C * C)), dim3(256), 0, s, w, dtype, C, out);
+  const long long n = (long long)prep_frag_bytes(C, C, 16) / 2;
+  hipLaunchKernelGGL(prep_phase_frag_kernel, dim3(grid_for(n)), dim3(256), 0, s, w, dtype, C, out);
   return hipGetLastError();
 }
 

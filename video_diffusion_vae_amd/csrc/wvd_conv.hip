@@ -6,13 +6,26 @@
 // GEMM view: M = output voxels (tile TF x TH x 16), N = output channels
 // (tile BN), K = taps x input channels.  The K loop runs segment by segment
 // (the main conv, then optionally a 1x1x1 shortcut over the raw block input),
-// input-channel chunk by chunk (BK channels), tap by tap.  For each chunk the
-// input halo of the tile -- (TF+KT-1) x (TH+2) x 18 voxels for a 3x3x3 conv --
-// sits in LDS once and every tap reads a shifted window of it, so the input
-// is fetched once per chunk instead of once per tap.  The next chunk's halo
-// and the next tap's weights are double-buffered in LDS.  The accumulation
-// order (segment, chunk, tap, k16 step) does not depend on where the tile
-// lies, which keeps every output bit-identical for any frames_per_pass.
+// input-channel chunk by chunk (BK channels), tap by tap.
+//
+//  * A (activations): for each chunk the input halo of the tile -- e.g.
+//    4 x 10 x 18 voxels for a 3x3x3 conv over a 2 x 8 x 16 tile -- is staged
+//    into LDS once (normalised on the way in), and every tap reads a shifted
+//    window of it.  Rows are padded to BK*2+16 bytes, which makes the 16-byte
+//    fragment reads of 16 consecutive voxels bank-conflict free and turns
+//    every tap offset into an instruction immediate.  The next chunk's halo
+//    is loaded while the current one is multiplied (double buffer), so the
+//    only barrier is one per chunk.
+//  * B (weights): wvd_prepare stores each conv in MFMA fragment order -- one
+//    1 KiB block per (32 output channels, 16 input channels, tap) holding
+//    exactly what the 64 lanes of a wave feed the matrix core -- so each wave
+//    streams its own B fragments from L2 into registers with fully coalesced
+//    loads, several taps ahead of use.  Activation operands of the attention
+//    GEMMs are read the same way from their row-major layout.
+//
+// The accumulation order (segment, chunk, tap, k16 step) does not depend on
+// where a tile lies, which keeps every output bit-identical for any
+// frames_per_pass.
 //
 // The conv definition (cross-correlation, causal in time with two history
 // frames, zero spatial padding) follows the decoder the Wan2.2 VAE decoder
@@ -25,24 +38,27 @@ namespace wvd {
 
 namespace {
 
-template <int NP>
-__device__ __forceinline__ int swz(int row) {
-  // XOR swizzle of the 16-byte parts of a row so that 8 consecutive rows
-  // reading the same part hit 8 different 16-byte bank groups.
-  if constexpr (NP == 4) return (row >> 1) & 3;
-  else return (row >> 2) & 1;
-}
+// Geometry of the specialised 3x3x3 tile: 2 frames x 8 rows x 16 columns.
+constexpr int kTF333 = 2;
+constexpr int kTH333 = 8;
+constexpr int kHX = kTileW + 2;
+constexpr int kHY333 = kTH333 + 2;
+constexpr int kHF333 = kTF333 + 2;
+constexpr int kNHV333 = kHF333 * kHY333 * kHX;  // 720 halo voxels
 
-template <int BK, int BN, int WAVES_N>
+__device__ __forceinline__ f16x8_t ld_frag(const h16_t* p) { return *reinterpret_cast<const f16x8_t*>(p); }
+
+template <int BK, int BN, int WAVES_N, bool K333>
 __global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
   constexpr int NP = BK / 8;            // 16-byte parts per voxel row
-  constexpr int ROWB = BK * 2;          // bytes per LDS row
+  constexpr int ROWB = BK * 2 + 16;     // padded LDS row (bytes)
+  constexpr int KS = BK / 16;           // k16 steps per chunk
   constexpr int WAVES_M = 4 / WAVES_N;
   constexpr int WM = kTileM / WAVES_M;
   constexpr int WN = BN / WAVES_N;
   constexpr int MI = WM / 32;
   constexpr int NJ = WN / 32;
-  constexpr int W_ITEMS = (BN * NP + 255) / 256;
+  typedef f16x8_t BFrag[NJ][KS];
 
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x;
@@ -51,11 +67,10 @@ __global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
   const int wave_m = wave / WAVES_N;
   const int wave_n = wave % WAVES_N;
 
-  // ---- LDS carve-up ----
+  // ---- LDS carve-up: two halo buffers, then the per-voxel tables ----
   const int halo_bytes = a.nhv_max * ROWB;
   unsigned char* halo_s[2] = {smem, smem + halo_bytes};
-  unsigned char* wbuf_s[2] = {smem + 2 * halo_bytes, smem + 2 * halo_bytes + BN * ROWB};
-  const h16_t** vptr_s = reinterpret_cast<const h16_t**>(smem + 2 * halo_bytes + 2 * BN * ROWB);
+  const h16_t** vptr_s = reinterpret_cast<const h16_t**>(smem + 2 * halo_bytes);
   float* rs_s = reinterpret_cast<float*>(vptr_s + a.nhv_max);
   float* gamma_s = rs_s + a.nhv_max;
 
@@ -73,12 +88,17 @@ __global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
   const int ph = (logical / nN) % a.nphase;
   const int mt = logical / (nN * a.nphase);
   const int py = ph >> 1, px = ph & 1;
+  const int TF = K333 ? kTF333 : a.TF;
+  const int TH = K333 ? kTH333 : a.TH;
   const int txi = mt % a.tiles_x;
   const int tyi = (mt / a.tiles_x) % a.tiles_y;
   const int tfi = mt / (a.tiles_x * a.tiles_y);
-  const int f0 = tfi * a.TF, y0 = tyi * a.TH, x0 = txi * kTileW;
+  const int f0 = tfi * TF, y0 = tyi * TH, x0 = txi * kTileW;
   const int n0 = nt * BN;
   const int HW = a.H * a.W;
+  const int kpart = lane >> 5;  // which 8-wide K group of a k16 step this lane feeds
+  const int lrow = lane & 31;
+  const int ncol0 = n0 + wave_n * WN;  // first output channel of this wave
 
   f32x16_t acc[MI][NJ];
 #pragma unroll
@@ -88,28 +108,23 @@ __global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  const int kpart = lane >> 5;  // which 8-wide K group of a k16 step this lane feeds
-  const int lrow = lane & 31;
-
   for (int s = 0; s < a.nseg; ++s) {
     const ConvSeg& S = a.seg[s];
-    const int KT = S.KT;
-    const int hs = S.KS == 1 ? 0 : 1;
-    const int K2 = S.KS == 3 ? 3 : (S.KS == 2 ? 2 : 1);
+    const bool spec = K333 && s == 0;  // the specialised 3x3x3 segment
+    const int KT = spec ? 3 : S.KT;
+    const int hs = spec ? 1 : (S.KS == 1 ? 0 : 1);
+    const int K2 = spec ? 3 : (S.KS == 3 ? 3 : (S.KS == 2 ? 2 : 1));
     const int HX = kTileW + 2 * hs;
-    const int HY = a.TH + 2 * hs;
-    const int HF = a.TF + KT - 1;
+    const int HY = TH + 2 * hs;
+    const int HF = TF + KT - 1;
     const int nhv = HF * HY * HX;
     const int ntaps = KT * K2 * K2;
     const int nchunks = S.Cin / BK;
     const int nitems = nhv * NP;
-    const int ipt = (nitems + 255) >> 8;
-    const int per_tap = (ipt + ntaps - 1) / ntaps;
     const bool norm = S.prologue != PRO_RAW;
     const bool act = S.prologue == PRO_NORM_SILU;
-    const h16_t* wseg = S.w + (long long)ph * ntaps * S.w_tap_stride + (long long)f0 * S.w_frame_stride;
 
-    __syncthreads();  // previous segment finished with the LDS tables
+    __syncthreads();  // the previous segment (or tile setup) is done with LDS
     // Per-halo-voxel source pointer (null = zero padding) and norm scale.
     for (int v = tid; v < nhv; v += 256) {
       const int hx = v % HX;
@@ -137,16 +152,15 @@ __global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
       for (int c = tid; c < S.Cin; c += 256) gamma_s[c] = S.gamma[c];
     __syncthreads();
 
-    // Halo voxel of each A row this lane feeds (tap (0,0,0) in halo coords).
+    // Byte address (halo buffer relative) of each A row this lane feeds at
+    // tap (0,0,0) and k16 step 0.
     int abase[MI];
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
       const int m = wave_m * WM + 32 * i + lrow;
       const int tx = m & (kTileW - 1);
       const int t2 = m / kTileW;
-      const int ty = t2 % a.TH;
-      const int tf = t2 / a.TH;
-      abase[i] = (tf * HY + ty) * HX + tx;
+      abase[i] = (((t2 / TH) * HY + (t2 % TH)) * HX + tx) * ROWB + kpart * 16;
     }
 
     auto load_item = [&](int idx, int chunk) -> uint4 {
@@ -168,103 +182,139 @@ __global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
         const float* g = gamma_s + chunk * BK + p * 8;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          float t = f[k] * sc * g[k];
-          f[k] = act ? silu(t) : t;
+          const float t = f[k] * sc * g[k];
+          f[k] = act ? t * __builtin_amdgcn_rcpf(1.0f + __expf(-t)) : t;
         }
         r = pack8h(f);
       }
-      *reinterpret_cast<uint4*>(hbuf + v * ROWB + 16 * (p ^ swz<NP>(v))) = r;
+      *reinterpret_cast<uint4*>(hbuf + v * ROWB + 16 * p) = r;
     };
-    auto load_w = [&](int chunk, int tap, uint4* wr) {
-      const h16_t* base = wseg + (long long)tap * S.w_tap_stride + chunk * BK;
+
+    // B fragment source.  Fragment-major weights: block (n32, k16, tap) of
+    // 512 halves, lane l at l*8.  Row-major operands: row n, column k.
+    const int U = S.Cin / 16;
+    const int wtaps = a.nphase * ntaps;
+    const h16_t* bsrc[NJ];
+    bool bok[NJ];
 #pragma unroll
-      for (int k = 0; k < W_ITEMS; ++k) {
-        const int idx = tid + 256 * k;
-        uint4 r = make_uint4(0, 0, 0, 0);
-        if (idx < BN * NP) {
-          const int n = idx / NP;
-          if (n0 + n < a.Cout)
-            r = *reinterpret_cast<const uint4*>(base + (long long)(n0 + n) * S.ldw + (idx % NP) * 8);
-        }
-        wr[k] = r;
+    for (int j = 0; j < NJ; ++j) {
+      if (S.wfrag) {
+        const int nb = ncol0 / 32 + j;
+        bok[j] = nb * 32 < a.Cout;
+        bsrc[j] = S.w + ((long long)nb * U * wtaps + ph * ntaps) * 512 + lane * 8;
+      } else {
+        const int n = ncol0 + 32 * j + lrow;
+        bok[j] = n < a.Cout;
+        bsrc[j] = S.w + (long long)f0 * S.w_frame_stride + (long long)n * S.ldw + kpart * 8;
       }
-    };
-    auto store_w = [&](const uint4* wr, unsigned char* wb) {
+    }
+    auto load_b = [&](BFrag& b, int chunk, int tap) {
 #pragma unroll
-      for (int k = 0; k < W_ITEMS; ++k) {
-        const int idx = tid + 256 * k;
-        if (idx < BN * NP) {
-          const int n = idx / NP;
-          const int p = idx % NP;
-          *reinterpret_cast<uint4*>(wb + n * ROWB + 16 * (p ^ swz<NP>(n))) = wr[k];
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if (bok[j]) {
+            const long long off = S.wfrag ? ((long long)(chunk * KS + ks) * wtaps + tap) * 512
+                                          : (long long)chunk * BK + ks * 16;
+            b[j][ks] = ld_frag(bsrc[j] + off);
+          } else {
+            b[j][ks] = f16x8_t{};
+          }
         }
+    };
+    auto mma_tap = [&](const unsigned char* hsrc, int toff_bytes, const BFrag& b) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        f16x8_t av[MI];
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+          av[i] = *reinterpret_cast<const f16x8_t*>(hsrc + abase[i] + toff_bytes + ks * 32);
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], b[j][ks], acc[i][j], 0, 0, 0);
       }
     };
 
-    // Chunk 0 halo and the first weight tile, synchronously.
+    // Chunk 0 halo, synchronously.
     for (int idx = tid; idx < nitems; idx += 256) store_item(idx, 0, load_item(idx, 0), halo_s[0]);
-    {
-      uint4 wr[W_ITEMS];
-      load_w(0, 0, wr);
-      store_w(wr, wbuf_s[0]);
-    }
     __syncthreads();
 
-    int hb = 0, wb = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      const bool hnext = c + 1 < nchunks;
-      for (int t = 0; t < ntaps; ++t) {
-        int cn = c, tn = t + 1;
-        if (tn == ntaps) { tn = 0; cn = c + 1; }
-        const bool wnext = cn < nchunks;
-        uint4 wr[W_ITEMS];
-        if (wnext) load_w(cn, tn, wr);
-        uint4 hr[kMaxHaloItemsPerTap];
-        const int j0 = t * per_tap;
-        if (hnext) {
+    if (spec) {
+      // ---- 3x3x3: 9 (dt, dy) groups of 3 dx taps per chunk ----
+      // B fragments of tap t live in slot t % 3 == dx and are refilled with
+      // tap t + 3 right after use.  Halo item t of the next chunk is loaded
+      // at tap t and normalised into LDS at tap t + 3 from slot dx.
+      constexpr int IPT = (kNHV333 * NP + 255) / 256;  // halo items per thread per chunk
+      static_assert(IPT + 3 <= 27, "halo items must land inside a chunk");
+      BFrag bq[3];
 #pragma unroll
-          for (int k = 0; k < kMaxHaloItemsPerTap; ++k)
-            if (k < per_tap) hr[k] = load_item(tid + 256 * (j0 + k), c + 1);
-        }
-        // Tap offset inside the halo.
-        const int dt = t / (K2 * K2);
-        const int a2 = (t / K2) % K2;
-        const int b2 = t % K2;
-        const int dy = S.KS == 2 ? py + a2 : a2;
-        const int dx = S.KS == 2 ? px + b2 : b2;
-        const int toff = (dt * HY + dy) * HX + dx;
-        const unsigned char* hsrc = halo_s[hb];
-        const unsigned char* wsrc = wbuf_s[wb];
+      for (int t = 0; t < 3; ++t) load_b(bq[t], 0, t);
+      for (int c = 0; c < nchunks; ++c) {
+        const unsigned char* hsrc = halo_s[c & 1];
+        unsigned char* hdst = halo_s[(c + 1) & 1];
+        const bool hnext = c + 1 < nchunks;
+        uint4 hr[3];
+        for (int g = 0; g < 9; ++g) {
+          const int goff = ((g / 3) * kHY333 + (g % 3)) * kHX * ROWB;
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-          const int part = kk * 2 + kpart;
-          f16x8_t av[MI], bv[NJ];
-#pragma unroll
-          for (int i = 0; i < MI; ++i) {
-            const int v = abase[i] + toff;
-            av[i] = *reinterpret_cast<const f16x8_t*>(hsrc + v * ROWB + 16 * (part ^ swz<NP>(v)));
+          for (int dx = 0; dx < 3; ++dx) {
+            const int t = 3 * g + dx;
+            if (hnext) {
+              if (t >= 3 && t - 3 < IPT) store_item(tid + 256 * (t - 3), c + 1, hr[dx], hdst);
+              if (t < IPT) hr[dx] = load_item(tid + 256 * t, c + 1);
+            }
+            mma_tap(hsrc, goff + dx * ROWB, bq[dx]);
+            const int tn = t + 3;
+            if (tn < 27) {
+              load_b(bq[dx], c, tn);
+            } else if (hnext) {
+              load_b(bq[dx], c + 1, tn - 27);
+            }
           }
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) {
-            const int n = wave_n * WN + 32 * j + lrow;
-            bv[j] = *reinterpret_cast<const f16x8_t*>(wsrc + n * ROWB + 16 * (part ^ swz<NP>(n)));
-          }
-#pragma unroll
-          for (int i = 0; i < MI; ++i)
-#pragma unroll
-            for (int j = 0; j < NJ; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
         }
-        if (hnext) {
-#pragma unroll
-          for (int k = 0; k < kMaxHaloItemsPerTap; ++k)
-            if (k < per_tap) store_item(tid + 256 * (j0 + k), c + 1, hr[k], halo_s[hb ^ 1]);
-        }
-        if (wnext) store_w(wr, wbuf_s[wb ^ 1]);
-        __syncthreads();
-        wb ^= 1;
+        __syncthreads();  // next chunk's halo complete; this chunk's reads done
       }
-      hb ^= 1;
+    } else {
+      // ---- generic taps: B one tap ahead, halo items spread over taps ----
+      const int ipt = (nitems + 255) >> 8;
+      const int per_tap = (ipt + ntaps - 1) / ntaps;
+      BFrag bc, bn;
+      load_b(bc, 0, 0);
+      for (int c = 0; c < nchunks; ++c) {
+        const unsigned char* hsrc = halo_s[c & 1];
+        unsigned char* hdst = halo_s[(c + 1) & 1];
+        const bool hnext = c + 1 < nchunks;
+        for (int t = 0; t < ntaps; ++t) {
+          int cn = c, tn = t + 1;
+          if (tn == ntaps) { tn = 0; cn = c + 1; }
+          if (cn < nchunks) load_b(bn, cn, tn);
+          uint4 hr[kMaxHaloItemsPerTap];
+          const int j0 = t * per_tap;
+          if (hnext) {
+#pragma unroll
+            for (int k = 0; k < kMaxHaloItemsPerTap; ++k)
+              if (k < per_tap) hr[k] = load_item(tid + 256 * (j0 + k), c + 1);
+          }
+          const int dt = t / (K2 * K2);
+          const int a2 = (t / K2) % K2;
+          const int b2 = t % K2;
+          const int dy = S.KS == 2 ? py + a2 : a2;
+          const int dx = S.KS == 2 ? px + b2 : b2;
+          mma_tap(hsrc, ((dt * HY + dy) * HX + dx) * ROWB, bc);
+          if (hnext) {
+#pragma unroll
+            for (int k = 0; k < kMaxHaloItemsPerTap; ++k)
+              if (k < per_tap) store_item(tid + 256 * (j0 + k), c + 1, hr[k], hdst);
+          }
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) bc[j][ks] = bn[j][ks];
+        }
+        __syncthreads();
+      }
     }
   }
 
@@ -275,7 +325,7 @@ __global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
   // out as 16-byte vectors along the channel axis.
   constexpr int CPL = WN / 2;          // channels per lane in the store phase
   constexpr int EROW = WN + 4;         // padded LDS row (floats)
-  __syncthreads();                     // all waves are done with the halo / weight tiles
+  __syncthreads();                     // all waves are done with the halo tiles
   float* ep = reinterpret_cast<float*>(smem) + wave * 32 * EROW;
   const int er = lane >> 1;            // row of the block this lane stores
   const int ec0 = (lane & 1) * CPL;    // first column of the block this lane stores
@@ -291,8 +341,8 @@ __global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
     const int m = wave_m * WM + 32 * i + er;
     const int tx = m & (kTileW - 1);
     const int t2 = m / kTileW;
-    const int f = f0 + t2 / a.TH, y = y0 + t2 % a.TH, x = x0 + tx;
-    const int nb = n0 + wave_n * WN + ec0;  // first output channel of this lane
+    const int f = f0 + t2 / TH, y = y0 + t2 % TH, x = x0 + tx;
+    const int nb = ncol0 + ec0;  // first output channel of this lane
     if (f < a.F && y < a.H && x < a.W && nb < a.Cout) {
       const long long pix = (long long)y * a.W + x;
       const float* row = ep + er * EROW + ec0;
@@ -356,11 +406,11 @@ __global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
   }
 }
 
-template <int BK, int BN, int WAVES_N>
+template <int BK, int BN, int WAVES_N, bool K333>
 hipError_t launch_impl(const ConvArgs& a, hipStream_t stream) {
   if (g_dry_run) return hipSuccess;
   const size_t lds = conv_lds_bytes(a);
-  auto kern = conv_igemm<BK, BN, WAVES_N>;
+  auto kern = conv_igemm<BK, BN, WAVES_N, K333>;
   static size_t attr_bytes = 0;
   if (lds > attr_bytes) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -376,18 +426,27 @@ hipError_t launch_impl(const ConvArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+int conv_bk(const ConvArgs& a) {
+  for (int s = 0; s < a.nseg; ++s)
+    if (a.seg[s].Cin % 32) return 16;
+  return 32;
+}
+
 }  // namespace
 
+bool conv_is_333(const ConvArgs& a) {
+  const ConvSeg& g = a.seg[0];
+  return g.KT == 3 && g.KS == 3 && a.TF == kTF333 && a.TH == kTH333 && a.Cout > 32 && conv_bk(a) == 32 &&
+         a.nphase == 1 && g.wfrag;
+}
+
 size_t conv_lds_bytes(const ConvArgs& a) {
-  int bk = 32;
-  for (int s = 0; s < a.nseg; ++s)
-    if (a.seg[s].Cin % 32) bk = 16;
+  const int bk = conv_bk(a);
   const int bn = a.Cout <= 32 ? 32 : 128;
   int cin_max = 0;
   for (int s = 0; s < a.nseg; ++s)
     if (a.seg[s].prologue != PRO_RAW && a.seg[s].Cin > cin_max) cin_max = a.seg[s].Cin;
-  const size_t main_loop = (size_t)2 * a.nhv_max * bk * 2 + (size_t)2 * bn * bk * 2 + (size_t)a.nhv_max * (8 + 4) +
-                           (size_t)cin_max * 4;
+  const size_t main_loop = (size_t)2 * a.nhv_max * (bk * 2 + 16) + (size_t)a.nhv_max * (8 + 4) + (size_t)cin_max * 4;
   const int wn = bn == 32 ? 32 : 64;  // wave tile width of the instantiation
   const size_t epilogue = (size_t)4 * 32 * (wn + 4) * 4;
   return main_loop > epilogue ? main_loop : epilogue;
@@ -399,10 +458,7 @@ const char* conv_check(const ConvArgs& a) {
   if (a.F < 1 || a.H < 1 || a.W < 1 || a.Cout < 1) return "empty output grid";
   if (a.nphase != 1 && a.nphase != 4) return "phase count";
   if (conv_lds_bytes(a) > 160 * 1024) return "LDS over 160 KiB";
-  // One BK for all segments: 16 when any segment's Cin is not a multiple of 32.
-  int bk = 32;
-  for (int s = 0; s < a.nseg; ++s)
-    if (a.seg[s].Cin % 32) bk = 16;
+  const int bk = conv_bk(a);
   for (int s = 0; s < a.nseg; ++s) {
     const ConvSeg& g = a.seg[s];
     const int hs = g.KS == 1 ? 0 : 1;
@@ -417,10 +473,12 @@ const char* conv_check(const ConvArgs& a) {
     if (nhv > a.nhv_max) return "halo larger than nhv_max";
     if ((ipt + ntaps - 1) / ntaps > kMaxHaloItemsPerTap) return "halo items per tap over the register budget";
     if (g.Cin < 16 || g.Cin % 16) return "Cin must be a positive multiple of 16";
-    if (g.lda % 8 || g.ldw % 8 || g.lda < g.Cin) return "row strides must be multiples of 8 and >= Cin";
+    if (g.lda % 8 || g.lda < g.Cin) return "input row stride must be a multiple of 8 and >= Cin";
+    if (!g.wfrag && (g.ldw % 8 || g.ldw < g.Cin)) return "row-major operand stride";
     if (g.prologue != PRO_RAW && (g.Cin > kMaxCin || !g.rs || !g.gamma)) return "norm prologue operands";
     if (g.n_hist < 0 || g.n_hist > 2 || (g.n_hist > 0 && (!g.ring || g.KT != 3))) return "history ring";
-    if (g.w_frame_stride && a.TF != 1) return "per-frame weights need TF == 1";
+    if (g.w_frame_stride && a.TF != 1) return "per-frame operands need TF == 1";
+    if (s > 0 && (g.KT != 1 || g.KS != 1)) return "second segment must be 1x1x1";
   }
   if (!a.out) return "null output";
   return nullptr;
@@ -428,14 +486,13 @@ const char* conv_check(const ConvArgs& a) {
 
 hipError_t launch_conv(const ConvArgs& a, hipStream_t stream) {
   if (conv_check(a)) return hipErrorInvalidValue;
-  bool bk16 = false;
-  for (int s = 0; s < a.nseg; ++s)
-    if (a.seg[s].Cin % 32) bk16 = true;
+  const bool bk16 = conv_bk(a) == 16;
   const bool small_n = a.Cout <= 32;
-  if (!bk16 && !small_n) return launch_impl<32, 128, 2>(a, stream);
-  if (!bk16 && small_n) return launch_impl<32, 32, 1>(a, stream);
-  if (bk16 && !small_n) return launch_impl<16, 128, 2>(a, stream);
-  return launch_impl<16, 32, 1>(a, stream);
+  if (conv_is_333(a)) return launch_impl<32, 128, 2, true>(a, stream);
+  if (!bk16 && !small_n) return launch_impl<32, 128, 2, false>(a, stream);
+  if (!bk16 && small_n) return launch_impl<32, 32, 1, false>(a, stream);
+  if (bk16 && !small_n) return launch_impl<16, 128, 2, false>(a, stream);
+  return launch_impl<16, 32, 1, false>(a, stream);
 }
 
 }  // namespace wvd

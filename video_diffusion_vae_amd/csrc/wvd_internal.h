@@ -30,7 +30,7 @@ struct ConvSeg {
   const h16_t* ring;        // [2][H][W][Cin] previous input frames (raw) or null
   const float* rs;          // [2+F][H][W] per-voxel 1/||x|| (slot 2+f = frame f)
   const float* gamma;       // [Cin] gamma * sqrt(Cin) (norm prologues)
-  const h16_t* w;           // [taps][rows][ldw] fp16, K contiguous
+  const h16_t* w;           // wfrag: prepared fragment-major weights; else row-major [rows][ldw]
   long long x_fstride;      // elements per input frame
   long long w_tap_stride;   // elements per tap
   long long w_frame_stride; // per-frame weight offset (attention GEMMs), else 0
@@ -39,6 +39,7 @@ struct ConvSeg {
   int KS;                   // spatial taps: 1 (1x1), 3 (3x3, pad 1), 2 (2x2 phase)
   int n_hist;               // valid history frames in ring (0..2)
   int prologue;             // Prologue
+  int wfrag;                // 1: w is in MFMA fragment order (see launch_prep_frag)
 };
 
 struct ConvArgs {
@@ -74,6 +75,8 @@ const char* conv_check(const ConvArgs& a);
 hipError_t launch_conv(const ConvArgs& a, hipStream_t stream);
 // LDS bytes the launch of `a` needs (host-side check).
 size_t conv_lds_bytes(const ConvArgs& a);
+// Whether `a` runs on the specialised 3x3x3 kernel.
+bool conv_is_333(const ConvArgs& a);
 
 // Auxiliary kernels (wvd_aux.hip).
 hipError_t launch_rms_stats(const h16_t* x, long long x_fstride, int lda, const h16_t* ring,
@@ -85,10 +88,18 @@ hipError_t launch_copy16(void* dst, const void* src, size_t bytes, hipStream_t s
 hipError_t launch_softmax_rows(const float* S, int rows, int L, int Lpad, h16_t* P, hipStream_t s);
 hipError_t launch_transpose_v(const h16_t* qkv, int F, int L, int C, int Lpad, h16_t* vt, hipStream_t s);
 // Prepare-time kernels.
-// Weights arrive as bf16 or fp32 (dtype); conv weights leave as fp16, vectors as fp32.
-hipError_t launch_prep_permute(const void* w, int dtype, int cout, int cin, int taps, int cin_pad, h16_t* out,
-                               hipStream_t s);
-hipError_t launch_prep_phase(const void* w, int dtype, int C, h16_t* out, hipStream_t s);
+// Weights arrive as bf16 or fp32 (dtype); conv weights leave as fp16 in MFMA
+// fragment order, vectors as fp32.  Fragment order: for output-channel block
+// nb (32 channels), input-channel block u (16 channels) and tap t, one block
+// of 512 halves at ((nb * U + u) * taps + t) * 512 in which lane l holds, at
+// l * 8 .. l * 8 + 7, W[t][nb*32 + l%32][u*16 + (l/32)*8 + 0..7] (zero
+// outside cout x cin).  U = cin_pad / 16; bytes = ceil(cout/32)*32*cin_pad*taps*2.
+size_t prep_frag_bytes(int cout, int cin_pad, int taps);
+hipError_t launch_prep_frag(const void* w, int dtype, int cout, int cin, int taps, int cin_pad, h16_t* out,
+                            hipStream_t s);
+// Up-conv phase weights in the same fragment order with taps = 16
+// (phase * 4 + 2x2 tap).
+hipError_t launch_prep_phase_frag(const void* w, int dtype, int C, h16_t* out, hipStream_t s);
 hipError_t launch_prep_vec(const void* v, int dtype, int n, float scale, float* out, hipStream_t s);
 // out[i] = a[i] + b[i] in fp32 (the two biases of a block with a shortcut).
 hipError_t launch_prep_vec_add(const void* a, const void* b, int dtype, int n, float* out, hipStream_t s);
