@@ -48,6 +48,8 @@ struct Layout {
   int attn_norm, qkv_w, qkv_b, proj_w, proj_b;
   int tc_w[2], tc_b[2], upc_w[3], upc_b[3];
   int head_norm, head_w, head_b;
+  size_t zero_off = 0;
+  int zero_len = 0;
   size_t total = 0;
 };
 
@@ -77,7 +79,9 @@ RB add_rb(Layout& L, int cin, int cout) {
   return r;
 }
 
-Layout make_layout(int c) {
+int lpad_of(int L);
+
+Layout make_layout(int c, int h, int w) {
   Layout L;
   const int c4 = 4 * c;
   const int widths[4] = {c4, c4, 2 * c, c};
@@ -109,6 +113,11 @@ Layout make_layout(int c) {
     it.off = off;
     off = align_up(off + it.bytes);
   }
+  // fp16 zeros: the source of padding voxels; as long as the widest
+  // reduction of any conv (the attention P.V contraction runs over h*w keys).
+  L.zero_off = off;
+  L.zero_len = std::max(kMaxCin, lpad_of(h * w));
+  off = align_up(off + (size_t)L.zero_len * 2);
   L.total = off;
   return L;
 }
@@ -238,6 +247,7 @@ struct Ctx {
   T* prep(int item) const { return reinterpret_cast<T*>(plan->prep + plan->L.items[item].off); }
   template <typename T>
   T* wsp(size_t off) const { return reinterpret_cast<T*>(ws + off); }
+  long long wbytes(int item) const { return (long long)plan->L.items[item].bytes; }
 
   hipEvent_t ev() {
     if (plan->pool_used == plan->pool.size()) {
@@ -267,7 +277,7 @@ struct Ctx {
 };
 
 ConvSeg seg_basic(const h16_t* x, long long x_fstride, int lda, int Cin, const h16_t* w, int ldw,
-                  long long tap_stride, int KT, int KS) {
+                  long long tap_stride, int KT, int KS, long long w_bytes = 0) {
   ConvSeg s;
   std::memset(&s, 0, sizeof(s));
   s.x = x;
@@ -281,6 +291,7 @@ ConvSeg seg_basic(const h16_t* x, long long x_fstride, int lda, int Cin, const h
   s.KS = KS;
   s.prologue = PRO_RAW;
   s.wfrag = 1;
+  s.w_bytes = w_bytes;
   return s;
 }
 
@@ -294,13 +305,19 @@ void set_grid(ConvArgs& a, int F, int H, int W, int TF) {
   a.tiles_y = (H + a.TH - 1) / a.TH;
   a.tiles_f = (F + TF - 1) / TF;
   if (a.nphase == 0) a.nphase = 1;
-  int nhv = 0;
+  // Halo rows per LDS buffer: every segment's halo, rounded up so that whole
+  // rounds of 256 16-byte items land on real (or spare) rows.
+  int np = 4;
+  for (int s = 0; s < a.nseg; ++s)
+    if (a.seg[s].Cin % 32) np = 2;
+  int rows = 0;
   for (int s = 0; s < a.nseg; ++s) {
     const ConvSeg& g = a.seg[s];
     const int hs = g.KS == 1 ? 0 : 1;
-    nhv = std::max(nhv, (TF + g.KT - 1) * (a.TH + 2 * hs) * (kTileW + 2 * hs));
+    const int nhv = (TF + g.KT - 1) * (a.TH + 2 * hs) * (kTileW + 2 * hs);
+    rows = std::max(rows, (nhv * np + 255) / 256 * 256 / np);
   }
-  a.nhv_max = nhv;
+  a.nhv_max = rows;
 }
 
 ConvArgs args_init() {
@@ -323,6 +340,8 @@ double conv_flops(const ConvArgs& a) {
 }
 
 void conv(Ctx& cx, ConvArgs& a, int cls) {
+  a.zero_row = reinterpret_cast<const h16_t*>(cx.plan->prep + cx.plan->L.zero_off);
+  a.zero_len = cx.plan->L.zero_len;
   const char* why = conv_check(a);
   if (why && cx.err == hipSuccess) {
     cx.err = hipErrorInvalidValue;
@@ -363,7 +382,8 @@ int tf_for(int KT, int F) {
 ConvArgs conv333(Ctx& cx, const Act& x, h16_t* ring, int nh, int gamma_item, int w_item, int b_item, int Cout) {
   ConvArgs a = args_init();
   ConvSeg& s = a.seg[0];
-  s = seg_basic(x.p, x.fstride(), x.C, x.C, cx.prep<h16_t>(w_item), x.C, (long long)Cout * x.C, 3, 3);
+  s = seg_basic(x.p, x.fstride(), x.C, x.C, cx.prep<h16_t>(w_item), x.C, (long long)Cout * x.C, 3, 3,
+                cx.wbytes(w_item));
   s.ring = ring;
   s.n_hist = nh;
   s.rs = cx.wsp<float>(cx.W->rs);
@@ -402,7 +422,7 @@ Act resblock(Ctx& cx, const RB& rb, const Act& x, h16_t* hbuf, h16_t* obuf, int 
     } else {
       // 1x1x1 shortcut over the raw block input as a second K segment; its
       // bias is pre-summed with conv2's into the shortcut bias slot.
-      a.seg[1] = seg_basic(x.p, x.fstride(), x.C, x.C, cx.prep<h16_t>(rb.scw), x.C, 0, 1, 1);
+      a.seg[1] = seg_basic(x.p, x.fstride(), x.C, x.C, cx.prep<h16_t>(rb.scw), x.C, 0, 1, 1, cx.wbytes(rb.scw));
       a.nseg = 2;
       a.bias = cx.prep<float>(rb.scb);
     }
@@ -428,7 +448,7 @@ void attention(Ctx& cx, const Act& x) {
   stats(cx, x, nullptr, 0);
   {  // qkv = Wqkv RMSNorm(x) + b
     ConvArgs a = args_init();
-    a.seg[0] = seg_basic(x.p, x.fstride(), C, C, cx.prep<h16_t>(L.qkv_w), C, 0, 1, 1);
+    a.seg[0] = seg_basic(x.p, x.fstride(), C, C, cx.prep<h16_t>(L.qkv_w), C, 0, 1, 1, cx.wbytes(L.qkv_w));
     a.seg[0].rs = cx.wsp<float>(cx.W->rs);
     a.seg[0].gamma = cx.prep<float>(L.attn_norm);
     a.seg[0].prologue = PRO_NORM;
@@ -475,7 +495,7 @@ void attention(Ctx& cx, const Act& x) {
   }
   {  // x += Wp O + bp
     ConvArgs a = args_init();
-    a.seg[0] = seg_basic(O, (long long)Lt * C, C, C, cx.prep<h16_t>(L.proj_w), C, 0, 1, 1);
+    a.seg[0] = seg_basic(O, (long long)Lt * C, C, C, cx.prep<h16_t>(L.proj_w), C, 0, 1, 1, cx.wbytes(L.proj_w));
     a.nseg = 1;
     a.Cout = C;
     a.bias = cx.prep<float>(L.proj_b);
@@ -504,7 +524,8 @@ Act time_upsample(Ctx& cx, int s, const Act& x, int g, h16_t* ybuf, int ring_id)
   if (sx.F == 0) return y;
   const int nh = std::min(2, std::max(0, g - 1));
   ConvArgs a = args_init();
-  a.seg[0] = seg_basic(sx.p, sx.fstride(), sx.C, sx.C, cx.prep<h16_t>(L.tc_w[s]), sx.C, 2LL * sx.C * sx.C, 3, 1);
+  a.seg[0] = seg_basic(sx.p, sx.fstride(), sx.C, sx.C, cx.prep<h16_t>(L.tc_w[s]), sx.C, 2LL * sx.C * sx.C, 3, 1,
+                       cx.wbytes(L.tc_w[s]));
   a.seg[0].ring = ring;
   a.seg[0].n_hist = nh;
   a.nseg = 1;
@@ -526,7 +547,8 @@ Act up_conv(Ctx& cx, int s, const Act& x, h16_t* ybuf) {
   const Layout& L = cx.plan->L;
   Act y{ybuf, x.C, x.F, 2 * x.H, 2 * x.W};
   ConvArgs a = args_init();
-  a.seg[0] = seg_basic(x.p, x.fstride(), x.C, x.C, cx.prep<h16_t>(L.upc_w[s]), x.C, (long long)x.C * x.C, 1, 2);
+  a.seg[0] = seg_basic(x.p, x.fstride(), x.C, x.C, cx.prep<h16_t>(L.upc_w[s]), x.C, (long long)x.C * x.C, 1, 2,
+                       cx.wbytes(L.upc_w[s]));
   a.nseg = 1;
   a.nphase = 4;
   a.Cout = x.C;
@@ -560,7 +582,7 @@ int wvd_prepared_bytes(int c, int h, int w, size_t* bytes) {
   if (!bytes) return WVD_EINVAL;
   int st = check_dims(c, h, w);
   if (st) return st;
-  *bytes = make_layout(c).total;
+  *bytes = make_layout(c, h, w).total;
   return WVD_OK;
 }
 
@@ -574,7 +596,7 @@ int wvd_prepare(int c, int h, int w, const void* const* weights, int n_weights, 
   for (int i = 0; i < n_weights; ++i)
     if (!weights[i]) return WVD_EINVAL;
   if (!aligned16(prepared)) return WVD_EINVAL;
-  Layout L = make_layout(c);
+  Layout L = make_layout(c, h, w);
   if ((int)L.items.size() != WVD_NUM_WEIGHTS) return WVD_EINVAL;
   if (prepared_bytes < L.total) return WVD_ENOSPACE;
   wvd_plan* p = new (std::nothrow) wvd_plan();
@@ -597,6 +619,7 @@ int wvd_prepare(int c, int h, int w, const void* const* weights, int n_weights, 
     else
       e = launch_prep_vec(src, weight_dtype, it.n, it.scale, static_cast<float*>(dst), s);
   }
+  if (e == hipSuccess) e = launch_fill_zero(p->prep + L.zero_off, align_up((size_t)L.zero_len * 2), s);
   // Blocks with a shortcut add two biases; keep their sum in the shortcut slot.
   const RB* sc_blocks[2] = {&L.up[2][0], &L.up[3][0]};
   for (const RB* rb : sc_blocks) {
@@ -657,7 +680,8 @@ int wvd_decode(const wvd_plan* cplan, const void* z, int z_dtype, int T, int fra
     {
       h16_t* ring = cx.wsp<h16_t>(W.ring[R_CONV_IN]);
       ConvArgs a = args_init();
-      a.seg[0] = seg_basic(zt, za.fstride(), 64, 64, cx.prep<h16_t>(L.conv_in_w), 64, (long long)c4 * 64, 3, 3);
+      a.seg[0] = seg_basic(zt, za.fstride(), 64, 64, cx.prep<h16_t>(L.conv_in_w), 64, (long long)c4 * 64, 3, 3,
+                           cx.wbytes(L.conv_in_w));
       a.seg[0].ring = ring;
       a.seg[0].n_hist = nh0;
       a.nseg = 1;

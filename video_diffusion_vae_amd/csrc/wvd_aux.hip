@@ -104,6 +104,12 @@ __global__ __launch_bounds__(256) void copy16_kernel(uint4* __restrict__ dst, co
     dst[e] = src[e];
 }
 
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint4* __restrict__ dst, long long n) {
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+       e += (long long)gridDim.x * blockDim.x)
+    dst[e] = make_uint4(0, 0, 0, 0);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
   return v;
@@ -157,7 +163,7 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const h16_t* __restric
 // layout w[o][i][tap] (taps flattened).
 __global__ void prep_frag_kernel(const void* __restrict__ w, int dtype, int cout, int cin, int taps, int cin_pad,
                                  h16_t* __restrict__ out) {
-  const int NB = (cout + 31) / 32, U = cin_pad / 16;
+  const int NB = (cout + 127) / 128 * 4, U = cin_pad / 16;
   const long long n = (long long)NB * U * taps * 512;
   for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n;
        e += (long long)gridDim.x * blockDim.x) {
@@ -180,7 +186,7 @@ __global__ void prep_frag_kernel(const void* __restrict__ w, int dtype, int cout
 // columns).  Sums in fp32, rounded once to fp16; fragment order with
 // tap = phase * 4 + a * 2 + b.
 __global__ void prep_phase_frag_kernel(const void* __restrict__ w, int dtype, int C, h16_t* __restrict__ out) {
-  const int NB = (C + 31) / 32, U = C / 16;
+  const int NB = (C + 127) / 128 * 4, U = C / 16;
   const long long n = (long long)NB * U * 16 * 512;
   for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n;
        e += (long long)gridDim.x * blockDim.x) {
@@ -264,6 +270,13 @@ hipError_t launch_copy16(void* dst, const void* src, size_t bytes, hipStream_t s
   return hipGetLastError();
 }
 
+hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t s) {
+  if (g_dry_run) return hipSuccess;
+  const long long n = (long long)(bytes / 16);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(n, 256, 16384)), dim3(256), 0, s, static_cast<uint4*>(dst), n);
+  return hipGetLastError();
+}
+
 hipError_t launch_softmax_rows(const float* S, int rows, int L, int Lpad, h16_t* P, hipStream_t s) {
   if (g_dry_run) return hipSuccess;
   hipLaunchKernelGGL(softmax_rows_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, S, rows, L, Lpad, P);
@@ -278,7 +291,7 @@ hipError_t launch_transpose_v(const h16_t* qkv, int F, int L, int C, int Lpad, h
 }
 
 size_t prep_frag_bytes(int cout, int cin_pad, int taps) {
-  return (size_t)((cout + 31) / 32) * 32 * cin_pad * taps * 2;
+  return (size_t)((cout + 127) / 128) * 128 * cin_pad * taps * 2;
 }
 
 hipError_t launch_prep_frag(const void* w, int dtype, int cout, int cin, int taps, int cin_pad, h16_t* out,

@@ -48,17 +48,209 @@ constexpr int kNHV333 = kHF333 * kHY333 * kHX;  // 720 halo voxels
 
 __device__ __forceinline__ f16x8_t ld_frag(const h16_t* p) { return *reinterpret_cast<const f16x8_t*>(p); }
 
-template <int BK, int BN, int WAVES_N, bool K333>
+// 16-byte load through the global address space.  Halo pointers come from an
+// LDS table, so the compiler cannot infer their address space; a generic
+// (flat) load would also count against the LDS wait counter and serialise the
+// fragment reads behind HBM latency.
+__device__ __forceinline__ uint4 ld_global16(const void* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  const v4u v = *(const __attribute__((address_space(1))) v4u*)(reinterpret_cast<uintptr_t>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return *static_cast<const uint4*>(p);
+#endif
+}
+
+// Per-segment state shared by the tap loops.
+template <int BK, int MI, int NJ>
+struct SegCtx {
+  static constexpr int NP = BK / 8;
+  static constexpr int ROWB = BK * 2 + 16;
+  static constexpr int KS = BK / 16;
+  unsigned char* halo0;  // halo buffer b at halo0 + b * halo_bytes
+  int halo_bytes;
+  const h16_t* const* vptr;
+  const float* rs;
+  const float* gamma;
+  int abase[MI];         // LDS byte address of each A row at tap (0,0,0), k16 step 0
+  int bvoff[NJ];         // buffer offset of this lane's B fragments (fragment order)
+  __amdgpu_buffer_rsrc_t wrsrc;
+  int wtaps, tap0;       // taps per (n32, k16) block and this phase's first tap
+  int tid;
+};
+
+// One halo item (row idx / NP, 16-byte part idx % NP) of chunk `chunk`.
+template <int BK, int MI, int NJ>
+__device__ __forceinline__ uint4 halo_load(const SegCtx<BK, MI, NJ>& g, int idx, int chunk) {
+  constexpr int NP = BK / 8;
+  return ld_global16(g.vptr[idx / NP] + chunk * BK + (idx % NP) * 8);
+}
+
+template <int BK, int MI, int NJ, bool NORM, bool ACT>
+__device__ __forceinline__ void halo_store(const SegCtx<BK, MI, NJ>& g, int idx, int chunk, uint4 r,
+                                           unsigned char* hbuf) {
+  constexpr int NP = BK / 8;
+  constexpr int ROWB = BK * 2 + 16;
+  const int v = idx / NP;
+  const int p = idx % NP;
+  if constexpr (NORM) {
+    float f[8];
+    unpack8h(r, f);
+    const float sc = g.rs[v];
+    const float* gm = g.gamma + chunk * BK + p * 8;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float t = f[k] * sc * gm[k];
+      f[k] = ACT ? t * __builtin_amdgcn_rcpf(1.0f + __expf(-t)) : t;
+    }
+    r = pack8h(f);
+  }
+  *reinterpret_cast<uint4*>(hbuf + v * ROWB + 16 * p) = r;
+}
+
+// B fragments of (chunk, tap) from fragment-order weights.
+template <int BK, int MI, int NJ>
+__device__ __forceinline__ void load_b_frag(const SegCtx<BK, MI, NJ>& g, f16x8_t (&b)[NJ][BK / 16], int chunk,
+                                            int tap) {
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int soff = ((chunk * (BK / 16) + ks) * g.wtaps + g.tap0 + tap) * 1024;
+      b[j][ks] = __builtin_bit_cast(f16x8_t, __builtin_amdgcn_raw_buffer_load_b128(g.wrsrc, g.bvoff[j], soff, 0));
+    }
+}
+
+template <int BK, int MI, int NJ>
+__device__ __forceinline__ void mma_tap(const SegCtx<BK, MI, NJ>& g, f32x16_t (&acc)[MI][NJ],
+                                        const unsigned char* hsrc, int toff_bytes,
+                                        const f16x8_t (&b)[NJ][BK / 16]) {
+#pragma unroll
+  for (int ks = 0; ks < BK / 16; ++ks) {
+    f16x8_t av[MI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+      av[i] = *reinterpret_cast<const f16x8_t*>(hsrc + g.abase[i] + toff_bytes + ks * 32);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], b[j][ks], acc[i][j], 0, 0, 0);
+  }
+}
+
+// 3x3x3 segment over a 2 x 8 x 16 tile: 9 (dt, dy) groups of 3 dx taps per
+// chunk.  B fragments of tap t live in slot t % 3 == dx and are refilled
+// with tap t + 3 right after use; halo item t of the next chunk is loaded at
+// tap t and normalised into LDS at tap t + 3 from slot dx.  Everything that
+// selects code is a compile-time constant here.
+template <int BK, int MI, int NJ, bool NORM, bool ACT>
+__device__ __forceinline__ void run_333(const SegCtx<BK, MI, NJ>& g, f32x16_t (&acc)[MI][NJ], int nchunks) {
+  constexpr int NP = BK / 8;
+  constexpr int ROWB = BK * 2 + 16;
+  constexpr int IPT = (kNHV333 * NP + 255) / 256;  // halo items per thread per chunk
+  static_assert(IPT + 3 <= 27, "halo items must land inside a chunk");
+  f16x8_t bq[3][NJ][BK / 16];
+#pragma unroll
+  for (int t = 0; t < 3; ++t) load_b_frag(g, bq[t], 0, t);
+  for (int c = 0; c < nchunks; ++c) {
+    const unsigned char* hsrc = g.halo0 + (c & 1) * g.halo_bytes;
+    unsigned char* hdst = g.halo0 + ((c + 1) & 1) * g.halo_bytes;
+    const bool hnext = c + 1 < nchunks;
+    uint4 hr[3];
+    for (int gi = 0; gi < 9; ++gi) {
+      const int goff = ((gi / 3) * kHY333 + (gi % 3)) * kHX * ROWB;
+#pragma unroll
+      for (int dx = 0; dx < 3; ++dx) {
+        const int t = 3 * gi + dx;
+        if (hnext) {
+          if (t >= 3 && t - 3 < IPT) halo_store<BK, MI, NJ, NORM, ACT>(g, g.tid + 256 * (t - 3), c + 1, hr[dx], hdst);
+          if (t < IPT) hr[dx] = halo_load(g, g.tid + 256 * t, c + 1);
+        }
+        mma_tap(g, acc, hsrc, goff + dx * ROWB, bq[dx]);
+        const int tn = t + 3;
+        if (tn < 27) {
+          load_b_frag(g, bq[dx], c, tn);
+        } else if (hnext) {
+          load_b_frag(g, bq[dx], c + 1, tn - 27);
+        }
+      }
+    }
+    __syncthreads();  // next chunk's halo complete; this chunk's reads done
+  }
+}
+
+// Any tap set (KT x K2 x K2, phases), B one tap ahead, halo items spread over
+// the taps.  B comes from fragment-order weights (WFRAG) or from a row-major
+// operand read with plain loads.
+template <int BK, int MI, int NJ, bool NORM, bool ACT, bool WFRAG>
+__device__ __forceinline__ void run_generic(const SegCtx<BK, MI, NJ>& g, f32x16_t (&acc)[MI][NJ], int nchunks,
+                                            int ntaps, int KT, int K2, int KSm, int HY, int HX, int py, int px,
+                                            int nitems, const h16_t* const (&bsrc)[NJ], const bool (&bok)[NJ]) {
+  constexpr int ROWB = BK * 2 + 16;
+  constexpr int KS = BK / 16;
+  const int ipt = (nitems + 255) >> 8;
+  const int per_tap = (ipt + ntaps - 1) / ntaps;
+  auto load_b = [&](f16x8_t (&b)[NJ][KS], int chunk, int tap) {
+    if constexpr (WFRAG) {
+      load_b_frag(g, b, chunk, tap);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) b[j][ks] = bok[j] ? ld_frag(bsrc[j] + chunk * BK + ks * 16) : f16x8_t{};
+    }
+  };
+  f16x8_t bc[NJ][KS], bn[NJ][KS];
+  load_b(bc, 0, 0);
+  for (int c = 0; c < nchunks; ++c) {
+    const unsigned char* hsrc = g.halo0 + (c & 1) * g.halo_bytes;
+    unsigned char* hdst = g.halo0 + ((c + 1) & 1) * g.halo_bytes;
+    const bool hnext = c + 1 < nchunks;
+    for (int t = 0; t < ntaps; ++t) {
+      int cn = c, tn = t + 1;
+      if (tn == ntaps) { tn = 0; cn = c + 1; }
+      if (cn < nchunks) load_b(bn, cn, tn);
+      uint4 hr[kMaxHaloItemsPerTap];
+      const int j0 = t * per_tap;
+      if (hnext) {
+#pragma unroll
+        for (int k = 0; k < kMaxHaloItemsPerTap; ++k)
+          if (k < per_tap && j0 + k < ipt) hr[k] = halo_load(g, g.tid + 256 * (j0 + k), c + 1);
+      }
+      const int dt = t / (K2 * K2);
+      const int a2 = (t / K2) % K2;
+      const int b2 = t % K2;
+      const int dy = KSm == 2 ? py + a2 : a2;
+      const int dx = KSm == 2 ? px + b2 : b2;
+      mma_tap(g, acc, hsrc, ((dt * HY + dy) * HX + dx) * ROWB, bc);
+      if (hnext) {
+#pragma unroll
+        for (int k = 0; k < kMaxHaloItemsPerTap; ++k)
+          if (k < per_tap && j0 + k < ipt)
+            halo_store<BK, MI, NJ, NORM, ACT>(g, g.tid + 256 * (j0 + k), c + 1, hr[k], hdst);
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) bc[j][ks] = bn[j][ks];
+    }
+    __syncthreads();
+  }
+}
+
+// PRO0: prologue of segment 0 fixed at compile time (PRO_RAW, PRO_NORM,
+// PRO_NORM_SILU) or -1 to take it from the arguments.
+template <int BK, int BN, int WAVES_N, bool K333, int PRO0>
 __global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
   constexpr int NP = BK / 8;            // 16-byte parts per voxel row
   constexpr int ROWB = BK * 2 + 16;     // padded LDS row (bytes)
-  constexpr int KS = BK / 16;           // k16 steps per chunk
   constexpr int WAVES_M = 4 / WAVES_N;
   constexpr int WM = kTileM / WAVES_M;
   constexpr int WN = BN / WAVES_N;
   constexpr int MI = WM / 32;
   constexpr int NJ = WN / 32;
-  typedef f16x8_t BFrag[NJ][KS];
 
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x;
@@ -69,7 +261,6 @@ __global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
 
   // ---- LDS carve-up: two halo buffers, then the per-voxel tables ----
   const int halo_bytes = a.nhv_max * ROWB;
-  unsigned char* halo_s[2] = {smem, smem + halo_bytes};
   const h16_t** vptr_s = reinterpret_cast<const h16_t**>(smem + 2 * halo_bytes);
   float* rs_s = reinterpret_cast<float*>(vptr_s + a.nhv_max);
   float* gamma_s = rs_s + a.nhv_max;
@@ -120,30 +311,37 @@ __global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
     const int nhv = HF * HY * HX;
     const int ntaps = KT * K2 * K2;
     const int nchunks = S.Cin / BK;
-    const int nitems = nhv * NP;
-    const bool norm = S.prologue != PRO_RAW;
-    const bool act = S.prologue == PRO_NORM_SILU;
+    const int pro = (PRO0 >= 0 && s == 0) ? PRO0 : S.prologue;
+    const bool norm = pro != PRO_RAW;
 
     __syncthreads();  // the previous segment (or tile setup) is done with LDS
-    // Per-halo-voxel source pointer (null = zero padding) and norm scale.
-    for (int v = tid; v < nhv; v += 256) {
-      const int hx = v % HX;
-      const int t2 = v / HX;
-      const int hy = t2 % HY;
-      const int hf = t2 / HY;
-      const int fo = f0 + hf - (KT - 1);
-      const int y = y0 + hy - hs;
-      const int x = x0 + hx - hs;
-      const h16_t* p = nullptr;
+    // Per-halo-row source pointer and norm scale.  Padding voxels and the
+    // spare rows past the halo read the zero row with scale 0, so the item
+    // loops need no per-lane branches.
+    for (int v = tid; v < a.nhv_max; v += 256) {
+      const h16_t* p = a.zero_row;
       float rsv = 0.0f;
-      if (y >= 0 && y < a.H && x >= 0 && x < a.W && fo < a.F) {
-        const long long pix = (long long)y * a.W + x;
-        if (fo >= 0) {
-          p = S.x + fo * S.x_fstride + pix * S.lda;
-        } else if (fo + 2 >= 2 - S.n_hist) {
-          p = S.ring + (long long)(fo + 2) * HW * S.Cin + pix * S.Cin;
+      if (v < nhv) {
+        const int hx = v % HX;
+        const int t2 = v / HX;
+        const int hy = t2 % HY;
+        const int hf = t2 / HY;
+        const int fo = f0 + hf - (KT - 1);
+        const int y = y0 + hy - hs;
+        const int x = x0 + hx - hs;
+        if (y >= 0 && y < a.H && x >= 0 && x < a.W && fo < a.F) {
+          const long long pix = (long long)y * a.W + x;
+          const h16_t* q = nullptr;
+          if (fo >= 0) {
+            q = S.x + fo * S.x_fstride + pix * S.lda;
+          } else if (fo + 2 >= 2 - S.n_hist) {
+            q = S.ring + (long long)(fo + 2) * HW * S.Cin + pix * S.Cin;
+          }
+          if (q) {
+            p = q;
+            if (norm) rsv = S.rs[(long long)(fo + 2) * HW + pix];
+          }
         }
-        if (p && norm) rsv = S.rs[(long long)(fo + 2) * HW + pix];
       }
       vptr_s[v] = p;
       rs_s[v] = rsv;
@@ -152,169 +350,71 @@ __global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
       for (int c = tid; c < S.Cin; c += 256) gamma_s[c] = S.gamma[c];
     __syncthreads();
 
-    // Byte address (halo buffer relative) of each A row this lane feeds at
-    // tap (0,0,0) and k16 step 0.
-    int abase[MI];
+    SegCtx<BK, MI, NJ> g;
+    g.halo0 = smem;
+    g.halo_bytes = halo_bytes;
+    g.vptr = vptr_s;
+    g.rs = rs_s;
+    g.gamma = gamma_s;
+    g.tid = tid;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
       const int m = wave_m * WM + 32 * i + lrow;
       const int tx = m & (kTileW - 1);
       const int t2 = m / kTileW;
-      abase[i] = (((t2 / TH) * HY + (t2 % TH)) * HX + tx) * ROWB + kpart * 16;
+      g.abase[i] = (((t2 / TH) * HY + (t2 % TH)) * HX + tx) * ROWB + kpart * 16;
     }
-
-    auto load_item = [&](int idx, int chunk) -> uint4 {
-      uint4 r = make_uint4(0, 0, 0, 0);
-      if (idx < nitems) {
-        const h16_t* p = vptr_s[idx / NP];
-        if (p) r = *reinterpret_cast<const uint4*>(p + chunk * BK + (idx % NP) * 8);
-      }
-      return r;
-    };
-    auto store_item = [&](int idx, int chunk, uint4 r, unsigned char* hbuf) {
-      if (idx >= nitems) return;
-      const int v = idx / NP;
-      const int p = idx % NP;
-      if (norm) {
-        float f[8];
-        unpack8h(r, f);
-        const float sc = rs_s[v];
-        const float* g = gamma_s + chunk * BK + p * 8;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float t = f[k] * sc * g[k];
-          f[k] = act ? t * __builtin_amdgcn_rcpf(1.0f + __expf(-t)) : t;
-        }
-        r = pack8h(f);
-      }
-      *reinterpret_cast<uint4*>(hbuf + v * ROWB + 16 * p) = r;
-    };
-
-    // B fragment source.  Fragment-major weights: block (n32, k16, tap) of
-    // 512 halves, lane l at l*8.  Row-major operands: row n, column k.
     const int U = S.Cin / 16;
-    const int wtaps = a.nphase * ntaps;
+    g.wtaps = a.nphase * ntaps;
+    g.tap0 = ph * ntaps;
+    g.wrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<h16_t*>(S.w), 0, (int)S.w_bytes, 0x00020000);
     const h16_t* bsrc[NJ];
     bool bok[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      if (S.wfrag) {
-        const int nb = ncol0 / 32 + j;
-        bok[j] = nb * 32 < a.Cout;
-        bsrc[j] = S.w + ((long long)nb * U * wtaps + ph * ntaps) * 512 + lane * 8;
-      } else {
-        const int n = ncol0 + 32 * j + lrow;
-        bok[j] = n < a.Cout;
-        bsrc[j] = S.w + (long long)f0 * S.w_frame_stride + (long long)n * S.ldw + kpart * 8;
-      }
+      const int nb = ncol0 / 32 + j;
+      g.bvoff[j] = (nb * U * g.wtaps) * 1024 + lane * 16;
+      const int n = ncol0 + 32 * j + lrow;
+      bok[j] = n < a.Cout;
+      bsrc[j] = S.w + (long long)f0 * S.w_frame_stride + (long long)n * S.ldw + kpart * 8;
     }
-    auto load_b = [&](BFrag& b, int chunk, int tap) {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          if (bok[j]) {
-            const long long off = S.wfrag ? ((long long)(chunk * KS + ks) * wtaps + tap) * 512
-                                          : (long long)chunk * BK + ks * 16;
-            b[j][ks] = ld_frag(bsrc[j] + off);
-          } else {
-            b[j][ks] = f16x8_t{};
-          }
-        }
-    };
-    auto mma_tap = [&](const unsigned char* hsrc, int toff_bytes, const BFrag& b) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        f16x8_t av[MI];
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-          av[i] = *reinterpret_cast<const f16x8_t*>(hsrc + abase[i] + toff_bytes + ks * 32);
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-          for (int j = 0; j < NJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], b[j][ks], acc[i][j], 0, 0, 0);
-      }
-    };
 
-    // Chunk 0 halo, synchronously.
-    for (int idx = tid; idx < nitems; idx += 256) store_item(idx, 0, load_item(idx, 0), halo_s[0]);
+    // Chunk 0 halo, synchronously (all rows, spare ones included).
+    const int rows_items = a.nhv_max * NP;
+    if (pro == PRO_NORM_SILU) {
+      for (int idx = tid; idx < rows_items; idx += 256)
+        halo_store<BK, MI, NJ, true, true>(g, idx, 0, halo_load(g, idx, 0), g.halo0);
+    } else if (pro == PRO_NORM) {
+      for (int idx = tid; idx < rows_items; idx += 256)
+        halo_store<BK, MI, NJ, true, false>(g, idx, 0, halo_load(g, idx, 0), g.halo0);
+    } else {
+      for (int idx = tid; idx < rows_items; idx += 256)
+        halo_store<BK, MI, NJ, false, false>(g, idx, 0, halo_load(g, idx, 0), g.halo0);
+    }
     __syncthreads();
 
-    if (spec) {
-      // ---- 3x3x3: 9 (dt, dy) groups of 3 dx taps per chunk ----
-      // B fragments of tap t live in slot t % 3 == dx and are refilled with
-      // tap t + 3 right after use.  Halo item t of the next chunk is loaded
-      // at tap t and normalised into LDS at tap t + 3 from slot dx.
-      constexpr int IPT = (kNHV333 * NP + 255) / 256;  // halo items per thread per chunk
-      static_assert(IPT + 3 <= 27, "halo items must land inside a chunk");
-      BFrag bq[3];
-#pragma unroll
-      for (int t = 0; t < 3; ++t) load_b(bq[t], 0, t);
-      for (int c = 0; c < nchunks; ++c) {
-        const unsigned char* hsrc = halo_s[c & 1];
-        unsigned char* hdst = halo_s[(c + 1) & 1];
-        const bool hnext = c + 1 < nchunks;
-        uint4 hr[3];
-        for (int g = 0; g < 9; ++g) {
-          const int goff = ((g / 3) * kHY333 + (g % 3)) * kHX * ROWB;
-#pragma unroll
-          for (int dx = 0; dx < 3; ++dx) {
-            const int t = 3 * g + dx;
-            if (hnext) {
-              if (t >= 3 && t - 3 < IPT) store_item(tid + 256 * (t - 3), c + 1, hr[dx], hdst);
-              if (t < IPT) hr[dx] = load_item(tid + 256 * t, c + 1);
-            }
-            mma_tap(hsrc, goff + dx * ROWB, bq[dx]);
-            const int tn = t + 3;
-            if (tn < 27) {
-              load_b(bq[dx], c, tn);
-            } else if (hnext) {
-              load_b(bq[dx], c + 1, tn - 27);
-            }
-          }
-        }
-        __syncthreads();  // next chunk's halo complete; this chunk's reads done
+    if constexpr (K333) {
+      if (s == 0) {
+        constexpr bool kNorm = PRO0 == PRO_NORM || PRO0 == PRO_NORM_SILU;
+        constexpr bool kAct = PRO0 == PRO_NORM_SILU;
+        run_333<BK, MI, NJ, kNorm, kAct>(g, acc, nchunks);
+        continue;
       }
+    }
+    const int nitems = nhv * NP;
+    if (S.wfrag) {
+      if (pro == PRO_NORM_SILU)
+        run_generic<BK, MI, NJ, true, true, true>(g, acc, nchunks, ntaps, KT, K2, S.KS, HY, HX, py, px, nitems,
+                                                   bsrc, bok);
+      else if (pro == PRO_NORM)
+        run_generic<BK, MI, NJ, true, false, true>(g, acc, nchunks, ntaps, KT, K2, S.KS, HY, HX, py, px, nitems,
+                                                    bsrc, bok);
+      else
+        run_generic<BK, MI, NJ, false, false, true>(g, acc, nchunks, ntaps, KT, K2, S.KS, HY, HX, py, px, nitems,
+                                                     bsrc, bok);
     } else {
-      // ---- generic taps: B one tap ahead, halo items spread over taps ----
-      const int ipt = (nitems + 255) >> 8;
-      const int per_tap = (ipt + ntaps - 1) / ntaps;
-      BFrag bc, bn;
-      load_b(bc, 0, 0);
-      for (int c = 0; c < nchunks; ++c) {
-        const unsigned char* hsrc = halo_s[c & 1];
-        unsigned char* hdst = halo_s[(c + 1) & 1];
-        const bool hnext = c + 1 < nchunks;
-        for (int t = 0; t < ntaps; ++t) {
-          int cn = c, tn = t + 1;
-          if (tn == ntaps) { tn = 0; cn = c + 1; }
-          if (cn < nchunks) load_b(bn, cn, tn);
-          uint4 hr[kMaxHaloItemsPerTap];
-          const int j0 = t * per_tap;
-          if (hnext) {
-#pragma unroll
-            for (int k = 0; k < kMaxHaloItemsPerTap; ++k)
-              if (k < per_tap) hr[k] = load_item(tid + 256 * (j0 + k), c + 1);
-          }
-          const int dt = t / (K2 * K2);
-          const int a2 = (t / K2) % K2;
-          const int b2 = t % K2;
-          const int dy = S.KS == 2 ? py + a2 : a2;
-          const int dx = S.KS == 2 ? px + b2 : b2;
-          mma_tap(hsrc, ((dt * HY + dy) * HX + dx) * ROWB, bc);
-          if (hnext) {
-#pragma unroll
-            for (int k = 0; k < kMaxHaloItemsPerTap; ++k)
-              if (k < per_tap) store_item(tid + 256 * (j0 + k), c + 1, hr[k], hdst);
-          }
-#pragma unroll
-          for (int j = 0; j < NJ; ++j)
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) bc[j][ks] = bn[j][ks];
-        }
-        __syncthreads();
-      }
+      run_generic<BK, MI, NJ, false, false, false>(g, acc, nchunks, ntaps, KT, K2, S.KS, HY, HX, py, px, nitems,
+                                                    bsrc, bok);
     }
   }
 
@@ -406,11 +506,11 @@ __global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
   }
 }
 
-template <int BK, int BN, int WAVES_N, bool K333>
+template <int BK, int BN, int WAVES_N, bool K333, int PRO0>
 hipError_t launch_impl(const ConvArgs& a, hipStream_t stream) {
   if (g_dry_run) return hipSuccess;
   const size_t lds = conv_lds_bytes(a);
-  auto kern = conv_igemm<BK, BN, WAVES_N, K333>;
+  auto kern = conv_igemm<BK, BN, WAVES_N, K333, PRO0>;
   static size_t attr_bytes = 0;
   if (lds > attr_bytes) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -471,8 +571,13 @@ const char* conv_check(const ConvArgs& a) {
     if (g.KS != 1 && g.KS != 2 && g.KS != 3) return "KS must be 1, 2 or 3";
     if ((g.KS == 2) != (a.nphase == 4)) return "phase taps need 4 phases";
     if (nhv > a.nhv_max) return "halo larger than nhv_max";
+    if ((g.KT == 3 && g.KS == 3 && a.TF == kTF333 && a.TH == kTH333 &&
+         ((kNHV333 * (bk / 8) + 255) / 256) * 256 / (bk / 8) > a.nhv_max))
+      return "nhv_max below the 3x3x3 item rows";
+    if (g.wfrag && (g.w_bytes <= 0 || g.w_bytes > 0x7fffffffLL)) return "fragment weights need 0 < bytes < 2 GiB";
     if ((ipt + ntaps - 1) / ntaps > kMaxHaloItemsPerTap) return "halo items per tap over the register budget";
     if (g.Cin < 16 || g.Cin % 16) return "Cin must be a positive multiple of 16";
+    if (g.Cin > a.zero_len) return "zero row shorter than Cin";
     if (g.lda % 8 || g.lda < g.Cin) return "input row stride must be a multiple of 8 and >= Cin";
     if (!g.wfrag && (g.ldw % 8 || g.ldw < g.Cin)) return "row-major operand stride";
     if (g.prologue != PRO_RAW && (g.Cin > kMaxCin || !g.rs || !g.gamma)) return "norm prologue operands";
@@ -480,7 +585,7 @@ const char* conv_check(const ConvArgs& a) {
     if (g.w_frame_stride && a.TF != 1) return "per-frame operands need TF == 1";
     if (s > 0 && (g.KT != 1 || g.KS != 1)) return "second segment must be 1x1x1";
   }
-  if (!a.out) return "null output";
+  if (!a.out || !a.zero_row) return "null output or zero row";
   return nullptr;
 }
 
@@ -488,11 +593,14 @@ hipError_t launch_conv(const ConvArgs& a, hipStream_t stream) {
   if (conv_check(a)) return hipErrorInvalidValue;
   const bool bk16 = conv_bk(a) == 16;
   const bool small_n = a.Cout <= 32;
-  if (conv_is_333(a)) return launch_impl<32, 128, 2, true>(a, stream);
-  if (!bk16 && !small_n) return launch_impl<32, 128, 2, false>(a, stream);
-  if (!bk16 && small_n) return launch_impl<32, 32, 1, false>(a, stream);
-  if (bk16 && !small_n) return launch_impl<16, 128, 2, false>(a, stream);
-  return launch_impl<16, 32, 1, false>(a, stream);
+  if (conv_is_333(a)) {
+    if (a.seg[0].prologue == PRO_NORM_SILU) return launch_impl<32, 128, 2, true, PRO_NORM_SILU>(a, stream);
+    if (a.seg[0].prologue == PRO_RAW) return launch_impl<32, 128, 2, true, PRO_RAW>(a, stream);
+  }
+  if (!bk16 && !small_n) return launch_impl<32, 128, 2, false, -1>(a, stream);
+  if (!bk16 && small_n) return launch_impl<32, 32, 1, false, -1>(a, stream);
+  if (bk16 && !small_n) return launch_impl<16, 128, 2, false, -1>(a, stream);
+  return launch_impl<16, 32, 1, false, -1>(a, stream);
 }
 
 }  // namespace wvd

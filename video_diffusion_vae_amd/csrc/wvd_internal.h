@@ -40,6 +40,7 @@ struct ConvSeg {
   int n_hist;               // valid history frames in ring (0..2)
   int prologue;             // Prologue
   int wfrag;                // 1: w is in MFMA fragment order (see launch_prep_frag)
+  long long w_bytes;        // bytes of w (fragment order: bounds of the buffer loads)
 };
 
 struct ConvArgs {
@@ -61,7 +62,9 @@ struct ConvArgs {
   int epi;
   int out_base;             // EPI_TIME frame base; EPI_VIDEO first frame index
   int video_T;              // EPI_VIDEO total frames of the video
-  int nhv_max;              // largest halo (voxels) over segments: LDS sizing
+  int nhv_max;              // halo rows per LDS buffer (>= every segment's item rows)
+  const h16_t* zero_row;    // zero_len fp16 zeros: source of padding voxels
+  int zero_len;             // >= every segment's Cin
 };
 
 // Host-validation mode: every launcher checks its arguments and returns
@@ -85,6 +88,8 @@ hipError_t launch_ring_update(h16_t* ring, const h16_t* x, long long x_fstride, 
                               int F, int HW, hipStream_t s);
 hipError_t launch_latent_to_cl(const void* z, int dtype, int T, int t0, int F, int HW, h16_t* zt, hipStream_t s);
 hipError_t launch_copy16(void* dst, const void* src, size_t bytes, hipStream_t s);
+// Zero-fills bytes (a multiple of 16) with a kernel (no memset node).
+hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_softmax_rows(const float* S, int rows, int L, int Lpad, h16_t* P, hipStream_t s);
 hipError_t launch_transpose_v(const h16_t* qkv, int F, int L, int C, int Lpad, h16_t* vt, hipStream_t s);
 // Prepare-time kernels.
@@ -93,7 +98,8 @@ hipError_t launch_transpose_v(const h16_t* qkv, int F, int L, int C, int Lpad, h
 // nb (32 channels), input-channel block u (16 channels) and tap t, one block
 // of 512 halves at ((nb * U + u) * taps + t) * 512 in which lane l holds, at
 // l * 8 .. l * 8 + 7, W[t][nb*32 + l%32][u*16 + (l/32)*8 + 0..7] (zero
-// outside cout x cin).  U = cin_pad / 16; bytes = ceil(cout/32)*32*cin_pad*taps*2.
+// outside cout x cin; output channels are padded to a multiple of 128).
+// U = cin_pad / 16; bytes = ceil(cout/128)*128*cin_pad*taps*2.
 size_t prep_frag_bytes(int cout, int cin_pad, int taps);
 hipError_t launch_prep_frag(const void* w, int dtype, int cout, int cin, int taps, int cin_pad, h16_t* out,
                             hipStream_t s);
