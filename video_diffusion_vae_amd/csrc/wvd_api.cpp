@@ -306,7 +306,7 @@ void set_grid(ConvArgs& a, int F, int H, int W, int TF) {
   a.tiles_f = (F + TF - 1) / TF;
   if (a.nphase == 0) a.nphase = 1;
   // Halo rows per LDS buffer: every segment's halo, rounded up so that whole
-  // rounds of 256 16-byte items land on real (or spare) rows.
+  // rounds of 16-byte items (one per thread) land on real (or spare) rows.
   int np = 4;
   for (int s = 0; s < a.nseg; ++s)
     if (a.seg[s].Cin % 32) np = 2;
@@ -315,7 +315,7 @@ void set_grid(ConvArgs& a, int F, int H, int W, int TF) {
     const ConvSeg& g = a.seg[s];
     const int hs = g.KS == 1 ? 0 : 1;
     const int nhv = (TF + g.KT - 1) * (a.TH + 2 * hs) * (kTileW + 2 * hs);
-    rows = std::max(rows, (nhv * np + 255) / 256 * 256 / np);
+    rows = std::max(rows, (nhv * np + 511) / 512 * 512 / np);  // whole rounds for 256 or 512 threads
   }
   a.nhv_max = rows;
 }

@@ -63,8 +63,9 @@ __device__ __forceinline__ uint4 ld_global16(const void* p) {
 }
 
 // Per-segment state shared by the tap loops.
-template <int BK, int MI, int NJ>
+template <int BK, int MI, int NJ, int NT_>
 struct SegCtx {
+  static constexpr int NT = NT_;        // threads per workgroup
   static constexpr int NP = BK / 8;
   static constexpr int ROWB = BK * 2 + 16;
   static constexpr int KS = BK / 16;
@@ -81,17 +82,17 @@ struct SegCtx {
 };
 
 // One halo item (row idx / NP, 16-byte part idx % NP) of chunk `chunk`.
-template <int BK, int MI, int NJ>
-__device__ __forceinline__ uint4 halo_load(const SegCtx<BK, MI, NJ>& g, int idx, int chunk) {
-  constexpr int NP = BK / 8;
-  return ld_global16(g.vptr[idx / NP] + chunk * BK + (idx % NP) * 8);
+template <class G>
+__device__ __forceinline__ uint4 halo_load(const G& g, int idx, int chunk) {
+  constexpr int NP = G::NP;
+  return ld_global16(g.vptr[idx / NP] + chunk * (NP * 8) + (idx % NP) * 8);
 }
 
-template <int BK, int MI, int NJ, bool NORM, bool ACT>
-__device__ __forceinline__ void halo_store(const SegCtx<BK, MI, NJ>& g, int idx, int chunk, uint4 r,
-                                           unsigned char* hbuf) {
-  constexpr int NP = BK / 8;
-  constexpr int ROWB = BK * 2 + 16;
+template <bool NORM, bool ACT, class G>
+__device__ __forceinline__ void halo_store(const G& g, int idx, int chunk, uint4 r, unsigned char* hbuf) {
+  constexpr int NP = G::NP;
+  constexpr int BK = NP * 8;
+  constexpr int ROWB = G::ROWB;
   const int v = idx / NP;
   const int p = idx % NP;
   if constexpr (NORM) {
@@ -110,9 +111,8 @@ __device__ __forceinline__ void halo_store(const SegCtx<BK, MI, NJ>& g, int idx,
 }
 
 // B fragments of (chunk, tap) from fragment-order weights.
-template <int BK, int MI, int NJ>
-__device__ __forceinline__ void load_b_frag(const SegCtx<BK, MI, NJ>& g, f16x8_t (&b)[NJ][BK / 16], int chunk,
-                                            int tap) {
+template <int BK, int NJ, class G>
+__device__ __forceinline__ void load_b_frag(const G& g, f16x8_t (&b)[NJ][BK / 16], int chunk, int tap) {
 #pragma unroll
   for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -122,8 +122,8 @@ __device__ __forceinline__ void load_b_frag(const SegCtx<BK, MI, NJ>& g, f16x8_t
     }
 }
 
-template <int BK, int MI, int NJ>
-__device__ __forceinline__ void mma_tap(const SegCtx<BK, MI, NJ>& g, f32x16_t (&acc)[MI][NJ],
+template <int BK, int MI, int NJ, class G>
+__device__ __forceinline__ void mma_tap(const G& g, f32x16_t (&acc)[MI][NJ],
                                         const unsigned char* hsrc, int toff_bytes,
                                         const f16x8_t (&b)[NJ][BK / 16]) {
 #pragma unroll
@@ -141,19 +141,30 @@ __device__ __forceinline__ void mma_tap(const SegCtx<BK, MI, NJ>& g, f32x16_t (&
 }
 
 // 3x3x3 segment over a 2 x 8 x 16 tile: 9 (dt, dy) groups of 3 dx taps per
-// chunk.  B fragments of tap t live in slot t % 3 == dx and are refilled
-// with tap t + 3 right after use; halo item t of the next chunk is loaded at
-// tap t and normalised into LDS at tap t + 3 from slot dx.  Everything that
-// selects code is a compile-time constant here.
-template <int BK, int MI, int NJ, bool NORM, bool ACT>
-__device__ __forceinline__ void run_333(const SegCtx<BK, MI, NJ>& g, f32x16_t (&acc)[MI][NJ], int nchunks) {
+// chunk, each tap two k16 steps.  B fragments of k16 step u (= 2 * tap + ks)
+// live in slot u % 3 and are refilled with step u + 3 right after use (1.5
+// taps of lookahead in 3 x NJ fragment registers); halo item t of the next
+// chunk is loaded at tap t and normalised into LDS at tap t + 3.  Everything
+// that selects code is a compile-time constant here.
+template <int BK, int MI, int NJ, bool NORM, bool ACT, class G>
+__device__ __forceinline__ void run_333(const G& g, f32x16_t (&acc)[MI][NJ], int nchunks) {
+  static_assert(BK == 32, "the 3x3x3 path runs two k16 steps per tap");
   constexpr int NP = BK / 8;
   constexpr int ROWB = BK * 2 + 16;
-  constexpr int IPT = (kNHV333 * NP + 255) / 256;  // halo items per thread per chunk
+  constexpr int NT = G::NT;
+  constexpr int IPT = (kNHV333 * NP + NT - 1) / NT;  // halo items per thread per chunk
   static_assert(IPT + 3 <= 27, "halo items must land inside a chunk");
-  f16x8_t bq[3][NJ][BK / 16];
+  f16x8_t bq[3][NJ];
+  auto load_step = [&](f16x8_t (&b)[NJ], int chunk, int tap, int ks) {
 #pragma unroll
-  for (int t = 0; t < 3; ++t) load_b_frag(g, bq[t], 0, t);
+    for (int j = 0; j < NJ; ++j) {
+      const int soff = ((chunk * 2 + ks) * g.wtaps + g.tap0 + tap) * 1024;
+      b[j] = __builtin_bit_cast(f16x8_t, __builtin_amdgcn_raw_buffer_load_b128(g.wrsrc, g.bvoff[j], soff, 0));
+    }
+  };
+  load_step(bq[0], 0, 0, 0);
+  load_step(bq[1], 0, 0, 1);
+  load_step(bq[2], 0, 1, 0);
   for (int c = 0; c < nchunks; ++c) {
     const unsigned char* hsrc = g.halo0 + (c & 1) * g.halo_bytes;
     unsigned char* hdst = g.halo0 + ((c + 1) & 1) * g.halo_bytes;
@@ -162,18 +173,31 @@ __device__ __forceinline__ void run_333(const SegCtx<BK, MI, NJ>& g, f32x16_t (&
     for (int gi = 0; gi < 9; ++gi) {
       const int goff = ((gi / 3) * kHY333 + (gi % 3)) * kHX * ROWB;
 #pragma unroll
-      for (int dx = 0; dx < 3; ++dx) {
+      for (int s6 = 0; s6 < 6; ++s6) {
+        const int dx = s6 >> 1, ks = s6 & 1;
         const int t = 3 * gi + dx;
-        if (hnext) {
-          if (t >= 3 && t - 3 < IPT) halo_store<BK, MI, NJ, NORM, ACT>(g, g.tid + 256 * (t - 3), c + 1, hr[dx], hdst);
-          if (t < IPT) hr[dx] = halo_load(g, g.tid + 256 * t, c + 1);
+        if (ks == 0 && hnext) {
+          if (t >= 3 && t - 3 < IPT) halo_store<NORM, ACT>(g, g.tid + NT * (t - 3), c + 1, hr[dx], hdst);
+          if (t < IPT) hr[dx] = halo_load(g, g.tid + NT * t, c + 1);
         }
-        mma_tap(g, acc, hsrc, goff + dx * ROWB, bq[dx]);
-        const int tn = t + 3;
-        if (tn < 27) {
-          load_b_frag(g, bq[dx], c, tn);
+        {
+          f16x8_t av[MI];
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+            av[i] = *reinterpret_cast<const f16x8_t*>(hsrc + g.abase[i] + goff + dx * ROWB + ks * 32);
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bq[s6 % 3][j], acc[i][j], 0, 0, 0);
+        }
+        // refill with k16 step u + 3
+        const int t3 = t + (s6 + 3) / 2 - dx;  // = 3 * gi + (s6 + 3) / 2
+        const int ks3 = (s6 + 1) & 1;
+        if (t3 < 27) {
+          load_step(bq[s6 % 3], c, t3, ks3);
         } else if (hnext) {
-          load_b_frag(g, bq[dx], c + 1, tn - 27);
+          load_step(bq[s6 % 3], c + 1, t3 - 27, ks3);
         }
       }
     }
@@ -181,20 +205,125 @@ __device__ __forceinline__ void run_333(const SegCtx<BK, MI, NJ>& g, f32x16_t (&
   }
 }
 
+// 3x3x3 segment for 8-wave workgroups (two waves per SIMD, 256 registers
+// each): a runtime loop over the 27 taps with the two k16 steps unrolled.  B
+// fragments of step ks of the next tap are refilled into slot ks as soon as
+// the current tap's step ks is issued (one tap of lookahead; the other wave
+// on the SIMD covers the rest), and halo item t of the next chunk is loaded
+// and normalised within tap t.
+template <int BK, int MI, int NJ, bool NORM, bool ACT, class G>
+__device__ __forceinline__ void run_333_lean(const G& g, f32x16_t (&acc)[MI][NJ], int nchunks) {
+  static_assert(BK == 32, "the 3x3x3 path runs two k16 steps per tap");
+  constexpr int NP = BK / 8;
+  constexpr int ROWB = BK * 2 + 16;
+  constexpr int NT = G::NT;
+  constexpr int IPT = (kNHV333 * NP + NT - 1) / NT;  // halo items per thread per chunk
+  static_assert(IPT <= 27, "halo items must land inside a chunk");
+  f16x8_t bq[2][NJ];
+  auto load_step = [&](f16x8_t (&b)[NJ], int chunk, int tap, int ks) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int soff = ((chunk * 2 + ks) * g.wtaps + g.tap0 + tap) * 1024;
+      b[j] = __builtin_bit_cast(f16x8_t, __builtin_amdgcn_raw_buffer_load_b128(g.wrsrc, g.bvoff[j], soff, 0));
+    }
+  };
+  load_step(bq[0], 0, 0, 0);
+  load_step(bq[1], 0, 0, 1);
+  for (int c = 0; c < nchunks; ++c) {
+    const unsigned char* hsrc = g.halo0 + (c & 1) * g.halo_bytes;
+    unsigned char* hdst = g.halo0 + ((c + 1) & 1) * g.halo_bytes;
+    const bool hnext = c + 1 < nchunks;
+    int dt = 0, dy = 0, dx = 0;
+    for (int t = 0; t < 27; ++t) {
+      const int toff = ((dt * kHY333 + dy) * kHX + dx) * ROWB;
+      const bool item = hnext && t < IPT;
+      uint4 hr;
+      if (item) hr = halo_load(g, g.tid + NT * t, c + 1);
+      const int tn = t + 1 < 27 ? t + 1 : 0;
+      const int cn = t + 1 < 27 ? c : c + 1;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        f16x8_t av[MI];
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+          av[i] = *reinterpret_cast<const f16x8_t*>(hsrc + g.abase[i] + toff + ks * 32);
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bq[ks][j], acc[i][j], 0, 0, 0);
+        if (cn < nchunks) load_step(bq[ks], cn, tn, ks);
+      }
+      if (item) halo_store<NORM, ACT>(g, g.tid + NT * t, c + 1, hr, hdst);
+      if (++dx == 3) {
+        dx = 0;
+        if (++dy == 3) {
+          dy = 0;
+          ++dt;
+        }
+      }
+    }
+    __syncthreads();  // next chunk's halo complete; this chunk's reads done
+  }
+}
+
+// 1x1x1 segment over raw input (the shortcut of a block whose width
+// changes) for 8-wave workgroups: per chunk two k16 steps, B one chunk
+// ahead, the next chunk's halo loaded and stored within the chunk.
+template <int BK, int MI, int NJ, class G>
+__device__ __forceinline__ void run_111_lean(const G& g, f32x16_t (&acc)[MI][NJ], int nchunks, int nitems) {
+  static_assert(BK == 32, "two k16 steps per chunk");
+  constexpr int NT = G::NT;
+  const int ipt = (nitems + NT - 1) / NT;
+  f16x8_t bq[2][NJ];
+  auto load_step = [&](f16x8_t (&b)[NJ], int chunk, int ks) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int soff = ((chunk * 2 + ks) * g.wtaps + g.tap0) * 1024;
+      b[j] = __builtin_bit_cast(f16x8_t, __builtin_amdgcn_raw_buffer_load_b128(g.wrsrc, g.bvoff[j], soff, 0));
+    }
+  };
+  load_step(bq[0], 0, 0);
+  load_step(bq[1], 0, 1);
+  for (int c = 0; c < nchunks; ++c) {
+    const unsigned char* hsrc = g.halo0 + (c & 1) * g.halo_bytes;
+    unsigned char* hdst = g.halo0 + ((c + 1) & 1) * g.halo_bytes;
+    const bool hnext = c + 1 < nchunks;
+    for (int k = 0; k < ipt && hnext; ++k) {
+      const int idx = g.tid + NT * k;
+      halo_store<false, false>(g, idx, c + 1, halo_load(g, idx, c + 1), hdst);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      f16x8_t av[MI];
+#pragma unroll
+      for (int i = 0; i < MI; ++i) av[i] = *reinterpret_cast<const f16x8_t*>(hsrc + g.abase[i] + ks * 32);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bq[ks][j], acc[i][j], 0, 0, 0);
+      if (hnext) load_step(bq[ks], c + 1, ks);
+    }
+    __syncthreads();
+  }
+}
+
 // Any tap set (KT x K2 x K2, phases), B one tap ahead, halo items spread over
 // the taps.  B comes from fragment-order weights (WFRAG) or from a row-major
 // operand read with plain loads.
-template <int BK, int MI, int NJ, bool NORM, bool ACT, bool WFRAG>
-__device__ __forceinline__ void run_generic(const SegCtx<BK, MI, NJ>& g, f32x16_t (&acc)[MI][NJ], int nchunks,
+template <int BK, int MI, int NJ, bool NORM, bool ACT, bool WFRAG, class G>
+__device__ __forceinline__ void run_generic(const G& g, f32x16_t (&acc)[MI][NJ], int nchunks,
                                             int ntaps, int KT, int K2, int KSm, int HY, int HX, int py, int px,
                                             int nitems, const h16_t* const (&bsrc)[NJ], const bool (&bok)[NJ]) {
   constexpr int ROWB = BK * 2 + 16;
   constexpr int KS = BK / 16;
-  const int ipt = (nitems + 255) >> 8;
+  constexpr int NT = G::NT;
+  const int ipt = (nitems + NT - 1) / NT;
   const int per_tap = (ipt + ntaps - 1) / ntaps;
   auto load_b = [&](f16x8_t (&b)[NJ][KS], int chunk, int tap) {
     if constexpr (WFRAG) {
-      load_b_frag(g, b, chunk, tap);
+      load_b_frag<BK, NJ>(g, b, chunk, tap);
     } else {
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
@@ -217,19 +346,19 @@ __device__ __forceinline__ void run_generic(const SegCtx<BK, MI, NJ>& g, f32x16_
       if (hnext) {
 #pragma unroll
         for (int k = 0; k < kMaxHaloItemsPerTap; ++k)
-          if (k < per_tap && j0 + k < ipt) hr[k] = halo_load(g, g.tid + 256 * (j0 + k), c + 1);
+          if (k < per_tap && j0 + k < ipt) hr[k] = halo_load(g, g.tid + NT * (j0 + k), c + 1);
       }
       const int dt = t / (K2 * K2);
       const int a2 = (t / K2) % K2;
       const int b2 = t % K2;
       const int dy = KSm == 2 ? py + a2 : a2;
       const int dx = KSm == 2 ? px + b2 : b2;
-      mma_tap(g, acc, hsrc, ((dt * HY + dy) * HX + dx) * ROWB, bc);
+      mma_tap<BK, MI, NJ>(g, acc, hsrc, ((dt * HY + dy) * HX + dx) * ROWB, bc);
       if (hnext) {
 #pragma unroll
         for (int k = 0; k < kMaxHaloItemsPerTap; ++k)
           if (k < per_tap && j0 + k < ipt)
-            halo_store<BK, MI, NJ, NORM, ACT>(g, g.tid + 256 * (j0 + k), c + 1, hr[k], hdst);
+            halo_store<NORM, ACT>(g, g.tid + NT * (j0 + k), c + 1, hr[k], hdst);
       }
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
@@ -242,11 +371,12 @@ __device__ __forceinline__ void run_generic(const SegCtx<BK, MI, NJ>& g, f32x16_
 
 // PRO0: prologue of segment 0 fixed at compile time (PRO_RAW, PRO_NORM,
 // PRO_NORM_SILU) or -1 to take it from the arguments.
-template <int BK, int BN, int WAVES_N, bool K333, int PRO0>
-__global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
+template <int BK, int BN, int WAVES_N, int NW, bool K333, int PRO0>
+__global__ __launch_bounds__(NW * 64) void conv_igemm(ConvArgs a) {
+  constexpr int NT = NW * 64;           // threads per workgroup
   constexpr int NP = BK / 8;            // 16-byte parts per voxel row
   constexpr int ROWB = BK * 2 + 16;     // padded LDS row (bytes)
-  constexpr int WAVES_M = 4 / WAVES_N;
+  constexpr int WAVES_M = NW / WAVES_N;
   constexpr int WM = kTileM / WAVES_M;
   constexpr int WN = BN / WAVES_N;
   constexpr int MI = WM / 32;
@@ -299,7 +429,9 @@ __global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  for (int s = 0; s < a.nseg; ++s) {
+  // Segments run as straight-line code (segment 0, then the optional second
+  // one), so the register allocator sees each tap loop on its own.
+  auto do_segment = [&](const int s) {
     const ConvSeg& S = a.seg[s];
     const bool spec = K333 && s == 0;  // the specialised 3x3x3 segment
     const int KT = spec ? 3 : S.KT;
@@ -318,7 +450,7 @@ __global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
     // Per-halo-row source pointer and norm scale.  Padding voxels and the
     // spare rows past the halo read the zero row with scale 0, so the item
     // loops need no per-lane branches.
-    for (int v = tid; v < a.nhv_max; v += 256) {
+    for (int v = tid; v < a.nhv_max; v += NT) {
       const h16_t* p = a.zero_row;
       float rsv = 0.0f;
       if (v < nhv) {
@@ -347,10 +479,10 @@ __global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
       rs_s[v] = rsv;
     }
     if (norm)
-      for (int c = tid; c < S.Cin; c += 256) gamma_s[c] = S.gamma[c];
+      for (int c = tid; c < S.Cin; c += NT) gamma_s[c] = S.gamma[c];
     __syncthreads();
 
-    SegCtx<BK, MI, NJ> g;
+    SegCtx<BK, MI, NJ, NT> g;
     g.halo0 = smem;
     g.halo_bytes = halo_bytes;
     g.vptr = vptr_s;
@@ -382,14 +514,14 @@ __global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
     // Chunk 0 halo, synchronously (all rows, spare ones included).
     const int rows_items = a.nhv_max * NP;
     if (pro == PRO_NORM_SILU) {
-      for (int idx = tid; idx < rows_items; idx += 256)
-        halo_store<BK, MI, NJ, true, true>(g, idx, 0, halo_load(g, idx, 0), g.halo0);
+      for (int idx = tid; idx < rows_items; idx += NT)
+        halo_store<true, true>(g, idx, 0, halo_load(g, idx, 0), g.halo0);
     } else if (pro == PRO_NORM) {
-      for (int idx = tid; idx < rows_items; idx += 256)
-        halo_store<BK, MI, NJ, true, false>(g, idx, 0, halo_load(g, idx, 0), g.halo0);
+      for (int idx = tid; idx < rows_items; idx += NT)
+        halo_store<true, false>(g, idx, 0, halo_load(g, idx, 0), g.halo0);
     } else {
-      for (int idx = tid; idx < rows_items; idx += 256)
-        halo_store<BK, MI, NJ, false, false>(g, idx, 0, halo_load(g, idx, 0), g.halo0);
+      for (int idx = tid; idx < rows_items; idx += NT)
+        halo_store<false, false>(g, idx, 0, halo_load(g, idx, 0), g.halo0);
     }
     __syncthreads();
 
@@ -397,11 +529,19 @@ __global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
       if (s == 0) {
         constexpr bool kNorm = PRO0 == PRO_NORM || PRO0 == PRO_NORM_SILU;
         constexpr bool kAct = PRO0 == PRO_NORM_SILU;
-        run_333<BK, MI, NJ, kNorm, kAct>(g, acc, nchunks);
-        continue;
+        if constexpr (NW == 8)
+          run_333_lean<BK, MI, NJ, kNorm, kAct>(g, acc, nchunks);
+        else
+          run_333<BK, MI, NJ, kNorm, kAct>(g, acc, nchunks);
+        return;
       }
     }
     const int nitems = nhv * NP;
+    if constexpr (NW == 8) {
+      // the 8-wave kernel's only other segment: a raw 1x1x1 shortcut
+      run_111_lean<BK, MI, NJ>(g, acc, nchunks, nitems);
+      return;
+    }
     if (S.wfrag) {
       if (pro == PRO_NORM_SILU)
         run_generic<BK, MI, NJ, true, true, true>(g, acc, nchunks, ntaps, KT, K2, S.KS, HY, HX, py, px, nitems,
@@ -416,7 +556,9 @@ __global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
       run_generic<BK, MI, NJ, false, false, false>(g, acc, nchunks, ntaps, KT, K2, S.KS, HY, HX, py, px, nitems,
                                                     bsrc, bok);
     }
-  }
+  };
+  do_segment(0);
+  if (a.nseg > 1) do_segment(1);
 
   // ---- epilogue ----
   // Each wave moves one 32-row block of its accumulators at a time through
@@ -506,11 +648,11 @@ __global__ __launch_bounds__(256) void conv_igemm(ConvArgs a) {
   }
 }
 
-template <int BK, int BN, int WAVES_N, bool K333, int PRO0>
+template <int BK, int BN, int WAVES_N, int NW, bool K333, int PRO0>
 hipError_t launch_impl(const ConvArgs& a, hipStream_t stream) {
   if (g_dry_run) return hipSuccess;
   const size_t lds = conv_lds_bytes(a);
-  auto kern = conv_igemm<BK, BN, WAVES_N, K333, PRO0>;
+  auto kern = conv_igemm<BK, BN, WAVES_N, NW, K333, PRO0>;
   static size_t attr_bytes = 0;
   if (lds > attr_bytes) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -522,7 +664,7 @@ hipError_t launch_impl(const ConvArgs& a, hipStream_t stream) {
   const int nN = (a.Cout + BN - 1) / BN;
   const long long total = (long long)nM * nN * a.nphase;
   if (total <= 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3((unsigned)total), dim3(256), lds, stream, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)total), dim3(NW * 64), lds, stream, a);
   return hipGetLastError();
 }
 
@@ -532,23 +674,43 @@ int conv_bk(const ConvArgs& a) {
   return 32;
 }
 
-}  // namespace
+// Kernel variant a launch runs on.
+struct Variant {
+  int bk, bn, nw;
+  bool k333;
+};
 
-bool conv_is_333(const ConvArgs& a) {
+Variant conv_variant(const ConvArgs& a) {
   const ConvSeg& g = a.seg[0];
-  return g.KT == 3 && g.KS == 3 && a.TF == kTF333 && a.TH == kTH333 && a.Cout > 32 && conv_bk(a) == 32 &&
-         a.nphase == 1 && g.wfrag;
+  Variant v;
+  v.bk = conv_bk(a);
+  v.k333 = g.KT == 3 && g.KS == 3 && a.TF == kTF333 && a.TH == kTH333 && a.Cout > 32 && v.bk == 32 &&
+           a.nphase == 1 && g.wfrag && (g.prologue == PRO_NORM_SILU || g.prologue == PRO_RAW);
+  const bool shortcut_ok = a.nseg == 1 || (a.seg[1].KT == 1 && a.seg[1].KS == 1 && a.seg[1].prologue == PRO_RAW &&
+                                            a.seg[1].wfrag && a.seg[1].Cin % 32 == 0);
+  if (v.k333 && a.Cout % 256 == 0 && shortcut_ok) {
+    v.bn = 256;
+    v.nw = 8;
+  } else {
+    v.bn = a.Cout <= 32 ? 32 : 128;
+    v.nw = 4;
+  }
+  return v;
 }
 
+}  // namespace
+
+bool conv_is_333(const ConvArgs& a) { return conv_variant(a).k333; }
+
 size_t conv_lds_bytes(const ConvArgs& a) {
-  const int bk = conv_bk(a);
-  const int bn = a.Cout <= 32 ? 32 : 128;
+  const Variant v = conv_variant(a);
   int cin_max = 0;
   for (int s = 0; s < a.nseg; ++s)
     if (a.seg[s].prologue != PRO_RAW && a.seg[s].Cin > cin_max) cin_max = a.seg[s].Cin;
-  const size_t main_loop = (size_t)2 * a.nhv_max * (bk * 2 + 16) + (size_t)a.nhv_max * (8 + 4) + (size_t)cin_max * 4;
-  const int wn = bn == 32 ? 32 : 64;  // wave tile width of the instantiation
-  const size_t epilogue = (size_t)4 * 32 * (wn + 4) * 4;
+  const size_t main_loop =
+      (size_t)2 * a.nhv_max * (v.bk * 2 + 16) + (size_t)a.nhv_max * (8 + 4) + (size_t)cin_max * 4;
+  const int wn = v.bn == 32 ? 32 : 64;  // wave tile width of the instantiation
+  const size_t epilogue = (size_t)v.nw * 32 * (wn + 4) * 4;
   return main_loop > epilogue ? main_loop : epilogue;
 }
 
@@ -564,7 +726,8 @@ const char* conv_check(const ConvArgs& a) {
     const int hs = g.KS == 1 ? 0 : 1;
     const int k2 = g.KS == 3 ? 3 : (g.KS == 2 ? 2 : 1);
     const int nhv = (a.TF + g.KT - 1) * (a.TH + 2 * hs) * (kTileW + 2 * hs);
-    const int ipt = (nhv * (bk / 8) + 255) / 256;
+    const int nt = conv_variant(a).nw * 64;
+    const int ipt = (nhv * (bk / 8) + nt - 1) / nt;
     const int ntaps = g.KT * k2 * k2;
     if (!g.x || !g.w) return "null operand";
     if (g.KT != 1 && g.KT != 3) return "KT must be 1 or 3";
@@ -572,7 +735,7 @@ const char* conv_check(const ConvArgs& a) {
     if ((g.KS == 2) != (a.nphase == 4)) return "phase taps need 4 phases";
     if (nhv > a.nhv_max) return "halo larger than nhv_max";
     if ((g.KT == 3 && g.KS == 3 && a.TF == kTF333 && a.TH == kTH333 &&
-         ((kNHV333 * (bk / 8) + 255) / 256) * 256 / (bk / 8) > a.nhv_max))
+         ((kNHV333 * (bk / 8) + 511) / 512) * 512 / (bk / 8) > a.nhv_max))
       return "nhv_max below the 3x3x3 item rows";
     if (g.wfrag && (g.w_bytes <= 0 || g.w_bytes > 0x7fffffffLL)) return "fragment weights need 0 < bytes < 2 GiB";
     if ((ipt + ntaps - 1) / ntaps > kMaxHaloItemsPerTap) return "halo items per tap over the register budget";
@@ -591,16 +754,19 @@ const char* conv_check(const ConvArgs& a) {
 
 hipError_t launch_conv(const ConvArgs& a, hipStream_t stream) {
   if (conv_check(a)) return hipErrorInvalidValue;
-  const bool bk16 = conv_bk(a) == 16;
-  const bool small_n = a.Cout <= 32;
-  if (conv_is_333(a)) {
-    if (a.seg[0].prologue == PRO_NORM_SILU) return launch_impl<32, 128, 2, true, PRO_NORM_SILU>(a, stream);
-    if (a.seg[0].prologue == PRO_RAW) return launch_impl<32, 128, 2, true, PRO_RAW>(a, stream);
+  const Variant v = conv_variant(a);
+  if (v.k333) {
+    const bool act = a.seg[0].prologue == PRO_NORM_SILU;
+    if (v.nw == 8)
+      return act ? launch_impl<32, 256, 4, 8, true, PRO_NORM_SILU>(a, stream)
+                 : launch_impl<32, 256, 4, 8, true, PRO_RAW>(a, stream);
+    return act ? launch_impl<32, 128, 2, 4, true, PRO_NORM_SILU>(a, stream)
+               : launch_impl<32, 128, 2, 4, true, PRO_RAW>(a, stream);
   }
-  if (!bk16 && !small_n) return launch_impl<32, 128, 2, false, -1>(a, stream);
-  if (!bk16 && small_n) return launch_impl<32, 32, 1, false, -1>(a, stream);
-  if (bk16 && !small_n) return launch_impl<16, 128, 2, false, -1>(a, stream);
-  return launch_impl<16, 32, 1, false, -1>(a, stream);
+  if (v.bk == 32 && v.bn == 128) return launch_impl<32, 128, 2, 4, false, -1>(a, stream);
+  if (v.bk == 32 && v.bn == 32) return launch_impl<32, 32, 1, 4, false, -1>(a, stream);
+  if (v.bk == 16 && v.bn == 128) return launch_impl<16, 128, 2, 4, false, -1>(a, stream);
+  return launch_impl<16, 32, 1, 4, false, -1>(a, stream);
 }
 
 }  // namespace wvd
