@@ -1,0 +1,85 @@
+"""The c=256 decoder at 704x1248 (latents 44x78), in the launch configuration
+the benchmark times (frames_per_pass=4 unless swept).
+
+* Elementwise parity at full size: by causality the first video frame of any
+  clip is the decode of its first latent frame, which the oracle computes in
+  full (1 x 3 x 704 x 1248 outputs); the GPU's first frame of the 13- and
+  49-latent-frame decodes must match it within the tolerances.
+* Properties that hold at any size, bit-exact on the device: identical video
+  for frames_per_pass 2, 4, 8 and 16 on the 121-latent-frame clip, and the
+  first 49 frames of the 49-frame clip equal to the 13-latent-frame decode
+  (causal prefix); every element finite and in [-1, 1].
+"""
+import numpy as np
+import pytest
+
+from tests.gpu_util import gpu_available, oracle_video, rel_l2
+from video_diffusion_vae_amd import synth
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+MAX_ABS = 3e-2
+REL_L2 = 1e-2
+
+
+@pytest.fixture(scope="module")
+def dec():
+    import torch
+
+    from video_diffusion_vae_amd import wvd
+    cfg = synth.config_by_name("c256_T49_704x1248")
+    W = synth.make_weights(cfg.c, seed=0)
+    d = wvd.Decoder({k: torch.from_numpy(v).to(torch.bfloat16) for k, v in W.items()}, cfg.c, cfg.h, cfg.w)
+    yield d
+    d.release_workspace()
+    torch.cuda.empty_cache()
+
+
+def decode(dec, T, P):
+    import torch
+    z = torch.from_numpy(synth.make_latents(T, 44, 78, seed=0)).cuda().to(torch.bfloat16)
+    out = dec.decode(z, frames_per_pass=P)
+    torch.cuda.synchronize()
+    return out
+
+
+def check_range(out):
+    import torch
+    assert bool(torch.isfinite(out).all()) and float(out.abs().max()) <= 1.0
+
+
+def test_first_frame_matches_oracle(dec):
+    ref = oracle_video(synth.config_by_name("c256_T13_704x1248"), seed=0, T=1)  # [1,3,1,704,1248]
+    for T in (13, 49):
+        print(f"case full-size first frame T={T} P=4", flush=True)
+        out = decode(dec, T, 4)
+        check_range(out)
+        got = out[:, :, :1].float().cpu().numpy()
+        d = np.abs(got.astype(np.float64) - ref)
+        r = rel_l2(got, ref)
+        print(f"T={T}: max_abs={d.max():.3e} rel_l2={r:.3e}", flush=True)
+        assert d.max() <= MAX_ABS and r <= REL_L2
+        del out
+
+
+def test_causal_prefix_bit_identical(dec):
+    import torch
+    print("case full-size causal prefix T=13 vs T=49", flush=True)
+    short = decode(dec, 13, 4)
+    full = decode(dec, 49, 4)
+    assert full.shape[2] == 193 and short.shape[2] == 49
+    assert torch.equal(full[:, :, :49], short)
+
+
+def test_frames_per_pass_sweep_bit_identical(dec):
+    import torch
+    print("case full-size T=121 P=4", flush=True)
+    ref = decode(dec, 121, 4)
+    check_range(ref)
+    for P in (2, 8, 16):
+        print(f"case full-size T=121 P={P}", flush=True)
+        dec.release_workspace()
+        torch.cuda.empty_cache()
+        out = decode(dec, 121, P)
+        assert torch.equal(out, ref), f"P={P}"
+        del out
