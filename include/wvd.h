@@ -118,14 +118,18 @@ void wvd_set_dry_run(int on);
  * dry-run mode); -1 for a null plan. */
 long long wvd_last_launch_count(const wvd_plan* plan);
 
-/* Enables (1) or disables (0) per-kernel HIP-event timing of wvd_decode's
- * launches on the plan; wvd_profile_read then returns, per kernel class
- * (0 conv 3x3x3, 1 conv other, 2 attention, 3 norm statistics, 4 copies),
- * the summed milliseconds and algorithmic FLOPs of the last decode.  The
- * timing synchronises the stream at the end of wvd_decode.  Returns
- * WVD_EINVAL on a null plan. */
+/* Enables (1) or disables (0) HIP-event timing of every kernel wvd_decode
+ * launches on the plan (events recorded on the decode's stream around each
+ * launch).  wvd_profile_read synchronises on the last recorded event and
+ * returns, per kernel class, the summed milliseconds, the summed algorithmic
+ * FLOPs (2 per multiply-add of the contraction each launch performs) and the
+ * number of launches since the previous read, then clears the record.
+ * Classes: 0 the dominant conv kernel (3x3x3, fused RMSNorm+SiLU prologue,
+ * 8-wave 256x256 tiles), 1 other convs (conv_in, head, time_conv, up-conv,
+ * 1x1), 2 attention GEMMs, 3 RMS statistics, 4 copies / layout / softmax.
+ * Profiling is not thread-safe.  WVD_EINVAL on a null plan or array. */
 int wvd_profile_enable(wvd_plan* plan, int on);
-int wvd_profile_read(const wvd_plan* plan, double* ms, double* flops, int n_classes);
+int wvd_profile_read(const wvd_plan* plan, double* ms, double* flops, long long* launches, int n_classes);
 
 #ifdef __cplusplus
 }

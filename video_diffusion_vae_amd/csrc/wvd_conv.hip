@@ -529,10 +529,7 @@ __global__ __launch_bounds__(NW * 64) void conv_igemm(ConvArgs a) {
       if (s == 0) {
         constexpr bool kNorm = PRO0 == PRO_NORM || PRO0 == PRO_NORM_SILU;
         constexpr bool kAct = PRO0 == PRO_NORM_SILU;
-        if constexpr (NW == 8)
-          run_333_lean<BK, MI, NJ, kNorm, kAct>(g, acc, nchunks);
-        else
-          run_333<BK, MI, NJ, kNorm, kAct>(g, acc, nchunks);
+        run_333<BK, MI, NJ, kNorm, kAct>(g, acc, nchunks);
         return;
       }
     }
@@ -701,6 +698,11 @@ Variant conv_variant(const ConvArgs& a) {
 }  // namespace
 
 bool conv_is_333(const ConvArgs& a) { return conv_variant(a).k333; }
+
+bool conv_is_main(const ConvArgs& a) {
+  const Variant v = conv_variant(a);
+  return v.k333 && v.nw == 8 && a.seg[0].prologue == PRO_NORM_SILU;
+}
 
 size_t conv_lds_bytes(const ConvArgs& a) {
   const Variant v = conv_variant(a);

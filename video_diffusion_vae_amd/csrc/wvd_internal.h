@@ -80,6 +80,9 @@ hipError_t launch_conv(const ConvArgs& a, hipStream_t stream);
 size_t conv_lds_bytes(const ConvArgs& a);
 // Whether `a` runs on the specialised 3x3x3 kernel.
 bool conv_is_333(const ConvArgs& a);
+// Whether `a` runs on the dominant instantiation: 8-wave 3x3x3 with the fused
+// RMSNorm+SiLU prologue (every ResBlock conv of width >= 256).
+bool conv_is_main(const ConvArgs& a);
 
 // Auxiliary kernels (wvd_aux.hip).
 hipError_t launch_rms_stats(const h16_t* x, long long x_fstride, int lda, const h16_t* ring,

@@ -22,7 +22,7 @@ WVD_EHIP = -5
 NUM_WEIGHTS = 84
 WVD_DTYPE_BF16 = 0
 WVD_DTYPE_F32 = 1
-PROFILE_CLASSES = ("conv3x3x3", "conv_other", "attention_gemm", "norm_stats", "copies")
+PROFILE_CLASSES = ("conv3x3x3_main", "conv_other", "attention_gemm", "norm_stats", "copies")
 
 
 class WvdError(RuntimeError):
@@ -61,7 +61,8 @@ def _load() -> ctypes.CDLL:
     lib.wvd_last_launch_count.restype = ctypes.c_longlong
     lib.wvd_profile_enable.argtypes = [vp, i]
     lib.wvd_profile_enable.restype = i
-    lib.wvd_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), i]
+    lib.wvd_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_longlong), i]
     lib.wvd_profile_read.restype = i
     return lib
 
@@ -131,8 +132,9 @@ def wvd_profile_read(plan: int) -> Dict[str, Dict[str, float]]:
     n = len(PROFILE_CLASSES)
     ms = (ctypes.c_double * n)()
     fl = (ctypes.c_double * n)()
-    _check(_lib.wvd_profile_read(plan, ms, fl, n), "wvd_profile_read")
-    return {k: {"ms": ms[i], "flops": fl[i]} for i, k in enumerate(PROFILE_CLASSES)}
+    cnt = (ctypes.c_longlong * n)()
+    _check(_lib.wvd_profile_read(plan, ms, fl, cnt, n), "wvd_profile_read")
+    return {k: {"ms": ms[i], "flops": fl[i], "launches": int(cnt[i])} for i, k in enumerate(PROFILE_CLASSES)}
 
 
 # ---- torch-facing wrapper ----
