@@ -34,6 +34,10 @@
 // norms and norm_out, statistics in fp32 (Wan2.2 page, "Limits").
 #include "wvd_internal.h"
 
+#ifndef WVD_BRING
+#define WVD_BRING 6
+#endif
+
 namespace wvd {
 
 namespace {
@@ -45,6 +49,7 @@ constexpr int kHX = kTileW + 2;
 constexpr int kHY333 = kTH333 + 2;
 constexpr int kHF333 = kTF333 + 2;
 constexpr int kNHV333 = kHF333 * kHY333 * kHX;  // 720 halo voxels
+constexpr int kBRing = WVD_BRING;              // k16 steps of B fragments in flight
 
 __device__ __forceinline__ f16x8_t ld_frag(const h16_t* p) { return *reinterpret_cast<const f16x8_t*>(p); }
 
@@ -146,15 +151,16 @@ __device__ __forceinline__ void mma_tap(const G& g, f32x16_t (&acc)[MI][NJ],
 // taps of lookahead in 3 x NJ fragment registers); halo item t of the next
 // chunk is loaded at tap t and normalised into LDS at tap t + 3.  Everything
 // that selects code is a compile-time constant here.
-template <int BK, int MI, int NJ, bool NORM, bool ACT, class G>
+template <int BK, int MI, int NJ, bool NORM, bool ACT, int DEPTH, class G>
 __device__ __forceinline__ void run_333(const G& g, f32x16_t (&acc)[MI][NJ], int nchunks) {
   static_assert(BK == 32, "the 3x3x3 path runs two k16 steps per tap");
+  static_assert(DEPTH == 3 || DEPTH == 6, "the B ring must divide the 6 k16 steps of a dx group");
   constexpr int NP = BK / 8;
   constexpr int ROWB = BK * 2 + 16;
   constexpr int NT = G::NT;
   constexpr int IPT = (kNHV333 * NP + NT - 1) / NT;  // halo items per thread per chunk
   static_assert(IPT + 3 <= 27, "halo items must land inside a chunk");
-  f16x8_t bq[3][NJ];
+  f16x8_t bq[DEPTH][NJ];
   auto load_step = [&](f16x8_t (&b)[NJ], int chunk, int tap, int ks) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
@@ -162,9 +168,8 @@ __device__ __forceinline__ void run_333(const G& g, f32x16_t (&acc)[MI][NJ], int
       b[j] = __builtin_bit_cast(f16x8_t, __builtin_amdgcn_raw_buffer_load_b128(g.wrsrc, g.bvoff[j], soff, 0));
     }
   };
-  load_step(bq[0], 0, 0, 0);
-  load_step(bq[1], 0, 0, 1);
-  load_step(bq[2], 0, 1, 0);
+#pragma unroll
+  for (int u = 0; u < DEPTH; ++u) load_step(bq[u], 0, u >> 1, u & 1);
   for (int c = 0; c < nchunks; ++c) {
     const unsigned char* hsrc = g.halo0 + (c & 1) * g.halo_bytes;
     unsigned char* hdst = g.halo0 + ((c + 1) & 1) * g.halo_bytes;
@@ -189,15 +194,15 @@ __device__ __forceinline__ void run_333(const G& g, f32x16_t (&acc)[MI][NJ], int
           for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bq[s6 % 3][j], acc[i][j], 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bq[s6 % DEPTH][j], acc[i][j], 0, 0, 0);
         }
-        // refill with k16 step u + 3
-        const int t3 = t + (s6 + 3) / 2 - dx;  // = 3 * gi + (s6 + 3) / 2
-        const int ks3 = (s6 + 1) & 1;
+        // refill with k16 step u + DEPTH
+        const int t3 = 3 * gi + (s6 + DEPTH) / 2;
+        const int ks3 = (s6 + DEPTH) & 1;
         if (t3 < 27) {
-          load_step(bq[s6 % 3], c, t3, ks3);
+          load_step(bq[s6 % DEPTH], c, t3, ks3);
         } else if (hnext) {
-          load_step(bq[s6 % 3], c + 1, t3 - 27, ks3);
+          load_step(bq[s6 % DEPTH], c + 1, t3 - 27, ks3);
         }
       }
     }
@@ -529,7 +534,7 @@ __global__ __launch_bounds__(NW * 64) void conv_igemm(ConvArgs a) {
       if (s == 0) {
         constexpr bool kNorm = PRO0 == PRO_NORM || PRO0 == PRO_NORM_SILU;
         constexpr bool kAct = PRO0 == PRO_NORM_SILU;
-        run_333<BK, MI, NJ, kNorm, kAct>(g, acc, nchunks);
+        run_333<BK, MI, NJ, kNorm, kAct, kBRing>(g, acc, nchunks);
         return;
       }
     }
