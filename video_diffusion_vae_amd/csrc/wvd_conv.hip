@@ -272,6 +272,66 @@ __device__ __forceinline__ void run_333_lean(const G& g, f32x16_t (&acc)[MI][NJ]
   }
 }
 
+// Up-conv phase segment (nearest-2x + 3x3 conv in phase form) over a
+// 1 x 16 x 16 low-resolution tile: per chunk the phase's 2x2 taps x two k16
+// steps run unrolled; B fragments of step u live in slot u % 4 and are
+// refilled with step u + 4 (two taps ahead, across chunks); halo item k of
+// the next chunk is loaded at step k and normalised into LDS LAG steps later.
+template <int BK, int MI, int NJ, class G>
+__device__ __forceinline__ void run_phase(const G& g, f32x16_t (&acc)[MI][NJ], int nchunks, int py, int px,
+                                          int nitems) {
+  static_assert(BK == 32, "two k16 steps per tap");
+  constexpr int ROWB = BK * 2 + 16;
+  constexpr int NT = G::NT;
+  constexpr int HX = kTileW + 2;
+  constexpr int IPT = ((1 * 18 * 18) * (BK / 8) + NT - 1) / NT;  // halo items per thread per chunk
+  constexpr int LAG = 8 - IPT;
+  static_assert(IPT >= 1 && IPT <= 7, "phase halo items per chunk");
+  (void)nitems;
+  int toff[4];
+#pragma unroll
+  for (int tap = 0; tap < 4; ++tap) toff[tap] = ((py + (tap >> 1)) * HX + (px + (tap & 1))) * ROWB;
+  f16x8_t bq[4][NJ];
+  auto load_step = [&](f16x8_t (&b)[NJ], int chunk, int tap, int ks) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int soff = ((chunk * 2 + ks) * g.wtaps + g.tap0 + tap) * 1024;
+      b[j] = __builtin_bit_cast(f16x8_t, __builtin_amdgcn_raw_buffer_load_b128(g.wrsrc, g.bvoff[j], soff, 0));
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < 4; ++u) load_step(bq[u], 0, u >> 1, u & 1);
+  for (int c = 0; c < nchunks; ++c) {
+    const unsigned char* hsrc = g.halo0 + (c & 1) * g.halo_bytes;
+    unsigned char* hdst = g.halo0 + ((c + 1) & 1) * g.halo_bytes;
+    const bool hnext = c + 1 < nchunks;
+    uint4 hr[IPT];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int tap = u >> 1, ks = u & 1;
+      if (hnext) {
+        if (u >= LAG && u - LAG < IPT) halo_store<false, false>(g, g.tid + NT * (u - LAG), c + 1, hr[u - LAG], hdst);
+        if (u < IPT) hr[u] = halo_load(g, g.tid + NT * u, c + 1);
+      }
+      f16x8_t av[MI];
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+        av[i] = *reinterpret_cast<const f16x8_t*>(hsrc + g.abase[i] + toff[tap] + ks * 32);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bq[u & 3][j], acc[i][j], 0, 0, 0);
+      if (u + 4 < 8) {
+        load_step(bq[u & 3], c, (u + 4) >> 1, ks);
+      } else if (hnext) {
+        load_step(bq[u & 3], c + 1, (u + 4 - 8) >> 1, ks);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // 1x1x1 segment over raw input (the shortcut of a block whose width
 // changes) for 8-wave workgroups: per chunk two k16 steps, B one chunk
 // ahead, the next chunk's halo loaded and stored within the chunk.
@@ -374,9 +434,11 @@ __device__ __forceinline__ void run_generic(const G& g, f32x16_t (&acc)[MI][NJ],
   }
 }
 
-// PRO0: prologue of segment 0 fixed at compile time (PRO_RAW, PRO_NORM,
-// PRO_NORM_SILU) or -1 to take it from the arguments.
-template <int BK, int BN, int WAVES_N, int NW, bool K333, int PRO0>
+// MODE: 0 any tap set, 1 specialised 3x3x3 (2 x 8 x 16 tiles), 2 specialised
+// up-conv phase (1 x 16 x 16 tiles).  PRO0: prologue of segment 0 fixed at
+// compile time (PRO_RAW, PRO_NORM, PRO_NORM_SILU) or -1 to take it from the
+// arguments.
+template <int BK, int BN, int WAVES_N, int NW, int MODE, int PRO0>
 __global__ __launch_bounds__(NW * 64) void conv_igemm(ConvArgs a) {
   constexpr int NT = NW * 64;           // threads per workgroup
   constexpr int NP = BK / 8;            // 16-byte parts per voxel row
@@ -414,8 +476,9 @@ __global__ __launch_bounds__(NW * 64) void conv_igemm(ConvArgs a) {
   const int ph = (logical / nN) % a.nphase;
   const int mt = logical / (nN * a.nphase);
   const int py = ph >> 1, px = ph & 1;
-  const int TF = K333 ? kTF333 : a.TF;
-  const int TH = K333 ? kTH333 : a.TH;
+  constexpr bool K333 = MODE == 1;
+  const int TF = K333 ? kTF333 : (MODE == 2 ? 1 : a.TF);
+  const int TH = K333 ? kTH333 : (MODE == 2 ? 16 : a.TH);
   const int txi = mt % a.tiles_x;
   const int tyi = (mt / a.tiles_x) % a.tiles_y;
   const int tfi = mt / (a.tiles_x * a.tiles_y);
@@ -539,6 +602,10 @@ __global__ __launch_bounds__(NW * 64) void conv_igemm(ConvArgs a) {
       }
     }
     const int nitems = nhv * NP;
+    if constexpr (MODE == 2) {
+      run_phase<BK, MI, NJ>(g, acc, nchunks, py, px, nitems);
+      return;
+    }
     if constexpr (NW == 8) {
       // the 8-wave kernel's only other segment: a raw 1x1x1 shortcut
       run_111_lean<BK, MI, NJ>(g, acc, nchunks, nitems);
@@ -650,11 +717,11 @@ __global__ __launch_bounds__(NW * 64) void conv_igemm(ConvArgs a) {
   }
 }
 
-template <int BK, int BN, int WAVES_N, int NW, bool K333, int PRO0>
+template <int BK, int BN, int WAVES_N, int NW, int MODE, int PRO0>
 hipError_t launch_impl(const ConvArgs& a, hipStream_t stream) {
   if (g_dry_run) return hipSuccess;
   const size_t lds = conv_lds_bytes(a);
-  auto kern = conv_igemm<BK, BN, WAVES_N, NW, K333, PRO0>;
+  auto kern = conv_igemm<BK, BN, WAVES_N, NW, MODE, PRO0>;
   static size_t attr_bytes = 0;
   if (lds > attr_bytes) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -679,18 +746,21 @@ int conv_bk(const ConvArgs& a) {
 // Kernel variant a launch runs on.
 struct Variant {
   int bk, bn, nw;
-  bool k333;
+  int mode;  // 0 generic, 1 3x3x3, 2 up-conv phase
 };
 
 Variant conv_variant(const ConvArgs& a) {
   const ConvSeg& g = a.seg[0];
   Variant v;
   v.bk = conv_bk(a);
-  v.k333 = g.KT == 3 && g.KS == 3 && a.TF == kTF333 && a.TH == kTH333 && a.Cout > 32 && v.bk == 32 &&
-           a.nphase == 1 && g.wfrag && (g.prologue == PRO_NORM_SILU || g.prologue == PRO_RAW);
+  const bool k333 = g.KT == 3 && g.KS == 3 && a.TF == kTF333 && a.TH == kTH333 && a.Cout > 32 && v.bk == 32 &&
+                    a.nphase == 1 && g.wfrag && (g.prologue == PRO_NORM_SILU || g.prologue == PRO_RAW);
+  const bool kph = g.KT == 1 && g.KS == 2 && a.nphase == 4 && a.TF == 1 && a.TH == 16 && a.Cout > 32 &&
+                   v.bk == 32 && a.nseg == 1 && g.wfrag && g.prologue == PRO_RAW;
   const bool shortcut_ok = a.nseg == 1 || (a.seg[1].KT == 1 && a.seg[1].KS == 1 && a.seg[1].prologue == PRO_RAW &&
                                             a.seg[1].wfrag && a.seg[1].Cin % 32 == 0);
-  if (v.k333 && a.Cout % 256 == 0 && shortcut_ok) {
+  v.mode = k333 ? 1 : (kph ? 2 : 0);
+  if (v.mode != 0 && a.Cout % 256 == 0 && shortcut_ok) {
     v.bn = 256;
     v.nw = 8;
   } else {
@@ -702,11 +772,11 @@ Variant conv_variant(const ConvArgs& a) {
 
 }  // namespace
 
-bool conv_is_333(const ConvArgs& a) { return conv_variant(a).k333; }
+bool conv_is_333(const ConvArgs& a) { return conv_variant(a).mode == 1; }
 
 bool conv_is_main(const ConvArgs& a) {
   const Variant v = conv_variant(a);
-  return v.k333 && v.nw == 8 && a.seg[0].prologue == PRO_NORM_SILU;
+  return v.mode == 1 && v.nw == 8 && a.seg[0].prologue == PRO_NORM_SILU;
 }
 
 size_t conv_lds_bytes(const ConvArgs& a) {
@@ -762,18 +832,22 @@ const char* conv_check(const ConvArgs& a) {
 hipError_t launch_conv(const ConvArgs& a, hipStream_t stream) {
   if (conv_check(a)) return hipErrorInvalidValue;
   const Variant v = conv_variant(a);
-  if (v.k333) {
+  if (v.mode == 1) {
     const bool act = a.seg[0].prologue == PRO_NORM_SILU;
     if (v.nw == 8)
-      return act ? launch_impl<32, 256, 4, 8, true, PRO_NORM_SILU>(a, stream)
-                 : launch_impl<32, 256, 4, 8, true, PRO_RAW>(a, stream);
-    return act ? launch_impl<32, 128, 2, 4, true, PRO_NORM_SILU>(a, stream)
-               : launch_impl<32, 128, 2, 4, true, PRO_RAW>(a, stream);
+      return act ? launch_impl<32, 256, 4, 8, 1, PRO_NORM_SILU>(a, stream)
+                 : launch_impl<32, 256, 4, 8, 1, PRO_RAW>(a, stream);
+    return act ? launch_impl<32, 128, 2, 4, 1, PRO_NORM_SILU>(a, stream)
+               : launch_impl<32, 128, 2, 4, 1, PRO_RAW>(a, stream);
   }
-  if (v.bk == 32 && v.bn == 128) return launch_impl<32, 128, 2, 4, false, -1>(a, stream);
-  if (v.bk == 32 && v.bn == 32) return launch_impl<32, 32, 1, 4, false, -1>(a, stream);
-  if (v.bk == 16 && v.bn == 128) return launch_impl<16, 128, 2, 4, false, -1>(a, stream);
-  return launch_impl<16, 32, 1, 4, false, -1>(a, stream);
+  if (v.mode == 2) {
+    if (v.nw == 8) return launch_impl<32, 256, 4, 8, 2, PRO_RAW>(a, stream);
+    return launch_impl<32, 128, 2, 4, 2, PRO_RAW>(a, stream);
+  }
+  if (v.bk == 32 && v.bn == 128) return launch_impl<32, 128, 2, 4, 0, -1>(a, stream);
+  if (v.bk == 32 && v.bn == 32) return launch_impl<32, 32, 1, 4, 0, -1>(a, stream);
+  if (v.bk == 16 && v.bn == 128) return launch_impl<16, 128, 2, 4, 0, -1>(a, stream);
+  return launch_impl<16, 32, 1, 4, 0, -1>(a, stream);
 }
 
 }  // namespace wvd
