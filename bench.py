@@ -63,7 +63,54 @@ def parse():
                     help="skip the cold 1 GiB copy that calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE")
     ap.add_argument("--cpu-sample-frames", type=int, default=1,
                     help="latent frames of the causal prefix the oracle decodes")
+    ap.add_argument("--sweep", default=None,
+                    help="comma-separated frames_per_pass values: print one JSON line per value with time "
+                         "and peak HBM (the 481-frame workload sweeps 2,4,8,16)")
     return ap.parse_args()
+
+
+def run_sweep(args):
+    """frames_per_pass sweep: time per decode and peak allocated HBM for each
+    value; outputs must be bit-identical across the sweep."""
+    import torch
+
+    from video_diffusion_vae_amd import synth, wvd
+
+    cfg = synth.config_by_name(args.config)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(0)
+    W = synth.make_weights(cfg.c, seed=args.seed, bf16=cfg.weights_bf16)
+    dec = wvd.Decoder({k: torch.from_numpy(v).to(torch.bfloat16) for k, v in W.items()}, cfg.c, cfg.h, cfg.w,
+                      device=dev)
+    z = torch.from_numpy(synth.make_latents(cfg.T, cfg.h, cfg.w, seed=args.seed)).to(dev).to(torch.bfloat16)
+    ref = None
+    for P in [int(p) for p in args.sweep.split(",")]:
+        dec.release_workspace()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats(dev)
+        base = torch.cuda.memory_allocated(dev)
+        out = torch.empty(cfg.video_shape, dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(dec.workspace_bytes(cfg.T, P), dtype=torch.uint8, device=dev)
+        for _ in range(args.warmup):
+            dec.decode(z, P, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            dec.decode(z, P, out=out, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        same = True if ref is None else bool(torch.equal(out, ref))
+        if ref is None:
+            ref = out.clone()
+        print(json.dumps({"workload": cfg.name, "frames_per_pass": P, "ms_per_decode": ms,
+                          "frames_per_s": (4 * cfg.T - 3) / (ms / 1e3),
+                          "peak_hbm_gib": torch.cuda.max_memory_allocated(dev) / 2 ** 30,
+                          "workspace_gib": ws.numel() / 2 ** 30, "video_gib": out.numel() * 2 / 2 ** 30,
+                          "resident_before_gib": base / 2 ** 30,
+                          "bit_identical_to_first": same}), flush=True)
+        del out, ws
 
 
 def cpu_baseline(cfg, W, seed, T_sample):
@@ -98,6 +145,9 @@ def main():
         print("bench.py runs on one GPU only: the decoder has no multi-GPU path "
               "(one GPU per process, no collectives); rerun with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.sweep:
+        run_sweep(args)
+        return
     import numpy as np
     import torch
 
