@@ -37,6 +37,9 @@
 #ifndef WVD_BRING
 #define WVD_BRING 6
 #endif
+#ifndef WVD_SCHED_PIN
+#define WVD_SCHED_PIN 1
+#endif
 
 namespace wvd {
 
@@ -168,12 +171,24 @@ __device__ __forceinline__ void run_333(const G& g, f32x16_t (&acc)[MI][NJ], int
       b[j] = __builtin_bit_cast(f16x8_t, __builtin_amdgcn_raw_buffer_load_b128(g.wrsrc, g.bvoff[j], soff, 0));
     }
   };
+  // Issue order matters: the wait at the top of the chunk loop must hold for
+  // both the first entry and the back edge, so the preloads go out in the
+  // same order as the in-loop refills.
 #pragma unroll
-  for (int u = 0; u < DEPTH; ++u) load_step(bq[u], 0, u >> 1, u & 1);
+  for (int u = 0; u < DEPTH; ++u) {
+    load_step(bq[u], 0, u >> 1, u & 1);
+#if WVD_SCHED_PIN
+    __builtin_amdgcn_sched_barrier(0);
+#endif
+  }
   for (int c = 0; c < nchunks; ++c) {
     const unsigned char* hsrc = g.halo0 + (c & 1) * g.halo_bytes;
     unsigned char* hdst = g.halo0 + ((c + 1) & 1) * g.halo_bytes;
-    const bool hnext = c + 1 < nchunks;
+    // The last chunk streams its own halo and weights once more into the
+    // spare buffer and ring slots instead of branching around the prefetch:
+    // with no branch the wait counters stay exact and keep the full ring in
+    // flight up to the chunk's end.
+    const int cn = c + 1 < nchunks ? c + 1 : c;
     uint4 hr[3];
     for (int gi = 0; gi < 9; ++gi) {
       const int goff = ((gi / 3) * kHY333 + (gi % 3)) * kHX * ROWB;
@@ -181,9 +196,9 @@ __device__ __forceinline__ void run_333(const G& g, f32x16_t (&acc)[MI][NJ], int
       for (int s6 = 0; s6 < 6; ++s6) {
         const int dx = s6 >> 1, ks = s6 & 1;
         const int t = 3 * gi + dx;
-        if (ks == 0 && hnext) {
-          if (t >= 3 && t - 3 < IPT) halo_store<NORM, ACT>(g, g.tid + NT * (t - 3), c + 1, hr[dx], hdst);
-          if (t < IPT) hr[dx] = halo_load(g, g.tid + NT * t, c + 1);
+        if (ks == 0) {
+          if (t >= 3 && t - 3 < IPT) halo_store<NORM, ACT>(g, g.tid + NT * (t - 3), cn, hr[dx], hdst);
+          if (t < IPT) hr[dx] = halo_load(g, g.tid + NT * t, cn);
         }
         {
           f16x8_t av[MI];
@@ -201,9 +216,12 @@ __device__ __forceinline__ void run_333(const G& g, f32x16_t (&acc)[MI][NJ], int
         const int ks3 = (s6 + DEPTH) & 1;
         if (t3 < 27) {
           load_step(bq[s6 % DEPTH], c, t3, ks3);
-        } else if (hnext) {
-          load_step(bq[s6 % DEPTH], c + 1, t3 - 27, ks3);
+        } else {
+          load_step(bq[s6 % DEPTH], cn, t3 - 27, ks3);
         }
+#if WVD_SCHED_PIN
+        __builtin_amdgcn_sched_barrier(0);
+#endif
       }
     }
     __syncthreads();  // next chunk's halo complete; this chunk's reads done
@@ -300,19 +318,24 @@ __device__ __forceinline__ void run_phase(const G& g, f32x16_t (&acc)[MI][NJ], i
     }
   };
 #pragma unroll
-  for (int u = 0; u < 4; ++u) load_step(bq[u], 0, u >> 1, u & 1);
+  for (int u = 0; u < 4; ++u) {
+    load_step(bq[u], 0, u >> 1, u & 1);
+#if WVD_SCHED_PIN
+    __builtin_amdgcn_sched_barrier(0);
+#endif
+  }
   for (int c = 0; c < nchunks; ++c) {
     const unsigned char* hsrc = g.halo0 + (c & 1) * g.halo_bytes;
     unsigned char* hdst = g.halo0 + ((c + 1) & 1) * g.halo_bytes;
-    const bool hnext = c + 1 < nchunks;
+    // the last chunk re-streams its own halo and weights (no branch: exact
+    // wait counters across the chunk boundary)
+    const int cn = c + 1 < nchunks ? c + 1 : c;
     uint4 hr[IPT];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int tap = u >> 1, ks = u & 1;
-      if (hnext) {
-        if (u >= LAG && u - LAG < IPT) halo_store<false, false>(g, g.tid + NT * (u - LAG), c + 1, hr[u - LAG], hdst);
-        if (u < IPT) hr[u] = halo_load(g, g.tid + NT * u, c + 1);
-      }
+      if (u >= LAG && u - LAG < IPT) halo_store<false, false>(g, g.tid + NT * (u - LAG), cn, hr[u - LAG], hdst);
+      if (u < IPT) hr[u] = halo_load(g, g.tid + NT * u, cn);
       f16x8_t av[MI];
 #pragma unroll
       for (int i = 0; i < MI; ++i)
@@ -324,9 +347,12 @@ __device__ __forceinline__ void run_phase(const G& g, f32x16_t (&acc)[MI][NJ], i
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bq[u & 3][j], acc[i][j], 0, 0, 0);
       if (u + 4 < 8) {
         load_step(bq[u & 3], c, (u + 4) >> 1, ks);
-      } else if (hnext) {
-        load_step(bq[u & 3], c + 1, (u + 4 - 8) >> 1, ks);
+      } else {
+        load_step(bq[u & 3], cn, (u + 4 - 8) >> 1, ks);
       }
+#if WVD_SCHED_PIN
+      __builtin_amdgcn_sched_barrier(0);
+#endif
     }
     __syncthreads();
   }
