@@ -718,17 +718,33 @@ int wvd_decode(const wvd_plan* cplan, const void* z, int z_dtype, int T, int fra
     x = resblock(cx, L.up[3][0], x, Hb, Y, R_UP30_1, R_UP30_2, nh2);
     x = resblock(cx, L.up[3][1], x, Hb, nullptr, R_UP31_1, R_UP31_2, nh2);
     // Head: RMSNorm + SiLU + conv c -> 12, pixel shuffle, clamp, NCTHW video.
+    // With only 12 output channels the conv's halo staging would normalise
+    // each voxel many times per output; the normalised input is written once
+    // instead (into the free H buffer), and the head's history ring holds
+    // normalised frames.
     {
       h16_t* ring = cx.wsp<h16_t>(W.ring[R_HEAD]);
-      stats(cx, x, ring, nh2);
-      ConvArgs a = conv333(cx, x, ring, nh2, L.head_norm, L.head_w, L.head_b, 12);
+      Act yn{Hb, x.C, x.F, x.H, x.W};
+      cx.what = "norm_silu";
+      cx.run(3, 0, [&] {
+        return launch_norm_silu(x.p, x.fstride(), x.C, x.C, x.F, x.H * x.W, cx.prep<float>(L.head_norm), yn.p,
+                                yn.fstride(), yn.C, cx.st);
+      });
+      ConvArgs a = args_init();
+      a.seg[0] = seg_basic(yn.p, yn.fstride(), yn.C, yn.C, cx.prep<h16_t>(L.head_w), yn.C, (long long)12 * yn.C, 3, 3,
+                           cx.wbytes(L.head_w));
+      a.seg[0].ring = ring;
+      a.seg[0].n_hist = nh2;
+      a.nseg = 1;
+      a.Cout = 12;
+      a.bias = cx.prep<float>(L.head_b);
       a.out = out;
       a.epi = EPI_VIDEO;
       a.out_base = g2;
       a.video_T = VT;
       set_grid(a, x.F, x.H, x.W, tf_for(3, x.F));
       conv(cx, a, 0);
-      ring_update(cx, ring, x);
+      ring_update(cx, ring, yn);
     }
   }
   if (cx.err != hipSuccess) return WVD_EHIP;

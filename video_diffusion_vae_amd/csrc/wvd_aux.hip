@@ -18,6 +18,9 @@ constexpr float kNormEps = 1e-12f;
 // fixed butterfly combines the G lanes, so the value of a voxel never depends
 // on where or when it is computed (fp32 statistics: Wan2.2 VAE decoder page,
 // "Limits").
+// Each wave takes kStatsU voxel sets per trip and issues all of their loads
+// before reducing any, so enough 16-byte loads are in flight to stream HBM.
+constexpr int kStatsU = 4;
 __global__ __launch_bounds__(256) void rms_stats_kernel(const h16_t* __restrict__ x, long long x_fstride,
                                                         int lda, const h16_t* __restrict__ ring,
                                                         int n_hist, int C, int F, int HW, int G,
@@ -29,28 +32,112 @@ __global__ __launch_bounds__(256) void rms_stats_kernel(const h16_t* __restrict_
   const long long nw = ((long long)gridDim.x * blockDim.x) >> 6;
   const int first_slot = 2 - n_hist;
   const long long nvox = (long long)(F + n_hist) * HW;
-  const int ngroups = C >> 3;
-  for (long long base = gw * vox_per_wave; base < nvox; base += nw * vox_per_wave) {
-    const long long vv = base + lane / G;
-    float ss = 0.0f;
-    const bool ok = vv < nvox;
-    long long slot = 0, pix = 0;
-    if (ok) {
-      slot = vv / HW + first_slot;
-      pix = vv % HW;
-      const h16_t* p = slot < 2 ? ring + (slot * HW + pix) * C : x + (slot - 2) * x_fstride + pix * lda;
-      for (int g = sub; g < ngroups; g += G) {
-        uint4 r = *reinterpret_cast<const uint4*>(p + g * 8);
+  // G is the largest power of two <= C / 8 (at most 64, and C <= 1024), so a
+  // lane holds one or two of the voxel's 8-channel groups: sub and sub + G.
+  const bool second = sub + G < (C >> 3);
+  const long long step = (long long)vox_per_wave * kStatsU;
+  for (long long base = gw * step; base < nvox; base += nw * step) {
+    uint4 r[kStatsU][2];
+    long long slot[kStatsU], pix[kStatsU];
+    bool ok[kStatsU];
+#pragma unroll
+    for (int u = 0; u < kStatsU; ++u) {
+      const long long vv = base + (long long)u * vox_per_wave + lane / G;
+      ok[u] = vv < nvox;
+      slot[u] = ok[u] ? vv / HW + first_slot : 2;
+      pix[u] = ok[u] ? vv % HW : 0;
+      const h16_t* p = slot[u] < 2 ? ring + (slot[u] * HW + pix[u]) * C : x + (slot[u] - 2) * x_fstride + pix[u] * lda;
+      r[u][1] = make_uint4(0, 0, 0, 0);
+      if (ok[u]) {
+        r[u][0] = *reinterpret_cast<const uint4*>(p + sub * 8);
+        if (second) r[u][1] = *reinterpret_cast<const uint4*>(p + (sub + G) * 8);
+      } else {
+        r[u][0] = make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kStatsU; ++u) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
         float f[8];
-        unpack8h(r, f);
+        unpack8h(r[u][q], f);
         float t = 0.0f;
 #pragma unroll
         for (int k = 0; k < 8; ++k) t += f[k] * f[k];
         ss += t;
       }
+      for (int off = 1; off < G; off <<= 1) ss += __shfl_xor(ss, off, 64);
+      if (ok[u] && sub == 0) rs[slot[u] * HW + pix[u]] = 1.0f / fmaxf(sqrtf(ss), kNormEps);
     }
-    for (int off = 1; off < G; off <<= 1) ss += __shfl_xor(ss, off, 64);
-    if (ok && sub == 0) rs[slot * HW + pix] = 1.0f / fmaxf(sqrtf(ss), kNormEps);
+  }
+}
+
+// y = SiLU(x * rs * gamma) for the F frames of a pass, rs from the voxel's
+// channel norm exactly as rms_stats_kernel computes it (same lane split and
+// butterfly).  Used where a norm-SiLU input feeds a conv with few output
+// channels (the head), so every voxel is normalised once instead of once per
+// halo that contains it.  The arithmetic per element is the conv prologue's.
+__global__ __launch_bounds__(256) void norm_silu_kernel(const h16_t* __restrict__ x, long long x_fstride, int lda,
+                                                        int C, int F, int HW, int G,
+                                                        const float* __restrict__ gamma, h16_t* __restrict__ y,
+                                                        long long y_fstride, int ldy) {
+  const int lane = threadIdx.x & 63;
+  const int sub = lane % G;
+  const int vox_per_wave = 64 / G;
+  const long long gw = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const long long nw = ((long long)gridDim.x * blockDim.x) >> 6;
+  const long long nvox = (long long)F * HW;
+  const bool second = sub + G < (C >> 3);
+  const long long step = (long long)vox_per_wave * kStatsU;
+  for (long long base = gw * step; base < nvox; base += nw * step) {
+    uint4 r[kStatsU][2];
+    long long fr[kStatsU], pix[kStatsU];
+    bool ok[kStatsU];
+#pragma unroll
+    for (int u = 0; u < kStatsU; ++u) {
+      const long long vv = base + (long long)u * vox_per_wave + lane / G;
+      ok[u] = vv < nvox;
+      fr[u] = ok[u] ? vv / HW : 0;
+      pix[u] = ok[u] ? vv % HW : 0;
+      const h16_t* p = x + fr[u] * x_fstride + pix[u] * lda;
+      r[u][0] = make_uint4(0, 0, 0, 0);
+      r[u][1] = make_uint4(0, 0, 0, 0);
+      if (ok[u]) {
+        r[u][0] = *reinterpret_cast<const uint4*>(p + sub * 8);
+        if (second) r[u][1] = *reinterpret_cast<const uint4*>(p + (sub + G) * 8);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kStatsU; ++u) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        float f[8];
+        unpack8h(r[u][q], f);
+        float t = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) t += f[k] * f[k];
+        ss += t;
+      }
+      for (int off = 1; off < G; off <<= 1) ss += __shfl_xor(ss, off, 64);
+      const float sc = 1.0f / fmaxf(sqrtf(ss), kNormEps);
+      if (!ok[u]) continue;
+      h16_t* o = y + fr[u] * y_fstride + pix[u] * ldy;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        if (q == 1 && !second) break;
+        const int g8 = (sub + q * G) * 8;
+        float f[8];
+        unpack8h(r[u][q], f);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float t = f[k] * sc * gamma[g8 + k];
+          f[k] = t * __builtin_amdgcn_rcpf(1.0f + __expf(-t));
+        }
+        *reinterpret_cast<uint4*>(o + g8) = pack8h(f);
+      }
+    }
   }
 }
 
@@ -239,10 +326,24 @@ hipError_t launch_rms_stats(const h16_t* x, long long x_fstride, int lda, const 
   if (g_dry_run) return hipSuccess;
   int G = 1;
   while (G < 64 && G * 2 <= C / 8) G *= 2;
+  if (C % 8 || C / 8 > 2 * G || C > 1024) return hipErrorInvalidValue;  // at most two groups per lane
   const long long nvox = (long long)(F + n_hist) * HW;
-  const long long waves = (nvox + (64 / G) - 1) / (64 / G);
+  const long long waves = (nvox + (64 / G) * kStatsU - 1) / ((64 / G) * kStatsU);
   hipLaunchKernelGGL(rms_stats_kernel, dim3(grid_for(waves * 64, 256, 16384)), dim3(256), 0, s, x, x_fstride, lda,
                      ring, n_hist, C, F, HW, G, rs);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_silu(const h16_t* x, long long x_fstride, int lda, int C, int F, int HW, const float* gamma,
+                            h16_t* y, long long y_fstride, int ldy, hipStream_t s) {
+  if (g_dry_run) return hipSuccess;
+  int G = 1;
+  while (G < 64 && G * 2 <= C / 8) G *= 2;
+  if (C % 8 || C / 8 > 2 * G || C > 1024) return hipErrorInvalidValue;
+  const long long nvox = (long long)F * HW;
+  const long long waves = (nvox + (64 / G) * kStatsU - 1) / ((64 / G) * kStatsU);
+  hipLaunchKernelGGL(norm_silu_kernel, dim3(grid_for(waves * 64, 256, 16384)), dim3(256), 0, s, x, x_fstride, lda, C,
+                     F, HW, G, gamma, y, y_fstride, ldy);
   return hipGetLastError();
 }
 

@@ -779,8 +779,9 @@ Variant conv_variant(const ConvArgs& a) {
   const ConvSeg& g = a.seg[0];
   Variant v;
   v.bk = conv_bk(a);
-  const bool k333 = g.KT == 3 && g.KS == 3 && a.TF == kTF333 && a.TH == kTH333 && a.Cout > 32 && v.bk == 32 &&
-                    a.nphase == 1 && g.wfrag && (g.prologue == PRO_NORM_SILU || g.prologue == PRO_RAW);
+  const bool k333 = g.KT == 3 && g.KS == 3 && a.TF == kTF333 && a.TH == kTH333 && v.bk == 32 && a.nphase == 1 &&
+                    g.wfrag && (a.Cout > 32 ? (g.prologue == PRO_NORM_SILU || g.prologue == PRO_RAW)
+                                            : (g.prologue == PRO_RAW && a.nseg == 1));
   const bool kph = g.KT == 1 && g.KS == 2 && a.nphase == 4 && a.TF == 1 && a.TH == 16 && a.Cout > 32 &&
                    v.bk == 32 && a.nseg == 1 && g.wfrag && g.prologue == PRO_RAW;
   const bool shortcut_ok = a.nseg == 1 || (a.seg[1].KT == 1 && a.seg[1].KS == 1 && a.seg[1].prologue == PRO_RAW &&
@@ -788,6 +789,11 @@ Variant conv_variant(const ConvArgs& a) {
   v.mode = k333 ? 1 : (kph ? 2 : 0);
   if (v.mode != 0 && a.Cout % 256 == 0 && shortcut_ok) {
     v.bn = 256;
+    v.nw = 8;
+  } else if (v.mode == 1 && a.Cout <= 32) {
+    // narrow raw 3x3x3 (the head): eight waves of 32 x 32, one MFMA per
+    // k16 step each, all sharing one B fragment stream
+    v.bn = 32;
     v.nw = 8;
   } else {
     v.bn = a.Cout <= 32 ? 32 : 128;
@@ -860,6 +866,10 @@ hipError_t launch_conv(const ConvArgs& a, hipStream_t stream) {
   const Variant v = conv_variant(a);
   if (v.mode == 1) {
     const bool act = a.seg[0].prologue == PRO_NORM_SILU;
+    if (v.nw == 8 && v.bn == 32) {
+      if (act) return hipErrorInvalidValue;  // the narrow 3x3x3 variant is raw-only
+      return launch_impl<32, 32, 1, 8, 1, PRO_RAW>(a, stream);
+    }
     if (v.nw == 8)
       return act ? launch_impl<32, 256, 4, 8, 1, PRO_NORM_SILU>(a, stream)
                  : launch_impl<32, 256, 4, 8, 1, PRO_RAW>(a, stream);

@@ -87,6 +87,9 @@ bool conv_is_main(const ConvArgs& a);
 // Auxiliary kernels (wvd_aux.hip).
 hipError_t launch_rms_stats(const h16_t* x, long long x_fstride, int lda, const h16_t* ring,
                             int n_hist, int C, int F, int HW, float* rs, hipStream_t s);
+// y = SiLU(x / ||x|| * gamma) per voxel over C channels (gamma carries sqrt(C)).
+hipError_t launch_norm_silu(const h16_t* x, long long x_fstride, int lda, int C, int F, int HW, const float* gamma,
+                            h16_t* y, long long y_fstride, int ldy, hipStream_t s);
 hipError_t launch_ring_update(h16_t* ring, const h16_t* x, long long x_fstride, int lda, int C,
                               int F, int HW, hipStream_t s);
 hipError_t launch_latent_to_cl(const void* z, int dtype, int T, int t0, int F, int HW, h16_t* zt, hipStream_t s);
