@@ -743,6 +743,410 @@ __global__ __launch_bounds__(NW * 64) void conv_igemm(ConvArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Persistent 8-wave kernel for the specialised one-segment convs (3x3x3 and
+// up-conv phase).  One workgroup per CU walks its XCD's share of the tiles;
+// while a tile's last chunk is multiplied, the next tile's first halo chunk
+// and B fragments stream in, and the halo tables of the tile after next are
+// built during the epilogue.  A tile switch then costs only the epilogue,
+// not a workgroup launch, two table/halo round trips and a B refill.
+
+// Work split: the 8 XCDs take contiguous ranges of logical tiles in
+// proportion to their workgroup count; workgroup `slot` of an XCD takes
+// tiles start + slot, start + slot + n, ... so the tiles running at one time
+// on an XCD are neighbours (shared weights and halos in its L2).
+struct TileSeq {
+  int start, end, slot, n;
+  __device__ int at(int k) const {
+    const int t = start + slot + k * n;
+    return t < end ? t : -1;
+  }
+};
+
+__device__ __forceinline__ TileSeq tile_seq(int total) {
+  const int G = gridDim.x, b = blockIdx.x, xcd = b & 7;
+  int before = 0;
+  for (int x = 0; x < xcd; ++x) before += (G - x + 7) >> 3;
+  const int n = (G - xcd + 7) >> 3;
+  TileSeq s;
+  s.start = (int)((long long)total * before / G);
+  s.end = (int)((long long)total * (before + n) / G);
+  s.slot = b >> 3;
+  s.n = n;
+  return s;
+}
+
+// Output tile of a logical tile index (same order as conv_igemm).
+struct TileGeo {
+  int f0, y0, x0, n0, ph;
+};
+
+template <int BN, int MODE>
+__device__ __forceinline__ TileGeo tile_geo(const ConvArgs& a, int logical) {
+  constexpr int TF = MODE == 1 ? kTF333 : 1;
+  constexpr int TH = MODE == 1 ? kTH333 : 16;
+  const int nN = (a.Cout + BN - 1) / BN;
+  const int nt = logical % nN;
+  const int ph = (logical / nN) % a.nphase;
+  const int mt = logical / (nN * a.nphase);
+  TileGeo t;
+  t.x0 = (mt % a.tiles_x) * kTileW;
+  t.y0 = ((mt / a.tiles_x) % a.tiles_y) * TH;
+  t.f0 = (mt / (a.tiles_x * a.tiles_y)) * TF;
+  t.n0 = nt * BN;
+  t.ph = ph;
+  return t;
+}
+
+template <int BN, int WAVES_N, int MODE, int PRO0>
+__global__ __launch_bounds__(512) void conv_persist(ConvArgs a) {
+  constexpr int BK = 32, NW = 8, NT = 512, NP = 4;
+  constexpr int ROWB = BK * 2 + 16;
+  constexpr int WAVES_M = NW / WAVES_N;
+  constexpr int WM = kTileM / WAVES_M;
+  constexpr int WN = BN / WAVES_N;
+  constexpr int MI = WM / 32;
+  constexpr int NJ = WN / 32;
+  constexpr bool K333 = MODE == 1;
+  constexpr bool NORM = PRO0 == PRO_NORM || PRO0 == PRO_NORM_SILU;
+  constexpr bool ACT = PRO0 == PRO_NORM_SILU;
+  constexpr int TF = K333 ? kTF333 : 1;
+  constexpr int TH = K333 ? kTH333 : 16;
+  constexpr int KT = K333 ? 3 : 1;
+  constexpr int HX = kTileW + 2, HY = TH + 2, HF = TF + KT - 1;
+  constexpr int NHV = HF * HY * HX;
+  constexpr int NTAPS = K333 ? 27 : 4;
+  static_assert(MODE == 1 || MODE == 2, "specialised tap sets only");
+  static_assert(WN % 32 == 0 && MI >= 1, "wave tile");
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wave_m = wave / WAVES_N;
+  const int wave_n = wave % WAVES_N;
+  const int kpart = lane >> 5;
+  const int lrow = lane & 31;
+  const ConvSeg& S = a.seg[0];
+
+  // LDS: halo[2] | vptr[2][nhv_max] | rs[2][nhv_max] | gamma[Cin]
+  const int nhv_max = a.nhv_max;
+  const int halo_bytes = nhv_max * ROWB;
+  const h16_t** vptr_s = reinterpret_cast<const h16_t**>(smem + 2 * halo_bytes);
+  float* rs_s = reinterpret_cast<float*>(vptr_s + 2 * nhv_max);
+  float* gamma_s = rs_s + 2 * nhv_max;
+  const int HW = a.H * a.W;
+  const int nchunks = S.Cin / BK;
+  const int nN = (a.Cout + BN - 1) / BN;
+  const int total = a.tiles_x * a.tiles_y * a.tiles_f * nN * a.nphase;
+  const TileSeq seq = tile_seq(total);
+  if (seq.at(0) < 0) return;  // uniform: no tile for this workgroup
+
+  // Halo table of tile `logical` into table set `tb`: per halo row the
+  // source pointer and (norm) scale; padding voxels read the zero row.
+  auto build_tables = [&](int tb, int logical) {
+    const TileGeo t = tile_geo<BN, MODE>(a, logical);
+    for (int v = tid; v < nhv_max; v += NT) {
+      const h16_t* p = a.zero_row;
+      float rsv = 0.0f;
+      if (v < NHV) {
+        const int hx = v % HX;
+        const int t2 = v / HX;
+        const int hy = t2 % HY;
+        const int hf = t2 / HY;
+        const int fo = t.f0 + hf - (KT - 1);
+        const int y = t.y0 + hy - 1;
+        const int x = t.x0 + hx - 1;
+        if (y >= 0 && y < a.H && x >= 0 && x < a.W && fo < a.F) {
+          const long long pix = (long long)y * a.W + x;
+          const h16_t* q = nullptr;
+          if (fo >= 0) {
+            q = S.x + fo * S.x_fstride + pix * S.lda;
+          } else if (fo + 2 >= 2 - S.n_hist) {
+            q = S.ring + (long long)(fo + 2) * HW * S.Cin + pix * S.Cin;
+          }
+          if (q) {
+            p = q;
+            if (NORM) rsv = S.rs[(long long)(fo + 2) * HW + pix];
+          }
+        }
+      }
+      vptr_s[tb * nhv_max + v] = p;
+      rs_s[tb * nhv_max + v] = rsv;
+    }
+  };
+
+  // Per-tile fragment addressing (A rows are the same for every tile).
+  SegCtx<BK, MI, NJ, NT> g0;
+  g0.halo0 = smem;
+  g0.halo_bytes = halo_bytes;
+  g0.gamma = gamma_s;
+  g0.tid = tid;
+  g0.wtaps = a.nphase * NTAPS;
+  g0.wrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<h16_t*>(S.w), 0, (int)S.w_bytes, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int m = wave_m * WM + 32 * i + lrow;
+    const int tx = m & (kTileW - 1);
+    const int t2 = m / kTileW;
+    g0.abase[i] = (((t2 / TH) * HY + (t2 % TH)) * HX + tx) * ROWB + kpart * 16;
+  }
+  const int U = S.Cin / 16;
+  auto ctx_for = [&](int logical, int tb) {
+    SegCtx<BK, MI, NJ, NT> g = g0;
+    const TileGeo t = tile_geo<BN, MODE>(a, logical);
+    g.vptr = vptr_s + tb * nhv_max;
+    g.rs = rs_s + tb * nhv_max;
+    g.tap0 = t.ph * NTAPS;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int nb = (t.n0 + wave_n * WN) / 32 + j;
+      g.bvoff[j] = (nb * U * g.wtaps) * 1024 + lane * 16;
+    }
+    return g;
+  };
+
+  f16x8_t bq[kBRing][NJ];
+  auto load_step = [&](const SegCtx<BK, MI, NJ, NT>& g, f16x8_t (&b)[NJ], int chunk, int tap, int ks) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int soff = ((chunk * 2 + ks) * g.wtaps + g.tap0 + tap) * 1024;
+      b[j] = __builtin_bit_cast(f16x8_t, __builtin_amdgcn_raw_buffer_load_b128(g.wrsrc, g.bvoff[j], soff, 0));
+    }
+  };
+
+  // ---- first tile: tables of tiles 0 and 1, synchronous first halo chunk ----
+  if (NORM)
+    for (int c = tid; c < S.Cin; c += NT) gamma_s[c] = S.gamma[c];
+  build_tables(0, seq.at(0));
+  if (seq.at(1) >= 0) build_tables(1, seq.at(1));
+  __syncthreads();
+  {
+    const SegCtx<BK, MI, NJ, NT> g = ctx_for(seq.at(0), 0);
+    for (int idx = tid; idx < nhv_max * NP; idx += NT)
+      halo_store<NORM, ACT>(g, idx, 0, halo_load(g, idx, 0), smem);
+    constexpr int PRE = K333 ? kBRing : 4;
+#pragma unroll
+    for (int u = 0; u < PRE; ++u) {
+      load_step(g, bq[u], 0, u >> 1, u & 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __syncthreads();
+
+  f32x16_t acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  int gc = 0;  // chunks done by this workgroup (halo buffer parity)
+  for (int k = 0;; ++k) {
+    const int cur = seq.at(k);
+    if (cur < 0) break;
+    const int nxt = seq.at(k + 1);
+    const SegCtx<BK, MI, NJ, NT> g = ctx_for(cur, k & 1);
+    // The last chunk prefetches the next tile's first chunk, or (no next
+    // tile) streams its own halo and weights once more into the spare
+    // buffer and ring slots: no branch, exact wait counters.
+    const SegCtx<BK, MI, NJ, NT> gl = nxt >= 0 ? ctx_for(nxt, (k + 1) & 1) : g;
+    const TileGeo geo = tile_geo<BN, MODE>(a, cur);
+
+    for (int c = 0; c < nchunks; ++c, ++gc) {
+      const bool last = c + 1 == nchunks;
+      const SegCtx<BK, MI, NJ, NT>& gn = last ? gl : g;
+      const int cn = last ? (nxt >= 0 ? 0 : c) : c + 1;
+      const unsigned char* hsrc = smem + (gc & 1) * halo_bytes;
+      unsigned char* hdst = smem + ((gc + 1) & 1) * halo_bytes;
+      if constexpr (K333) {
+        constexpr int IPT = (kNHV333 * NP + NT - 1) / NT;
+        static_assert(IPT + 3 <= 27, "halo items must land inside a chunk");
+        uint4 hr[3];
+#pragma unroll
+        for (int gi = 0; gi < 9; ++gi) {
+          const int goff = ((gi / 3) * kHY333 + (gi % 3)) * kHX * ROWB;
+#pragma unroll
+          for (int s6 = 0; s6 < 6; ++s6) {
+            const int dx = s6 >> 1, ks = s6 & 1;
+            const int t = 3 * gi + dx;
+            if (ks == 0) {
+              if (t >= 3 && t - 3 < IPT) halo_store<NORM, ACT>(gn, tid + NT * (t - 3), cn, hr[dx], hdst);
+              if (t < IPT) hr[dx] = halo_load(gn, tid + NT * t, cn);
+            }
+            f16x8_t av[MI];
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+              av[i] = *reinterpret_cast<const f16x8_t*>(hsrc + g.abase[i] + goff + dx * ROWB + ks * 32);
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+              for (int j = 0; j < NJ; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bq[s6 % kBRing][j], acc[i][j], 0, 0, 0);
+            // refill with k16 step u + kBRing
+            const int t3 = 3 * gi + (s6 + kBRing) / 2;
+            const int ks3 = (s6 + kBRing) & 1;
+            if (t3 < 27)
+              load_step(g, bq[s6 % kBRing], c, t3, ks3);
+            else
+              load_step(gn, bq[s6 % kBRing], cn, t3 - 27, ks3);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      } else {
+        constexpr int IPT = ((1 * 18 * 18) * NP + NT - 1) / NT;
+        constexpr int LAG = 8 - IPT;
+        static_assert(IPT >= 1 && IPT <= 7, "phase halo items per chunk");
+        const int py = geo.ph >> 1, px = geo.ph & 1;
+        uint4 hr[IPT];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int tap = u >> 1, ks = u & 1;
+          if (u >= LAG && u - LAG < IPT) halo_store<false, false>(gn, tid + NT * (u - LAG), cn, hr[u - LAG], hdst);
+          if (u < IPT) hr[u] = halo_load(gn, tid + NT * u, cn);
+          const int toff = ((py + (tap >> 1)) * HX + (px + (tap & 1))) * ROWB;
+          f16x8_t av[MI];
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+            av[i] = *reinterpret_cast<const f16x8_t*>(hsrc + g.abase[i] + toff + ks * 32);
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bq[u & 3][j], acc[i][j], 0, 0, 0);
+          if (u + 4 < 8)
+            load_step(g, bq[u & 3], c, (u + 4) >> 1, ks);
+          else
+            load_step(gn, bq[u & 3], cn, (u + 4 - 8) >> 1, ks);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __syncthreads();  // next chunk's halo complete; this chunk's reads done
+    }
+
+    // Tables of the tile after next go into this tile's (now unused) set.
+    const int nn = seq.at(k + 2);
+    if (nn >= 0) build_tables(k & 1, nn);
+
+    // ---- epilogue: 8-row quarters of each 32-row block through the last
+    // chunk's halo buffer (free now), then 16-byte stores along channels ----
+    constexpr int EROW = WN + 8;          // padded LDS row (floats)
+    constexpr int LPR = 64 / 8;           // lanes per staged row
+    constexpr int CPL = WN / LPR;         // channels per lane
+    float* ep = reinterpret_cast<float*>(smem + ((gc - 1) & 1) * halo_bytes) + wave * 8 * EROW;
+    const int er = lane / LPR;
+    const int ec0 = (lane % LPR) * CPL;
+    const int ncol0 = geo.n0 + wave_n * WN;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int e = 4 * q; e < 4 * q + 4; ++e) ep[(4 * kpart + (e & 3)) * EROW + 32 * j + lrow] = acc[i][j][e];
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the rows are in LDS
+        __builtin_amdgcn_wave_barrier();
+        const int m = wave_m * WM + 32 * i + 8 * q + er;
+        const int tx = m & (kTileW - 1);
+        const int t2 = m / kTileW;
+        const int f = geo.f0 + t2 / TH, y = geo.y0 + t2 % TH, x = geo.x0 + tx;
+        const int nb = ncol0 + ec0;
+        if (f < a.F && y < a.H && x < a.W && nb < a.Cout) {
+          const long long pix = (long long)y * a.W + x;
+          const float* row = ep + er * EROW + ec0;
+          if (a.epi == EPI_VIDEO) {
+            for (int cc = 0; cc < CPL && nb + cc < a.Cout; ++cc) {
+              const int n = nb + cc;
+              float v = row[cc] * a.scale + (a.bias ? a.bias[n] : 0.0f);
+              v = fminf(fmaxf(v, -1.0f), 1.0f);
+              const int kk = n >> 2, ddy = (n >> 1) & 1, ddx = n & 1;
+              const long long r2 = ((long long)kk * a.video_T + a.out_base + f) * (2 * a.H) + 2 * y + ddy;
+              static_cast<bf16_t*>(a.out)[r2 * (2 * a.W) + 2 * x + ddx] = (bf16_t)f2bf(v);
+            }
+          } else if constexpr (CPL % 8 == 0) {
+            h16_t* o;
+            if (a.epi == EPI_PHASE) {
+              const long long op = (long long)(2 * y + (geo.ph >> 1)) * (2 * a.W) + (2 * x + (geo.ph & 1));
+              o = static_cast<h16_t*>(a.out) + f * a.out_fstride + op * a.ldo;
+            } else {
+              o = static_cast<h16_t*>(a.out) + f * a.out_fstride + pix * a.ldo;
+            }
+            const h16_t* rp = a.res ? a.res + f * a.res_fstride + pix * a.ldr + nb : nullptr;
+            const bool full = nb + CPL <= a.Cout;
+#pragma unroll
+            for (int c8 = 0; c8 < CPL; c8 += 8) {
+              float v[8];
+#pragma unroll
+              for (int kk = 0; kk < 8; ++kk) v[kk] = row[c8 + kk] * a.scale;
+              if (full) {
+                if (a.bias) {
+#pragma unroll
+                  for (int kk = 0; kk < 8; ++kk) v[kk] += a.bias[nb + c8 + kk];
+                }
+                if (rp) {
+                  float r[8];
+                  unpack8h(*reinterpret_cast<const uint4*>(rp + c8), r);
+#pragma unroll
+                  for (int kk = 0; kk < 8; ++kk) v[kk] += r[kk];
+                }
+                *reinterpret_cast<uint4*>(o + nb + c8) = pack8h(v);
+              } else {
+                for (int kk = 0; kk < 8 && nb + c8 + kk < a.Cout; ++kk) {
+                  float t = v[kk] + (a.bias ? a.bias[nb + c8 + kk] : 0.0f);
+                  if (rp) t += h2f(rp[c8 + kk]);
+                  o[nb + c8 + kk] = (h16_t)f2h(t);
+                }
+              }
+            }
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    // staging buffer and the new tables are complete before the next tile
+    // stores halo rows into that buffer and reads those tables
+    __syncthreads();
+  }
+}
+
+template <int BN, int WAVES_N, int MODE, int PRO0>
+hipError_t launch_persist_impl(const ConvArgs& a, hipStream_t stream) {
+  if (g_dry_run) return hipSuccess;
+  const size_t lds = conv_lds_bytes(a);
+  auto kern = conv_persist<BN, WAVES_N, MODE, PRO0>;
+  static size_t attr_bytes = 0;
+  if (lds > attr_bytes) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_bytes = lds;
+  }
+  const int nM = a.tiles_x * a.tiles_y * a.tiles_f;
+  const int nN = (a.Cout + BN - 1) / BN;
+  const long long total = (long long)nM * nN * a.nphase;
+  if (total <= 0) return hipSuccess;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static int ncu[64] = {0};
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!ncu[dev]) {
+    e = hipDeviceGetAttribute(&ncu[dev], hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+  }
+  const long long grid = total < ncu[dev] ? total : ncu[dev];
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), lds, stream, a);
+  return hipGetLastError();
+}
+
 template <int BK, int BN, int WAVES_N, int NW, int MODE, int PRO0>
 hipError_t launch_impl(const ConvArgs& a, hipStream_t stream) {
   if (g_dry_run) return hipSuccess;
@@ -804,11 +1208,20 @@ Variant conv_variant(const ConvArgs& a) {
 
 }  // namespace
 
+// Launches that run on the persistent kernel: the specialised one-segment
+// tap sets on 8-wave tiles, with the epilogues that kernel implements.
+bool conv_persistent(const ConvArgs& a) {
+  const Variant v = conv_variant(a);
+  if (v.mode == 0 || v.nw != 8 || a.nseg != 1) return false;
+  if (v.bn == 32) return v.mode == 1 && a.epi == EPI_VIDEO && a.seg[0].prologue == PRO_RAW;
+  return a.epi == (v.mode == 2 ? EPI_PHASE : EPI_H16) || (v.mode == 1 && a.epi == EPI_VIDEO);
+}
+
 bool conv_is_333(const ConvArgs& a) { return conv_variant(a).mode == 1; }
 
 bool conv_is_main(const ConvArgs& a) {
   const Variant v = conv_variant(a);
-  return v.mode == 1 && v.nw == 8 && a.seg[0].prologue == PRO_NORM_SILU;
+  return conv_persistent(a) && v.mode == 1 && v.bn == 256 && a.seg[0].prologue == PRO_NORM_SILU;
 }
 
 size_t conv_lds_bytes(const ConvArgs& a) {
@@ -816,6 +1229,8 @@ size_t conv_lds_bytes(const ConvArgs& a) {
   int cin_max = 0;
   for (int s = 0; s < a.nseg; ++s)
     if (a.seg[s].prologue != PRO_RAW && a.seg[s].Cin > cin_max) cin_max = a.seg[s].Cin;
+  if (conv_persistent(a))  // two halo buffers, two table sets, gamma; the epilogue stages inside a halo buffer
+    return (size_t)2 * a.nhv_max * (v.bk * 2 + 16) + (size_t)2 * a.nhv_max * (8 + 4) + (size_t)cin_max * 4;
   const size_t main_loop =
       (size_t)2 * a.nhv_max * (v.bk * 2 + 16) + (size_t)a.nhv_max * (8 + 4) + (size_t)cin_max * 4;
   const int wn = v.bn == 32 ? 32 : 64;  // wave tile width of the instantiation
@@ -864,6 +1279,13 @@ const char* conv_check(const ConvArgs& a) {
 hipError_t launch_conv(const ConvArgs& a, hipStream_t stream) {
   if (conv_check(a)) return hipErrorInvalidValue;
   const Variant v = conv_variant(a);
+  if (conv_persistent(a)) {
+    const int pro = a.seg[0].prologue;
+    if (v.mode == 2) return launch_persist_impl<256, 4, 2, PRO_RAW>(a, stream);
+    if (v.bn == 32) return launch_persist_impl<32, 1, 1, PRO_RAW>(a, stream);
+    return pro == PRO_NORM_SILU ? launch_persist_impl<256, 4, 1, PRO_NORM_SILU>(a, stream)
+                                : launch_persist_impl<256, 4, 1, PRO_RAW>(a, stream);
+  }
   if (v.mode == 1) {
     const bool act = a.seg[0].prologue == PRO_NORM_SILU;
     if (v.nw == 8 && v.bn == 32) {

@@ -76,6 +76,9 @@ extern bool g_dry_run;
 const char* conv_check(const ConvArgs& a);
 // Launches one implicit-GEMM convolution; returns hipSuccess or the error.
 hipError_t launch_conv(const ConvArgs& a, hipStream_t stream);
+// True when `a` runs on the persistent kernel (one workgroup per CU walking
+// tiles) rather than one workgroup per tile.
+bool conv_persistent(const ConvArgs& a);
 // LDS bytes the launch of `a` needs (host-side check).
 size_t conv_lds_bytes(const ConvArgs& a);
 // Whether `a` runs on the specialised 3x3x3 kernel.
