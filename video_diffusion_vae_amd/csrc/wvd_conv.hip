@@ -783,8 +783,8 @@ struct TileGeo {
 
 template <int BN, int MODE>
 __device__ __forceinline__ TileGeo tile_geo(const ConvArgs& a, int logical) {
-  constexpr int TF = MODE == 1 ? kTF333 : 1;
-  constexpr int TH = MODE == 1 ? kTH333 : 16;
+  constexpr int TF = MODE == 2 ? 1 : kTF333;
+  constexpr int TH = MODE == 2 ? 16 : kTH333;
   const int nN = (a.Cout + BN - 1) / BN;
   const int nt = logical % nN;
   const int ph = (logical / nN) % a.nphase;
@@ -810,13 +810,15 @@ __global__ __launch_bounds__(512) void conv_persist(ConvArgs a) {
   constexpr bool K333 = MODE == 1;
   constexpr bool NORM = PRO0 == PRO_NORM || PRO0 == PRO_NORM_SILU;
   constexpr bool ACT = PRO0 == PRO_NORM_SILU;
-  constexpr int TF = K333 ? kTF333 : 1;
-  constexpr int TH = K333 ? kTH333 : 16;
-  constexpr int KT = K333 ? 3 : 1;
-  constexpr int HX = kTileW + 2, HY = TH + 2, HF = TF + KT - 1;
+  constexpr bool KT3 = MODE == 3;  // 3x1x1 temporal conv (time_conv)
+  constexpr int TF = MODE == 2 ? 1 : kTF333;
+  constexpr int TH = MODE == 2 ? 16 : kTH333;
+  constexpr int KT = MODE == 2 ? 1 : 3;
+  constexpr int HS = KT3 ? 0 : 1;  // spatial halo
+  constexpr int HX = kTileW + 2 * HS, HY = TH + 2 * HS, HF = TF + KT - 1;
   constexpr int NHV = HF * HY * HX;
-  constexpr int NTAPS = K333 ? 27 : 4;
-  static_assert(MODE == 1 || MODE == 2, "specialised tap sets only");
+  constexpr int NTAPS = K333 ? 27 : (KT3 ? 3 : 4);
+  static_assert(MODE >= 1 && MODE <= 3, "specialised tap sets only");
   static_assert(WN % 32 == 0 && MI >= 1, "wave tile");
 
   extern __shared__ __align__(16) unsigned char smem[];
@@ -855,8 +857,8 @@ __global__ __launch_bounds__(512) void conv_persist(ConvArgs a) {
         const int hy = t2 % HY;
         const int hf = t2 / HY;
         const int fo = t.f0 + hf - (KT - 1);
-        const int y = t.y0 + hy - 1;
-        const int x = t.x0 + hx - 1;
+        const int y = t.y0 + hy - HS;
+        const int x = t.x0 + hx - HS;
         if (y >= 0 && y < a.H && x >= 0 && x < a.W && fo < a.F) {
           const long long pix = (long long)y * a.W + x;
           const h16_t* q = nullptr;
@@ -925,7 +927,7 @@ __global__ __launch_bounds__(512) void conv_persist(ConvArgs a) {
     const SegCtx<BK, MI, NJ, NT> g = ctx_for(seq.at(0), 0);
     for (int idx = tid; idx < nhv_max * NP; idx += NT)
       halo_store<NORM, ACT>(g, idx, 0, halo_load(g, idx, 0), smem);
-    constexpr int PRE = K333 ? kBRing : 4;
+    constexpr int PRE = K333 ? kBRing : (KT3 ? 3 : 4);
 #pragma unroll
     for (int u = 0; u < PRE; ++u) {
       load_step(g, bq[u], 0, u >> 1, u & 1);
@@ -993,6 +995,39 @@ __global__ __launch_bounds__(512) void conv_persist(ConvArgs a) {
               load_step(gn, bq[s6 % kBRing], cn, t3 - 27, ks3);
             __builtin_amdgcn_sched_barrier(0);
           }
+        }
+      } else if constexpr (KT3) {
+        // three temporal taps x two k16 steps; B fragments of step u live in
+        // slot u % 3 and are refilled with step u + 3 (half a chunk ahead)
+        // halo items: two loads at each of steps 0 and 1, stored four steps
+        // later (HBM latency covered by four steps of MFMAs)
+        constexpr int IPT = (NHV * NP + NT - 1) / NT;
+        static_assert(IPT >= 1 && IPT <= 4, "time_conv halo items per chunk");
+        uint4 hr[4];
+#pragma unroll
+        for (int u = 0; u < 6; ++u) {
+          const int tap = u >> 1, ks = u & 1;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int is = 2 * (u - 4) + q, il = 2 * u + q;
+            if (u >= 4 && is < IPT) halo_store<false, false>(gn, tid + NT * is, cn, hr[is], hdst);
+            if (u < 2 && il < IPT) hr[il] = halo_load(gn, tid + NT * il, cn);
+          }
+          const int toff = tap * (HY * HX) * ROWB;
+          f16x8_t av[MI];
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+            av[i] = *reinterpret_cast<const f16x8_t*>(hsrc + g.abase[i] + toff + ks * 32);
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bq[u % 3][j], acc[i][j], 0, 0, 0);
+          if (u + 3 < 6)
+            load_step(g, bq[u % 3], c, (u + 3) >> 1, (u + 3) & 1);
+          else
+            load_step(gn, bq[u % 3], cn, (u - 3) >> 1, (u - 3) & 1);
+          __builtin_amdgcn_sched_barrier(0);
         }
       } else {
         constexpr int IPT = ((1 * 18 * 18) * NP + NT - 1) / NT;
@@ -1067,9 +1102,16 @@ __global__ __launch_bounds__(512) void conv_persist(ConvArgs a) {
             }
           } else if constexpr (CPL % 8 == 0) {
             h16_t* o;
+            int ob = nb;  // output channel of this lane's first column
             if (a.epi == EPI_PHASE) {
               const long long op = (long long)(2 * y + (geo.ph >> 1)) * (2 * a.W) + (2 * x + (geo.ph & 1));
               o = static_cast<h16_t*>(a.out) + f * a.out_fstride + op * a.ldo;
+            } else if (a.epi == EPI_TIME) {
+              // channel half h of frame f -> output frame out_base + 2f + h
+              const int Chalf = a.Cout >> 1;
+              const int half = nb >= Chalf ? 1 : 0;
+              ob = nb - half * Chalf;
+              o = static_cast<h16_t*>(a.out) + (long long)(a.out_base + 2 * f + half) * a.out_fstride + pix * a.ldo;
             } else {
               o = static_cast<h16_t*>(a.out) + f * a.out_fstride + pix * a.ldo;
             }
@@ -1091,12 +1133,12 @@ __global__ __launch_bounds__(512) void conv_persist(ConvArgs a) {
 #pragma unroll
                   for (int kk = 0; kk < 8; ++kk) v[kk] += r[kk];
                 }
-                *reinterpret_cast<uint4*>(o + nb + c8) = pack8h(v);
+                *reinterpret_cast<uint4*>(o + ob + c8) = pack8h(v);
               } else {
                 for (int kk = 0; kk < 8 && nb + c8 + kk < a.Cout; ++kk) {
                   float t = v[kk] + (a.bias ? a.bias[nb + c8 + kk] : 0.0f);
                   if (rp) t += h2f(rp[c8 + kk]);
-                  o[nb + c8 + kk] = (h16_t)f2h(t);
+                  o[ob + c8 + kk] = (h16_t)f2h(t);
                 }
               }
             }
@@ -1188,9 +1230,11 @@ Variant conv_variant(const ConvArgs& a) {
                                             : (g.prologue == PRO_RAW && a.nseg == 1));
   const bool kph = g.KT == 1 && g.KS == 2 && a.nphase == 4 && a.TF == 1 && a.TH == 16 && a.Cout > 32 &&
                    v.bk == 32 && a.nseg == 1 && g.wfrag && g.prologue == PRO_RAW;
+  const bool kt3 = g.KT == 3 && g.KS == 1 && a.nphase == 1 && a.TF == kTF333 && a.TH == kTH333 && v.bk == 32 &&
+                   a.nseg == 1 && g.wfrag && g.prologue == PRO_RAW && a.Cout % 256 == 0 && a.epi == EPI_TIME;
   const bool shortcut_ok = a.nseg == 1 || (a.seg[1].KT == 1 && a.seg[1].KS == 1 && a.seg[1].prologue == PRO_RAW &&
                                             a.seg[1].wfrag && a.seg[1].Cin % 32 == 0);
-  v.mode = k333 ? 1 : (kph ? 2 : 0);
+  v.mode = k333 ? 1 : (kph ? 2 : (kt3 ? 3 : 0));
   if (v.mode != 0 && a.Cout % 256 == 0 && shortcut_ok) {
     v.bn = 256;
     v.nw = 8;
@@ -1214,6 +1258,7 @@ bool conv_persistent(const ConvArgs& a) {
   const Variant v = conv_variant(a);
   if (v.mode == 0 || v.nw != 8 || a.nseg != 1) return false;
   if (v.bn == 32) return v.mode == 1 && a.epi == EPI_VIDEO && a.seg[0].prologue == PRO_RAW;
+  if (v.mode == 3) return a.epi == EPI_TIME;
   return a.epi == (v.mode == 2 ? EPI_PHASE : EPI_H16) || (v.mode == 1 && a.epi == EPI_VIDEO);
 }
 
@@ -1282,10 +1327,12 @@ hipError_t launch_conv(const ConvArgs& a, hipStream_t stream) {
   if (conv_persistent(a)) {
     const int pro = a.seg[0].prologue;
     if (v.mode == 2) return launch_persist_impl<256, 4, 2, PRO_RAW>(a, stream);
+    if (v.mode == 3) return launch_persist_impl<256, 4, 3, PRO_RAW>(a, stream);
     if (v.bn == 32) return launch_persist_impl<32, 1, 1, PRO_RAW>(a, stream);
     return pro == PRO_NORM_SILU ? launch_persist_impl<256, 4, 1, PRO_NORM_SILU>(a, stream)
                                 : launch_persist_impl<256, 4, 1, PRO_RAW>(a, stream);
   }
+  if (v.mode == 3) return hipErrorInvalidValue;  // the time_conv tap set exists only in the persistent kernel
   if (v.mode == 1) {
     const bool act = a.seg[0].prologue == PRO_NORM_SILU;
     if (v.nw == 8 && v.bn == 32) {
