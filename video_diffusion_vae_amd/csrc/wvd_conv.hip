@@ -40,6 +40,12 @@
 #ifndef WVD_SCHED_PIN
 #define WVD_SCHED_PIN 1
 #endif
+#ifndef WVD_MAIN_W4
+#define WVD_MAIN_W4 1
+#endif
+#ifndef WVD_ILV
+#define WVD_ILV 1
+#endif
 
 namespace wvd {
 
@@ -798,9 +804,13 @@ __device__ __forceinline__ TileGeo tile_geo(const ConvArgs& a, int logical) {
   return t;
 }
 
-template <int BN, int WAVES_N, int MODE, int PRO0>
-__global__ __launch_bounds__(512) void conv_persist(ConvArgs a) {
-  constexpr int BK = 32, NW = 8, NT = 512, NP = 4;
+template <int BN, int WAVES_N, int MODE, int PRO0, int NW = 8>
+__global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
+  constexpr int BK = 32, NT = NW * 64, NP = 4;
+  // With 4 waves (one per SIMD, 512 registers: accumulators in AGPRs) each
+  // wave owns a 128 x 128 sub-tile and reads its A fragments one k16 step
+  // ahead; with 8 waves the second wave on the SIMD hides that latency.
+  constexpr bool APF = NW == 4;
   constexpr int ROWB = BK * 2 + 16;
   constexpr int WAVES_M = NW / WAVES_N;
   constexpr int WM = kTileM / WAVES_M;
@@ -966,6 +976,11 @@ __global__ __launch_bounds__(512) void conv_persist(ConvArgs a) {
         constexpr int IPT = (kNHV333 * NP + NT - 1) / NT;
         static_assert(IPT + 3 <= 27, "halo items must land inside a chunk");
         uint4 hr[3];
+        f16x8_t ap[2][MI];  // A fragments one step ahead (APF)
+        if constexpr (APF) {
+#pragma unroll
+          for (int i = 0; i < MI; ++i) ap[0][i] = *reinterpret_cast<const f16x8_t*>(hsrc + g.abase[i]);
+        }
 #pragma unroll
         for (int gi = 0; gi < 9; ++gi) {
           const int goff = ((gi / 3) * kHY333 + (gi % 3)) * kHX * ROWB;
@@ -973,19 +988,43 @@ __global__ __launch_bounds__(512) void conv_persist(ConvArgs a) {
           for (int s6 = 0; s6 < 6; ++s6) {
             const int dx = s6 >> 1, ks = s6 & 1;
             const int t = 3 * gi + dx;
-            if (ks == 0) {
-              if (t >= 3 && t - 3 < IPT) halo_store<NORM, ACT>(gn, tid + NT * (t - 3), cn, hr[dx], hdst);
-              if (t < IPT) hr[dx] = halo_load(gn, tid + NT * t, cn);
-            }
             f16x8_t av[MI];
+            if constexpr (APF) {
+              const int u1 = 6 * gi + s6 + 1;  // next k16 step of this chunk
+              if (u1 < 54) {
+                const int g1 = u1 / 6, s1 = u1 % 6;
+                const int off = ((g1 / 3) * kHY333 + (g1 % 3)) * kHX * ROWB + (s1 >> 1) * ROWB + (s1 & 1) * 32;
 #pragma unroll
-            for (int i = 0; i < MI; ++i)
-              av[i] = *reinterpret_cast<const f16x8_t*>(hsrc + g.abase[i] + goff + dx * ROWB + ks * 32);
+                for (int i = 0; i < MI; ++i)
+                  ap[(s6 + 1) & 1][i] = *reinterpret_cast<const f16x8_t*>(hsrc + g.abase[i] + off);
+              }
+              __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+              for (int i = 0; i < MI; ++i) av[i] = ap[s6 & 1][i];
+            } else {
+#pragma unroll
+              for (int i = 0; i < MI; ++i)
+                av[i] = *reinterpret_cast<const f16x8_t*>(hsrc + g.abase[i] + goff + dx * ROWB + ks * 32);
+            }
+            // the halo item's normalisation shares the step with the MFMAs so
+            // the scheduler can interleave its VALU work between them
+            const bool hstore = ks == 0 && t >= 3 && t - 3 < IPT;
+            if (hstore) halo_store<NORM, ACT>(gn, tid + NT * (t - 3), cn, hr[dx], hdst);
+            if (ks == 0 && t < IPT) hr[dx] = halo_load(gn, tid + NT * t, cn);
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
               for (int j = 0; j < NJ; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bq[s6 % kBRing][j], acc[i][j], 0, 0, 0);
+#if WVD_ILV
+            if (hstore) {
+#pragma unroll
+              for (int q = 0; q < MI * NJ; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, NORM ? 80 / (MI * NJ) : 1, 0);  // then VALU
+              }
+            }
+#endif
             // refill with k16 step u + kBRing
             const int t3 = 3 * gi + (s6 + kBRing) / 2;
             const int ks3 = (s6 + kBRing) & 1;
@@ -1159,11 +1198,11 @@ __global__ __launch_bounds__(512) void conv_persist(ConvArgs a) {
   }
 }
 
-template <int BN, int WAVES_N, int MODE, int PRO0>
+template <int BN, int WAVES_N, int MODE, int PRO0, int NW = 8>
 hipError_t launch_persist_impl(const ConvArgs& a, hipStream_t stream) {
   if (g_dry_run) return hipSuccess;
   const size_t lds = conv_lds_bytes(a);
-  auto kern = conv_persist<BN, WAVES_N, MODE, PRO0>;
+  auto kern = conv_persist<BN, WAVES_N, MODE, PRO0, NW>;
   static size_t attr_bytes = 0;
   if (lds > attr_bytes) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1185,7 +1224,7 @@ hipError_t launch_persist_impl(const ConvArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   const long long grid = total < ncu[dev] ? total : ncu[dev];
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), lds, stream, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NW * 64), lds, stream, a);
   return hipGetLastError();
 }
 
@@ -1329,6 +1368,9 @@ hipError_t launch_conv(const ConvArgs& a, hipStream_t stream) {
     if (v.mode == 2) return launch_persist_impl<256, 4, 2, PRO_RAW>(a, stream);
     if (v.mode == 3) return launch_persist_impl<256, 4, 3, PRO_RAW>(a, stream);
     if (v.bn == 32) return launch_persist_impl<32, 1, 1, PRO_RAW>(a, stream);
+#if WVD_MAIN_W4
+    if (pro == PRO_NORM_SILU) return launch_persist_impl<256, 2, 1, PRO_NORM_SILU, 4>(a, stream);
+#endif
     return pro == PRO_NORM_SILU ? launch_persist_impl<256, 4, 1, PRO_NORM_SILU>(a, stream)
                                 : launch_persist_impl<256, 4, 1, PRO_RAW>(a, stream);
   }
