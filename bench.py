@@ -236,8 +236,8 @@ def main():
                    "video": list(cfg.video_shape), "frames_per_pass": P, "c": cfg.c},
         "roofline": {"bound": "mfma", "achieved": conv_tflops, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": conv_tflops / MFMA_PEAK_TFLOPS, "traffic": measured_traffic(),
-                     "kernel": "conv_persist<256, 4, 1, 2>: 3x3x3 causal conv, fused RMSNorm+SiLU "
-                               "prologue, 256x256 tiles, one persistent workgroup per CU",
+                     "kernel": "conv_persist<256, 2, 1, 2, 4>: 3x3x3 causal conv, fused RMSNorm+SiLU "
+                               "prologue, 256x256 tiles on 4 waves, one persistent workgroup per CU",
                      "avg_launch_ms": avg_launch_ms, "avg_launch_tflop": avg_launch_flops / 1e12,
                      "launches_per_step": conv["launches"] / args.steps},
         "conv_all_tflops": all_conv_fl / (all_conv_ms / 1e3) / 1e12 if all_conv_ms > 0 else 0.0,
