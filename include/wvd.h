@@ -121,12 +121,15 @@ long long wvd_last_launch_count(const wvd_plan* plan);
 /* Enables (1) or disables (0) HIP-event timing of every kernel wvd_decode
  * launches on the plan (events recorded on the decode's stream around each
  * launch).  wvd_profile_read synchronises on the last recorded event and
- * returns, per kernel class, the summed milliseconds, the summed algorithmic
- * FLOPs (2 per multiply-add of the contraction each launch performs) and the
- * number of launches since the previous read, then clears the record.
- * Classes: 0 the dominant conv kernel (3x3x3, fused RMSNorm+SiLU prologue,
- * 8-wave 256x256 tiles), 1 other convs (conv_in, head, time_conv, up-conv,
- * 1x1), 2 attention GEMMs, 3 RMS statistics, 4 copies / layout / softmax.
+ * returns, per kernel class, the summed milliseconds, the summed FLOPs (2 per
+ * multiply-add each launch performs: for the Winograd-domain GEMMs that is
+ * 2/3 of the direct 3x3x3 count) and the number of launches since the
+ * previous read, then clears the record.
+ * Classes: 0 the dominant conv kernel (the Winograd-domain GEMM of the
+ * norm-SiLU 3x3x3 convs; the direct 3x3x3 kernel for widths it does not
+ * cover), 1 other convs (conv_in, head, time_conv, up-conv, shortcut blocks),
+ * 2 attention GEMMs, 3 RMS statistics and the head's norm-SiLU, 4 copies /
+ * layout / softmax, 5 Winograd input and output transforms.
  * Profiling is not thread-safe.  WVD_EINVAL on a null plan or array. */
 int wvd_profile_enable(wvd_plan* plan, int on);
 int wvd_profile_read(const wvd_plan* plan, double* ms, double* flops, long long* launches, int n_classes);

@@ -23,7 +23,16 @@ namespace {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
-enum ItemKind { K_CONV = 0, K_PHASE = 1, K_VEC = 2 };
+enum ItemKind { K_CONV = 0, K_PHASE = 1, K_VEC = 2, K_WINO = 3 };
+
+#ifndef WVD_WINO
+#define WVD_WINO 1
+#endif
+
+// A 3x3x3 norm-SiLU conv runs in Winograd form (F(2,3) along x: input
+// transform, four xi-plane GEMMs on the persistent kernel, output transform)
+// when its widths suit the 256-wide persistent tiles and 32-channel chunks.
+bool wino_ok(int cin, int cout) { return WVD_WINO && cin % 32 == 0 && cout % 256 == 0; }
 
 // One canonical weight tensor and where its prepared form lives.
 struct Item {
@@ -39,6 +48,7 @@ struct Item {
 struct RB {
   int norm1, conv1w, conv1b, norm2, conv2w, conv2b, scw = -1, scb = -1;
   int cin, cout;
+  bool wino1 = false, wino2 = false;  // conv1 / conv2 prepared and run in Winograd form
 };
 
 struct Layout {
@@ -76,6 +86,16 @@ RB add_rb(Layout& L, int cin, int cout) {
   r.norm2 = add_vec(L, cout, std::sqrt((float)cout));
   add_conv(L, cout, cout, 27, cout, &r.conv2w, &r.conv2b);
   if (cin != cout) add_conv(L, cout, cin, 1, cin, &r.scw, &r.scb);
+  auto to_wino = [&](int item) {
+    Item& it = L.items[item];
+    it.kind = K_WINO;
+    it.taps = 36;  // 4 xi x 3 dt x 3 dy
+    it.bytes = prep_frag_bytes(it.cout, it.cin_pad, 36);
+  };
+  r.wino1 = wino_ok(cin, cout);
+  r.wino2 = cin == cout && wino_ok(cout, cout);  // a shortcut block's conv2 keeps the direct form
+  if (r.wino1) to_wino(r.conv1w);
+  if (r.wino2) to_wino(r.conv2w);
   return r;
 }
 
@@ -125,6 +145,7 @@ Layout make_layout(int c, int h, int w) {
 // Workspace carve-up for a given maximum number of latent frames per pass.
 struct Work {
   size_t X, H, Y, zt, rs, qkv, S, Pm, Vt, O;
+  size_t U, M;               // Winograd input planes and products
   std::vector<size_t> ring;  // 24 rings
   size_t total;
 };
@@ -183,6 +204,23 @@ Work make_work(int c, int h, int w, int P) {
   W.Pm = take((size_t)F0 * L * Lp * 2);
   W.Vt = take((size_t)F0 * c4 * Lp * 2);
   W.O = take((size_t)F0 * L * c4 * 2);
+  {
+    // Winograd planes: U = [4][F+2][H][ceil(W/2)][Cin], M = [4][F][H][ceil(W/2)][Cout]
+    // per level (Cin / Cout of that level's widest Winograd conv).
+    const long long hl[4] = {h, 2LL * h, 4LL * h, 8LL * h};
+    const long long w2[4] = {(w + 1) / 2, (long long)w, 2LL * w, 4LL * w};
+    const long long fl[4] = {F0, F1, F2, F2};
+    const long long ci[4] = {c4, c4, c4, c2};
+    const long long co[4] = {c4, c4, c2, c};
+    long long u = 0, m = 0;
+    for (int l = 0; l < 4; ++l) {
+      if (!wino_ok((int)ci[l], (int)co[l]) && !wino_ok((int)co[l], (int)co[l])) continue;
+      u = std::max(u, 4 * (fl[l] + 2) * hl[l] * w2[l] * ci[l]);
+      m = std::max(m, 4 * fl[l] * hl[l] * w2[l] * co[l]);
+    }
+    W.U = take((size_t)u * 2);
+    W.M = take((size_t)m * 2);
+  }
   for (int i = 0; i < R_COUNT; ++i) {
     RingInfo ri = ring_info(c, i);
     W.ring.push_back(take((size_t)2 * res[ri.level] * ri.cin * 2));
@@ -312,8 +350,9 @@ void set_grid(ConvArgs& a, int F, int H, int W, int TF) {
   int rows = 0;
   for (int s = 0; s < a.nseg; ++s) {
     const ConvSeg& g = a.seg[s];
-    const int hs = g.KS == 1 ? 0 : 1;
-    const int nhv = (TF + g.KT - 1) * (a.TH + 2 * hs) * (kTileW + 2 * hs);
+    const int hsy = g.KS == KS_1x1 ? 0 : 1;
+    const int hsx = g.KS == KS_1x1 || g.KS == KS_3x1 ? 0 : 1;
+    const int nhv = (TF + g.KT - 1) * (a.TH + 2 * hsy) * (kTileW + 2 * hsx);
     rows = std::max(rows, (nhv * np + 511) / 512 * 512 / np);  // whole rounds for 256 or 512 threads
   }
   a.nhv_max = rows;
@@ -332,7 +371,7 @@ double conv_flops(const ConvArgs& a) {
   const double vox = (double)a.F * a.H * a.W * a.nphase;
   for (int s = 0; s < a.nseg; ++s) {
     const ConvSeg& g = a.seg[s];
-    const int k2 = g.KS == 3 ? 9 : (g.KS == 2 ? 4 : 1);
+    const int k2 = g.KS == KS_3x3 ? 9 : (g.KS == KS_PHASE ? 4 : (g.KS == KS_3x1 ? 3 : 1));
     f += 2.0 * vox * a.Cout * (double)g.KT * k2 * g.Cin;
   }
   return f;
@@ -380,6 +419,48 @@ int tf_for(int KT, int F) {
   return KT == 3 ? 2 : 1;
 }
 
+// Causal 3x3x3 norm-SiLU conv in Winograd form along x:
+//   U = F(2,3) input transform of SiLU(norm(x)) over the F frames and the
+//       valid history frames (rs from rms_stats for the same slots),
+//   M[xi] = causal (t, y) 3x3 conv of U[xi] with the transformed weights,
+//   out = output transform of M + bias (+ res).
+// Same function as conv333 + EPI_H16, with 2/3 of the multiply-adds.
+void conv_wino(Ctx& cx, const Act& x, h16_t* ring, int nh, int gamma_item, int w_item, int b_item, int Cout,
+               const Act& out, const h16_t* res, long long res_fstride, int ldr) {
+  const int W2 = (x.W + 1) / 2;
+  h16_t* U = cx.wsp<h16_t>(cx.W->U);
+  h16_t* M = cx.wsp<h16_t>(cx.W->M);
+  const long long uslot = (long long)x.H * W2 * x.C;         // elements per U frame
+  const long long uplane = (long long)(x.F + 2) * uslot;      // per xi plane
+  const long long mframe = (long long)x.H * W2 * Cout;
+  cx.what = "wino_in";
+  cx.run(5, 0, [&] {
+    return launch_wino_in(x.p, x.fstride(), x.C, ring, nh, x.C, x.F, x.H, x.W, cx.wsp<float>(cx.W->rs),
+                          cx.prep<float>(gamma_item), U, cx.st);
+  });
+  ConvArgs a = args_init();
+  ConvSeg& g = a.seg[0];
+  g = seg_basic(U + 2 * uslot, uslot, x.C, x.C, cx.prep<h16_t>(w_item), x.C, 0, 3, KS_3x1, cx.wbytes(w_item));
+  g.ring = U;  // slots 0 and 1 of every plane: the history frames
+  g.n_hist = nh;
+  g.x_pstride = uplane;
+  a.nseg = 1;
+  a.nphase = 4;
+  a.Cout = Cout;
+  a.out = M;
+  a.out_fstride = mframe;
+  a.out_pstride = (long long)x.F * mframe;
+  a.ldo = Cout;
+  a.epi = EPI_WINO;
+  set_grid(a, x.F, x.H, W2, tf_for(3, x.F));
+  conv(cx, a, 0);
+  cx.what = "wino_out";
+  cx.run(5, 0, [&] {
+    return launch_wino_out(M, Cout, x.F, x.H, x.W, cx.prep<float>(b_item), res, res_fstride, ldr, out.p,
+                           out.fstride(), out.C, cx.st);
+  });
+}
+
 // Causal 3x3x3 conv with the fused RMSNorm+SiLU prologue.
 ConvArgs conv333(Ctx& cx, const Act& x, h16_t* ring, int nh, int gamma_item, int w_item, int b_item, int Cout) {
   ConvArgs a = args_init();
@@ -403,7 +484,9 @@ Act resblock(Ctx& cx, const RB& rb, const Act& x, h16_t* hbuf, h16_t* obuf, int 
   h16_t* r2 = cx.wsp<h16_t>(cx.W->ring[ring2]);
   stats(cx, x, r1, nh);
   Act h{hbuf, rb.cout, x.F, x.H, x.W};
-  {
+  if (rb.wino1) {
+    conv_wino(cx, x, r1, nh, rb.norm1, rb.conv1w, rb.conv1b, rb.cout, h, nullptr, 0, 0);
+  } else {
     ConvArgs a = conv333(cx, x, r1, nh, rb.norm1, rb.conv1w, rb.conv1b, rb.cout);
     a.out = h.p;
     a.out_fstride = h.fstride();
@@ -415,7 +498,9 @@ Act resblock(Ctx& cx, const RB& rb, const Act& x, h16_t* hbuf, h16_t* obuf, int 
   ring_update(cx, r1, x);
   stats(cx, h, r2, nh);
   Act out{rb.cin == rb.cout ? x.p : obuf, rb.cout, x.F, x.H, x.W};
-  {
+  if (rb.wino2) {  // widths equal: residual x, written in place
+    conv_wino(cx, h, r2, nh, rb.norm2, rb.conv2w, rb.conv2b, rb.cout, out, x.p, x.fstride(), x.C);
+  } else {
     ConvArgs a = conv333(cx, h, r2, nh, rb.norm2, rb.conv2w, rb.conv2b, rb.cout);
     if (rb.cin == rb.cout) {
       a.res = x.p;
@@ -614,7 +699,9 @@ int wvd_prepare(int c, int h, int w, const void* const* weights, int n_weights, 
     const Item& it = L.items[i];
     const void* src = weights[i];
     void* dst = p->prep + it.off;
-    if (it.kind == K_CONV)
+    if (it.kind == K_WINO)
+      e = launch_prep_wino_frag(src, weight_dtype, it.cout, it.cin, static_cast<h16_t*>(dst), s);
+    else if (it.kind == K_CONV)
       e = launch_prep_frag(src, weight_dtype, it.cout, it.cin, it.taps, it.cin_pad, static_cast<h16_t*>(dst), s);
     else if (it.kind == K_PHASE)
       e = launch_prep_phase_frag(src, weight_dtype, it.cout, static_cast<h16_t*>(dst), s);
@@ -774,8 +861,8 @@ int wvd_profile_read(const wvd_plan* cplan, double* ms, double* flops, long long
   if (!plan_ok(cplan) || !ms || !flops || !launches || n_classes < 1) return WVD_EINVAL;
   wvd_plan* plan = const_cast<wvd_plan*>(cplan);
   if (!plan->recs.empty() && hipEventSynchronize(plan->recs.back().e1) != hipSuccess) return WVD_EHIP;
-  double m[5] = {0, 0, 0, 0, 0}, f[5] = {0, 0, 0, 0, 0};
-  long long n[5] = {0, 0, 0, 0, 0};
+  double m[6] = {0, 0, 0, 0, 0, 0}, f[6] = {0, 0, 0, 0, 0, 0};
+  long long n[6] = {0, 0, 0, 0, 0, 0};
   for (const ProfRec& r : plan->recs) {
     float t = 0;
     if (hipEventElapsedTime(&t, r.e0, r.e1) != hipSuccess) return WVD_EHIP;
@@ -783,7 +870,7 @@ int wvd_profile_read(const wvd_plan* cplan, double* ms, double* flops, long long
     f[r.cls] += r.flops;
     n[r.cls] += 1;
   }
-  for (int i = 0; i < n_classes && i < 5; ++i) {
+  for (int i = 0; i < n_classes && i < 6; ++i) {
     ms[i] = m[i];
     flops[i] = f[i];
     launches[i] = n[i];

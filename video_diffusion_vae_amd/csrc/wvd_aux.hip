@@ -301,6 +301,131 @@ __global__ void prep_phase_frag_kernel(const void* __restrict__ w, int dtype, in
   }
 }
 
+// Winograd F(2,3) weights along x (Lavin and Gray's minimal filtering with
+// interpolation points 0, 1, -1, infinity): for each (o, i, dt, dy) the x taps
+// g0..g2 become V = (g0, (g0+g1+g2)/2, (g0-g1+g2)/2, g2), computed in fp32
+// and rounded once to fp16; fragment order with tap = xi * 9 + dt * 3 + dy.
+__global__ void prep_wino_frag_kernel(const void* __restrict__ w, int dtype, int cout, int cin,
+                                      h16_t* __restrict__ out) {
+  const int NB = (cout + 127) / 128 * 4, U = cin / 16;
+  const long long n = (long long)NB * U * 36 * 512;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+       e += (long long)gridDim.x * blockDim.x) {
+    const int j = (int)(e & 7);
+    const int l = (int)((e >> 3) & 63);
+    const long long blk = e >> 9;
+    const int t36 = (int)(blk % 36);
+    const int u = (int)((blk / 36) % U);
+    const int nb = (int)(blk / (36LL * U));
+    const int o = nb * 32 + (l & 31);
+    const int i = u * 16 + (l >> 5) * 8 + j;
+    float v = 0.0f;
+    if (o < cout && i < cin) {
+      const int xi = t36 / 9, tdy = t36 % 9;  // tdy = dt * 3 + dy
+      const long long wp = ((long long)o * cin + i) * 27 + tdy * 3;
+      const float g0 = load_in(w, wp, dtype), g1 = load_in(w, wp + 1, dtype), g2 = load_in(w, wp + 2, dtype);
+      v = xi == 0 ? g0 : (xi == 1 ? 0.5f * (g0 + g1 + g2) : (xi == 2 ? 0.5f * (g0 - g1 + g2) : g2));
+    }
+    out[e] = (h16_t)f2h(v);
+  }
+}
+
+// Input transform: one thread per (slot, row, pair, 8-channel group).
+__global__ __launch_bounds__(256) void wino_in_kernel(const h16_t* __restrict__ x, long long x_fstride, int lda,
+                                                      const h16_t* __restrict__ ring, int first_slot, int C, int S,
+                                                      int H, int W, int W2, const float* __restrict__ rs,
+                                                      const float* __restrict__ gamma, h16_t* __restrict__ U) {
+  const int G8 = C >> 3;
+  const long long HW = (long long)H * W;
+  const long long plane = (long long)S * H * W2 * C;  // elements per xi plane
+  const long long n = (long long)(S - first_slot) * H * W2 * G8;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+       e += (long long)gridDim.x * blockDim.x) {
+    const int g = (int)(e % G8);
+    long long r = e / G8;
+    const int p = (int)(r % W2);
+    r /= W2;
+    const int row = (int)(r % H);
+    const int slot = (int)(r / H) + first_slot;
+    float gm[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) gm[k] = gamma[g * 8 + k];
+    float y[4][8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int col = 2 * p - 1 + k;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) y[k][q] = 0.0f;
+      if (col >= 0 && col < W) {
+        const long long pix = (long long)row * W + col;
+        const h16_t* src = slot < 2 ? ring + ((long long)slot * HW + pix) * C : x + (slot - 2) * x_fstride + pix * lda;
+        float f[8];
+        unpack8h(*reinterpret_cast<const uint4*>(src + g * 8), f);
+        const float sc = rs[(long long)slot * HW + pix];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float t = f[q] * sc * gm[q];
+          y[k][q] = t * __builtin_amdgcn_rcpf(1.0f + __expf(-t));
+        }
+      }
+    }
+    h16_t* dst = U + ((long long)slot * H * W2 + (long long)row * W2 + p) * C + g * 8;
+    float u[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) u[q] = y[0][q] - y[2][q];
+    *reinterpret_cast<uint4*>(dst) = pack8h(u);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) u[q] = y[1][q] + y[2][q];
+    *reinterpret_cast<uint4*>(dst + plane) = pack8h(u);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) u[q] = y[2][q] - y[1][q];
+    *reinterpret_cast<uint4*>(dst + 2 * plane) = pack8h(u);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) u[q] = y[1][q] - y[3][q];
+    *reinterpret_cast<uint4*>(dst + 3 * plane) = pack8h(u);
+  }
+}
+
+// Output transform: one thread per (frame, row, pair, 8-channel group).
+__global__ __launch_bounds__(256) void wino_out_kernel(const h16_t* __restrict__ M, int Cout, int F, int H, int W,
+                                                       int W2, const float* __restrict__ bias,
+                                                       const h16_t* res, long long res_fstride, int ldr, h16_t* out,
+                                                       long long out_fstride, int ldo) {
+  const int G8 = Cout >> 3;
+  const long long plane = (long long)F * H * W2 * Cout;
+  const long long n = (long long)F * H * W2 * G8;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+       e += (long long)gridDim.x * blockDim.x) {
+    const int g = (int)(e % G8);
+    long long r = e / G8;
+    const int p = (int)(r % W2);
+    r /= W2;
+    const int row = (int)(r % H);
+    const int f = (int)(r / H);
+    const h16_t* src = M + (((long long)f * H + row) * W2 + p) * Cout + g * 8;
+    float m[4][8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) unpack8h(*reinterpret_cast<const uint4*>(src + k * plane), m[k]);
+#pragma unroll
+    for (int e2 = 0; e2 < 2; ++e2) {
+      const int col = 2 * p + e2;
+      if (col >= W) break;
+      const long long pix = (long long)row * W + col;
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        v[q] = (e2 == 0 ? m[0][q] + m[1][q] + m[2][q] : m[1][q] - m[2][q] - m[3][q]) + (bias ? bias[g * 8 + q] : 0.0f);
+      if (res) {
+        float rr[8];
+        unpack8h(*reinterpret_cast<const uint4*>(res + f * res_fstride + pix * ldr + g * 8), rr);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] += rr[q];
+      }
+      *reinterpret_cast<uint4*>(out + f * out_fstride + pix * ldo + g * 8) = pack8h(v);
+    }
+  }
+}
+
 __global__ void prep_vec_kernel(const void* __restrict__ v, int dtype, int n, float scale, float* __restrict__ out) {
   for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < n; e += gridDim.x * blockDim.x)
     out[e] = load_in(v, e, dtype) * scale;
@@ -407,6 +532,36 @@ hipError_t launch_prep_phase_frag(const void* w, int dtype, int C, h16_t* out, h
   if (g_dry_run) return hipSuccess;
   const long long n = (long long)prep_frag_bytes(C, C, 16) / 2;
   hipLaunchKernelGGL(prep_phase_frag_kernel, dim3(grid_for(n)), dim3(256), 0, s, w, dtype, C, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep_wino_frag(const void* w, int dtype, int cout, int cin, h16_t* out, hipStream_t s) {
+  if (g_dry_run) return hipSuccess;
+  if (cin % 16) return hipErrorInvalidValue;
+  const long long n = (long long)prep_frag_bytes(cout, cin, 36) / 2;
+  hipLaunchKernelGGL(prep_wino_frag_kernel, dim3(grid_for(n)), dim3(256), 0, s, w, dtype, cout, cin, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_wino_in(const h16_t* x, long long x_fstride, int lda, const h16_t* ring, int n_hist, int C, int F,
+                          int H, int W, const float* rs, const float* gamma, h16_t* U, hipStream_t s) {
+  if (g_dry_run) return hipSuccess;
+  if (C % 8 || n_hist < 0 || n_hist > 2 || (n_hist > 0 && !ring) || F < 1) return hipErrorInvalidValue;
+  const int W2 = (W + 1) / 2;
+  const long long n = (long long)(F + n_hist) * H * W2 * (C / 8);
+  hipLaunchKernelGGL(wino_in_kernel, dim3(grid_for(n, 256, 65536)), dim3(256), 0, s, x, x_fstride, lda, ring,
+                     2 - n_hist, C, F + 2, H, W, W2, rs, gamma, U);
+  return hipGetLastError();
+}
+
+hipError_t launch_wino_out(const h16_t* M, int Cout, int F, int H, int W, const float* bias, const h16_t* res,
+                           long long res_fstride, int ldr, h16_t* out, long long out_fstride, int ldo, hipStream_t s) {
+  if (g_dry_run) return hipSuccess;
+  if (Cout % 8 || ldo % 8 || (res && ldr % 8)) return hipErrorInvalidValue;
+  const int W2 = (W + 1) / 2;
+  const long long n = (long long)F * H * W2 * (Cout / 8);
+  hipLaunchKernelGGL(wino_out_kernel, dim3(grid_for(n, 256, 65536)), dim3(256), 0, s, M, Cout, F, H, W, W2, bias, res,
+                     res_fstride, ldr, out, out_fstride, ldo);
   return hipGetLastError();
 }
 

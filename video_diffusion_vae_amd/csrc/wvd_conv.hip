@@ -820,15 +820,17 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
   constexpr bool K333 = MODE == 1;
   constexpr bool NORM = PRO0 == PRO_NORM || PRO0 == PRO_NORM_SILU;
   constexpr bool ACT = PRO0 == PRO_NORM_SILU;
-  constexpr bool KT3 = MODE == 3;  // 3x1x1 temporal conv (time_conv)
+  constexpr bool KT3 = MODE == 3;   // 3x1x1 temporal conv (time_conv)
+  constexpr bool WINO = MODE == 4;  // Winograd-domain 3x3x1 (t, y) GEMM, one xi per phase
   constexpr int TF = MODE == 2 ? 1 : kTF333;
   constexpr int TH = MODE == 2 ? 16 : kTH333;
   constexpr int KT = MODE == 2 ? 1 : 3;
-  constexpr int HS = KT3 ? 0 : 1;  // spatial halo
-  constexpr int HX = kTileW + 2 * HS, HY = TH + 2 * HS, HF = TF + KT - 1;
+  constexpr int HSX = KT3 || WINO ? 0 : 1;  // spatial halo along x
+  constexpr int HSY = KT3 ? 0 : 1;          // and along y
+  constexpr int HX = kTileW + 2 * HSX, HY = TH + 2 * HSY, HF = TF + KT - 1;
   constexpr int NHV = HF * HY * HX;
-  constexpr int NTAPS = K333 ? 27 : (KT3 ? 3 : 4);
-  static_assert(MODE >= 1 && MODE <= 3, "specialised tap sets only");
+  constexpr int NTAPS = K333 ? 27 : (KT3 ? 3 : (WINO ? 9 : 4));
+  static_assert(MODE >= 1 && MODE <= 4, "specialised tap sets only");
   static_assert(WN % 32 == 0 && MI >= 1, "wave tile");
 
   extern __shared__ __align__(16) unsigned char smem[];
@@ -867,15 +869,15 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
         const int hy = t2 % HY;
         const int hf = t2 / HY;
         const int fo = t.f0 + hf - (KT - 1);
-        const int y = t.y0 + hy - HS;
-        const int x = t.x0 + hx - HS;
+        const int y = t.y0 + hy - HSY;
+        const int x = t.x0 + hx - HSX;
         if (y >= 0 && y < a.H && x >= 0 && x < a.W && fo < a.F) {
           const long long pix = (long long)y * a.W + x;
           const h16_t* q = nullptr;
           if (fo >= 0) {
-            q = S.x + fo * S.x_fstride + pix * S.lda;
+            q = S.x + t.ph * S.x_pstride + fo * S.x_fstride + pix * S.lda;
           } else if (fo + 2 >= 2 - S.n_hist) {
-            q = S.ring + (long long)(fo + 2) * HW * S.Cin + pix * S.Cin;
+            q = S.ring + t.ph * S.x_pstride + (long long)(fo + 2) * HW * S.Cin + pix * S.Cin;
           }
           if (q) {
             p = q;
@@ -937,7 +939,7 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
     const SegCtx<BK, MI, NJ, NT> g = ctx_for(seq.at(0), 0);
     for (int idx = tid; idx < nhv_max * NP; idx += NT)
       halo_store<NORM, ACT>(g, idx, 0, halo_load(g, idx, 0), smem);
-    constexpr int PRE = K333 ? kBRing : (KT3 ? 3 : 4);
+    constexpr int PRE = K333 || WINO ? kBRing : (KT3 ? 3 : 4);
 #pragma unroll
     for (int u = 0; u < PRE; ++u) {
       load_step(g, bq[u], 0, u >> 1, u & 1);
@@ -1034,6 +1036,37 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
               load_step(gn, bq[s6 % kBRing], cn, t3 - 27, ks3);
             __builtin_amdgcn_sched_barrier(0);
           }
+        }
+      } else if constexpr (WINO) {
+        // 9 (dt, dy) taps x two k16 steps over one xi plane; B fragments of
+        // step u in slot u % 6, refilled with step u + 6 (three taps ahead);
+        // halo item t loaded at tap t and stored at tap t + 3.
+        constexpr int IPT = (NHV * NP + NT - 1) / NT;
+        static_assert(IPT + 3 <= 9, "halo items must land inside a chunk");
+        uint4 hr[3];
+#pragma unroll
+        for (int u = 0; u < 18; ++u) {
+          const int tap = u >> 1, ks = u & 1;
+          const int dt = tap / 3, dy = tap % 3;
+          if (ks == 0) {
+            if (tap >= 3 && tap - 3 < IPT) halo_store<false, false>(gn, tid + NT * (tap - 3), cn, hr[tap % 3], hdst);
+            if (tap < IPT) hr[tap % 3] = halo_load(gn, tid + NT * tap, cn);
+          }
+          const int toff = (dt * HY + dy) * HX * ROWB;
+          f16x8_t av[MI];
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+            av[i] = *reinterpret_cast<const f16x8_t*>(hsrc + g.abase[i] + toff + ks * 32);
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bq[u % kBRing][j], acc[i][j], 0, 0, 0);
+          if (u + kBRing < 18)
+            load_step(g, bq[u % kBRing], c, (u + kBRing) >> 1, (u + kBRing) & 1);
+          else
+            load_step(gn, bq[u % kBRing], cn, (u + kBRing - 18) >> 1, (u + kBRing) & 1);
+          __builtin_amdgcn_sched_barrier(0);
         }
       } else if constexpr (KT3) {
         // three temporal taps x two k16 steps; B fragments of step u live in
@@ -1145,6 +1178,8 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
             if (a.epi == EPI_PHASE) {
               const long long op = (long long)(2 * y + (geo.ph >> 1)) * (2 * a.W) + (2 * x + (geo.ph & 1));
               o = static_cast<h16_t*>(a.out) + f * a.out_fstride + op * a.ldo;
+            } else if (a.epi == EPI_WINO) {
+              o = static_cast<h16_t*>(a.out) + geo.ph * a.out_pstride + f * a.out_fstride + pix * a.ldo;
             } else if (a.epi == EPI_TIME) {
               // channel half h of frame f -> output frame out_base + 2f + h
               const int Chalf = a.Cout >> 1;
@@ -1271,9 +1306,12 @@ Variant conv_variant(const ConvArgs& a) {
                    v.bk == 32 && a.nseg == 1 && g.wfrag && g.prologue == PRO_RAW;
   const bool kt3 = g.KT == 3 && g.KS == 1 && a.nphase == 1 && a.TF == kTF333 && a.TH == kTH333 && v.bk == 32 &&
                    a.nseg == 1 && g.wfrag && g.prologue == PRO_RAW && a.Cout % 256 == 0 && a.epi == EPI_TIME;
+  const bool kwino = g.KT == 3 && g.KS == KS_3x1 && a.nphase == 4 && a.TF == kTF333 && a.TH == kTH333 &&
+                     v.bk == 32 && a.nseg == 1 && g.wfrag && g.prologue == PRO_RAW && a.Cout % 256 == 0 &&
+                     a.epi == EPI_WINO;
   const bool shortcut_ok = a.nseg == 1 || (a.seg[1].KT == 1 && a.seg[1].KS == 1 && a.seg[1].prologue == PRO_RAW &&
                                             a.seg[1].wfrag && a.seg[1].Cin % 32 == 0);
-  v.mode = k333 ? 1 : (kph ? 2 : (kt3 ? 3 : 0));
+  v.mode = k333 ? 1 : (kph ? 2 : (kt3 ? 3 : (kwino ? 4 : 0)));
   if (v.mode != 0 && a.Cout % 256 == 0 && shortcut_ok) {
     v.bn = 256;
     v.nw = 8;
@@ -1298,6 +1336,7 @@ bool conv_persistent(const ConvArgs& a) {
   if (v.mode == 0 || v.nw != 8 || a.nseg != 1) return false;
   if (v.bn == 32) return v.mode == 1 && a.epi == EPI_VIDEO && a.seg[0].prologue == PRO_RAW;
   if (v.mode == 3) return a.epi == EPI_TIME;
+  if (v.mode == 4) return a.epi == EPI_WINO;
   return a.epi == (v.mode == 2 ? EPI_PHASE : EPI_H16) || (v.mode == 1 && a.epi == EPI_VIDEO);
 }
 
@@ -1305,7 +1344,8 @@ bool conv_is_333(const ConvArgs& a) { return conv_variant(a).mode == 1; }
 
 bool conv_is_main(const ConvArgs& a) {
   const Variant v = conv_variant(a);
-  return conv_persistent(a) && v.mode == 1 && v.bn == 256 && a.seg[0].prologue == PRO_NORM_SILU;
+  return conv_persistent(a) &&
+         (v.mode == 4 || (v.mode == 1 && v.bn == 256 && a.seg[0].prologue == PRO_NORM_SILU));
 }
 
 size_t conv_lds_bytes(const ConvArgs& a) {
@@ -1331,16 +1371,20 @@ const char* conv_check(const ConvArgs& a) {
   const int bk = conv_bk(a);
   for (int s = 0; s < a.nseg; ++s) {
     const ConvSeg& g = a.seg[s];
-    const int hs = g.KS == 1 ? 0 : 1;
-    const int k2 = g.KS == 3 ? 3 : (g.KS == 2 ? 2 : 1);
-    const int nhv = (a.TF + g.KT - 1) * (a.TH + 2 * hs) * (kTileW + 2 * hs);
+    const int hsy = g.KS == KS_1x1 ? 0 : 1;
+    const int hsx = g.KS == KS_1x1 || g.KS == KS_3x1 ? 0 : 1;
+    const int k2 = g.KS == KS_3x3 ? 9 : (g.KS == KS_PHASE ? 4 : (g.KS == KS_3x1 ? 3 : 1));
+    const int nhv = (a.TF + g.KT - 1) * (a.TH + 2 * hsy) * (kTileW + 2 * hsx);
     const int nt = conv_variant(a).nw * 64;
     const int ipt = (nhv * (bk / 8) + nt - 1) / nt;
-    const int ntaps = g.KT * k2 * k2;
+    const int ntaps = g.KT * k2;
     if (!g.x || !g.w) return "null operand";
     if (g.KT != 1 && g.KT != 3) return "KT must be 1 or 3";
-    if (g.KS != 1 && g.KS != 2 && g.KS != 3) return "KS must be 1, 2 or 3";
-    if ((g.KS == 2) != (a.nphase == 4)) return "phase taps need 4 phases";
+    if (g.KS < KS_1x1 || g.KS > KS_3x1) return "unknown spatial tap code";
+    if ((g.KS == KS_PHASE || g.KS == KS_3x1) != (a.nphase == 4)) return "phase / xi taps need 4 phases";
+    if (g.KS == KS_3x1 && (a.epi != EPI_WINO || conv_variant(a).mode != 4))
+      return "3x1 taps run only as the Winograd-domain GEMM";
+    if ((a.epi == EPI_WINO) != (g.KS == KS_3x1)) return "EPI_WINO needs the 3x1 taps";
     if (nhv > a.nhv_max) return "halo larger than nhv_max";
     if ((g.KT == 3 && g.KS == 3 && a.TF == kTF333 && a.TH == kTH333 &&
          ((kNHV333 * (bk / 8) + 511) / 512) * 512 / (bk / 8) > a.nhv_max))
@@ -1367,6 +1411,7 @@ hipError_t launch_conv(const ConvArgs& a, hipStream_t stream) {
     const int pro = a.seg[0].prologue;
     if (v.mode == 2) return launch_persist_impl<256, 4, 2, PRO_RAW>(a, stream);
     if (v.mode == 3) return launch_persist_impl<256, 4, 3, PRO_RAW>(a, stream);
+    if (v.mode == 4) return launch_persist_impl<256, 4, 4, PRO_RAW>(a, stream);
     if (v.bn == 32) return launch_persist_impl<32, 1, 1, PRO_RAW>(a, stream);
 #if WVD_MAIN_W4
     if (pro == PRO_NORM_SILU) return launch_persist_impl<256, 2, 1, PRO_NORM_SILU, 4>(a, stream);
@@ -1374,7 +1419,7 @@ hipError_t launch_conv(const ConvArgs& a, hipStream_t stream) {
     return pro == PRO_NORM_SILU ? launch_persist_impl<256, 4, 1, PRO_NORM_SILU>(a, stream)
                                 : launch_persist_impl<256, 4, 1, PRO_RAW>(a, stream);
   }
-  if (v.mode == 3) return hipErrorInvalidValue;  // the time_conv tap set exists only in the persistent kernel
+  if (v.mode >= 3) return hipErrorInvalidValue;  // these tap sets exist only in the persistent kernel
   if (v.mode == 1) {
     const bool act = a.seg[0].prologue == PRO_NORM_SILU;
     if (v.nw == 8 && v.bn == 32) {

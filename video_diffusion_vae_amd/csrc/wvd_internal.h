@@ -20,7 +20,16 @@ enum Epilogue {
   EPI_F32 = 1,     // fp32 (scaled), e.g. attention logits
   EPI_TIME = 2,    // time_conv: channels [0,C) -> frame 2s+base, [C,2C) -> 2s+1+base
   EPI_PHASE = 3,   // up-conv phase (py,px): voxel (y,x) -> (2y+py, 2x+px)
-  EPI_VIDEO = 4    // head: 2x2 pixel shuffle of 12 channels, clamp, NCTHW video
+  EPI_VIDEO = 4,   // head: 2x2 pixel shuffle of 12 channels, clamp, NCTHW video
+  EPI_WINO = 5     // Winograd-domain product M[xi] (fp16, no bias): out + xi * out_pstride
+};
+
+// Spatial tap codes of a K segment (ConvSeg::KS).
+enum SpatialTaps {
+  KS_1x1 = 1,    // 1x1
+  KS_PHASE = 2,  // 2x2 phase taps of an up-conv
+  KS_3x3 = 3,    // 3x3, pad 1
+  KS_3x1 = 4     // 3 rows x 1 column, row pad 1 (the Winograd-domain GEMM along x)
 };
 
 // One K segment of the implicit GEMM: a (possibly normalised) input tensor,
@@ -36,11 +45,12 @@ struct ConvSeg {
   long long w_frame_stride; // per-frame weight offset (attention GEMMs), else 0
   int lda, ldw, Cin;
   int KT;                   // temporal taps: 1 or 3 (causal, history frames first)
-  int KS;                   // spatial taps: 1 (1x1), 3 (3x3, pad 1), 2 (2x2 phase)
+  int KS;                   // spatial taps (SpatialTaps)
   int n_hist;               // valid history frames in ring (0..2)
   int prologue;             // Prologue
   int wfrag;                // 1: w is in MFMA fragment order (see launch_prep_frag)
   long long w_bytes;        // bytes of w (fragment order: bounds of the buffer loads)
+  long long x_pstride;      // per-phase input offset (Winograd xi planes), else 0
 };
 
 struct ConvArgs {
@@ -49,7 +59,7 @@ struct ConvArgs {
   int F, H, W;              // output voxel grid (input grid for phase mode)
   int TF, TH;               // tile frames / rows
   int tiles_x, tiles_y, tiles_f;
-  int nphase;               // 4 for EPI_PHASE, else 1
+  int nphase;               // 4 for EPI_PHASE and EPI_WINO (xi), else 1
   int Cout;
   const float* bias;        // [Cout] fp32 or null
   float scale;
@@ -58,6 +68,7 @@ struct ConvArgs {
   int ldr;
   void* out;
   long long out_fstride;
+  long long out_pstride;    // EPI_WINO: elements per xi plane of the output
   int ldo;
   int epi;
   int out_base;             // EPI_TIME frame base; EPI_VIDEO first frame index
@@ -115,6 +126,23 @@ hipError_t launch_prep_frag(const void* w, int dtype, int cout, int cin, int tap
 // Up-conv phase weights in the same fragment order with taps = 16
 // (phase * 4 + 2x2 tap).
 hipError_t launch_prep_phase_frag(const void* w, int dtype, int C, h16_t* out, hipStream_t s);
+// Winograd F(2,3) weights of a 3x3x3 conv along x: for each (dt, dy) the three
+// x taps g become V = (g0, (g0+g1+g2)/2, (g0-g1+g2)/2, g2) (fp32, rounded once
+// to fp16), in fragment order with taps = 36 (xi * 9 + dt * 3 + dy).
+hipError_t launch_prep_wino_frag(const void* w, int dtype, int cout, int cin, h16_t* out, hipStream_t s);
+
+// Winograd F(2,3) along x of the normalised input: for slots s = 0..F+1
+// (s = 0, 1: the two history frames in `ring`, only the last n_hist valid;
+// s >= 2: frame s-2 of x), every column pair p and channel,
+//   y_k = SiLU(x[2p-1+k] * rs * gamma)  (k = 0..3, zero outside 0..W-1)
+//   U[xi][s][row][p] = (y0-y2, y1+y2, y2-y1, y1-y3)[xi]   (fp16)
+// U is [4][F+2][H][W2][C] with W2 = ceil(W/2); rs as rms_stats writes it.
+hipError_t launch_wino_in(const h16_t* x, long long x_fstride, int lda, const h16_t* ring, int n_hist, int C, int F,
+                          int H, int W, const float* rs, const float* gamma, h16_t* U, hipStream_t s);
+// Output transform: out[f][row][2p] = M0+M1+M2 + bias (+ res), out[..][2p+1] =
+// M1-M2-M3 + bias (+ res), M = [4][F][H][W2][Cout] fp16; out may alias res.
+hipError_t launch_wino_out(const h16_t* M, int Cout, int F, int H, int W, const float* bias, const h16_t* res,
+                           long long res_fstride, int ldr, h16_t* out, long long out_fstride, int ldo, hipStream_t s);
 hipError_t launch_prep_vec(const void* v, int dtype, int n, float scale, float* out, hipStream_t s);
 // out[i] = a[i] + b[i] in fp32 (the two biases of a block with a shortcut).
 hipError_t launch_prep_vec_add(const void* a, const void* b, int dtype, int n, float* out, hipStream_t s);

@@ -22,7 +22,7 @@ WVD_EHIP = -5
 NUM_WEIGHTS = 84
 WVD_DTYPE_BF16 = 0
 WVD_DTYPE_F32 = 1
-PROFILE_CLASSES = ("conv3x3x3_main", "conv_other", "attention_gemm", "norm_stats", "copies")
+PROFILE_CLASSES = ("conv3x3x3_main", "conv_other", "attention_gemm", "norm_stats", "copies", "wino_transforms")
 
 
 class WvdError(RuntimeError):
