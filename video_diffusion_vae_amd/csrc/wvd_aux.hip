@@ -348,8 +348,12 @@ __global__ __launch_bounds__(256) void wino_in_kernel(const h16_t* __restrict__ 
     const int row = (int)(r % H);
     const int slot = (int)(r / H) + first_slot;
     float gm[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) gm[k] = gamma[g * 8 + k];
+    {
+      const float4 g0 = *reinterpret_cast<const float4*>(gamma + g * 8);
+      const float4 g1 = *reinterpret_cast<const float4*>(gamma + g * 8 + 4);
+      gm[0] = g0.x; gm[1] = g0.y; gm[2] = g0.z; gm[3] = g0.w;
+      gm[4] = g1.x; gm[5] = g1.y; gm[6] = g1.z; gm[7] = g1.w;
+    }
     float y[4][8];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -403,25 +407,35 @@ __global__ __launch_bounds__(256) void wino_out_kernel(const h16_t* __restrict__
     const int row = (int)(r % H);
     const int f = (int)(r / H);
     const h16_t* src = M + (((long long)f * H + row) * W2 + p) * Cout + g * 8;
+    uint4 mr[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) mr[k] = *reinterpret_cast<const uint4*>(src + k * plane);
+    const bool two = 2 * p + 1 < W;
+    const long long pix0 = (long long)row * W + 2 * p;
+    uint4 rr[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+    if (res) {
+      rr[0] = *reinterpret_cast<const uint4*>(res + f * res_fstride + pix0 * ldr + g * 8);
+      if (two) rr[1] = *reinterpret_cast<const uint4*>(res + f * res_fstride + (pix0 + 1) * ldr + g * 8);
+    }
+    float b[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (bias) {
+      const float4 b0 = *reinterpret_cast<const float4*>(bias + g * 8);
+      const float4 b1 = *reinterpret_cast<const float4*>(bias + g * 8 + 4);
+      b[0] = b0.x; b[1] = b0.y; b[2] = b0.z; b[3] = b0.w;
+      b[4] = b1.x; b[5] = b1.y; b[6] = b1.z; b[7] = b1.w;
+    }
     float m[4][8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) unpack8h(*reinterpret_cast<const uint4*>(src + k * plane), m[k]);
+    for (int k = 0; k < 4; ++k) unpack8h(mr[k], m[k]);
 #pragma unroll
     for (int e2 = 0; e2 < 2; ++e2) {
-      const int col = 2 * p + e2;
-      if (col >= W) break;
-      const long long pix = (long long)row * W + col;
-      float v[8];
+      if (e2 == 1 && !two) break;
+      float v[8], r8[8];
+      unpack8h(rr[e2], r8);
 #pragma unroll
       for (int q = 0; q < 8; ++q)
-        v[q] = (e2 == 0 ? m[0][q] + m[1][q] + m[2][q] : m[1][q] - m[2][q] - m[3][q]) + (bias ? bias[g * 8 + q] : 0.0f);
-      if (res) {
-        float rr[8];
-        unpack8h(*reinterpret_cast<const uint4*>(res + f * res_fstride + pix * ldr + g * 8), rr);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] += rr[q];
-      }
-      *reinterpret_cast<uint4*>(out + f * out_fstride + pix * ldo + g * 8) = pack8h(v);
+        v[q] = (e2 == 0 ? m[0][q] + m[1][q] + m[2][q] : m[1][q] - m[2][q] - m[3][q]) + b[q] + r8[q];
+      *reinterpret_cast<uint4*>(out + f * out_fstride + (pix0 + e2) * ldo + g * 8) = pack8h(v);
     }
   }
 }
