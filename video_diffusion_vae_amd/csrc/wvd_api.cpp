@@ -279,6 +279,10 @@ struct Ctx {
   const Work* W;
   hipError_t err = hipSuccess;
   const char* what = "";
+  // The tensor (data pointer and frame count) whose pass-frame statistics the
+  // rs buffer already holds (written by a Winograd output transform), or null.
+  const h16_t* rs_tensor = nullptr;
+  int rs_frames = 0;
 
   template <typename T>
   T* prep(int item) const { return reinterpret_cast<T*>(plan->prep + plan->L.items[item].off); }
@@ -387,6 +391,7 @@ void conv(Ctx& cx, ConvArgs& a, int cls) {
     return;
   }
   cx.what = "conv";
+  cx.rs_tensor = nullptr;  // any conv may overwrite the tensor whose statistics rs holds
   // Class 0 is exactly the dominant kernel instantiation; other convs of
   // the caller's class 0 are reported as class 1.
   if (cls == 0 && !conv_is_main(a)) cls = 1;
@@ -401,10 +406,15 @@ struct Act {
   long long fstride() const { return (long long)H * W * C; }
 };
 
+// rs for the history slots and the F pass frames of x; the pass frames are
+// skipped when the output transform that produced x already wrote them.
 void stats(Ctx& cx, const Act& x, const h16_t* ring, int nh) {
   float* rs = cx.wsp<float>(cx.W->rs);
+  const int F = (cx.rs_tensor == x.p && cx.rs_frames == x.F) ? 0 : x.F;
+  cx.rs_tensor = nullptr;
+  if (F + nh == 0) return;
   cx.what = "rms_stats";
-  cx.run(3, 0, [&] { return launch_rms_stats(x.p, x.fstride(), x.C, ring, nh, x.C, x.F, x.H * x.W, rs, cx.st); });
+  cx.run(3, 0, [&] { return launch_rms_stats(x.p, x.fstride(), x.C, ring, nh, x.C, F, x.H * x.W, rs, cx.st); });
 }
 
 void ring_update(Ctx& cx, h16_t* ring, const Act& x) {
@@ -457,8 +467,10 @@ void conv_wino(Ctx& cx, const Act& x, h16_t* ring, int nh, int gamma_item, int w
   cx.what = "wino_out";
   cx.run(5, 0, [&] {
     return launch_wino_out(M, Cout, x.F, x.H, x.W, cx.prep<float>(b_item), res, res_fstride, ldr, out.p,
-                           out.fstride(), out.C, cx.st);
+                           out.fstride(), out.C, cx.wsp<float>(cx.W->rs), cx.st);
   });
+  cx.rs_tensor = out.p;
+  cx.rs_frames = x.F;
 }
 
 // Causal 3x3x3 conv with the fused RMSNorm+SiLU prologue.

@@ -390,52 +390,83 @@ __global__ __launch_bounds__(256) void wino_in_kernel(const h16_t* __restrict__ 
   }
 }
 
-// Output transform: one thread per (frame, row, pair, 8-channel group).
+// Output transform.  G lanes share a column pair (G as in rms_stats_kernel);
+// lane `sub` takes channel groups sub and sub + G.  With rs != null the
+// kernel also writes the norm statistics of both output voxels, summed over
+// the rounded fp16 outputs in exactly rms_stats_kernel's order (lane sums in
+// group order, then the same butterfly), so a voxel's statistic does not
+// depend on which kernel computed it.
 __global__ __launch_bounds__(256) void wino_out_kernel(const h16_t* __restrict__ M, int Cout, int F, int H, int W,
-                                                       int W2, const float* __restrict__ bias,
+                                                       int W2, int G, const float* __restrict__ bias,
                                                        const h16_t* res, long long res_fstride, int ldr, h16_t* out,
-                                                       long long out_fstride, int ldo) {
+                                                       long long out_fstride, int ldo, float* __restrict__ rs) {
+  const int lane = threadIdx.x & 63;
+  const int sub = lane % G;
   const int G8 = Cout >> 3;
   const long long plane = (long long)F * H * W2 * Cout;
-  const long long n = (long long)F * H * W2 * G8;
-  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n;
-       e += (long long)gridDim.x * blockDim.x) {
-    const int g = (int)(e % G8);
-    long long r = e / G8;
-    const int p = (int)(r % W2);
-    r /= W2;
+  const long long npair = (long long)F * H * W2;
+  const int pairs_per_wave = 64 / G;
+  const long long gw = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const long long nw = ((long long)gridDim.x * blockDim.x) >> 6;
+  for (long long base = gw * pairs_per_wave; base < npair; base += nw * pairs_per_wave) {
+    const long long pr = base + lane / G;
+    const bool ok = pr < npair;
+    const int p = ok ? (int)(pr % W2) : 0;
+    const long long r = ok ? pr / W2 : 0;
     const int row = (int)(r % H);
     const int f = (int)(r / H);
-    const h16_t* src = M + (((long long)f * H + row) * W2 + p) * Cout + g * 8;
-    uint4 mr[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) mr[k] = *reinterpret_cast<const uint4*>(src + k * plane);
     const bool two = 2 * p + 1 < W;
     const long long pix0 = (long long)row * W + 2 * p;
-    uint4 rr[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
-    if (res) {
-      rr[0] = *reinterpret_cast<const uint4*>(res + f * res_fstride + pix0 * ldr + g * 8);
-      if (two) rr[1] = *reinterpret_cast<const uint4*>(res + f * res_fstride + (pix0 + 1) * ldr + g * 8);
+    float ss[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) {
+      const int g = sub + q2 * G;
+      if (!ok || g >= G8) continue;
+      const h16_t* src = M + (((long long)f * H + row) * W2 + p) * Cout + g * 8;
+      uint4 mr[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) mr[k] = *reinterpret_cast<const uint4*>(src + k * plane);
+      uint4 rr[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+      if (res) {
+        rr[0] = *reinterpret_cast<const uint4*>(res + f * res_fstride + pix0 * ldr + g * 8);
+        if (two) rr[1] = *reinterpret_cast<const uint4*>(res + f * res_fstride + (pix0 + 1) * ldr + g * 8);
+      }
+      float b[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (bias) {
+        const float4 b0 = *reinterpret_cast<const float4*>(bias + g * 8);
+        const float4 b1 = *reinterpret_cast<const float4*>(bias + g * 8 + 4);
+        b[0] = b0.x; b[1] = b0.y; b[2] = b0.z; b[3] = b0.w;
+        b[4] = b1.x; b[5] = b1.y; b[6] = b1.z; b[7] = b1.w;
+      }
+      float m[4][8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) unpack8h(mr[k], m[k]);
+#pragma unroll
+      for (int e2 = 0; e2 < 2; ++e2) {
+        if (e2 == 1 && !two) break;
+        float v[8], r8[8];
+        unpack8h(rr[e2], r8);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          v[q] = (e2 == 0 ? m[0][q] + m[1][q] + m[2][q] : m[1][q] - m[2][q] - m[3][q]) + b[q] + r8[q];
+        const uint4 packed = pack8h(v);
+        *reinterpret_cast<uint4*>(out + f * out_fstride + (pix0 + e2) * ldo + g * 8) = packed;
+        float h[8];
+        unpack8h(packed, h);
+        float t = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) t += h[k] * h[k];
+        ss[e2] += t;
+      }
     }
-    float b[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (bias) {
-      const float4 b0 = *reinterpret_cast<const float4*>(bias + g * 8);
-      const float4 b1 = *reinterpret_cast<const float4*>(bias + g * 8 + 4);
-      b[0] = b0.x; b[1] = b0.y; b[2] = b0.z; b[3] = b0.w;
-      b[4] = b1.x; b[5] = b1.y; b[6] = b1.z; b[7] = b1.w;
-    }
-    float m[4][8];
+    if (rs) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) unpack8h(mr[k], m[k]);
-#pragma unroll
-    for (int e2 = 0; e2 < 2; ++e2) {
-      if (e2 == 1 && !two) break;
-      float v[8], r8[8];
-      unpack8h(rr[e2], r8);
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-        v[q] = (e2 == 0 ? m[0][q] + m[1][q] + m[2][q] : m[1][q] - m[2][q] - m[3][q]) + b[q] + r8[q];
-      *reinterpret_cast<uint4*>(out + f * out_fstride + (pix0 + e2) * ldo + g * 8) = pack8h(v);
+      for (int e2 = 0; e2 < 2; ++e2) {
+        float v = ss[e2];
+        for (int off = 1; off < G; off <<= 1) v += __shfl_xor(v, off, 64);
+        if (ok && sub == 0 && (e2 == 0 || two))
+          rs[(long long)(f + 2) * H * W + pix0 + e2] = 1.0f / fmaxf(sqrtf(v), kNormEps);
+      }
     }
   }
 }
@@ -569,13 +600,17 @@ hipError_t launch_wino_in(const h16_t* x, long long x_fstride, int lda, const h1
 }
 
 hipError_t launch_wino_out(const h16_t* M, int Cout, int F, int H, int W, const float* bias, const h16_t* res,
-                           long long res_fstride, int ldr, h16_t* out, long long out_fstride, int ldo, hipStream_t s) {
+                           long long res_fstride, int ldr, h16_t* out, long long out_fstride, int ldo, float* rs,
+                           hipStream_t s) {
   if (g_dry_run) return hipSuccess;
-  if (Cout % 8 || ldo % 8 || (res && ldr % 8)) return hipErrorInvalidValue;
+  if (Cout % 8 || ldo % 8 || (res && ldr % 8) || Cout > 1024) return hipErrorInvalidValue;
+  int G = 1;
+  while (G < 64 && G * 2 <= Cout / 8) G *= 2;
   const int W2 = (W + 1) / 2;
-  const long long n = (long long)F * H * W2 * (Cout / 8);
-  hipLaunchKernelGGL(wino_out_kernel, dim3(grid_for(n, 256, 65536)), dim3(256), 0, s, M, Cout, F, H, W, W2, bias, res,
-                     res_fstride, ldr, out, out_fstride, ldo);
+  const long long npair = (long long)F * H * W2;
+  const long long waves = (npair + (64 / G) - 1) / (64 / G);
+  hipLaunchKernelGGL(wino_out_kernel, dim3(grid_for(waves * 64, 256, 65536)), dim3(256), 0, s, M, Cout, F, H, W, W2, G,
+                     bias, res, res_fstride, ldr, out, out_fstride, ldo, rs);
   return hipGetLastError();
 }
 

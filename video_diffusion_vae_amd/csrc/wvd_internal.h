@@ -141,8 +141,11 @@ hipError_t launch_wino_in(const h16_t* x, long long x_fstride, int lda, const h1
                           int H, int W, const float* rs, const float* gamma, h16_t* U, hipStream_t s);
 // Output transform: out[f][row][2p] = M0+M1+M2 + bias (+ res), out[..][2p+1] =
 // M1-M2-M3 + bias (+ res), M = [4][F][H][W2][Cout] fp16; out may alias res.
+// With rs != null also writes rs[2+f][row][col] = 1/||out voxel|| exactly as
+// launch_rms_stats would for these frames.
 hipError_t launch_wino_out(const h16_t* M, int Cout, int F, int H, int W, const float* bias, const h16_t* res,
-                           long long res_fstride, int ldr, h16_t* out, long long out_fstride, int ldo, hipStream_t s);
+                           long long res_fstride, int ldr, h16_t* out, long long out_fstride, int ldo, float* rs,
+                           hipStream_t s);
 hipError_t launch_prep_vec(const void* v, int dtype, int n, float scale, float* out, hipStream_t s);
 // out[i] = a[i] + b[i] in fp32 (the two biases of a block with a shortcut).
 hipError_t launch_prep_vec_add(const void* a, const void* b, int dtype, int n, float* out, hipStream_t s);
