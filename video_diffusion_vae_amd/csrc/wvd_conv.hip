@@ -46,6 +46,9 @@
 #ifndef WVD_ILV
 #define WVD_ILV 1
 #endif
+#ifndef WVD_WINO_W4
+#define WVD_WINO_W4 1
+#endif
 
 namespace wvd {
 
@@ -1040,23 +1043,47 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
       } else if constexpr (WINO) {
         // 9 (dt, dy) taps x two k16 steps over one xi plane; B fragments of
         // step u in slot u % 6, refilled with step u + 6 (three taps ahead);
-        // halo item t loaded at tap t and stored at tap t + 3.
+        // IPK halo items loaded at each of taps 0..4 and stored three taps
+        // later.  With APF (4 waves) A fragments run one step ahead.
         constexpr int IPT = (NHV * NP + NT - 1) / NT;
-        static_assert(IPT + 3 <= 9, "halo items must land inside a chunk");
-        uint4 hr[3];
+        constexpr int IPK = (IPT + 4) / 5;
+        static_assert(IPK <= 2, "halo items per tap");
+        uint4 hr[3][IPK];
+        f16x8_t ap[2][MI];
+        if constexpr (APF) {
+#pragma unroll
+          for (int i = 0; i < MI; ++i) ap[0][i] = *reinterpret_cast<const f16x8_t*>(hsrc + g.abase[i]);
+        }
 #pragma unroll
         for (int u = 0; u < 18; ++u) {
           const int tap = u >> 1, ks = u & 1;
           const int dt = tap / 3, dy = tap % 3;
-          if (ks == 0) {
-            if (tap >= 3 && tap - 3 < IPT) halo_store<false, false>(gn, tid + NT * (tap - 3), cn, hr[tap % 3], hdst);
-            if (tap < IPT) hr[tap % 3] = halo_load(gn, tid + NT * tap, cn);
-          }
-          const int toff = (dt * HY + dy) * HX * ROWB;
           f16x8_t av[MI];
+          if constexpr (APF) {
+            if (u + 1 < 18) {
+              const int t1 = (u + 1) >> 1, k1 = (u + 1) & 1;
+              const int off = ((t1 / 3) * HY + t1 % 3) * HX * ROWB + k1 * 32;
 #pragma unroll
-          for (int i = 0; i < MI; ++i)
-            av[i] = *reinterpret_cast<const f16x8_t*>(hsrc + g.abase[i] + toff + ks * 32);
+              for (int i = 0; i < MI; ++i)
+                ap[(u + 1) & 1][i] = *reinterpret_cast<const f16x8_t*>(hsrc + g.abase[i] + off);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < MI; ++i) av[i] = ap[u & 1][i];
+          } else {
+            const int toff = (dt * HY + dy) * HX * ROWB;
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+              av[i] = *reinterpret_cast<const f16x8_t*>(hsrc + g.abase[i] + toff + ks * 32);
+          }
+          if (ks == 0) {
+#pragma unroll
+            for (int j = 0; j < IPK; ++j) {
+              const int is = (tap - 3) * IPK + j, il = tap * IPK + j;
+              if (tap >= 3 && is < IPT) halo_store<false, false>(gn, tid + NT * is, cn, hr[tap % 3][j], hdst);
+              if (tap < 5 && il < IPT) hr[tap % 3][j] = halo_load(gn, tid + NT * il, cn);
+            }
+          }
 #pragma unroll
           for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -1411,6 +1438,9 @@ hipError_t launch_conv(const ConvArgs& a, hipStream_t stream) {
     const int pro = a.seg[0].prologue;
     if (v.mode == 2) return launch_persist_impl<256, 4, 2, PRO_RAW>(a, stream);
     if (v.mode == 3) return launch_persist_impl<256, 4, 3, PRO_RAW>(a, stream);
+#if WVD_WINO_W4
+    if (v.mode == 4) return launch_persist_impl<256, 2, 4, PRO_RAW, 4>(a, stream);
+#endif
     if (v.mode == 4) return launch_persist_impl<256, 4, 4, PRO_RAW>(a, stream);
     if (v.bn == 32) return launch_persist_impl<32, 1, 1, PRO_RAW>(a, stream);
 #if WVD_MAIN_W4
