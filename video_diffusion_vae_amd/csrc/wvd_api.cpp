@@ -462,7 +462,7 @@ void conv_wino(Ctx& cx, const Act& x, h16_t* ring, int nh, int gamma_item, int w
   a.out_pstride = (long long)x.F * mframe;
   a.ldo = Cout;
   a.epi = EPI_WINO;
-  set_grid(a, x.F, x.H, W2, tf_for(3, x.F));
+  set_grid(a, x.F, x.H, W2, kWinoTF);
   conv(cx, a, 0);
   cx.what = "wino_out";
   cx.run(5, 0, [&] {

@@ -62,6 +62,10 @@ constexpr int kHY333 = kTH333 + 2;
 constexpr int kHF333 = kTF333 + 2;
 constexpr int kNHV333 = kHF333 * kHY333 * kHX;  // 720 halo voxels
 constexpr int kBRing = WVD_BRING;              // k16 steps of B fragments in flight
+// Tile of the Winograd-domain GEMM: 2 frames x 8 rows x 16 column pairs
+// (halo 4 x 10 x 16 rows; a 4 x 4 x 16 tile has fewer halo rows but measured slower).
+constexpr int kTFWino = kWinoTF;
+constexpr int kTHWino = kTileM / kTileW / kTFWino;
 
 __device__ __forceinline__ f16x8_t ld_frag(const h16_t* p) { return *reinterpret_cast<const f16x8_t*>(p); }
 
@@ -792,8 +796,8 @@ struct TileGeo {
 
 template <int BN, int MODE>
 __device__ __forceinline__ TileGeo tile_geo(const ConvArgs& a, int logical) {
-  constexpr int TF = MODE == 2 ? 1 : kTF333;
-  constexpr int TH = MODE == 2 ? 16 : kTH333;
+  constexpr int TF = MODE == 2 ? 1 : (MODE == 4 ? kTFWino : kTF333);
+  constexpr int TH = MODE == 2 ? 16 : (MODE == 4 ? kTHWino : kTH333);
   const int nN = (a.Cout + BN - 1) / BN;
   const int nt = logical % nN;
   const int ph = (logical / nN) % a.nphase;
@@ -825,8 +829,8 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
   constexpr bool ACT = PRO0 == PRO_NORM_SILU;
   constexpr bool KT3 = MODE == 3;   // 3x1x1 temporal conv (time_conv)
   constexpr bool WINO = MODE == 4;  // Winograd-domain 3x3x1 (t, y) GEMM, one xi per phase
-  constexpr int TF = MODE == 2 ? 1 : kTF333;
-  constexpr int TH = MODE == 2 ? 16 : kTH333;
+  constexpr int TF = MODE == 2 ? 1 : (MODE == 4 ? kTFWino : kTF333);
+  constexpr int TH = MODE == 2 ? 16 : (MODE == 4 ? kTHWino : kTH333);
   constexpr int KT = MODE == 2 ? 1 : 3;
   constexpr int HSX = KT3 || WINO ? 0 : 1;  // spatial halo along x
   constexpr int HSY = KT3 ? 0 : 1;          // and along y
@@ -1333,7 +1337,7 @@ Variant conv_variant(const ConvArgs& a) {
                    v.bk == 32 && a.nseg == 1 && g.wfrag && g.prologue == PRO_RAW;
   const bool kt3 = g.KT == 3 && g.KS == 1 && a.nphase == 1 && a.TF == kTF333 && a.TH == kTH333 && v.bk == 32 &&
                    a.nseg == 1 && g.wfrag && g.prologue == PRO_RAW && a.Cout % 256 == 0 && a.epi == EPI_TIME;
-  const bool kwino = g.KT == 3 && g.KS == KS_3x1 && a.nphase == 4 && a.TF == kTF333 && a.TH == kTH333 &&
+  const bool kwino = g.KT == 3 && g.KS == KS_3x1 && a.nphase == 4 && a.TF == kTFWino && a.TH == kTHWino &&
                      v.bk == 32 && a.nseg == 1 && g.wfrag && g.prologue == PRO_RAW && a.Cout % 256 == 0 &&
                      a.epi == EPI_WINO;
   const bool shortcut_ok = a.nseg == 1 || (a.seg[1].KT == 1 && a.seg[1].KS == 1 && a.seg[1].prologue == PRO_RAW &&

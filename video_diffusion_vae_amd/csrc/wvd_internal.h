@@ -13,6 +13,7 @@ constexpr int kTileW = 16;
 constexpr int kTileM = 256;
 constexpr int kMaxHaloItemsPerTap = 4;  // 16-byte halo items per thread per tap
 constexpr int kMaxCin = 1024;           // largest norm input width kept in LDS
+constexpr int kWinoTF = 2;              // frames per tile of the Winograd-domain GEMM
 
 enum Prologue { PRO_RAW = 0, PRO_NORM = 1, PRO_NORM_SILU = 2 };
 enum Epilogue {
