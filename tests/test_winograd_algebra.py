@@ -1,0 +1,66 @@
+"""The Winograd F(2,3) algebra the GPU path uses for its 3x3x3 convs, restated
+on the host and checked against direct correlation (CPU only).
+
+Along x, with zero padding of one column on each side, output columns 2p and
+2p+1 of a 3-tap correlation with taps g = (g0, g1, g2) use the inputs
+d_k = x[2p-1+k], k = 0..3.  The GPU path stores
+  U = (d0 - d2, d1 + d2, d2 - d1, d1 - d3)          (input transform)
+  V = (g0, (g0+g1+g2)/2, (g0-g1+g2)/2, g2)          (weight transform)
+multiplies them per xi (summed over channels and the (t, y) taps), and
+recovers
+  y[2p] = M0 + M1 + M2,  y[2p+1] = M1 - M2 - M3      (output transform).
+These are the minimal-filtering identities for interpolation points
+0, 1, -1 and infinity.
+"""
+import numpy as np
+import pytest
+
+
+def wino_1d(x, g):
+    W = x.shape[-1]
+    W2 = (W + 1) // 2
+    xp = np.zeros(x.shape[:-1] + (2 * W2 + 2,), x.dtype)
+    xp[..., 1:W + 1] = x
+    d = [xp[..., k:k + 2 * W2:2] for k in range(4)]  # d_k[p] = x[2p-1+k]
+    U = [d[0] - d[2], d[1] + d[2], d[2] - d[1], d[1] - d[3]]
+    g0, g1, g2 = g
+    V = [g0, (g0 + g1 + g2) / 2, (g0 - g1 + g2) / 2, g2]
+    M = [u * v for u, v in zip(U, V)]
+    y = np.empty(x.shape[:-1] + (2 * W2,), x.dtype)
+    y[..., 0::2] = M[0] + M[1] + M[2]
+    y[..., 1::2] = M[1] - M[2] - M[3]
+    return y[..., :W]
+
+
+def direct_1d(x, g):
+    W = x.shape[-1]
+    xp = np.pad(x, [(0, 0)] * (x.ndim - 1) + [(1, 1)])
+    return sum(g[k] * xp[..., k:k + W] for k in range(3))
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 7, 16, 39, 78])
+def test_f23_equals_direct_correlation(W):
+    rng = np.random.default_rng(W)
+    x = rng.standard_normal((5, W))
+    g = rng.standard_normal(3)
+    np.testing.assert_allclose(wino_1d(x, g), direct_1d(x, g), rtol=1e-12, atol=1e-12)
+
+
+def test_f23_with_channel_contraction_and_other_taps():
+    # A full 3x3x3 conv = sum over (dt, dy) of x-correlations; the transform
+    # commutes with the channel contraction and with the (t, y) tap sum.
+    rng = np.random.default_rng(7)
+    Cin, Cout, T, H, W = 3, 2, 4, 3, 10
+    x = rng.standard_normal((Cin, T, H, W))
+    w = rng.standard_normal((Cout, Cin, 3, 3, 3))
+    xp = np.pad(x, [(0, 0), (2, 0), (1, 1), (0, 0)])  # causal in t, pad 1 in y
+    ref = np.zeros((Cout, T, H, W))
+    win = np.zeros((Cout, T, H, W))
+    for o in range(Cout):
+        for i in range(Cin):
+            for dt in range(3):
+                for dy in range(3):
+                    rows = xp[i, dt:dt + T, dy:dy + H, :]
+                    ref[o] += direct_1d(rows, w[o, i, dt, dy])
+                    win[o] += wino_1d(rows, w[o, i, dt, dy])
+    np.testing.assert_allclose(win, ref, rtol=1e-11, atol=1e-11)
