@@ -26,6 +26,9 @@ MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 MFMA
 HBM_PEAK_GBS = 8000.0
 CONV_SRC = os.path.join(ROOT, "video_diffusion_vae_amd", "csrc", "wvd_conv.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv3x3x3_main_c256_T49_704x1248_traffic.json")
+# Direct 3x3x3 multiply-adds per Winograd-domain multiply-add: F(4,3) along x
+# replaces 4 outputs x 27 taps by 6 planes x 9 (t, y) taps.
+WINO_DIRECT_PER_EXECUTED = (4 * 27) / (6 * 9)
 
 
 def conv_src_hash() -> str:
@@ -237,10 +240,10 @@ def main():
         "roofline": {"bound": "mfma", "achieved": conv_tflops, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": conv_tflops / MFMA_PEAK_TFLOPS, "traffic": measured_traffic(),
                      "kernel": "conv_persist<256, 2, 4, 0, 4>: Winograd-domain GEMM of the norm-SiLU 3x3x3 "
-                               "convs (F(2,3) along x, four xi planes, causal (t,y) 3x3 taps), 256x256 tiles "
+                               "convs (F(4,3) along x, six xi planes, causal (t,y) 3x3 taps), 256x256 tiles "
                                "on 4 waves, one persistent workgroup per CU",
-                     "flops_counted": "multiply-adds the kernel performs (2/3 of the direct 3x3x3 count)",
-                     "direct_equivalent_tflops": conv_tflops * 1.5,
+                     "flops_counted": "multiply-adds the kernel performs (1/2 of the direct 3x3x3 count)",
+                     "direct_equivalent_tflops": conv_tflops * WINO_DIRECT_PER_EXECUTED,
                      "avg_launch_ms": avg_launch_ms, "avg_launch_tflop": avg_launch_flops / 1e12,
                      "launches_per_step": conv["launches"] / args.steps},
         "conv_all_tflops": all_conv_fl / (all_conv_ms / 1e3) / 1e12 if all_conv_ms > 0 else 0.0,

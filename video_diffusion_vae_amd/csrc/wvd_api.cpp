@@ -29,7 +29,7 @@ enum ItemKind { K_CONV = 0, K_PHASE = 1, K_VEC = 2, K_WINO = 3 };
 #define WVD_WINO 1
 #endif
 
-// A 3x3x3 norm-SiLU conv runs in Winograd form (F(2,3) along x: input
+// A 3x3x3 norm-SiLU conv runs in Winograd form (F(kWinoM,3) along x: input
 // transform, four xi-plane GEMMs on the persistent kernel, output transform)
 // when its widths suit the 256-wide persistent tiles and 32-channel chunks.
 bool wino_ok(int cin, int cout) { return WVD_WINO && cin % 32 == 0 && cout % 256 == 0; }
@@ -89,8 +89,8 @@ RB add_rb(Layout& L, int cin, int cout) {
   auto to_wino = [&](int item) {
     Item& it = L.items[item];
     it.kind = K_WINO;
-    it.taps = 36;  // 4 xi x 3 dt x 3 dy
-    it.bytes = prep_frag_bytes(it.cout, it.cin_pad, 36);
+    it.taps = kWinoN * 9;  // xi x 3 dt x 3 dy
+    it.bytes = prep_frag_bytes(it.cout, it.cin_pad, it.taps);
   };
   r.wino1 = wino_ok(cin, cout);
   r.wino2 = cin == cout && wino_ok(cout, cout);  // a shortcut block's conv2 keeps the direct form
@@ -205,18 +205,20 @@ Work make_work(int c, int h, int w, int P) {
   W.Vt = take((size_t)F0 * c4 * Lp * 2);
   W.O = take((size_t)F0 * L * c4 * 2);
   {
-    // Winograd planes: U = [4][F+2][H][ceil(W/2)][Cin], M = [4][F][H][ceil(W/2)][Cout]
-    // per level (Cin / Cout of that level's widest Winograd conv).
+    // Winograd planes: U = [N][F+2][H][WQ][Cin], M = [N][F][H][WQ][Cout] with
+    // N = kWinoN planes and WQ = ceil(W / kWinoM) column groups, per level
+    // (Cin / Cout of that level's widest Winograd conv).
     const long long hl[4] = {h, 2LL * h, 4LL * h, 8LL * h};
-    const long long w2[4] = {(w + 1) / 2, (long long)w, 2LL * w, 4LL * w};
+    long long w2[4];
+    for (int l = 0; l < 4; ++l) w2[l] = (((long long)w << l) + kWinoM - 1) / kWinoM;
     const long long fl[4] = {F0, F1, F2, F2};
     const long long ci[4] = {c4, c4, c4, c2};
     const long long co[4] = {c4, c4, c2, c};
     long long u = 0, m = 0;
     for (int l = 0; l < 4; ++l) {
       if (!wino_ok((int)ci[l], (int)co[l]) && !wino_ok((int)co[l], (int)co[l])) continue;
-      u = std::max(u, 4 * (fl[l] + 2) * hl[l] * w2[l] * ci[l]);
-      m = std::max(m, 4 * fl[l] * hl[l] * w2[l] * co[l]);
+      u = std::max(u, kWinoN * (fl[l] + 2) * hl[l] * w2[l] * ci[l]);
+      m = std::max(m, kWinoN * fl[l] * hl[l] * w2[l] * co[l]);
     }
     W.U = take((size_t)u * 2);
     W.M = take((size_t)m * 2);
@@ -430,14 +432,14 @@ int tf_for(int KT, int F) {
 }
 
 // Causal 3x3x3 norm-SiLU conv in Winograd form along x:
-//   U = F(2,3) input transform of SiLU(norm(x)) over the F frames and the
+//   U = F(kWinoM,3) input transform of SiLU(norm(x)) over the F frames and the
 //       valid history frames (rs from rms_stats for the same slots),
 //   M[xi] = causal (t, y) 3x3 conv of U[xi] with the transformed weights,
 //   out = output transform of M + bias (+ res).
-// Same function as conv333 + EPI_H16, with 2/3 of the multiply-adds.
+// Same function as conv333 + EPI_H16, with half of the multiply-adds (F(4,3)).
 void conv_wino(Ctx& cx, const Act& x, h16_t* ring, int nh, int gamma_item, int w_item, int b_item, int Cout,
                const Act& out, const h16_t* res, long long res_fstride, int ldr) {
-  const int W2 = (x.W + 1) / 2;
+  const int W2 = (x.W + kWinoM - 1) / kWinoM;  // column groups
   h16_t* U = cx.wsp<h16_t>(cx.W->U);
   h16_t* M = cx.wsp<h16_t>(cx.W->M);
   const long long uslot = (long long)x.H * W2 * x.C;         // elements per U frame
@@ -455,7 +457,7 @@ void conv_wino(Ctx& cx, const Act& x, h16_t* ring, int nh, int gamma_item, int w
   g.n_hist = nh;
   g.x_pstride = uplane;
   a.nseg = 1;
-  a.nphase = 4;
+  a.nphase = kWinoN;
   a.Cout = Cout;
   a.out = M;
   a.out_fstride = mframe;

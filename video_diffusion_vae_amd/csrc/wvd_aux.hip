@@ -301,50 +301,111 @@ __global__ void prep_phase_frag_kernel(const void* __restrict__ w, int dtype, in
   }
 }
 
-// Winograd F(2,3) weights along x (Lavin and Gray's minimal filtering with
-// interpolation points 0, 1, -1, infinity): for each (o, i, dt, dy) the x taps
-// g0..g2 become V = (g0, (g0+g1+g2)/2, (g0-g1+g2)/2, g2), computed in fp32
-// and rounded once to fp16; fragment order with tap = xi * 9 + dt * 3 + dy.
+// Winograd F(m,3) along x (Lavin and Gray's minimal filtering; m = 2 with
+// interpolation points 0, 1, -1, infinity, m = 4 with 0, 1, -1, 2, -2,
+// infinity).  m outputs x[mq .. mq+m-1] of a 3-tap correlation (pad 1) come
+// from the n = m + 2 inputs d_k = x[mq-1+k]:
+//   U = B^T d (input transform),  V = G g (weight transform),
+//   M = sum over channels and (t, y) taps of U * V,  y = A^T M.
+template <int WM>
+struct Wino;
+
+template <>
+struct Wino<2> {
+  static constexpr int N = 4;
+  __device__ static void weights(float g0, float g1, float g2, float* v) {
+    v[0] = g0;
+    v[1] = 0.5f * (g0 + g1 + g2);
+    v[2] = 0.5f * (g0 - g1 + g2);
+    v[3] = g2;
+  }
+  __device__ static void input(const float* d, float* u) {
+    u[0] = d[0] - d[2];
+    u[1] = d[1] + d[2];
+    u[2] = d[2] - d[1];
+    u[3] = d[1] - d[3];
+  }
+  __device__ static void output(const float* m, float* o) {
+    o[0] = m[0] + m[1] + m[2];
+    o[1] = m[1] - m[2] - m[3];
+  }
+};
+
+template <>
+struct Wino<4> {
+  static constexpr int N = 6;
+  __device__ static void weights(float g0, float g1, float g2, float* v) {
+    v[0] = 0.25f * g0;
+    v[1] = -(g0 + g1 + g2) / 6.0f;
+    v[2] = -(g0 - g1 + g2) / 6.0f;
+    v[3] = g0 / 24.0f + g1 / 12.0f + g2 / 6.0f;
+    v[4] = g0 / 24.0f - g1 / 12.0f + g2 / 6.0f;
+    v[5] = g2;
+  }
+  __device__ static void input(const float* d, float* u) {
+    u[0] = 4.0f * d[0] - 5.0f * d[2] + d[4];
+    u[1] = -4.0f * d[1] - 4.0f * d[2] + d[3] + d[4];
+    u[2] = 4.0f * d[1] - 4.0f * d[2] - d[3] + d[4];
+    u[3] = -2.0f * d[1] - d[2] + 2.0f * d[3] + d[4];
+    u[4] = 2.0f * d[1] - d[2] - 2.0f * d[3] + d[4];
+    u[5] = 4.0f * d[1] - 5.0f * d[3] + d[5];
+  }
+  __device__ static void output(const float* m, float* o) {
+    o[0] = m[0] + m[1] + m[2] + m[3] + m[4];
+    o[1] = m[1] - m[2] + 2.0f * m[3] - 2.0f * m[4];
+    o[2] = m[1] + m[2] + 4.0f * m[3] + 4.0f * m[4];
+    o[3] = m[1] - m[2] + 8.0f * m[3] - 8.0f * m[4] + m[5];
+  }
+};
+
+// Winograd weights of a 3x3x3 conv: for each (o, i, dt, dy) the x taps
+// g0..g2 become V = G g (fp32, rounded once to fp16), in fragment order with
+// tap = xi * 9 + dt * 3 + dy.
 __global__ void prep_wino_frag_kernel(const void* __restrict__ w, int dtype, int cout, int cin,
                                       h16_t* __restrict__ out) {
+  constexpr int NX = Wino<kWinoM>::N;
   const int NB = (cout + 127) / 128 * 4, U = cin / 16;
-  const long long n = (long long)NB * U * 36 * 512;
+  const long long n = (long long)NB * U * (NX * 9) * 512;
   for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n;
        e += (long long)gridDim.x * blockDim.x) {
     const int j = (int)(e & 7);
     const int l = (int)((e >> 3) & 63);
     const long long blk = e >> 9;
-    const int t36 = (int)(blk % 36);
-    const int u = (int)((blk / 36) % U);
-    const int nb = (int)(blk / (36LL * U));
+    const int tx = (int)(blk % (NX * 9));
+    const int u = (int)((blk / (NX * 9)) % U);
+    const int nb = (int)(blk / ((long long)NX * 9 * U));
     const int o = nb * 32 + (l & 31);
     const int i = u * 16 + (l >> 5) * 8 + j;
     float v = 0.0f;
     if (o < cout && i < cin) {
-      const int xi = t36 / 9, tdy = t36 % 9;  // tdy = dt * 3 + dy
+      const int xi = tx / 9, tdy = tx % 9;  // tdy = dt * 3 + dy
       const long long wp = ((long long)o * cin + i) * 27 + tdy * 3;
-      const float g0 = load_in(w, wp, dtype), g1 = load_in(w, wp + 1, dtype), g2 = load_in(w, wp + 2, dtype);
-      v = xi == 0 ? g0 : (xi == 1 ? 0.5f * (g0 + g1 + g2) : (xi == 2 ? 0.5f * (g0 - g1 + g2) : g2));
+      float vv[NX];
+      Wino<kWinoM>::weights(load_in(w, wp, dtype), load_in(w, wp + 1, dtype), load_in(w, wp + 2, dtype), vv);
+#pragma unroll
+      for (int k = 0; k < NX; ++k)
+        if (k == xi) v = vv[k];
     }
     out[e] = (h16_t)f2h(v);
   }
 }
 
-// Input transform: one thread per (slot, row, pair, 8-channel group).
+// Input transform: one thread per (slot, row, column group, 8-channel group).
 __global__ __launch_bounds__(256) void wino_in_kernel(const h16_t* __restrict__ x, long long x_fstride, int lda,
                                                       const h16_t* __restrict__ ring, int first_slot, int C, int S,
-                                                      int H, int W, int W2, const float* __restrict__ rs,
+                                                      int H, int W, int WQ, const float* __restrict__ rs,
                                                       const float* __restrict__ gamma, h16_t* __restrict__ U) {
+  constexpr int WM = kWinoM, NX = Wino<WM>::N;
   const int G8 = C >> 3;
   const long long HW = (long long)H * W;
-  const long long plane = (long long)S * H * W2 * C;  // elements per xi plane
-  const long long n = (long long)(S - first_slot) * H * W2 * G8;
+  const long long plane = (long long)S * H * WQ * C;  // elements per xi plane
+  const long long n = (long long)(S - first_slot) * H * WQ * G8;
   for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n;
        e += (long long)gridDim.x * blockDim.x) {
     const int g = (int)(e % G8);
     long long r = e / G8;
-    const int p = (int)(r % W2);
-    r /= W2;
+    const int q = (int)(r % WQ);
+    r /= WQ;
     const int row = (int)(r % H);
     const int slot = (int)(r / H) + first_slot;
     float gm[8];
@@ -354,12 +415,12 @@ __global__ __launch_bounds__(256) void wino_in_kernel(const h16_t* __restrict__ 
       gm[0] = g0.x; gm[1] = g0.y; gm[2] = g0.z; gm[3] = g0.w;
       gm[4] = g1.x; gm[5] = g1.y; gm[6] = g1.z; gm[7] = g1.w;
     }
-    float y[4][8];
+    float y[NX][8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int col = 2 * p - 1 + k;
+    for (int k = 0; k < NX; ++k) {
+      const int col = WM * q - 1 + k;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) y[k][q] = 0.0f;
+      for (int c = 0; c < 8; ++c) y[k][c] = 0.0f;
       if (col >= 0 && col < W) {
         const long long pix = (long long)row * W + col;
         const h16_t* src = slot < 2 ? ring + ((long long)slot * HW + pix) * C : x + (slot - 2) * x_fstride + pix * lda;
@@ -367,69 +428,72 @@ __global__ __launch_bounds__(256) void wino_in_kernel(const h16_t* __restrict__ 
         unpack8h(*reinterpret_cast<const uint4*>(src + g * 8), f);
         const float sc = rs[(long long)slot * HW + pix];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float t = f[q] * sc * gm[q];
-          y[k][q] = t * __builtin_amdgcn_rcpf(1.0f + __expf(-t));
+        for (int c = 0; c < 8; ++c) {
+          const float t = f[c] * sc * gm[c];
+          y[k][c] = t * __builtin_amdgcn_rcpf(1.0f + __expf(-t));
         }
       }
     }
-    h16_t* dst = U + ((long long)slot * H * W2 + (long long)row * W2 + p) * C + g * 8;
-    float u[8];
+    float u[NX][8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) u[q] = y[0][q] - y[2][q];
-    *reinterpret_cast<uint4*>(dst) = pack8h(u);
+    for (int c = 0; c < 8; ++c) {
+      float d[NX], uu[NX];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) u[q] = y[1][q] + y[2][q];
-    *reinterpret_cast<uint4*>(dst + plane) = pack8h(u);
+      for (int k = 0; k < NX; ++k) d[k] = y[k][c];
+      Wino<WM>::input(d, uu);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) u[q] = y[2][q] - y[1][q];
-    *reinterpret_cast<uint4*>(dst + 2 * plane) = pack8h(u);
+      for (int k = 0; k < NX; ++k) u[k][c] = uu[k];
+    }
+    h16_t* dst = U + ((long long)slot * H * WQ + (long long)row * WQ + q) * C + g * 8;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) u[q] = y[1][q] - y[3][q];
-    *reinterpret_cast<uint4*>(dst + 3 * plane) = pack8h(u);
+    for (int k = 0; k < NX; ++k) *reinterpret_cast<uint4*>(dst + k * plane) = pack8h(u[k]);
   }
 }
 
-// Output transform.  G lanes share a column pair (G as in rms_stats_kernel);
+// Output transform.  G lanes share a column group (G as in rms_stats_kernel);
 // lane `sub` takes channel groups sub and sub + G.  With rs != null the
-// kernel also writes the norm statistics of both output voxels, summed over
-// the rounded fp16 outputs in exactly rms_stats_kernel's order (lane sums in
-// group order, then the same butterfly), so a voxel's statistic does not
-// depend on which kernel computed it.
+// kernel also writes the norm statistics of the group's output voxels,
+// summed over the rounded fp16 outputs in exactly rms_stats_kernel's order
+// (lane sums in group order, then the same butterfly), so a voxel's
+// statistic does not depend on which kernel computed it.
 __global__ __launch_bounds__(256) void wino_out_kernel(const h16_t* __restrict__ M, int Cout, int F, int H, int W,
-                                                       int W2, int G, const float* __restrict__ bias,
+                                                       int WQ, int G, const float* __restrict__ bias,
                                                        const h16_t* res, long long res_fstride, int ldr, h16_t* out,
                                                        long long out_fstride, int ldo, float* __restrict__ rs) {
+  constexpr int WM = kWinoM, NX = Wino<WM>::N;
   const int lane = threadIdx.x & 63;
   const int sub = lane % G;
   const int G8 = Cout >> 3;
-  const long long plane = (long long)F * H * W2 * Cout;
-  const long long npair = (long long)F * H * W2;
-  const int pairs_per_wave = 64 / G;
+  const long long plane = (long long)F * H * WQ * Cout;
+  const long long ngrp = (long long)F * H * WQ;
+  const int grp_per_wave = 64 / G;
   const long long gw = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const long long nw = ((long long)gridDim.x * blockDim.x) >> 6;
-  for (long long base = gw * pairs_per_wave; base < npair; base += nw * pairs_per_wave) {
+  for (long long base = gw * grp_per_wave; base < ngrp; base += nw * grp_per_wave) {
     const long long pr = base + lane / G;
-    const bool ok = pr < npair;
-    const int p = ok ? (int)(pr % W2) : 0;
-    const long long r = ok ? pr / W2 : 0;
+    const bool ok = pr < ngrp;
+    const int q = ok ? (int)(pr % WQ) : 0;
+    const long long r = ok ? pr / WQ : 0;
     const int row = (int)(r % H);
     const int f = (int)(r / H);
-    const bool two = 2 * p + 1 < W;
-    const long long pix0 = (long long)row * W + 2 * p;
-    float ss[2] = {0.0f, 0.0f};
+    const int nout = min(WM, W - WM * q);  // output columns of this group
+    const long long pix0 = (long long)row * W + WM * q;
+    float ss[WM];
+#pragma unroll
+    for (int e2 = 0; e2 < WM; ++e2) ss[e2] = 0.0f;
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) {
       const int g = sub + q2 * G;
       if (!ok || g >= G8) continue;
-      const h16_t* src = M + (((long long)f * H + row) * W2 + p) * Cout + g * 8;
-      uint4 mr[4];
+      const h16_t* src = M + (((long long)f * H + row) * WQ + q) * Cout + g * 8;
+      uint4 mr[NX];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) mr[k] = *reinterpret_cast<const uint4*>(src + k * plane);
-      uint4 rr[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
-      if (res) {
-        rr[0] = *reinterpret_cast<const uint4*>(res + f * res_fstride + pix0 * ldr + g * 8);
-        if (two) rr[1] = *reinterpret_cast<const uint4*>(res + f * res_fstride + (pix0 + 1) * ldr + g * 8);
+      for (int k = 0; k < NX; ++k) mr[k] = *reinterpret_cast<const uint4*>(src + k * plane);
+      uint4 rr[WM];
+#pragma unroll
+      for (int e2 = 0; e2 < WM; ++e2) {
+        rr[e2] = make_uint4(0, 0, 0, 0);
+        if (res && e2 < nout) rr[e2] = *reinterpret_cast<const uint4*>(res + f * res_fstride + (pix0 + e2) * ldr + g * 8);
       }
       float b[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       if (bias) {
@@ -438,17 +502,26 @@ __global__ __launch_bounds__(256) void wino_out_kernel(const h16_t* __restrict__
         b[0] = b0.x; b[1] = b0.y; b[2] = b0.z; b[3] = b0.w;
         b[4] = b1.x; b[5] = b1.y; b[6] = b1.z; b[7] = b1.w;
       }
-      float m[4][8];
+      float m[NX][8];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) unpack8h(mr[k], m[k]);
+      for (int k = 0; k < NX; ++k) unpack8h(mr[k], m[k]);
+      float o[WM][8];
 #pragma unroll
-      for (int e2 = 0; e2 < 2; ++e2) {
-        if (e2 == 1 && !two) break;
+      for (int c = 0; c < 8; ++c) {
+        float mm[NX], oo[WM];
+#pragma unroll
+        for (int k = 0; k < NX; ++k) mm[k] = m[k][c];
+        Wino<WM>::output(mm, oo);
+#pragma unroll
+        for (int e2 = 0; e2 < WM; ++e2) o[e2][c] = oo[e2];
+      }
+#pragma unroll
+      for (int e2 = 0; e2 < WM; ++e2) {
+        if (e2 >= nout) break;
         float v[8], r8[8];
         unpack8h(rr[e2], r8);
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-          v[q] = (e2 == 0 ? m[0][q] + m[1][q] + m[2][q] : m[1][q] - m[2][q] - m[3][q]) + b[q] + r8[q];
+        for (int c = 0; c < 8; ++c) v[c] = o[e2][c] + b[c] + r8[c];
         const uint4 packed = pack8h(v);
         *reinterpret_cast<uint4*>(out + f * out_fstride + (pix0 + e2) * ldo + g * 8) = packed;
         float h[8];
@@ -461,11 +534,10 @@ __global__ __launch_bounds__(256) void wino_out_kernel(const h16_t* __restrict__
     }
     if (rs) {
 #pragma unroll
-      for (int e2 = 0; e2 < 2; ++e2) {
+      for (int e2 = 0; e2 < WM; ++e2) {
         float v = ss[e2];
         for (int off = 1; off < G; off <<= 1) v += __shfl_xor(v, off, 64);
-        if (ok && sub == 0 && (e2 == 0 || two))
-          rs[(long long)(f + 2) * H * W + pix0 + e2] = 1.0f / fmaxf(sqrtf(v), kNormEps);
+        if (ok && sub == 0 && e2 < nout) rs[(long long)(f + 2) * H * W + pix0 + e2] = 1.0f / fmaxf(sqrtf(v), kNormEps);
       }
     }
   }
@@ -583,7 +655,7 @@ hipError_t launch_prep_phase_frag(const void* w, int dtype, int C, h16_t* out, h
 hipError_t launch_prep_wino_frag(const void* w, int dtype, int cout, int cin, h16_t* out, hipStream_t s) {
   if (g_dry_run) return hipSuccess;
   if (cin % 16) return hipErrorInvalidValue;
-  const long long n = (long long)prep_frag_bytes(cout, cin, 36) / 2;
+  const long long n = (long long)prep_frag_bytes(cout, cin, kWinoN * 9) / 2;
   hipLaunchKernelGGL(prep_wino_frag_kernel, dim3(grid_for(n)), dim3(256), 0, s, w, dtype, cout, cin, out);
   return hipGetLastError();
 }
@@ -592,10 +664,10 @@ hipError_t launch_wino_in(const h16_t* x, long long x_fstride, int lda, const h1
                           int H, int W, const float* rs, const float* gamma, h16_t* U, hipStream_t s) {
   if (g_dry_run) return hipSuccess;
   if (C % 8 || n_hist < 0 || n_hist > 2 || (n_hist > 0 && !ring) || F < 1) return hipErrorInvalidValue;
-  const int W2 = (W + 1) / 2;
-  const long long n = (long long)(F + n_hist) * H * W2 * (C / 8);
+  const int WQ = (W + kWinoM - 1) / kWinoM;
+  const long long n = (long long)(F + n_hist) * H * WQ * (C / 8);
   hipLaunchKernelGGL(wino_in_kernel, dim3(grid_for(n, 256, 65536)), dim3(256), 0, s, x, x_fstride, lda, ring,
-                     2 - n_hist, C, F + 2, H, W, W2, rs, gamma, U);
+                     2 - n_hist, C, F + 2, H, W, WQ, rs, gamma, U);
   return hipGetLastError();
 }
 
@@ -606,10 +678,10 @@ hipError_t launch_wino_out(const h16_t* M, int Cout, int F, int H, int W, const 
   if (Cout % 8 || ldo % 8 || (res && ldr % 8) || Cout > 1024) return hipErrorInvalidValue;
   int G = 1;
   while (G < 64 && G * 2 <= Cout / 8) G *= 2;
-  const int W2 = (W + 1) / 2;
-  const long long npair = (long long)F * H * W2;
-  const long long waves = (npair + (64 / G) - 1) / (64 / G);
-  hipLaunchKernelGGL(wino_out_kernel, dim3(grid_for(waves * 64, 256, 65536)), dim3(256), 0, s, M, Cout, F, H, W, W2, G,
+  const int WQ = (W + kWinoM - 1) / kWinoM;
+  const long long ngrp = (long long)F * H * WQ;
+  const long long waves = (ngrp + (64 / G) - 1) / (64 / G);
+  hipLaunchKernelGGL(wino_out_kernel, dim3(grid_for(waves * 64, 256, 65536)), dim3(256), 0, s, M, Cout, F, H, W, WQ, G,
                      bias, res, res_fstride, ldr, out, out_fstride, ldo, rs);
   return hipGetLastError();
 }

@@ -62,7 +62,7 @@ constexpr int kHY333 = kTH333 + 2;
 constexpr int kHF333 = kTF333 + 2;
 constexpr int kNHV333 = kHF333 * kHY333 * kHX;  // 720 halo voxels
 constexpr int kBRing = WVD_BRING;              // k16 steps of B fragments in flight
-// Tile of the Winograd-domain GEMM: 2 frames x 8 rows x 16 column pairs
+// Tile of the Winograd-domain GEMM: 2 frames x 8 rows x 16 column groups
 // (halo 4 x 10 x 16 rows; a 4 x 4 x 16 tile has fewer halo rows but measured slower).
 constexpr int kTFWino = kWinoTF;
 constexpr int kTHWino = kTileM / kTileW / kTFWino;
@@ -1337,7 +1337,7 @@ Variant conv_variant(const ConvArgs& a) {
                    v.bk == 32 && a.nseg == 1 && g.wfrag && g.prologue == PRO_RAW;
   const bool kt3 = g.KT == 3 && g.KS == 1 && a.nphase == 1 && a.TF == kTF333 && a.TH == kTH333 && v.bk == 32 &&
                    a.nseg == 1 && g.wfrag && g.prologue == PRO_RAW && a.Cout % 256 == 0 && a.epi == EPI_TIME;
-  const bool kwino = g.KT == 3 && g.KS == KS_3x1 && a.nphase == 4 && a.TF == kTFWino && a.TH == kTHWino &&
+  const bool kwino = g.KT == 3 && g.KS == KS_3x1 && a.nphase == kWinoN && a.TF == kTFWino && a.TH == kTHWino &&
                      v.bk == 32 && a.nseg == 1 && g.wfrag && g.prologue == PRO_RAW && a.Cout % 256 == 0 &&
                      a.epi == EPI_WINO;
   const bool shortcut_ok = a.nseg == 1 || (a.seg[1].KT == 1 && a.seg[1].KS == 1 && a.seg[1].prologue == PRO_RAW &&
@@ -1397,7 +1397,7 @@ const char* conv_check(const ConvArgs& a) {
   if (a.TF < 1 || a.TF * a.TH * kTileW != kTileM) return "tile TF*TH*16 != 256";
   if (a.nseg < 1 || a.nseg > 2) return "segment count";
   if (a.F < 1 || a.H < 1 || a.W < 1 || a.Cout < 1) return "empty output grid";
-  if (a.nphase != 1 && a.nphase != 4) return "phase count";
+  if (a.nphase != 1 && a.nphase != 4 && a.nphase != kWinoN) return "phase count";
   if (conv_lds_bytes(a) > 160 * 1024) return "LDS over 160 KiB";
   const int bk = conv_bk(a);
   for (int s = 0; s < a.nseg; ++s) {
@@ -1412,7 +1412,9 @@ const char* conv_check(const ConvArgs& a) {
     if (!g.x || !g.w) return "null operand";
     if (g.KT != 1 && g.KT != 3) return "KT must be 1 or 3";
     if (g.KS < KS_1x1 || g.KS > KS_3x1) return "unknown spatial tap code";
-    if ((g.KS == KS_PHASE || g.KS == KS_3x1) != (a.nphase == 4)) return "phase / xi taps need 4 phases";
+    if (g.KS == KS_PHASE && a.nphase != 4) return "phase taps need 4 phases";
+    if (g.KS == KS_3x1 && a.nphase != kWinoN) return "Winograd taps need one phase per xi plane";
+    if (a.nphase != 1 && g.KS != KS_PHASE && g.KS != KS_3x1) return "phases need phase or Winograd taps";
     if (g.KS == KS_3x1 && (a.epi != EPI_WINO || conv_variant(a).mode != 4))
       return "3x1 taps run only as the Winograd-domain GEMM";
     if ((a.epi == EPI_WINO) != (g.KS == KS_3x1)) return "EPI_WINO needs the 3x1 taps";

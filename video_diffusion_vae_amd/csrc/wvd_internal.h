@@ -14,6 +14,8 @@ constexpr int kTileM = 256;
 constexpr int kMaxHaloItemsPerTap = 4;  // 16-byte halo items per thread per tap
 constexpr int kMaxCin = 1024;           // largest norm input width kept in LDS
 constexpr int kWinoTF = 2;              // frames per tile of the Winograd-domain GEMM
+constexpr int kWinoM = 4;               // Winograd F(m,3) along x: output columns per group
+constexpr int kWinoN = kWinoM + 2;      // transformed planes (xi) per group
 
 enum Prologue { PRO_RAW = 0, PRO_NORM = 1, PRO_NORM_SILU = 2 };
 enum Epilogue {
@@ -127,21 +129,21 @@ hipError_t launch_prep_frag(const void* w, int dtype, int cout, int cin, int tap
 // Up-conv phase weights in the same fragment order with taps = 16
 // (phase * 4 + 2x2 tap).
 hipError_t launch_prep_phase_frag(const void* w, int dtype, int C, h16_t* out, hipStream_t s);
-// Winograd F(2,3) weights of a 3x3x3 conv along x: for each (dt, dy) the three
-// x taps g become V = (g0, (g0+g1+g2)/2, (g0-g1+g2)/2, g2) (fp32, rounded once
-// to fp16), in fragment order with taps = 36 (xi * 9 + dt * 3 + dy).
+// Winograd F(kWinoM,3) weights of a 3x3x3 conv along x: for each (dt, dy)
+// the three x taps g become V = G g (fp32, rounded once to fp16), in
+// fragment order with taps = kWinoN * 9 (xi * 9 + dt * 3 + dy).
 hipError_t launch_prep_wino_frag(const void* w, int dtype, int cout, int cin, h16_t* out, hipStream_t s);
 
-// Winograd F(2,3) along x of the normalised input: for slots s = 0..F+1
-// (s = 0, 1: the two history frames in `ring`, only the last n_hist valid;
-// s >= 2: frame s-2 of x), every column pair p and channel,
-//   y_k = SiLU(x[2p-1+k] * rs * gamma)  (k = 0..3, zero outside 0..W-1)
-//   U[xi][s][row][p] = (y0-y2, y1+y2, y2-y1, y1-y3)[xi]   (fp16)
-// U is [4][F+2][H][W2][C] with W2 = ceil(W/2); rs as rms_stats writes it.
+// Winograd F(m,3) (m = kWinoM) along x of the normalised input: for slots
+// s = 0..F+1 (s = 0, 1: the two history frames in `ring`, only the last
+// n_hist valid; s >= 2: frame s-2 of x), every column group q and channel,
+//   y_k = SiLU(x[mq-1+k] * rs * gamma)  (k = 0..m+1, zero outside 0..W-1)
+//   U[xi][s][row][q] = (B^T y)[xi]   (fp16)
+// U is [kWinoN][F+2][H][WQ][C] with WQ = ceil(W/m); rs as rms_stats writes it.
 hipError_t launch_wino_in(const h16_t* x, long long x_fstride, int lda, const h16_t* ring, int n_hist, int C, int F,
                           int H, int W, const float* rs, const float* gamma, h16_t* U, hipStream_t s);
-// Output transform: out[f][row][2p] = M0+M1+M2 + bias (+ res), out[..][2p+1] =
-// M1-M2-M3 + bias (+ res), M = [4][F][H][W2][Cout] fp16; out may alias res.
+// Output transform: out[f][row][mq + j] = (A^T M)[j] + bias (+ res), with
+// M = [kWinoN][F][H][WQ][Cout] fp16; out may alias res.
 // With rs != null also writes rs[2+f][row][col] = 1/||out voxel|| exactly as
 // launch_rms_stats would for these frames.
 hipError_t launch_wino_out(const h16_t* M, int Cout, int F, int H, int W, const float* bias, const h16_t* res,
