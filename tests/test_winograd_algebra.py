@@ -1,5 +1,6 @@
-"""The Winograd F(2,3) algebra the GPU path uses for its 3x3x3 convs, restated
-on the host and checked against direct correlation (CPU only).
+"""The Winograd F(m,3) algebra the GPU path uses for its 3x3x3 convs (m = 4;
+m = 2 is kept as an option), restated on the host and checked against direct
+correlation (CPU only).
 
 Along x, with zero padding of one column on each side, output columns 2p and
 2p+1 of a 3-tap correlation with taps g = (g0, g1, g2) use the inputs
@@ -10,7 +11,12 @@ multiplies them per xi (summed over channels and the (t, y) taps), and
 recovers
   y[2p] = M0 + M1 + M2,  y[2p+1] = M1 - M2 - M3      (output transform).
 These are the minimal-filtering identities for interpolation points
-0, 1, -1 and infinity.
+0, 1, -1 and infinity.  F(4,3) uses 0, 1, -1, 2, -2, infinity: six inputs
+d_k = x[4q-1+k] give four outputs x[4q..4q+3] through
+  U = (4d0-5d2+d4, -4d1-4d2+d3+d4, 4d1-4d2-d3+d4, -2d1-d2+2d3+d4,
+       2d1-d2-2d3+d4, 4d1-5d3+d5)
+  V = (g0/4, -(g0+g1+g2)/6, -(g0-g1+g2)/6, g0/24+g1/12+g2/6, g0/24-g1/12+g2/6, g2)
+  y = (M0+M1+M2+M3+M4, M1-M2+2M3-2M4, M1+M2+4M3+4M4, M1-M2+8M3-8M4+M5).
 """
 import numpy as np
 import pytest
@@ -32,6 +38,26 @@ def wino_1d(x, g):
     return y[..., :W]
 
 
+def wino4_1d(x, g):
+    W = x.shape[-1]
+    WQ = (W + 3) // 4
+    xp = np.zeros(x.shape[:-1] + (4 * WQ + 2,), x.dtype)
+    xp[..., 1:W + 1] = x
+    d = [xp[..., k:k + 4 * WQ:4] for k in range(6)]  # d_k[q] = x[4q-1+k]
+    U = [4 * d[0] - 5 * d[2] + d[4], -4 * d[1] - 4 * d[2] + d[3] + d[4], 4 * d[1] - 4 * d[2] - d[3] + d[4],
+         -2 * d[1] - d[2] + 2 * d[3] + d[4], 2 * d[1] - d[2] - 2 * d[3] + d[4], 4 * d[1] - 5 * d[3] + d[5]]
+    g0, g1, g2 = g
+    V = [g0 / 4, -(g0 + g1 + g2) / 6, -(g0 - g1 + g2) / 6, g0 / 24 + g1 / 12 + g2 / 6,
+         g0 / 24 - g1 / 12 + g2 / 6, g2]
+    M = [u * v for u, v in zip(U, V)]
+    y = np.empty(x.shape[:-1] + (4 * WQ,), x.dtype)
+    y[..., 0::4] = M[0] + M[1] + M[2] + M[3] + M[4]
+    y[..., 1::4] = M[1] - M[2] + 2 * M[3] - 2 * M[4]
+    y[..., 2::4] = M[1] + M[2] + 4 * M[3] + 4 * M[4]
+    y[..., 3::4] = M[1] - M[2] + 8 * M[3] - 8 * M[4] + M[5]
+    return y[..., :W]
+
+
 def direct_1d(x, g):
     W = x.shape[-1]
     xp = np.pad(x, [(0, 0)] * (x.ndim - 1) + [(1, 1)])
@@ -44,6 +70,14 @@ def test_f23_equals_direct_correlation(W):
     x = rng.standard_normal((5, W))
     g = rng.standard_normal(3)
     np.testing.assert_allclose(wino_1d(x, g), direct_1d(x, g), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 5, 7, 16, 39, 78, 624])
+def test_f43_equals_direct_correlation(W):
+    rng = np.random.default_rng(100 + W)
+    x = rng.standard_normal((5, W))
+    g = rng.standard_normal(3)
+    np.testing.assert_allclose(wino4_1d(x, g), direct_1d(x, g), rtol=1e-10, atol=1e-10)
 
 
 def test_f23_with_channel_contraction_and_other_taps():
@@ -62,5 +96,5 @@ def test_f23_with_channel_contraction_and_other_taps():
                 for dy in range(3):
                     rows = xp[i, dt:dt + T, dy:dy + H, :]
                     ref[o] += direct_1d(rows, w[o, i, dt, dy])
-                    win[o] += wino_1d(rows, w[o, i, dt, dy])
+                    win[o] += wino4_1d(rows, w[o, i, dt, dy])
     np.testing.assert_allclose(win, ref, rtol=1e-11, atol=1e-11)
