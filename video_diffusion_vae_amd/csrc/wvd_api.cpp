@@ -93,7 +93,9 @@ RB add_rb(Layout& L, int cin, int cout) {
     it.bytes = prep_frag_bytes(it.cout, it.cin_pad, it.taps);
   };
   r.wino1 = wino_ok(cin, cout);
-  r.wino2 = cin == cout && wino_ok(cout, cout);  // a shortcut block's conv2 keeps the direct form
+  // a width-changing block's conv2 runs in Winograd form too when its
+  // shortcut suits the 1x1 GEMM (K a multiple of 64)
+  r.wino2 = wino_ok(cout, cout) && (cin == cout || cin % 64 == 0);
   if (r.wino1) to_wino(r.conv1w);
   if (r.wino2) to_wino(r.conv2w);
   return r;
@@ -468,8 +470,8 @@ void conv_wino(Ctx& cx, const Act& x, h16_t* ring, int nh, int gamma_item, int w
   conv(cx, a, 0);
   cx.what = "wino_out";
   cx.run(5, 0, [&] {
-    return launch_wino_out(M, Cout, x.F, x.H, x.W, cx.prep<float>(b_item), res, res_fstride, ldr, out.p,
-                           out.fstride(), out.C, cx.wsp<float>(cx.W->rs), cx.st);
+    return launch_wino_out(M, Cout, x.F, x.H, x.W, b_item >= 0 ? cx.prep<float>(b_item) : nullptr, res, res_fstride,
+                           ldr, out.p, out.fstride(), out.C, cx.wsp<float>(cx.W->rs), cx.st);
   });
   cx.rs_tensor = out.p;
   cx.rs_frames = x.F;
@@ -512,8 +514,19 @@ Act resblock(Ctx& cx, const RB& rb, const Act& x, h16_t* hbuf, h16_t* obuf, int 
   ring_update(cx, r1, x);
   stats(cx, h, r2, nh);
   Act out{rb.cin == rb.cout ? x.p : obuf, rb.cout, x.F, x.H, x.W};
-  if (rb.wino2) {  // widths equal: residual x, written in place
+  if (rb.wino2 && rb.cin == rb.cout) {  // residual x, written in place
     conv_wino(cx, h, r2, nh, rb.norm2, rb.conv2w, rb.conv2b, rb.cout, out, x.p, x.fstride(), x.C);
+  } else if (rb.wino2) {
+    // shortcut first (1x1 GEMM over the raw input, with the pre-summed
+    // biases of conv2 and the shortcut), then conv2 adds onto it in place
+    const long long Mv = (long long)x.F * x.H * x.W;
+    cx.what = "shortcut_gemm";
+    cx.rs_tensor = nullptr;
+    cx.run(1, 2.0 * Mv * rb.cout * rb.cin, [&] {
+      return launch_gemm1x1(x.p, Mv, x.C, rb.cin, cx.prep<h16_t>(rb.scw), cx.wbytes(rb.scw), rb.cout,
+                            cx.prep<float>(rb.scb), out.p, out.C, cx.st);
+    });
+    conv_wino(cx, h, r2, nh, rb.norm2, rb.conv2w, -1, rb.cout, out, out.p, out.fstride(), out.C);
   } else {
     ConvArgs a = conv333(cx, h, r2, nh, rb.norm2, rb.conv2w, rb.conv2b, rb.cout);
     if (rb.cin == rb.cout) {

@@ -1358,7 +1358,126 @@ Variant conv_variant(const ConvArgs& a) {
   return v;
 }
 
+// ---------------------------------------------------------------------------
+// 1x1 convolution as a plain GEMM, out[m][n] = sum_k x[m][k] w[n][k] + bias[n]
+// (the shortcut of a width-changing block).  There is no spatial reuse to
+// stage, so both operands stream from L2 straight into MFMA fragment
+// registers: no LDS in the K loop and no barriers.  256 x 256 tiles on four
+// waves of 128 x 128 (accumulators in AGPRs); A and B fragments of k16 step
+// u live in ring slot u % kG1Depth and are refilled with step u + kG1Depth.
+constexpr int kG1Depth = 4;
+
+__global__ __launch_bounds__(256) void gemm1x1_kernel(const h16_t* __restrict__ x, long long M, int lda, int K,
+                                                      const h16_t* __restrict__ w, int w_bytes, int N,
+                                                      const float* __restrict__ bias, h16_t* __restrict__ out,
+                                                      int ldo) {
+  constexpr int MI = 4, NJ = 4, D = kG1Depth;
+  __shared__ __align__(16) float ep_s[4 * 8 * (128 + 8)];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the A descriptor lives in SGPRs
+  const int wm = wave >> 1, wn = wave & 1;
+  const int kpart = lane >> 5, lrow = lane & 31;
+  const int nN = N / 256;
+  const long long bm = blockIdx.x / nN;
+  const int bn = blockIdx.x % nN;
+  const long long r0 = bm * 256 + wm * 128;  // first row of this wave
+  const int c0 = bn * 256 + wn * 128;        // first column of this wave
+  const long long rows_left = M - r0;
+  const int nrows = rows_left <= 0 ? 0 : (rows_left >= 128 ? 128 : (int)rows_left);
+  // rows past M read zeros (buffer range check), their outputs are skipped
+  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<h16_t*>(x + (nrows > 0 ? r0 : 0) * lda), 0, nrows * lda * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t brsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<h16_t*>(w), 0, w_bytes, 0x00020000);
+  const int U = K / 16;
+  int aoff[MI], boff[NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) aoff[i] = ((32 * i + lrow) * lda + kpart * 8) * 2;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) boff[j] = ((c0 / 32 + j) * U * 512 + lane * 8) * 2;
+  f16x8_t aq[D][MI], bq[D][NJ];
+  auto load_step = [&](int slot, int u) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+      aq[slot][i] = __builtin_bit_cast(f16x8_t, __builtin_amdgcn_raw_buffer_load_b128(arsrc, aoff[i], u * 32, 0));
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      bq[slot][j] = __builtin_bit_cast(f16x8_t, __builtin_amdgcn_raw_buffer_load_b128(brsrc, boff[j], u * 1024, 0));
+  };
+  f32x16_t acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+#pragma unroll
+  for (int s = 0; s < D; ++s) {
+    load_step(s, s);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int u0 = 0; u0 < U; u0 += D) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aq[s][i], bq[s][j], acc[i][j], 0, 0, 0);
+      const int un = u0 + s + D;
+      load_step(s, un < U ? un : U - 1);  // past the end: reload the last step (no branch)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // epilogue: 8-row quarters of each 32-row block through LDS, 16-byte stores
+  float* ep = ep_s + wave * 8 * (128 + 8);
+  const int er = lane >> 3, ec0 = (lane & 7) * 16;
+  float bv[16];
+#pragma unroll
+  for (int k4 = 0; k4 < 4; ++k4) {
+    const float4 b4 = bias ? *reinterpret_cast<const float4*>(bias + c0 + ec0 + 4 * k4) : make_float4(0, 0, 0, 0);
+    bv[4 * k4] = b4.x; bv[4 * k4 + 1] = b4.y; bv[4 * k4 + 2] = b4.z; bv[4 * k4 + 3] = b4.w;
+  }
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int e = 4 * q; e < 4 * q + 4; ++e) ep[(4 * kpart + (e & 3)) * (128 + 8) + 32 * j + lrow] = acc[i][j][e];
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      __builtin_amdgcn_wave_barrier();
+      const int rr = 32 * i + 8 * q + er;
+      if (rr < nrows) {
+        const float* row = ep + er * (128 + 8) + ec0;
+        h16_t* o = out + (r0 + rr) * ldo + c0 + ec0;
+#pragma unroll
+        for (int c8 = 0; c8 < 16; c8 += 8) {
+          float v[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) v[k] = row[c8 + k] + bv[c8 + k];
+          *reinterpret_cast<uint4*>(o + c8) = pack8h(v);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_gemm1x1(const h16_t* x, long long M, int lda, int K, const h16_t* w, long long w_bytes, int N,
+                          const float* bias, h16_t* out, int ldo, hipStream_t stream) {
+  if (g_dry_run) return hipSuccess;
+  if (!x || !w || !out || M < 1 || N % 256 || K % (16 * kG1Depth) || lda % 8 || lda < K || ldo % 8 || ldo < N ||
+      w_bytes <= 0 || w_bytes > 0x7fffffffLL || (long long)128 * lda * 2 > 0x7fffffffLL)
+    return hipErrorInvalidValue;
+  const long long tiles = (M + 255) / 256 * (N / 256);
+  if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gemm1x1_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, x, M, lda, K, w, (int)w_bytes, N, bias,
+                     out, ldo);
+  return hipGetLastError();
+}
 
 // Launches that run on the persistent kernel: the specialised one-segment
 // tap sets on 8-wave tiles, with the epilogues that kernel implements.

@@ -101,6 +101,11 @@ bool conv_is_333(const ConvArgs& a);
 // RMSNorm+SiLU prologue (every ResBlock conv of width >= 256).
 bool conv_is_main(const ConvArgs& a);
 
+// out[m][n] = sum_k x[m][k] w[n][k] + bias[n] for the M rows of x (stride
+// lda) with fragment-order weights (taps = 1); N a multiple of 256, K of 64.
+hipError_t launch_gemm1x1(const h16_t* x, long long M, int lda, int K, const h16_t* w, long long w_bytes, int N,
+                          const float* bias, h16_t* out, int ldo, hipStream_t stream);
+
 // Auxiliary kernels (wvd_aux.hip).
 hipError_t launch_rms_stats(const h16_t* x, long long x_fstride, int lda, const h16_t* ring,
                             int n_hist, int C, int F, int HW, float* rs, hipStream_t s);
