@@ -109,6 +109,19 @@ __device__ __forceinline__ uint4 halo_load(const G& g, int idx, int chunk) {
   return ld_global16(g.vptr[idx / NP] + chunk * (NP * 8) + (idx % NP) * 8);
 }
 
+// The same item split in two: its row's address (an LDS table read that can
+// be issued a step early) and the load of chunk `chunk` of the item from it.
+template <class G>
+__device__ __forceinline__ const h16_t* halo_row(const G& g, int idx) {
+  return g.vptr[idx / G::NP];
+}
+
+template <class G>
+__device__ __forceinline__ uint4 halo_load_at(const h16_t* row, int idx, int chunk) {
+  constexpr int NP = G::NP;
+  return ld_global16(row + chunk * (NP * 8) + (idx % NP) * 8);
+}
+
 template <bool NORM, bool ACT, class G>
 __device__ __forceinline__ void halo_store(const G& g, int idx, int chunk, uint4 r, unsigned char* hbuf) {
   constexpr int NP = G::NP;
@@ -1054,6 +1067,14 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
         static_assert(IPK <= 2, "halo items per tap");
         uint4 hr[3][IPK];
         f16x8_t ap[2][MI];
+        // Row addresses of a tap's halo items come from the LDS table one
+        // step before their loads (tap 0's ahead of the chunk's first A
+        // reads), so waiting for them never waits for A reads issued later.
+        const h16_t* hp[2][IPK];
+#pragma unroll
+        for (int j = 0; j < IPK; ++j)
+          if (j < IPT) hp[0][j] = halo_row(gn, tid + NT * j);
+        __builtin_amdgcn_sched_barrier(0);
         if constexpr (APF) {
 #pragma unroll
           for (int i = 0; i < MI; ++i) ap[0][i] = *reinterpret_cast<const f16x8_t*>(hsrc + g.abase[i]);
@@ -1085,14 +1106,23 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
             for (int j = 0; j < IPK; ++j) {
               const int is = (tap - 3) * IPK + j, il = tap * IPK + j;
               if (tap >= 3 && is < IPT) halo_store<false, false>(gn, tid + NT * is, cn, hr[tap % 3][j], hdst);
-              if (tap < 5 && il < IPT) hr[tap % 3][j] = halo_load(gn, tid + NT * il, cn);
+              if (tap < 5 && il < IPT) hr[tap % 3][j] = halo_load_at<SegCtx<BK, MI, NJ, NT>>(hp[tap & 1][j], tid + NT * il, cn);
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < IPK; ++j) {
+              const int il = (tap + 1) * IPK + j;
+              if (tap + 1 < 5 && il < IPT) hp[(tap + 1) & 1][j] = halo_row(gn, tid + NT * il);
             }
           }
 #pragma unroll
           for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bq[u % kBRing][j], acc[i][j], 0, 0, 0);
+              // operands swapped: rows of the product are output channels and
+              // columns positions, so a lane's accumulators are runs of four
+              // consecutive channels of one position
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bq[u % kBRing][j], av[i], acc[i][j], 0, 0, 0);
           if (u + kBRing < 18)
             load_step(g, bq[u % kBRing], c, (u + kBRing) >> 1, (u + kBRing) & 1);
           else
@@ -1167,89 +1197,145 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
     const int nn = seq.at(k + 2);
     if (nn >= 0) build_tables(k & 1, nn);
 
-    // ---- epilogue: 8-row quarters of each 32-row block through the last
-    // chunk's halo buffer (free now), then 16-byte stores along channels ----
-    constexpr int EROW = WN + 8;          // padded LDS row (floats)
-    constexpr int LPR = 64 / 8;           // lanes per staged row
-    constexpr int CPL = WN / LPR;         // channels per lane
-    float* ep = reinterpret_cast<float*>(smem + ((gc - 1) & 1) * halo_bytes) + wave * 8 * EROW;
-    const int er = lane / LPR;
-    const int ec0 = (lane % LPR) * CPL;
-    const int ncol0 = geo.n0 + wave_n * WN;
+    if constexpr (WINO) {
+      // ---- Winograd epilogue: lane (kpart, lrow) of block (i, j) holds
+      // position 32i + lrow of the wave's rows and channels
+      // 32j + 8g + 4*kpart + r (accumulator 4g + r).  Per 32 positions and
+      // 64 channels the wave writes the runs of four straight from the
+      // accumulators into its own fp32 LDS rows (16-byte writes), then
+      // reads eight channels per lane, packs them to fp16 and stores 16
+      // bytes per lane along the output row.
+      constexpr int JH = NW == 4 ? 2 : 1;   // channel blocks per staging round
+      constexpr int SCH = 32 * JH;          // staged channels per row
+      constexpr int SROW = SCH * 4 + 16;    // staged row bytes: fp32 + pad
+      constexpr int LPR = SCH / 8;          // lanes per staged row (8 channels each)
+      constexpr int RPI = 64 / LPR;         // rows per read
+      static_assert(NJ % JH == 0 && 64 % LPR == 0, "staging split");
+      static_assert(NHV * ROWB >= NW * 32 * SROW, "staged rows fit in one halo buffer");
+      unsigned char* st = smem + ((gc - 1) & 1) * halo_bytes + wave * 32 * SROW;
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
+      for (int i = 0; i < MI; ++i) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+        for (int jh = 0; jh < NJ / JH; ++jh) {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
+          for (int jj = 0; jj < JH; ++jj)
 #pragma unroll
-          for (int e = 4 * q; e < 4 * q + 4; ++e) ep[(4 * kpart + (e & 3)) * EROW + 32 * j + lrow] = acc[i][j][e];
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the rows are in LDS
-        __builtin_amdgcn_wave_barrier();
-        const int m = wave_m * WM + 32 * i + 8 * q + er;
-        const int tx = m & (kTileW - 1);
-        const int t2 = m / kTileW;
-        const int f = geo.f0 + t2 / TH, y = geo.y0 + t2 % TH, x = geo.x0 + tx;
-        const int nb = ncol0 + ec0;
-        if (f < a.F && y < a.H && x < a.W && nb < a.Cout) {
-          const long long pix = (long long)y * a.W + x;
-          const float* row = ep + er * EROW + ec0;
-          if (a.epi == EPI_VIDEO) {
-            for (int cc = 0; cc < CPL && nb + cc < a.Cout; ++cc) {
-              const int n = nb + cc;
-              float v = row[cc] * a.scale + (a.bias ? a.bias[n] : 0.0f);
-              v = fminf(fmaxf(v, -1.0f), 1.0f);
-              const int kk = n >> 2, ddy = (n >> 1) & 1, ddx = n & 1;
-              const long long r2 = ((long long)kk * a.video_T + a.out_base + f) * (2 * a.H) + 2 * y + ddy;
-              static_cast<bf16_t*>(a.out)[r2 * (2 * a.W) + 2 * x + ddx] = (bf16_t)f2bf(v);
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const f32x16_t& c = acc[i][jh * JH + jj];
+              f32x4_t v = {c[4 * g4], c[4 * g4 + 1], c[4 * g4 + 2], c[4 * g4 + 3]};
+              *reinterpret_cast<f32x4_t*>(st + lrow * SROW + (32 * jj + 8 * g4 + 4 * kpart) * 4) = v;
             }
-          } else if constexpr (CPL % 8 == 0) {
-            h16_t* o;
-            int ob = nb;  // output channel of this lane's first column
-            if (a.epi == EPI_PHASE) {
-              const long long op = (long long)(2 * y + (geo.ph >> 1)) * (2 * a.W) + (2 * x + (geo.ph & 1));
-              o = static_cast<h16_t*>(a.out) + f * a.out_fstride + op * a.ldo;
-            } else if (a.epi == EPI_WINO) {
-              o = static_cast<h16_t*>(a.out) + geo.ph * a.out_pstride + f * a.out_fstride + pix * a.ldo;
-            } else if (a.epi == EPI_TIME) {
-              // channel half h of frame f -> output frame out_base + 2f + h
-              const int Chalf = a.Cout >> 1;
-              const int half = nb >= Chalf ? 1 : 0;
-              ob = nb - half * Chalf;
-              o = static_cast<h16_t*>(a.out) + (long long)(a.out_base + 2 * f + half) * a.out_fstride + pix * a.ldo;
-            } else {
-              o = static_cast<h16_t*>(a.out) + f * a.out_fstride + pix * a.ldo;
+          __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the block is in LDS
+          __builtin_amdgcn_wave_barrier();
+          const int ncol = geo.n0 + wave_n * WN + jh * SCH + (lane % LPR) * 8;
+#pragma unroll
+          for (int rr = 0; rr < 32 / RPI; ++rr) {
+            const int r = rr * RPI + lane / LPR;
+            const float* row = reinterpret_cast<const float*>(st + r * SROW) + (lane % LPR) * 8;
+            const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(row);
+            const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(row + 4);
+            const int m = wave_m * WM + 32 * i + r;
+            const int tx = m & (kTileW - 1);
+            const int t2 = m / kTileW;
+            const int f = geo.f0 + t2 / TH, y = geo.y0 + t2 % TH, x = geo.x0 + tx;
+            if (f < a.F && y < a.H && x < a.W) {
+              const float v8[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+              const long long pix = (long long)y * a.W + x;
+              h16_t* o = static_cast<h16_t*>(a.out) + geo.ph * a.out_pstride + f * a.out_fstride + pix * a.ldo;
+              *reinterpret_cast<uint4*>(o + ncol) = pack8h(v8);
             }
-            const h16_t* rp = a.res ? a.res + f * a.res_fstride + pix * a.ldr + nb : nullptr;
-            const bool full = nb + CPL <= a.Cout;
-#pragma unroll
-            for (int c8 = 0; c8 < CPL; c8 += 8) {
-              float v[8];
-#pragma unroll
-              for (int kk = 0; kk < 8; ++kk) v[kk] = row[c8 + kk] * a.scale;
-              if (full) {
-                if (a.bias) {
-#pragma unroll
-                  for (int kk = 0; kk < 8; ++kk) v[kk] += a.bias[nb + c8 + kk];
-                }
-                if (rp) {
-                  float r[8];
-                  unpack8h(*reinterpret_cast<const uint4*>(rp + c8), r);
-#pragma unroll
-                  for (int kk = 0; kk < 8; ++kk) v[kk] += r[kk];
-                }
-                *reinterpret_cast<uint4*>(o + ob + c8) = pack8h(v);
+          }
+          // the next round's writes reuse these rows: this round's reads first
+          __builtin_amdgcn_s_waitcnt(0xc07f);
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    } else {
+      // ---- epilogue: 8-row quarters of each 32-row block through the last
+      // chunk's halo buffer (free now), then 16-byte stores along channels ----
+      constexpr int EROW = WN + 8;          // padded LDS row (floats)
+      constexpr int LPR = 64 / 8;           // lanes per staged row
+      constexpr int CPL = WN / LPR;         // channels per lane
+      float* ep = reinterpret_cast<float*>(smem + ((gc - 1) & 1) * halo_bytes) + wave * 8 * EROW;
+      const int er = lane / LPR;
+      const int ec0 = (lane % LPR) * CPL;
+      const int ncol0 = geo.n0 + wave_n * WN;
+  #pragma unroll
+      for (int i = 0; i < MI; ++i) {
+  #pragma unroll
+        for (int q = 0; q < 4; ++q) {
+  #pragma unroll
+          for (int j = 0; j < NJ; ++j)
+  #pragma unroll
+            for (int e = 4 * q; e < 4 * q + 4; ++e) ep[(4 * kpart + (e & 3)) * EROW + 32 * j + lrow] = acc[i][j][e];
+          __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the rows are in LDS
+          __builtin_amdgcn_wave_barrier();
+          const int m = wave_m * WM + 32 * i + 8 * q + er;
+          const int tx = m & (kTileW - 1);
+          const int t2 = m / kTileW;
+          const int f = geo.f0 + t2 / TH, y = geo.y0 + t2 % TH, x = geo.x0 + tx;
+          const int nb = ncol0 + ec0;
+          if (f < a.F && y < a.H && x < a.W && nb < a.Cout) {
+            const long long pix = (long long)y * a.W + x;
+            const float* row = ep + er * EROW + ec0;
+            if (a.epi == EPI_VIDEO) {
+              for (int cc = 0; cc < CPL && nb + cc < a.Cout; ++cc) {
+                const int n = nb + cc;
+                float v = row[cc] * a.scale + (a.bias ? a.bias[n] : 0.0f);
+                v = fminf(fmaxf(v, -1.0f), 1.0f);
+                const int kk = n >> 2, ddy = (n >> 1) & 1, ddx = n & 1;
+                const long long r2 = ((long long)kk * a.video_T + a.out_base + f) * (2 * a.H) + 2 * y + ddy;
+                static_cast<bf16_t*>(a.out)[r2 * (2 * a.W) + 2 * x + ddx] = (bf16_t)f2bf(v);
+              }
+            } else if constexpr (CPL % 8 == 0) {
+              h16_t* o;
+              int ob = nb;  // output channel of this lane's first column
+              if (a.epi == EPI_PHASE) {
+                const long long op = (long long)(2 * y + (geo.ph >> 1)) * (2 * a.W) + (2 * x + (geo.ph & 1));
+                o = static_cast<h16_t*>(a.out) + f * a.out_fstride + op * a.ldo;
+              } else if (a.epi == EPI_WINO) {
+                o = static_cast<h16_t*>(a.out) + geo.ph * a.out_pstride + f * a.out_fstride + pix * a.ldo;
+              } else if (a.epi == EPI_TIME) {
+                // channel half h of frame f -> output frame out_base + 2f + h
+                const int Chalf = a.Cout >> 1;
+                const int half = nb >= Chalf ? 1 : 0;
+                ob = nb - half * Chalf;
+                o = static_cast<h16_t*>(a.out) + (long long)(a.out_base + 2 * f + half) * a.out_fstride + pix * a.ldo;
               } else {
-                for (int kk = 0; kk < 8 && nb + c8 + kk < a.Cout; ++kk) {
-                  float t = v[kk] + (a.bias ? a.bias[nb + c8 + kk] : 0.0f);
-                  if (rp) t += h2f(rp[c8 + kk]);
-                  o[ob + c8 + kk] = (h16_t)f2h(t);
+                o = static_cast<h16_t*>(a.out) + f * a.out_fstride + pix * a.ldo;
+              }
+              const h16_t* rp = a.res ? a.res + f * a.res_fstride + pix * a.ldr + nb : nullptr;
+              const bool full = nb + CPL <= a.Cout;
+  #pragma unroll
+              for (int c8 = 0; c8 < CPL; c8 += 8) {
+                float v[8];
+  #pragma unroll
+                for (int kk = 0; kk < 8; ++kk) v[kk] = row[c8 + kk] * a.scale;
+                if (full) {
+                  if (a.bias) {
+  #pragma unroll
+                    for (int kk = 0; kk < 8; ++kk) v[kk] += a.bias[nb + c8 + kk];
+                  }
+                  if (rp) {
+                    float r[8];
+                    unpack8h(*reinterpret_cast<const uint4*>(rp + c8), r);
+  #pragma unroll
+                    for (int kk = 0; kk < 8; ++kk) v[kk] += r[kk];
+                  }
+                  *reinterpret_cast<uint4*>(o + ob + c8) = pack8h(v);
+                } else {
+                  for (int kk = 0; kk < 8 && nb + c8 + kk < a.Cout; ++kk) {
+                    float t = v[kk] + (a.bias ? a.bias[nb + c8 + kk] : 0.0f);
+                    if (rp) t += h2f(rp[c8 + kk]);
+                    o[ob + c8 + kk] = (h16_t)f2h(t);
+                  }
                 }
               }
             }
           }
+          __builtin_amdgcn_wave_barrier();
         }
-        __builtin_amdgcn_wave_barrier();
       }
     }
 #pragma unroll
@@ -1537,6 +1623,8 @@ const char* conv_check(const ConvArgs& a) {
     if (g.KS == KS_3x1 && (a.epi != EPI_WINO || conv_variant(a).mode != 4))
       return "3x1 taps run only as the Winograd-domain GEMM";
     if ((a.epi == EPI_WINO) != (g.KS == KS_3x1)) return "EPI_WINO needs the 3x1 taps";
+    if (a.epi == EPI_WINO && (a.bias || a.res || a.scale != 1.0f))
+      return "the Winograd-domain GEMM stores plain products (no bias, residual or scale)";
     if (nhv > a.nhv_max) return "halo larger than nhv_max";
     if ((g.KT == 3 && g.KS == 3 && a.TF == kTF333 && a.TH == kTH333 &&
          ((kNHV333 * (bk / 8) + 511) / 512) * 512 / (bk / 8) > a.nhv_max))
