@@ -362,6 +362,9 @@ void set_grid(ConvArgs& a, int F, int H, int W, int TF) {
     const int hsx = g.KS == KS_1x1 || g.KS == KS_3x1 ? 0 : 1;
     const int nhv = (TF + g.KT - 1) * (a.TH + 2 * hsy) * (kTileW + 2 * hsx);
     rows = std::max(rows, (nhv * np + 511) / 512 * 512 / np);  // whole rounds for 256 or 512 threads
+    // the Winograd and up-conv epilogues stage their rows in one halo buffer
+    if (g.KS == KS_3x1 || g.KS == KS_PHASE)
+      rows = std::max(rows, (kSwapEpiBytes / (32 * 2 + 16) + 16) / 16 * 16);
   }
   a.nhv_max = rows;
 }

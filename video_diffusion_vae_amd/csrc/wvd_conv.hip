@@ -46,6 +46,9 @@
 #ifndef WVD_ILV
 #define WVD_ILV 1
 #endif
+#ifndef WVD_WINO_LAG
+#define WVD_WINO_LAG 3  // Winograd GEMM: taps between a halo item's load and its LDS store
+#endif
 #ifndef WVD_WINO_W4
 #define WVD_WINO_W4 1
 #endif
@@ -842,6 +845,9 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
   constexpr bool ACT = PRO0 == PRO_NORM_SILU;
   constexpr bool KT3 = MODE == 3;   // 3x1x1 temporal conv (time_conv)
   constexpr bool WINO = MODE == 4;  // Winograd-domain 3x3x1 (t, y) GEMM, one xi per phase
+  // the Winograd and phase loops pass B as the MFMA's first operand: rows of
+  // the product are output channels, columns output positions
+  constexpr bool SWAPPED = WINO || MODE == 2;
   constexpr int TF = MODE == 2 ? 1 : (MODE == 4 ? kTFWino : kTF333);
   constexpr int TH = MODE == 2 ? 16 : (MODE == 4 ? kTHWino : kTH333);
   constexpr int KT = MODE == 2 ? 1 : 3;
@@ -1065,7 +1071,9 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
         constexpr int IPT = (NHV * NP + NT - 1) / NT;
         constexpr int IPK = (IPT + 4) / 5;
         static_assert(IPK <= 2, "halo items per tap");
-        uint4 hr[3][IPK];
+        constexpr int LAGT = WVD_WINO_LAG;
+        static_assert(LAGT >= 1 && LAGT + 4 <= 8, "halo items stored inside the chunk");
+        uint4 hr[LAGT][IPK];
         f16x8_t ap[2][MI];
         // Row addresses of a tap's halo items come from the LDS table one
         // step before their loads (tap 0's ahead of the chunk's first A
@@ -1104,9 +1112,9 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
           if (ks == 0) {
 #pragma unroll
             for (int j = 0; j < IPK; ++j) {
-              const int is = (tap - 3) * IPK + j, il = tap * IPK + j;
-              if (tap >= 3 && is < IPT) halo_store<false, false>(gn, tid + NT * is, cn, hr[tap % 3][j], hdst);
-              if (tap < 5 && il < IPT) hr[tap % 3][j] = halo_load_at<SegCtx<BK, MI, NJ, NT>>(hp[tap & 1][j], tid + NT * il, cn);
+              const int is = (tap - LAGT) * IPK + j, il = tap * IPK + j;
+              if (tap >= LAGT && is < IPT) halo_store<false, false>(gn, tid + NT * is, cn, hr[tap % LAGT][j], hdst);
+              if (tap < 5 && il < IPT) hr[tap % LAGT][j] = halo_load_at<SegCtx<BK, MI, NJ, NT>>(hp[tap & 1][j], tid + NT * il, cn);
             }
           } else {
 #pragma unroll
@@ -1182,7 +1190,7 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
           for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bq[u & 3][j], acc[i][j], 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bq[u & 3][j], av[i], acc[i][j], 0, 0, 0);  // swapped, as below
           if (u + 4 < 8)
             load_step(g, bq[u & 3], c, (u + 4) >> 1, ks);
           else
@@ -1197,21 +1205,22 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
     const int nn = seq.at(k + 2);
     if (nn >= 0) build_tables(k & 1, nn);
 
-    if constexpr (WINO) {
-      // ---- Winograd epilogue: lane (kpart, lrow) of block (i, j) holds
-      // position 32i + lrow of the wave's rows and channels
-      // 32j + 8g + 4*kpart + r (accumulator 4g + r).  Per 32 positions and
-      // 64 channels the wave writes the runs of four straight from the
-      // accumulators into its own fp32 LDS rows (16-byte writes), then
-      // reads eight channels per lane, packs them to fp16 and stores 16
-      // bytes per lane along the output row.
+    if constexpr (SWAPPED) {
+      // ---- epilogue of the swapped-operand loops (Winograd-domain GEMM,
+      // up-conv phases): lane (kpart, lrow) of block (i, j) holds position
+      // 32i + lrow of the wave's rows and channels 32j + 8g + 4*kpart + r
+      // (accumulator 4g + r).  Per 32 positions and SCH channels the wave
+      // writes the runs of four straight from the accumulators into its own
+      // fp32 LDS rows (16-byte writes), then reads eight channels per lane,
+      // adds the bias, packs them to fp16 and stores 16 bytes per lane along
+      // the output row.
       constexpr int JH = NW == 4 ? 2 : 1;   // channel blocks per staging round
       constexpr int SCH = 32 * JH;          // staged channels per row
       constexpr int SROW = SCH * 4 + 16;    // staged row bytes: fp32 + pad
       constexpr int LPR = SCH / 8;          // lanes per staged row (8 channels each)
       constexpr int RPI = 64 / LPR;         // rows per read
       static_assert(NJ % JH == 0 && 64 % LPR == 0, "staging split");
-      static_assert(NHV * ROWB >= NW * 32 * SROW, "staged rows fit in one halo buffer");
+      static_assert(NW * 32 * SROW <= kSwapEpiBytes, "staged rows fit in one halo buffer (nhv_max)");
       unsigned char* st = smem + ((gc - 1) & 1) * halo_bytes + wave * 32 * SROW;
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
@@ -1228,6 +1237,18 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
           __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the block is in LDS
           __builtin_amdgcn_wave_barrier();
           const int ncol = geo.n0 + wave_n * WN + jh * SCH + (lane % LPR) * 8;
+          float bv[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) bv[k] = 0.0f;
+          if (!WINO && a.bias) {
+            const f32x4_t b0 = *reinterpret_cast<const f32x4_t*>(a.bias + ncol);
+            const f32x4_t b1 = *reinterpret_cast<const f32x4_t*>(a.bias + ncol + 4);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              bv[k] = b0[k];
+              bv[4 + k] = b1[k];
+            }
+          }
 #pragma unroll
           for (int rr = 0; rr < 32 / RPI; ++rr) {
             const int r = rr * RPI + lane / LPR;
@@ -1239,9 +1260,17 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
             const int t2 = m / kTileW;
             const int f = geo.f0 + t2 / TH, y = geo.y0 + t2 % TH, x = geo.x0 + tx;
             if (f < a.F && y < a.H && x < a.W) {
-              const float v8[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-              const long long pix = (long long)y * a.W + x;
-              h16_t* o = static_cast<h16_t*>(a.out) + geo.ph * a.out_pstride + f * a.out_fstride + pix * a.ldo;
+              float v8[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+              h16_t* o;
+              if constexpr (WINO) {
+                const long long pix = (long long)y * a.W + x;
+                o = static_cast<h16_t*>(a.out) + geo.ph * a.out_pstride + f * a.out_fstride + pix * a.ldo;
+              } else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) v8[k] = v8[k] * a.scale + bv[k];
+                const long long op = (long long)(2 * y + (geo.ph >> 1)) * (2 * a.W) + (2 * x + (geo.ph & 1));
+                o = static_cast<h16_t*>(a.out) + f * a.out_fstride + op * a.ldo;
+              }
               *reinterpret_cast<uint4*>(o + ncol) = pack8h(v8);
             }
           }
@@ -1623,6 +1652,9 @@ const char* conv_check(const ConvArgs& a) {
     if (g.KS == KS_3x1 && (a.epi != EPI_WINO || conv_variant(a).mode != 4))
       return "3x1 taps run only as the Winograd-domain GEMM";
     if ((a.epi == EPI_WINO) != (g.KS == KS_3x1)) return "EPI_WINO needs the 3x1 taps";
+    if ((a.epi == EPI_WINO || a.epi == EPI_PHASE) && a.nhv_max * (bk * 2 + 16) < kSwapEpiBytes)
+      return "halo buffer below the epilogue's staging rows";
+    if (a.epi == EPI_PHASE && a.res) return "the up-conv epilogue adds no residual";
     if (a.epi == EPI_WINO && (a.bias || a.res || a.scale != 1.0f))
       return "the Winograd-domain GEMM stores plain products (no bias, residual or scale)";
     if (nhv > a.nhv_max) return "halo larger than nhv_max";
