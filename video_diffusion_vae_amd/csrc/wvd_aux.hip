@@ -390,22 +390,24 @@ __global__ void prep_wino_frag_kernel(const void* __restrict__ w, int dtype, int
   }
 }
 
-// Input transform: one thread per (slot, row, column group, 8-channel group).
+// Input transform: one thread per (slot, row, run of kWinoInRun column groups,
+// 8-channel group).
 __global__ __launch_bounds__(256) void wino_in_kernel(const h16_t* __restrict__ x, long long x_fstride, int lda,
                                                       const h16_t* __restrict__ ring, int first_slot, int C, int S,
                                                       int H, int W, int WQ, const float* __restrict__ rs,
                                                       const float* __restrict__ gamma, h16_t* __restrict__ U) {
-  constexpr int WM = kWinoM, NX = Wino<WM>::N;
+  constexpr int WM = kWinoM, NX = Wino<WM>::N, R = kWinoInRun;
   const int G8 = C >> 3;
+  const int QB = (WQ + R - 1) / R;  // runs of R column groups per row
   const long long HW = (long long)H * W;
   const long long plane = (long long)S * H * WQ * C;  // elements per xi plane
-  const long long n = (long long)(S - first_slot) * H * WQ * G8;
+  const long long n = (long long)(S - first_slot) * H * QB * G8;
   for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n;
        e += (long long)gridDim.x * blockDim.x) {
     const int g = (int)(e % G8);
     long long r = e / G8;
-    const int q = (int)(r % WQ);
-    r /= WQ;
+    const int qb = (int)(r % QB);
+    r /= QB;
     const int row = (int)(r % H);
     const int slot = (int)(r / H) + first_slot;
     float gm[8];
@@ -415,38 +417,55 @@ __global__ __launch_bounds__(256) void wino_in_kernel(const h16_t* __restrict__ 
       gm[0] = g0.x; gm[1] = g0.y; gm[2] = g0.z; gm[3] = g0.w;
       gm[4] = g1.x; gm[5] = g1.y; gm[6] = g1.z; gm[7] = g1.w;
     }
-    float y[NX][8];
+    const h16_t* src_row = slot < 2 ? ring + ((long long)slot * HW + (long long)row * W) * C
+                                    : x + (slot - 2) * x_fstride + (long long)row * W * lda;
+    const long long ld = slot < 2 ? C : lda;
+    const float* rs_row = rs + (long long)slot * HW + (long long)row * W;
+    // SiLU(x * rs * gamma) of column `col` (zero outside the row)
+    auto act = [&](int col, float* y) {
 #pragma unroll
-    for (int k = 0; k < NX; ++k) {
-      const int col = WM * q - 1 + k;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) y[k][c] = 0.0f;
+      for (int c = 0; c < 8; ++c) y[c] = 0.0f;
       if (col >= 0 && col < W) {
-        const long long pix = (long long)row * W + col;
-        const h16_t* src = slot < 2 ? ring + ((long long)slot * HW + pix) * C : x + (slot - 2) * x_fstride + pix * lda;
         float f[8];
-        unpack8h(*reinterpret_cast<const uint4*>(src + g * 8), f);
-        const float sc = rs[(long long)slot * HW + pix];
+        unpack8h(*reinterpret_cast<const uint4*>(src_row + col * ld + g * 8), f);
+        const float sc = rs_row[col];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           const float t = f[c] * sc * gm[c];
-          y[k][c] = t * __builtin_amdgcn_rcpf(1.0f + __expf(-t));
+          y[c] = t * __builtin_amdgcn_rcpf(1.0f + __expf(-t));
         }
       }
+    };
+    // A run of R neighbouring column groups slides a six-column window by
+    // four: each activated column is computed once (groups share two).
+    float y[NX][8];
+    const int q0 = qb * R;
+#pragma unroll
+    for (int k = 0; k < NX - WM; ++k) act(WM * q0 - 1 + k, y[k]);
+    h16_t* dst = U + ((long long)slot * H * WQ + (long long)row * WQ + q0) * C + g * 8;
+#pragma unroll
+    for (int qq = 0; qq < R; ++qq) {
+      if (q0 + qq >= WQ) break;
+#pragma unroll
+      for (int k = NX - WM; k < NX; ++k) act(WM * (q0 + qq) - 1 + k, y[k]);
+      float u[NX][8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        float d[NX], uu[NX];
+#pragma unroll
+        for (int k = 0; k < NX; ++k) d[k] = y[k][c];
+        Wino<WM>::input(d, uu);
+#pragma unroll
+        for (int k = 0; k < NX; ++k) u[k][c] = uu[k];
+      }
+#pragma unroll
+      for (int k = 0; k < NX; ++k) *reinterpret_cast<uint4*>(dst + qq * C + k * plane) = pack8h(u[k]);
+      // the last two columns of this window open the next one
+#pragma unroll
+      for (int k = 0; k < NX - WM; ++k)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) y[k][c] = y[WM + k][c];
     }
-    float u[NX][8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      float d[NX], uu[NX];
-#pragma unroll
-      for (int k = 0; k < NX; ++k) d[k] = y[k][c];
-      Wino<WM>::input(d, uu);
-#pragma unroll
-      for (int k = 0; k < NX; ++k) u[k][c] = uu[k];
-    }
-    h16_t* dst = U + ((long long)slot * H * WQ + (long long)row * WQ + q) * C + g * 8;
-#pragma unroll
-    for (int k = 0; k < NX; ++k) *reinterpret_cast<uint4*>(dst + k * plane) = pack8h(u[k]);
   }
 }
 
@@ -665,7 +684,7 @@ hipError_t launch_wino_in(const h16_t* x, long long x_fstride, int lda, const h1
   if (g_dry_run) return hipSuccess;
   if (C % 8 || n_hist < 0 || n_hist > 2 || (n_hist > 0 && !ring) || F < 1) return hipErrorInvalidValue;
   const int WQ = (W + kWinoM - 1) / kWinoM;
-  const long long n = (long long)(F + n_hist) * H * WQ * (C / 8);
+  const long long n = (long long)(F + n_hist) * H * ((WQ + kWinoInRun - 1) / kWinoInRun) * (C / 8);
   hipLaunchKernelGGL(wino_in_kernel, dim3(grid_for(n, 256, 65536)), dim3(256), 0, s, x, x_fstride, lda, ring,
                      2 - n_hist, C, F + 2, H, W, WQ, rs, gamma, U);
   return hipGetLastError();

@@ -16,6 +16,7 @@ constexpr int kMaxCin = 1024;           // largest norm input width kept in LDS
 constexpr int kWinoTF = 2;              // frames per tile of the Winograd-domain GEMM
 constexpr int kWinoM = 4;               // Winograd F(m,3) along x: output columns per group
 constexpr int kWinoN = kWinoM + 2;      // transformed planes (xi) per group
+constexpr int kWinoInRun = 4;           // column groups per thread of the input transform
 // LDS bytes the Winograd and up-conv epilogues stage in one halo buffer:
 // 8 waves x 32 positions x (32 fp32 channels + 16 bytes of pad), or 4 waves
 // x 32 x (64 channels + pad), whichever is larger.
