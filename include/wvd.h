@@ -97,6 +97,40 @@ int wvd_workspace_bytes(const wvd_plan* plan, int T, int frames_per_pass, size_t
 int wvd_decode(const wvd_plan* plan, const void* z, int z_dtype, int T, int frames_per_pass,
                void* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Streaming decode (the temporal caching of the norm-SiLU issue, "Feature,
+ * motivation and proposed scope"; the segment-wise generation of the Wan2.2
+ * page's introduction): latents arrive in chunks and each chunk's video is
+ * produced as soon as it arrives.  The causal history (the last two raw input
+ * frames of every temporal conv) is carried between calls in a caller-owned
+ * state buffer.
+ *
+ * wvd_state_bytes: bytes of that state for the plan (independent of T and of
+ * frames_per_pass).
+ * wvd_chunk_workspace_bytes: workspace bytes wvd_decode_chunk needs for a
+ * chunk of T latent frames at frames_per_pass (the state is not part of it).
+ *
+ * wvd_decode_chunk decodes latent frames [t_begin, t_begin + T) of a clip:
+ *   z:       device [1, 48, T, h, w] of z_dtype, contiguous: those frames only.
+ *   t_begin: latent frames of this clip already decoded into `state`; 0
+ *            starts a new clip (the state's contents are then ignored).
+ *   state:   device buffer of state_bytes >= wvd_state_bytes(plan), 16-byte
+ *            aligned, owned by the caller.  Read (t_begin > 0) and rewritten
+ *            by the call; it must hold the state the previous chunk of the
+ *            same clip left (that chunk ending at t_begin), on the same plan.
+ *            One state per clip: concurrent chunks of one clip are invalid.
+ *   out:     device bf16 [1, 3, V, 16h, 16w], contiguous, with
+ *            V = v(t_begin + T) - v(t_begin), v(t) = (t > 0 ? 4t - 3 : 0):
+ *            the clip's video frames [v(t_begin), v(t_begin + T)).
+ *   workspace: at least wvd_chunk_workspace_bytes(plan, T, frames_per_pass).
+ * The video of a clip decoded in chunks of any sizes, at any frames_per_pass,
+ * is bit-identical to wvd_decode of the whole clip.  Errors as wvd_decode;
+ * WVD_ENOSPACE also for a short state. */
+int wvd_state_bytes(const wvd_plan* plan, size_t* bytes);
+int wvd_chunk_workspace_bytes(const wvd_plan* plan, int T, int frames_per_pass, size_t* bytes);
+int wvd_decode_chunk(const wvd_plan* plan, const void* z, int z_dtype, int T, int t_begin, int frames_per_pass,
+                     void* state, size_t state_bytes, void* out, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
 /* Release a plan (host memory only; the prepared buffer stays the caller's).
  * NULL is ignored. */
 void wvd_destroy(wvd_plan* plan);

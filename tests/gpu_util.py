@@ -86,3 +86,22 @@ def decode_gpu(cfg: synth.Config, seed: int = 0, frames_per_pass: int = 1, T: Op
     out = dec.decode(zt, frames_per_pass=frames_per_pass)
     torch.cuda.synchronize()
     return out.float().cpu().numpy()
+
+
+def decode_gpu_chunks(cfg: synth.Config, chunks, seed: int = 0, frames_per_pass: int = 1) -> np.ndarray:
+    """The clip of sum(chunks) latent frames decoded chunk by chunk through
+    wvd_decode_chunk (one stream state), the chunks' videos concatenated."""
+    import torch
+    T = sum(chunks)
+    dec = decoder_for(cfg, seed)
+    z = synth.make_latents(T, cfg.h, cfg.w, seed=seed, bf16=cfg.weights_bf16)
+    zt = torch.from_numpy(z).to("cuda")
+    if cfg.weights_bf16:
+        zt = zt.to(torch.bfloat16)
+    st = dec.stream()
+    parts, t = [], 0
+    for n in chunks:
+        parts.append(st.decode(zt[:, :, t:t + n], frames_per_pass=frames_per_pass))
+        t += n
+    torch.cuda.synchronize()
+    return torch.cat(parts, dim=2).float().cpu().numpy()

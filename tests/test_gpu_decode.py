@@ -10,7 +10,7 @@ import sys
 import numpy as np
 import pytest
 
-from tests.gpu_util import decode_gpu, gpu_available, oracle_video, rel_l2
+from tests.gpu_util import decode_gpu, decode_gpu_chunks, gpu_available, oracle_video, rel_l2
 from video_diffusion_vae_amd import synth
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
@@ -60,3 +60,23 @@ def test_single_latent_frame_matches_oracle():
     got = decode_gpu(cfg, seed=1, frames_per_pass=1, T=1)
     assert got.shape == (1, 3, 1, 64, 96)
     check_close(got, ref, "tiny T=1")
+
+
+@pytest.mark.parametrize("cfg_name,splits", [
+    ("tiny_c16_T2_4x6", [[1, 1]]),
+    ("c64_T3_352x624", [[1, 2], [2, 1], [1, 1, 1]]),
+])
+def test_chunked_stream_decode_bit_identical(cfg_name, splits):
+    """Streaming decode: the clip decoded chunk by chunk, with the causal
+    history carried in the stream state, equals the whole-clip decode bit for
+    bit (and so matches the oracle)."""
+    cfg = synth.config_by_name(cfg_name)
+    whole = decode_gpu(cfg, seed=0, frames_per_pass=cfg.T)
+    ref = oracle_video(cfg, seed=0)
+    for chunks in splits:
+        for P in (1, 2):
+            print(f"case {cfg_name} chunks={chunks} P={P}", flush=True)
+            got = decode_gpu_chunks(cfg, chunks, seed=0, frames_per_pass=P)
+            assert got.shape == cfg.video_shape
+            assert np.array_equal(got, whole), (chunks, P)
+    check_close(got, ref, f"{cfg_name} chunked")

@@ -6,9 +6,10 @@ the benchmark times (frames_per_pass=4 unless swept).
   full (1 x 3 x 704 x 1248 outputs); the GPU's first frame of the 13- and
   49-latent-frame decodes must match it within the tolerances.
 * Properties that hold at any size, bit-exact on the device: identical video
-  for frames_per_pass 2, 4, 8 and 16 on the 121-latent-frame clip, and the
+  for frames_per_pass 2, 4, 8 and 16 on the 121-latent-frame clip, the
   first 49 frames of the 49-frame clip equal to the 13-latent-frame decode
-  (causal prefix); every element finite and in [-1, 1].
+  (causal prefix), the 13-frame clip streamed in chunks of 5 and 8 latent
+  frames equal to its whole-clip decode; every element finite and in [-1, 1].
 """
 import numpy as np
 import pytest
@@ -69,6 +70,20 @@ def test_causal_prefix_bit_identical(dec):
     full = decode(dec, 49, 4)
     assert full.shape[2] == 193 and short.shape[2] == 49
     assert torch.equal(full[:, :, :49], short)
+
+
+def test_chunked_stream_bit_identical(dec):
+    import torch
+    print("case full-size T=13 streamed as chunks 5 + 8, P=4", flush=True)
+    z = torch.from_numpy(synth.make_latents(13, 44, 78, seed=0)).cuda().to(torch.bfloat16)
+    whole = dec.decode(z, frames_per_pass=4).clone()
+    st = dec.stream()
+    a = st.decode(z[:, :, :5], frames_per_pass=4)
+    b = st.decode(z[:, :, 5:], frames_per_pass=4)
+    torch.cuda.synchronize()
+    assert a.shape[2] == 17 and b.shape[2] == 32
+    assert torch.equal(torch.cat([a, b], dim=2), whole)
+    del a, b, whole, st
 
 
 def test_frames_per_pass_sweep_bit_identical(dec):

@@ -71,3 +71,41 @@ def test_workspace_fits_288GB_at_the_largest_sweep_point(dry):
         assert sizes[2] < sizes[4] < sizes[8] < sizes[16] < 200e9
     finally:
         wvd.wvd_destroy(plan)
+
+
+def test_chunked_decode_schedules_and_validates(dry):
+    """wvd_decode_chunk: the chunks of a clip walk the same per-pass schedule
+    as the whole clip (same launches when the chunks fall on pass
+    boundaries), and bad states, offsets and workspaces are rejected."""
+    wvd = dry
+    plan = plan_for(wvd, 64, 22, 39)
+    try:
+        sb = wvd.wvd_state_bytes(plan)
+        assert sb > 0
+        ws = wvd.wvd_workspace_bytes(plan, 4, 2)
+        cws = wvd.wvd_chunk_workspace_bytes(plan, 2, 2)
+        assert cws + sb <= ws  # the whole-clip workspace holds the rings itself
+        wvd.wvd_decode(plan, FAKE, 0, 4, 2, FAKE, FAKE, ws, 0)
+        whole = wvd.wvd_last_launch_count(plan)
+        n = 0
+        for t0 in (0, 2):
+            wvd.wvd_decode_chunk(plan, FAKE, 0, 2, t0, 2, FAKE, sb, FAKE, FAKE, cws, 0)
+            n += wvd.wvd_last_launch_count(plan)
+        assert n == whole
+        bad = [
+            (dict(state_bytes=sb - 1), wvd.WVD_ENOSPACE),
+            (dict(ws_bytes=cws - 1), wvd.WVD_ENOSPACE),
+            (dict(t_begin=-1), wvd.WVD_EINVAL),
+            (dict(state_ptr=0), wvd.WVD_EINVAL),
+            (dict(state_ptr=FAKE + 8), wvd.WVD_EINVAL),
+            (dict(T=0), wvd.WVD_EINVAL),
+        ]
+        for kw, status in bad:
+            a = dict(T=2, t_begin=2, state_ptr=FAKE, state_bytes=sb, ws_bytes=cws)
+            a.update(kw)
+            with pytest.raises(wvd.WvdError) as e:
+                wvd.wvd_decode_chunk(plan, FAKE, 0, a["T"], a["t_begin"], 2, a["state_ptr"], a["state_bytes"], FAKE,
+                                     FAKE, a["ws_bytes"], 0)
+            assert e.value.status == status, kw
+    finally:
+        wvd.wvd_destroy(plan)

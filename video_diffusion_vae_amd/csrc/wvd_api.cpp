@@ -148,9 +148,13 @@ Layout make_layout(int c, int h, int w) {
 struct Work {
   size_t X, H, Y, zt, rs, qkv, S, Pm, Vt, O;
   size_t U, M;               // Winograd input planes and products
-  std::vector<size_t> ring;  // 24 rings
+  std::vector<size_t> ring;  // 24 rings: offsets inside the ring block
+  size_t rings;              // ring block offset in the workspace (npos: caller-owned state)
+  size_t ring_bytes;         // ring block size
   size_t total;
 };
+
+constexpr size_t kNoRings = ~(size_t)0;
 
 struct RingInfo {
   int cin;
@@ -182,7 +186,7 @@ RingInfo ring_info(int c, int id) {
 
 int lpad_of(int L) { return (L + 31) / 32 * 32; }
 
-Work make_work(int c, int h, int w, int P) {
+Work make_work(int c, int h, int w, int P, bool rings_in_workspace = true) {
   Work W;
   const long long r0 = (long long)h * w;
   const long long res[4] = {r0, 4 * r0, 16 * r0, 64 * r0};
@@ -225,10 +229,17 @@ Work make_work(int c, int h, int w, int P) {
     W.U = take((size_t)u * 2);
     W.M = take((size_t)m * 2);
   }
+  // The causal history (two raw input frames of every temporal conv) lives
+  // in one block: inside the workspace for a whole-clip decode, or in the
+  // caller's stream state for chunked decodes.
+  size_t roff = 0;
   for (int i = 0; i < R_COUNT; ++i) {
     RingInfo ri = ring_info(c, i);
-    W.ring.push_back(take((size_t)2 * res[ri.level] * ri.cin * 2));
+    W.ring.push_back(roff);
+    roff = align_up(roff + (size_t)2 * res[ri.level] * ri.cin * 2);
   }
+  W.ring_bytes = roff;
+  W.rings = rings_in_workspace ? take(roff) : kNoRings;
   W.total = off;
   return W;
 }
@@ -292,6 +303,8 @@ struct Ctx {
   T* prep(int item) const { return reinterpret_cast<T*>(plan->prep + plan->L.items[item].off); }
   template <typename T>
   T* wsp(size_t off) const { return reinterpret_cast<T*>(ws + off); }
+  unsigned char* ringbase = nullptr;  // the ring block (workspace or stream state)
+  h16_t* ring(int id) const { return reinterpret_cast<h16_t*>(ringbase + W->ring[id]); }
   long long wbytes(int item) const { return (long long)plan->L.items[item].bytes; }
 
   hipEvent_t ev() {
@@ -499,8 +512,8 @@ ConvArgs conv333(Ctx& cx, const Act& x, h16_t* ring, int nh, int gamma_item, int
 
 // ResBlock: x -> x (in place) when widths match, else x -> out.
 Act resblock(Ctx& cx, const RB& rb, const Act& x, h16_t* hbuf, h16_t* obuf, int ring1, int ring2, int nh) {
-  h16_t* r1 = cx.wsp<h16_t>(cx.W->ring[ring1]);
-  h16_t* r2 = cx.wsp<h16_t>(cx.W->ring[ring2]);
+  h16_t* r1 = cx.ring(ring1);
+  h16_t* r2 = cx.ring(ring2);
   stats(cx, x, r1, nh);
   Act h{hbuf, rb.cout, x.F, x.H, x.W};
   if (rb.wino1) {
@@ -631,7 +644,7 @@ void attention(Ctx& cx, const Act& x) {
 // time_conv: x (F frames, first global frame g) -> y (interleaved frames).
 Act time_upsample(Ctx& cx, int s, const Act& x, int g, h16_t* ybuf, int ring_id) {
   const Layout& L = cx.plan->L;
-  h16_t* ring = cx.wsp<h16_t>(cx.W->ring[ring_id]);
+  h16_t* ring = cx.ring(ring_id);
   const bool first = g == 0;
   Act y{ybuf, x.C, first ? 2 * x.F - 1 : 2 * x.F, x.H, x.W};
   if (first) {
@@ -762,34 +775,44 @@ int wvd_workspace_bytes(const wvd_plan* plan, int T, int frames_per_pass, size_t
   return WVD_OK;
 }
 
-int wvd_decode(const wvd_plan* cplan, const void* z, int z_dtype, int T, int frames_per_pass, void* out,
-               void* workspace, size_t workspace_bytes, void* stream) {
-  if (!plan_ok(cplan) || !z || !out || !workspace || T < 1 || frames_per_pass < 1) return WVD_EINVAL;
-  if (z_dtype != WVD_DTYPE_BF16 && z_dtype != WVD_DTYPE_F32) return WVD_EINVAL;
-  if (!aligned16(workspace)) return WVD_EINVAL;
-  wvd_plan* plan = const_cast<wvd_plan*>(cplan);
+}  // extern "C"
+
+namespace {
+
+// Video frames of the first t latent frames.
+long long video_frames(long long t) { return t > 0 ? 4 * t - 3 : 0; }
+
+// Decode latent frames [t_begin, t_begin + T) (z holds just those) into their
+// video frames [video_frames(t_begin), video_frames(t_begin + T)).  The rings
+// carry the causal history: in the workspace (t_begin = 0, state = null) or
+// in the caller's stream state.
+int decode_impl(wvd_plan* plan, const void* z, int z_dtype, int T, int t_begin, int frames_per_pass, void* state,
+                void* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const int c = plan->c, h = plan->h, w = plan->w;
   const int P = std::min(T, frames_per_pass);
-  Work W = make_work(c, h, w, P);
+  Work W = make_work(c, h, w, P, state == nullptr);
   if (workspace_bytes < W.total) return WVD_ENOSPACE;
   const Layout& L = plan->L;
   Ctx cx;
   cx.plan = plan;
-  cx.st = static_cast<hipStream_t>(stream);
+  cx.st = stream;
   cx.ws = static_cast<unsigned char*>(workspace);
   cx.W = &W;
+  cx.ringbase = state ? static_cast<unsigned char*>(state) : cx.ws + W.rings;
   plan->launches = 0;
   const int c4 = 4 * c;
   h16_t* X = cx.wsp<h16_t>(W.X);
   h16_t* Hb = cx.wsp<h16_t>(W.H);
   h16_t* Y = cx.wsp<h16_t>(W.Y);
   h16_t* zt = cx.wsp<h16_t>(W.zt);
-  const int VT = 4 * T - 3;
+  const long long vbase = video_frames(t_begin);
+  const int VT = (int)(video_frames((long long)t_begin + T) - vbase);
 
   for (int t0 = 0; t0 < T && cx.err == hipSuccess; t0 += P) {
     const int F0 = std::min(P, T - t0);
-    const bool first = t0 == 0;
-    const int g0 = t0, g1 = first ? 0 : 2 * t0 - 1, g2 = first ? 0 : 4 * t0 - 3;
+    const int G = t_begin + t0;  // global index of the pass's first latent frame
+    const bool first = G == 0;
+    const int g0 = G, g1 = first ? 0 : 2 * G - 1, g2 = first ? 0 : 4 * G - 3;
     const int nh0 = std::min(2, g0), nh1 = std::min(2, g1), nh2 = std::min(2, g2);
     // conv_in on the channels-last latents.
     cx.what = "latent_to_cl";
@@ -797,7 +820,7 @@ int wvd_decode(const wvd_plan* cplan, const void* z, int z_dtype, int T, int fra
     Act za{zt, 64, F0, h, w};
     Act x{X, c4, F0, h, w};
     {
-      h16_t* ring = cx.wsp<h16_t>(W.ring[R_CONV_IN]);
+      h16_t* ring = cx.ring(R_CONV_IN);
       ConvArgs a = args_init();
       a.seg[0] = seg_basic(zt, za.fstride(), 64, 64, cx.prep<h16_t>(L.conv_in_w), 64, (long long)c4 * 64, 3, 3,
                            cx.wbytes(L.conv_in_w));
@@ -840,7 +863,7 @@ int wvd_decode(const wvd_plan* cplan, const void* z, int z_dtype, int T, int fra
     // instead (into the free H buffer), and the head's history ring holds
     // normalised frames.
     {
-      h16_t* ring = cx.wsp<h16_t>(W.ring[R_HEAD]);
+      h16_t* ring = cx.ring(R_HEAD);
       Act yn{Hb, x.C, x.F, x.H, x.W};
       cx.what = "norm_silu";
       cx.run(3, 0, [&] {
@@ -857,7 +880,7 @@ int wvd_decode(const wvd_plan* cplan, const void* z, int z_dtype, int T, int fra
       a.bias = cx.prep<float>(L.head_b);
       a.out = out;
       a.epi = EPI_VIDEO;
-      a.out_base = g2;
+      a.out_base = (int)(g2 - vbase);
       a.video_T = VT;
       set_grid(a, x.F, x.H, x.W, tf_for(3, x.F));
       conv(cx, a, 0);
@@ -866,6 +889,46 @@ int wvd_decode(const wvd_plan* cplan, const void* z, int z_dtype, int T, int fra
   }
   if (cx.err != hipSuccess) return WVD_EHIP;
   return WVD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int wvd_decode(const wvd_plan* cplan, const void* z, int z_dtype, int T, int frames_per_pass, void* out,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  if (!plan_ok(cplan) || !z || !out || !workspace || T < 1 || frames_per_pass < 1) return WVD_EINVAL;
+  if (z_dtype != WVD_DTYPE_BF16 && z_dtype != WVD_DTYPE_F32) return WVD_EINVAL;
+  if (!aligned16(workspace)) return WVD_EINVAL;
+  return decode_impl(const_cast<wvd_plan*>(cplan), z, z_dtype, T, 0, frames_per_pass, nullptr, out, workspace,
+                     workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int wvd_state_bytes(const wvd_plan* plan, size_t* bytes) {
+  if (!plan_ok(plan) || !bytes) return WVD_EINVAL;
+  *bytes = make_work(plan->c, plan->h, plan->w, 1, false).ring_bytes;
+  return WVD_OK;
+}
+
+int wvd_chunk_workspace_bytes(const wvd_plan* plan, int T, int frames_per_pass, size_t* bytes) {
+  if (!plan_ok(plan) || !bytes || T < 1 || frames_per_pass < 1) return WVD_EINVAL;
+  *bytes = make_work(plan->c, plan->h, plan->w, std::min(T, frames_per_pass), false).total;
+  return WVD_OK;
+}
+
+int wvd_decode_chunk(const wvd_plan* cplan, const void* z, int z_dtype, int T, int t_begin, int frames_per_pass,
+                     void* state, size_t state_bytes, void* out, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  if (!plan_ok(cplan) || !z || !out || !workspace || !state || T < 1 || t_begin < 0 || frames_per_pass < 1)
+    return WVD_EINVAL;
+  if (z_dtype != WVD_DTYPE_BF16 && z_dtype != WVD_DTYPE_F32) return WVD_EINVAL;
+  if (!aligned16(workspace) || !aligned16(state)) return WVD_EINVAL;
+  if ((long long)t_begin + T > (1LL << 28)) return WVD_EINVAL;  // video frame indices stay in int
+  size_t need = 0;
+  wvd_state_bytes(cplan, &need);
+  if (state_bytes < need) return WVD_ENOSPACE;
+  return decode_impl(const_cast<wvd_plan*>(cplan), z, z_dtype, T, t_begin, frames_per_pass, state, out, workspace,
+                     workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 const char* wvd_last_error(void) { return g_last_error.c_str(); }

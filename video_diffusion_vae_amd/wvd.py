@@ -49,6 +49,12 @@ def _load() -> ctypes.CDLL:
     lib.wvd_workspace_bytes.restype = i
     lib.wvd_decode.argtypes = [vp, vp, i, i, i, vp, vp, sz, vp]
     lib.wvd_decode.restype = i
+    lib.wvd_state_bytes.argtypes = [vp, ctypes.POINTER(sz)]
+    lib.wvd_state_bytes.restype = i
+    lib.wvd_chunk_workspace_bytes.argtypes = [vp, i, i, ctypes.POINTER(sz)]
+    lib.wvd_chunk_workspace_bytes.restype = i
+    lib.wvd_decode_chunk.argtypes = [vp, vp, i, i, i, i, vp, sz, vp, vp, sz, vp]
+    lib.wvd_decode_chunk.restype = i
     lib.wvd_destroy.argtypes = [vp]
     lib.wvd_destroy.restype = None
     lib.wvd_status_string.argtypes = [i]
@@ -110,6 +116,30 @@ def wvd_decode(plan: int, z_ptr: int, z_dtype: int, T: int, frames_per_pass: int
                ws_bytes: int, stream_ptr: int) -> None:
     _check(_lib.wvd_decode(plan, z_ptr, z_dtype, T, frames_per_pass, out_ptr, ws_ptr, ws_bytes, stream_ptr),
            "wvd_decode")
+
+
+def wvd_state_bytes(plan: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.wvd_state_bytes(plan, ctypes.byref(n)), "wvd_state_bytes")
+    return n.value
+
+
+def wvd_chunk_workspace_bytes(plan: int, T: int, frames_per_pass: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.wvd_chunk_workspace_bytes(plan, T, frames_per_pass, ctypes.byref(n)), "wvd_chunk_workspace_bytes")
+    return n.value
+
+
+def wvd_decode_chunk(plan: int, z_ptr: int, z_dtype: int, T: int, t_begin: int, frames_per_pass: int,
+                     state_ptr: int, state_bytes: int, out_ptr: int, ws_ptr: int, ws_bytes: int,
+                     stream_ptr: int) -> None:
+    _check(_lib.wvd_decode_chunk(plan, z_ptr, z_dtype, T, t_begin, frames_per_pass, state_ptr, state_bytes, out_ptr,
+                                 ws_ptr, ws_bytes, stream_ptr), "wvd_decode_chunk")
+
+
+def video_frames(t: int) -> int:
+    """Video frames of the first t latent frames."""
+    return 4 * t - 3 if t > 0 else 0
 
 
 def wvd_destroy(plan: int) -> None:
@@ -184,17 +214,24 @@ class Decoder:
             out = torch.empty(shape, dtype=torch.bfloat16, device=self.device)
         elif tuple(out.shape) != shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
             raise WvdError(WVD_ESHAPE, f"decode: out must be contiguous bf16 {shape}")
-        need = self.workspace_bytes(T, frames_per_pass)
-        if workspace is None:
-            if self._ws is None or self._ws.numel() < need:
-                self._ws = None
-                self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
-            workspace = self._ws
+        workspace = self._workspace(self.workspace_bytes(T, frames_per_pass), workspace)
         stream = torch.cuda.current_stream(self.device)
         wvd_decode(self.plan, z.data_ptr(), WVD_DTYPE_F32 if zdt == torch.float32 else WVD_DTYPE_BF16, T,
                    int(frames_per_pass), out.data_ptr(), workspace.data_ptr(), workspace.numel(),
                    stream.cuda_stream)
         return out
+
+    def _workspace(self, need: int, workspace):
+        if workspace is None:
+            if self._ws is None or self._ws.numel() < need:
+                self._ws = None
+                self._ws = self.torch.empty(need, dtype=self.torch.uint8, device=self.device)
+            workspace = self._ws
+        return workspace
+
+    def stream(self) -> "DecodeStream":
+        """A clip decoded chunk by chunk (see DecodeStream)."""
+        return DecodeStream(self)
 
     def release_workspace(self) -> None:
         self._ws = None
@@ -210,3 +247,37 @@ class Decoder:
         if plan:
             wvd_destroy(plan)
             self.plan = None
+
+
+class DecodeStream:
+    """One clip decoded as its latents arrive: each decode(z_chunk) returns the
+    video frames of those latent frames, continuing the causal history from the
+    previous chunks (kept in a device state buffer).  The concatenated chunks
+    are bit-identical to Decoder.decode of the whole clip."""
+
+    def __init__(self, dec: Decoder):
+        torch = dec.torch
+        self.dec = dec
+        self.state = torch.empty(wvd_state_bytes(dec.plan), dtype=torch.uint8, device=dec.device)
+        self.t = 0  # latent frames decoded so far
+
+    def decode(self, z, frames_per_pass: int = 4, out=None, workspace=None):
+        dec, torch = self.dec, self.dec.torch
+        if z.dim() != 5 or tuple(z.shape[:2]) != (1, 48) or tuple(z.shape[3:]) != (dec.h, dec.w):
+            raise WvdError(WVD_ESHAPE, f"decode_chunk: latents of shape {tuple(z.shape)}")
+        zdt = torch.float32 if z.dtype == torch.float32 else torch.bfloat16
+        z = z.to(device=dec.device, dtype=zdt).contiguous()
+        T = int(z.shape[2])
+        V = video_frames(self.t + T) - video_frames(self.t)
+        shape = (1, 3, V, 16 * dec.h, 16 * dec.w)
+        if out is None:
+            out = torch.empty(shape, dtype=torch.bfloat16, device=dec.device)
+        elif tuple(out.shape) != shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
+            raise WvdError(WVD_ESHAPE, f"decode_chunk: out must be contiguous bf16 {shape}")
+        workspace = dec._workspace(wvd_chunk_workspace_bytes(dec.plan, T, frames_per_pass), workspace)
+        stream = torch.cuda.current_stream(dec.device)
+        wvd_decode_chunk(dec.plan, z.data_ptr(), WVD_DTYPE_F32 if zdt == torch.float32 else WVD_DTYPE_BF16, T, self.t,
+                         int(frames_per_pass), self.state.data_ptr(), self.state.numel(), out.data_ptr(),
+                         workspace.data_ptr(), workspace.numel(), stream.cuda_stream)
+        self.t += T
+        return out
