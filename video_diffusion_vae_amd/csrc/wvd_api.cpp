@@ -353,13 +353,14 @@ ConvSeg seg_basic(const h16_t* x, long long x_fstride, int lda, int Cin, const h
   return s;
 }
 
-void set_grid(ConvArgs& a, int F, int H, int W, int TF) {
+void set_grid(ConvArgs& a, int F, int H, int W, int TF, int TW = kTileW) {
   a.F = F;
   a.H = H;
   a.W = W;
   a.TF = TF;
-  a.TH = kTileM / kTileW / TF;
-  a.tiles_x = (W + kTileW - 1) / kTileW;
+  a.TW = TW;
+  a.TH = kTileM / TW / TF;
+  a.tiles_x = (W + TW - 1) / TW;
   a.tiles_y = (H + a.TH - 1) / a.TH;
   a.tiles_f = (F + TF - 1) / TF;
   if (a.nphase == 0) a.nphase = 1;
@@ -373,7 +374,7 @@ void set_grid(ConvArgs& a, int F, int H, int W, int TF) {
     const ConvSeg& g = a.seg[s];
     const int hsy = g.KS == KS_1x1 ? 0 : 1;
     const int hsx = g.KS == KS_1x1 || g.KS == KS_3x1 ? 0 : 1;
-    const int nhv = (TF + g.KT - 1) * (a.TH + 2 * hsy) * (kTileW + 2 * hsx);
+    const int nhv = (TF + g.KT - 1) * (a.TH + 2 * hsy) * (TW + 2 * hsx);
     rows = std::max(rows, (nhv * np + 511) / 512 * 512 / np);  // whole rounds for 256 or 512 threads
     // the Winograd and up-conv epilogues stage their rows in one halo buffer
     if (g.KS == KS_3x1 || g.KS == KS_PHASE)
@@ -386,6 +387,7 @@ ConvArgs args_init() {
   ConvArgs a;
   std::memset(&a, 0, sizeof(a));
   a.scale = 1.0f;
+  a.TW = kTileW;
   a.nphase = 1;
   return a;
 }
@@ -453,6 +455,28 @@ int tf_for(int KT, int F) {
 //   U = F(kWinoM,3) input transform of SiLU(norm(x)) over the F frames and the
 //       valid history frames (rs from rms_stats for the same slots),
 //   M[xi] = causal (t, y) 3x3 conv of U[xi] with the transformed weights,
+// Tile width (column groups) of the Winograd-domain GEMM: 16 x 8 rows, or
+// 8 x 16 rows where that needs fewer rounds of tiles over the CUs (the small
+// levels, whose 20 or 39 column groups leave wide tiles mostly empty).
+int wino_tile_w(int F, int H, int WQ, int Cout) {
+  static int slots = 0;
+  if (!slots) {
+    int dev = 0, n = 0;
+    if (!g_dry_run && hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      slots = n;
+    else
+      slots = 256;
+  }
+  auto rounds = [&](int tw) {
+    const int th = kTileM / tw / kWinoTF;
+    const long long tiles = (long long)((WQ + tw - 1) / tw) * ((H + th - 1) / th) * ((F + kWinoTF - 1) / kWinoTF) *
+                            kWinoN * ((Cout + 255) / 256);
+    return (tiles + slots - 1) / slots;
+  };
+  return rounds(8) < rounds(16) ? 8 : 16;
+}
+
 //   out = output transform of M + bias (+ res).
 // Same function as conv333 + EPI_H16, with half of the multiply-adds (F(4,3)).
 void conv_wino(Ctx& cx, const Act& x, h16_t* ring, int nh, int gamma_item, int w_item, int b_item, int Cout,
@@ -482,7 +506,7 @@ void conv_wino(Ctx& cx, const Act& x, h16_t* ring, int nh, int gamma_item, int w
   a.out_pstride = (long long)x.F * mframe;
   a.ldo = Cout;
   a.epi = EPI_WINO;
-  set_grid(a, x.F, x.H, W2, kWinoTF);
+  set_grid(a, x.F, x.H, W2, kWinoTF, wino_tile_w(x.F, x.H, W2, Cout));
   conv(cx, a, 0);
   cx.what = "wino_out";
   cx.run(5, 0, [&] {

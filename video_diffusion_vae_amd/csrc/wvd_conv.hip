@@ -810,16 +810,16 @@ struct TileGeo {
   int f0, y0, x0, n0, ph;
 };
 
-template <int BN, int MODE>
+template <int BN, int MODE, int TW = kTileW>
 __device__ __forceinline__ TileGeo tile_geo(const ConvArgs& a, int logical) {
   constexpr int TF = MODE == 2 ? 1 : (MODE == 4 ? kTFWino : kTF333);
-  constexpr int TH = MODE == 2 ? 16 : (MODE == 4 ? kTHWino : kTH333);
+  constexpr int TH = MODE == 2 ? 16 : (MODE == 4 ? kTileM / TW / kTFWino : kTH333);
   const int nN = (a.Cout + BN - 1) / BN;
   const int nt = logical % nN;
   const int ph = (logical / nN) % a.nphase;
   const int mt = logical / (nN * a.nphase);
   TileGeo t;
-  t.x0 = (mt % a.tiles_x) * kTileW;
+  t.x0 = (mt % a.tiles_x) * TW;
   t.y0 = ((mt / a.tiles_x) % a.tiles_y) * TH;
   t.f0 = (mt / (a.tiles_x * a.tiles_y)) * TF;
   t.n0 = nt * BN;
@@ -827,7 +827,7 @@ __device__ __forceinline__ TileGeo tile_geo(const ConvArgs& a, int logical) {
   return t;
 }
 
-template <int BN, int WAVES_N, int MODE, int PRO0, int NW = 8>
+template <int BN, int WAVES_N, int MODE, int PRO0, int NW = 8, int TWW = kTileW>
 __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
   constexpr int BK = 32, NT = NW * 64, NP = 4;
   // With 4 waves (one per SIMD, 512 registers: accumulators in AGPRs) each
@@ -848,12 +848,14 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
   // the Winograd and phase loops pass B as the MFMA's first operand: rows of
   // the product are output channels, columns output positions
   constexpr bool SWAPPED = WINO || MODE == 2;
+  constexpr int TW = MODE == 4 ? TWW : kTileW;  // tile columns (Winograd: column groups)
+  static_assert(MODE == 4 || TWW == kTileW, "tile width choice is the Winograd GEMM's");
   constexpr int TF = MODE == 2 ? 1 : (MODE == 4 ? kTFWino : kTF333);
-  constexpr int TH = MODE == 2 ? 16 : (MODE == 4 ? kTHWino : kTH333);
+  constexpr int TH = MODE == 2 ? 16 : (MODE == 4 ? kTileM / TW / kTFWino : kTH333);
   constexpr int KT = MODE == 2 ? 1 : 3;
   constexpr int HSX = KT3 || WINO ? 0 : 1;  // spatial halo along x
   constexpr int HSY = KT3 ? 0 : 1;          // and along y
-  constexpr int HX = kTileW + 2 * HSX, HY = TH + 2 * HSY, HF = TF + KT - 1;
+  constexpr int HX = TW + 2 * HSX, HY = TH + 2 * HSY, HF = TF + KT - 1;
   constexpr int NHV = HF * HY * HX;
   constexpr int NTAPS = K333 ? 27 : (KT3 ? 3 : (WINO ? 9 : 4));
   static_assert(MODE >= 1 && MODE <= 4, "specialised tap sets only");
@@ -885,7 +887,7 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
   // Halo table of tile `logical` into table set `tb`: per halo row the
   // source pointer and (norm) scale; padding voxels read the zero row.
   auto build_tables = [&](int tb, int logical) {
-    const TileGeo t = tile_geo<BN, MODE>(a, logical);
+    const TileGeo t = tile_geo<BN, MODE, TW>(a, logical);
     for (int v = tid; v < nhv_max; v += NT) {
       const h16_t* p = a.zero_row;
       float rsv = 0.0f;
@@ -927,14 +929,14 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
     const int m = wave_m * WM + 32 * i + lrow;
-    const int tx = m & (kTileW - 1);
-    const int t2 = m / kTileW;
+    const int tx = m & (TW - 1);
+    const int t2 = m / TW;
     g0.abase[i] = (((t2 / TH) * HY + (t2 % TH)) * HX + tx) * ROWB + kpart * 16;
   }
   const int U = S.Cin / 16;
   auto ctx_for = [&](int logical, int tb) {
     SegCtx<BK, MI, NJ, NT> g = g0;
-    const TileGeo t = tile_geo<BN, MODE>(a, logical);
+    const TileGeo t = tile_geo<BN, MODE, TW>(a, logical);
     g.vptr = vptr_s + tb * nhv_max;
     g.rs = rs_s + tb * nhv_max;
     g.tap0 = t.ph * NTAPS;
@@ -992,7 +994,7 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
     // tile) streams its own halo and weights once more into the spare
     // buffer and ring slots: no branch, exact wait counters.
     const SegCtx<BK, MI, NJ, NT> gl = nxt >= 0 ? ctx_for(nxt, (k + 1) & 1) : g;
-    const TileGeo geo = tile_geo<BN, MODE>(a, cur);
+    const TileGeo geo = tile_geo<BN, MODE, TW>(a, cur);
 
     for (int c = 0; c < nchunks; ++c, ++gc) {
       const bool last = c + 1 == nchunks;
@@ -1256,8 +1258,8 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
             const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(row);
             const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(row + 4);
             const int m = wave_m * WM + 32 * i + r;
-            const int tx = m & (kTileW - 1);
-            const int t2 = m / kTileW;
+            const int tx = m & (TW - 1);
+            const int t2 = m / TW;
             const int f = geo.f0 + t2 / TH, y = geo.y0 + t2 % TH, x = geo.x0 + tx;
             if (f < a.F && y < a.H && x < a.W) {
               float v8[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -1301,8 +1303,8 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
           __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the rows are in LDS
           __builtin_amdgcn_wave_barrier();
           const int m = wave_m * WM + 32 * i + 8 * q + er;
-          const int tx = m & (kTileW - 1);
-          const int t2 = m / kTileW;
+          const int tx = m & (TW - 1);
+          const int t2 = m / TW;
           const int f = geo.f0 + t2 / TH, y = geo.y0 + t2 % TH, x = geo.x0 + tx;
           const int nb = ncol0 + ec0;
           if (f < a.F && y < a.H && x < a.W && nb < a.Cout) {
@@ -1379,11 +1381,11 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
   }
 }
 
-template <int BN, int WAVES_N, int MODE, int PRO0, int NW = 8>
+template <int BN, int WAVES_N, int MODE, int PRO0, int NW = 8, int TW = kTileW>
 hipError_t launch_persist_impl(const ConvArgs& a, hipStream_t stream) {
   if (g_dry_run) return hipSuccess;
   const size_t lds = conv_lds_bytes(a);
-  auto kern = conv_persist<BN, WAVES_N, MODE, PRO0, NW>;
+  auto kern = conv_persist<BN, WAVES_N, MODE, PRO0, NW, TW>;
   static size_t attr_bytes = 0;
   if (lds > attr_bytes) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1452,7 +1454,8 @@ Variant conv_variant(const ConvArgs& a) {
                    v.bk == 32 && a.nseg == 1 && g.wfrag && g.prologue == PRO_RAW;
   const bool kt3 = g.KT == 3 && g.KS == 1 && a.nphase == 1 && a.TF == kTF333 && a.TH == kTH333 && v.bk == 32 &&
                    a.nseg == 1 && g.wfrag && g.prologue == PRO_RAW && a.Cout % 256 == 0 && a.epi == EPI_TIME;
-  const bool kwino = g.KT == 3 && g.KS == KS_3x1 && a.nphase == kWinoN && a.TF == kTFWino && a.TH == kTHWino &&
+  const bool kwino = g.KT == 3 && g.KS == KS_3x1 && a.nphase == kWinoN && a.TF == kTFWino &&
+                     ((a.TW == kTileW && a.TH == kTHWino) || (a.TW == 8 && a.TH == kTileM / 8 / kTFWino)) &&
                      v.bk == 32 && a.nseg == 1 && g.wfrag && g.prologue == PRO_RAW && a.Cout % 256 == 0 &&
                      a.epi == EPI_WINO;
   const bool shortcut_ok = a.nseg == 1 || (a.seg[1].KT == 1 && a.seg[1].KS == 1 && a.seg[1].prologue == PRO_RAW &&
@@ -1628,8 +1631,9 @@ size_t conv_lds_bytes(const ConvArgs& a) {
 }
 
 const char* conv_check(const ConvArgs& a) {
-  if (a.TF < 1 || a.TF * a.TH * kTileW != kTileM) return "tile TF*TH*16 != 256";
   if (a.nseg < 1 || a.nseg > 2) return "segment count";
+  if (a.TW != kTileW && !(a.TW == 8 && a.seg[0].KS == KS_3x1)) return "tile width 8 is the Winograd GEMM's only";
+  if (a.TF < 1 || a.TF * a.TH * a.TW != kTileM) return "tile TF*TH*TW != 256";
   if (a.F < 1 || a.H < 1 || a.W < 1 || a.Cout < 1) return "empty output grid";
   if (a.nphase != 1 && a.nphase != 4 && a.nphase != kWinoN) return "phase count";
   if (conv_lds_bytes(a) > 160 * 1024) return "LDS over 160 KiB";
@@ -1639,7 +1643,7 @@ const char* conv_check(const ConvArgs& a) {
     const int hsy = g.KS == KS_1x1 ? 0 : 1;
     const int hsx = g.KS == KS_1x1 || g.KS == KS_3x1 ? 0 : 1;
     const int k2 = g.KS == KS_3x3 ? 9 : (g.KS == KS_PHASE ? 4 : (g.KS == KS_3x1 ? 3 : 1));
-    const int nhv = (a.TF + g.KT - 1) * (a.TH + 2 * hsy) * (kTileW + 2 * hsx);
+    const int nhv = (a.TF + g.KT - 1) * (a.TH + 2 * hsy) * (a.TW + 2 * hsx);
     const int nt = conv_variant(a).nw * 64;
     const int ipt = (nhv * (bk / 8) + nt - 1) / nt;
     const int ntaps = g.KT * k2;
@@ -1684,8 +1688,10 @@ hipError_t launch_conv(const ConvArgs& a, hipStream_t stream) {
     if (v.mode == 2) return launch_persist_impl<256, 4, 2, PRO_RAW>(a, stream);
     if (v.mode == 3) return launch_persist_impl<256, 4, 3, PRO_RAW>(a, stream);
 #if WVD_WINO_W4
+    if (v.mode == 4 && a.TW == 8) return launch_persist_impl<256, 2, 4, PRO_RAW, 4, 8>(a, stream);
     if (v.mode == 4) return launch_persist_impl<256, 2, 4, PRO_RAW, 4>(a, stream);
 #endif
+    if (v.mode == 4 && a.TW == 8) return launch_persist_impl<256, 4, 4, PRO_RAW, 8, 8>(a, stream);
     if (v.mode == 4) return launch_persist_impl<256, 4, 4, PRO_RAW>(a, stream);
     if (v.bn == 32) return launch_persist_impl<32, 1, 1, PRO_RAW>(a, stream);
 #if WVD_MAIN_W4

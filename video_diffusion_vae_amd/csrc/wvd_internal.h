@@ -65,7 +65,7 @@ struct ConvArgs {
   ConvSeg seg[2];
   int nseg;
   int F, H, W;              // output voxel grid (input grid for phase mode)
-  int TF, TH;               // tile frames / rows
+  int TF, TH, TW;           // tile frames / rows / columns (TW = kTileW except the Winograd GEMM's 8)
   int tiles_x, tiles_y, tiles_f;
   int nphase;               // 4 for EPI_PHASE and EPI_WINO (xi), else 1
   int Cout;
