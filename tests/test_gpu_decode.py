@@ -80,3 +80,22 @@ def test_chunked_stream_decode_bit_identical(cfg_name, splits):
             assert got.shape == cfg.video_shape
             assert np.array_equal(got, whole), (chunks, P)
     check_close(got, ref, f"{cfg_name} chunked")
+
+
+# The full-width (c=256) network at a tiny latent size: every pass is smaller
+# than one 256-row GEMM tile (the shortcut GEMM takes its generic 1x1 path),
+# the Winograd planes hold a single column group, and attention has 6 tokens.
+EDGE_C256 = synth.Config("c256_T3_2x3", 256, 3, 2, 3, (1, 3))
+
+
+def test_full_width_tiny_latents_match_oracle():
+    cfg = EDGE_C256
+    ref = oracle_video(cfg, seed=0)
+    outs = []
+    for P in cfg.passes:
+        print(f"case {cfg.name} P={P}", flush=True)
+        outs.append(decode_gpu(cfg, seed=0, frames_per_pass=P))
+        check_close(outs[-1], ref, f"{cfg.name} P={P}")
+    assert np.array_equal(outs[0], outs[1])
+    print(f"case {cfg.name} chunks=[1, 2]", flush=True)
+    assert np.array_equal(decode_gpu_chunks(cfg, [1, 2], seed=0, frames_per_pass=1), outs[0])

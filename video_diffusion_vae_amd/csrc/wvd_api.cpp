@@ -560,12 +560,26 @@ Act resblock(Ctx& cx, const RB& rb, const Act& x, h16_t* hbuf, h16_t* obuf, int 
     // shortcut first (1x1 GEMM over the raw input, with the pre-summed
     // biases of conv2 and the shortcut), then conv2 adds onto it in place
     const long long Mv = (long long)x.F * x.H * x.W;
-    cx.what = "shortcut_gemm";
     cx.rs_tensor = nullptr;
-    cx.run(1, 2.0 * Mv * rb.cout * rb.cin, [&] {
-      return launch_gemm1x1(x.p, Mv, x.C, rb.cin, cx.prep<h16_t>(rb.scw), cx.wbytes(rb.scw), rb.cout,
-                            cx.prep<float>(rb.scb), out.p, out.C, cx.st);
-    });
+    if (Mv >= 256 && rb.cin % 128 == 0) {
+      cx.what = "shortcut_gemm";
+      cx.run(1, 2.0 * Mv * rb.cout * rb.cin, [&] {
+        return launch_gemm1x1(x.p, Mv, x.C, rb.cin, cx.prep<h16_t>(rb.scw), cx.wbytes(rb.scw), rb.cout,
+                              cx.prep<float>(rb.scb), out.p, out.C, cx.st);
+      });
+    } else {  // passes too small for a 256-row tile: the generic 1x1 conv
+      ConvArgs a = args_init();
+      a.seg[0] = seg_basic(x.p, x.fstride(), x.C, rb.cin, cx.prep<h16_t>(rb.scw), rb.cin, 0, 1, 1, cx.wbytes(rb.scw));
+      a.nseg = 1;
+      a.Cout = rb.cout;
+      a.bias = cx.prep<float>(rb.scb);
+      a.out = out.p;
+      a.out_fstride = out.fstride();
+      a.ldo = out.C;
+      a.epi = EPI_H16;
+      set_grid(a, x.F, x.H, x.W, 1);
+      conv(cx, a, 1);
+    }
     conv_wino(cx, h, r2, nh, rb.norm2, rb.conv2w, -1, rb.cout, out, out.p, out.fstride(), out.C);
   } else {
     ConvArgs a = conv333(cx, h, r2, nh, rb.norm2, rb.conv2w, rb.conv2b, rb.cout);

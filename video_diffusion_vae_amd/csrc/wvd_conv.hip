@@ -1478,49 +1478,89 @@ Variant conv_variant(const ConvArgs& a) {
 
 // ---------------------------------------------------------------------------
 // 1x1 convolution as a plain GEMM, out[m][n] = sum_k x[m][k] w[n][k] + bias[n]
-// (the shortcut of a width-changing block).  There is no spatial reuse to
-// stage, so both operands stream from L2 straight into MFMA fragment
-// registers: no LDS in the K loop and no barriers.  256 x 256 tiles on four
-// waves of 128 x 128 (accumulators in AGPRs); A and B fragments of k16 step
-// u live in ring slot u % kG1Depth and are refilled with step u + kG1Depth.
-constexpr int kG1Depth = 4;
+// (the shortcut of a width-changing block).  It streams its activations from
+// HBM once, so it is organised for that: one persistent workgroup per CU walks
+// 256 x 256 tiles in K chunks of kG1K channels.  Every thread issues all of a
+// chunk's loads (16 coalesced 16-byte pieces of A rows, 16 of fragment-order
+// weights) at the start of the previous chunk and commits them to LDS at its
+// end, so the only wait on memory is one per chunk, a whole chunk of MFMAs
+// after the loads were issued (a per-step register ring would make every
+// weight fetch wait, in order, behind the slower activation fetches).  Four
+// waves of 128 x 128 (accumulators in AGPRs, weights as the MFMA's first
+// operand) read their fragments from LDS one k16 step ahead.
+constexpr int kG1K = 128;               // K channels per chunk
+constexpr int kG1ARow = kG1K * 2 + 16;  // staged A row bytes (+16 pad: conflict-free fragment reads)
+constexpr int kG1Lds = 256 * kG1ARow + 256 * kG1K * 2;
 
 __global__ __launch_bounds__(256) void gemm1x1_kernel(const h16_t* __restrict__ x, long long M, int lda, int K,
                                                       const h16_t* __restrict__ w, int w_bytes, int N,
                                                       const float* __restrict__ bias, h16_t* __restrict__ out,
                                                       int ldo) {
-  constexpr int MI = 4, NJ = 4, D = kG1Depth;
-  __shared__ __align__(16) float ep_s[4 * 8 * (128 + 8)];
+  constexpr int MI = 4, NJ = 4, CS = kG1K / 16, PPR = kG1K * 2 / 16, IPT = 16;
+  static_assert(PPR == 16 && IPT == 16 && CS == 8, "16 A pieces (16 rows apart) and 16 B blocks per thread");
+  extern __shared__ __align__(16) unsigned char g1s[];
+  unsigned char* As = g1s;
+  unsigned char* Bs = g1s + 256 * kG1ARow;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the A descriptor lives in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int kpart = lane >> 5, lrow = lane & 31;
   const int nN = N / 256;
-  const long long bm = blockIdx.x / nN;
-  const int bn = blockIdx.x % nN;
-  const long long r0 = bm * 256 + wm * 128;  // first row of this wave
-  const int c0 = bn * 256 + wn * 128;        // first column of this wave
-  const long long rows_left = M - r0;
-  const int nrows = rows_left <= 0 ? 0 : (rows_left >= 128 ? 128 : (int)rows_left);
-  // rows past M read zeros (buffer range check), their outputs are skipped
-  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<h16_t*>(x + (nrows > 0 ? r0 : 0) * lda), 0, nrows * lda * 2, 0x00020000);
-  const __amdgpu_buffer_rsrc_t brsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<h16_t*>(w), 0, w_bytes, 0x00020000);
+  const long long nMt = (M + 255) / 256;
+  const TileSeq seq = tile_seq((int)(nMt * nN));
+  if (seq.at(0) < 0) return;
+  const int nch = K / kG1K;
   const int U = K / 16;
-  int aoff[MI], boff[NJ];
-#pragma unroll
-  for (int i = 0; i < MI; ++i) aoff[i] = ((32 * i + lrow) * lda + kpart * 8) * 2;
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) boff[j] = ((c0 / 32 + j) * U * 512 + lane * 8) * 2;
-  f16x8_t aq[D][MI], bq[D][NJ];
-  auto load_step = [&](int slot, int u) {
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-      aq[slot][i] = __builtin_bit_cast(f16x8_t, __builtin_amdgcn_raw_buffer_load_b128(arsrc, aoff[i], u * 32, 0));
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      bq[slot][j] = __builtin_bit_cast(f16x8_t, __builtin_amdgcn_raw_buffer_load_b128(brsrc, boff[j], u * 1024, 0));
+  const __amdgpu_buffer_rsrc_t brsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<h16_t*>(w), 0, w_bytes, 0x00020000);
+
+  // this thread's pieces: A row (tid / PPR) + 16 r, part tid % PPR; B block
+  // (tid + 256 r) / 64 = (32-column block nbl, k16 step s), lane (tid % 64)
+  uint4 sa[IPT], sb[IPT];
+  // Only the lane-dependent parts of the addresses live in VGPRs; the piece
+  // index r and the chunk go into the scalar offset.
+  const int avoff = ((tid / PPR) * lda + (tid % PPR) * 8) * 2;
+  const int bvoff = lane * 16;
+  // The last row tile is shifted back to end at row M (M >= 256), so every
+  // A read is in range; its rows that the previous tile also covers are
+  // recomputed with the same values.
+  auto tile_m0 = [&](int tile) {
+    const long long m0 = (long long)(tile / nN) * 256;
+    return m0 + 256 <= M ? m0 : M - 256;
   };
+  auto issue = [&](int tile, int ch) {
+    const long long m0 = tile_m0(tile);
+    const int bn = tile % nN;
+    const __amdgpu_buffer_rsrc_t arsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<h16_t*>(x + m0 * lda), 0, 256 * lda * 2, 0x00020000);
+#pragma unroll
+    for (int r = 0; r < IPT; ++r)
+      sa[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            arsrc, avoff, (16 * r * lda + ch * kG1K) * 2, 0));
+#pragma unroll
+    for (int r = 0; r < IPT; ++r) {
+      // block (wave + 4r): 32-column block r / 2, k16 step wave + 4 (r % 2)
+      const int nb = bn * 8 + r / 2, u = ch * CS + wave + 4 * (r % 2);
+      sb[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(brsrc, bvoff, (nb * U + u) * 1024, 0));
+    }
+  };
+  const int aloff = (tid / PPR) * kG1ARow + (tid % PPR) * 16;
+  const int bloff = wave * 1024 + lane * 16;
+  auto commit = [&]() {
+#pragma unroll
+    for (int r = 0; r < IPT; ++r) {
+      *reinterpret_cast<uint4*>(As + aloff + 16 * r * kG1ARow) = sa[r];
+      *reinterpret_cast<uint4*>(Bs + bloff + r * 4096) = sb[r];
+    }
+  };
+  int abase[MI], bbase[NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) abase[i] = (wm * 128 + 32 * i + lrow) * kG1ARow + kpart * 16;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) bbase[j] = (wn * 4 + j) * CS * 1024 + lane * 16;
+
+  issue(seq.at(0), 0);
+  commit();
+  __syncthreads();
   f32x16_t acc[MI][NJ];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
@@ -1528,56 +1568,107 @@ __global__ __launch_bounds__(256) void gemm1x1_kernel(const h16_t* __restrict__ 
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-#pragma unroll
-  for (int s = 0; s < D; ++s) {
-    load_step(s, s);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  for (int u0 = 0; u0 < U; u0 += D) {
-#pragma unroll
-    for (int s = 0; s < D; ++s) {
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aq[s][i], bq[s][j], acc[i][j], 0, 0, 0);
-      const int un = u0 + s + D;
-      load_step(s, un < U ? un : U - 1);  // past the end: reload the last step (no branch)
+
+  for (int k = 0;; ++k) {
+    const int cur = seq.at(k);
+    if (cur < 0) break;
+    const int nxt = seq.at(k + 1);
+    for (int ch = 0; ch < nch; ++ch) {
+      const bool last = ch + 1 == nch;
+      const bool more = !last || nxt >= 0;  // uniform
+      if (more) issue(last ? nxt : cur, last ? 0 : ch + 1);
       __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  // epilogue: 8-row quarters of each 32-row block through LDS, 16-byte stores
-  float* ep = ep_s + wave * 8 * (128 + 8);
-  const int er = lane >> 3, ec0 = (lane & 7) * 16;
-  float bv[16];
+      f16x8_t ap[2][MI], bp[2][NJ];
 #pragma unroll
-  for (int k4 = 0; k4 < 4; ++k4) {
-    const float4 b4 = bias ? *reinterpret_cast<const float4*>(bias + c0 + ec0 + 4 * k4) : make_float4(0, 0, 0, 0);
-    bv[4 * k4] = b4.x; bv[4 * k4 + 1] = b4.y; bv[4 * k4 + 2] = b4.z; bv[4 * k4 + 3] = b4.w;
-  }
+      for (int i = 0; i < MI; ++i) ap[0][i] = *reinterpret_cast<const f16x8_t*>(As + abase[i]);
 #pragma unroll
-  for (int i = 0; i < MI; ++i) {
+      for (int j = 0; j < NJ; ++j) bp[0][j] = *reinterpret_cast<const f16x8_t*>(Bs + bbase[j]);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+      for (int s = 0; s < CS; ++s) {
+        if (s + 1 < CS) {
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
+          for (int i = 0; i < MI; ++i)
+            ap[(s + 1) & 1][i] = *reinterpret_cast<const f16x8_t*>(As + abase[i] + (s + 1) * 32);
 #pragma unroll
-        for (int e = 4 * q; e < 4 * q + 4; ++e) ep[(4 * kpart + (e & 3)) * (128 + 8) + 32 * j + lrow] = acc[i][j][e];
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-      __builtin_amdgcn_wave_barrier();
-      const int rr = 32 * i + 8 * q + er;
-      if (rr < nrows) {
-        const float* row = ep + er * (128 + 8) + ec0;
-        h16_t* o = out + (r0 + rr) * ldo + c0 + ec0;
-#pragma unroll
-        for (int c8 = 0; c8 < 16; c8 += 8) {
-          float v[8];
-#pragma unroll
-          for (int k = 0; k < 8; ++k) v[k] = row[c8 + k] + bv[c8 + k];
-          *reinterpret_cast<uint4*>(o + c8) = pack8h(v);
+          for (int j = 0; j < NJ; ++j)
+            bp[(s + 1) & 1][j] = *reinterpret_cast<const f16x8_t*>(Bs + bbase[j] + (s + 1) * 1024);
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bp[s & 1][j], ap[s & 1][i], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_wave_barrier();
+      __syncthreads();  // every wave is done reading this chunk
+      if (last) {
+        // epilogue through the A region: lane (kpart, lrow) of block (i, j)
+        // holds row 32i + lrow of the wave's rows and channels
+        // 32j + 8g + 4*kpart + r (accumulator 4g + r); per 32 rows and 64
+        // channels the runs go straight from the accumulators into fp32 LDS
+        // rows, then eight channels per lane get the bias, fp16 and a
+        // 16-byte store.
+        constexpr int SROW = 64 * 4 + 16, LPR = 8, RPI = 8;
+        static_assert(4 * 32 * SROW <= 256 * kG1ARow, "staging fits in the A region");
+        unsigned char* st = As + wave * 32 * SROW;
+        const long long m0 = tile_m0(cur);
+        const int n0 = (cur % nN) * 256 + wn * 128;
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+#pragma unroll
+          for (int jh = 0; jh < NJ / 2; ++jh) {
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+              for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x16_t& c = acc[i][jh * 2 + jj];
+                f32x4_t v = {c[4 * g4], c[4 * g4 + 1], c[4 * g4 + 2], c[4 * g4 + 3]};
+                *reinterpret_cast<f32x4_t*>(st + lrow * SROW + (32 * jj + 8 * g4 + 4 * kpart) * 4) = v;
+              }
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the block is in LDS
+            __builtin_amdgcn_wave_barrier();
+            const int ncol = n0 + jh * 64 + (lane % LPR) * 8;
+            float bv[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) bv[q] = 0.0f;
+            if (bias) {
+              const f32x4_t b0 = *reinterpret_cast<const f32x4_t*>(bias + ncol);
+              const f32x4_t b1 = *reinterpret_cast<const f32x4_t*>(bias + ncol + 4);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                bv[q] = b0[q];
+                bv[4 + q] = b1[q];
+              }
+            }
+#pragma unroll
+            for (int rr = 0; rr < 32 / RPI; ++rr) {
+              const int r = rr * RPI + lane / LPR;
+              const float* row = reinterpret_cast<const float*>(st + r * SROW) + (lane % LPR) * 8;
+              const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(row);
+              const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(row + 4);
+              const long long m = m0 + wm * 128 + 32 * i + r;
+              {
+                const float v8[8] = {lo[0] + bv[0], lo[1] + bv[1], lo[2] + bv[2], lo[3] + bv[3],
+                                     hi[0] + bv[4], hi[1] + bv[5], hi[2] + bv[6], hi[3] + bv[7]};
+                *reinterpret_cast<uint4*>(out + m * ldo + ncol) = pack8h(v8);
+              }
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // this round's reads before the next round's writes
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+        __syncthreads();  // the staging rows are free again
+      }
+      if (more) commit();
+      __syncthreads();
     }
   }
 }
@@ -1587,13 +1678,25 @@ __global__ __launch_bounds__(256) void gemm1x1_kernel(const h16_t* __restrict__ 
 hipError_t launch_gemm1x1(const h16_t* x, long long M, int lda, int K, const h16_t* w, long long w_bytes, int N,
                           const float* bias, h16_t* out, int ldo, hipStream_t stream) {
   if (g_dry_run) return hipSuccess;
-  if (!x || !w || !out || M < 1 || N % 256 || K % (16 * kG1Depth) || lda % 8 || lda < K || ldo % 8 || ldo < N ||
-      w_bytes <= 0 || w_bytes > 0x7fffffffLL || (long long)128 * lda * 2 > 0x7fffffffLL)
+  if (!x || !w || !out || M < 256 || N % 256 || K % kG1K || K > 4096 || lda % 8 || lda < K || ldo % 8 || ldo < N ||
+      w_bytes <= 0 || w_bytes > 0x7fffffffLL || (long long)256 * lda * 2 > 0x7fffffffLL)
     return hipErrorInvalidValue;
   const long long tiles = (M + 255) / 256 * (N / 256);
   if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gemm1x1_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, x, M, lda, K, w, (int)w_bytes, N, bias,
-                     out, ldo);
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm1x1_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kG1Lds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  int dev = 0, ncu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const long long grid = tiles < ncu ? tiles : ncu;
+  hipLaunchKernelGGL(gemm1x1_kernel, dim3((unsigned)grid), dim3(256), kG1Lds, stream, x, M, lda, K, w, (int)w_bytes,
+                     N, bias, out, ldo);
   return hipGetLastError();
 }
 
