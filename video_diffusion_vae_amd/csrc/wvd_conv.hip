@@ -805,7 +805,7 @@ __device__ __forceinline__ TileSeq tile_seq(int total) {
   return s;
 }
 
-// Output tile of a logical tile index (same order as conv_igemm).
+// Output tile of a logical tile index.
 struct TileGeo {
   int f0, y0, x0, n0, ph;
 };
@@ -814,10 +814,14 @@ template <int BN, int MODE, int TW = kTileW>
 __device__ __forceinline__ TileGeo tile_geo(const ConvArgs& a, int logical) {
   constexpr int TF = MODE == 2 ? 1 : (MODE == 4 ? kTFWino : kTF333);
   constexpr int TH = MODE == 2 ? 16 : (MODE == 4 ? kTileM / TW / kTFWino : kTH333);
+  // Output positions vary fastest: the tiles running together on an XCD
+  // share one (phase, channel block) of weights in its L2 and neighbouring
+  // halos (interleaving the phases made them stream six weight sets).
   const int nN = (a.Cout + BN - 1) / BN;
-  const int nt = logical % nN;
-  const int ph = (logical / nN) % a.nphase;
-  const int mt = logical / (nN * a.nphase);
+  const int nMt = a.tiles_x * a.tiles_y * a.tiles_f;
+  const int mt = logical % nMt;
+  const int nt = (logical / nMt) % nN;
+  const int ph = logical / (nMt * nN);
   TileGeo t;
   t.x0 = (mt % a.tiles_x) * TW;
   t.y0 = ((mt / a.tiles_x) % a.tiles_y) * TH;
