@@ -451,10 +451,6 @@ int tf_for(int KT, int F) {
   return KT == 3 ? 2 : 1;
 }
 
-// Causal 3x3x3 norm-SiLU conv in Winograd form along x:
-//   U = F(kWinoM,3) input transform of SiLU(norm(x)) over the F frames and the
-//       valid history frames (rs from rms_stats for the same slots),
-//   M[xi] = causal (t, y) 3x3 conv of U[xi] with the transformed weights,
 // Tile width (column groups) of the Winograd-domain GEMM: 16 x 8 rows, or
 // 8 x 16 rows where that needs fewer rounds of tiles over the CUs (the small
 // levels, whose 20 or 39 column groups leave wide tiles mostly empty).
@@ -477,6 +473,10 @@ int wino_tile_w(int F, int H, int WQ, int Cout) {
   return rounds(8) < rounds(16) ? 8 : 16;
 }
 
+// Causal 3x3x3 norm-SiLU conv in Winograd form along x:
+//   U = F(kWinoM,3) input transform of SiLU(norm(x)) over the F frames and the
+//       valid history frames (the transform computes the norm statistics),
+//   M[xi] = causal (t, y) 3x3 conv of U[xi] with the transformed weights,
 //   out = output transform of M + bias (+ res).
 // Same function as conv333 + EPI_H16, with half of the multiply-adds (F(4,3)).
 void conv_wino(Ctx& cx, const Act& x, h16_t* ring, int nh, int gamma_item, int w_item, int b_item, int Cout,
@@ -489,8 +489,7 @@ void conv_wino(Ctx& cx, const Act& x, h16_t* ring, int nh, int gamma_item, int w
   const long long mframe = (long long)x.H * W2 * Cout;
   cx.what = "wino_in";
   cx.run(5, 0, [&] {
-    return launch_wino_in(x.p, x.fstride(), x.C, ring, nh, x.C, x.F, x.H, x.W, cx.wsp<float>(cx.W->rs),
-                          cx.prep<float>(gamma_item), U, cx.st);
+    return launch_wino_in(x.p, x.fstride(), x.C, ring, nh, x.C, x.F, x.H, x.W, cx.prep<float>(gamma_item), U, cx.st);
   });
   ConvArgs a = args_init();
   ConvSeg& g = a.seg[0];
@@ -538,7 +537,7 @@ ConvArgs conv333(Ctx& cx, const Act& x, h16_t* ring, int nh, int gamma_item, int
 Act resblock(Ctx& cx, const RB& rb, const Act& x, h16_t* hbuf, h16_t* obuf, int ring1, int ring2, int nh) {
   h16_t* r1 = cx.ring(ring1);
   h16_t* r2 = cx.ring(ring2);
-  stats(cx, x, r1, nh);
+  if (!rb.wino1) stats(cx, x, r1, nh);  // the Winograd input transform computes its own
   Act h{hbuf, rb.cout, x.F, x.H, x.W};
   if (rb.wino1) {
     conv_wino(cx, x, r1, nh, rb.norm1, rb.conv1w, rb.conv1b, rb.cout, h, nullptr, 0, 0);
@@ -552,7 +551,7 @@ Act resblock(Ctx& cx, const RB& rb, const Act& x, h16_t* hbuf, h16_t* obuf, int 
     conv(cx, a, 0);
   }
   ring_update(cx, r1, x);
-  stats(cx, h, r2, nh);
+  if (!rb.wino2) stats(cx, h, r2, nh);
   Act out{rb.cin == rb.cout ? x.p : obuf, rb.cout, x.F, x.H, x.W};
   if (rb.wino2 && rb.cin == rb.cout) {  // residual x, written in place
     conv_wino(cx, h, r2, nh, rb.norm2, rb.conv2w, rb.conv2b, rb.cout, out, x.p, x.fstride(), x.C);

@@ -390,81 +390,149 @@ __global__ void prep_wino_frag_kernel(const void* __restrict__ w, int dtype, int
   }
 }
 
-// Input transform: one thread per (slot, row, run of kWinoInRun column groups,
-// 8-channel group).
+// Sum of v over aligned groups of G lanes (G a power of two <= 64), the
+// same value, added in the same order, in every lane of a group: DPP steps
+// pair lanes within rows of 16 (xor 1, xor 2, then mirrored halves of 8 and
+// of 16), cross-lane permutes take the rows of 32 and 64.
+__device__ __forceinline__ float dpp_f32(float a, int ctrl) {
+  const int x = __builtin_bit_cast(int, a);
+  switch (ctrl) {
+    case 0: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));
+    case 1: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));
+    case 2: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false));
+    default: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false));
+  }
+}
+
+__device__ __forceinline__ float lane_group_sum(float v, int G) {
+  if (G >= 2) v += dpp_f32(v, 0);   // quad_perm [1,0,3,2]
+  if (G >= 4) v += dpp_f32(v, 1);   // quad_perm [2,3,0,1]
+  if (G >= 8) v += dpp_f32(v, 2);   // row_half_mirror
+  if (G >= 16) v += dpp_f32(v, 3);  // row_mirror
+  if (G >= 32) v += __shfl_xor(v, 16, 64);
+  if (G >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+// Input transform with its own norm statistics.  A group of G lanes (G the
+// largest power of two <= min(64, C / 8)) takes a run of kWinoInRun column
+// groups of one row of one slot; lane sub holds the 8-channel groups sub and
+// sub + G (when C / 8 > G).  Each column is loaded once: the lanes sum the
+// squares of their channels, a reduction over the G lanes gives the voxel's
+// 1/||x|| (the formula of rms_stats_kernel), and SiLU(x * rs *
+// gamma) of the column enters a six-column window that slides by four per
+// column group.  History slots (from the ring) and pass frames go through the
+// same code, so a voxel's activation does not depend on which pass holds it.
+template <int NG>  // 8-channel groups per lane: 1 (C <= 512) or 2
 __global__ __launch_bounds__(256) void wino_in_kernel(const h16_t* __restrict__ x, long long x_fstride, int lda,
                                                       const h16_t* __restrict__ ring, int first_slot, int C, int S,
-                                                      int H, int W, int WQ, const float* __restrict__ rs,
+                                                      int H, int W, int WQ, int G,
                                                       const float* __restrict__ gamma, h16_t* __restrict__ U) {
   constexpr int WM = kWinoM, NX = Wino<WM>::N, R = kWinoInRun;
+  const int lane = threadIdx.x & 63;
+  const int sub = lane % G;
   const int G8 = C >> 3;
-  const int QB = (WQ + R - 1) / R;  // runs of R column groups per row
+  const bool second = NG == 2 && sub + G < G8;  // this lane's second channel group exists
+  const int QB = (WQ + R - 1) / R;   // runs of R column groups per row
   const long long HW = (long long)H * W;
   const long long plane = (long long)S * H * WQ * C;  // elements per xi plane
-  const long long n = (long long)(S - first_slot) * H * QB * G8;
-  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n;
-       e += (long long)gridDim.x * blockDim.x) {
-    const int g = (int)(e % G8);
-    long long r = e / G8;
-    const int qb = (int)(r % QB);
-    r /= QB;
-    const int row = (int)(r % H);
-    const int slot = (int)(r / H) + first_slot;
-    float gm[8];
-    {
+  const long long nrun = (long long)(S - first_slot) * H * QB;
+  const int runs_per_wave = 64 / G;
+  const long long gw = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const long long nw = ((long long)gridDim.x * blockDim.x) >> 6;
+  float gm[NG][8];
+#pragma unroll
+  for (int h = 0; h < NG; ++h) {
+    const int g = sub + h * G;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) gm[h][c] = 0.0f;
+    if (h == 0 || second) {
       const float4 g0 = *reinterpret_cast<const float4*>(gamma + g * 8);
       const float4 g1 = *reinterpret_cast<const float4*>(gamma + g * 8 + 4);
-      gm[0] = g0.x; gm[1] = g0.y; gm[2] = g0.z; gm[3] = g0.w;
-      gm[4] = g1.x; gm[5] = g1.y; gm[6] = g1.z; gm[7] = g1.w;
+      gm[h][0] = g0.x; gm[h][1] = g0.y; gm[h][2] = g0.z; gm[h][3] = g0.w;
+      gm[h][4] = g1.x; gm[h][5] = g1.y; gm[h][6] = g1.z; gm[h][7] = g1.w;
     }
+  }
+  for (long long base = gw * runs_per_wave; base < nrun; base += nw * runs_per_wave) {
+    const long long e = base + lane / G;
+    const bool ok = e < nrun;  // whole lane groups agree
+    const long long ee = ok ? e : 0;
+    const int qb = (int)(ee % QB);
+    const long long r = ee / QB;
+    const int row = (int)(r % H);
+    const int slot = (int)(r / H) + first_slot;
     const h16_t* src_row = slot < 2 ? ring + ((long long)slot * HW + (long long)row * W) * C
                                     : x + (slot - 2) * x_fstride + (long long)row * W * lda;
     const long long ld = slot < 2 ? C : lda;
-    const float* rs_row = rs + (long long)slot * HW + (long long)row * W;
-    // SiLU(x * rs * gamma) of column `col` (zero outside the row)
-    auto act = [&](int col, float* y) {
+    // SiLU(x * rs * gamma) of column `col` for this lane's channels (zero
+    // outside the row); every lane of the group runs it (butterfly)
+    auto act = [&](int col, float (&y)[NG][8]) {
+      const bool in = ok && col >= 0 && col < W;
+      uint4 v[NG];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) y[c] = 0.0f;
-      if (col >= 0 && col < W) {
-        float f[8];
-        unpack8h(*reinterpret_cast<const uint4*>(src_row + col * ld + g * 8), f);
-        const float sc = rs_row[col];
+      for (int h = 0; h < NG; ++h) v[h] = make_uint4(0, 0, 0, 0);
+      if (in) {
+        const h16_t* p = src_row + (long long)col * ld;
+        v[0] = *reinterpret_cast<const uint4*>(p + sub * 8);
+        if (second) v[NG - 1] = *reinterpret_cast<const uint4*>(p + (sub + G) * 8);
+      }
+      float f[NG][8];
+#pragma unroll
+      for (int h = 0; h < NG; ++h) unpack8h(v[h], f[h]);
+      float ss = 0.0f;
+#pragma unroll
+      for (int h = 0; h < NG; ++h) {
+        float t = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) t += f[h][k] * f[h][k];
+        ss += t;
+      }
+      ss = lane_group_sum(ss, G);
+      const float sc = 1.0f / fmaxf(sqrtf(ss), kNormEps);
+#pragma unroll
+      for (int h = 0; h < NG; ++h)
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          const float t = f[c] * sc * gm[c];
-          y[c] = t * __builtin_amdgcn_rcpf(1.0f + __expf(-t));
+          const float t = f[h][c] * sc * gm[h][c];
+          y[h][c] = in ? t * __builtin_amdgcn_rcpf(1.0f + __expf(-t)) : 0.0f;
         }
-      }
     };
-    // A run of R neighbouring column groups slides a six-column window by
-    // four: each activated column is computed once (groups share two).
-    float y[NX][8];
+    float y[NX][NG][8];
     const int q0 = qb * R;
 #pragma unroll
     for (int k = 0; k < NX - WM; ++k) act(WM * q0 - 1 + k, y[k]);
-    h16_t* dst = U + ((long long)slot * H * WQ + (long long)row * WQ + q0) * C + g * 8;
+    h16_t* dst = U + ((long long)slot * H * WQ + (long long)row * WQ + q0) * C;
 #pragma unroll
     for (int qq = 0; qq < R; ++qq) {
-      if (q0 + qq >= WQ) break;
+      if (q0 + qq >= WQ) break;  // uniform over the lane group
 #pragma unroll
       for (int k = NX - WM; k < NX; ++k) act(WM * (q0 + qq) - 1 + k, y[k]);
-      float u[NX][8];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        float d[NX], uu[NX];
+      for (int h = 0; h < NG; ++h) {
+        if (h == 1 && !second) break;
+        float u[NX][8];
 #pragma unroll
-        for (int k = 0; k < NX; ++k) d[k] = y[k][c];
-        Wino<WM>::input(d, uu);
+        for (int c = 0; c < 8; ++c) {
+          float d[NX], uu[NX];
 #pragma unroll
-        for (int k = 0; k < NX; ++k) u[k][c] = uu[k];
+          for (int k = 0; k < NX; ++k) d[k] = y[k][h][c];
+          Wino<WM>::input(d, uu);
+#pragma unroll
+          for (int k = 0; k < NX; ++k) u[k][c] = uu[k];
+        }
+        if (ok) {
+#pragma unroll
+          for (int k = 0; k < NX; ++k)
+            *reinterpret_cast<uint4*>(dst + qq * C + (sub + h * G) * 8 + k * plane) = pack8h(u[k]);
+        }
       }
-#pragma unroll
-      for (int k = 0; k < NX; ++k) *reinterpret_cast<uint4*>(dst + qq * C + k * plane) = pack8h(u[k]);
       // the last two columns of this window open the next one
 #pragma unroll
       for (int k = 0; k < NX - WM; ++k)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) y[k][c] = y[WM + k][c];
+        for (int h = 0; h < NG; ++h)
+#pragma unroll
+          for (int c = 0; c < 8; ++c) y[k][h][c] = y[WM + k][h][c];
     }
   }
 }
@@ -680,13 +748,20 @@ hipError_t launch_prep_wino_frag(const void* w, int dtype, int cout, int cin, h1
 }
 
 hipError_t launch_wino_in(const h16_t* x, long long x_fstride, int lda, const h16_t* ring, int n_hist, int C, int F,
-                          int H, int W, const float* rs, const float* gamma, h16_t* U, hipStream_t s) {
+                          int H, int W, const float* gamma, h16_t* U, hipStream_t s) {
   if (g_dry_run) return hipSuccess;
-  if (C % 8 || n_hist < 0 || n_hist > 2 || (n_hist > 0 && !ring) || F < 1) return hipErrorInvalidValue;
+  if (C % 8 || C > 1024 || n_hist < 0 || n_hist > 2 || (n_hist > 0 && !ring) || F < 1) return hipErrorInvalidValue;
   const int WQ = (W + kWinoM - 1) / kWinoM;
-  const long long n = (long long)(F + n_hist) * H * ((WQ + kWinoInRun - 1) / kWinoInRun) * (C / 8);
-  hipLaunchKernelGGL(wino_in_kernel, dim3(grid_for(n, 256, 65536)), dim3(256), 0, s, x, x_fstride, lda, ring,
-                     2 - n_hist, C, F + 2, H, W, WQ, rs, gamma, U);
+  int G = 1;
+  while (G * 2 <= (C >> 3) && G * 2 <= 64) G *= 2;
+  const long long runs = (long long)(F + n_hist) * H * ((WQ + kWinoInRun - 1) / kWinoInRun);
+  const long long threads = (runs + 64 / G - 1) / (64 / G) * 64;
+  if (C / 8 > G)
+    hipLaunchKernelGGL(wino_in_kernel<2>, dim3(grid_for(threads, 256, 65536)), dim3(256), 0, s, x, x_fstride, lda,
+                       ring, 2 - n_hist, C, F + 2, H, W, WQ, G, gamma, U);
+  else
+    hipLaunchKernelGGL(wino_in_kernel<1>, dim3(grid_for(threads, 256, 65536)), dim3(256), 0, s, x, x_fstride, lda,
+                       ring, 2 - n_hist, C, F + 2, H, W, WQ, G, gamma, U);
   return hipGetLastError();
 }
 
