@@ -46,6 +46,9 @@
 #ifndef WVD_ILV
 #define WVD_ILV 1
 #endif
+#ifndef WVD_PHASE_W4
+#define WVD_PHASE_W4 0  // 1: up-conv phases on 4 waves of 128 x 128 (measured no faster than 8)
+#endif
 #ifndef WVD_WINO_LAG
 #define WVD_WINO_LAG 3  // Winograd GEMM: taps between a halo item's load and its LDS store
 #endif
@@ -65,6 +68,7 @@ constexpr int kHY333 = kTH333 + 2;
 constexpr int kHF333 = kTF333 + 2;
 constexpr int kNHV333 = kHF333 * kHY333 * kHX;  // 720 halo voxels
 constexpr int kBRing = WVD_BRING;              // k16 steps of B fragments in flight
+constexpr int kPhaseBRing = WVD_PHASE_W4 ? 2 : 4;  // the same for the up-conv phase loop
 // Tile of the Winograd-domain GEMM: 2 frames x 8 rows x 16 column groups
 // (halo 4 x 10 x 16 rows; a 4 x 4 x 16 tile has fewer halo rows but measured slower).
 constexpr int kTFWino = kWinoTF;
@@ -971,7 +975,7 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
     const SegCtx<BK, MI, NJ, NT> g = ctx_for(seq.at(0), 0);
     for (int idx = tid; idx < nhv_max * NP; idx += NT)
       halo_store<NORM, ACT>(g, idx, 0, halo_load(g, idx, 0), smem);
-    constexpr int PRE = K333 || WINO ? kBRing : (KT3 ? 3 : 4);
+    constexpr int PRE = K333 || WINO ? kBRing : (KT3 ? 3 : kPhaseBRing);
 #pragma unroll
     for (int u = 0; u < PRE; ++u) {
       load_step(g, bq[u], 0, u >> 1, u & 1);
@@ -1177,30 +1181,61 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
       } else {
+        // four 2x2 taps x two k16 steps; halo items are loaded LPS per step
+        // over the first NLS steps and stored LAG steps later; with APF (4
+        // waves) A fragments run one step ahead
         constexpr int IPT = ((1 * 18 * 18) * NP + NT - 1) / NT;
-        constexpr int LAG = 8 - IPT;
-        static_assert(IPT >= 1 && IPT <= 7, "phase halo items per chunk");
+        constexpr int PD = kPhaseBRing;  // B fragments of step u in slot u % PD, refilled with step u + PD
+        constexpr int LPS = APF ? 2 : 1;
+        constexpr int NLS = (IPT + LPS - 1) / LPS;
+        constexpr int LAG = 8 - NLS;
+        static_assert(NLS >= 1 && LAG >= 3, "phase halo items land inside a chunk");
         const int py = geo.ph >> 1, px = geo.ph & 1;
+        auto toff = [&](int u) {
+          const int tap = u >> 1;
+          return ((py + (tap >> 1)) * HX + (px + (tap & 1))) * ROWB + (u & 1) * 32;
+        };
         uint4 hr[IPT];
+        f16x8_t ap[2][MI];
+        if constexpr (APF) {
+          const int o0 = toff(0);
+#pragma unroll
+          for (int i = 0; i < MI; ++i) ap[0][i] = *reinterpret_cast<const f16x8_t*>(hsrc + g.abase[i] + o0);
+        }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int tap = u >> 1, ks = u & 1;
-          if (u >= LAG && u - LAG < IPT) halo_store<false, false>(gn, tid + NT * (u - LAG), cn, hr[u - LAG], hdst);
-          if (u < IPT) hr[u] = halo_load(gn, tid + NT * u, cn);
-          const int toff = ((py + (tap >> 1)) * HX + (px + (tap & 1))) * ROWB;
+          const int ks = u & 1;
           f16x8_t av[MI];
+          if constexpr (APF) {
+            if (u + 1 < 8) {
+              const int o1 = toff(u + 1);
 #pragma unroll
-          for (int i = 0; i < MI; ++i)
-            av[i] = *reinterpret_cast<const f16x8_t*>(hsrc + g.abase[i] + toff + ks * 32);
+              for (int i = 0; i < MI; ++i)
+                ap[(u + 1) & 1][i] = *reinterpret_cast<const f16x8_t*>(hsrc + g.abase[i] + o1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < MI; ++i) av[i] = ap[u & 1][i];
+          } else {
+            const int o = toff(u);
+#pragma unroll
+            for (int i = 0; i < MI; ++i) av[i] = *reinterpret_cast<const f16x8_t*>(hsrc + g.abase[i] + o);
+          }
+#pragma unroll
+          for (int q = 0; q < LPS; ++q) {
+            const int is = (u - LAG) * LPS + q, il = u * LPS + q;
+            if (u >= LAG && is < IPT) halo_store<false, false>(gn, tid + NT * is, cn, hr[is], hdst);
+            if (u < NLS && il < IPT) hr[il] = halo_load(gn, tid + NT * il, cn);
+          }
 #pragma unroll
           for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bq[u & 3][j], av[i], acc[i][j], 0, 0, 0);  // swapped, as below
-          if (u + 4 < 8)
-            load_step(g, bq[u & 3], c, (u + 4) >> 1, ks);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bq[u % PD][j], av[i], acc[i][j], 0, 0, 0);  // swapped, as below
+          if (u + PD < 8)
+            load_step(g, bq[u % PD], c, (u + PD) >> 1, (u + PD) & 1);
           else
-            load_step(gn, bq[u & 3], cn, (u + 4 - 8) >> 1, ks);
+            load_step(gn, bq[u % PD], cn, (u + PD - 8) >> 1, (u + PD) & 1);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -1792,6 +1827,9 @@ hipError_t launch_conv(const ConvArgs& a, hipStream_t stream) {
   const Variant v = conv_variant(a);
   if (conv_persistent(a)) {
     const int pro = a.seg[0].prologue;
+#if WVD_PHASE_W4
+    if (v.mode == 2) return launch_persist_impl<256, 2, 2, PRO_RAW, 4>(a, stream);
+#endif
     if (v.mode == 2) return launch_persist_impl<256, 4, 2, PRO_RAW>(a, stream);
     if (v.mode == 3) return launch_persist_impl<256, 4, 3, PRO_RAW>(a, stream);
 #if WVD_WINO_W4
