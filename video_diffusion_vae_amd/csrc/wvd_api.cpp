@@ -479,18 +479,15 @@ int wino_tile_w(int F, int H, int WQ, int Cout) {
 //   M[xi] = causal (t, y) 3x3 conv of U[xi] with the transformed weights,
 //   out = output transform of M + bias (+ res).
 // Same function as conv333 + EPI_H16, with half of the multiply-adds (F(4,3)).
-void conv_wino(Ctx& cx, const Act& x, h16_t* ring, int nh, int gamma_item, int w_item, int b_item, int Cout,
-               const Act& out, const h16_t* res, long long res_fstride, int ldr) {
+// The Winograd GEMM over the U planes the input transform (or the fused
+// transform) left for input x: M = the six planes of products.
+void wino_gemm(Ctx& cx, const Act& x, int nh, int w_item, int Cout) {
   const int W2 = (x.W + kWinoM - 1) / kWinoM;  // column groups
   h16_t* U = cx.wsp<h16_t>(cx.W->U);
   h16_t* M = cx.wsp<h16_t>(cx.W->M);
-  const long long uslot = (long long)x.H * W2 * x.C;         // elements per U frame
-  const long long uplane = (long long)(x.F + 2) * uslot;      // per xi plane
+  const long long uslot = (long long)x.H * W2 * x.C;     // elements per U frame
+  const long long uplane = (long long)(x.F + 2) * uslot;  // per xi plane
   const long long mframe = (long long)x.H * W2 * Cout;
-  cx.what = "wino_in";
-  cx.run(5, 0, [&] {
-    return launch_wino_in(x.p, x.fstride(), x.C, ring, nh, x.C, x.F, x.H, x.W, cx.prep<float>(gamma_item), U, cx.st);
-  });
   ConvArgs a = args_init();
   ConvSeg& g = a.seg[0];
   g = seg_basic(U + 2 * uslot, uslot, x.C, x.C, cx.prep<h16_t>(w_item), x.C, 0, 3, KS_3x1, cx.wbytes(w_item));
@@ -507,13 +504,28 @@ void conv_wino(Ctx& cx, const Act& x, h16_t* ring, int nh, int gamma_item, int w
   a.epi = EPI_WINO;
   set_grid(a, x.F, x.H, W2, kWinoTF, wino_tile_w(x.F, x.H, W2, Cout));
   conv(cx, a, 0);
+}
+
+void wino_out(Ctx& cx, const Act& x, int b_item, int Cout, const Act& out, const h16_t* res, long long res_fstride,
+              int ldr) {
   cx.what = "wino_out";
   cx.run(5, 0, [&] {
-    return launch_wino_out(M, Cout, x.F, x.H, x.W, b_item >= 0 ? cx.prep<float>(b_item) : nullptr, res, res_fstride,
-                           ldr, out.p, out.fstride(), out.C, cx.wsp<float>(cx.W->rs), cx.st);
+    return launch_wino_out(cx.wsp<h16_t>(cx.W->M), Cout, x.F, x.H, x.W, b_item >= 0 ? cx.prep<float>(b_item) : nullptr,
+                           res, res_fstride, ldr, out.p, out.fstride(), out.C, cx.wsp<float>(cx.W->rs), cx.st);
   });
   cx.rs_tensor = out.p;
   cx.rs_frames = x.F;
+}
+
+void conv_wino(Ctx& cx, const Act& x, h16_t* ring, int nh, int gamma_item, int w_item, int b_item, int Cout,
+               const Act& out, const h16_t* res, long long res_fstride, int ldr) {
+  cx.what = "wino_in";
+  cx.run(5, 0, [&] {
+    return launch_wino_in(x.p, x.fstride(), x.C, ring, nh, x.C, x.F, x.H, x.W, cx.prep<float>(gamma_item),
+                          cx.wsp<h16_t>(cx.W->U), cx.st);
+  });
+  wino_gemm(cx, x, nh, w_item, Cout);
+  wino_out(cx, x, b_item, Cout, out, res, res_fstride, ldr);
 }
 
 // Causal 3x3x3 conv with the fused RMSNorm+SiLU prologue.
@@ -539,7 +551,29 @@ Act resblock(Ctx& cx, const RB& rb, const Act& x, h16_t* hbuf, h16_t* obuf, int 
   h16_t* r2 = cx.ring(ring2);
   if (!rb.wino1) stats(cx, x, r1, nh);  // the Winograd input transform computes its own
   Act h{hbuf, rb.cout, x.F, x.H, x.W};
-  if (rb.wino1) {
+  const bool fused = rb.wino1 && rb.wino2 && wino_mid_ok(rb.cout);
+  if (fused) {
+    // conv1's products go straight into conv2's input planes: h is stored
+    // only for the frames the next pass reads as history (its ring)
+    cx.what = "wino_in";
+    cx.run(5, 0, [&] {
+      return launch_wino_in(x.p, x.fstride(), x.C, r1, nh, x.C, x.F, x.H, x.W, cx.prep<float>(rb.norm1),
+                            cx.wsp<h16_t>(cx.W->U), cx.st);
+    });
+    wino_gemm(cx, x, nh, rb.conv1w, rb.cout);
+    cx.what = "wino_in_history";
+    cx.run(5, 0, [&] {
+      return launch_wino_in(h.p, h.fstride(), h.C, r2, nh, h.C, h.F, h.H, h.W, cx.prep<float>(rb.norm2),
+                            cx.wsp<h16_t>(cx.W->U), cx.st, true);
+    });
+    cx.what = "wino_mid";
+    cx.run(5, 0, [&] {
+      return launch_wino_mid(cx.wsp<h16_t>(cx.W->M), cx.prep<float>(rb.conv1b), rb.cout, x.F, x.H, x.W,
+                             cx.prep<float>(rb.norm2), cx.wsp<h16_t>(cx.W->U), h.p, h.fstride(), h.C,
+                             std::max(0, x.F - 2), cx.st);
+    });
+    cx.rs_tensor = nullptr;
+  } else if (rb.wino1) {
     conv_wino(cx, x, r1, nh, rb.norm1, rb.conv1w, rb.conv1b, rb.cout, h, nullptr, 0, 0);
   } else {
     ConvArgs a = conv333(cx, x, r1, nh, rb.norm1, rb.conv1w, rb.conv1b, rb.cout);
@@ -553,8 +587,17 @@ Act resblock(Ctx& cx, const RB& rb, const Act& x, h16_t* hbuf, h16_t* obuf, int 
   ring_update(cx, r1, x);
   if (!rb.wino2) stats(cx, h, r2, nh);
   Act out{rb.cin == rb.cout ? x.p : obuf, rb.cout, x.F, x.H, x.W};
+  // conv2: input planes from its own transform, or already there (fused)
+  auto conv2_wino = [&](int b_item, const h16_t* res, long long res_fstride, int ldr) {
+    if (fused) {
+      wino_gemm(cx, h, nh, rb.conv2w, rb.cout);
+      wino_out(cx, h, b_item, rb.cout, out, res, res_fstride, ldr);
+    } else {
+      conv_wino(cx, h, r2, nh, rb.norm2, rb.conv2w, b_item, rb.cout, out, res, res_fstride, ldr);
+    }
+  };
   if (rb.wino2 && rb.cin == rb.cout) {  // residual x, written in place
-    conv_wino(cx, h, r2, nh, rb.norm2, rb.conv2w, rb.conv2b, rb.cout, out, x.p, x.fstride(), x.C);
+    conv2_wino(rb.conv2b, x.p, x.fstride(), x.C);
   } else if (rb.wino2) {
     // shortcut first (1x1 GEMM over the raw input, with the pre-summed
     // biases of conv2 and the shortcut), then conv2 adds onto it in place
@@ -579,7 +622,7 @@ Act resblock(Ctx& cx, const RB& rb, const Act& x, h16_t* hbuf, h16_t* obuf, int 
       set_grid(a, x.F, x.H, x.W, 1);
       conv(cx, a, 1);
     }
-    conv_wino(cx, h, r2, nh, rb.norm2, rb.conv2w, -1, rb.cout, out, out.p, out.fstride(), out.C);
+    conv2_wino(-1, out.p, out.fstride(), out.C);
   } else {
     ConvArgs a = conv333(cx, h, r2, nh, rb.norm2, rb.conv2w, rb.conv2b, rb.cout);
     if (rb.cin == rb.cout) {

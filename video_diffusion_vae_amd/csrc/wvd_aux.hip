@@ -414,6 +414,35 @@ __device__ __forceinline__ float lane_group_sum(float v, int G) {
   return v;
 }
 
+// SiLU(v * rs * gamma) of one column from its fp16 channel values (this
+// lane's NG 8-channel groups), with rs = 1 / ||v|| over the column's C
+// channels (a sum over the G lanes of the group); zero where !in.  The
+// Winograd input transforms take every activation through this function.
+template <int NG>
+__device__ __forceinline__ void act_column(const uint4 (&v)[NG], bool in, int G, const float (&gm)[NG][8],
+                                           float (&y)[NG][8]) {
+  float f[NG][8];
+#pragma unroll
+  for (int h = 0; h < NG; ++h) unpack8h(v[h], f[h]);
+  float ss = 0.0f;
+#pragma unroll
+  for (int h = 0; h < NG; ++h) {
+    float t = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) t += f[h][k] * f[h][k];
+    ss += t;
+  }
+  ss = lane_group_sum(ss, G);
+  const float sc = 1.0f / fmaxf(sqrtf(ss), kNormEps);
+#pragma unroll
+  for (int h = 0; h < NG; ++h)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float t = f[h][c] * sc * gm[h][c];
+      y[h][c] = in ? t * __builtin_amdgcn_rcpf(1.0f + __expf(-t)) : 0.0f;
+    }
+}
+
 // Input transform with its own norm statistics.  A group of G lanes (G the
 // largest power of two <= min(64, C / 8)) takes a run of kWinoInRun column
 // groups of one row of one slot; lane sub holds the 8-channel groups sub and
@@ -425,8 +454,8 @@ __device__ __forceinline__ float lane_group_sum(float v, int G) {
 // same code, so a voxel's activation does not depend on which pass holds it.
 template <int NG>  // 8-channel groups per lane: 1 (C <= 512) or 2
 __global__ __launch_bounds__(256) void wino_in_kernel(const h16_t* __restrict__ x, long long x_fstride, int lda,
-                                                      const h16_t* __restrict__ ring, int first_slot, int C, int S,
-                                                      int H, int W, int WQ, int G,
+                                                      const h16_t* __restrict__ ring, int first_slot, int slot_end,
+                                                      int C, int S, int H, int W, int WQ, int G,
                                                       const float* __restrict__ gamma, h16_t* __restrict__ U) {
   constexpr int WM = kWinoM, NX = Wino<WM>::N, R = kWinoInRun;
   const int lane = threadIdx.x & 63;
@@ -436,7 +465,7 @@ __global__ __launch_bounds__(256) void wino_in_kernel(const h16_t* __restrict__ 
   const int QB = (WQ + R - 1) / R;   // runs of R column groups per row
   const long long HW = (long long)H * W;
   const long long plane = (long long)S * H * WQ * C;  // elements per xi plane
-  const long long nrun = (long long)(S - first_slot) * H * QB;
+  const long long nrun = (long long)(slot_end - first_slot) * H * QB;
   const int runs_per_wave = 64 / G;
   const long long gw = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const long long nw = ((long long)gridDim.x * blockDim.x) >> 6;
@@ -476,26 +505,7 @@ __global__ __launch_bounds__(256) void wino_in_kernel(const h16_t* __restrict__ 
         v[0] = *reinterpret_cast<const uint4*>(p + sub * 8);
         if (second) v[NG - 1] = *reinterpret_cast<const uint4*>(p + (sub + G) * 8);
       }
-      float f[NG][8];
-#pragma unroll
-      for (int h = 0; h < NG; ++h) unpack8h(v[h], f[h]);
-      float ss = 0.0f;
-#pragma unroll
-      for (int h = 0; h < NG; ++h) {
-        float t = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) t += f[h][k] * f[h][k];
-        ss += t;
-      }
-      ss = lane_group_sum(ss, G);
-      const float sc = 1.0f / fmaxf(sqrtf(ss), kNormEps);
-#pragma unroll
-      for (int h = 0; h < NG; ++h)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const float t = f[h][c] * sc * gm[h][c];
-          y[h][c] = in ? t * __builtin_amdgcn_rcpf(1.0f + __expf(-t)) : 0.0f;
-        }
+      act_column<NG>(v, in, G, gm, y);
     };
     float y[NX][NG][8];
     const int q0 = qb * R;
@@ -533,6 +543,167 @@ __global__ __launch_bounds__(256) void wino_in_kernel(const h16_t* __restrict__ 
         for (int h = 0; h < NG; ++h)
 #pragma unroll
           for (int c = 0; c < 8; ++c) y[k][h][c] = y[WM + k][h][c];
+    }
+  }
+}
+
+// Output transform of one conv fused with the input transform of the next
+// (conv1 -> conv2 of a ResBlock): from the six planes of conv1's products,
+// a run of kWinoInRun column groups gets h = A^T M + bias rounded to fp16
+// (exactly the values the unfused path would store), each column is
+// activated once through act_column, and the six-column window of conv2's
+// input transform slides over them.  The window's outer columns come from
+// the neighbouring groups (the last column of group q0 - 1, the first of
+// q0 + R), so a run reads R + 2 groups of products.  h itself is written only
+// for frames >= tail_from (the frames the next pass reads as history).
+template <int NG>
+__global__ __launch_bounds__(256) void wino_mid_kernel(const h16_t* __restrict__ M, const float* __restrict__ bias,
+                                                       int C, int F, int H, int W, int WQ, int G,
+                                                       const float* __restrict__ gamma, h16_t* __restrict__ U,
+                                                       h16_t* __restrict__ hout, long long h_fstride, int ldh,
+                                                       int tail_from) {
+  constexpr int WM = kWinoM, NX = Wino<WM>::N, R = kWinoInRun;
+  const int lane = threadIdx.x & 63;
+  const int sub = lane % G;
+  const int G8 = C >> 3;
+  const bool second = NG == 2 && sub + G < G8;
+  const int QB = (WQ + R - 1) / R;
+  const long long mplane = (long long)F * H * WQ * C;        // conv1 product planes
+  const long long uplane = (long long)(F + 2) * H * WQ * C;  // conv2 input planes (two history slots first)
+  const long long nrun = (long long)F * H * QB;
+  const int runs_per_wave = 64 / G;
+  const long long gw = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const long long nw = ((long long)gridDim.x * blockDim.x) >> 6;
+  float gm[NG][8], bv[NG][8];
+#pragma unroll
+  for (int h = 0; h < NG; ++h) {
+    const int g = sub + h * G;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) gm[h][c] = bv[h][c] = 0.0f;
+    if (h == 0 || second) {
+      const float4 g0 = *reinterpret_cast<const float4*>(gamma + g * 8);
+      const float4 g1 = *reinterpret_cast<const float4*>(gamma + g * 8 + 4);
+      gm[h][0] = g0.x; gm[h][1] = g0.y; gm[h][2] = g0.z; gm[h][3] = g0.w;
+      gm[h][4] = g1.x; gm[h][5] = g1.y; gm[h][6] = g1.z; gm[h][7] = g1.w;
+      if (bias) {
+        const float4 b0 = *reinterpret_cast<const float4*>(bias + g * 8);
+        const float4 b1 = *reinterpret_cast<const float4*>(bias + g * 8 + 4);
+        bv[h][0] = b0.x; bv[h][1] = b0.y; bv[h][2] = b0.z; bv[h][3] = b0.w;
+        bv[h][4] = b1.x; bv[h][5] = b1.y; bv[h][6] = b1.z; bv[h][7] = b1.w;
+      }
+    }
+  }
+  for (long long base = gw * runs_per_wave; base < nrun; base += nw * runs_per_wave) {
+    const long long e = base + lane / G;
+    const bool ok = e < nrun;
+    const long long ee = ok ? e : 0;
+    const int qb = (int)(ee % QB);
+    const long long r = ee / QB;
+    const int row = (int)(r % H);
+    const int f = (int)(r / H);
+    // h (fp16, as stored) of the four columns of group q; zero outside
+    auto group = [&](int q, uint4 (&hv)[WM][NG]) {
+      const bool valid = ok && q >= 0 && q < WQ;
+      uint4 mr[NX][NG];
+#pragma unroll
+      for (int k = 0; k < NX; ++k)
+#pragma unroll
+        for (int h = 0; h < NG; ++h) {
+          mr[k][h] = make_uint4(0, 0, 0, 0);
+          if (valid && (h == 0 || second))
+            mr[k][h] = *reinterpret_cast<const uint4*>(M + k * mplane + (((long long)f * H + row) * WQ + q) * C +
+                                                       (sub + h * G) * 8);
+        }
+#pragma unroll
+      for (int h = 0; h < NG; ++h) {
+        float m[NX][8];
+#pragma unroll
+        for (int k = 0; k < NX; ++k) unpack8h(mr[k][h], m[k]);
+        float o[WM][8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          float mm[NX], oo[WM];
+#pragma unroll
+          for (int k = 0; k < NX; ++k) mm[k] = m[k][c];
+          Wino<WM>::output(mm, oo);
+#pragma unroll
+          for (int e2 = 0; e2 < WM; ++e2) o[e2][c] = oo[e2];
+        }
+#pragma unroll
+        for (int e2 = 0; e2 < WM; ++e2) {
+          float v[8];
+#pragma unroll
+          for (int c = 0; c < 8; ++c) v[c] = o[e2][c] + bv[h][c];
+          hv[e2][h] = (valid && WM * q + e2 < W) ? pack8h(v) : make_uint4(0, 0, 0, 0);
+        }
+      }
+    };
+    const int q0 = qb * R;
+    float y[NX][NG][8];
+    float yn[NG][8];  // activation of the next group's first column
+    uint4 nxt[WM][NG];
+    {
+      uint4 prev[WM][NG];
+      group(q0 - 1, prev);
+      act_column<NG>(prev[WM - 1], ok && q0 > 0, G, gm, y[0]);
+    }
+    group(q0, nxt);
+    act_column<NG>(nxt[0], ok, G, gm, yn);
+#pragma unroll
+    for (int qq = 0; qq < R; ++qq) {
+      const int q = q0 + qq;
+      if (q >= WQ) break;  // uniform over the lane group
+      uint4 cur[WM][NG];
+#pragma unroll
+      for (int e2 = 0; e2 < WM; ++e2)
+#pragma unroll
+        for (int h = 0; h < NG; ++h) cur[e2][h] = nxt[e2][h];
+      if (ok && f >= tail_from) {
+#pragma unroll
+        for (int e2 = 0; e2 < WM; ++e2)
+#pragma unroll
+          for (int h = 0; h < NG; ++h)
+            if (WM * q + e2 < W && (h == 0 || second))
+              *reinterpret_cast<uint4*>(hout + f * h_fstride + ((long long)row * W + WM * q + e2) * ldh +
+                                        (sub + h * G) * 8) = cur[e2][h];
+      }
+#pragma unroll
+      for (int h = 0; h < NG; ++h)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) y[1][h][c] = yn[h][c];
+#pragma unroll
+      for (int e2 = 1; e2 < WM; ++e2) act_column<NG>(cur[e2], ok && WM * q + e2 < W, G, gm, y[1 + e2]);
+      group(q + 1, nxt);
+      act_column<NG>(nxt[0], ok && q + 1 < WQ, G, gm, yn);
+#pragma unroll
+      for (int h = 0; h < NG; ++h)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) y[NX - 1][h][c] = yn[h][c];
+      h16_t* dst = U + ((long long)(f + 2) * H * WQ + (long long)row * WQ + q) * C;
+#pragma unroll
+      for (int h = 0; h < NG; ++h) {
+        if (h == 1 && !second) break;
+        float u[NX][8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          float d[NX], uu[NX];
+#pragma unroll
+          for (int k = 0; k < NX; ++k) d[k] = y[k][h][c];
+          Wino<WM>::input(d, uu);
+#pragma unroll
+          for (int k = 0; k < NX; ++k) u[k][c] = uu[k];
+        }
+        if (ok) {
+#pragma unroll
+          for (int k = 0; k < NX; ++k)
+            *reinterpret_cast<uint4*>(dst + (sub + h * G) * 8 + k * uplane) = pack8h(u[k]);
+        }
+      }
+      // this group's last column opens the next window
+#pragma unroll
+      for (int h = 0; h < NG; ++h)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) y[0][h][c] = y[WM][h][c];
     }
   }
 }
@@ -748,20 +919,38 @@ hipError_t launch_prep_wino_frag(const void* w, int dtype, int cout, int cin, h1
 }
 
 hipError_t launch_wino_in(const h16_t* x, long long x_fstride, int lda, const h16_t* ring, int n_hist, int C, int F,
-                          int H, int W, const float* gamma, h16_t* U, hipStream_t s) {
+                          int H, int W, const float* gamma, h16_t* U, hipStream_t s, bool history_only) {
   if (g_dry_run) return hipSuccess;
   if (C % 8 || C > 1024 || n_hist < 0 || n_hist > 2 || (n_hist > 0 && !ring) || F < 1) return hipErrorInvalidValue;
   const int WQ = (W + kWinoM - 1) / kWinoM;
   int G = 1;
   while (G * 2 <= (C >> 3) && G * 2 <= 64) G *= 2;
-  const long long runs = (long long)(F + n_hist) * H * ((WQ + kWinoInRun - 1) / kWinoInRun);
+  const int first = 2 - n_hist, end = history_only ? 2 : F + 2;
+  if (end <= first) return hipSuccess;
+  const long long runs = (long long)(end - first) * H * ((WQ + kWinoInRun - 1) / kWinoInRun);
   const long long threads = (runs + 64 / G - 1) / (64 / G) * 64;
   if (C / 8 > G)
     hipLaunchKernelGGL(wino_in_kernel<2>, dim3(grid_for(threads, 256, 65536)), dim3(256), 0, s, x, x_fstride, lda,
-                       ring, 2 - n_hist, C, F + 2, H, W, WQ, G, gamma, U);
+                       ring, first, end, C, F + 2, H, W, WQ, G, gamma, U);
   else
     hipLaunchKernelGGL(wino_in_kernel<1>, dim3(grid_for(threads, 256, 65536)), dim3(256), 0, s, x, x_fstride, lda,
-                       ring, 2 - n_hist, C, F + 2, H, W, WQ, G, gamma, U);
+                       ring, first, end, C, F + 2, H, W, WQ, G, gamma, U);
+  return hipGetLastError();
+}
+
+bool wino_mid_ok(int C) { return C % 8 == 0 && C <= 512; }
+
+hipError_t launch_wino_mid(const h16_t* M, const float* bias, int C, int F, int H, int W, const float* gamma,
+                           h16_t* U, h16_t* hout, long long h_fstride, int ldh, int tail_from, hipStream_t s) {
+  if (g_dry_run) return hipSuccess;
+  if (!wino_mid_ok(C) || F < 1 || ldh % 8 || ldh < C) return hipErrorInvalidValue;
+  const int WQ = (W + kWinoM - 1) / kWinoM;
+  int G = 1;
+  while (G * 2 <= (C >> 3) && G * 2 <= 64) G *= 2;
+  const long long runs = (long long)F * H * ((WQ + kWinoInRun - 1) / kWinoInRun);
+  const long long threads = (runs + 64 / G - 1) / (64 / G) * 64;
+  hipLaunchKernelGGL(wino_mid_kernel<1>, dim3(grid_for(threads, 256, 65536)), dim3(256), 0, s, M, bias, C, F, H, W,
+                     WQ, G, gamma, U, hout, h_fstride, ldh, tail_from);
   return hipGetLastError();
 }
 

@@ -151,7 +151,12 @@ hipError_t launch_prep_wino_frag(const void* w, int dtype, int cout, int cin, h1
 //   U[xi][s][row][q] = (B^T y)[xi]   (fp16)
 // U is [kWinoN][F+2][H][WQ][C] with WQ = ceil(W/m); rs as rms_stats writes it.
 hipError_t launch_wino_in(const h16_t* x, long long x_fstride, int lda, const h16_t* ring, int n_hist, int C, int F,
-                          int H, int W, const float* gamma, h16_t* U, hipStream_t s);
+                          int H, int W, const float* gamma, h16_t* U, hipStream_t s, bool history_only = false);
+// Output transform of conv1's products fused with conv2's input transform
+// (C <= 512): U slots 2..F+1 of conv2, h written for frames >= tail_from.
+bool wino_mid_ok(int C);
+hipError_t launch_wino_mid(const h16_t* M, const float* bias, int C, int F, int H, int W, const float* gamma,
+                           h16_t* U, h16_t* hout, long long h_fstride, int ldh, int tail_from, hipStream_t s);
 // Output transform: out[f][row][mq + j] = (A^T M)[j] + bias (+ res), with
 // M = [kWinoN][F][H][WQ][Cout] fp16; out may alias res.
 // With rs != null also writes rs[2+f][row][col] = 1/||out voxel|| exactly as
