@@ -827,9 +827,16 @@ __device__ __forceinline__ TileGeo tile_geo(const ConvArgs& a, int logical) {
   const int nt = (logical / nMt) % nN;
   const int ph = logical / (nMt * nN);
   TileGeo t;
-  t.x0 = (mt % a.tiles_x) * TW;
-  t.y0 = ((mt / a.tiles_x) % a.tiles_y) * TH;
-  t.f0 = (mt / (a.tiles_x * a.tiles_y)) * TF;
+  if (MODE == 2) {  // no temporal halo: rows of x-neighbours (shared x halo)
+    t.x0 = (mt % a.tiles_x) * TW;
+    t.y0 = ((mt / a.tiles_x) % a.tiles_y) * TH;
+    t.f0 = (mt / (a.tiles_x * a.tiles_y)) * TF;
+  } else {  // temporal taps: frames fastest, so the tiles that share their
+            // history frames run together and read them from one L2
+    t.f0 = (mt % a.tiles_f) * TF;
+    t.x0 = ((mt / a.tiles_f) % a.tiles_x) * TW;
+    t.y0 = (mt / (a.tiles_f * a.tiles_x)) * TH;
+  }
   t.n0 = nt * BN;
   t.ph = ph;
   return t;
