@@ -451,10 +451,18 @@ int tf_for(int KT, int F) {
   return KT == 3 ? 2 : 1;
 }
 
-// Tile width (column groups) of the Winograd-domain GEMM: 16 x 8 rows, or
-// 8 x 16 rows where that needs fewer rounds of tiles over the CUs (the small
-// levels, whose 20 or 39 column groups leave wide tiles mostly empty).
-int wino_tile_w(int F, int H, int WQ, int Cout) {
+// Tile shape of the Winograd-domain GEMM: TF frames x TH rows x TW column
+// groups (256 positions).  The GEMM is power-limited, and its halo loads (U
+// rows of the TF + 2 frames and TH + 2 rows around the tile) are much of the
+// power: deeper tiles in t and y load fewer halo rows per output.  The choice
+// minimises rounds of tiles over the CUs times (1 + 0.1 x halo rows per
+// output), which also keeps the 20- and 39-column-group levels from mostly
+// empty wide tiles.
+struct WinoShape {
+  int TF, TW;
+};
+
+WinoShape wino_tile_shape(int F, int H, int WQ, int Cout) {
   static int slots = 0;
   if (!slots) {
     int dev = 0, n = 0;
@@ -464,13 +472,21 @@ int wino_tile_w(int F, int H, int WQ, int Cout) {
     else
       slots = 256;
   }
-  auto rounds = [&](int tw) {
-    const int th = kTileM / tw / kWinoTF;
-    const long long tiles = (long long)((WQ + tw - 1) / tw) * ((H + th - 1) / th) * ((F + kWinoTF - 1) / kWinoTF) *
+  static const WinoShape cand[] = {{2, 16}, {2, 8}, {4, 8}, {4, 4}, {8, 4}};
+  WinoShape best = cand[0];
+  double best_cost = 1e300;
+  for (const WinoShape& c : cand) {
+    const int th = kTileM / c.TW / c.TF;
+    const long long tiles = (long long)((WQ + c.TW - 1) / c.TW) * ((H + th - 1) / th) * ((F + c.TF - 1) / c.TF) *
                             kWinoN * ((Cout + 255) / 256);
-    return (tiles + slots - 1) / slots;
-  };
-  return rounds(8) < rounds(16) ? 8 : 16;
+    const double halo = (double)(c.TF + 2) * (th + 2) / (c.TF * th);
+    const double cost = (double)((tiles + slots - 1) / slots) * (1.0 + 0.1 * halo);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = c;
+    }
+  }
+  return best;
 }
 
 // Causal 3x3x3 norm-SiLU conv in Winograd form along x:
@@ -502,7 +518,8 @@ void wino_gemm(Ctx& cx, const Act& x, int nh, int w_item, int Cout) {
   a.out_pstride = (long long)x.F * mframe;
   a.ldo = Cout;
   a.epi = EPI_WINO;
-  set_grid(a, x.F, x.H, W2, kWinoTF, wino_tile_w(x.F, x.H, W2, Cout));
+  const WinoShape ts = wino_tile_shape(x.F, x.H, W2, Cout);
+  set_grid(a, x.F, x.H, W2, ts.TF, ts.TW);
   conv(cx, a, 0);
 }
 

@@ -73,6 +73,13 @@ constexpr int kPhaseBRing = WVD_PHASE_W4 ? 2 : 4;  // the same for the up-conv p
 // (halo 4 x 10 x 16 rows; a 4 x 4 x 16 tile has fewer halo rows but measured slower).
 constexpr int kTFWino = kWinoTF;
 constexpr int kTHWino = kTileM / kTileW / kTFWino;
+}  // namespace
+// Tile shapes (frames x column groups) the Winograd-domain GEMM is built for;
+// rows = 256 / (TF * TW).  Deeper tiles in t and y cut the halo per output.
+bool wino_tile_shape_ok(int TF, int TW) {
+  return (TF == 2 && (TW == 16 || TW == 8)) || (TF == 4 && (TW == 8 || TW == 4)) || (TF == 8 && TW == 4);
+}
+namespace {
 
 __device__ __forceinline__ f16x8_t ld_frag(const h16_t* p) { return *reinterpret_cast<const f16x8_t*>(p); }
 
@@ -814,10 +821,10 @@ struct TileGeo {
   int f0, y0, x0, n0, ph;
 };
 
-template <int BN, int MODE, int TW = kTileW>
+template <int BN, int MODE, int TW = kTileW, int TF4 = kTFWino>
 __device__ __forceinline__ TileGeo tile_geo(const ConvArgs& a, int logical) {
-  constexpr int TF = MODE == 2 ? 1 : (MODE == 4 ? kTFWino : kTF333);
-  constexpr int TH = MODE == 2 ? 16 : (MODE == 4 ? kTileM / TW / kTFWino : kTH333);
+  constexpr int TF = MODE == 2 ? 1 : (MODE == 4 ? TF4 : kTF333);
+  constexpr int TH = MODE == 2 ? 16 : (MODE == 4 ? kTileM / TW / TF4 : kTH333);
   // Output positions vary fastest: the tiles running together on an XCD
   // share one (phase, channel block) of weights in its L2 and neighbouring
   // halos (interleaving the phases made them stream six weight sets).
@@ -842,7 +849,7 @@ __device__ __forceinline__ TileGeo tile_geo(const ConvArgs& a, int logical) {
   return t;
 }
 
-template <int BN, int WAVES_N, int MODE, int PRO0, int NW = 8, int TWW = kTileW>
+template <int BN, int WAVES_N, int MODE, int PRO0, int NW = 8, int TWW = kTileW, int TFW = kTFWino>
 __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
   constexpr int BK = 32, NT = NW * 64, NP = 4;
   // With 4 waves (one per SIMD, 512 registers: accumulators in AGPRs) each
@@ -864,9 +871,9 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
   // the product are output channels, columns output positions
   constexpr bool SWAPPED = WINO || MODE == 2;
   constexpr int TW = MODE == 4 ? TWW : kTileW;  // tile columns (Winograd: column groups)
-  static_assert(MODE == 4 || TWW == kTileW, "tile width choice is the Winograd GEMM's");
-  constexpr int TF = MODE == 2 ? 1 : (MODE == 4 ? kTFWino : kTF333);
-  constexpr int TH = MODE == 2 ? 16 : (MODE == 4 ? kTileM / TW / kTFWino : kTH333);
+  static_assert(MODE == 4 || (TWW == kTileW && TFW == kTFWino), "tile shape choice is the Winograd GEMM's");
+  constexpr int TF = MODE == 2 ? 1 : (MODE == 4 ? TFW : kTF333);
+  constexpr int TH = MODE == 2 ? 16 : (MODE == 4 ? kTileM / TW / TFW : kTH333);
   constexpr int KT = MODE == 2 ? 1 : 3;
   constexpr int HSX = KT3 || WINO ? 0 : 1;  // spatial halo along x
   constexpr int HSY = KT3 ? 0 : 1;          // and along y
@@ -902,7 +909,7 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
   // Halo table of tile `logical` into table set `tb`: per halo row the
   // source pointer and (norm) scale; padding voxels read the zero row.
   auto build_tables = [&](int tb, int logical) {
-    const TileGeo t = tile_geo<BN, MODE, TW>(a, logical);
+    const TileGeo t = tile_geo<BN, MODE, TW, TF>(a, logical);
     for (int v = tid; v < nhv_max; v += NT) {
       const h16_t* p = a.zero_row;
       float rsv = 0.0f;
@@ -951,7 +958,7 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
   const int U = S.Cin / 16;
   auto ctx_for = [&](int logical, int tb) {
     SegCtx<BK, MI, NJ, NT> g = g0;
-    const TileGeo t = tile_geo<BN, MODE, TW>(a, logical);
+    const TileGeo t = tile_geo<BN, MODE, TW, TF>(a, logical);
     g.vptr = vptr_s + tb * nhv_max;
     g.rs = rs_s + tb * nhv_max;
     g.tap0 = t.ph * NTAPS;
@@ -1009,7 +1016,7 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
     // tile) streams its own halo and weights once more into the spare
     // buffer and ring slots: no branch, exact wait counters.
     const SegCtx<BK, MI, NJ, NT> gl = nxt >= 0 ? ctx_for(nxt, (k + 1) & 1) : g;
-    const TileGeo geo = tile_geo<BN, MODE, TW>(a, cur);
+    const TileGeo geo = tile_geo<BN, MODE, TW, TF>(a, cur);
 
     for (int c = 0; c < nchunks; ++c, ++gc) {
       const bool last = c + 1 == nchunks;
@@ -1427,11 +1434,11 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
   }
 }
 
-template <int BN, int WAVES_N, int MODE, int PRO0, int NW = 8, int TW = kTileW>
+template <int BN, int WAVES_N, int MODE, int PRO0, int NW = 8, int TW = kTileW, int TF = kTFWino>
 hipError_t launch_persist_impl(const ConvArgs& a, hipStream_t stream) {
   if (g_dry_run) return hipSuccess;
   const size_t lds = conv_lds_bytes(a);
-  auto kern = conv_persist<BN, WAVES_N, MODE, PRO0, NW, TW>;
+  auto kern = conv_persist<BN, WAVES_N, MODE, PRO0, NW, TW, TF>;
   static size_t attr_bytes = 0;
   if (lds > attr_bytes) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1500,8 +1507,8 @@ Variant conv_variant(const ConvArgs& a) {
                    v.bk == 32 && a.nseg == 1 && g.wfrag && g.prologue == PRO_RAW;
   const bool kt3 = g.KT == 3 && g.KS == 1 && a.nphase == 1 && a.TF == kTF333 && a.TH == kTH333 && v.bk == 32 &&
                    a.nseg == 1 && g.wfrag && g.prologue == PRO_RAW && a.Cout % 256 == 0 && a.epi == EPI_TIME;
-  const bool kwino = g.KT == 3 && g.KS == KS_3x1 && a.nphase == kWinoN && a.TF == kTFWino &&
-                     ((a.TW == kTileW && a.TH == kTHWino) || (a.TW == 8 && a.TH == kTileM / 8 / kTFWino)) &&
+  const bool kwino = g.KT == 3 && g.KS == KS_3x1 && a.nphase == kWinoN && wino_tile_shape_ok(a.TF, a.TW) &&
+                     a.TF * a.TH * a.TW == kTileM &&
                      v.bk == 32 && a.nseg == 1 && g.wfrag && g.prologue == PRO_RAW && a.Cout % 256 == 0 &&
                      a.epi == EPI_WINO;
   const bool shortcut_ok = a.nseg == 1 || (a.seg[1].KT == 1 && a.seg[1].KS == 1 && a.seg[1].prologue == PRO_RAW &&
@@ -1781,7 +1788,7 @@ size_t conv_lds_bytes(const ConvArgs& a) {
 
 const char* conv_check(const ConvArgs& a) {
   if (a.nseg < 1 || a.nseg > 2) return "segment count";
-  if (a.TW != kTileW && !(a.TW == 8 && a.seg[0].KS == KS_3x1)) return "tile width 8 is the Winograd GEMM's only";
+  if (a.seg[0].KS == KS_3x1 ? !wino_tile_shape_ok(a.TF, a.TW) : a.TW != kTileW) return "unsupported tile shape";
   if (a.TF < 1 || a.TF * a.TH * a.TW != kTileM) return "tile TF*TH*TW != 256";
   if (a.F < 1 || a.H < 1 || a.W < 1 || a.Cout < 1) return "empty output grid";
   if (a.nphase != 1 && a.nphase != 4 && a.nphase != kWinoN) return "phase count";
@@ -1840,10 +1847,14 @@ hipError_t launch_conv(const ConvArgs& a, hipStream_t stream) {
     if (v.mode == 2) return launch_persist_impl<256, 4, 2, PRO_RAW>(a, stream);
     if (v.mode == 3) return launch_persist_impl<256, 4, 3, PRO_RAW>(a, stream);
 #if WVD_WINO_W4
-    if (v.mode == 4 && a.TW == 8) return launch_persist_impl<256, 2, 4, PRO_RAW, 4, 8>(a, stream);
-    if (v.mode == 4) return launch_persist_impl<256, 2, 4, PRO_RAW, 4>(a, stream);
+    if (v.mode == 4) {  // one instantiation per Winograd tile shape (TF frames x TW column groups)
+      if (a.TF == 2 && a.TW == 8) return launch_persist_impl<256, 2, 4, PRO_RAW, 4, 8, 2>(a, stream);
+      if (a.TF == 4 && a.TW == 8) return launch_persist_impl<256, 2, 4, PRO_RAW, 4, 8, 4>(a, stream);
+      if (a.TF == 8 && a.TW == 4) return launch_persist_impl<256, 2, 4, PRO_RAW, 4, 4, 8>(a, stream);
+      if (a.TF == 4 && a.TW == 4) return launch_persist_impl<256, 2, 4, PRO_RAW, 4, 4, 4>(a, stream);
+      return launch_persist_impl<256, 2, 4, PRO_RAW, 4>(a, stream);
+    }
 #endif
-    if (v.mode == 4 && a.TW == 8) return launch_persist_impl<256, 4, 4, PRO_RAW, 8, 8>(a, stream);
     if (v.mode == 4) return launch_persist_impl<256, 4, 4, PRO_RAW>(a, stream);
     if (v.bn == 32) return launch_persist_impl<32, 1, 1, PRO_RAW>(a, stream);
 #if WVD_MAIN_W4

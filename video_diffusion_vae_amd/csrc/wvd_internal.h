@@ -155,6 +155,8 @@ hipError_t launch_wino_in(const h16_t* x, long long x_fstride, int lda, const h1
 // Output transform of conv1's products fused with conv2's input transform
 // (C <= 512): U slots 2..F+1 of conv2, h written for frames >= tail_from.
 bool wino_mid_ok(int C);
+// Tile shapes (TF frames x TW column groups) of the Winograd-domain GEMM.
+bool wino_tile_shape_ok(int TF, int TW);
 hipError_t launch_wino_mid(const h16_t* M, const float* bias, int C, int F, int H, int W, const float* gamma,
                            h16_t* U, h16_t* hout, long long h_fstride, int ldh, int tail_from, hipStream_t s);
 // Output transform: out[f][row][mq + j] = (A^T M)[j] + bias (+ res), with
