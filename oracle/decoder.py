@@ -209,14 +209,22 @@ def pixel_shuffle_video(y: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 def decode_chunk(z: np.ndarray, W: Dict[str, np.ndarray], c: int, cache: Cache) -> np.ndarray:
-    """One chunk of latent frames z [F, h, w, 48] -> video [3, F', 16h, 16w]."""
+    """One chunk of latent frames z [F, h, w, 48] -> video [3, F', 16h, 16w].
+
+    The deep variant (its weights hold "pre_conv") first applies the 48 -> 48
+    1x1x1 conv to the latents and has three ResBlocks per up stage (the
+    Wan2.2 page's 110 decoder tensors, "Use")."""
+    if "pre_conv.weight" in W:
+        z = causal_conv3d(z, W["pre_conv.weight"], W["pre_conv.bias"])
     x = cache.conv("conv_in", z, W["conv_in.weight"], W["conv_in.bias"])
     x = resblock(x, W, "mid.res0", cache)
     x = attention(x, W, "mid.attn")
     x = resblock(x, W, "mid.res1", cache)
     for s in range(4):
-        x = resblock(x, W, f"up{s}.res0", cache)
-        x = resblock(x, W, f"up{s}.res1", cache)
+        k = 0
+        while f"up{s}.res{k}.norm1.gamma" in W:
+            x = resblock(x, W, f"up{s}.res{k}", cache)
+            k += 1
         if s < 2:
             x = time_upsample(x, W[f"up{s}.time_conv.weight"], W[f"up{s}.time_conv.bias"],
                               f"up{s}.time_conv", cache)

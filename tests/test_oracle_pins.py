@@ -354,3 +354,42 @@ def test_flop_count_brute():
     macs += F2 * r3 * (c * 2 * c * 27 + 3 * c * c * 27 + c * 2 * c)            # up3 (+ shortcut)
     macs += F2 * r3 * 12 * c * 27
     assert O.conv_flops(c, T, h, w) == 2.0 * macs
+
+
+def test_deep_variant_reduces_to_the_base_decoder(tiny):
+    """Deep variant (110 tensors): with pre_conv = identity and the third
+    ResBlock of every stage silenced (conv2 = 0, so the block is x + 0), the
+    decode equals the 84-tensor decoder with the same shared weights; a
+    nonzero third block changes the video, so the blocks are wired in."""
+    W, z = tiny
+    Wd = synth.make_weights(C_TINY, seed=5, bf16=False, deep=True)
+    assert len(Wd) == synth.NUM_WEIGHTS_DEEP and len(W) == synth.NUM_WEIGHTS
+    for k, v in W.items():
+        Wd[k] = v
+    Wd["pre_conv.weight"] = np.eye(48, dtype=np.float32)[:, :, None, None, None]
+    Wd["pre_conv.bias"] = np.zeros(48, np.float32)
+    live = dict(Wd)
+    for s in range(4):
+        Wd[f"up{s}.res2.conv2.weight"] = np.zeros_like(Wd[f"up{s}.res2.conv2.weight"])
+        Wd[f"up{s}.res2.conv2.bias"] = np.zeros_like(Wd[f"up{s}.res2.conv2.bias"])
+    base = O.decode(z[:, :, :2], W, C_TINY)
+    np.testing.assert_array_equal(O.decode(z[:, :, :2], Wd, C_TINY), base)
+    assert not np.array_equal(O.decode(z[:, :, :2], live, C_TINY), base)
+
+
+def test_deep_pre_conv_is_a_per_voxel_matrix(tiny):
+    """pre_conv is a 1x1x1 conv: scaling its weight and shifting its bias is
+    the same as scaling and shifting the latents fed to a pre_conv-free
+    decoder (it has no temporal or spatial taps)."""
+    W, z = tiny
+    Wd = synth.make_weights(C_TINY, seed=6, bf16=False, deep=True)
+    rng = np.random.default_rng(4)
+    A = rng.uniform(-0.3, 0.3, (48, 48)).astype(np.float32)
+    b = rng.uniform(-0.1, 0.1, 48).astype(np.float32)
+    Wd["pre_conv.weight"] = A[:, :, None, None, None]
+    Wd["pre_conv.bias"] = b
+    zz = z[:, :, :2]
+    zpre = (np.einsum("oi,itxy->otxy", A.astype(np.float64), zz[0].astype(np.float64)) +
+            b[:, None, None, None]).astype(np.float32)[None]
+    Wn = {k: v for k, v in Wd.items() if not k.startswith("pre_conv")}
+    np.testing.assert_allclose(O.decode(zz, Wd, C_TINY), O.decode(zpre, Wn, C_TINY), rtol=1e-5, atol=1e-5)

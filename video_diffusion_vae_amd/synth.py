@@ -14,6 +14,11 @@ this decoder as the Wan2.2 VAE decoder with 48 latent channels, 16x16 spatial
 and 4x temporal compression ("Wan2.2 VAE decoder", introduction); the exact
 layer list is the plainest reading of that description.
 
+A deeper variant ("deep", 110 tensors) has three ResBlocks per up stage and
+a 48 -> 48 1x1x1 conv applied to the latents before conv_in: the Wan2.2 page
+("Use") counts 110 decoder tensors, which is the 84 above plus one more
+ResBlock per stage (4 x 6) and that 1x1x1 conv (2).
+
 Initialisation: every conv / linear weight is uniform(-1/sqrt(fan_in),
 +1/sqrt(fan_in)) with fan_in = Cin*kt*kh*kw, every RMSNorm gamma is
 1 + 0.1*N(0,1) and every bias 0.01*N(0,1).  Tensor i of the canonical list is
@@ -64,10 +69,21 @@ def _resblock(name: str, cin: int, cout: int) -> List[WeightSpec]:
     return out
 
 
-def weight_specs(c: int) -> List[WeightSpec]:
-    """The 84 decoder tensors in canonical order (PyTorch layouts)."""
+NUM_WEIGHTS = 84
+NUM_WEIGHTS_DEEP = 110
+
+
+def res_per_stage(deep: bool) -> int:
+    return 3 if deep else 2
+
+
+def weight_specs(c: int, deep: bool = False) -> List[WeightSpec]:
+    """The decoder tensors in canonical order (PyTorch layouts): 84, or 110
+    for the deep variant (pre_conv first, three ResBlocks per up stage)."""
     c4 = 4 * c
     specs: List[WeightSpec] = []
+    if deep:
+        specs += _conv("pre_conv", LATENT_CHANNELS, LATENT_CHANNELS, (1, 1, 1))
     specs += _conv("conv_in", c4, LATENT_CHANNELS, (3, 3, 3))
     specs += _resblock("mid.res0", c4, c4)
     specs += [WeightSpec("mid.attn.norm.gamma", (c4,), "gamma")]
@@ -78,7 +94,8 @@ def weight_specs(c: int) -> List[WeightSpec]:
     prev = c4
     for s, cs in enumerate(widths):
         specs += _resblock(f"up{s}.res0", prev, cs)
-        specs += _resblock(f"up{s}.res1", cs, cs)
+        for k in range(1, res_per_stage(deep)):
+            specs += _resblock(f"up{s}.res{k}", cs, cs)
         if s < 2:
             specs += _conv(f"up{s}.time_conv", 2 * cs, cs, (3, 1, 1))
         if s < 3:
@@ -89,8 +106,8 @@ def weight_specs(c: int) -> List[WeightSpec]:
     return specs
 
 
-def weight_names(c: int) -> List[str]:
-    return [s.name for s in weight_specs(c)]
+def weight_names(c: int, deep: bool = False) -> List[str]:
+    return [s.name for s in weight_specs(c, deep)]
 
 
 def bf16_round(a: np.ndarray) -> np.ndarray:
@@ -111,14 +128,14 @@ def bf16_bits(a: np.ndarray) -> np.ndarray:
     return (a.view(np.uint32) >> 16).astype(np.uint16)
 
 
-def make_weights(c: int, seed: int = 0, bf16: bool = True) -> Dict[str, np.ndarray]:
+def make_weights(c: int, seed: int = 0, bf16: bool = True, deep: bool = False) -> Dict[str, np.ndarray]:
     """Seeded float32 weights in canonical order (dict preserves the order).
 
     With bf16=True every tensor is rounded to bf16 (RNE) and that rounded
     model is the model both the oracle and the GPU evaluate.
     """
     out: Dict[str, np.ndarray] = {}
-    for i, sp in enumerate(weight_specs(c)):
+    for i, sp in enumerate(weight_specs(c, deep)):
         rng = np.random.Generator(np.random.PCG64([seed, i]))
         if sp.kind == "weight":
             bound = 1.0 / np.sqrt(sp.fan_in)
@@ -155,6 +172,7 @@ class Config:
     w: int
     passes: Tuple[int, ...]
     weights_bf16: bool = True
+    deep: bool = False
 
     @property
     def video_shape(self) -> Tuple[int, int, int, int, int]:
@@ -172,8 +190,17 @@ CONFIGS: Sequence[Config] = (
 )
 
 
+# The deep (110-tensor) variant at the same sizes: parity cases and a bench
+# line beside the five workloads.
+DEEP_CONFIGS: Sequence[Config] = (
+    Config("deep_tiny_c16_T2_4x6", 16, 2, 4, 6, (1, 2), weights_bf16=False, deep=True),
+    Config("deep_c64_T3_352x624", 64, 3, 22, 39, (1, 3), deep=True),
+    Config("deep_c256_T49_704x1248", 256, 49, 44, 78, (4,), deep=True),
+)
+
+
 def config_by_name(name: str) -> Config:
-    for cfg in CONFIGS:
+    for cfg in tuple(CONFIGS) + tuple(DEEP_CONFIGS):
         if cfg.name == name:
             return cfg
     raise KeyError(name)
