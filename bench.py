@@ -82,7 +82,7 @@ def run_sweep(args):
     cfg = synth.config_by_name(args.config)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(0)
-    W = synth.make_weights(cfg.c, seed=args.seed, bf16=cfg.weights_bf16)
+    W = synth.make_weights(cfg.c, seed=args.seed, bf16=cfg.weights_bf16, deep=cfg.deep)
     dec = wvd.Decoder({k: torch.from_numpy(v).to(torch.bfloat16) for k, v in W.items()}, cfg.c, cfg.h, cfg.w,
                       device=dev)
     z = torch.from_numpy(synth.make_latents(cfg.T, cfg.h, cfg.w, seed=args.seed)).to(dev).to(torch.bfloat16)
@@ -138,7 +138,7 @@ def cpu_baseline(cfg, W, seed, T_sample):
         "sample": f"exact causal prefix: {T_sample} latent frame(s) -> {frames} video frame(s) of "
                   f"{cfg.name}, full decoder, numpy fp32 ({dt:.1f} s)",
         "seconds": dt,
-        "gflops": O.conv_flops(cfg.c, T_sample, cfg.h, cfg.w) / dt / 1e9,
+        "gflops": O.conv_flops(cfg.c, T_sample, cfg.h, cfg.w, cfg.deep) / dt / 1e9,
     }
 
 
@@ -164,7 +164,7 @@ def main():
     P = args.frames_per_pass or cfg.passes[0]
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
-    W = synth.make_weights(cfg.c, seed=args.seed, bf16=cfg.weights_bf16)
+    W = synth.make_weights(cfg.c, seed=args.seed, bf16=cfg.weights_bf16, deep=cfg.deep)
     wt = {k: torch.from_numpy(v) for k, v in W.items()}
     if cfg.weights_bf16:
         wt = {k: v.to(torch.bfloat16) for k, v in wt.items()}
@@ -213,7 +213,7 @@ def main():
 
     frames = 4 * cfg.T - 3
     fps = frames / (ms / 1e3)
-    total_flops = O.conv_flops(cfg.c, cfg.T, cfg.h, cfg.w)  # nominal (9-tap up-convs)
+    total_flops = O.conv_flops(cfg.c, cfg.T, cfg.h, cfg.w, cfg.deep)  # nominal (9-tap up-convs)
     alg_flops = sum(v["flops"] for v in prof.values()) / args.steps
     conv = prof["conv3x3x3_main"]
     launches = max(conv["launches"], 1)

@@ -52,13 +52,20 @@ enum wvd_status {
 
 /* Number of weight tensors in the canonical order (see wvd_prepare). */
 #define WVD_NUM_WEIGHTS 84
+/* The deep variant: a 48 -> 48 1x1x1 conv on the latents before conv_in and
+ * three ResBlocks per up stage (the 110 decoder tensors of the Wan2.2 page,
+ * "Use"). */
+#define WVD_NUM_WEIGHTS_DEEP 110
 
 /* Element type of the weights and latents handed to wvd_prepare/wvd_decode. */
 enum wvd_dtype { WVD_DTYPE_BF16 = 0, WVD_DTYPE_F32 = 1 };
 
 /* Bytes of the prepared-weights buffer for base width c at latent size h x w.
- * c: positive multiple of 16; 1 <= h, w <= 4096.  Writes *bytes. */
+ * c: positive multiple of 16; 1 <= h, w <= 4096.  Writes *bytes.
+ * wvd_prepared_bytes is the 84-tensor decoder; wvd_prepared_bytes_n takes the
+ * tensor count (WVD_NUM_WEIGHTS or WVD_NUM_WEIGHTS_DEEP). */
 int wvd_prepared_bytes(int c, int h, int w, size_t* bytes);
+int wvd_prepared_bytes_n(int c, int h, int w, int n_weights, size_t* bytes);
 
 /* One-time weight preparation (Wan2.2 VAE decoder page, "Use": layout and
  * phase transforms of the weights, done once).
@@ -74,7 +81,11 @@ int wvd_prepared_bytes(int c, int h, int w, size_t* bytes);
  *             [2Cs,Cs,3,1,1], bias; s < 2), up_conv (weight [Cs,Cs,3,3],
  *             bias; s < 3); head (norm.gamma [c], conv.weight [12,c,3,3,3],
  *             conv.bias).
- *   prepared: caller-owned device buffer of wvd_prepared_bytes(c,h,w) bytes.
+ *   n_weights: WVD_NUM_WEIGHTS, or WVD_NUM_WEIGHTS_DEEP for the deep
+ *             variant, whose list starts with pre_conv (weight
+ *             [48,48,1,1,1], bias) and has res0, res1, res2 in every stage.
+ *   prepared: caller-owned device buffer of wvd_prepared_bytes_n(c, h, w,
+ *             n_weights) bytes.
  * The input weights may be freed once the enqueued work has completed.  On
  * success *plan_out receives a host object to release with wvd_destroy. */
 int wvd_prepare(int c, int h, int w, const void* const* weights, int n_weights,

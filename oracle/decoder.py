@@ -257,13 +257,16 @@ def decode(z: np.ndarray, W: Dict[str, np.ndarray], c: int,
     return np.concatenate(outs, axis=1)[None]
 
 
-def conv_flops(c: int, T: int, h: int, w: int) -> float:
+def conv_flops(c: int, T: int, h: int, w: int, deep: bool = False) -> float:
     """Multiply-add FLOPs (2 per MAC) of the decoder as the oracle computes it
-    (up-convs as 3x3 convs on the upsampled frames)."""
+    (up-convs as 3x3 convs on the upsampled frames); deep adds the 48 -> 48
+    1x1x1 conv and a third ResBlock per up stage."""
     c4 = 4 * c
     F0, F1, F2 = T, 2 * T - 1, 4 * T - 3
     r = [h * w, 4 * h * w, 16 * h * w, 64 * h * w]
     fl = 0.0
+    if deep:
+        fl += F0 * r[0] * 48 * 48
     fl += F0 * r[0] * c4 * 48 * 27
     fl += 2 * (2 * F0 * r[0] * c4 * c4 * 27)
     fl += F0 * r[0] * (3 * c4 * c4 + c4 * c4) + F0 * 2 * r[0] * r[0] * c4
@@ -275,7 +278,7 @@ def conv_flops(c: int, T: int, h: int, w: int) -> float:
         fl += Fr * px * cs * prev * 27 + Fr * px * cs * cs * 27
         if prev != cs:
             fl += Fr * px * cs * prev
-        fl += 2 * Fr * px * cs * cs * 27
+        fl += (4 if deep else 2) * Fr * px * cs * cs * 27
         if s < 2:
             fl += (Fr - 1) * px * 2 * cs * cs * 3
         if s < 3:

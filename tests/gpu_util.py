@@ -39,7 +39,7 @@ def _src_hash() -> str:
 
 def inputs(cfg: synth.Config, seed: int, T: Optional[int] = None):
     T = cfg.T if T is None else T
-    W = synth.make_weights(cfg.c, seed=seed, bf16=cfg.weights_bf16)
+    W = synth.make_weights(cfg.c, seed=seed, bf16=cfg.weights_bf16, deep=cfg.deep)
     z = synth.make_latents(T, cfg.h, cfg.w, seed=seed, bf16=cfg.weights_bf16)
     return W, z
 
@@ -64,7 +64,7 @@ _decoders: Dict[Tuple[int, int, int, int, bool], object] = {}
 
 def decoder_for(cfg: synth.Config, seed: int):
     from video_diffusion_vae_amd import wvd
-    key = (cfg.c, cfg.h, cfg.w, seed, cfg.weights_bf16)
+    key = (cfg.c, cfg.h, cfg.w, seed, cfg.weights_bf16, cfg.deep)
     if key not in _decoders:
         import torch
         W, _ = inputs(cfg, seed, 1)

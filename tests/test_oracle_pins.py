@@ -354,6 +354,12 @@ def test_flop_count_brute():
     macs += F2 * r3 * (c * 2 * c * 27 + 3 * c * c * 27 + c * 2 * c)            # up3 (+ shortcut)
     macs += F2 * r3 * 12 * c * 27
     assert O.conv_flops(c, T, h, w) == 2.0 * macs
+    # deep: + the 48x48 latent conv and one more same-width ResBlock (two
+    # 3x3x3 convs) per stage at that stage's resolution and frame count
+    extra = F0 * r0 * 48 * 48
+    for cs, Fr, px in ((c4, F0, r0), (c4, F1, r1), (2 * c, F2, r2), (c, F2, r3)):
+        extra += 2 * Fr * px * cs * cs * 27
+    assert O.conv_flops(c, T, h, w, deep=True) == 2.0 * (macs + extra)
 
 
 def test_deep_variant_reduces_to_the_base_decoder(tiny):

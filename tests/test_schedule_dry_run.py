@@ -15,15 +15,16 @@ def dry():
     wvd.wvd_set_dry_run(False)
 
 
-def plan_for(wvd, c, h, w):
-    n = wvd.wvd_prepared_bytes(c, h, w)
-    return wvd.wvd_prepare(c, h, w, [FAKE] * 84, wvd.WVD_DTYPE_BF16, FAKE, n, 0)
+def plan_for(wvd, c, h, w, deep=False):
+    nw = wvd.NUM_WEIGHTS_DEEP if deep else wvd.NUM_WEIGHTS
+    n = wvd.wvd_prepared_bytes_n(c, h, w, nw)
+    return wvd.wvd_prepare(c, h, w, [FAKE] * nw, wvd.WVD_DTYPE_BF16, FAKE, n, 0)
 
 
-@pytest.mark.parametrize("cfg", synth.CONFIGS, ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", tuple(synth.CONFIGS) + tuple(synth.DEEP_CONFIGS), ids=lambda c: c.name)
 def test_every_config_schedules(dry, cfg):
     wvd = dry
-    plan = plan_for(wvd, cfg.c, cfg.h, cfg.w)
+    plan = plan_for(wvd, cfg.c, cfg.h, cfg.w, cfg.deep)
     try:
         counts = {}
         for P in sorted(set(cfg.passes) | {1, cfg.T, cfg.T + 3}):
@@ -109,3 +110,25 @@ def test_chunked_decode_schedules_and_validates(dry):
             assert e.value.status == status, kw
     finally:
         wvd.wvd_destroy(plan)
+
+
+def test_deep_variant_has_more_launches_and_weights(dry):
+    """The deep variant prepares more bytes, keeps more rings in its stream
+    state, and launches more kernels per pass than the 84-tensor decoder."""
+    wvd = dry
+    base, deep = plan_for(wvd, 64, 22, 39), plan_for(wvd, 64, 22, 39, deep=True)
+    try:
+        assert wvd.wvd_prepared_bytes_n(64, 22, 39, 110) > wvd.wvd_prepared_bytes(64, 22, 39)
+        assert wvd.wvd_state_bytes(deep) > wvd.wvd_state_bytes(base)
+        counts = []
+        for plan in (base, deep):
+            ws = wvd.wvd_workspace_bytes(plan, 3, 3)
+            wvd.wvd_decode(plan, FAKE, 0, 3, 3, FAKE, FAKE, ws, 0)
+            counts.append(wvd.wvd_last_launch_count(plan))
+        assert counts[1] > counts[0]
+        for bad in (83, 85, 109, 111):
+            with pytest.raises(wvd.WvdError):
+                wvd.wvd_prepared_bytes_n(64, 22, 39, bad)
+    finally:
+        wvd.wvd_destroy(base)
+        wvd.wvd_destroy(deep)

@@ -51,10 +51,14 @@ struct RB {
   bool wino1 = false, wino2 = false;  // conv1 / conv2 prepared and run in Winograd form
 };
 
+constexpr int kMaxResPerStage = 3;
+
 struct Layout {
   std::vector<Item> items;
+  int nrb = 2;                  // ResBlocks per up stage (3 in the deep variant)
+  int pre_w = -1, pre_b = -1;   // deep variant: 48 -> 48 1x1x1 conv on the latents (fp32 matrix, bias)
   int conv_in_w, conv_in_b;
-  RB mid0, mid1, up[4][2];
+  RB mid0, mid1, up[4][kMaxResPerStage];
   int attn_norm, qkv_w, qkv_b, proj_w, proj_b;
   int tc_w[2], tc_b[2], upc_w[3], upc_b[3];
   int head_norm, head_w, head_b;
@@ -103,10 +107,15 @@ RB add_rb(Layout& L, int cin, int cout) {
 
 int lpad_of(int L);
 
-Layout make_layout(int c, int h, int w) {
+Layout make_layout(int c, int h, int w, bool deep = false) {
   Layout L;
   const int c4 = 4 * c;
   const int widths[4] = {c4, c4, 2 * c, c};
+  L.nrb = deep ? 3 : 2;
+  if (deep) {
+    L.pre_w = add_vec(L, 48 * 48, 1.0f);  // [out][in] as fp32
+    L.pre_b = add_vec(L, 48, 1.0f);
+  }
   add_conv(L, c4, 48, 27, 64, &L.conv_in_w, &L.conv_in_b);
   L.mid0 = add_rb(L, c4, c4);
   L.attn_norm = add_vec(L, c4, std::sqrt((float)c4));
@@ -117,7 +126,7 @@ Layout make_layout(int c, int h, int w) {
   for (int s = 0; s < 4; ++s) {
     const int cs = widths[s];
     L.up[s][0] = add_rb(L, prev, cs);
-    L.up[s][1] = add_rb(L, cs, cs);
+    for (int k = 1; k < L.nrb; ++k) L.up[s][k] = add_rb(L, cs, cs);
     if (s < 2) add_conv(L, 2 * cs, cs, 3, cs, &L.tc_w[s], &L.tc_b[s]);
     if (s < 3) {
       add_conv(L, cs, cs, 9, cs, &L.upc_w[s], &L.upc_b[s]);
@@ -146,7 +155,7 @@ Layout make_layout(int c, int h, int w) {
 
 // Workspace carve-up for a given maximum number of latent frames per pass.
 struct Work {
-  size_t X, H, Y, zt, rs, qkv, S, Pm, Vt, O;
+  size_t X, H, Y, zt, zp, rs, qkv, S, Pm, Vt, O;
   size_t U, M;               // Winograd input planes and products
   std::vector<size_t> ring;  // 24 rings: offsets inside the ring block
   size_t rings;              // ring block offset in the workspace (npos: caller-owned state)
@@ -161,32 +170,39 @@ struct RingInfo {
   int level;
 };
 
-enum RingId {
-  R_CONV_IN = 0, R_MID0_1, R_MID0_2, R_MID1_1, R_MID1_2,
-  R_UP00_1, R_UP00_2, R_UP01_1, R_UP01_2, R_TC0,
-  R_UP10_1, R_UP10_2, R_UP11_1, R_UP11_2, R_TC1,
-  R_UP20_1, R_UP20_2, R_UP21_1, R_UP21_2,
-  R_UP30_1, R_UP30_2, R_UP31_1, R_UP31_2,
-  R_HEAD, R_COUNT
-};
+// Rings (the last two raw input frames of every temporal conv), in a fixed
+// order: conv_in, the mid block's four convs, per up stage two per ResBlock
+// and the time_conv of stages 0 and 1, then the head.
+enum { R_CONV_IN = 0, R_MID0_1, R_MID0_2, R_MID1_1, R_MID1_2, R_UP_BASE };
 
-RingInfo ring_info(int c, int id) {
-  const int c4 = 4 * c, c2 = 2 * c;
-  switch (id) {
-    case R_CONV_IN: return {64, 0};
-    case R_MID0_1: case R_MID0_2: case R_MID1_1: case R_MID1_2:
-    case R_UP00_1: case R_UP00_2: case R_UP01_1: case R_UP01_2: case R_TC0: return {c4, 0};
-    case R_UP10_1: case R_UP10_2: case R_UP11_1: case R_UP11_2: case R_TC1: return {c4, 1};
-    case R_UP20_1: return {c4, 2};
-    case R_UP20_2: case R_UP21_1: case R_UP21_2: return {c2, 2};
-    case R_UP30_1: return {c2, 3};
-    default: return {c, 3};  // R_UP30_2, R_UP31_*, R_HEAD
+int ring_up(int nrb, int s, int k, int conv) {  // conv 0: conv1's input, 1: conv2's input
+  int id = R_UP_BASE;
+  for (int t = 0; t < s; ++t) id += 2 * nrb + (t < 2 ? 1 : 0);
+  return id + 2 * k + conv;
+}
+int ring_tc(int nrb, int s) { return ring_up(nrb, s, nrb, 0); }
+int ring_head(int nrb) { return ring_up(nrb, 3, nrb, 0); }
+int ring_count(int nrb) { return ring_head(nrb) + 1; }
+
+RingInfo ring_info(int c, int nrb, int id) {
+  const int c4 = 4 * c;
+  const int widths[4] = {c4, c4, 2 * c, c};
+  if (id < R_UP_BASE) return {id == R_CONV_IN ? 64 : c4, 0};
+  if (id == ring_head(nrb)) return {c, 3};
+  int prev = c4;
+  for (int s = 0; s < 4; ++s) {
+    for (int k = 0; k < nrb; ++k)
+      for (int cv = 0; cv < 2; ++cv)
+        if (id == ring_up(nrb, s, k, cv)) return {(k == 0 && cv == 0) ? prev : widths[s], s};
+    if (s < 2 && id == ring_tc(nrb, s)) return {widths[s], s};
+    prev = widths[s];
   }
+  return {c, 3};
 }
 
 int lpad_of(int L) { return (L + 31) / 32 * 32; }
 
-Work make_work(int c, int h, int w, int P, bool rings_in_workspace = true) {
+Work make_work(int c, int h, int w, int P, bool rings_in_workspace = true, int nrb = 2) {
   Work W;
   const long long r0 = (long long)h * w;
   const long long res[4] = {r0, 4 * r0, 16 * r0, 64 * r0};
@@ -204,6 +220,7 @@ Work make_work(int c, int h, int w, int P, bool rings_in_workspace = true) {
   W.H = take(act * 2);
   W.Y = take(act * 2);
   W.zt = take((size_t)F0 * r0 * 64 * 2);
+  W.zp = take((size_t)F0 * r0 * 64 * 2);  // latents after the deep variant's 1x1x1 conv
   W.rs = take((size_t)(F2 + 2) * res[3] * 4);
   W.qkv = take((size_t)F0 * L * 3 * c4 * 2);
   W.S = take((size_t)F0 * L * Lp * 4);
@@ -233,8 +250,8 @@ Work make_work(int c, int h, int w, int P, bool rings_in_workspace = true) {
   // in one block: inside the workspace for a whole-clip decode, or in the
   // caller's stream state for chunked decodes.
   size_t roff = 0;
-  for (int i = 0; i < R_COUNT; ++i) {
-    RingInfo ri = ring_info(c, i);
+  for (int i = 0; i < ring_count(nrb); ++i) {
+    RingInfo ri = ring_info(c, nrb, i);
     W.ring.push_back(roff);
     roff = align_up(roff + (size_t)2 * res[ri.level] * ri.cin * 2);
   }
@@ -806,10 +823,15 @@ const char* wvd_status_string(int st) {
 }
 
 int wvd_prepared_bytes(int c, int h, int w, size_t* bytes) {
+  return wvd_prepared_bytes_n(c, h, w, WVD_NUM_WEIGHTS, bytes);
+}
+
+int wvd_prepared_bytes_n(int c, int h, int w, int n_weights, size_t* bytes) {
   if (!bytes) return WVD_EINVAL;
+  if (n_weights != WVD_NUM_WEIGHTS && n_weights != WVD_NUM_WEIGHTS_DEEP) return WVD_EINVAL;
   int st = check_dims(c, h, w);
   if (st) return st;
-  *bytes = make_layout(c, h, w).total;
+  *bytes = make_layout(c, h, w, n_weights == WVD_NUM_WEIGHTS_DEEP).total;
   return WVD_OK;
 }
 
@@ -819,12 +841,12 @@ int wvd_prepare(int c, int h, int w, const void* const* weights, int n_weights, 
   if (weight_dtype != WVD_DTYPE_BF16 && weight_dtype != WVD_DTYPE_F32) return WVD_EINVAL;
   int st = check_dims(c, h, w);
   if (st) return st;
-  if (n_weights != WVD_NUM_WEIGHTS) return WVD_EINVAL;
+  if (n_weights != WVD_NUM_WEIGHTS && n_weights != WVD_NUM_WEIGHTS_DEEP) return WVD_EINVAL;
   for (int i = 0; i < n_weights; ++i)
     if (!weights[i]) return WVD_EINVAL;
   if (!aligned16(prepared)) return WVD_EINVAL;
-  Layout L = make_layout(c, h, w);
-  if ((int)L.items.size() != WVD_NUM_WEIGHTS) return WVD_EINVAL;
+  Layout L = make_layout(c, h, w, n_weights == WVD_NUM_WEIGHTS_DEEP);
+  if ((int)L.items.size() != n_weights) return WVD_EINVAL;
   if (prepared_bytes < L.total) return WVD_ENOSPACE;
   wvd_plan* p = new (std::nothrow) wvd_plan();
   if (!p) return WVD_EINVAL;
@@ -835,7 +857,7 @@ int wvd_prepare(int c, int h, int w, const void* const* weights, int n_weights, 
   p->prep = static_cast<unsigned char*>(prepared);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
-  for (int i = 0; i < WVD_NUM_WEIGHTS && e == hipSuccess; ++i) {
+  for (int i = 0; i < n_weights && e == hipSuccess; ++i) {
     const Item& it = L.items[i];
     const void* src = weights[i];
     void* dst = p->prep + it.off;
@@ -868,7 +890,7 @@ int wvd_prepare(int c, int h, int w, const void* const* weights, int n_weights, 
 int wvd_workspace_bytes(const wvd_plan* plan, int T, int frames_per_pass, size_t* bytes) {
   if (!plan_ok(plan) || !bytes || T < 1 || frames_per_pass < 1) return WVD_EINVAL;
   const int P = std::min(T, frames_per_pass);
-  *bytes = make_work(plan->c, plan->h, plan->w, P).total;
+  *bytes = make_work(plan->c, plan->h, plan->w, P, true, plan->L.nrb).total;
   return WVD_OK;
 }
 
@@ -887,7 +909,7 @@ int decode_impl(wvd_plan* plan, const void* z, int z_dtype, int T, int t_begin, 
                 void* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const int c = plan->c, h = plan->h, w = plan->w;
   const int P = std::min(T, frames_per_pass);
-  Work W = make_work(c, h, w, P, state == nullptr);
+  Work W = make_work(c, h, w, P, state == nullptr, plan->L.nrb);
   if (workspace_bytes < W.total) return WVD_ENOSPACE;
   const Layout& L = plan->L;
   Ctx cx;
@@ -901,7 +923,7 @@ int decode_impl(wvd_plan* plan, const void* z, int z_dtype, int T, int t_begin, 
   h16_t* X = cx.wsp<h16_t>(W.X);
   h16_t* Hb = cx.wsp<h16_t>(W.H);
   h16_t* Y = cx.wsp<h16_t>(W.Y);
-  h16_t* zt = cx.wsp<h16_t>(W.zt);
+  h16_t* const zt0 = cx.wsp<h16_t>(W.zt);
   const long long vbase = video_frames(t_begin);
   const int VT = (int)(video_frames((long long)t_begin + T) - vbase);
 
@@ -913,7 +935,16 @@ int decode_impl(wvd_plan* plan, const void* z, int z_dtype, int T, int t_begin, 
     const int nh0 = std::min(2, g0), nh1 = std::min(2, g1), nh2 = std::min(2, g2);
     // conv_in on the channels-last latents.
     cx.what = "latent_to_cl";
+    h16_t* zt = zt0;
     cx.run(4, 0, [&] { return launch_latent_to_cl(z, z_dtype, T, t0, F0, h * w, zt, cx.st); });
+    if (L.pre_w >= 0) {  // deep variant: the 48 -> 48 1x1x1 conv on the latents
+      h16_t* zp = cx.wsp<h16_t>(W.zp);
+      cx.what = "pre_conv";
+      cx.run(1, 2.0 * F0 * h * w * 48 * 48, [&] {
+        return launch_pre_conv(zt, F0 * h * w, cx.prep<float>(L.pre_w), cx.prep<float>(L.pre_b), zp, cx.st);
+      });
+      zt = zp;
+    }
     Act za{zt, 64, F0, h, w};
     Act x{X, c4, F0, h, w};
     {
@@ -937,30 +968,32 @@ int decode_impl(wvd_plan* plan, const void* z, int z_dtype, int T, int t_begin, 
     x = resblock(cx, L.mid0, x, Hb, nullptr, R_MID0_1, R_MID0_2, nh0);
     attention(cx, x);
     x = resblock(cx, L.mid1, x, Hb, nullptr, R_MID1_1, R_MID1_2, nh0);
+    const int nrb = L.nrb;
+    auto stage = [&](int s, int nh) {  // the stage's ResBlocks; the first may change the width
+      for (int k = 0; k < nrb; ++k)
+        x = resblock(cx, L.up[s][k], x, Hb, k == 0 && s >= 2 ? Y : nullptr, ring_up(nrb, s, k, 0),
+                     ring_up(nrb, s, k, 1), nh);
+    };
     // Stage 0 (h x w), time_conv, up-conv to 2h x 2w.
-    x = resblock(cx, L.up[0][0], x, Hb, nullptr, R_UP00_1, R_UP00_2, nh0);
-    x = resblock(cx, L.up[0][1], x, Hb, nullptr, R_UP01_1, R_UP01_2, nh0);
-    Act y = time_upsample(cx, 0, x, g0, Y, R_TC0);
+    stage(0, nh0);
+    Act y = time_upsample(cx, 0, x, g0, Y, ring_tc(nrb, 0));
     x = up_conv(cx, 0, y, X);
     // Stage 1 (2h x 2w).
-    x = resblock(cx, L.up[1][0], x, Hb, nullptr, R_UP10_1, R_UP10_2, nh1);
-    x = resblock(cx, L.up[1][1], x, Hb, nullptr, R_UP11_1, R_UP11_2, nh1);
-    y = time_upsample(cx, 1, x, g1, Y, R_TC1);
+    stage(1, nh1);
+    y = time_upsample(cx, 1, x, g1, Y, ring_tc(nrb, 1));
     x = up_conv(cx, 1, y, X);
     // Stage 2 (4h x 4w): 4c -> 2c.
-    x = resblock(cx, L.up[2][0], x, Hb, Y, R_UP20_1, R_UP20_2, nh2);
-    x = resblock(cx, L.up[2][1], x, Hb, nullptr, R_UP21_1, R_UP21_2, nh2);
+    stage(2, nh2);
     x = up_conv(cx, 2, x, X);
     // Stage 3 (8h x 8w): 2c -> c.
-    x = resblock(cx, L.up[3][0], x, Hb, Y, R_UP30_1, R_UP30_2, nh2);
-    x = resblock(cx, L.up[3][1], x, Hb, nullptr, R_UP31_1, R_UP31_2, nh2);
+    stage(3, nh2);
     // Head: RMSNorm + SiLU + conv c -> 12, pixel shuffle, clamp, NCTHW video.
     // With only 12 output channels the conv's halo staging would normalise
     // each voxel many times per output; the normalised input is written once
     // instead (into the free H buffer), and the head's history ring holds
     // normalised frames.
     {
-      h16_t* ring = cx.ring(R_HEAD);
+      h16_t* ring = cx.ring(ring_head(L.nrb));
       Act yn{Hb, x.C, x.F, x.H, x.W};
       cx.what = "norm_silu";
       cx.run(3, 0, [&] {
@@ -1003,13 +1036,13 @@ int wvd_decode(const wvd_plan* cplan, const void* z, int z_dtype, int T, int fra
 
 int wvd_state_bytes(const wvd_plan* plan, size_t* bytes) {
   if (!plan_ok(plan) || !bytes) return WVD_EINVAL;
-  *bytes = make_work(plan->c, plan->h, plan->w, 1, false).ring_bytes;
+  *bytes = make_work(plan->c, plan->h, plan->w, 1, false, plan->L.nrb).ring_bytes;
   return WVD_OK;
 }
 
 int wvd_chunk_workspace_bytes(const wvd_plan* plan, int T, int frames_per_pass, size_t* bytes) {
   if (!plan_ok(plan) || !bytes || T < 1 || frames_per_pass < 1) return WVD_EINVAL;
-  *bytes = make_work(plan->c, plan->h, plan->w, std::min(T, frames_per_pass), false).total;
+  *bytes = make_work(plan->c, plan->h, plan->w, std::min(T, frames_per_pass), false, plan->L.nrb).total;
   return WVD_OK;
 }
 

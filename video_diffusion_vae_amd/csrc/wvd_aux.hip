@@ -160,6 +160,37 @@ __global__ __launch_bounds__(256) void ring_update_kernel(h16_t* __restrict__ ri
   }
 }
 
+// Deep variant's 1x1x1 conv on the latents: zp[v][o] = b[o] + sum_i A[o][i]
+// zt[v][i] for the 48 latent channels (fp32 accumulation in channel order,
+// fp16 store); channels 48..63 of the 64-wide layout stay zero.  One thread
+// per (voxel, 8 output channels).
+__global__ __launch_bounds__(256) void pre_conv_kernel(const h16_t* __restrict__ zt, long long nvox,
+                                                       const float* __restrict__ A, const float* __restrict__ b,
+                                                       h16_t* __restrict__ zp) {
+  const long long n = nvox * 8;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+       e += (long long)gridDim.x * blockDim.x) {
+    const long long v = e >> 3;
+    const int og = (int)(e & 7);
+    uint4 r = make_uint4(0, 0, 0, 0);
+    if (og < 6) {
+      float f[48];
+#pragma unroll
+      for (int q = 0; q < 6; ++q) unpack8h(*reinterpret_cast<const uint4*>(zt + v * 64 + q * 8), f + q * 8);
+      float o[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int oc = og * 8 + k;
+        float acc = b[oc];
+        for (int i = 0; i < 48; ++i) acc += A[oc * 48 + i] * f[i];
+        o[k] = acc;
+      }
+      r = pack8h(o);
+    }
+    *reinterpret_cast<uint4*>(zp + v * 64 + og * 8) = r;
+  }
+}
+
 // z [48][T][HW] (bf16 or fp32) frames t0..t0+F-1 -> zt [F][HW][64] fp16
 // (channels 48..63 zero).
 __global__ __launch_bounds__(256) void latent_to_cl_kernel(const void* __restrict__ z, int dtype, int T, int t0,
@@ -853,6 +884,14 @@ hipError_t launch_ring_update(h16_t* ring, const h16_t* x, long long x_fstride, 
   const long long n = (long long)HW * (C / 8);
   hipLaunchKernelGGL(ring_update_kernel, dim3(grid_for(n, 256, 16384)), dim3(256), 0, s, ring, x, x_fstride, lda, C,
                      F, HW);
+  return hipGetLastError();
+}
+
+hipError_t launch_pre_conv(const h16_t* zt, long long nvox, const float* A, const float* b, h16_t* zp,
+                           hipStream_t s) {
+  if (g_dry_run) return hipSuccess;
+  if (!zt || !A || !b || !zp || nvox < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pre_conv_kernel, dim3(grid_for(nvox * 8)), dim3(256), 0, s, zt, nvox, A, b, zp);
   return hipGetLastError();
 }
 

@@ -119,6 +119,9 @@ hipError_t launch_norm_silu(const h16_t* x, long long x_fstride, int lda, int C,
                             h16_t* y, long long y_fstride, int ldy, hipStream_t s);
 hipError_t launch_ring_update(h16_t* ring, const h16_t* x, long long x_fstride, int lda, int C,
                               int F, int HW, hipStream_t s);
+// Deep variant: 48 -> 48 1x1x1 conv of the 64-wide channels-last latents.
+hipError_t launch_pre_conv(const h16_t* zt, long long nvox, const float* A, const float* b, h16_t* zp,
+                           hipStream_t s);
 hipError_t launch_latent_to_cl(const void* z, int dtype, int T, int t0, int F, int HW, h16_t* zt, hipStream_t s);
 hipError_t launch_copy16(void* dst, const void* src, size_t bytes, hipStream_t s);
 // Zero-fills bytes (a multiple of 16) with a kernel (no memset node).

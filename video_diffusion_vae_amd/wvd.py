@@ -20,6 +20,7 @@ WVD_ENOSPACE = -3
 WVD_EUNSUPPORTED = -4
 WVD_EHIP = -5
 NUM_WEIGHTS = 84
+NUM_WEIGHTS_DEEP = 110  # deep variant: pre_conv + three ResBlocks per up stage
 WVD_DTYPE_BF16 = 0
 WVD_DTYPE_F32 = 1
 PROFILE_CLASSES = ("conv3x3x3_main", "conv_other", "attention_gemm", "norm_stats", "copies", "wino_transforms")
@@ -43,6 +44,8 @@ def _load() -> ctypes.CDLL:
     i = ctypes.c_int
     lib.wvd_prepared_bytes.argtypes = [i, i, i, ctypes.POINTER(sz)]
     lib.wvd_prepared_bytes.restype = i
+    lib.wvd_prepared_bytes_n.argtypes = [i, i, i, i, ctypes.POINTER(sz)]
+    lib.wvd_prepared_bytes_n.restype = i
     lib.wvd_prepare.argtypes = [i, i, i, ctypes.POINTER(vp), i, i, vp, sz, vp, ctypes.POINTER(vp)]
     lib.wvd_prepare.restype = i
     lib.wvd_workspace_bytes.argtypes = [vp, i, i, ctypes.POINTER(sz)]
@@ -90,6 +93,12 @@ def _check(status: int, where: str) -> None:
 
 
 # ---- raw entry points (same names as the C ABI) ----
+
+def wvd_prepared_bytes_n(c: int, h: int, w: int, n_weights: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.wvd_prepared_bytes_n(c, h, w, n_weights, ctypes.byref(n)), "wvd_prepared_bytes_n")
+    return n.value
+
 
 def wvd_prepared_bytes(c: int, h: int, w: int) -> int:
     n = ctypes.c_size_t(0)
@@ -183,14 +192,14 @@ class Decoder:
         self.c, self.h, self.w = int(c), int(h), int(w)
         self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
         ws = list(weights.values()) if isinstance(weights, dict) else list(weights)
-        if len(ws) != NUM_WEIGHTS:
-            raise WvdError(WVD_EINVAL, f"Decoder: expected {NUM_WEIGHTS} weights, got {len(ws)}")
+        if len(ws) not in (NUM_WEIGHTS, NUM_WEIGHTS_DEEP):
+            raise WvdError(WVD_EINVAL, f"Decoder: expected {NUM_WEIGHTS} or {NUM_WEIGHTS_DEEP} weights, got {len(ws)}")
         ts = [torch.as_tensor(t) for t in ws]
         f32 = all(t.dtype == torch.float32 for t in ts)
         dt = torch.float32 if f32 else torch.bfloat16
         self.weight_dtype = WVD_DTYPE_F32 if f32 else WVD_DTYPE_BF16
         dev_ws = [t.to(device=self.device, dtype=dt).contiguous() for t in ts]
-        nbytes = wvd_prepared_bytes(self.c, self.h, self.w)
+        nbytes = wvd_prepared_bytes_n(self.c, self.h, self.w, len(ws))
         self.prepared = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         stream = torch.cuda.current_stream(self.device)
         self.plan = wvd_prepare(self.c, self.h, self.w, [t.data_ptr() for t in dev_ws], self.weight_dtype,
