@@ -244,10 +244,10 @@ def main():
                    "video": list(cfg.video_shape), "frames_per_pass": P, "c": cfg.c},
         "roofline": {"bound": "mfma", "achieved": conv_tflops, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": conv_tflops / MFMA_PEAK_TFLOPS, "traffic": measured_traffic(),
-                     "kernel": "conv_persist<256, 2, 4, 0, 4, 16|8>: Winograd-domain GEMM of the norm-SiLU "
+                     "kernel": "conv_persist<256, 2, 4, 0, 4, *>: Winograd-domain GEMM of the norm-SiLU "
                                "3x3x3 convs (F(4,3) along x, six xi planes, causal (t,y) 3x3 taps), 256x256 "
-                               "tiles (16 column groups x 8 rows, or 8 x 16 at the two small levels) on 4 "
-                               "waves, one persistent workgroup per CU",
+                               "tiles of frames x rows x column groups (2x8x16 up to 8x8x4, chosen per "
+                               "launch) on 4 waves, one persistent workgroup per CU; all tile shapes together",
                      "flops": "algorithmic: the direct 3x3x3 convolution FLOPs of the launches; the kernel "
                               "performs half as many multiply-adds (F(4,3))",
                      "executed_mfma_tflops": exec_tflops, "executed_mfma_frac": exec_tflops / MFMA_PEAK_TFLOPS,
