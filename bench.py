@@ -26,9 +26,9 @@ MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 MFMA
 HBM_PEAK_GBS = 8000.0
 CONV_SRC = os.path.join(ROOT, "video_diffusion_vae_amd", "csrc", "wvd_conv.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv3x3x3_main_c256_T49_704x1248_traffic.json")
-# Direct 3x3x3 multiply-adds per Winograd-domain multiply-add: F(4,3) along x
-# replaces 4 outputs x 27 taps by 6 planes x 9 (t, y) taps.
-WINO_DIRECT_PER_EXECUTED = (4 * 27) / (6 * 9)
+# Direct 3x3x3 multiply-adds per Winograd-domain multiply-add: F(6,3) along x
+# replaces 6 outputs x 27 taps by 8 planes x 9 (t, y) taps.
+WINO_DIRECT_PER_EXECUTED = (6 * 27) / (8 * 9)
 
 
 def conv_src_hash() -> str:
@@ -245,11 +245,11 @@ def main():
         "roofline": {"bound": "mfma", "achieved": conv_tflops, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": conv_tflops / MFMA_PEAK_TFLOPS, "traffic": measured_traffic(),
                      "kernel": "conv_persist<256, 2, 4, 0, 4, *>: Winograd-domain GEMM of the norm-SiLU "
-                               "3x3x3 convs (F(4,3) along x, six xi planes, causal (t,y) 3x3 taps), 256x256 "
+                               "3x3x3 convs (F(6,3) along x, eight xi planes, causal (t,y) 3x3 taps), 256x256 "
                                "tiles of frames x rows x column groups (2x8x16 up to 8x8x4, chosen per "
                                "launch) on 4 waves, one persistent workgroup per CU; all tile shapes together",
                      "flops": "algorithmic: the direct 3x3x3 convolution FLOPs of the launches; the kernel "
-                              "performs half as many multiply-adds (F(4,3))",
+                              "performs 4/9 as many multiply-adds (F(6,3))",
                      "executed_mfma_tflops": exec_tflops, "executed_mfma_frac": exec_tflops / MFMA_PEAK_TFLOPS,
                      "avg_launch_ms": avg_launch_ms, "avg_launch_tflop": avg_launch_flops / 1e12,
                      "launches_per_step": conv["launches"] / args.steps},

@@ -47,10 +47,11 @@ def test_prepared_bytes_validation(wvd):
     n64 = wvd.wvd_prepared_bytes(64, 22, 39)
     assert 0 < n16 < n64
     # 424M parameters as fp16 (0.85 GB), the phase-form up-convs at 16/9 of
-    # their 3x3 size, and the ResBlock convs held in Winograd form: F(4,3)
-    # along x keeps 6 planes x 9 (t, y) taps = 2x their 27 taps.
+    # their 3x3 size, and the ResBlock convs (383M parameters) held in
+    # Winograd form: F(6,3) along x keeps 8 planes x 9 (t, y) taps = 8/3 of
+    # their 27 taps (2.16 GB in all).
     n256 = wvd.wvd_prepared_bytes(256, 44, 78)
-    assert 0.8e9 < n256 < 2.0e9
+    assert 2.0e9 < n256 < 2.4e9
     for bad in ((0, 4, 6), (24, 4, 6), (512, 4, 6), (16, 0, 6), (16, 4, 5000)):
         with pytest.raises(wvd.WvdError) as e:
             wvd.wvd_prepared_bytes(*bad)

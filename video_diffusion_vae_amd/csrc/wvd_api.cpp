@@ -30,7 +30,7 @@ enum ItemKind { K_CONV = 0, K_PHASE = 1, K_VEC = 2, K_WINO = 3 };
 #endif
 
 // A 3x3x3 norm-SiLU conv runs in Winograd form (F(kWinoM,3) along x: input
-// transform, four xi-plane GEMMs on the persistent kernel, output transform)
+// transform, kWinoN xi-plane GEMMs on the persistent kernel, output transform)
 // when its widths suit the 256-wide persistent tiles and 32-channel chunks.
 bool wino_ok(int cin, int cout) { return WVD_WINO && cin % 32 == 0 && cout % 256 == 0; }
 
@@ -511,9 +511,10 @@ WinoShape wino_tile_shape(int F, int H, int WQ, int Cout) {
 //       valid history frames (the transform computes the norm statistics),
 //   M[xi] = causal (t, y) 3x3 conv of U[xi] with the transformed weights,
 //   out = output transform of M + bias (+ res).
-// Same function as conv333 + EPI_H16, with half of the multiply-adds (F(4,3)).
+// Same function as conv333 + EPI_H16, with 4/9 of the multiply-adds (F(6,3):
+// 8 planes x 9 (t, y) taps for 6 outputs x 27 taps).
 // The Winograd GEMM over the U planes the input transform (or the fused
-// transform) left for input x: M = the six planes of products.
+// transform) left for input x: M = the kWinoN planes of products.
 void wino_gemm(Ctx& cx, const Act& x, int nh, int w_item, int Cout) {
   const int W2 = (x.W + kWinoM - 1) / kWinoM;  // column groups
   h16_t* U = cx.wsp<h16_t>(cx.W->U);

@@ -5,6 +5,13 @@
 
 namespace wvd {
 
+// No implicit multiply-add fusion in this file: a value that two kernels
+// compute (a voxel's norm statistic, the Winograd input transform of a
+// history frame and of the same frame inside a pass) must round the same
+// way in both, whatever the surrounding code lets the compiler fuse.  The
+// fused multiply-adds are written out (fmaf) where they are meant.
+#pragma clang fp contract(off)
+
 bool g_dry_run = false;
 
 namespace {
@@ -64,7 +71,7 @@ __global__ __launch_bounds__(256) void rms_stats_kernel(const h16_t* __restrict_
         unpack8h(r[u][q], f);
         float t = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) t += f[k] * f[k];
+        for (int k = 0; k < 8; ++k) t = fmaf(f[k], f[k], t);
         ss += t;
       }
       for (int off = 1; off < G; off <<= 1) ss += __shfl_xor(ss, off, 64);
@@ -117,7 +124,7 @@ __global__ __launch_bounds__(256) void norm_silu_kernel(const h16_t* __restrict_
         unpack8h(r[u][q], f);
         float t = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) t += f[k] * f[k];
+        for (int k = 0; k < 8; ++k) t = fmaf(f[k], f[k], t);
         ss += t;
       }
       for (int off = 1; off < G; off <<= 1) ss += __shfl_xor(ss, off, 64);
@@ -389,6 +396,54 @@ struct Wino<4> {
   }
 };
 
+// F(6,3): interpolation points 0, 1, -1, 1/2, -1/2, 2, -2 and infinity
+// (Toom-Cook).  Eight inputs d_k = x[6q-1+k] give six outputs x[6q..6q+5].
+// The rows of G are scaled so that V has the magnitude of the taps (fp16
+// weights stay out of the subnormal range), the matching factors 2/9, 32/45
+// and 2/45 sit in the output transform, and the input transform keeps
+// dyadic coefficients (exact in fp32).
+template <>
+struct Wino<6> {
+  static constexpr int N = 8;
+  __device__ static void weights(float g0, float g1, float g2, float* v) {
+    v[0] = g0;
+    v[1] = -(g0 + g1 + g2);
+    v[2] = -(g0 - g1 + g2);
+    v[3] = g0 + 0.5f * g1 + 0.25f * g2;
+    v[4] = g0 - 0.5f * g1 + 0.25f * g2;
+    v[5] = 0.25f * g0 + 0.5f * g1 + g2;
+    v[6] = 0.25f * g0 - 0.5f * g1 + g2;
+    v[7] = g2;
+  }
+  __device__ static void input(const float* d, float* u) {
+    u[0] = fmaf(5.25f, d[4] - d[2], d[0] - d[6]);
+    const float t1 = fmaf(-4.25f, d[4], d[2] + d[6]), t2 = fmaf(-4.25f, d[3], d[1] + d[5]);
+    u[1] = t1 + t2;
+    u[2] = t1 - t2;
+    const float t3 = fmaf(-5.0f, d[4], fmaf(4.0f, d[2], d[6]));
+    const float t4 = fmaf(0.5f, d[5], fmaf(-2.5f, d[3], 2.0f * d[1]));
+    u[3] = t3 + t4;
+    u[4] = t3 - t4;
+    const float t5 = fmaf(-1.25f, d[4], fmaf(0.25f, d[2], d[6]));
+    const float t6 = fmaf(2.0f, d[5], fmaf(-2.5f, d[3], 0.5f * d[1]));
+    u[5] = t5 + t6;
+    u[6] = t5 - t6;
+    u[7] = fmaf(5.25f, d[3] - d[5], d[7] - d[1]);
+  }
+  __device__ static void output(const float* m, float* o) {
+    constexpr float k29 = 2.0f / 9.0f, k45 = 1.0f / 45.0f;
+    const float a = k29 * (m[1] + m[2]), b = k29 * (m[1] - m[2]);
+    const float c = k45 * (m[3] + m[4]), d = k45 * (m[3] - m[4]);
+    const float e = k45 * (m[5] + m[6]), f = k45 * (m[5] - m[6]);
+    o[0] = m[0] + a + 32.0f * c + 2.0f * e;
+    o[1] = b + 16.0f * d + 4.0f * f;
+    o[2] = a + 8.0f * c + 8.0f * e;
+    o[3] = b + 4.0f * d + 16.0f * f;
+    o[4] = a + 2.0f * c + 32.0f * e;
+    o[5] = b + d + 64.0f * f + m[7];
+  }
+};
+
 // Winograd weights of a 3x3x3 conv: for each (o, i, dt, dy) the x taps
 // g0..g2 become V = G g (fp32, rounded once to fp16), in fragment order with
 // tap = xi * 9 + dt * 3 + dy.
@@ -460,7 +515,7 @@ __device__ __forceinline__ void act_column(const uint4 (&v)[NG], bool in, int G,
   for (int h = 0; h < NG; ++h) {
     float t = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) t += f[h][k] * f[h][k];
+    for (int k = 0; k < 8; ++k) t = fmaf(f[h][k], f[h][k], t);
     ss += t;
   }
   ss = lane_group_sum(ss, G);
@@ -480,8 +535,8 @@ __device__ __forceinline__ void act_column(const uint4 (&v)[NG], bool in, int G,
 // sub + G (when C / 8 > G).  Each column is loaded once: the lanes sum the
 // squares of their channels, a reduction over the G lanes gives the voxel's
 // 1/||x|| (the formula of rms_stats_kernel), and SiLU(x * rs *
-// gamma) of the column enters a six-column window that slides by four per
-// column group.  History slots (from the ring) and pass frames go through the
+// gamma) of the column enters a window of Wino<kWinoM>::N columns that
+// slides by kWinoM per column group.  History slots (from the ring) and pass frames go through the
 // same code, so a voxel's activation does not depend on which pass holds it.
 template <int NG>  // 8-channel groups per lane: 1 (C <= 512) or 2
 __global__ __launch_bounds__(256) void wino_in_kernel(const h16_t* __restrict__ x, long long x_fstride, int lda,
@@ -579,10 +634,10 @@ __global__ __launch_bounds__(256) void wino_in_kernel(const h16_t* __restrict__ 
 }
 
 // Output transform of one conv fused with the input transform of the next
-// (conv1 -> conv2 of a ResBlock): from the six planes of conv1's products,
+// (conv1 -> conv2 of a ResBlock): from the planes of conv1's products,
 // a run of kWinoInRun column groups gets h = A^T M + bias rounded to fp16
 // (exactly the values the unfused path would store), each column is
-// activated once through act_column, and the six-column window of conv2's
+// activated once through act_column, and the column window of conv2's
 // input transform slides over them.  The window's outer columns come from
 // the neighbouring groups (the last column of group q0 - 1, the first of
 // q0 + R), so a run reads R + 2 groups of products.  h itself is written only
@@ -632,7 +687,7 @@ __global__ __launch_bounds__(256) void wino_mid_kernel(const h16_t* __restrict__
     const long long r = ee / QB;
     const int row = (int)(r % H);
     const int f = (int)(r / H);
-    // h (fp16, as stored) of the four columns of group q; zero outside
+    // h (fp16, as stored) of the kWinoM columns of group q; zero outside
     auto group = [&](int q, uint4 (&hv)[WM][NG]) {
       const bool valid = ok && q >= 0 && q < WQ;
       uint4 mr[NX][NG];
@@ -817,7 +872,7 @@ __global__ __launch_bounds__(256) void wino_out_kernel(const h16_t* __restrict__
         unpack8h(packed, h);
         float t = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) t += h[k] * h[k];
+        for (int k = 0; k < 8; ++k) t = fmaf(h[k], h[k], t);
         ss[e2] += t;
       }
     }

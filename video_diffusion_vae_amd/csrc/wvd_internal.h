@@ -14,7 +14,7 @@ constexpr int kTileM = 256;
 constexpr int kMaxHaloItemsPerTap = 4;  // 16-byte halo items per thread per tap
 constexpr int kMaxCin = 1024;           // largest norm input width kept in LDS
 constexpr int kWinoTF = 2;              // frames per tile of the Winograd-domain GEMM
-constexpr int kWinoM = 4;               // Winograd F(m,3) along x: output columns per group
+constexpr int kWinoM = 6;               // Winograd F(m,3) along x: output columns per group
 constexpr int kWinoN = kWinoM + 2;      // transformed planes (xi) per group
 constexpr int kWinoInRun = 4;           // column groups per thread of the input transform
 // LDS bytes the Winograd and up-conv epilogues stage in one halo buffer:
