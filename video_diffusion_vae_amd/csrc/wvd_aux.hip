@@ -581,28 +581,43 @@ __global__ __launch_bounds__(256) void wino_in_kernel(const h16_t* __restrict__ 
     const long long ld = slot < 2 ? C : lda;
     // SiLU(x * rs * gamma) of column `col` for this lane's channels (zero
     // outside the row); every lane of the group runs it (butterfly)
-    auto act = [&](int col, float (&y)[NG][8]) {
-      const bool in = ok && col >= 0 && col < W;
-      uint4 v[NG];
+    // raw channels of column `col` (zero outside the row)
+    auto load_col = [&](int col, uint4 (&v)[NG]) {
 #pragma unroll
       for (int h = 0; h < NG; ++h) v[h] = make_uint4(0, 0, 0, 0);
-      if (in) {
+      if (ok && col >= 0 && col < W) {
         const h16_t* p = src_row + (long long)col * ld;
         v[0] = *reinterpret_cast<const uint4*>(p + sub * 8);
         if (second) v[NG - 1] = *reinterpret_cast<const uint4*>(p + (sub + G) * 8);
       }
-      act_column<NG>(v, in, G, gm, y);
     };
+    auto in_row = [&](int col) { return ok && col >= 0 && col < W; };
     float y[NX][NG][8];
     const int q0 = qb * R;
+    {
+      uint4 v[NX - WM][NG];
 #pragma unroll
-    for (int k = 0; k < NX - WM; ++k) act(WM * q0 - 1 + k, y[k]);
+      for (int k = 0; k < NX - WM; ++k) load_col(WM * q0 - 1 + k, v[k]);
+#pragma unroll
+      for (int k = 0; k < NX - WM; ++k) act_column<NG>(v[k], in_row(WM * q0 - 1 + k), G, gm, y[k]);
+    }
+    // the columns a group adds to the window, loaded one group ahead so
+    // the loads are in flight while the previous group is transformed
+    uint4 raw[WM][NG];
+#pragma unroll
+    for (int k = 0; k < WM; ++k) load_col(WM * q0 + (NX - WM) - 1 + k, raw[k]);
     h16_t* dst = U + ((long long)slot * H * WQ + (long long)row * WQ + q0) * C;
 #pragma unroll
     for (int qq = 0; qq < R; ++qq) {
-      if (q0 + qq >= WQ) break;  // uniform over the lane group
+      const int q = q0 + qq;
+      if (q >= WQ) break;  // uniform over the lane group
 #pragma unroll
-      for (int k = NX - WM; k < NX; ++k) act(WM * (q0 + qq) - 1 + k, y[k]);
+      for (int k = 0; k < WM; ++k)
+        act_column<NG>(raw[k], in_row(WM * q + (NX - WM) - 1 + k), G, gm, y[NX - WM + k]);
+      if (qq + 1 < R) {
+#pragma unroll
+        for (int k = 0; k < WM; ++k) load_col(WM * (q + 1) + (NX - WM) - 1 + k, raw[k]);
+      }
 #pragma unroll
       for (int h = 0; h < NG; ++h) {
         if (h == 1 && !second) break;
@@ -687,10 +702,9 @@ __global__ __launch_bounds__(256) void wino_mid_kernel(const h16_t* __restrict__
     const long long r = ee / QB;
     const int row = (int)(r % H);
     const int f = (int)(r / H);
-    // h (fp16, as stored) of the kWinoM columns of group q; zero outside
-    auto group = [&](int q, uint4 (&hv)[WM][NG]) {
+    // raw products of group q (zero outside)
+    auto load_group = [&](int q, uint4 (&mr)[NX][NG]) {
       const bool valid = ok && q >= 0 && q < WQ;
-      uint4 mr[NX][NG];
 #pragma unroll
       for (int k = 0; k < NX; ++k)
 #pragma unroll
@@ -700,6 +714,10 @@ __global__ __launch_bounds__(256) void wino_mid_kernel(const h16_t* __restrict__
             mr[k][h] = *reinterpret_cast<const uint4*>(M + k * mplane + (((long long)f * H + row) * WQ + q) * C +
                                                        (sub + h * G) * 8);
         }
+    };
+    // h (fp16, as stored) of the kWinoM columns of group q; zero outside
+    auto finish_group = [&](int q, const uint4 (&mr)[NX][NG], uint4 (&hv)[WM][NG]) {
+      const bool valid = ok && q >= 0 && q < WQ;
 #pragma unroll
       for (int h = 0; h < NG; ++h) {
         float m[NX][8];
@@ -728,12 +746,16 @@ __global__ __launch_bounds__(256) void wino_mid_kernel(const h16_t* __restrict__
     float y[NX][NG][8];
     float yn[NG][8];  // activation of the next group's first column
     uint4 nxt[WM][NG];
+    uint4 mr[NX][NG];  // products of the group after next, loaded one group ahead
     {
       uint4 prev[WM][NG];
-      group(q0 - 1, prev);
+      load_group(q0 - 1, mr);
+      finish_group(q0 - 1, mr, prev);
       act_column<NG>(prev[WM - 1], ok && q0 > 0, G, gm, y[0]);
     }
-    group(q0, nxt);
+    load_group(q0, mr);
+    finish_group(q0, mr, nxt);
+    load_group(q0 + 1, mr);
     act_column<NG>(nxt[0], ok, G, gm, yn);
 #pragma unroll
     for (int qq = 0; qq < R; ++qq) {
@@ -759,7 +781,8 @@ __global__ __launch_bounds__(256) void wino_mid_kernel(const h16_t* __restrict__
         for (int c = 0; c < 8; ++c) y[1][h][c] = yn[h][c];
 #pragma unroll
       for (int e2 = 1; e2 < WM; ++e2) act_column<NG>(cur[e2], ok && WM * q + e2 < W, G, gm, y[1 + e2]);
-      group(q + 1, nxt);
+      finish_group(q + 1, mr, nxt);
+      if (qq + 1 < R) load_group(q + 2, mr);
       act_column<NG>(nxt[0], ok && q + 1 < WQ, G, gm, yn);
 #pragma unroll
       for (int h = 0; h < NG; ++h)
