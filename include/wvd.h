@@ -168,7 +168,7 @@ long long wvd_last_launch_count(const wvd_plan* plan);
  * launch).  wvd_profile_read synchronises on the last recorded event and
  * returns, per kernel class, the summed milliseconds, the summed FLOPs (2 per
  * multiply-add each launch performs: for the Winograd-domain GEMMs that is
- * 1/2 of the direct 3x3x3 count) and the number of launches since the
+ * 4/9 of the direct 3x3x3 count, F(6,3) along x) and the number of launches since the
  * previous read, then clears the record.
  * Classes: 0 the dominant conv kernel (the Winograd-domain GEMM of the
  * norm-SiLU 3x3x3 convs; the direct 3x3x3 kernel for widths it does not

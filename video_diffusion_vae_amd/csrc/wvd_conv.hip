@@ -827,7 +827,7 @@ __device__ __forceinline__ TileGeo tile_geo(const ConvArgs& a, int logical) {
   constexpr int TH = MODE == 2 ? 16 : (MODE == 4 ? kTileM / TW / TF4 : kTH333);
   // Output positions vary fastest: the tiles running together on an XCD
   // share one (phase, channel block) of weights in its L2 and neighbouring
-  // halos (interleaving the phases made them stream six weight sets).
+  // halos (interleaving the phases made them stream one weight set per phase).
   const int nN = (a.Cout + BN - 1) / BN;
   const int nMt = a.tiles_x * a.tiles_y * a.tiles_f;
   const int mt = logical % nMt;
