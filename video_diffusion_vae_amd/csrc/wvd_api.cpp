@@ -601,11 +601,16 @@ Act resblock(Ctx& cx, const RB& rb, const Act& x, h16_t* hbuf, h16_t* obuf, int 
       return launch_wino_in(h.p, h.fstride(), h.C, r2, nh, h.C, h.F, h.H, h.W, cx.prep<float>(rb.norm2),
                             cx.wsp<h16_t>(cx.W->U), cx.st, true);
     });
+    // With two or more frames in the pass the last two are exactly the next
+    // pass's history: they go straight into the ring (slots 0, 1); a
+    // one-frame pass stores its frame in h and shifts the ring below.
+    const int tail = std::max(0, x.F - 2);
     cx.what = "wino_mid";
     cx.run(5, 0, [&] {
       return launch_wino_mid(cx.wsp<h16_t>(cx.W->M), cx.prep<float>(rb.conv1b), rb.cout, x.F, x.H, x.W,
-                             cx.prep<float>(rb.norm2), cx.wsp<h16_t>(cx.W->U), h.p, h.fstride(), h.C,
-                             std::max(0, x.F - 2), cx.st);
+                             cx.prep<float>(rb.norm2), cx.wsp<h16_t>(cx.W->U), x.F >= 2 ? r2 : h.p,
+                             x.F >= 2 ? (long long)x.H * x.W * h.C : h.fstride(), h.C, tail, x.F >= 2 ? tail : 0,
+                             cx.st);
     });
     cx.rs_tensor = nullptr;
   } else if (rb.wino1) {
@@ -678,7 +683,7 @@ Act resblock(Ctx& cx, const RB& rb, const Act& x, h16_t* hbuf, h16_t* obuf, int 
     set_grid(a, x.F, x.H, x.W, tf_for(3, x.F));
     conv(cx, a, 0);
   }
-  ring_update(cx, r2, h);
+  if (!(fused && x.F >= 2)) ring_update(cx, r2, h);
   return out;
 }
 

@@ -656,13 +656,14 @@ __global__ __launch_bounds__(256) void wino_in_kernel(const h16_t* __restrict__ 
 // input transform slides over them.  The window's outer columns come from
 // the neighbouring groups (the last column of group q0 - 1, the first of
 // q0 + R), so a run reads R + 2 groups of products.  h itself is written only
-// for frames >= tail_from (the frames the next pass reads as history).
+// for frames >= tail_from (the frames the next pass reads as history), frame
+// f at hout + (f - h_first) * h_fstride.
 template <int NG>
 __global__ __launch_bounds__(256) void wino_mid_kernel(const h16_t* __restrict__ M, const float* __restrict__ bias,
                                                        int C, int F, int H, int W, int WQ, int G,
                                                        const float* __restrict__ gamma, h16_t* __restrict__ U,
                                                        h16_t* __restrict__ hout, long long h_fstride, int ldh,
-                                                       int tail_from) {
+                                                       int tail_from, int h_first) {
   constexpr int WM = kWinoM, NX = Wino<WM>::N, R = kWinoInRun;
   const int lane = threadIdx.x & 63;
   const int sub = lane % G;
@@ -772,7 +773,7 @@ __global__ __launch_bounds__(256) void wino_mid_kernel(const h16_t* __restrict__
 #pragma unroll
           for (int h = 0; h < NG; ++h)
             if (WM * q + e2 < W && (h == 0 || second))
-              *reinterpret_cast<uint4*>(hout + f * h_fstride + ((long long)row * W + WM * q + e2) * ldh +
+              *reinterpret_cast<uint4*>(hout + (f - h_first) * h_fstride + ((long long)row * W + WM * q + e2) * ldh +
                                         (sub + h * G) * 8) = cur[e2][h];
       }
 #pragma unroll
@@ -1058,7 +1059,8 @@ hipError_t launch_wino_in(const h16_t* x, long long x_fstride, int lda, const h1
 bool wino_mid_ok(int C) { return C % 8 == 0 && C <= 512; }
 
 hipError_t launch_wino_mid(const h16_t* M, const float* bias, int C, int F, int H, int W, const float* gamma,
-                           h16_t* U, h16_t* hout, long long h_fstride, int ldh, int tail_from, hipStream_t s) {
+                           h16_t* U, h16_t* hout, long long h_fstride, int ldh, int tail_from, int h_first,
+                           hipStream_t s) {
   if (g_dry_run) return hipSuccess;
   if (!wino_mid_ok(C) || F < 1 || ldh % 8 || ldh < C) return hipErrorInvalidValue;
   const int WQ = (W + kWinoM - 1) / kWinoM;
@@ -1067,7 +1069,7 @@ hipError_t launch_wino_mid(const h16_t* M, const float* bias, int C, int F, int 
   const long long runs = (long long)F * H * ((WQ + kWinoInRun - 1) / kWinoInRun);
   const long long threads = (runs + 64 / G - 1) / (64 / G) * 64;
   hipLaunchKernelGGL(wino_mid_kernel<1>, dim3(grid_for(threads, 256, 65536)), dim3(256), 0, s, M, bias, C, F, H, W,
-                     WQ, G, gamma, U, hout, h_fstride, ldh, tail_from);
+                     WQ, G, gamma, U, hout, h_fstride, ldh, tail_from, h_first);
   return hipGetLastError();
 }
 

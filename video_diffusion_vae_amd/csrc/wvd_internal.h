@@ -161,7 +161,8 @@ bool wino_mid_ok(int C);
 // Tile shapes (TF frames x TW column groups) of the Winograd-domain GEMM.
 bool wino_tile_shape_ok(int TF, int TW);
 hipError_t launch_wino_mid(const h16_t* M, const float* bias, int C, int F, int H, int W, const float* gamma,
-                           h16_t* U, h16_t* hout, long long h_fstride, int ldh, int tail_from, hipStream_t s);
+                           h16_t* U, h16_t* hout, long long h_fstride, int ldh, int tail_from, int h_first,
+                           hipStream_t s);
 // Output transform: out[f][row][mq + j] = (A^T M)[j] + bias (+ res), with
 // M = [kWinoN][F][H][WQ][Cout] fp16; out may alias res.
 // With rs != null also writes rs[2+f][row][col] = 1/||out voxel|| exactly as
