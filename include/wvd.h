@@ -8,14 +8,17 @@
  * same page, "Use": the decoder prepares the weights once and its raw entry
  * points are destination-passing on the current stream); decoding writes into
  * a caller-owned bf16 video buffer on the caller's stream.  Arithmetic: the
- * pages' kernel keeps bf16 weights and activations with fp32 accumulation and
- * fp32 RMS-norm statistics (same page, "Limits"); this library keeps the same
- * 2-byte storage and MFMA operand width but in fp16 (which gfx950 multiplies
- * at the bf16 rate and into which every bf16 weight of normal range converts
- * exactly), with fp32 accumulation and fp32 norm statistics; values beyond
- * the fp16 range saturate.  frames_per_pass latent frames are carried through the
- * whole decoder per pass; it trades memory for speed and leaves the video
- * bit-identical (same page, "Performance and memory").
+ * pages' kernel stores weights and activations in two-byte bf16 and keeps its
+ * sums and norm statistics in fp32 (same page, "Limits"); this library keeps
+ * the two-byte storage and MFMA operand width but in fp16 (which gfx950
+ * multiplies at the bf16 rate and into which every bf16 weight of normal
+ * range converts exactly), with fp32 accumulation and fp32 norm statistics.
+ * A stored value beyond the fp16 range saturates to +-65504 and a NaN is
+ * stored as NaN; both are recorded in the device's range flags
+ * (wvd_range_flags).  Each pass carries frames_per_pass latent frames through
+ * the whole decoder: a larger value needs more workspace and runs faster, and
+ * the video is bit-identical for every value (same page, "Performance and
+ * memory").
  *
  * Memory ownership: the caller owns every device buffer (weights, prepared
  * buffer, workspace, latents, video).  A plan refers to the prepared buffer
@@ -152,6 +155,27 @@ const char* wvd_status_string(int status);
 /* Text naming the launch and HIP error behind the last WVD_EHIP returned on
  * the calling thread ("" if none).  Valid until the next call on the thread. */
 const char* wvd_last_error(void);
+
+/* Range events of the values stored as fp16 on the current device since the
+ * last clear, by every decode on that device: *flags gets bit 0
+ * (WVD_RANGE_SATURATED) when a finite value beyond +-65504 was stored
+ * (saturated there) and bit 1 (WVD_RANGE_NAN) when a NaN was stored; 0 for a
+ * decode whose every stored value was in range.  Waits for the work enqueued
+ * on `stream`; with clear != 0 then resets the flags.  The flags are shared by
+ * all plans and streams of the device: read them when no other decode on it
+ * is in flight.  WVD_EINVAL on a null `flags`; in dry-run mode *flags = 0. */
+#define WVD_RANGE_SATURATED 1u
+#define WVD_RANGE_NAN 2u
+int wvd_range_flags(void* stream, int clear, unsigned int* flags);
+
+/* Math self-test: for n fp32 inputs x (device, n <= 2^31) writes the SiLU
+ * (t / (1 + e^-t)) and the exponential e^t exactly as the decoder's kernels
+ * evaluate them (the hardware exp2 and reciprocal; the norm-SiLU issue,
+ * "Prototype evidence and limits", asks that such fast exp/sqrt lowering be
+ * reviewed) into silu_out and exp_out (device, n floats each), on `stream`.
+ * A test bounds their error against an exact reference over the input ranges
+ * the decoder feeds them.  WVD_EINVAL on null buffers or a bad n. */
+int wvd_math_probe(const float* x, float* silu_out, float* exp_out, long long n, void* stream);
 
 /* Host-validation mode for testing without a GPU: with on != 0, every entry
  * point validates its arguments and walks the full launch schedule (all

@@ -12,10 +12,10 @@ the layout [frames, height, width, channels].
 
 Sources: the Wan2.2 VAE decoder page (FastVideo "wan22_vae_decode" README)
 fixes the input/output law (latents [1,48,T,h,w] -> video [1,3,4T-3,16h,16w],
-introduction), the numerics (bf16 weights and activations, fp32 accumulation
-and fp32 RMS-norm statistics, "Limits"), frame chunking that leaves the video
-unchanged ("Performance and memory") and every output in [-1, 1]
-("Correctness").  The TensorRT-LLM issue "Opt-in BF16 norm-SiLU fusion for Wan
+introduction), the numerics (two-byte bf16 storage, with sums and the norm's
+statistics kept in fp32; "Limits"), that cutting the clip into passes does
+not change the video ("Performance and memory") and that every output lies
+in [-1, 1] ("Correctness").  The TensorRT-LLM issue "Opt-in BF16 norm-SiLU fusion for Wan
 VAE decoding" (description) names the decoder's residual norm1/norm2 and
 norm_out as channel normalization + affine scale + SiLU, and its temporal
 caching.  The layer list itself (see synth.weight_specs) and the readings
@@ -243,7 +243,7 @@ def decode(z: np.ndarray, W: Dict[str, np.ndarray], c: int,
     frames_per_pass=None decodes the whole clip at once; otherwise the clip is
     cut into chunks of that many latent frames and every temporal conv carries
     its last two input frames from chunk to chunk (the pages' frames_per_pass,
-    which leaves the video unchanged).
+    whose value must not change the video).
     """
     assert z.ndim == 5 and z.shape[0] == 1 and z.shape[1] == 48
     T = z.shape[2]

@@ -75,6 +75,14 @@ def decoder_for(cfg: synth.Config, seed: int):
     return _decoders[key]
 
 
+def assert_range_clean() -> None:
+    """Every value the decodes since the last check stored as fp16 was finite
+    and inside the fp16 range (the library's device range flags are 0)."""
+    from video_diffusion_vae_amd import wvd
+    flags = wvd.range_flags(clear=True)
+    assert flags == 0, f"fp16 range flags {flags:#x} (1: saturated, 2: NaN)"
+
+
 def decode_gpu(cfg: synth.Config, seed: int = 0, frames_per_pass: int = 1, T: Optional[int] = None) -> np.ndarray:
     import torch
     T = cfg.T if T is None else T
@@ -85,6 +93,7 @@ def decode_gpu(cfg: synth.Config, seed: int = 0, frames_per_pass: int = 1, T: Op
         zt = zt.to(torch.bfloat16)
     out = dec.decode(zt, frames_per_pass=frames_per_pass)
     torch.cuda.synchronize()
+    assert_range_clean()
     return out.float().cpu().numpy()
 
 
@@ -104,4 +113,5 @@ def decode_gpu_chunks(cfg: synth.Config, chunks, seed: int = 0, frames_per_pass:
         parts.append(st.decode(zt[:, :, t:t + n], frames_per_pass=frames_per_pass))
         t += n
     torch.cuda.synchronize()
+    assert_range_clean()
     return torch.cat(parts, dim=2).float().cpu().numpy()

@@ -132,3 +132,4 @@ def test_deep_variant_has_more_launches_and_weights(dry):
     finally:
         wvd.wvd_destroy(base)
         wvd.wvd_destroy(deep)
+

@@ -1,9 +1,9 @@
 // Host side of the wvd library: the C ABI, the prepared-weight layout, the
 // workspace plan and the pass scheduler that walks the decoder frames_per_pass
 // latent frames at a time, carrying two history frames per causal conv in a
-// ring (the "temporal caching" of the TensorRT-LLM norm-SiLU issue; chunked
-// decoding that leaves the video unchanged, Wan2.2 VAE decoder page,
-// "Performance and memory").
+// ring (the "temporal caching" of the TensorRT-LLM norm-SiLU issue; the
+// Wan2.2 VAE decoder page, "Performance and memory", decodes in passes of
+// frames_per_pass latent frames without changing the video).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -25,14 +25,10 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 enum ItemKind { K_CONV = 0, K_PHASE = 1, K_VEC = 2, K_WINO = 3 };
 
-#ifndef WVD_WINO
-#define WVD_WINO 1
-#endif
-
 // A 3x3x3 norm-SiLU conv runs in Winograd form (F(kWinoM,3) along x: input
 // transform, kWinoN xi-plane GEMMs on the persistent kernel, output transform)
 // when its widths suit the 256-wide persistent tiles and 32-channel chunks.
-bool wino_ok(int cin, int cout) { return WVD_WINO && cin % 32 == 0 && cout % 256 == 0; }
+bool wino_ok(int cin, int cout) { return cin % 32 == 0 && cout % 256 == 0; }
 
 // One canonical weight tensor and where its prepared form lives.
 struct Item {
@@ -1068,6 +1064,39 @@ int wvd_decode_chunk(const wvd_plan* cplan, const void* z, int z_dtype, int T, i
 }
 
 const char* wvd_last_error(void) { return g_last_error.c_str(); }
+
+int wvd_math_probe(const float* x, float* silu_out, float* exp_out, long long n, void* stream) {
+  if (n < 0 || (n > 0 && (!x || !silu_out || !exp_out))) return WVD_EINVAL;
+  if (n > (1LL << 31)) return WVD_EINVAL;
+  hipError_t e = launch_math_probe(x, silu_out, exp_out, n, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    set_error("wvd_math_probe", e);
+    return WVD_EHIP;
+  }
+  return WVD_OK;
+}
+
+int wvd_range_flags(void* stream, int clear, unsigned int* flags) {
+  if (!flags) return WVD_EINVAL;
+  *flags = 0;
+  if (g_dry_run) return WVD_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  unsigned int* addr[2] = {nullptr, nullptr};
+  unsigned int host[2] = {0, 0};
+  hipError_t e = conv_range_flags_addr(&addr[0]);
+  if (e == hipSuccess) e = aux_range_flags_addr(&addr[1]);
+  for (int i = 0; i < 2 && e == hipSuccess; ++i)
+    e = hipMemcpyAsync(&host[i], addr[i], sizeof(unsigned int), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  for (int i = 0; i < 2 && e == hipSuccess && clear; ++i) e = hipMemsetAsync(addr[i], 0, sizeof(unsigned int), st);
+  if (e == hipSuccess && clear) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) {
+    set_error("wvd_range_flags", e);
+    return WVD_EHIP;
+  }
+  *flags = host[0] | host[1];
+  return WVD_OK;
+}
 
 void wvd_set_dry_run(int on) { g_dry_run = on != 0; }
 

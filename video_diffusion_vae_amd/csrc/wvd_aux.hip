@@ -140,7 +140,7 @@ __global__ __launch_bounds__(256) void norm_silu_kernel(const h16_t* __restrict_
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           const float t = f[k] * sc * gamma[g8 + k];
-          f[k] = t * __builtin_amdgcn_rcpf(1.0f + __expf(-t));
+          f[k] = silu_hw(t);
         }
         *reinterpret_cast<uint4*>(o + g8) = pack8h(f);
       }
@@ -256,11 +256,11 @@ __global__ __launch_bounds__(256) void softmax_rows_kernel(const float* __restri
   for (int j = lane; j < L; j += 64) mx = fmaxf(mx, s[j]);
   mx = wave_max(mx);
   float sum = 0.0f;
-  for (int j = lane; j < L; j += 64) sum += __expf(s[j] - mx);
+  for (int j = lane; j < L; j += 64) sum += exp_hw(s[j] - mx);
   sum = wave_sum(sum);
   const float inv = 1.0f / sum;
   h16_t* p = P + row * Lpad;
-  for (int j = lane; j < Lpad; j += 64) p[j] = j < L ? (h16_t)f2h(__expf(s[j] - mx) * inv) : (h16_t)0;
+  for (int j = lane; j < Lpad; j += 64) p[j] = j < L ? (h16_t)f2h(exp_hw(s[j] - mx) * inv) : (h16_t)0;
 }
 
 // V^T per frame: vt[f][c][l] = qkv[f][l][2C + c], zero for l >= L.
@@ -525,7 +525,7 @@ __device__ __forceinline__ void act_column(const uint4 (&v)[NG], bool in, int G,
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const float t = f[h][c] * sc * gm[h][c];
-      y[h][c] = in ? t * __builtin_amdgcn_rcpf(1.0f + __expf(-t)) : 0.0f;
+      y[h][c] = in ? silu_hw(t) : 0.0f;
     }
 }
 
@@ -1098,6 +1098,28 @@ hipError_t launch_prep_vec_add(const void* a, const void* b, int dtype, int n, f
   if (g_dry_run) return hipSuccess;
   hipLaunchKernelGGL(prep_vec_add_kernel, dim3(grid_for(n)), dim3(256), 0, s, a, b, dtype, n, out);
   return hipGetLastError();
+}
+
+// The device SiLU and exp of the kernels, evaluated elementwise (the math
+// self-test bounds their error against an exact reference).
+__global__ void math_probe_kernel(const float* __restrict__ x, float* __restrict__ silu_out,
+                                  float* __restrict__ exp_out, long long n) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float t = x[i];
+  silu_out[i] = silu_hw(t);
+  exp_out[i] = exp_hw(t);
+}
+
+hipError_t launch_math_probe(const float* x, float* silu_out, float* exp_out, long long n, hipStream_t s) {
+  if (g_dry_run || n == 0) return hipSuccess;
+  hipLaunchKernelGGL(math_probe_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, silu_out, exp_out, n);
+  return hipGetLastError();
+}
+
+// Device address of this code object's range flags on the current device.
+hipError_t aux_range_flags_addr(unsigned int** p) {
+  return hipGetSymbolAddress(reinterpret_cast<void**>(p), HIP_SYMBOL(g_range_flags));
 }
 
 }  // namespace wvd

@@ -22,8 +22,9 @@ enum DType { DT_BF16 = 0, DT_F32 = 1 };
 
 __device__ __forceinline__ float bf2f(uint32_t u16) { return __uint_as_float(u16 << 16); }
 
-// fp32 -> bf16, round to nearest even (inputs are finite).
+// fp32 -> bf16, round to nearest even; a NaN stays a (quiet) NaN.
 __device__ __forceinline__ uint32_t f2bf(float f) {
+  if (f != f) return 0x7fc0u;
   uint32_t u = __float_as_uint(f);
   u += 0x7fffu + ((u >> 16) & 1u);
   return u >> 16;
@@ -33,18 +34,49 @@ __device__ __forceinline__ float h2f(uint32_t u16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)u16);
 }
 
-// fp32 -> fp16, round to nearest even, saturating at +-65504.
-__device__ __forceinline__ uint32_t f2h(float f) {
-  f = fminf(fmaxf(f, -kF16Max), kF16Max);
+// Range events of the values this code object stores as fp16, one word per
+// translation unit and device: bit 0 (kRangeSaturated) a finite value beyond
+// the fp16 range was stored as +-65504, bit 1 (kRangeNaN) a NaN was stored.
+// The host reads and clears them through wvd_range_flags.
+constexpr unsigned kRangeSaturated = 1u;
+constexpr unsigned kRangeNaN = 2u;
+static __device__ unsigned int g_range_flags;
+
+// |f| as bits: above kF16MaxBits means beyond +-65504, inf or NaN.
+constexpr uint32_t kF16MaxBits = 0x477fe000u;  // 65504.0f
+__device__ __forceinline__ uint32_t abs_bits(float f) { return __float_as_uint(f) & 0x7fffffffu; }
+
+__device__ __forceinline__ uint32_t h16_bits(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
 }
+
+// The rare path of f2h: saturate (flagged) or keep a NaN (flagged).
+__device__ __noinline__ uint32_t f2h_out_of_range(float f) {
+  if (abs_bits(f) > kF16MaxBits) {
+    __hip_atomic_fetch_or(&g_range_flags, f != f ? kRangeNaN : kRangeSaturated, __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return h16_bits(f != f ? f : fminf(fmaxf(f, -kF16Max), kF16Max));
+}
+
+// fp32 -> fp16, round to nearest even.  A finite value beyond +-65504
+// saturates there and a NaN stays NaN; either one sets the range flags.
+__device__ __forceinline__ uint32_t f2h(float f) {
+  return abs_bits(f) <= kF16MaxBits ? h16_bits(f) : f2h_out_of_range(f);
+}
+
+// clamp(v, -1, 1) that keeps a NaN (the video's final clamp).
+__device__ __forceinline__ float clamp_unit(float v) { return v != v ? v : fminf(fmaxf(v, -1.0f), 1.0f); }
 
 // Element of an input tensor of type dt as fp32.
 __device__ __forceinline__ float load_in(const void* p, long long i, int dt) {
   return dt == DT_F32 ? static_cast<const float*>(p)[i] : bf2f(static_cast<const bf16_t*>(p)[i]);
 }
 
-__device__ __forceinline__ uint32_t pack2h(float lo, float hi) { return f2h(lo) | (f2h(hi) << 16); }
+__device__ __forceinline__ uint32_t pack2h(float lo, float hi) {
+  if (max(abs_bits(lo), abs_bits(hi)) <= kF16MaxBits) return h16_bits(lo) | (h16_bits(hi) << 16);
+  return f2h_out_of_range(lo) | (f2h_out_of_range(hi) << 16);
+}
 
 // Unpack 8 fp16 held in a uint4 into floats.
 __device__ __forceinline__ void unpack8h(const uint4& v, float* f) {
@@ -54,14 +86,31 @@ __device__ __forceinline__ void unpack8h(const uint4& v, float* f) {
   f[6] = h2f(v.w & 0xffffu); f[7] = h2f(v.w >> 16);
 }
 
+// Eight values at once: one range test for all eight on the common path.
 __device__ __forceinline__ uint4 pack8h(const float* f) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) m = max(m, abs_bits(f[k]));
   uint4 r;
-  r.x = pack2h(f[0], f[1]); r.y = pack2h(f[2], f[3]);
-  r.z = pack2h(f[4], f[5]); r.w = pack2h(f[6], f[7]);
+  if (m <= kF16MaxBits) {
+    r.x = h16_bits(f[0]) | (h16_bits(f[1]) << 16); r.y = h16_bits(f[2]) | (h16_bits(f[3]) << 16);
+    r.z = h16_bits(f[4]) | (h16_bits(f[5]) << 16); r.w = h16_bits(f[6]) | (h16_bits(f[7]) << 16);
+  } else {
+    r.x = f2h_out_of_range(f[0]) | (f2h_out_of_range(f[1]) << 16);
+    r.y = f2h_out_of_range(f[2]) | (f2h_out_of_range(f[3]) << 16);
+    r.z = f2h_out_of_range(f[4]) | (f2h_out_of_range(f[5]) << 16);
+    r.w = f2h_out_of_range(f[6]) | (f2h_out_of_range(f[7]) << 16);
+  }
   return r;
 }
 
-// SiLU(v) = v / (1 + exp(-v)); exp via the hardware exp2 path.
-__device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }
+// SiLU(t) = t / (1 + e^-t) as every kernel evaluates it: __expf (the
+// hardware exp2 of t * log2(e)) and the hardware reciprocal.  Its error
+// against the exact value is bounded by the math self-test
+// (wvd_math_probe) over the activations' input range.
+__device__ __forceinline__ float silu_hw(float t) { return t * __builtin_amdgcn_rcpf(1.0f + __expf(-t)); }
+
+// e^t as the attention softmax evaluates it (hardware exp2 of t * log2(e)).
+__device__ __forceinline__ float exp_hw(float t) { return __expf(t); }
 
 }  // namespace wvd

@@ -34,28 +34,6 @@
 // norms and norm_out, statistics in fp32 (Wan2.2 page, "Limits").
 #include "wvd_internal.h"
 
-#ifndef WVD_BRING
-#define WVD_BRING 6
-#endif
-#ifndef WVD_SCHED_PIN
-#define WVD_SCHED_PIN 1
-#endif
-#ifndef WVD_MAIN_W4
-#define WVD_MAIN_W4 1
-#endif
-#ifndef WVD_ILV
-#define WVD_ILV 1
-#endif
-#ifndef WVD_PHASE_W4
-#define WVD_PHASE_W4 0  // 1: up-conv phases on 4 waves of 128 x 128 (measured no faster than 8)
-#endif
-#ifndef WVD_WINO_LAG
-#define WVD_WINO_LAG 3  // Winograd GEMM: taps between a halo item's load and its LDS store
-#endif
-#ifndef WVD_WINO_W4
-#define WVD_WINO_W4 1
-#endif
-
 namespace wvd {
 
 namespace {
@@ -67,8 +45,9 @@ constexpr int kHX = kTileW + 2;
 constexpr int kHY333 = kTH333 + 2;
 constexpr int kHF333 = kTF333 + 2;
 constexpr int kNHV333 = kHF333 * kHY333 * kHX;  // 720 halo voxels
-constexpr int kBRing = WVD_BRING;              // k16 steps of B fragments in flight
-constexpr int kPhaseBRing = WVD_PHASE_W4 ? 2 : 4;  // the same for the up-conv phase loop
+constexpr int kBRing = 6;       // k16 steps of B fragments in flight
+constexpr int kPhaseBRing = 4;  // the same for the up-conv phase loop
+constexpr int kWinoLag = 3;     // Winograd GEMM: taps between a halo item's load and its LDS store
 // Tile of the Winograd-domain GEMM: 2 frames x 8 rows x 16 column groups
 // (halo 4 x 10 x 16 rows; a 4 x 4 x 16 tile has fewer halo rows but measured slower).
 constexpr int kTFWino = kWinoTF;
@@ -151,7 +130,7 @@ __device__ __forceinline__ void halo_store(const G& g, int idx, int chunk, uint4
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const float t = f[k] * sc * gm[k];
-      f[k] = ACT ? t * __builtin_amdgcn_rcpf(1.0f + __expf(-t)) : t;
+      f[k] = ACT ? silu_hw(t) : t;
     }
     r = pack8h(f);
   }
@@ -217,9 +196,7 @@ __device__ __forceinline__ void run_333(const G& g, f32x16_t (&acc)[MI][NJ], int
 #pragma unroll
   for (int u = 0; u < DEPTH; ++u) {
     load_step(bq[u], 0, u >> 1, u & 1);
-#if WVD_SCHED_PIN
     __builtin_amdgcn_sched_barrier(0);
-#endif
   }
   for (int c = 0; c < nchunks; ++c) {
     const unsigned char* hsrc = g.halo0 + (c & 1) * g.halo_bytes;
@@ -259,9 +236,7 @@ __device__ __forceinline__ void run_333(const G& g, f32x16_t (&acc)[MI][NJ], int
         } else {
           load_step(bq[s6 % DEPTH], cn, t3 - 27, ks3);
         }
-#if WVD_SCHED_PIN
         __builtin_amdgcn_sched_barrier(0);
-#endif
       }
     }
     __syncthreads();  // next chunk's halo complete; this chunk's reads done
@@ -360,9 +335,7 @@ __device__ __forceinline__ void run_phase(const G& g, f32x16_t (&acc)[MI][NJ], i
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     load_step(bq[u], 0, u >> 1, u & 1);
-#if WVD_SCHED_PIN
     __builtin_amdgcn_sched_barrier(0);
-#endif
   }
   for (int c = 0; c < nchunks; ++c) {
     const unsigned char* hsrc = g.halo0 + (c & 1) * g.halo_bytes;
@@ -390,9 +363,7 @@ __device__ __forceinline__ void run_phase(const G& g, f32x16_t (&acc)[MI][NJ], i
       } else {
         load_step(bq[u & 3], cn, (u + 4 - 8) >> 1, ks);
       }
-#if WVD_SCHED_PIN
       __builtin_amdgcn_sched_barrier(0);
-#endif
     }
     __syncthreads();
   }
@@ -727,7 +698,7 @@ __global__ __launch_bounds__(NW * 64) void conv_igemm(ConvArgs a) {
         for (int c = 0; c < CPL && nb + c < a.Cout; ++c) {
           const int n = nb + c;
           float v = row[c] * a.scale + (a.bias ? a.bias[n] : 0.0f);
-          v = fminf(fmaxf(v, -1.0f), 1.0f);
+          v = clamp_unit(v);
           const int k = n >> 2, ddy = (n >> 1) & 1, ddx = n & 1;
           const long long r2 = ((long long)k * a.video_T + a.out_base + f) * (2 * a.H) + 2 * y + ddy;
           static_cast<bf16_t*>(a.out)[r2 * (2 * a.W) + 2 * x + ddx] = (bf16_t)f2bf(v);
@@ -1068,7 +1039,6 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
 #pragma unroll
               for (int j = 0; j < NJ; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bq[s6 % kBRing][j], acc[i][j], 0, 0, 0);
-#if WVD_ILV
             if (hstore) {
 #pragma unroll
               for (int q = 0; q < MI * NJ; ++q) {
@@ -1076,7 +1046,6 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
                 __builtin_amdgcn_sched_group_barrier(0x002, NORM ? 80 / (MI * NJ) : 1, 0);  // then VALU
               }
             }
-#endif
             // refill with k16 step u + kBRing
             const int t3 = 3 * gi + (s6 + kBRing) / 2;
             const int ks3 = (s6 + kBRing) & 1;
@@ -1095,7 +1064,7 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
         constexpr int IPT = (NHV * NP + NT - 1) / NT;
         constexpr int IPK = (IPT + 4) / 5;
         static_assert(IPK <= 2, "halo items per tap");
-        constexpr int LAGT = WVD_WINO_LAG;
+        constexpr int LAGT = kWinoLag;
         static_assert(LAGT >= 1 && LAGT + 4 <= 8, "halo items stored inside the chunk");
         uint4 hr[LAGT][IPK];
         f16x8_t ap[2][MI];
@@ -1195,13 +1164,12 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
       } else {
-        // four 2x2 taps x two k16 steps; halo items are loaded LPS per step
-        // over the first NLS steps and stored LAG steps later; with APF (4
-        // waves) A fragments run one step ahead
+        // four 2x2 taps x two k16 steps on 8 waves; halo items are loaded
+        // one per step over the first NLS steps and stored LAG steps later
+        static_assert(!APF, "the phase loop runs on 8 waves");
         constexpr int IPT = ((1 * 18 * 18) * NP + NT - 1) / NT;
         constexpr int PD = kPhaseBRing;  // B fragments of step u in slot u % PD, refilled with step u + PD
-        constexpr int LPS = APF ? 2 : 1;
-        constexpr int NLS = (IPT + LPS - 1) / LPS;
+        constexpr int NLS = IPT;
         constexpr int LAG = 8 - NLS;
         static_assert(NLS >= 1 && LAG >= 3, "phase halo items land inside a chunk");
         const int py = geo.ph >> 1, px = geo.ph & 1;
@@ -1210,34 +1178,16 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
           return ((py + (tap >> 1)) * HX + (px + (tap & 1))) * ROWB + (u & 1) * 32;
         };
         uint4 hr[IPT];
-        f16x8_t ap[2][MI];
-        if constexpr (APF) {
-          const int o0 = toff(0);
-#pragma unroll
-          for (int i = 0; i < MI; ++i) ap[0][i] = *reinterpret_cast<const f16x8_t*>(hsrc + g.abase[i] + o0);
-        }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int ks = u & 1;
           f16x8_t av[MI];
-          if constexpr (APF) {
-            if (u + 1 < 8) {
-              const int o1 = toff(u + 1);
-#pragma unroll
-              for (int i = 0; i < MI; ++i)
-                ap[(u + 1) & 1][i] = *reinterpret_cast<const f16x8_t*>(hsrc + g.abase[i] + o1);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int i = 0; i < MI; ++i) av[i] = ap[u & 1][i];
-          } else {
+          {
             const int o = toff(u);
 #pragma unroll
             for (int i = 0; i < MI; ++i) av[i] = *reinterpret_cast<const f16x8_t*>(hsrc + g.abase[i] + o);
           }
-#pragma unroll
-          for (int q = 0; q < LPS; ++q) {
-            const int is = (u - LAG) * LPS + q, il = u * LPS + q;
+          {
+            const int is = u - LAG, il = u;
             if (u >= LAG && is < IPT) halo_store<false, false>(gn, tid + NT * is, cn, hr[is], hdst);
             if (u < NLS && il < IPT) hr[il] = halo_load(gn, tid + NT * il, cn);
           }
@@ -1367,7 +1317,7 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
               for (int cc = 0; cc < CPL && nb + cc < a.Cout; ++cc) {
                 const int n = nb + cc;
                 float v = row[cc] * a.scale + (a.bias ? a.bias[n] : 0.0f);
-                v = fminf(fmaxf(v, -1.0f), 1.0f);
+                v = clamp_unit(v);
                 const int kk = n >> 2, ddy = (n >> 1) & 1, ddx = n & 1;
                 const long long r2 = ((long long)kk * a.video_T + a.out_base + f) * (2 * a.H) + 2 * y + ddy;
                 static_cast<bf16_t*>(a.out)[r2 * (2 * a.W) + 2 * x + ddx] = (bf16_t)f2bf(v);
@@ -1841,12 +1791,8 @@ hipError_t launch_conv(const ConvArgs& a, hipStream_t stream) {
   const Variant v = conv_variant(a);
   if (conv_persistent(a)) {
     const int pro = a.seg[0].prologue;
-#if WVD_PHASE_W4
-    if (v.mode == 2) return launch_persist_impl<256, 2, 2, PRO_RAW, 4>(a, stream);
-#endif
     if (v.mode == 2) return launch_persist_impl<256, 4, 2, PRO_RAW>(a, stream);
     if (v.mode == 3) return launch_persist_impl<256, 4, 3, PRO_RAW>(a, stream);
-#if WVD_WINO_W4
     if (v.mode == 4) {  // one instantiation per Winograd tile shape (TF frames x TW column groups)
       if (a.TF == 2 && a.TW == 8) return launch_persist_impl<256, 2, 4, PRO_RAW, 4, 8, 2>(a, stream);
       if (a.TF == 4 && a.TW == 8) return launch_persist_impl<256, 2, 4, PRO_RAW, 4, 8, 4>(a, stream);
@@ -1854,14 +1800,9 @@ hipError_t launch_conv(const ConvArgs& a, hipStream_t stream) {
       if (a.TF == 4 && a.TW == 4) return launch_persist_impl<256, 2, 4, PRO_RAW, 4, 4, 4>(a, stream);
       return launch_persist_impl<256, 2, 4, PRO_RAW, 4>(a, stream);
     }
-#endif
-    if (v.mode == 4) return launch_persist_impl<256, 4, 4, PRO_RAW>(a, stream);
     if (v.bn == 32) return launch_persist_impl<32, 1, 1, PRO_RAW>(a, stream);
-#if WVD_MAIN_W4
     if (pro == PRO_NORM_SILU) return launch_persist_impl<256, 2, 1, PRO_NORM_SILU, 4>(a, stream);
-#endif
-    return pro == PRO_NORM_SILU ? launch_persist_impl<256, 4, 1, PRO_NORM_SILU>(a, stream)
-                                : launch_persist_impl<256, 4, 1, PRO_RAW>(a, stream);
+    return launch_persist_impl<256, 4, 1, PRO_RAW>(a, stream);
   }
   if (v.mode >= 3) return hipErrorInvalidValue;  // these tap sets exist only in the persistent kernel
   if (v.mode == 1) {
@@ -1884,6 +1825,11 @@ hipError_t launch_conv(const ConvArgs& a, hipStream_t stream) {
   if (v.bk == 32 && v.bn == 32) return launch_impl<32, 32, 1, 4, 0, -1>(a, stream);
   if (v.bk == 16 && v.bn == 128) return launch_impl<16, 128, 2, 4, 0, -1>(a, stream);
   return launch_impl<16, 32, 1, 4, 0, -1>(a, stream);
+}
+
+// Device address of this code object's range flags on the current device.
+hipError_t conv_range_flags_addr(unsigned int** p) {
+  return hipGetSymbolAddress(reinterpret_cast<void**>(p), HIP_SYMBOL(g_range_flags));
 }
 
 }  // namespace wvd

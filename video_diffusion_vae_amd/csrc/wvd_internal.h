@@ -174,4 +174,12 @@ hipError_t launch_prep_vec(const void* v, int dtype, int n, float scale, float* 
 // out[i] = a[i] + b[i] in fp32 (the two biases of a block with a shortcut).
 hipError_t launch_prep_vec_add(const void* a, const void* b, int dtype, int n, float* out, hipStream_t s);
 
+// silu_hw and exp_hw of n fp32 inputs (math self-test).
+hipError_t launch_math_probe(const float* x, float* silu_out, float* exp_out, long long n, hipStream_t s);
+
+// Device addresses of the range flags (see g_range_flags) of the two kernel
+// code objects on the current device.
+hipError_t conv_range_flags_addr(unsigned int** p);
+hipError_t aux_range_flags_addr(unsigned int** p);
+
 }  // namespace wvd

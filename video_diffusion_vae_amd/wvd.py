@@ -21,6 +21,8 @@ WVD_EUNSUPPORTED = -4
 WVD_EHIP = -5
 NUM_WEIGHTS = 84
 NUM_WEIGHTS_DEEP = 110  # deep variant: pre_conv + three ResBlocks per up stage
+WVD_RANGE_SATURATED = 1
+WVD_RANGE_NAN = 2
 WVD_DTYPE_BF16 = 0
 WVD_DTYPE_F32 = 1
 PROFILE_CLASSES = ("conv3x3x3_main", "conv_other", "attention_gemm", "norm_stats", "copies", "wino_transforms")
@@ -68,6 +70,10 @@ def _load() -> ctypes.CDLL:
     lib.wvd_set_dry_run.restype = None
     lib.wvd_last_launch_count.argtypes = [vp]
     lib.wvd_last_launch_count.restype = ctypes.c_longlong
+    lib.wvd_math_probe.argtypes = [vp, vp, vp, ctypes.c_longlong, vp]
+    lib.wvd_math_probe.restype = i
+    lib.wvd_range_flags.argtypes = [vp, i, ctypes.POINTER(ctypes.c_uint)]
+    lib.wvd_range_flags.restype = i
     lib.wvd_profile_enable.argtypes = [vp, i]
     lib.wvd_profile_enable.restype = i
     lib.wvd_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
@@ -149,6 +155,24 @@ def wvd_decode_chunk(plan: int, z_ptr: int, z_dtype: int, T: int, t_begin: int, 
 def video_frames(t: int) -> int:
     """Video frames of the first t latent frames."""
     return 4 * t - 3 if t > 0 else 0
+
+
+def wvd_range_flags(stream_ptr: int, clear: bool) -> int:
+    """Range flags of the fp16 stores on the current device (bit 0 saturated,
+    bit 1 NaN); waits for `stream_ptr`, then clears them if asked."""
+    f = ctypes.c_uint(0)
+    _check(_lib.wvd_range_flags(stream_ptr, 1 if clear else 0, ctypes.byref(f)), "wvd_range_flags")
+    return f.value
+
+
+def wvd_math_probe(x_ptr: int, silu_ptr: int, exp_ptr: int, n: int, stream_ptr: int) -> None:
+    _check(_lib.wvd_math_probe(x_ptr, silu_ptr, exp_ptr, n, stream_ptr), "wvd_math_probe")
+
+
+def range_flags(clear: bool = True) -> int:
+    """wvd_range_flags on torch's current stream of the current device."""
+    import torch
+    return wvd_range_flags(torch.cuda.current_stream().cuda_stream, clear)
 
 
 def wvd_destroy(plan: int) -> None:
