@@ -111,6 +111,25 @@ int wvd_workspace_bytes(const wvd_plan* plan, int T, int frames_per_pass, size_t
 int wvd_decode(const wvd_plan* plan, const void* z, int z_dtype, int T, int frames_per_pass,
                void* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* wvd_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same decode into the caller's `out`, with the workspace taken from a static
+ * device array of WVD_STATIC_WORKSPACE_BYTES inside the library (one per
+ * device, held until the process ends; 32 MiB fits e.g. the c=16 decoder at
+ * 4 x 6 latents for frames_per_pass <= 10, or c=256 at 2 x 3 for <= 3).
+ * It calls no hipMalloc, hipFree or other allocating routine.
+ *   Same arguments, video and bit-identity as wvd_decode without the
+ *   workspace.  WVD_ENOSPACE (with the sizes in wvd_last_error) when
+ *   wvd_workspace_bytes(plan, T, frames_per_pass) exceeds the static size;
+ *   nothing is enqueued then.
+ * Every call on a device shares that device's array and leaves its contents
+ * behind (no decode depends on them): calls on one device whose work overlaps
+ * in time (several host threads, or several streams) race and corrupt each
+ * other's video.  Serialise them on one stream. */
+#define WVD_STATIC_WORKSPACE_BYTES ((size_t)32 << 20)
+int wvd_decode_static(const wvd_plan* plan, const void* z, int z_dtype, int T, int frames_per_pass, void* out,
+                      void* stream);
+
 /* Streaming decode (the temporal caching of the norm-SiLU issue, "Feature,
  * motivation and proposed scope"; the segment-wise generation of the Wan2.2
  * page's introduction): latents arrive in chunks and each chunk's video is
@@ -153,7 +172,8 @@ void wvd_destroy(wvd_plan* plan);
 const char* wvd_status_string(int status);
 
 /* Text naming the launch and HIP error behind the last WVD_EHIP returned on
- * the calling thread ("" if none).  Valid until the next call on the thread. */
+ * the calling thread (and the sizes behind a WVD_ENOSPACE of
+ * wvd_decode_static); "" if none.  Valid until the next call on the thread. */
 const char* wvd_last_error(void);
 
 /* Range events of the values stored as fp16 on the current device since the

@@ -47,6 +47,8 @@ void run_case(const Case& k) {
       EXPECT(wvd_decode(plan, fake(3), WVD_DTYPE_BF16, T, P, fake(4), fake(5), nws, nullptr) == WVD_OK);
       EXPECT(wvd_last_launch_count(plan) > 0);
       EXPECT(wvd_decode(plan, fake(3), WVD_DTYPE_F32, T, P, fake(4), fake(5), nws - 1, nullptr) == WVD_ENOSPACE);
+      const int st = wvd_decode_static(plan, fake(3), WVD_DTYPE_BF16, T, P, fake(4), nullptr);
+      EXPECT(st == (nws <= WVD_STATIC_WORKSPACE_BYTES ? WVD_OK : WVD_ENOSPACE));
       // the clip in two chunks
       if (T >= 2) {
         const int a = T / 2;
@@ -99,6 +101,7 @@ int main() {
   EXPECT(wvd_prepared_bytes(24, 4, 6, &n) == WVD_EUNSUPPORTED);
   EXPECT(wvd_prepared_bytes(16, 4, 6, nullptr) == WVD_EINVAL);
   EXPECT(wvd_workspace_bytes(nullptr, 1, 1, &n) == WVD_EINVAL);
+  EXPECT(wvd_decode_static(nullptr, fake(3), 0, 1, 1, fake(4), nullptr) == WVD_EINVAL);
   EXPECT(wvd_last_launch_count(nullptr) == -1);
   wvd_destroy(nullptr);
   EXPECT(wvd_status_string(-5)[0] != 0 && wvd_last_error() != nullptr);

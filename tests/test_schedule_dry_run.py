@@ -133,3 +133,27 @@ def test_deep_variant_has_more_launches_and_weights(dry):
         wvd.wvd_destroy(base)
         wvd.wvd_destroy(deep)
 
+
+def test_static_decode_checks_its_workspace_limit(dry):
+    """wvd_decode_static takes its workspace from the library's static array:
+    decodes that fit run their schedule, larger ones are refused on the host."""
+    wvd = dry
+    plan = plan_for(wvd, 16, 4, 6)
+    try:
+        assert wvd.wvd_workspace_bytes(plan, 4, 4) <= wvd.WVD_STATIC_WORKSPACE_BYTES
+        wvd.wvd_decode_static(plan, FAKE, wvd.WVD_DTYPE_BF16, 4, 4, FAKE, 0)
+        assert wvd.wvd_last_launch_count(plan) > 0
+    finally:
+        wvd.wvd_destroy(plan)
+    plan = plan_for(wvd, 64, 22, 39)
+    try:
+        assert wvd.wvd_workspace_bytes(plan, 3, 1) > wvd.WVD_STATIC_WORKSPACE_BYTES
+        with pytest.raises(wvd.WvdError) as e:
+            wvd.wvd_decode_static(plan, FAKE, wvd.WVD_DTYPE_BF16, 3, 1, FAKE, 0)
+        assert e.value.status == wvd.WVD_ENOSPACE and "static workspace" in str(e.value)
+        for bad in ((0, 1), (3, 0)):
+            with pytest.raises(wvd.WvdError) as e:
+                wvd.wvd_decode_static(plan, FAKE, wvd.WVD_DTYPE_BF16, bad[0], bad[1], FAKE, 0)
+            assert e.value.status == wvd.WVD_EINVAL
+    finally:
+        wvd.wvd_destroy(plan)

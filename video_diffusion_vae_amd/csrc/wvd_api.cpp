@@ -9,6 +9,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -1034,6 +1035,76 @@ int wvd_decode(const wvd_plan* cplan, const void* z, int z_dtype, int T, int fra
   if (!aligned16(workspace)) return WVD_EINVAL;
   return decode_impl(const_cast<wvd_plan*>(cplan), z, z_dtype, T, 0, frames_per_pass, nullptr, out, workspace,
                      workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------------
+// Decode without allocation: the workspace is this file-scope device array
+// (one copy per device, held until the process ends).  Host code never uses
+// the array's name as an address: the device address of each device's copy is
+// looked up once, with that device current, and kept in g_scratch_addr.
+// ---------------------------------------------------------------------------
+
+namespace {
+
+constexpr size_t kStaticWorkspaceBytes = WVD_STATIC_WORKSPACE_BYTES;
+constexpr int kMaxDevices = 64;
+static_assert(kStaticWorkspaceBytes % kAlign == 0, "static workspace size");
+
+__device__ __align__(256) unsigned char scratch[kStaticWorkspaceBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (looked up on the first call on
+// each device).
+int static_workspace(void** addr) {
+  if (g_dry_run) {  // nothing is dereferenced: any aligned placeholder will do
+    *addr = reinterpret_cast<void*>(static_cast<uintptr_t>(1) << 20);
+    return WVD_OK;
+  }
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    set_error("wvd_decode_static: hipGetDevice", e);
+    return WVD_EHIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    g_last_error = "wvd_decode_static: device index beyond the static table";
+    return WVD_EUNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      set_error("wvd_decode_static: hipGetSymbolAddress(scratch)", e != hipSuccess ? e : hipErrorInvalidSymbol);
+      return WVD_EHIP;
+    }
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return WVD_OK;
+}
+
+}  // namespace
+
+int wvd_decode_static(const wvd_plan* cplan, const void* z, int z_dtype, int T, int frames_per_pass, void* out,
+                      void* stream) {
+  if (!plan_ok(cplan) || !z || !out || T < 1 || frames_per_pass < 1) return WVD_EINVAL;
+  if (z_dtype != WVD_DTYPE_BF16 && z_dtype != WVD_DTYPE_F32) return WVD_EINVAL;
+  const int P = std::min(T, frames_per_pass);
+  const size_t need = make_work(cplan->c, cplan->h, cplan->w, P, true, cplan->L.nrb).total;
+  if (need > kStaticWorkspaceBytes) {
+    g_last_error = "wvd_decode_static: this decode needs " + std::to_string(need) +
+                   " workspace bytes, more than the static workspace of " + std::to_string(kStaticWorkspaceBytes) +
+                   " bytes (use wvd_decode with a caller-owned workspace, or a smaller frames_per_pass)";
+    return WVD_ENOSPACE;
+  }
+  void* ws = nullptr;
+  const int st = static_workspace(&ws);
+  if (st != WVD_OK) return st;
+  return decode_impl(const_cast<wvd_plan*>(cplan), z, z_dtype, T, 0, frames_per_pass, nullptr, out, ws,
+                     kStaticWorkspaceBytes, static_cast<hipStream_t>(stream));
 }
 
 int wvd_state_bytes(const wvd_plan* plan, size_t* bytes) {

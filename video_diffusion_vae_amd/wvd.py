@@ -54,6 +54,8 @@ def _load() -> ctypes.CDLL:
     lib.wvd_workspace_bytes.restype = i
     lib.wvd_decode.argtypes = [vp, vp, i, i, i, vp, vp, sz, vp]
     lib.wvd_decode.restype = i
+    lib.wvd_decode_static.argtypes = [vp, vp, i, i, i, vp, vp]
+    lib.wvd_decode_static.restype = i
     lib.wvd_state_bytes.argtypes = [vp, ctypes.POINTER(sz)]
     lib.wvd_state_bytes.restype = i
     lib.wvd_chunk_workspace_bytes.argtypes = [vp, i, i, ctypes.POINTER(sz)]
@@ -131,6 +133,18 @@ def wvd_decode(plan: int, z_ptr: int, z_dtype: int, T: int, frames_per_pass: int
                ws_bytes: int, stream_ptr: int) -> None:
     _check(_lib.wvd_decode(plan, z_ptr, z_dtype, T, frames_per_pass, out_ptr, ws_ptr, ws_bytes, stream_ptr),
            "wvd_decode")
+
+
+WVD_STATIC_WORKSPACE_BYTES = 32 << 20
+
+
+def wvd_decode_static(plan: int, z_ptr: int, z_dtype: int, T: int, frames_per_pass: int, out_ptr: int,
+                      stream_ptr: int) -> None:
+    """wvd_decode with the library's static workspace (no allocation)."""
+    st = _lib.wvd_decode_static(plan, z_ptr, z_dtype, T, frames_per_pass, out_ptr, stream_ptr)
+    if st == WVD_ENOSPACE:
+        raise WvdError(st, "wvd_decode_static: " + _lib.wvd_last_error().decode())
+    _check(st, "wvd_decode_static")
 
 
 def wvd_state_bytes(plan: int) -> int:
