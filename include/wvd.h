@@ -164,6 +164,48 @@ int wvd_decode_chunk(const wvd_plan* plan, const void* z, int z_dtype, int T, in
                      void* state, size_t state_bytes, void* out, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/* ---- The encoder: video [1, 3, 4T-3, 16h, 16w] -> latents [1, 48, T, h, w].
+ * The pages say only that the decoder's encoder stays native (the norm-SiLU
+ * issue, "Feature, motivation and proposed scope"); this one is the decoder's
+ * mirror image: a 2x2 patchify into 12 channels (channel 4k+2dy+dx = pixel
+ * (2Y+dy, 2X+dx) of colour k), conv_in 12 -> c, four down stages of widths
+ * [c, 2c, 4c, 4c] with two ResBlocks each, a 3x3 stride-2 (zero pad 1)
+ * down-conv after stages 0-2, a temporal down-conv after those of stages 1
+ * and 2 (the clip's first frame kept single; later frames in pairs (2s+1,
+ * 2s+2), channels concatenated, causal 3x1x1 conv 2C -> C), a mid block
+ * (ResBlock, attention, ResBlock) and a head (RMSNorm, SiLU, causal 3x3x3
+ * conv 4c -> 48).  Same numerics as the decoder (fp16 storage, fp32
+ * accumulation), fp32 latents.
+ *
+ * wvd_encoder_prepared_bytes / wvd_encoder_prepare: as wvd_prepared_bytes /
+ *   wvd_prepare for the encoder's WVD_NUM_WEIGHTS_ENCODER tensors in their
+ *   canonical order and PyTorch layouts: conv_in (weight [c,12,3,3,3],
+ *   bias); for stage s = 0..3 of width Cs: res0 (norm1.gamma, conv1.weight,
+ *   conv1.bias, norm2.gamma, conv2.weight, conv2.bias, + shortcut.weight
+ *   [Cs,Cprev,1,1,1], shortcut.bias when the width changes), res1,
+ *   down_conv (weight [Cs,Cs,3,3], bias; s < 3), time_conv (weight
+ *   [Cs,2Cs,3,1,1], bias; s = 1, 2); mid.res0; mid.attn (norm.gamma,
+ *   qkv.weight [12c,4c], qkv.bias, proj.weight [4c,4c], proj.bias);
+ *   mid.res1; head (norm.gamma [4c], conv.weight [48,4c,3,3,3], conv.bias).
+ *   The plan serves only the wvd_encode* calls (the decoder calls return
+ *   WVD_EINVAL on it, and these on a decoder plan).
+ * wvd_encode_workspace_bytes: workspace for T latent frames at
+ *   frames_per_pass (depends on min(T, frames_per_pass)).
+ * wvd_encode: video: device [1, 3, 4T-3, 16h, 16w] of video_dtype
+ *   (WVD_DTYPE_BF16 or WVD_DTYPE_F32), contiguous; latents: device fp32
+ *   [1, 48, T, h, w], contiguous, every element written.  Pass k covers
+ *   latent frames [kP, kP+P) (video frames [0, 4P-3), then [4kP-3,
+ *   4(k+1)P-3)); the latents are bit-identical for every frames_per_pass and
+ *   their first k frames to the encode of the first 4k-3 video frames.
+ *   Errors as wvd_decode. */
+#define WVD_NUM_WEIGHTS_ENCODER 84
+int wvd_encoder_prepared_bytes(int c, int h, int w, size_t* bytes);
+int wvd_encoder_prepare(int c, int h, int w, const void* const* weights, int n_weights, int weight_dtype,
+                        void* prepared, size_t prepared_bytes, void* stream, wvd_plan** plan_out);
+int wvd_encode_workspace_bytes(const wvd_plan* plan, int T, int frames_per_pass, size_t* bytes);
+int wvd_encode(const wvd_plan* plan, const void* video, int video_dtype, int T, int frames_per_pass, float* latents,
+               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Release a plan (host memory only; the prepared buffer stays the caller's).
  * NULL is ignored. */
 void wvd_destroy(wvd_plan* plan);

@@ -157,3 +157,40 @@ def test_static_decode_checks_its_workspace_limit(dry):
             assert e.value.status == wvd.WVD_EINVAL
     finally:
         wvd.wvd_destroy(plan)
+
+
+@pytest.mark.parametrize("cfg", __import__("video_diffusion_vae_amd.synth_encoder", fromlist=["x"]).ENCODER_CONFIGS,
+                         ids=lambda c: c.name)
+def test_every_encoder_config_schedules(dry, cfg):
+    """The encoder's pass scheduler and per-launch checks for every workload
+    and frames_per_pass; decoder calls refuse an encoder plan."""
+    wvd = dry
+    n = wvd.wvd_encoder_prepared_bytes(cfg.c, cfg.h, cfg.w)
+    plan = wvd.wvd_encoder_prepare(cfg.c, cfg.h, cfg.w, [FAKE] * wvd.NUM_WEIGHTS_ENCODER, wvd.WVD_DTYPE_BF16, FAKE,
+                                   n, 0)
+    try:
+        counts = {}
+        for P in sorted(set(cfg.passes) | {1, cfg.T, cfg.T + 3}):
+            ws = wvd.wvd_encode_workspace_bytes(plan, cfg.T, P)
+            wvd.wvd_encode(plan, FAKE, wvd.WVD_DTYPE_BF16, cfg.T, P, FAKE, FAKE, ws, 0)
+            counts[P] = wvd.wvd_last_launch_count(plan)
+            assert counts[P] > 0
+            with pytest.raises(wvd.WvdError) as e:
+                wvd.wvd_encode(plan, FAKE, wvd.WVD_DTYPE_BF16, cfg.T, P, FAKE, FAKE, ws - 1, 0)
+            assert e.value.status == wvd.WVD_ENOSPACE
+        assert counts[cfg.T] == counts[cfg.T + 3]
+        with pytest.raises(wvd.WvdError) as e:
+            wvd.wvd_workspace_bytes(plan, cfg.T, 1)
+        assert e.value.status == wvd.WVD_EINVAL
+    finally:
+        wvd.wvd_destroy(plan)
+    dplan = plan_for(wvd, cfg.c, cfg.h, cfg.w)
+    try:
+        with pytest.raises(wvd.WvdError) as e:
+            wvd.wvd_encode_workspace_bytes(dplan, cfg.T, 1)
+        assert e.value.status == wvd.WVD_EINVAL
+    finally:
+        wvd.wvd_destroy(dplan)
+    with pytest.raises(wvd.WvdError) as e:
+        wvd.wvd_encoder_prepare(cfg.c, cfg.h, cfg.w, [FAKE] * wvd.NUM_WEIGHTS_DEEP, wvd.WVD_DTYPE_BF16, FAKE, n, 0)
+    assert e.value.status == wvd.WVD_EINVAL

@@ -24,7 +24,7 @@ namespace {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
-enum ItemKind { K_CONV = 0, K_PHASE = 1, K_VEC = 2, K_WINO = 3 };
+enum ItemKind { K_CONV = 0, K_PHASE = 1, K_VEC = 2, K_WINO = 3, K_CONV_PART = 4 };
 
 // A 3x3x3 norm-SiLU conv runs in Winograd form (F(kWinoM,3) along x: input
 // transform, kWinoN xi-plane GEMMs on the persistent kernel, output transform)
@@ -39,6 +39,10 @@ struct Item {
   float scale;                    // vec scale (sqrt(C) for gammas)
   size_t off;                     // byte offset in the prepared buffer
   size_t bytes;
+  // K_CONV_PART: input channels [cin_off, cin_off + cin) of a tensor with
+  // cin_src input channels, the canonical tensor `src` (-1: this item's own
+  // index)
+  int src = -1, cin_src = 0, cin_off = 0;
 };
 
 // Indices of the canonical tensors of one ResBlock.
@@ -59,6 +63,13 @@ struct Layout {
   int attn_norm, qkv_w, qkv_b, proj_w, proj_b;
   int tc_w[2], tc_b[2], upc_w[3], upc_b[3];
   int head_norm, head_w, head_b;
+  // The encoder (R13-R16): down stages, strided down-convs, and the temporal
+  // down-convs of stages 1 and 2 as two K segments (the pair's first and
+  // second frame) with a shared bias.
+  bool encoder = false;
+  RB down[4][2];
+  int dc_w[3], dc_b[3];
+  int td_w[2][2], td_b[2];
   size_t zero_off = 0;
   int zero_len = 0;
   size_t total = 0;
@@ -258,6 +269,150 @@ Work make_work(int c, int h, int w, int P, bool rings_in_workspace = true, int n
   return W;
 }
 
+// ---------------------------------------------------------------------------
+// Encoder layout, rings and workspace (the decoder's mirror image, R13-R16)
+// ---------------------------------------------------------------------------
+
+int enc_width(int c, int s) { return s == 0 ? c : (s == 1 ? 2 * c : 4 * c); }
+
+// Items 0..83 are the canonical tensors in order; the second halves of the
+// two temporal down-convs' weights follow.
+Layout make_layout_enc(int c, int h, int w) {
+  Layout L;
+  L.encoder = true;
+  const int c4 = 4 * c;
+  add_conv(L, c, 12, 27, 16, &L.conv_in_w, &L.conv_in_b);  // 12 patch channels, padded to 16
+  int prev = c;
+  for (int s = 0; s < 4; ++s) {
+    const int cs = enc_width(c, s);
+    L.down[s][0] = add_rb(L, prev, cs);
+    L.down[s][1] = add_rb(L, cs, cs);
+    if (s < 3) add_conv(L, cs, cs, 9, cs, &L.dc_w[s], &L.dc_b[s]);
+    if (s == 1 || s == 2) {
+      const int k = s - 1;
+      add_conv(L, cs, cs, 3, cs, &L.td_w[k][0], &L.td_b[k]);
+      Item& it = L.items[L.td_w[k][0]];
+      it.kind = K_CONV_PART;  // the pair's first frame: input channels [0, cs) of [cs, 2cs, 3, 1, 1]
+      it.cin_src = 2 * cs;
+      it.cin_off = 0;
+    }
+    prev = cs;
+  }
+  L.mid0 = add_rb(L, c4, c4);
+  L.attn_norm = add_vec(L, c4, std::sqrt((float)c4));
+  add_conv(L, 3 * c4, c4, 1, c4, &L.qkv_w, &L.qkv_b);
+  add_conv(L, c4, c4, 1, c4, &L.proj_w, &L.proj_b);
+  L.mid1 = add_rb(L, c4, c4);
+  L.head_norm = add_vec(L, c4, std::sqrt((float)c4));
+  add_conv(L, 48, c4, 27, c4, &L.head_w, &L.head_b);
+  for (int k = 0; k < 2; ++k) {  // the pair's second frame: input channels [cs, 2cs)
+    const int cs = enc_width(c, k + 1);
+    Item it = L.items[L.td_w[k][0]];
+    it.src = L.td_w[k][0];
+    it.cin_off = cs;
+    L.td_w[k][1] = (int)L.items.size();
+    L.items.push_back(it);
+  }
+  size_t off = 0;
+  for (auto& it : L.items) {
+    it.off = off;
+    off = align_up(off + it.bytes);
+  }
+  L.zero_off = off;
+  L.zero_len = std::max(kMaxCin, lpad_of(h * w));
+  off = align_up(off + (size_t)L.zero_len * 2);
+  L.total = off;
+  return L;
+}
+
+// Encoder rings: conv_in; per down stage s, ResBlock k, conv cv one each;
+// the temporal down-convs' two segments (first / second frame of a pair);
+// the mid block's four convs; the head.
+enum {
+  E_CONV_IN = 0,
+  E_DOWN_BASE = 1,                 // + 4 s + 2 k + cv
+  E_TD_BASE = E_DOWN_BASE + 16,    // + 2 k + half
+  E_MID_BASE = E_TD_BASE + 4,      // mid0 conv1, conv2, mid1 conv1, conv2
+  E_HEAD = E_MID_BASE + 4,
+  E_RING_COUNT = E_HEAD + 1
+};
+
+int enc_ring_down(int s, int k, int cv) { return E_DOWN_BASE + 4 * s + 2 * k + cv; }
+
+// Channels and level (0: h x w, ..., 3: 8h x 8w) of encoder ring id.
+RingInfo enc_ring_info(int c, int id) {
+  if (id == E_CONV_IN) return {16, 3};
+  if (id < E_TD_BASE) {
+    const int r = id - E_DOWN_BASE, s = r / 4, k = (r / 2) % 2, cv = r % 2;
+    const int cin = (k == 0 && cv == 0) ? (s == 0 ? c : enc_width(c, s - 1)) : enc_width(c, s);
+    return {cin, 3 - s};
+  }
+  if (id < E_MID_BASE) {
+    const int k = (id - E_TD_BASE) / 2;  // stage k + 1, after its spatial down-conv
+    return {enc_width(c, k + 1), 1 - k};
+  }
+  return {4 * c, 0};
+}
+
+Work make_work_enc(int c, int h, int w, int P) {
+  Work W;
+  const long long r0 = (long long)h * w;
+  const long long res[4] = {r0, 4 * r0, 16 * r0, 64 * r0};
+  const long long c4 = 4 * c, c2 = 2 * c;
+  const long long F0 = P, F1 = 2LL * P, F2 = 4LL * P;
+  const long long act = std::max({F2 * res[3] * std::max<long long>(c, 16), F2 * res[2] * c2, F2 * res[1] * c2,
+                                  F1 * res[1] * c4, F1 * res[0] * c4, F0 * res[0] * c4});
+  const long long L = r0, Lp = lpad_of((int)r0);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  W.X = take(act * 2);
+  W.H = take(act * 2);
+  W.Y = take(act * 2);
+  W.zt = W.zp = take(0);
+  W.rs = take((size_t)(F2 + 2) * res[3] * 4);
+  W.qkv = take((size_t)F0 * L * 3 * c4 * 2);
+  W.S = take((size_t)F0 * L * Lp * 4);
+  W.Pm = take((size_t)F0 * L * Lp * 2);
+  W.Vt = take((size_t)F0 * c4 * Lp * 2);
+  W.O = take((size_t)F0 * L * c4 * 2);
+  {
+    // Winograd planes of the ResBlock convs of each level (frames, input and
+    // output widths), as make_work does for the decoder.
+    struct Lv { long long F, H, W; long long cin[4], cout[4]; };
+    const Lv lv[4] = {
+        {F2, 8LL * h, 8LL * w, {c, c, c, c}, {c, c, c, c}},
+        {F2, 4LL * h, 4LL * w, {c, c2, c2, c2}, {c2, c2, c2, c2}},
+        {F1, 2LL * h, 2LL * w, {c2, c4, c4, c4}, {c4, c4, c4, c4}},
+        {F0, (long long)h, (long long)w, {c4, c4, c4, c4}, {c4, c4, c4, c4}},
+    };
+    long long u = 0, m = 0;
+    for (const Lv& l : lv) {
+      const long long wq = (l.W + kWinoM - 1) / kWinoM;
+      for (int i = 0; i < 4; ++i) {
+        if (!wino_ok((int)l.cin[i], (int)l.cout[i])) continue;
+        u = std::max(u, kWinoN * (l.F + 2) * l.H * wq * l.cin[i]);
+        m = std::max(m, kWinoN * l.F * l.H * wq * l.cout[i]);
+      }
+    }
+    W.U = take((size_t)u * 2);
+    W.M = take((size_t)m * 2);
+  }
+  size_t roff = 0;
+  for (int i = 0; i < E_RING_COUNT; ++i) {
+    RingInfo ri = enc_ring_info(c, i);
+    W.ring.push_back(roff);
+    roff = align_up(roff + (size_t)2 * res[ri.level] * ri.cin * 2);
+  }
+  W.ring_bytes = roff;
+  W.rings = take(roff);
+  W.total = off;
+  return W;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 struct ProfRec {
@@ -284,6 +439,8 @@ struct wvd_plan {
 namespace {
 
 bool plan_ok(const wvd_plan* p) { return p && p->magic == 0x77766470; }
+bool dec_plan_ok(const wvd_plan* p) { return plan_ok(p) && !p->L.encoder; }
+bool enc_plan_ok(const wvd_plan* p) { return plan_ok(p) && p->L.encoder; }
 
 int check_dims(int c, int h, int w) {
   if (c <= 0 || c % 16 != 0 || 4 * c > kMaxCin) return WVD_EUNSUPPORTED;
@@ -388,7 +545,9 @@ void set_grid(ConvArgs& a, int F, int H, int W, int TF, int TW = kTileW) {
     const ConvSeg& g = a.seg[s];
     const int hsy = g.KS == KS_1x1 ? 0 : 1;
     const int hsx = g.KS == KS_1x1 || g.KS == KS_3x1 ? 0 : 1;
-    const int nhv = (TF + g.KT - 1) * (a.TH + 2 * hsy) * (TW + 2 * hsx);
+    const int st = g.stride == 2 ? 2 : 1;
+    const int nhv = (TF + g.KT - 1) * (st * a.TH + 2 * hsy - (st - 1)) * (st * TW + 2 * hsx - (st - 1));
+    if (st == 2) np = 2;  // strided halos are staged in 16-channel chunks
     rows = std::max(rows, (nhv * np + 511) / 512 * 512 / np);  // whole rounds for 256 or 512 threads
     // the Winograd and up-conv epilogues stage their rows in one halo buffer
     if (g.KS == KS_3x1 || g.KS == KS_PHASE)
@@ -809,6 +968,51 @@ Act up_conv(Ctx& cx, int s, const Act& x, h16_t* ybuf) {
   return y;
 }
 
+// Prepares every item of layout L from the canonical tensors and returns the
+// plan (wvd_prepare and wvd_encoder_prepare).
+int prepare_plan(int c, int h, int w, const Layout& L, const void* const* weights, int weight_dtype, void* prepared,
+                 hipStream_t s, wvd_plan** plan_out) {
+  wvd_plan* p = new (std::nothrow) wvd_plan();
+  if (!p) return WVD_EINVAL;
+  p->c = c;
+  p->h = h;
+  p->w = w;
+  p->L = L;
+  p->prep = static_cast<unsigned char*>(prepared);
+  hipError_t e = hipSuccess;
+  for (size_t i = 0; i < L.items.size() && e == hipSuccess; ++i) {
+    const Item& it = L.items[i];
+    const void* src = weights[it.src >= 0 ? it.src : (int)i];
+    void* dst = p->prep + it.off;
+    if (it.kind == K_WINO)
+      e = launch_prep_wino_frag(src, weight_dtype, it.cout, it.cin, static_cast<h16_t*>(dst), s);
+    else if (it.kind == K_CONV)
+      e = launch_prep_frag(src, weight_dtype, it.cout, it.cin, it.taps, it.cin_pad, static_cast<h16_t*>(dst), s);
+    else if (it.kind == K_CONV_PART)
+      e = launch_prep_frag_part(src, weight_dtype, it.cout, it.cin_src, it.cin_off, it.cin, it.taps, it.cin_pad,
+                                static_cast<h16_t*>(dst), s);
+    else if (it.kind == K_PHASE)
+      e = launch_prep_phase_frag(src, weight_dtype, it.cout, static_cast<h16_t*>(dst), s);
+    else
+      e = launch_prep_vec(src, weight_dtype, it.n, it.scale, static_cast<float*>(dst), s);
+  }
+  if (e == hipSuccess) e = launch_fill_zero(p->prep + L.zero_off, align_up((size_t)L.zero_len * 2), s);
+  // Blocks with a shortcut add two biases; keep their sum in the shortcut slot.
+  const RB* sc_blocks[2] = {L.encoder ? &L.down[1][0] : &L.up[2][0], L.encoder ? &L.down[2][0] : &L.up[3][0]};
+  for (const RB* rb : sc_blocks) {
+    if (e != hipSuccess) break;
+    e = launch_prep_vec_add(weights[rb->conv2b], weights[rb->scb], weight_dtype, rb->cout,
+                            reinterpret_cast<float*>(p->prep + L.items[rb->scb].off), s);
+  }
+  if (e != hipSuccess) {
+    set_error(L.encoder ? "wvd_encoder_prepare" : "wvd_prepare", e);
+    delete p;
+    return WVD_EHIP;
+  }
+  *plan_out = p;
+  return WVD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -851,47 +1055,11 @@ int wvd_prepare(int c, int h, int w, const void* const* weights, int n_weights, 
   Layout L = make_layout(c, h, w, n_weights == WVD_NUM_WEIGHTS_DEEP);
   if ((int)L.items.size() != n_weights) return WVD_EINVAL;
   if (prepared_bytes < L.total) return WVD_ENOSPACE;
-  wvd_plan* p = new (std::nothrow) wvd_plan();
-  if (!p) return WVD_EINVAL;
-  p->c = c;
-  p->h = h;
-  p->w = w;
-  p->L = L;
-  p->prep = static_cast<unsigned char*>(prepared);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = hipSuccess;
-  for (int i = 0; i < n_weights && e == hipSuccess; ++i) {
-    const Item& it = L.items[i];
-    const void* src = weights[i];
-    void* dst = p->prep + it.off;
-    if (it.kind == K_WINO)
-      e = launch_prep_wino_frag(src, weight_dtype, it.cout, it.cin, static_cast<h16_t*>(dst), s);
-    else if (it.kind == K_CONV)
-      e = launch_prep_frag(src, weight_dtype, it.cout, it.cin, it.taps, it.cin_pad, static_cast<h16_t*>(dst), s);
-    else if (it.kind == K_PHASE)
-      e = launch_prep_phase_frag(src, weight_dtype, it.cout, static_cast<h16_t*>(dst), s);
-    else
-      e = launch_prep_vec(src, weight_dtype, it.n, it.scale, static_cast<float*>(dst), s);
-  }
-  if (e == hipSuccess) e = launch_fill_zero(p->prep + L.zero_off, align_up((size_t)L.zero_len * 2), s);
-  // Blocks with a shortcut add two biases; keep their sum in the shortcut slot.
-  const RB* sc_blocks[2] = {&L.up[2][0], &L.up[3][0]};
-  for (const RB* rb : sc_blocks) {
-    if (e != hipSuccess) break;
-    e = launch_prep_vec_add(weights[rb->conv2b], weights[rb->scb], weight_dtype, rb->cout,
-                            reinterpret_cast<float*>(p->prep + L.items[rb->scb].off), s);
-  }
-  if (e != hipSuccess) {
-    set_error("wvd_prepare", e);
-    delete p;
-    return WVD_EHIP;
-  }
-  *plan_out = p;
-  return WVD_OK;
+  return prepare_plan(c, h, w, L, weights, weight_dtype, prepared, static_cast<hipStream_t>(stream), plan_out);
 }
 
 int wvd_workspace_bytes(const wvd_plan* plan, int T, int frames_per_pass, size_t* bytes) {
-  if (!plan_ok(plan) || !bytes || T < 1 || frames_per_pass < 1) return WVD_EINVAL;
+  if (!dec_plan_ok(plan) || !bytes || T < 1 || frames_per_pass < 1) return WVD_EINVAL;
   const int P = std::min(T, frames_per_pass);
   *bytes = make_work(plan->c, plan->h, plan->w, P, true, plan->L.nrb).total;
   return WVD_OK;
@@ -1024,13 +1192,170 @@ int decode_impl(wvd_plan* plan, const void* z, int z_dtype, int T, int t_begin, 
   return WVD_OK;
 }
 
+
+// ---------------------------------------------------------------------------
+// Encoder (R13-R16): video [1, 3, 4T-3, 16h, 16w] -> latents [1, 48, T, h, w]
+// ---------------------------------------------------------------------------
+
+// Spatial down-conv (R14): Conv2d 3x3, stride 2, zero pad 1, per frame:
+// x [F][2H][2W][C] -> y [F][H][W][Cout].
+Act down_conv(Ctx& cx, int s, const Act& x, h16_t* ybuf) {
+  const Layout& L = cx.plan->L;
+  Act y{ybuf, x.C, x.F, x.H / 2, x.W / 2};
+  ConvArgs a = args_init();
+  a.seg[0] = seg_basic(x.p, x.fstride(), x.C, x.C, cx.prep<h16_t>(L.dc_w[s]), x.C, 0, 1, KS_3x3,
+                       cx.wbytes(L.dc_w[s]));
+  a.seg[0].stride = 2;
+  a.nseg = 1;
+  a.Cout = x.C;
+  a.bias = cx.prep<float>(L.dc_b[s]);
+  a.out = y.p;
+  a.out_fstride = y.fstride();
+  a.ldo = y.C;
+  a.epi = EPI_H16;
+  set_grid(a, y.F, y.H, y.W, 1);
+  conv(cx, a, 1);
+  return y;
+}
+
+// Temporal down-conv (R15) of stage k + 1: x (F frames, the clip's first
+// frame first when `first`) -> y.  The clip's first frame is copied; the
+// pairs (2s+1, 2s+2) after it (or (2s, 2s+1) in a later pass) are the two K
+// segments of one causal 3x1x1 conv, each reading every second frame and
+// carrying its own two history frames.
+Act time_down(Ctx& cx, int k, const Act& x, bool first, h16_t* ybuf, int nh) {
+  const Layout& L = cx.plan->L;
+  const int npairs = first ? (x.F - 1) / 2 : x.F / 2;
+  Act y{ybuf, x.C, npairs + (first ? 1 : 0), x.H, x.W};
+  if (first) {
+    cx.what = "copy";
+    cx.run(4, 0, [&] { return launch_copy16(y.p, x.p, (size_t)x.fstride() * 2, cx.st); });
+  }
+  if (npairs == 0) return y;
+  const h16_t* p0 = first ? x.p + x.fstride() : x.p;  // first frame of the first pair
+  const long long pstride = 2 * x.fstride();
+  ConvArgs a = args_init();
+  for (int h = 0; h < 2; ++h) {
+    a.seg[h] = seg_basic(p0 + h * x.fstride(), pstride, x.C, x.C, cx.prep<h16_t>(L.td_w[k][h]), x.C, 0, 3, KS_1x1,
+                         cx.wbytes(L.td_w[k][h]));
+    a.seg[h].ring = cx.ring(E_TD_BASE + 2 * k + h);
+    a.seg[h].n_hist = nh;
+  }
+  a.nseg = 2;
+  a.Cout = x.C;
+  a.bias = cx.prep<float>(L.td_b[k]);
+  a.out = y.p + (first ? y.fstride() : 0);
+  a.out_fstride = y.fstride();
+  a.ldo = y.C;
+  a.epi = EPI_H16;
+  set_grid(a, npairs, x.H, x.W, tf_for(3, npairs));
+  conv(cx, a, 1);
+  for (int h = 0; h < 2; ++h) {
+    h16_t* ring = cx.ring(E_TD_BASE + 2 * k + h);
+    cx.what = "ring_update";
+    cx.run(4, 0, [&] {
+      return launch_ring_update(ring, p0 + h * x.fstride(), pstride, x.C, x.C, npairs, x.H * x.W, cx.st);
+    });
+  }
+  return y;
+}
+
+int encode_impl(wvd_plan* plan, const void* video, int v_dtype, int T, int frames_per_pass, float* latents,
+                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int c = plan->c, h = plan->h, w = plan->w;
+  const int P = std::min(T, frames_per_pass);
+  Work W = make_work_enc(c, h, w, P);
+  if (workspace_bytes < W.total) return WVD_ENOSPACE;
+  const Layout& L = plan->L;
+  Ctx cx;
+  cx.plan = plan;
+  cx.st = stream;
+  cx.ws = static_cast<unsigned char*>(workspace);
+  cx.W = &W;
+  cx.ringbase = cx.ws + W.rings;
+  plan->launches = 0;
+  const int c4 = 4 * c;
+  h16_t* X = cx.wsp<h16_t>(W.X);
+  h16_t* Hb = cx.wsp<h16_t>(W.H);
+  h16_t* Y = cx.wsp<h16_t>(W.Y);
+  const int Tv = 4 * T - 3;
+  for (int t0 = 0; t0 < T && cx.err == hipSuccess; t0 += P) {
+    const int F0 = std::min(P, T - t0);
+    const bool first = t0 == 0;
+    const int vb = first ? 0 : 4 * t0 - 3;  // first video frame of the pass
+    const int F2 = first ? 4 * F0 - 3 : 4 * F0;
+    const int g2 = vb, g1 = first ? 0 : 2 * t0 - 1, g0 = t0;
+    const int nh2 = std::min(2, g2), nh1 = std::min(2, g1), nh0 = std::min(2, g0);
+    // 2x2 patchify into 16 channels (12 + zero pad), then conv_in 12 -> c.
+    Act zt{Y, 16, F2, 8 * h, 8 * w};
+    cx.what = "patchify";
+    cx.run(4, 0, [&] { return launch_patchify(video, v_dtype, Tv, vb, F2, 8 * h, 8 * w, Y, cx.st); });
+    Act x{X, c, F2, 8 * h, 8 * w};
+    {
+      h16_t* ring = cx.ring(E_CONV_IN);
+      ConvArgs a = args_init();
+      a.seg[0] = seg_basic(zt.p, zt.fstride(), 16, 16, cx.prep<h16_t>(L.conv_in_w), 16, 0, 3, KS_3x3,
+                           cx.wbytes(L.conv_in_w));
+      a.seg[0].ring = ring;
+      a.seg[0].n_hist = nh2;
+      a.nseg = 1;
+      a.Cout = c;
+      a.bias = cx.prep<float>(L.conv_in_b);
+      a.out = x.p;
+      a.out_fstride = x.fstride();
+      a.ldo = c;
+      a.epi = EPI_H16;
+      set_grid(a, F2, x.H, x.W, tf_for(3, F2));
+      conv(cx, a, 1);
+      ring_update(cx, ring, zt);
+    }
+    // Stage 0 (8h x 8w, c), down to 4h x 4w.
+    x = resblock(cx, L.down[0][0], x, Hb, nullptr, enc_ring_down(0, 0, 0), enc_ring_down(0, 0, 1), nh2);
+    x = resblock(cx, L.down[0][1], x, Hb, nullptr, enc_ring_down(0, 1, 0), enc_ring_down(0, 1, 1), nh2);
+    x = down_conv(cx, 0, x, Y);
+    // Stage 1 (4h x 4w, c -> 2c), down to 2h x 2w, frames 4T-3 -> 2T-1.
+    x = resblock(cx, L.down[1][0], x, Hb, X, enc_ring_down(1, 0, 0), enc_ring_down(1, 0, 1), nh2);
+    x = resblock(cx, L.down[1][1], x, Hb, nullptr, enc_ring_down(1, 1, 0), enc_ring_down(1, 1, 1), nh2);
+    x = down_conv(cx, 1, x, Y);
+    x = time_down(cx, 0, x, first, X, first ? 0 : std::min(2, 2 * t0 - 2));
+    // Stage 2 (2h x 2w, 2c -> 4c), down to h x w, frames 2T-1 -> T.
+    x = resblock(cx, L.down[2][0], x, Hb, Y, enc_ring_down(2, 0, 0), enc_ring_down(2, 0, 1), nh1);
+    x = resblock(cx, L.down[2][1], x, Hb, nullptr, enc_ring_down(2, 1, 0), enc_ring_down(2, 1, 1), nh1);
+    x = down_conv(cx, 2, x, X);
+    x = time_down(cx, 1, x, first, Y, first ? 0 : std::min(2, t0 - 1));
+    // Stage 3 (h x w, 4c), then the mid block.
+    x = resblock(cx, L.down[3][0], x, Hb, nullptr, enc_ring_down(3, 0, 0), enc_ring_down(3, 0, 1), nh0);
+    x = resblock(cx, L.down[3][1], x, Hb, nullptr, enc_ring_down(3, 1, 0), enc_ring_down(3, 1, 1), nh0);
+    x = resblock(cx, L.mid0, x, Hb, nullptr, E_MID_BASE, E_MID_BASE + 1, nh0);
+    attention(cx, x);
+    x = resblock(cx, L.mid1, x, Hb, nullptr, E_MID_BASE + 2, E_MID_BASE + 3, nh0);
+    // Head: RMSNorm + SiLU in the conv prologue, causal 3x3x3 conv 4c -> 48,
+    // fp32 NCTHW latents.
+    {
+      h16_t* ring = cx.ring(E_HEAD);
+      stats(cx, x, ring, nh0);
+      ConvArgs a = conv333(cx, x, ring, nh0, L.head_norm, L.head_w, L.head_b, 48);
+      a.out = latents;
+      a.epi = EPI_LATENT;
+      a.out_base = t0;
+      a.video_T = T;
+      set_grid(a, x.F, x.H, x.W, tf_for(3, x.F));
+      conv(cx, a, 1);
+      ring_update(cx, ring, x);
+    }
+    (void)c4;
+  }
+  if (cx.err != hipSuccess) return WVD_EHIP;
+  return WVD_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 int wvd_decode(const wvd_plan* cplan, const void* z, int z_dtype, int T, int frames_per_pass, void* out,
                void* workspace, size_t workspace_bytes, void* stream) {
-  if (!plan_ok(cplan) || !z || !out || !workspace || T < 1 || frames_per_pass < 1) return WVD_EINVAL;
+  if (!dec_plan_ok(cplan) || !z || !out || !workspace || T < 1 || frames_per_pass < 1) return WVD_EINVAL;
   if (z_dtype != WVD_DTYPE_BF16 && z_dtype != WVD_DTYPE_F32) return WVD_EINVAL;
   if (!aligned16(workspace)) return WVD_EINVAL;
   return decode_impl(const_cast<wvd_plan*>(cplan), z, z_dtype, T, 0, frames_per_pass, nullptr, out, workspace,
@@ -1090,7 +1415,7 @@ int static_workspace(void** addr) {
 
 int wvd_decode_static(const wvd_plan* cplan, const void* z, int z_dtype, int T, int frames_per_pass, void* out,
                       void* stream) {
-  if (!plan_ok(cplan) || !z || !out || T < 1 || frames_per_pass < 1) return WVD_EINVAL;
+  if (!dec_plan_ok(cplan) || !z || !out || T < 1 || frames_per_pass < 1) return WVD_EINVAL;
   if (z_dtype != WVD_DTYPE_BF16 && z_dtype != WVD_DTYPE_F32) return WVD_EINVAL;
   const int P = std::min(T, frames_per_pass);
   const size_t need = make_work(cplan->c, cplan->h, cplan->w, P, true, cplan->L.nrb).total;
@@ -1108,13 +1433,13 @@ int wvd_decode_static(const wvd_plan* cplan, const void* z, int z_dtype, int T, 
 }
 
 int wvd_state_bytes(const wvd_plan* plan, size_t* bytes) {
-  if (!plan_ok(plan) || !bytes) return WVD_EINVAL;
+  if (!dec_plan_ok(plan) || !bytes) return WVD_EINVAL;
   *bytes = make_work(plan->c, plan->h, plan->w, 1, false, plan->L.nrb).ring_bytes;
   return WVD_OK;
 }
 
 int wvd_chunk_workspace_bytes(const wvd_plan* plan, int T, int frames_per_pass, size_t* bytes) {
-  if (!plan_ok(plan) || !bytes || T < 1 || frames_per_pass < 1) return WVD_EINVAL;
+  if (!dec_plan_ok(plan) || !bytes || T < 1 || frames_per_pass < 1) return WVD_EINVAL;
   *bytes = make_work(plan->c, plan->h, plan->w, std::min(T, frames_per_pass), false, plan->L.nrb).total;
   return WVD_OK;
 }
@@ -1122,7 +1447,7 @@ int wvd_chunk_workspace_bytes(const wvd_plan* plan, int T, int frames_per_pass, 
 int wvd_decode_chunk(const wvd_plan* cplan, const void* z, int z_dtype, int T, int t_begin, int frames_per_pass,
                      void* state, size_t state_bytes, void* out, void* workspace, size_t workspace_bytes,
                      void* stream) {
-  if (!plan_ok(cplan) || !z || !out || !workspace || !state || T < 1 || t_begin < 0 || frames_per_pass < 1)
+  if (!dec_plan_ok(cplan) || !z || !out || !workspace || !state || T < 1 || t_begin < 0 || frames_per_pass < 1)
     return WVD_EINVAL;
   if (z_dtype != WVD_DTYPE_BF16 && z_dtype != WVD_DTYPE_F32) return WVD_EINVAL;
   if (!aligned16(workspace) || !aligned16(state)) return WVD_EINVAL;
@@ -1207,6 +1532,47 @@ int wvd_profile_read(const wvd_plan* cplan, double* ms, double* flops, long long
   plan->recs.clear();
   plan->pool_used = 0;
   return WVD_OK;
+}
+
+// ---- encoder ----
+
+int wvd_encoder_prepared_bytes(int c, int h, int w, size_t* bytes) {
+  if (!bytes) return WVD_EINVAL;
+  int st = check_dims(c, h, w);
+  if (st) return st;
+  *bytes = make_layout_enc(c, h, w).total;
+  return WVD_OK;
+}
+
+int wvd_encoder_prepare(int c, int h, int w, const void* const* weights, int n_weights, int weight_dtype,
+                        void* prepared, size_t prepared_bytes, void* stream, wvd_plan** plan_out) {
+  if (!weights || !prepared || !plan_out) return WVD_EINVAL;
+  if (weight_dtype != WVD_DTYPE_BF16 && weight_dtype != WVD_DTYPE_F32) return WVD_EINVAL;
+  int st = check_dims(c, h, w);
+  if (st) return st;
+  if (n_weights != WVD_NUM_WEIGHTS_ENCODER) return WVD_EINVAL;
+  for (int i = 0; i < n_weights; ++i)
+    if (!weights[i]) return WVD_EINVAL;
+  if (!aligned16(prepared)) return WVD_EINVAL;
+  Layout L = make_layout_enc(c, h, w);
+  if (prepared_bytes < L.total) return WVD_ENOSPACE;
+  return prepare_plan(c, h, w, L, weights, weight_dtype, prepared, static_cast<hipStream_t>(stream), plan_out);
+}
+
+int wvd_encode_workspace_bytes(const wvd_plan* plan, int T, int frames_per_pass, size_t* bytes) {
+  if (!enc_plan_ok(plan) || !bytes || T < 1 || frames_per_pass < 1) return WVD_EINVAL;
+  *bytes = make_work_enc(plan->c, plan->h, plan->w, std::min(T, frames_per_pass)).total;
+  return WVD_OK;
+}
+
+int wvd_encode(const wvd_plan* cplan, const void* video, int video_dtype, int T, int frames_per_pass, float* latents,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  if (!enc_plan_ok(cplan) || !video || !latents || !workspace || T < 1 || frames_per_pass < 1) return WVD_EINVAL;
+  if (video_dtype != WVD_DTYPE_BF16 && video_dtype != WVD_DTYPE_F32) return WVD_EINVAL;
+  if (!aligned16(workspace)) return WVD_EINVAL;
+  if (T > (1 << 28)) return WVD_EINVAL;
+  return encode_impl(const_cast<wvd_plan*>(cplan), video, video_dtype, T, frames_per_pass, latents, workspace,
+                     workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -223,6 +223,33 @@ __global__ __launch_bounds__(256) void latent_to_cl_kernel(const void* __restric
   }
 }
 
+// Encoder input: frames t0.. of the video [3][T][2H][2W] -> [F][H][W][16]
+// fp16 with channel 4k + 2dy + dx = pixel (2Y+dy, 2X+dx) of colour k (the
+// inverse of the decoder's pixel shuffle) and channels 12..15 zero.
+__global__ __launch_bounds__(256) void patchify_kernel(const void* __restrict__ v, int dtype, int T, int t0, int F,
+                                                       int H, int W, h16_t* __restrict__ out) {
+  const long long n = (long long)F * H * W;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+       e += (long long)gridDim.x * blockDim.x) {
+    const int X = (int)(e % W);
+    const int Y = (int)((e / W) % H);
+    const long long f = e / ((long long)W * H);
+    float c[16];
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const long long row = ((long long)k * T + t0 + f) * (2 * H) + 2 * Y + (d >> 1);
+        c[4 * k + d] = load_in(v, row * (2 * W) + 2 * X + (d & 1), dtype);
+      }
+#pragma unroll
+    for (int k = 12; k < 16; ++k) c[k] = 0.0f;
+    uint4* dst = reinterpret_cast<uint4*>(out + e * 16);
+    dst[0] = pack8h(c);
+    dst[1] = pack8h(c + 8);
+  }
+}
+
 __global__ __launch_bounds__(256) void copy16_kernel(uint4* __restrict__ dst, const uint4* __restrict__ src, long long n) {
   for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n;
        e += (long long)gridDim.x * blockDim.x)
@@ -286,8 +313,8 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const h16_t* __restric
 
 // Fragment-order conv weights (layout in wvd_internal.h) from the PyTorch
 // layout w[o][i][tap] (taps flattened).
-__global__ void prep_frag_kernel(const void* __restrict__ w, int dtype, int cout, int cin, int taps, int cin_pad,
-                                 h16_t* __restrict__ out) {
+__global__ void prep_frag_kernel(const void* __restrict__ w, int dtype, int cout, int cin_src, int cin_off, int cin,
+                                 int taps, int cin_pad, h16_t* __restrict__ out) {
   const int NB = (cout + 127) / 128 * 4, U = cin_pad / 16;
   const long long n = (long long)NB * U * taps * 512;
   for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n;
@@ -300,7 +327,9 @@ __global__ void prep_frag_kernel(const void* __restrict__ w, int dtype, int cout
     const int nb = (int)(blk / ((long long)taps * U));
     const int o = nb * 32 + (l & 31);
     const int i = u * 16 + (l >> 5) * 8 + j;
-    out[e] = (o < cout && i < cin) ? (h16_t)f2h(load_in(w, ((long long)o * cin + i) * taps + t, dtype)) : (h16_t)0;
+    out[e] = (o < cout && i < cin)
+                 ? (h16_t)f2h(load_in(w, ((long long)o * cin_src + cin_off + i) * taps + t, dtype))
+                 : (h16_t)0;
   }
 }
 
@@ -981,6 +1010,15 @@ hipError_t launch_latent_to_cl(const void* z, int dtype, int T, int t0, int F, i
   return hipGetLastError();
 }
 
+hipError_t launch_patchify(const void* video, int dtype, int T, int t0, int F, int H, int W, h16_t* out,
+                           hipStream_t s) {
+  if (g_dry_run) return hipSuccess;
+  const long long n = (long long)F * H * W;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(patchify_kernel, dim3(grid_for(n)), dim3(256), 0, s, video, dtype, T, t0, F, H, W, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_copy16(void* dst, const void* src, size_t bytes, hipStream_t s) {
   if (g_dry_run) return hipSuccess;
   const long long n = (long long)(bytes / 16);
@@ -1017,7 +1055,18 @@ hipError_t launch_prep_frag(const void* w, int dtype, int cout, int cin, int tap
                             hipStream_t s) {
   if (g_dry_run) return hipSuccess;
   const long long n = (long long)prep_frag_bytes(cout, cin_pad, taps) / 2;
-  hipLaunchKernelGGL(prep_frag_kernel, dim3(grid_for(n)), dim3(256), 0, s, w, dtype, cout, cin, taps, cin_pad, out);
+  hipLaunchKernelGGL(prep_frag_kernel, dim3(grid_for(n)), dim3(256), 0, s, w, dtype, cout, cin, 0, cin, taps,
+                     cin_pad, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep_frag_part(const void* w, int dtype, int cout, int cin_src, int cin_off, int cin, int taps,
+                                 int cin_pad, h16_t* out, hipStream_t s) {
+  if (g_dry_run) return hipSuccess;
+  if (cin_off < 0 || cin_off + cin > cin_src || cin > cin_pad) return hipErrorInvalidValue;
+  const long long n = (long long)prep_frag_bytes(cout, cin_pad, taps) / 2;
+  hipLaunchKernelGGL(prep_frag_kernel, dim3(grid_for(n)), dim3(256), 0, s, w, dtype, cout, cin_src, cin_off, cin,
+                     taps, cin_pad, out);
   return hipGetLastError();
 }
 

@@ -542,8 +542,10 @@ __global__ __launch_bounds__(NW * 64) void conv_igemm(ConvArgs a) {
     const int KT = spec ? 3 : S.KT;
     const int hs = spec ? 1 : (S.KS == 1 ? 0 : 1);
     const int K2 = spec ? 3 : (S.KS == 3 ? 3 : (S.KS == 2 ? 2 : 1));
-    const int HX = kTileW + 2 * hs;
-    const int HY = TH + 2 * hs;
+    const int st = S.stride == 2 ? 2 : 1;   // input rows/columns per output row/column
+    const int HX = st * kTileW + 2 * hs - (st - 1);
+    const int HY = st * TH + 2 * hs - (st - 1);
+    const int IH = st * a.H, IW = st * a.W;  // input grid
     const int HF = TF + KT - 1;
     const int nhv = HF * HY * HX;
     const int ntaps = KT * K2 * K2;
@@ -564,10 +566,10 @@ __global__ __launch_bounds__(NW * 64) void conv_igemm(ConvArgs a) {
         const int hy = t2 % HY;
         const int hf = t2 / HY;
         const int fo = f0 + hf - (KT - 1);
-        const int y = y0 + hy - hs;
-        const int x = x0 + hx - hs;
-        if (y >= 0 && y < a.H && x >= 0 && x < a.W && fo < a.F) {
-          const long long pix = (long long)y * a.W + x;
+        const int y = st * y0 + hy - hs;
+        const int x = st * x0 + hx - hs;
+        if (y >= 0 && y < IH && x >= 0 && x < IW && fo < a.F) {
+          const long long pix = (long long)y * IW + x;
           const h16_t* q = nullptr;
           if (fo >= 0) {
             q = S.x + fo * S.x_fstride + pix * S.lda;
@@ -599,7 +601,7 @@ __global__ __launch_bounds__(NW * 64) void conv_igemm(ConvArgs a) {
       const int m = wave_m * WM + 32 * i + lrow;
       const int tx = m & (kTileW - 1);
       const int t2 = m / kTileW;
-      g.abase[i] = (((t2 / TH) * HY + (t2 % TH)) * HX + tx) * ROWB + kpart * 16;
+      g.abase[i] = (((t2 / TH) * HY + st * (t2 % TH)) * HX + st * tx) * ROWB + kpart * 16;
     }
     const int U = S.Cin / 16;
     g.wtaps = a.nphase * ntaps;
@@ -707,6 +709,12 @@ __global__ __launch_bounds__(NW * 64) void conv_igemm(ConvArgs a) {
         float* o = static_cast<float*>(a.out) + f * a.out_fstride + pix * a.ldo;
         for (int c = 0; c < CPL && nb + c < a.Cout; ++c)
           o[nb + c] = row[c] * a.scale + (a.bias ? a.bias[nb + c] : 0.0f);
+      } else if (a.epi == EPI_LATENT) {
+        float* o = static_cast<float*>(a.out);
+        for (int c = 0; c < CPL && nb + c < a.Cout; ++c) {
+          const int n = nb + c;
+          o[((long long)n * a.video_T + a.out_base + f) * HW + pix] = row[c] * a.scale + (a.bias ? a.bias[n] : 0.0f);
+        }
       } else {
         // fp16 channels-last destinations: plain, time-interleaved or phase.
         h16_t* o;
@@ -1436,7 +1444,7 @@ hipError_t launch_impl(const ConvArgs& a, hipStream_t stream) {
 
 int conv_bk(const ConvArgs& a) {
   for (int s = 0; s < a.nseg; ++s)
-    if (a.seg[s].Cin % 32) return 16;
+    if (a.seg[s].Cin % 32 || a.seg[s].stride == 2) return 16;  // strided halos are 4x larger: 16-channel chunks
   return 32;
 }
 
@@ -1749,7 +1757,8 @@ const char* conv_check(const ConvArgs& a) {
     const int hsy = g.KS == KS_1x1 ? 0 : 1;
     const int hsx = g.KS == KS_1x1 || g.KS == KS_3x1 ? 0 : 1;
     const int k2 = g.KS == KS_3x3 ? 9 : (g.KS == KS_PHASE ? 4 : (g.KS == KS_3x1 ? 3 : 1));
-    const int nhv = (a.TF + g.KT - 1) * (a.TH + 2 * hsy) * (a.TW + 2 * hsx);
+    const int st = g.stride == 2 ? 2 : 1;
+    const int nhv = (a.TF + g.KT - 1) * (st * a.TH + 2 * hsy - (st - 1)) * (st * a.TW + 2 * hsx - (st - 1));
     const int nt = conv_variant(a).nw * 64;
     const int ipt = (nhv * (bk / 8) + nt - 1) / nt;
     const int ntaps = g.KT * k2;
@@ -1780,8 +1789,16 @@ const char* conv_check(const ConvArgs& a) {
     if (g.prologue != PRO_RAW && (g.Cin > kMaxCin || !g.rs || !g.gamma)) return "norm prologue operands";
     if (g.n_hist < 0 || g.n_hist > 2 || (g.n_hist > 0 && (!g.ring || g.KT != 3))) return "history ring";
     if (g.w_frame_stride && a.TF != 1) return "per-frame operands need TF == 1";
-    if (s > 0 && (g.KT != 1 || g.KS != 1)) return "second segment must be 1x1x1";
+    if (g.stride != 0 && g.stride != 1 && g.stride != 2) return "stride must be 1 or 2";
+    if (g.stride == 2 && (g.KT != 1 || g.KS != KS_3x3 || g.prologue != PRO_RAW || g.n_hist != 0 ||
+                          conv_variant(a).mode != 0 || a.nphase != 1 || a.nseg != 1))
+      return "stride 2 only for a raw one-segment 3x3 conv on the generic kernel";
+    if (s > 0 && (g.KT != 1 || g.KS != 1) && conv_variant(a).mode != 0)
+      return "the specialised kernels take only a 1x1x1 second segment";
+    if (s > 0 && g.KS != KS_1x1) return "second segment must have 1x1 spatial taps";
   }
+  if (a.epi == EPI_LATENT && (conv_persistent(a) || a.video_T < 1 || a.out_base < 0 || a.out_base + a.F > a.video_T))
+    return "latent epilogue: generic kernel, frames inside the clip";
   if (!a.out || !a.zero_row) return "null output or zero row";
   return nullptr;
 }

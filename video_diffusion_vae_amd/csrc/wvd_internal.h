@@ -29,7 +29,9 @@ enum Epilogue {
   EPI_TIME = 2,    // time_conv: channels [0,C) -> frame 2s+base, [C,2C) -> 2s+1+base
   EPI_PHASE = 3,   // up-conv phase (py,px): voxel (y,x) -> (2y+py, 2x+px)
   EPI_VIDEO = 4,   // head: 2x2 pixel shuffle of 12 channels, clamp, NCTHW video
-  EPI_WINO = 5     // Winograd-domain product M[xi] (fp16, no bias): out + xi * out_pstride
+  EPI_WINO = 5,    // Winograd-domain product M[xi] (fp16, no bias): out + xi * out_pstride
+  EPI_LATENT = 6   // encoder head: fp32 NCTHW latents, channel n of frame f -> [n][out_base + f]
+                   // of a clip of video_T frames (generic kernel only)
 };
 
 // Spatial tap codes of a K segment (ConvSeg::KS).
@@ -59,6 +61,10 @@ struct ConvSeg {
   int wfrag;                // 1: w is in MFMA fragment order (see launch_prep_frag)
   long long w_bytes;        // bytes of w (fragment order: bounds of the buffer loads)
   long long x_pstride;      // per-phase input offset (Winograd xi planes), else 0
+  int stride;               // spatial stride: 0 or 1, or 2 (the encoder's down-convs: the
+                            // input grid is 2H x 2W, output voxel (y, x) reads input
+                            // rows 2y-1..2y+1 and columns 2x-1..2x+1; generic kernel,
+                            // one frame, KT = 1, raw input)
 };
 
 struct ConvArgs {
@@ -139,6 +145,16 @@ hipError_t launch_transpose_v(const h16_t* qkv, int F, int L, int C, int Lpad, h
 size_t prep_frag_bytes(int cout, int cin_pad, int taps);
 hipError_t launch_prep_frag(const void* w, int dtype, int cout, int cin, int taps, int cin_pad, h16_t* out,
                             hipStream_t s);
+// The same for input channels [cin_off, cin_off + cin) of a tensor with
+// cin_src input channels (one operand of a conv split into K segments).
+hipError_t launch_prep_frag_part(const void* w, int dtype, int cout, int cin_src, int cin_off, int cin, int taps,
+                                 int cin_pad, h16_t* out, hipStream_t s);
+// Encoder input: video [3][T][2H][2W] (bf16 or fp32; NCTHW without the batch)
+// frames t0..t0+F-1 -> channels-last fp16 [F][H][W][16], channel 4k+2dy+dx =
+// pixel (2Y+dy, 2X+dx) of colour k (the inverse of the 2x2 pixel shuffle),
+// channels 12..15 zero.
+hipError_t launch_patchify(const void* video, int dtype, int T, int t0, int F, int H, int W, h16_t* out,
+                           hipStream_t s);
 // Up-conv phase weights in the same fragment order with taps = 16
 // (phase * 4 + 2x2 tap).
 hipError_t launch_prep_phase_frag(const void* w, int dtype, int C, h16_t* out, hipStream_t s);

@@ -21,6 +21,7 @@ WVD_EUNSUPPORTED = -4
 WVD_EHIP = -5
 NUM_WEIGHTS = 84
 NUM_WEIGHTS_DEEP = 110  # deep variant: pre_conv + three ResBlocks per up stage
+NUM_WEIGHTS_ENCODER = 84
 WVD_RANGE_SATURATED = 1
 WVD_RANGE_NAN = 2
 WVD_DTYPE_BF16 = 0
@@ -62,6 +63,14 @@ def _load() -> ctypes.CDLL:
     lib.wvd_chunk_workspace_bytes.restype = i
     lib.wvd_decode_chunk.argtypes = [vp, vp, i, i, i, i, vp, sz, vp, vp, sz, vp]
     lib.wvd_decode_chunk.restype = i
+    lib.wvd_encoder_prepared_bytes.argtypes = [i, i, i, ctypes.POINTER(sz)]
+    lib.wvd_encoder_prepared_bytes.restype = i
+    lib.wvd_encoder_prepare.argtypes = [i, i, i, ctypes.POINTER(vp), i, i, vp, sz, vp, ctypes.POINTER(vp)]
+    lib.wvd_encoder_prepare.restype = i
+    lib.wvd_encode_workspace_bytes.argtypes = [vp, i, i, ctypes.POINTER(sz)]
+    lib.wvd_encode_workspace_bytes.restype = i
+    lib.wvd_encode.argtypes = [vp, vp, i, i, i, vp, vp, sz, vp]
+    lib.wvd_encode.restype = i
     lib.wvd_destroy.argtypes = [vp]
     lib.wvd_destroy.restype = None
     lib.wvd_status_string.argtypes = [i]
@@ -164,6 +173,33 @@ def wvd_decode_chunk(plan: int, z_ptr: int, z_dtype: int, T: int, t_begin: int, 
                      stream_ptr: int) -> None:
     _check(_lib.wvd_decode_chunk(plan, z_ptr, z_dtype, T, t_begin, frames_per_pass, state_ptr, state_bytes, out_ptr,
                                  ws_ptr, ws_bytes, stream_ptr), "wvd_decode_chunk")
+
+
+def wvd_encoder_prepared_bytes(c: int, h: int, w: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.wvd_encoder_prepared_bytes(c, h, w, ctypes.byref(n)), "wvd_encoder_prepared_bytes")
+    return n.value
+
+
+def wvd_encoder_prepare(c: int, h: int, w: int, weight_ptrs: Sequence[int], weight_dtype: int, prepared_ptr: int,
+                        prepared_bytes: int, stream_ptr: int) -> int:
+    arr = (ctypes.c_void_p * len(weight_ptrs))(*weight_ptrs)
+    plan = ctypes.c_void_p(0)
+    _check(_lib.wvd_encoder_prepare(c, h, w, arr, len(weight_ptrs), weight_dtype, prepared_ptr, prepared_bytes,
+                                    stream_ptr, ctypes.byref(plan)), "wvd_encoder_prepare")
+    return plan.value
+
+
+def wvd_encode_workspace_bytes(plan: int, T: int, frames_per_pass: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.wvd_encode_workspace_bytes(plan, T, frames_per_pass, ctypes.byref(n)), "wvd_encode_workspace_bytes")
+    return n.value
+
+
+def wvd_encode(plan: int, video_ptr: int, video_dtype: int, T: int, frames_per_pass: int, latents_ptr: int,
+               ws_ptr: int, ws_bytes: int, stream_ptr: int) -> None:
+    _check(_lib.wvd_encode(plan, video_ptr, video_dtype, T, frames_per_pass, latents_ptr, ws_ptr, ws_bytes,
+                           stream_ptr), "wvd_encode")
 
 
 def video_frames(t: int) -> int:
@@ -328,3 +364,77 @@ class DecodeStream:
                          workspace.data_ptr(), workspace.numel(), stream.cuda_stream)
         self.t += T
         return out
+
+
+class Encoder:
+    """Prepared encoder (the decoder's mirror image) for base width c at
+    latent size h x w on the current CUDA (HIP) device.  `weights` are its 84
+    tensors in canonical order (video_diffusion_vae_amd.synth_encoder), as
+    numpy arrays or tensors; float32 weights are handed over as fp32, any
+    other float type as bf16."""
+
+    def __init__(self, weights: Union[Sequence, Dict[str, object]], c: int, h: int, w: int, device=None):
+        import torch
+
+        self.torch = torch
+        self.c, self.h, self.w = int(c), int(h), int(w)
+        self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        ws = list(weights.values()) if isinstance(weights, dict) else list(weights)
+        if len(ws) != NUM_WEIGHTS_ENCODER:
+            raise WvdError(WVD_EINVAL, f"Encoder: expected {NUM_WEIGHTS_ENCODER} weights, got {len(ws)}")
+        ts = [torch.as_tensor(t) for t in ws]
+        f32 = all(t.dtype == torch.float32 for t in ts)
+        dt = torch.float32 if f32 else torch.bfloat16
+        dev_ws = [t.to(device=self.device, dtype=dt).contiguous() for t in ts]
+        nbytes = wvd_encoder_prepared_bytes(self.c, self.h, self.w)
+        self.prepared = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        stream = torch.cuda.current_stream(self.device)
+        self.plan = wvd_encoder_prepare(self.c, self.h, self.w, [t.data_ptr() for t in dev_ws],
+                                        WVD_DTYPE_F32 if f32 else WVD_DTYPE_BF16, self.prepared.data_ptr(), nbytes,
+                                        stream.cuda_stream)
+        stream.synchronize()
+        del dev_ws
+        self._ws = None
+
+    def workspace_bytes(self, T: int, frames_per_pass: int) -> int:
+        return wvd_encode_workspace_bytes(self.plan, T, frames_per_pass)
+
+    def encode(self, video, frames_per_pass: int = 4, out=None, workspace=None):
+        """video [1, 3, 4T-3, 16h, 16w] (bf16 or fp32) -> fp32 latents [1, 48, T, h, w]."""
+        torch = self.torch
+        if (video.dim() != 5 or tuple(video.shape[:2]) != (1, 3) or tuple(video.shape[3:]) != (16 * self.h, 16 * self.w)
+                or video.shape[2] % 4 != 1):
+            raise WvdError(WVD_ESHAPE, f"encode: video of shape {tuple(video.shape)}")
+        vdt = torch.float32 if video.dtype == torch.float32 else torch.bfloat16
+        video = video.to(device=self.device, dtype=vdt).contiguous()
+        T = (int(video.shape[2]) + 3) // 4
+        shape = (1, 48, T, self.h, self.w)
+        if out is None:
+            out = torch.empty(shape, dtype=torch.float32, device=self.device)
+        elif tuple(out.shape) != shape or out.dtype != torch.float32 or not out.is_contiguous():
+            raise WvdError(WVD_ESHAPE, f"encode: out must be contiguous fp32 {shape}")
+        need = self.workspace_bytes(T, frames_per_pass)
+        if workspace is None:
+            if self._ws is None or self._ws.numel() < need:
+                self._ws = None
+                self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+            workspace = self._ws
+        stream = torch.cuda.current_stream(self.device)
+        wvd_encode(self.plan, video.data_ptr(), WVD_DTYPE_F32 if vdt == torch.float32 else WVD_DTYPE_BF16, T,
+                   int(frames_per_pass), out.data_ptr(), workspace.data_ptr(), workspace.numel(), stream.cuda_stream)
+        return out
+
+    def release_workspace(self) -> None:
+        self._ws = None
+
+    def profile(self, on: bool = True) -> None:
+        wvd_profile_enable(self.plan, on)
+
+    def profile_read(self) -> Dict[str, Dict[str, float]]:
+        return wvd_profile_read(self.plan)
+
+    def __del__(self):
+        plan = getattr(self, "plan", None)
+        if plan:
+            wvd_destroy(plan)
+            self.plan = None
