@@ -5,6 +5,7 @@ all passes) with the latents already resident in HBM.  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--config NAME] [--frames-per-pass P]
                   [--profile-steps N] [--no-cpu-baseline] [--gpus 1]
+  python bench.py --config enc_c256_T13_704x1248    (the encoder)
 
 The headline `value` is timed over K decodes with nothing else recorded on
 the stream.  A separate pass of N decodes with HIP-event timing around every
@@ -172,6 +173,102 @@ def cpu_baseline(cfg, W, seed, T_sample):
     }
 
 
+def run_encoder(args):
+    """The encoder (the decoder's mirror image): encoded video frames/s of
+    the clip, the dominant kernel's roofline from a separate profiled pass,
+    and the encoder oracle on the first five video frames beside it."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle import encoder as OE
+    from video_diffusion_vae_amd import synth_encoder as SE
+    from video_diffusion_vae_amd import wvd
+
+    cfg = SE.encoder_config_by_name(args.config)
+    P = args.frames_per_pass or cfg.passes[0]
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    W = SE.make_encoder_weights(cfg.c, seed=args.seed, bf16=cfg.weights_bf16)
+    dt = torch.bfloat16 if cfg.weights_bf16 else torch.float32
+    enc = wvd.Encoder({k: torch.from_numpy(v).to(dt) for k, v in W.items()}, cfg.c, cfg.h, cfg.w, device=dev)
+    v = torch.from_numpy(SE.make_video(cfg.T, cfg.h, cfg.w, seed=args.seed, bf16=cfg.weights_bf16)).to(dev).to(dt)
+    out = torch.empty(cfg.latent_shape, dtype=torch.float32, device=dev)
+    ws = torch.empty(enc.workspace_bytes(cfg.T, P), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        enc.encode(v, P, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    wvd.range_flags(clear=True)
+    torch.cuda.reset_peak_memory_stats(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        enc.encode(v, P, out=out, workspace=ws)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    peak_alloc, peak_res = torch.cuda.max_memory_allocated(dev), torch.cuda.max_memory_reserved(dev)
+    nprof = max(1, args.profile_steps)
+    enc.profile(True)
+    enc.profile_read()
+    for _ in range(nprof):
+        enc.encode(v, P, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    prof = enc.profile_read()
+    enc.profile(False)
+    flags = wvd.range_flags(clear=True)
+    frames = 4 * cfg.T - 3
+    conv = prof["conv3x3x3_main"]
+    launches = max(conv["launches"], 1)
+    avg_ms = conv["ms"] / launches
+    exec_tflops = conv["flops"] / launches / (avg_ms / 1e3) / 1e12 if conv["ms"] > 0 else 0.0
+    res = {
+        "metric": "encoded video frames/s at 704x1248 (the decoder's mirror-image encoder), 1 GPU",
+        "value": frames / (ms / 1e3), "unit": "frames/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic: seeded random-init weights (uniform +-1/sqrt(fan_in)), video uniform(-1,1), bf16-exact",
+        "config": {"workload": cfg.name, "video": list(cfg.video_shape), "latents": list(cfg.latent_shape),
+                   "frames_per_pass": P, "c": cfg.c},
+        "roofline": {"bound": "mfma", "achieved": exec_tflops, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": exec_tflops / MFMA_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "conv_persist<256, 2, 4, 0, 4, *>: Winograd-domain GEMM of the norm-SiLU 3x3x3 "
+                               "convs, all tile shapes",
+                     "flops": "the Winograd-domain multiply-adds the kernel performs",
+                     "avg_launch_ms": avg_ms, "launches_per_step": conv["launches"] / nprof},
+        "executed_tflop_per_step": sum(x["flops"] for x in prof.values()) / nprof / 1e12,
+        "nominal_tflop_per_step": OE.encoder_flops(cfg.c, cfg.T, cfg.h, cfg.w) / 1e12,
+        "time_split_ms_per_step": {k: x["ms"] / nprof for k, x in prof.items()},
+        "peak_hbm_gib": peak_alloc / 2 ** 30, "peak_hbm_reserved_gib": peak_res / 2 ** 30,
+        "fp16_range_flags": flags,
+    }
+    if not args.no_cpu_baseline:
+        Ts = args.cpu_sample_frames
+        head = out[:, :, :Ts].cpu().numpy()
+        del out, ws, v
+        torch.cuda.empty_cache()
+        vs = SE.make_video(Ts, cfg.h, cfg.w, seed=args.seed, bf16=cfg.weights_bf16)
+        cores = len(os.sched_getaffinity(0))
+        with threadpool_limits(limits=cores):
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+            t0 = time.perf_counter()
+            ref = OE.encode(vs, W, cfg.c)
+            dt_cpu = time.perf_counter() - t0
+        res["cpu_baseline"] = {
+            "value": vs.shape[2] / dt_cpu, "unit": "frames/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"exact causal prefix: {vs.shape[2]} video frame(s) -> {Ts} latent frame(s) of {cfg.name}, "
+                      f"full encoder, numpy fp32 ({dt_cpu:.1f} s)",
+            "gflops": OE.encoder_flops(cfg.c, Ts, cfg.h, cfg.w) / dt_cpu / 1e9, "cpu_model": cpu_model(),
+            "affinity_cores": cores}
+        d = np.abs(head.astype(np.float64) - ref)
+        res["parity_vs_oracle_prefix"] = {
+            "latent_frames": Ts, "max_abs": float(d.max()),
+            "rel_l2": float(np.linalg.norm(head.astype(np.float64) - ref) / np.linalg.norm(ref)),
+            "tolerance": {"max_abs": 3e-2, "rel_l2": 1e-2}}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -180,6 +277,9 @@ def main():
         sys.exit(2)
     if args.sweep:
         run_sweep(args)
+        return
+    if args.config.startswith("enc_"):
+        run_encoder(args)
         return
     import numpy as np
     import torch
