@@ -164,6 +164,7 @@ Layout make_layout(int c, int h, int w, bool deep = false) {
 // Workspace carve-up for a given maximum number of latent frames per pass.
 struct Work {
   size_t X, H, Y, zt, zp, rs, qkv, S, Pm, Vt, O;
+  size_t kf, vf, st, mi;     // attention on the batched GEMM: K, V^T fragments, score statistics
   size_t U, M;               // Winograd input planes and products
   std::vector<size_t> ring;  // 24 rings: offsets inside the ring block
   size_t rings;              // ring block offset in the workspace (npos: caller-owned state)
@@ -210,6 +211,30 @@ RingInfo ring_info(int c, int nrb, int id) {
 
 int lpad_of(int L) { return (L + 31) / 32 * 32; }
 
+// The mid attention runs on the batched 256 x 256 GEMM (scores never stored:
+// a statistics pass, then a probability pass) when a frame has at least 256
+// tokens and the width is a multiple of 256; smaller shapes use the generic
+// conv kernel with stored fp32 scores.
+bool attn_fast(int C, long long L) { return L >= 256 && C % 256 == 0; }
+long long attn_np(long long L) { return (L + 255) / 256 * 256; }
+
+// Attention buffers of F frames of L tokens at width C: the fp32 scores,
+// probabilities and V^T of the generic path, or the probabilities, K and V^T
+// fragments and score statistics of the batched-GEMM path.
+template <class Take>
+void take_attention(Work& W, Take& take, long long F, long long L, long long C) {
+  const long long Lp = lpad_of((int)L), Np = attn_np(L);
+  const bool fast = attn_fast((int)C, L);
+  W.S = take(fast ? 0 : (size_t)F * L * Lp * 4);
+  W.Pm = take((size_t)F * L * (fast ? Np : Lp) * 2);
+  W.Vt = take(fast ? 0 : (size_t)F * C * Lp * 2);
+  W.O = take((size_t)F * L * C * 2);
+  W.kf = take(fast ? (size_t)F * Np * C * 2 : 0);
+  W.vf = take(fast ? (size_t)F * Np * C * 2 : 0);
+  W.st = take(fast ? (size_t)F * L * (Np / 64) * 8 : 0);
+  W.mi = take(fast ? (size_t)F * L * 8 : 0);
+}
+
 Work make_work(int c, int h, int w, int P, bool rings_in_workspace = true, int nrb = 2) {
   Work W;
   const long long r0 = (long long)h * w;
@@ -231,10 +256,7 @@ Work make_work(int c, int h, int w, int P, bool rings_in_workspace = true, int n
   W.zp = take((size_t)F0 * r0 * 64 * 2);  // latents after the deep variant's 1x1x1 conv
   W.rs = take((size_t)(F2 + 2) * res[3] * 4);
   W.qkv = take((size_t)F0 * L * 3 * c4 * 2);
-  W.S = take((size_t)F0 * L * Lp * 4);
-  W.Pm = take((size_t)F0 * L * Lp * 2);
-  W.Vt = take((size_t)F0 * c4 * Lp * 2);
-  W.O = take((size_t)F0 * L * c4 * 2);
+  take_attention(W, take, F0, L, c4);
   {
     // Winograd planes: U = [N][F+2][H][WQ][Cin], M = [N][F][H][WQ][Cout] with
     // N = kWinoN planes and WQ = ceil(W / kWinoM) column groups, per level
@@ -375,10 +397,7 @@ Work make_work_enc(int c, int h, int w, int P) {
   W.zt = W.zp = take(0);
   W.rs = take((size_t)(F2 + 2) * res[3] * 4);
   W.qkv = take((size_t)F0 * L * 3 * c4 * 2);
-  W.S = take((size_t)F0 * L * Lp * 4);
-  W.Pm = take((size_t)F0 * L * Lp * 2);
-  W.Vt = take((size_t)F0 * c4 * Lp * 2);
-  W.O = take((size_t)F0 * L * c4 * 2);
+  take_attention(W, take, F0, L, c4);
   {
     // Winograd planes of the ResBlock convs of each level (frames, input and
     // output widths), as make_work does for the decoder.
@@ -843,7 +862,120 @@ Act resblock(Ctx& cx, const RB& rb, const Act& x, h16_t* hbuf, h16_t* obuf, int 
   return out;
 }
 
+GemmArgs gemm_args() {
+  GemmArgs g;
+  std::memset(&g, 0, sizeof(g));
+  g.scale = 1.0f;
+  g.nF = 1;
+  return g;
+}
+
+// Per-frame single-head attention on the batched 256 x 256 GEMM:
+//   xn = RMSNorm(x); qkv = xn Wqkv^T + b;
+//   per frame, with K and V^T in fragment order: the score pass computes,
+//   per query and group of 64 keys, the maximum and the sum of e^(s - max)
+//   of s = q.k / sqrt(C); a reduction gives each query's maximum M and
+//   1 / sum; the probability pass recomputes the scores and stores
+//   P = e^(s - M) / sum in fp16 (zero for the padding keys);
+//   O = P V; x += O Wp^T + bp.
+// The fp32 scores are never stored.
+void attention_fast(Ctx& cx, const Act& x) {
+  const Layout& L = cx.plan->L;
+  const int C = x.C, Lt = x.H * x.W;
+  const long long Np = attn_np(Lt);
+  h16_t* qkv = cx.wsp<h16_t>(cx.W->qkv);
+  h16_t* O = cx.wsp<h16_t>(cx.W->O);  // also xn, which is dead before O is written
+  h16_t* P = cx.wsp<h16_t>(cx.W->Pm);
+  h16_t* kf = cx.wsp<h16_t>(cx.W->kf);
+  h16_t* vf = cx.wsp<h16_t>(cx.W->vf);
+  float* st = cx.wsp<float>(cx.W->st);
+  float* mi = cx.wsp<float>(cx.W->mi);
+  const long long rows = (long long)x.F * Lt;
+  cx.rs_tensor = nullptr;
+  cx.what = "attention norm";
+  cx.run(3, 0, [&] {
+    return launch_norm_silu(x.p, x.fstride(), C, C, x.F, Lt, cx.prep<float>(L.attn_norm), O, (long long)Lt * C, C,
+                            cx.st, false);
+  });
+  GemmArgs g = gemm_args();
+  g.x = O;
+  g.M = rows;
+  g.lda = C;
+  g.K = C;
+  g.w = cx.prep<h16_t>(L.qkv_w);
+  g.w_bytes = cx.wbytes(L.qkv_w);
+  g.N = 3 * C;
+  g.bias = cx.prep<float>(L.qkv_b);
+  g.out = qkv;
+  g.ldo = 3 * C;
+  cx.what = "attention qkv";
+  cx.run(2, 2.0 * rows * 3 * C * C, [&] { return launch_gemm_nt(g, G_H16, cx.st); });
+  cx.what = "attention fragments";
+  cx.run(4, 0, [&] { return launch_attn_frag(qkv, x.F, Lt, C, (int)Np, kf, vf, cx.st); });
+  g = gemm_args();
+  g.x = qkv;  // queries: the first third of each qkv row
+  g.M = Lt;
+  g.lda = 3 * C;
+  g.K = C;
+  g.w = kf;
+  g.w_bytes = Np * C * 2;
+  g.N = (int)Np;
+  g.scale = 1.0f / std::sqrt((float)C);
+  g.nF = x.F;
+  g.a_fs = (long long)Lt * 3 * C;
+  g.w_fs = Np * C;
+  g.n_valid = Lt;
+  g.stats = st;
+  const double score_flops = 2.0 * x.F * Lt * Np * C;
+  cx.what = "attention scores (statistics)";
+  cx.run(2, score_flops, [&] { return launch_gemm_nt(g, G_STATS, cx.st); });
+  cx.what = "attention statistics";
+  cx.run(4, 0, [&] { return launch_attn_stats(st, rows, (int)(Np / 64), mi, cx.st); });
+  g.stats = nullptr;
+  g.mi = mi;
+  g.out = P;
+  g.ldo = (int)Np;
+  g.o_fs = Lt * Np;
+  cx.what = "attention scores (probabilities)";
+  cx.run(2, score_flops, [&] { return launch_gemm_nt(g, G_PROB, cx.st); });
+  g = gemm_args();
+  g.x = P;
+  g.M = Lt;
+  g.lda = (int)Np;
+  g.K = (int)Np;
+  g.w = vf;
+  g.w_bytes = Np * C * 2;
+  g.N = C;
+  g.nF = x.F;
+  g.a_fs = Lt * Np;
+  g.w_fs = Np * C;
+  g.out = O;
+  g.ldo = C;
+  g.o_fs = (long long)Lt * C;
+  cx.what = "attention P V";
+  cx.run(2, 2.0 * x.F * Lt * C * Np, [&] { return launch_gemm_nt(g, G_H16, cx.st); });
+  g = gemm_args();
+  g.x = O;
+  g.M = rows;
+  g.lda = C;
+  g.K = C;
+  g.w = cx.prep<h16_t>(L.proj_w);
+  g.w_bytes = cx.wbytes(L.proj_w);
+  g.N = C;
+  g.bias = cx.prep<float>(L.proj_b);
+  g.res = x.p;
+  g.ldr = C;
+  g.out = x.p;
+  g.ldo = C;
+  cx.what = "attention projection";
+  cx.run(2, 2.0 * rows * C * C, [&] { return launch_gemm_nt(g, G_H16, cx.st); });
+}
+
 void attention(Ctx& cx, const Act& x) {
+  if (attn_fast(x.C, (long long)x.H * x.W)) {
+    attention_fast(cx, x);
+    return;
+  }
   const Layout& L = cx.plan->L;
   const int C = x.C, Lt = x.H * x.W, Lp = lpad_of(Lt);
   h16_t* qkv = cx.wsp<h16_t>(cx.W->qkv);

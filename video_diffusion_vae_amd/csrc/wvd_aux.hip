@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void rms_stats_kernel(const h16_t* __restrict_
 __global__ __launch_bounds__(256) void norm_silu_kernel(const h16_t* __restrict__ x, long long x_fstride, int lda,
                                                         int C, int F, int HW, int G,
                                                         const float* __restrict__ gamma, h16_t* __restrict__ y,
-                                                        long long y_fstride, int ldy) {
+                                                        long long y_fstride, int ldy, int act) {
   const int lane = threadIdx.x & 63;
   const int sub = lane % G;
   const int vox_per_wave = 64 / G;
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(256) void norm_silu_kernel(const h16_t* __restrict_
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           const float t = f[k] * sc * gamma[g8 + k];
-          f[k] = silu_hw(t);
+          f[k] = act ? silu_hw(t) : t;
         }
         *reinterpret_cast<uint4*>(o + g8) = pack8h(f);
       }
@@ -220,6 +220,67 @@ __global__ __launch_bounds__(256) void latent_to_cl_kernel(const void* __restric
     uint4* dst = reinterpret_cast<uint4*>(zt + e * 64);
 #pragma unroll
     for (int q = 0; q < 8; ++q) dst[q] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+  }
+}
+
+// Attention operands in MFMA fragment order, per frame f of qkv [F][L][3C]
+// (q | k | v thirds): kf = the keys as the "weights" of S = Q K^T (N = Np
+// keys, K = C), vf = V^T as the weights of O = P V (N = C, K = Np keys).
+// Block (nb, u) of 512 halves: lane l holds at l*8..l*8+7 row nb*32 + l%32
+// and columns u*16 + (l/32)*8 + 0..7 of the N x K operand; keys >= L are 0.
+__global__ __launch_bounds__(256) void attn_frag_kernel(const h16_t* __restrict__ qkv, int L, int C, int Np,
+                                                        h16_t* __restrict__ kf, h16_t* __restrict__ vf) {
+  const int f = blockIdx.y;
+  const h16_t* q = qkv + (long long)f * L * 3 * C;
+  const long long nk = (long long)(Np / 32) * (C / 16) * 64;  // 16-byte pieces of kf per frame
+  const long long nv = (long long)(C / 32) * (Np / 16) * 64;
+  h16_t* kff = kf + (long long)f * Np * C;
+  h16_t* vff = vf + (long long)f * Np * C;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < nk + nv;
+       e += (long long)gridDim.x * blockDim.x) {
+    if (e < nk) {
+      const int l = (int)(e & 63);
+      const long long blk = e >> 6;
+      const int U = C / 16;
+      const int u = (int)(blk % U), nb = (int)(blk / U);
+      const int key = nb * 32 + (l & 31), d0 = u * 16 + (l >> 5) * 8;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (key < L) v = *reinterpret_cast<const uint4*>(q + (long long)key * 3 * C + C + d0);
+      *reinterpret_cast<uint4*>(kff + e * 8) = v;
+    } else {
+      const long long ev = e - nk;
+      const int l = (int)(ev & 63);
+      const long long blk = ev >> 6;
+      const int U = Np / 16;
+      const int u = (int)(blk % U), nb = (int)(blk / U);
+      const int d = nb * 32 + (l & 31), key0 = u * 16 + (l >> 5) * 8;
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k0 = key0 + 2 * j, k1 = k0 + 1;
+        const uint32_t lo = k0 < L ? q[(long long)k0 * 3 * C + 2 * C + d] : 0u;
+        const uint32_t hi = k1 < L ? q[(long long)k1 * 3 * C + 2 * C + d] : 0u;
+        w[j] = lo | (hi << 16);
+      }
+      *reinterpret_cast<uint4*>(vff + ev * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
+// Per query row: the maximum M and 1 / sum of e^(s - M) over its keys, from
+// the nst partial (maximum, sum of e^(s - partial maximum)) pairs the score
+// pass wrote for groups of 128 keys.
+__global__ __launch_bounds__(256) void attn_stats_kernel(const float2* __restrict__ st, long long rows, int nst,
+                                                         float2* __restrict__ mi) {
+  for (long long r = (long long)blockIdx.x * blockDim.x + threadIdx.x; r < rows;
+       r += (long long)gridDim.x * blockDim.x) {
+    const float2* p = st + r * nst;
+    float m = -INFINITY;
+    for (int t = 0; t < nst; ++t) m = fmaxf(m, p[t].x);
+    float l = 0.0f;
+    for (int t = 0; t < nst; ++t)
+      if (p[t].y > 0.0f) l += p[t].y * exp_hw(p[t].x - m);
+    mi[r] = make_float2(m, 1.0f / l);
   }
 }
 
@@ -974,7 +1035,7 @@ hipError_t launch_rms_stats(const h16_t* x, long long x_fstride, int lda, const 
 }
 
 hipError_t launch_norm_silu(const h16_t* x, long long x_fstride, int lda, int C, int F, int HW, const float* gamma,
-                            h16_t* y, long long y_fstride, int ldy, hipStream_t s) {
+                            h16_t* y, long long y_fstride, int ldy, hipStream_t s, bool act) {
   if (g_dry_run) return hipSuccess;
   int G = 1;
   while (G < 64 && G * 2 <= C / 8) G *= 2;
@@ -982,7 +1043,7 @@ hipError_t launch_norm_silu(const h16_t* x, long long x_fstride, int lda, int C,
   const long long nvox = (long long)F * HW;
   const long long waves = (nvox + (64 / G) * kStatsU - 1) / ((64 / G) * kStatsU);
   hipLaunchKernelGGL(norm_silu_kernel, dim3(grid_for(waves * 64, 256, 16384)), dim3(256), 0, s, x, x_fstride, lda, C,
-                     F, HW, G, gamma, y, y_fstride, ldy);
+                     F, HW, G, gamma, y, y_fstride, ldy, act ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -1007,6 +1068,22 @@ hipError_t launch_latent_to_cl(const void* z, int dtype, int T, int t0, int F, i
   if (g_dry_run) return hipSuccess;
   hipLaunchKernelGGL(latent_to_cl_kernel, dim3(grid_for((long long)F * HW)), dim3(256), 0, s, z, dtype, T, t0, F, HW,
                      zt);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_frag(const h16_t* qkv, int F, int L, int C, int Np, h16_t* kf, h16_t* vf, hipStream_t s) {
+  if (g_dry_run) return hipSuccess;
+  if (F < 1 || L < 1 || C % 32 || Np % 256 || Np < L || F > 65535) return hipErrorInvalidValue;
+  const long long n = (long long)(Np / 32) * (C / 16) * 64 + (long long)(C / 32) * (Np / 16) * 64;
+  hipLaunchKernelGGL(attn_frag_kernel, dim3(grid_for(n, 256, 4096), F), dim3(256), 0, s, qkv, L, C, Np, kf, vf);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_stats(const float* st, long long rows, int nst, float* mi, hipStream_t s) {
+  if (g_dry_run) return hipSuccess;
+  if (rows < 1 || nst < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attn_stats_kernel, dim3(grid_for(rows)), dim3(256), 0, s, reinterpret_cast<const float2*>(st),
+                     rows, nst, reinterpret_cast<float2*>(mi));
   return hipGetLastError();
 }
 

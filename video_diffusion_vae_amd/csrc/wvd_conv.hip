@@ -32,6 +32,8 @@
 // page describes; normalisation is channel RMSNorm with affine scale and SiLU
 // as the TensorRT-LLM norm-SiLU issue describes for the decoder's residual
 // norms and norm_out, statistics in fp32 (Wan2.2 page, "Limits").
+#include <cstring>
+
 #include "wvd_internal.h"
 
 namespace wvd {
@@ -1684,7 +1686,285 @@ __global__ __launch_bounds__(256) void gemm1x1_kernel(const h16_t* __restrict__ 
   }
 }
 
+// Frames: tile t of the whole grid is frame t / (row tiles x column tiles);
+// A, B, the output and the residual of frame f start f times their strides
+// further.  The epilogue (EPI, a GemmEpi) is chosen at compile time.  The
+// last row tile of a frame is shifted back to end at row M; the rows it
+// shares with the tile before are stored by that tile only.
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs ga) {
+  constexpr int MI = 4, NJ = 4, CS = kG1K / 16, PPR = kG1K * 2 / 16, IPT = 16;
+  static_assert(PPR == 16 && IPT == 16 && CS == 8, "16 A pieces (16 rows apart) and 16 B blocks per thread");
+  extern __shared__ __align__(16) unsigned char g1s[];
+  unsigned char* As = g1s;
+  unsigned char* Bs = g1s + 256 * kG1ARow;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int kpart = lane >> 5, lrow = lane & 31;
+  const long long M = ga.M;
+  const int lda = ga.lda, K = ga.K, N = ga.N;
+  const int nN = N / 256;
+  const long long nMt = (M + 255) / 256;
+  const int tpf = (int)(nMt * nN);  // tiles per frame
+  const TileSeq seq = tile_seq(tpf * ga.nF);
+  if (seq.at(0) < 0) return;
+  const int nch = K / kG1K;
+  const int U = K / 16;
+
+  // this thread's pieces: A row (tid / PPR) + 16 r, part tid % PPR; B block
+  // (tid + 256 r) / 64 = (32-column block nbl, k16 step s), lane (tid % 64)
+  uint4 sa[IPT], sb[IPT];
+  // Only the lane-dependent parts of the addresses live in VGPRs; the piece
+  // index r and the chunk go into the scalar offset.
+  const int avoff = ((tid / PPR) * lda + (tid % PPR) * 8) * 2;
+  const int bvoff = lane * 16;
+  // The last row tile is shifted back to end at row M (M >= 256), so every
+  // A read is in range; its rows that the previous tile also covers are
+  // recomputed but stored by the previous tile only.
+  auto tile_m0 = [&](int tile) {
+    const long long m0 = (long long)((tile % tpf) / nN) * 256;
+    return m0 + 256 <= M ? m0 : M - 256;
+  };
+  auto issue = [&](int tile, int ch) {
+    const int f = tile / tpf;
+    const long long m0 = tile_m0(tile);
+    const int bn = (tile % tpf) % nN;
+    const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<h16_t*>(ga.x + f * ga.a_fs + m0 * lda), 0, 256 * lda * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t brsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<h16_t*>(ga.w + f * ga.w_fs), 0, (int)ga.w_bytes, 0x00020000);
+#pragma unroll
+    for (int r = 0; r < IPT; ++r)
+      sa[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            arsrc, avoff, (16 * r * lda + ch * kG1K) * 2, 0));
+#pragma unroll
+    for (int r = 0; r < IPT; ++r) {
+      // block (wave + 4r): 32-column block r / 2, k16 step wave + 4 (r % 2)
+      const int nb = bn * 8 + r / 2, u = ch * CS + wave + 4 * (r % 2);
+      sb[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(brsrc, bvoff, (nb * U + u) * 1024, 0));
+    }
+  };
+  const int aloff = (tid / PPR) * kG1ARow + (tid % PPR) * 16;
+  const int bloff = wave * 1024 + lane * 16;
+  auto commit = [&]() {
+#pragma unroll
+    for (int r = 0; r < IPT; ++r) {
+      *reinterpret_cast<uint4*>(As + aloff + 16 * r * kG1ARow) = sa[r];
+      *reinterpret_cast<uint4*>(Bs + bloff + r * 4096) = sb[r];
+    }
+  };
+  int abase[MI], bbase[NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) abase[i] = (wm * 128 + 32 * i + lrow) * kG1ARow + kpart * 16;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) bbase[j] = (wn * 4 + j) * CS * 1024 + lane * 16;
+
+  issue(seq.at(0), 0);
+  commit();
+  __syncthreads();
+  f32x16_t acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  for (int k = 0;; ++k) {
+    const int cur = seq.at(k);
+    if (cur < 0) break;
+    const int nxt = seq.at(k + 1);
+    for (int ch = 0; ch < nch; ++ch) {
+      const bool last = ch + 1 == nch;
+      const bool more = !last || nxt >= 0;  // uniform
+      if (more) issue(last ? nxt : cur, last ? 0 : ch + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      f16x8_t ap[2][MI], bp[2][NJ];
+#pragma unroll
+      for (int i = 0; i < MI; ++i) ap[0][i] = *reinterpret_cast<const f16x8_t*>(As + abase[i]);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) bp[0][j] = *reinterpret_cast<const f16x8_t*>(Bs + bbase[j]);
+#pragma unroll
+      for (int s = 0; s < CS; ++s) {
+        if (s + 1 < CS) {
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+            ap[(s + 1) & 1][i] = *reinterpret_cast<const f16x8_t*>(As + abase[i] + (s + 1) * 32);
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            bp[(s + 1) & 1][j] = *reinterpret_cast<const f16x8_t*>(Bs + bbase[j] + (s + 1) * 1024);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bp[s & 1][j], ap[s & 1][i], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __syncthreads();  // every wave is done reading this chunk
+      if (last) {
+        // lane (kpart, lrow) of block (i, j) holds row 32i + lrow of the
+        // wave's rows and columns 32j + 8g + 4*kpart + r (accumulator 4g + r)
+        const int f = cur / tpf;
+        const long long m0 = tile_m0(cur);
+        // rows below mown belong to the previous row tile (the last tile is
+        // shifted back): only their owner stores them, so an in-place
+        // residual is read and written once per row
+        const long long mown = (long long)((cur % tpf) / nN) * 256;
+        const int ct = (cur % tpf) % nN;  // column tile
+        const int n0 = ct * 256 + wn * 128;
+        // Every epilogue goes through the A region: per 32 rows and 64
+        // columns the accumulator runs go straight into fp32 LDS rows; then
+        // each lane takes eight columns of one row (eight lanes per row):
+        //   G_H16: bias (and residual), fp16, a 16-byte store;
+        //   G_STATS: the row's max and sum of e^(v - max) over those 64
+        //     columns (a reduction over the eight lanes), one float2;
+        //   G_PROB: e^(v - M) / S with the row's (M, 1/S), fp16, a store.
+        constexpr int SROW = 64 * 4 + 16, LPR = 8, RPI = 8;
+        static_assert(4 * 32 * SROW <= 256 * kG1ARow, "staging fits in the A region");
+        unsigned char* st = As + wave * 32 * SROW;
+        const float scale = ga.scale;
+        // per-tile row bases (uniform): row m of the tile's frame is row
+        // m - m0 + (tile base), so the loops below need 32-bit offsets only
+        h16_t* const outb = EPI == G_STATS ? nullptr : ga.out + f * ga.o_fs + m0 * ga.ldo;
+        const h16_t* const resb = EPI == G_H16 && ga.res ? ga.res + f * ga.r_fs + m0 * ga.ldr : nullptr;
+        const float* const mib = EPI == G_PROB ? ga.mi + (f * M + m0) * 2 : nullptr;
+        float* const stb = EPI == G_STATS ? ga.stats + (f * M + m0) * (N / 64) * 2 : nullptr;
+        const int mskip = (int)(mown - m0);  // tile rows below this belong to the previous tile
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+#pragma unroll
+          for (int jh = 0; jh < NJ / 2; ++jh) {
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+              for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x16_t& c = acc[i][jh * 2 + jj];
+                f32x4_t v = {c[4 * g4], c[4 * g4 + 1], c[4 * g4 + 2], c[4 * g4 + 3]};
+                *reinterpret_cast<f32x4_t*>(st + lrow * SROW + (32 * jj + 8 * g4 + 4 * kpart) * 4) = v;
+              }
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the block is in LDS
+            __builtin_amdgcn_wave_barrier();
+            const int ncol = n0 + jh * 64 + (lane % LPR) * 8;
+            float bv[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) bv[q] = 0.0f;
+            if (EPI == G_H16 && ga.bias) {
+              const f32x4_t b0 = *reinterpret_cast<const f32x4_t*>(ga.bias + ncol);
+              const f32x4_t b1 = *reinterpret_cast<const f32x4_t*>(ga.bias + ncol + 4);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                bv[q] = b0[q];
+                bv[4 + q] = b1[q];
+              }
+            }
+#pragma unroll 1
+            for (int rr = 0; rr < 32 / RPI; ++rr) {
+              const int r = rr * RPI + lane / LPR;
+              const float* row = reinterpret_cast<const float*>(st + r * SROW) + (lane % LPR) * 8;
+              const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(row);
+              const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(row + 4);
+              const int mt = wm * 128 + 32 * i + r;  // row within the tile
+              float v8[8] = {lo[0] * scale + bv[0], lo[1] * scale + bv[1], lo[2] * scale + bv[2],
+                             lo[3] * scale + bv[3], hi[0] * scale + bv[4], hi[1] * scale + bv[5],
+                             hi[2] * scale + bv[6], hi[3] * scale + bv[7]};
+              if constexpr (EPI == G_STATS) {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                  if (ncol + q < ga.n_valid) mx = fmaxf(mx, v8[q]);
+                mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+                mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+                mx = fmaxf(mx, __shfl_xor(mx, 4, 64));
+                float sm = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                  if (ncol + q < ga.n_valid) sm += exp_hw(v8[q] - mx);
+                sm += __shfl_xor(sm, 1, 64);
+                sm += __shfl_xor(sm, 2, 64);
+                sm += __shfl_xor(sm, 4, 64);
+                if (lane % LPR == 0 && mt >= mskip)
+                  *reinterpret_cast<float2*>(stb + (mt * (N / 64) + ct * 4 + wn * 2 + jh) * 2) = make_float2(mx, sm);
+              } else {
+                if (mt < mskip) continue;
+                if constexpr (EPI == G_PROB) {
+                  const float2 ms = *reinterpret_cast<const float2*>(mib + mt * 2);
+#pragma unroll
+                  for (int q = 0; q < 8; ++q) v8[q] = ncol + q < ga.n_valid ? exp_hw(v8[q] - ms.x) * ms.y : 0.0f;
+                } else if (resb) {
+                  float rv[8];
+                  unpack8h(*reinterpret_cast<const uint4*>(resb + mt * ga.ldr + ncol), rv);
+#pragma unroll
+                  for (int q = 0; q < 8; ++q) v8[q] += rv[q];
+                }
+                *reinterpret_cast<uint4*>(outb + mt * ga.ldo + ncol) = pack8h(v8);
+              }
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // this round's reads before the next round's writes
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+        __syncthreads();  // the staging rows are free again
+      }
+      if (more) commit();
+      __syncthreads();
+    }
+  }
+}
+
 }  // namespace
+
+const char* gemm_nt_check(const GemmArgs& g, int epi) {
+  if (!g.x || !g.w || g.M < 256 || g.N % 256 || g.K % kG1K || g.K > 4096 || g.lda % 8 || g.lda < g.K)
+    return "A / B shapes";
+  if (g.w_bytes <= 0 || g.w_bytes > 0x7fffffffLL || (long long)256 * g.lda * 2 > 0x7fffffffLL) return "B bytes";
+  if (g.nF < 1 || (g.nF > 1 && (g.a_fs < 0 || g.w_fs < 0 || g.o_fs < 0 || g.r_fs < 0))) return "frames";
+  if ((long long)(g.M + 255) / 256 * (g.N / 256) * g.nF > 0x7fffffffLL) return "tile count";
+  if (epi == G_STATS) {
+    if (!g.stats || g.n_valid < 1 || g.n_valid > g.N) return "statistics operands";
+  } else {
+    if (!g.out || g.ldo % 8 || g.ldo < g.N) return "output";
+    if (g.res && (g.ldr % 8 || g.ldr < g.N || epi != G_H16)) return "residual";
+    if (epi == G_PROB && (!g.mi || g.n_valid < 1 || g.n_valid > g.N || g.bias)) return "probability operands";
+  }
+  return nullptr;
+}
+
+hipError_t launch_gemm_nt(const GemmArgs& g, int epi, hipStream_t stream) {
+  if (g_dry_run) return gemm_nt_check(g, epi) ? hipErrorInvalidValue : hipSuccess;
+  if (gemm_nt_check(g, epi)) return hipErrorInvalidValue;
+  const void* kern = epi == G_STATS   ? reinterpret_cast<const void*>(gemm_nt_kernel<G_STATS>)
+                     : epi == G_PROB  ? reinterpret_cast<const void*>(gemm_nt_kernel<G_PROB>)
+                                      : reinterpret_cast<const void*>(gemm_nt_kernel<G_H16>);
+  static bool attr[3] = {false, false, false};
+  if (!attr[epi]) {
+    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, kG1Lds);
+    if (e != hipSuccess) return e;
+    attr[epi] = true;
+  }
+  const long long tiles = (g.M + 255) / 256 * (g.N / 256) * g.nF;
+  int dev = 0, ncu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const long long grid = tiles < ncu ? tiles : ncu;
+  if (epi == G_STATS)
+    hipLaunchKernelGGL(gemm_nt_kernel<G_STATS>, dim3((unsigned)grid), dim3(256), kG1Lds, stream, g);
+  else if (epi == G_PROB)
+    hipLaunchKernelGGL(gemm_nt_kernel<G_PROB>, dim3((unsigned)grid), dim3(256), kG1Lds, stream, g);
+  else
+    hipLaunchKernelGGL(gemm_nt_kernel<G_H16>, dim3((unsigned)grid), dim3(256), kG1Lds, stream, g);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm1x1(const h16_t* x, long long M, int lda, int K, const h16_t* w, long long w_bytes, int N,
                           const float* bias, h16_t* out, int ldo, hipStream_t stream) {

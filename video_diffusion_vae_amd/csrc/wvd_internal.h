@@ -120,9 +120,47 @@ hipError_t launch_gemm1x1(const h16_t* x, long long M, int lda, int K, const h16
 // Auxiliary kernels (wvd_aux.hip).
 hipError_t launch_rms_stats(const h16_t* x, long long x_fstride, int lda, const h16_t* ring,
                             int n_hist, int C, int F, int HW, float* rs, hipStream_t s);
-// y = SiLU(x / ||x|| * gamma) per voxel over C channels (gamma carries sqrt(C)).
+// y = SiLU(x / ||x|| * gamma) per voxel over C channels (gamma carries sqrt(C));
+// without act, y = x / ||x|| * gamma.
 hipError_t launch_norm_silu(const h16_t* x, long long x_fstride, int lda, int C, int F, int HW, const float* gamma,
-                            h16_t* y, long long y_fstride, int ldy, hipStream_t s);
+                            h16_t* y, long long y_fstride, int ldy, hipStream_t s, bool act = true);
+// Attention operands of F frames of qkv [F][L][3C] in fragment order (Np keys,
+// a multiple of 256, zero past L): kf [F][Np x C], vf [F][C x Np].
+hipError_t launch_attn_frag(const h16_t* qkv, int F, int L, int C, int Np, h16_t* kf, h16_t* vf, hipStream_t s);
+// mi[r] = (M, 1 / sum e^(s - M)) of each score row r from its nst partial
+// (max, sum of e^(s - max)) pairs st[r][0..nst) (float2 as two floats).
+hipError_t launch_attn_stats(const float* st, long long rows, int nst, float* mi, hipStream_t s);
+
+// Batched NT GEMM on fragment-order B (the persistent 256 x 256 kernel of
+// the 1x1 shortcut): for frames f < nF, out[f][m][n] = epilogue of
+// sum_k x[f][m][k] w[f][n][k], M rows (>= 256) per frame, K a multiple of
+// 128, N of 256.
+enum GemmEpi {
+  G_H16 = 0,    // fp16 out = acc * scale + bias (+ res, which may alias out)
+  G_STATS = 1,  // no out: per row and group of 64 columns, (max, sum of e^(v - max)) of v = acc * scale
+                // over the columns < n_valid, into stats [f][M][N / 64] (float2)
+  G_PROB = 2    // fp16 out = e^(acc * scale - M) / S with (M, 1/S) = mi[f][m] (float2); 0 for columns >= n_valid
+};
+struct GemmArgs {
+  const h16_t* x;
+  long long M;
+  int lda, K;
+  const h16_t* w;
+  long long w_bytes;  // per frame
+  int N;
+  const float* bias;
+  float scale;
+  const h16_t* res;
+  int ldr;
+  h16_t* out;
+  int ldo;
+  int nF;
+  long long a_fs, w_fs, o_fs, r_fs;  // per-frame strides (elements)
+  int n_valid;
+  float* stats;
+  const float* mi;
+};
+hipError_t launch_gemm_nt(const GemmArgs& g, int epi, hipStream_t stream);
 hipError_t launch_ring_update(h16_t* ring, const h16_t* x, long long x_fstride, int lda, int C,
                               int F, int HW, hipStream_t s);
 // Deep variant: 48 -> 48 1x1x1 conv of the 64-wide channels-last latents.
