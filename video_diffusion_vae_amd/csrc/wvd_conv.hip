@@ -1320,19 +1320,25 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
           const int t2 = m / TW;
           const int f = geo.f0 + t2 / TH, y = geo.y0 + t2 % TH, x = geo.x0 + tx;
           const int nb = ncol0 + ec0;
-          if (f < a.F && y < a.H && x < a.W && nb < a.Cout) {
+          if (a.epi == EPI_VIDEO) {
+            // head (12 channels): lane slot sl < 6 of the row's eight writes
+            // colour sl / 2, video row 2y + sl % 2: channels 4k + 2dy + 0, 1
+            // as one bf16 pair, so the eight rows of a quarter (consecutive
+            // x) fill 32 contiguous bytes of each video row
+            const int sl = lane % LPR;
+            if (f < a.F && y < a.H && x < a.W && sl < 6) {
+              const int kk = sl >> 1, ddy = sl & 1, n = 4 * kk + 2 * ddy;
+              const float* rowv = ep + er * EROW + n - ncol0;
+              const float v0 = clamp_unit(rowv[0] * a.scale + (a.bias ? a.bias[n] : 0.0f));
+              const float v1 = clamp_unit(rowv[1] * a.scale + (a.bias ? a.bias[n + 1] : 0.0f));
+              const long long r2 = ((long long)kk * a.video_T + a.out_base + f) * (2 * a.H) + 2 * y + ddy;
+              *reinterpret_cast<uint32_t*>(static_cast<bf16_t*>(a.out) + r2 * (2 * a.W) + 2 * x) =
+                  f2bf(v0) | (f2bf(v1) << 16);
+            }
+          } else if (f < a.F && y < a.H && x < a.W && nb < a.Cout) {
             const long long pix = (long long)y * a.W + x;
             const float* row = ep + er * EROW + ec0;
-            if (a.epi == EPI_VIDEO) {
-              for (int cc = 0; cc < CPL && nb + cc < a.Cout; ++cc) {
-                const int n = nb + cc;
-                float v = row[cc] * a.scale + (a.bias ? a.bias[n] : 0.0f);
-                v = clamp_unit(v);
-                const int kk = n >> 2, ddy = (n >> 1) & 1, ddx = n & 1;
-                const long long r2 = ((long long)kk * a.video_T + a.out_base + f) * (2 * a.H) + 2 * y + ddy;
-                static_cast<bf16_t*>(a.out)[r2 * (2 * a.W) + 2 * x + ddx] = (bf16_t)f2bf(v);
-              }
-            } else if constexpr (CPL % 8 == 0) {
+            if constexpr (CPL % 8 == 0) {
               h16_t* o;
               int ob = nb;  // output channel of this lane's first column
               if (a.epi == EPI_PHASE) {
@@ -2077,6 +2083,7 @@ const char* conv_check(const ConvArgs& a) {
       return "the specialised kernels take only a 1x1x1 second segment";
     if (s > 0 && g.KS != KS_1x1) return "second segment must have 1x1 spatial taps";
   }
+  if (a.epi == EPI_VIDEO && a.Cout != 12) return "the video epilogue takes the head's 12 channels";
   if (a.epi == EPI_LATENT && (conv_persistent(a) || a.video_T < 1 || a.out_base < 0 || a.out_base + a.F > a.video_T))
     return "latent epilogue: generic kernel, frames inside the clip";
   if (!a.out || !a.zero_row) return "null output or zero row";
