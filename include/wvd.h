@@ -239,6 +239,21 @@ int wvd_range_flags(void* stream, int clear, unsigned int* flags);
  * the decoder feeds them.  WVD_EINVAL on null buffers or a bad n. */
 int wvd_math_probe(const float* x, float* silu_out, float* exp_out, long long n, void* stream);
 
+/* Conversion self-test: for n fp32 inputs x (device; n a multiple of 8,
+ * n <= 2^31; x, h_out and rs_out 16-byte aligned) writes, on `stream`:
+ *   h_out[i]  = the fp16 bit pattern the kernels store for x[i], packed eight
+ *               values at a time as every kernel packs them (round to
+ *               nearest even; a finite value beyond +-65504 saturates there
+ *               and a NaN stays NaN, each raising its range flag);
+ *   rs_out[i] = the norm scale 1 / max(sqrt(x[i]), 1e-12) as the Winograd
+ *               input transforms compute it from a channel sum of squares
+ *               x[i] >= 0 (one hardware reciprocal square root).
+ * The RMSNorm the decoder's residual blocks use is the Wan2.2 VAE decoder
+ * page's; a test compares h_out with IEEE round-to-nearest-even bit for bit
+ * and bounds rs_out against an exact reference.  WVD_EINVAL on null or
+ * misaligned buffers or a bad n. */
+int wvd_f16_probe(const float* x, unsigned short* h_out, float* rs_out, long long n, void* stream);
+
 /* Host-validation mode for testing without a GPU: with on != 0, every entry
  * point validates its arguments and walks the full launch schedule (all
  * per-launch checks included) but enqueues no GPU work and dereferences no

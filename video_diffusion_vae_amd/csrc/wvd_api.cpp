@@ -1604,6 +1604,18 @@ int wvd_math_probe(const float* x, float* silu_out, float* exp_out, long long n,
   return WVD_OK;
 }
 
+int wvd_f16_probe(const float* x, unsigned short* h_out, float* rs_out, long long n, void* stream) {
+  if (n < 0 || n % 8 || (n > 0 && (!x || !h_out || !rs_out))) return WVD_EINVAL;
+  if (n > (1LL << 31)) return WVD_EINVAL;
+  if (!aligned16(x) || !aligned16(h_out) || !aligned16(rs_out)) return WVD_EINVAL;
+  hipError_t e = launch_f16_probe(x, h_out, rs_out, n, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    set_error("wvd_f16_probe", e);
+    return WVD_EHIP;
+  }
+  return WVD_OK;
+}
+
 int wvd_range_flags(void* stream, int clear, unsigned int* flags) {
   if (!flags) return WVD_EINVAL;
   *flags = 0;

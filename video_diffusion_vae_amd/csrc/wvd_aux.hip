@@ -590,6 +590,10 @@ __device__ __forceinline__ float lane_group_sum(float v, int G) {
   return v;
 }
 
+// Zeros that the transforms read in place of columns outside a row (no
+// branch around the loads): at least as long as the widest channel count.
+__device__ __align__(16) h16_t g_zero_row[1024];
+
 // SiLU(v * rs * gamma) of one column from its fp16 channel values (this
 // lane's NG 8-channel groups), with rs = 1 / ||v|| over the column's C
 // channels (a sum over the G lanes of the group); zero where !in.  The
@@ -609,13 +613,20 @@ __device__ __forceinline__ void act_column(const uint4 (&v)[NG], bool in, int G,
     ss += t;
   }
   ss = lane_group_sum(ss, G);
-  const float sc = 1.0f / fmaxf(sqrtf(ss), kNormEps);
+  // every activation of a Winograd conv's input comes from this function,
+  // so the hardware rsqrt here (not the correctly rounded form of
+  // rms_stats_kernel) is the same for every pass
+  static_assert(kNormEps == 1e-12f, "norm_scale's floor");
+  const float sc = norm_scale(ss);
+  // SiLU first, then the select: a conditional expression with the SiLU
+  // inside it becomes a branch per element pair
 #pragma unroll
   for (int h = 0; h < NG; ++h)
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const float t = f[h][c] * sc * gm[h][c];
-      y[h][c] = in ? silu_hw(t) : 0.0f;
+      const float a = silu_hw(t);
+      y[h][c] = in ? a : 0.0f;
     }
 }
 
@@ -641,10 +652,10 @@ __global__ __launch_bounds__(256) void wino_in_kernel(const h16_t* __restrict__ 
   const int QB = (WQ + R - 1) / R;   // runs of R column groups per row
   const long long HW = (long long)H * W;
   const long long plane = (long long)S * H * WQ * C;  // elements per xi plane
-  const long long nrun = (long long)(slot_end - first_slot) * H * QB;
+  const int nrun = (slot_end - first_slot) * H * QB;  // (the launcher checks the range)
   const int runs_per_wave = 64 / G;
-  const long long gw = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-  const long long nw = ((long long)gridDim.x * blockDim.x) >> 6;
+  const int gw = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int nw = (gridDim.x * blockDim.x) >> 6;
   float gm[NG][8];
 #pragma unroll
   for (int h = 0; h < NG; ++h) {
@@ -658,14 +669,14 @@ __global__ __launch_bounds__(256) void wino_in_kernel(const h16_t* __restrict__ 
       gm[h][4] = g1.x; gm[h][5] = g1.y; gm[h][6] = g1.z; gm[h][7] = g1.w;
     }
   }
-  for (long long base = gw * runs_per_wave; base < nrun; base += nw * runs_per_wave) {
-    const long long e = base + lane / G;
+  for (int base = gw * runs_per_wave; base < nrun; base += nw * runs_per_wave) {
+    const int e = base + lane / G;
     const bool ok = e < nrun;  // whole lane groups agree
-    const long long ee = ok ? e : 0;
-    const int qb = (int)(ee % QB);
-    const long long r = ee / QB;
-    const int row = (int)(r % H);
-    const int slot = (int)(r / H) + first_slot;
+    const int ee = ok ? e : 0;
+    const int qb = ee % QB;
+    const int r = ee / QB;
+    const int row = r % H;
+    const int slot = r / H + first_slot;
     const h16_t* src_row = slot < 2 ? ring + ((long long)slot * HW + (long long)row * W) * C
                                     : x + (slot - 2) * x_fstride + (long long)row * W * lda;
     const long long ld = slot < 2 ? C : lda;
@@ -673,13 +684,9 @@ __global__ __launch_bounds__(256) void wino_in_kernel(const h16_t* __restrict__ 
     // outside the row); every lane of the group runs it (butterfly)
     // raw channels of column `col` (zero outside the row)
     auto load_col = [&](int col, uint4 (&v)[NG]) {
-#pragma unroll
-      for (int h = 0; h < NG; ++h) v[h] = make_uint4(0, 0, 0, 0);
-      if (ok && col >= 0 && col < W) {
-        const h16_t* p = src_row + (long long)col * ld;
-        v[0] = *reinterpret_cast<const uint4*>(p + sub * 8);
-        if (second) v[NG - 1] = *reinterpret_cast<const uint4*>(p + (sub + G) * 8);
-      }
+      const h16_t* p = ok && col >= 0 && col < W ? src_row + (long long)col * ld : g_zero_row;
+      v[0] = *reinterpret_cast<const uint4*>(p + sub * 8);
+      if (NG == 2) v[NG - 1] = *reinterpret_cast<const uint4*>(second ? p + (sub + G) * 8 : g_zero_row);
     };
     auto in_row = [&](int col) { return ok && col >= 0 && col < W; };
     float y[NX][NG][8];
@@ -762,10 +769,10 @@ __global__ __launch_bounds__(256) void wino_mid_kernel(const h16_t* __restrict__
   const int QB = (WQ + R - 1) / R;
   const long long mplane = (long long)F * H * WQ * C;        // conv1 product planes
   const long long uplane = (long long)(F + 2) * H * WQ * C;  // conv2 input planes (two history slots first)
-  const long long nrun = (long long)F * H * QB;
+  const int nrun = F * H * QB;  // (the launcher checks the range)
   const int runs_per_wave = 64 / G;
-  const long long gw = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-  const long long nw = ((long long)gridDim.x * blockDim.x) >> 6;
+  const int gw = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int nw = (gridDim.x * blockDim.x) >> 6;
   float gm[NG][8], bv[NG][8];
 #pragma unroll
   for (int h = 0; h < NG; ++h) {
@@ -785,26 +792,24 @@ __global__ __launch_bounds__(256) void wino_mid_kernel(const h16_t* __restrict__
       }
     }
   }
-  for (long long base = gw * runs_per_wave; base < nrun; base += nw * runs_per_wave) {
-    const long long e = base + lane / G;
+  for (int base = gw * runs_per_wave; base < nrun; base += nw * runs_per_wave) {
+    const int e = base + lane / G;
     const bool ok = e < nrun;
-    const long long ee = ok ? e : 0;
-    const int qb = (int)(ee % QB);
-    const long long r = ee / QB;
-    const int row = (int)(r % H);
-    const int f = (int)(r / H);
-    // raw products of group q (zero outside)
+    const int ee = ok ? e : 0;
+    const int qb = ee % QB;
+    const int r = ee / QB;
+    const int row = r % H;
+    const int f = r / H;
+    // raw products of group q (zero outside: the zero row, plane stride 0)
     auto load_group = [&](int q, uint4 (&mr)[NX][NG]) {
       const bool valid = ok && q >= 0 && q < WQ;
+      const h16_t* p = valid ? M + (long long)((f * H + row) * WQ + q) * C : g_zero_row;
+      const long long ps = valid ? mplane : 0;
 #pragma unroll
       for (int k = 0; k < NX; ++k)
 #pragma unroll
-        for (int h = 0; h < NG; ++h) {
-          mr[k][h] = make_uint4(0, 0, 0, 0);
-          if (valid && (h == 0 || second))
-            mr[k][h] = *reinterpret_cast<const uint4*>(M + k * mplane + (((long long)f * H + row) * WQ + q) * C +
-                                                       (sub + h * G) * 8);
-        }
+        for (int h = 0; h < NG; ++h)
+          mr[k][h] = *reinterpret_cast<const uint4*>(h == 0 || second ? p + k * ps + (sub + h * G) * 8 : g_zero_row);
     };
     // h (fp16, as stored) of the kWinoM columns of group q; zero outside
     auto finish_group = [&](int q, const uint4 (&mr)[NX][NG], uint4 (&hv)[WM][NG]) {
@@ -1172,6 +1177,7 @@ hipError_t launch_wino_in(const h16_t* x, long long x_fstride, int lda, const h1
   const int first = 2 - n_hist, end = history_only ? 2 : F + 2;
   if (end <= first) return hipSuccess;
   const long long runs = (long long)(end - first) * H * ((WQ + kWinoInRun - 1) / kWinoInRun);
+  if (runs >= (1LL << 30)) return hipErrorInvalidValue;  // the kernel counts runs in 32 bits
   const long long threads = (runs + 64 / G - 1) / (64 / G) * 64;
   if (C / 8 > G)
     hipLaunchKernelGGL(wino_in_kernel<2>, dim3(grid_for(threads, 256, 65536)), dim3(256), 0, s, x, x_fstride, lda,
@@ -1193,6 +1199,8 @@ hipError_t launch_wino_mid(const h16_t* M, const float* bias, int C, int F, int 
   int G = 1;
   while (G * 2 <= (C >> 3) && G * 2 <= 64) G *= 2;
   const long long runs = (long long)F * H * ((WQ + kWinoInRun - 1) / kWinoInRun);
+  // the kernel counts runs and column groups in 32 bits
+  if ((long long)F * H * WQ >= (1LL << 30)) return hipErrorInvalidValue;
   const long long threads = (runs + 64 / G - 1) / (64 / G) * 64;
   hipLaunchKernelGGL(wino_mid_kernel<1>, dim3(grid_for(threads, 256, 65536)), dim3(256), 0, s, M, bias, C, F, H, W,
                      WQ, G, gamma, U, hout, h_fstride, ldh, tail_from, h_first);
@@ -1240,6 +1248,30 @@ __global__ void math_probe_kernel(const float* __restrict__ x, float* __restrict
 hipError_t launch_math_probe(const float* x, float* silu_out, float* exp_out, long long n, hipStream_t s) {
   if (g_dry_run || n == 0) return hipSuccess;
   hipLaunchKernelGGL(math_probe_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, silu_out, exp_out, n);
+  return hipGetLastError();
+}
+
+// The kernels' fp16 packing (eight values at a time) and the input
+// transforms' norm scale, elementwise (the conversion self-test).
+__global__ void f16_probe_kernel(const float* __restrict__ x, uint16_t* __restrict__ h_out,
+                                 float* __restrict__ rs_out, long long n8) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  const float4 a = *reinterpret_cast<const float4*>(x + 8 * i);
+  const float4 b = *reinterpret_cast<const float4*>(x + 8 * i + 4);
+  const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  *reinterpret_cast<uint4*>(h_out + 8 * i) = pack8h(f);
+  float r[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) r[k] = norm_scale(f[k]);
+  *reinterpret_cast<float4*>(rs_out + 8 * i) = make_float4(r[0], r[1], r[2], r[3]);
+  *reinterpret_cast<float4*>(rs_out + 8 * i + 4) = make_float4(r[4], r[5], r[6], r[7]);
+}
+
+hipError_t launch_f16_probe(const float* x, uint16_t* h_out, float* rs_out, long long n, hipStream_t s) {
+  if (g_dry_run || n == 0) return hipSuccess;
+  const long long n8 = n / 8;
+  hipLaunchKernelGGL(f16_probe_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, x, h_out, rs_out, n8);
   return hipGetLastError();
 }
 

@@ -50,13 +50,20 @@ __device__ __forceinline__ uint32_t h16_bits(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
-// The rare path of f2h: saturate (flagged) or keep a NaN (flagged).
-__device__ __noinline__ uint32_t f2h_out_of_range(float f) {
-  if (abs_bits(f) > kF16MaxBits) {
-    __hip_atomic_fetch_or(&g_range_flags, f != f ? kRangeNaN : kRangeSaturated, __ATOMIC_RELAXED,
-                          __HIP_MEMORY_SCOPE_AGENT);
-  }
+// The rare path of the fp16 conversions: a finite value beyond +-65504
+// saturates and a NaN stays NaN; `flags` collects which of the two occurred.
+__device__ __forceinline__ uint32_t f2h_saturate(float f, uint32_t& flags) {
+  if (abs_bits(f) > kF16MaxBits) flags |= f != f ? kRangeNaN : kRangeSaturated;
   return h16_bits(f != f ? f : fminf(fmaxf(f, -kF16Max), kF16Max));
+}
+__device__ __forceinline__ void raise_range_flags(uint32_t flags) {
+  if (flags) __hip_atomic_fetch_or(&g_range_flags, flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __noinline__ uint32_t f2h_out_of_range(float f) {
+  uint32_t fl = 0;
+  const uint32_t r = f2h_saturate(f, fl);
+  raise_range_flags(fl);
+  return r;
 }
 
 // fp32 -> fp16, round to nearest even.  A finite value beyond +-65504
@@ -64,6 +71,12 @@ __device__ __noinline__ uint32_t f2h_out_of_range(float f) {
 __device__ __forceinline__ uint32_t f2h(float f) {
   return abs_bits(f) <= kF16MaxBits ? h16_bits(f) : f2h_out_of_range(f);
 }
+
+// Norm scale 1 / max(||v||, 1e-12) of a channel sum of squares ss >= 0, as
+// the Winograd input transforms compute it: min(rsqrt(ss), 1e12), one
+// hardware reciprocal square root (the conversion self-test, wvd_f16_probe,
+// bounds its error).
+__device__ __forceinline__ float norm_scale(float ss) { return fminf(__builtin_amdgcn_rsqf(ss), 1e12f); }
 
 // clamp(v, -1, 1) that keeps a NaN (the video's final clamp).
 __device__ __forceinline__ float clamp_unit(float v) { return v != v ? v : fminf(fmaxf(v, -1.0f), 1.0f); }
@@ -73,9 +86,38 @@ __device__ __forceinline__ float load_in(const void* p, long long i, int dt) {
   return dt == DT_F32 ? static_cast<const float*>(p)[i] : bf2f(static_cast<const bf16_t*>(p)[i]);
 }
 
+// Two values in one conversion instruction (v_cvt_pk_f16_f32, round to
+// nearest even like the scalar conversion), lo in the low half.
+typedef float f32x2v_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2v_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t h16x2_bits(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v_t){lo, hi}, f16x2v_t));
+}
+
+// The rare paths of pack2h / pack8h (leaf functions: no stack frame).
+__device__ __noinline__ uint32_t pack2h_out_of_range(float lo, float hi) {
+  uint32_t fl = 0;
+  const uint32_t r = f2h_saturate(lo, fl) | (f2h_saturate(hi, fl) << 16);
+  raise_range_flags(fl);
+  return r;
+}
+__device__ __noinline__ uint4 pack8h_out_of_range(float f0, float f1, float f2, float f3, float f4, float f5,
+                                                  float f6, float f7) {
+  uint32_t fl = 0;
+  const uint4 r = make_uint4(f2h_saturate(f0, fl) | (f2h_saturate(f1, fl) << 16),
+                             f2h_saturate(f2, fl) | (f2h_saturate(f3, fl) << 16),
+                             f2h_saturate(f4, fl) | (f2h_saturate(f5, fl) << 16),
+                             f2h_saturate(f6, fl) | (f2h_saturate(f7, fl) << 16));
+  raise_range_flags(fl);
+  return r;
+}
+
+// The common path converts unconditionally; only an out-of-range value
+// branches, and then the rare path recomputes the whole result.
 __device__ __forceinline__ uint32_t pack2h(float lo, float hi) {
-  if (max(abs_bits(lo), abs_bits(hi)) <= kF16MaxBits) return h16_bits(lo) | (h16_bits(hi) << 16);
-  return f2h_out_of_range(lo) | (f2h_out_of_range(hi) << 16);
+  uint32_t r = h16x2_bits(lo, hi);
+  if (max(abs_bits(lo), abs_bits(hi)) > kF16MaxBits) r = pack2h_out_of_range(lo, hi);
+  return r;
 }
 
 // Unpack 8 fp16 held in a uint4 into floats.
@@ -91,16 +133,9 @@ __device__ __forceinline__ uint4 pack8h(const float* f) {
   uint32_t m = 0;
 #pragma unroll
   for (int k = 0; k < 8; ++k) m = max(m, abs_bits(f[k]));
-  uint4 r;
-  if (m <= kF16MaxBits) {
-    r.x = h16_bits(f[0]) | (h16_bits(f[1]) << 16); r.y = h16_bits(f[2]) | (h16_bits(f[3]) << 16);
-    r.z = h16_bits(f[4]) | (h16_bits(f[5]) << 16); r.w = h16_bits(f[6]) | (h16_bits(f[7]) << 16);
-  } else {
-    r.x = f2h_out_of_range(f[0]) | (f2h_out_of_range(f[1]) << 16);
-    r.y = f2h_out_of_range(f[2]) | (f2h_out_of_range(f[3]) << 16);
-    r.z = f2h_out_of_range(f[4]) | (f2h_out_of_range(f[5]) << 16);
-    r.w = f2h_out_of_range(f[6]) | (f2h_out_of_range(f[7]) << 16);
-  }
+  uint4 r = make_uint4(h16x2_bits(f[0], f[1]), h16x2_bits(f[2], f[3]), h16x2_bits(f[4], f[5]),
+                       h16x2_bits(f[6], f[7]));
+  if (m > kF16MaxBits) r = pack8h_out_of_range(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
   return r;
 }
 

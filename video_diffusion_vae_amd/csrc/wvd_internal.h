@@ -230,6 +230,7 @@ hipError_t launch_prep_vec_add(const void* a, const void* b, int dtype, int n, f
 
 // silu_hw and exp_hw of n fp32 inputs (math self-test).
 hipError_t launch_math_probe(const float* x, float* silu_out, float* exp_out, long long n, hipStream_t s);
+hipError_t launch_f16_probe(const float* x, uint16_t* h_out, float* rs_out, long long n, hipStream_t s);
 
 // Device addresses of the range flags (see g_range_flags) of the two kernel
 // code objects on the current device.

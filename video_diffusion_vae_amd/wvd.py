@@ -83,6 +83,8 @@ def _load() -> ctypes.CDLL:
     lib.wvd_last_launch_count.restype = ctypes.c_longlong
     lib.wvd_math_probe.argtypes = [vp, vp, vp, ctypes.c_longlong, vp]
     lib.wvd_math_probe.restype = i
+    lib.wvd_f16_probe.argtypes = [vp, vp, vp, ctypes.c_longlong, vp]
+    lib.wvd_f16_probe.restype = i
     lib.wvd_range_flags.argtypes = [vp, i, ctypes.POINTER(ctypes.c_uint)]
     lib.wvd_range_flags.restype = i
     lib.wvd_profile_enable.argtypes = [vp, i]
@@ -217,6 +219,10 @@ def wvd_range_flags(stream_ptr: int, clear: bool) -> int:
 
 def wvd_math_probe(x_ptr: int, silu_ptr: int, exp_ptr: int, n: int, stream_ptr: int) -> None:
     _check(_lib.wvd_math_probe(x_ptr, silu_ptr, exp_ptr, n, stream_ptr), "wvd_math_probe")
+
+
+def wvd_f16_probe(x_ptr: int, h_ptr: int, rs_ptr: int, n: int, stream_ptr: int) -> None:
+    _check(_lib.wvd_f16_probe(x_ptr, h_ptr, rs_ptr, n, stream_ptr), "wvd_f16_probe")
 
 
 def range_flags(clear: bool = True) -> int:
