@@ -1008,6 +1008,7 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
       if constexpr (K333) {
         constexpr int IPT = (kNHV333 * NP + NT - 1) / NT;
         static_assert(IPT + 3 <= 27, "halo items must land inside a chunk");
+        static_assert(6 % kBRing == 0, "slot s6 % kBRing must continue across tap groups");
         uint4 hr[3];
         f16x8_t ap[2][MI];  // A fragments one step ahead (APF)
         if constexpr (APF) {
@@ -1074,6 +1075,7 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
         constexpr int IPT = (NHV * NP + NT - 1) / NT;
         constexpr int IPK = (IPT + 4) / 5;
         static_assert(IPK <= 2, "halo items per tap");
+        static_assert(18 % kBRing == 0, "slot u % kBRing must continue across chunks");
         constexpr int LAGT = kWinoLag;
         static_assert(LAGT >= 1 && LAGT + 4 <= 8, "halo items stored inside the chunk");
         uint4 hr[LAGT][IPK];
@@ -1179,6 +1181,7 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
         static_assert(!APF, "the phase loop runs on 8 waves");
         constexpr int IPT = ((1 * 18 * 18) * NP + NT - 1) / NT;
         constexpr int PD = kPhaseBRing;  // B fragments of step u in slot u % PD, refilled with step u + PD
+        static_assert(8 % PD == 0, "slot u % PD must continue across chunks");
         constexpr int NLS = IPT;
         constexpr int LAG = 8 - NLS;
         static_assert(NLS >= 1 && LAG >= 3, "phase halo items land inside a chunk");
