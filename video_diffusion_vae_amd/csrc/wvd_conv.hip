@@ -33,6 +33,7 @@
 // as the TensorRT-LLM norm-SiLU issue describes for the decoder's residual
 // norms and norm_out, statistics in fp32 (Wan2.2 page, "Limits").
 #include <cstring>
+#include <type_traits>
 
 #include "wvd_internal.h"
 
@@ -1499,30 +1500,38 @@ Variant conv_variant(const ConvArgs& a) {
 }
 
 // ---------------------------------------------------------------------------
-// 1x1 convolution as a plain GEMM, out[m][n] = sum_k x[m][k] w[n][k] + bias[n]
-// (the shortcut of a width-changing block).  It streams its activations from
-// HBM once, so it is organised for that: one persistent workgroup per CU walks
-// 256 x 256 tiles in K chunks of kG1K channels.  Every thread issues all of a
-// chunk's loads (16 coalesced 16-byte pieces of A rows, 16 of fragment-order
-// weights) at the start of the previous chunk and commits them to LDS at its
-// end, so the only wait on memory is one per chunk, a whole chunk of MFMAs
-// after the loads were issued (a per-step register ring would make every
-// weight fetch wait, in order, behind the slower activation fetches).  Four
-// waves of 128 x 128 (accumulators in AGPRs, weights as the MFMA's first
-// operand) read their fragments from LDS one k16 step ahead.
+// Batched NT GEMM tiles (gemm_nt_kernel below): 256 x 256 tiles in K chunks of
+// kG1K channels, one chunk of loads in flight.
 constexpr int kG1K = 128;               // K channels per chunk
 constexpr int kG1ARow = kG1K * 2 + 16;  // staged A row bytes (+16 pad: conflict-free fragment reads)
 constexpr int kG1Lds = 256 * kG1ARow + 256 * kG1K * 2;
+
+// 1x1 convolution as a plain GEMM, out[m][n] = sum_k x[m][k] w[n][k] + bias[n]
+// (the shortcut of a width-changing block).  It streams its activations from
+// HBM once, so it is organised for that: one persistent workgroup per CU walks
+// 256 x 256 tiles in K chunks of kS1K channels, a chunk stream that runs on
+// from one tile into the next.  Two LDS buffers hold chunks g and g + 1 and two
+// register sets stage the loads (8 coalesced 16-byte pieces of A rows and 8
+// fragment-order weight blocks per thread): chunk g + 2 is issued at the start
+// of chunk g and chunk g + 1 committed to LDS at its end, so every load has two
+// chunks of MFMAs to arrive in and every CU keeps two chunks of loads in
+// flight.  Four waves of 128 x 128 (accumulators in AGPRs, weights as the
+// MFMA's first operand) read their fragments from LDS one k16 step ahead.
+// A call is about 0.9 TFLOP over 5.4 GB at the c=256 shapes, so the MFMA and
+// HBM floors (about 0.7 and 0.9 ms) are both close to its time (1.3 ms); the
+// rolling pipeline measured 3 % faster than one 128-channel chunk per wait.
+constexpr int kS1K = 64;                 // K channels per chunk
+constexpr int kS1ARow = kS1K * 2 + 16;   // staged A row bytes (36 dwords: conflict-free fragment reads)
+constexpr int kS1Buf = 256 * kS1ARow + 256 * kS1K * 2;
+constexpr int kS1Lds = 2 * kS1Buf;
 
 __global__ __launch_bounds__(256) void gemm1x1_kernel(const h16_t* __restrict__ x, long long M, int lda, int K,
                                                       const h16_t* __restrict__ w, int w_bytes, int N,
                                                       const float* __restrict__ bias, h16_t* __restrict__ out,
                                                       int ldo) {
-  constexpr int MI = 4, NJ = 4, CS = kG1K / 16, PPR = kG1K * 2 / 16, IPT = 16;
-  static_assert(PPR == 16 && IPT == 16 && CS == 8, "16 A pieces (16 rows apart) and 16 B blocks per thread");
+  constexpr int MI = 4, NJ = 4, CS = kS1K / 16, PPR = kS1K * 2 / 16, IPT = 8;
+  static_assert(PPR == 8 && CS == 4 && 256 * PPR == 256 * IPT, "8 A pieces (32 rows apart) and 8 B blocks per thread");
   extern __shared__ __align__(16) unsigned char g1s[];
-  unsigned char* As = g1s;
-  unsigned char* Bs = g1s + 256 * kG1ARow;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -1531,15 +1540,13 @@ __global__ __launch_bounds__(256) void gemm1x1_kernel(const h16_t* __restrict__ 
   const long long nMt = (M + 255) / 256;
   const TileSeq seq = tile_seq((int)(nMt * nN));
   if (seq.at(0) < 0) return;
-  const int nch = K / kG1K;
+  const int nch = K / kS1K;  // even (the launcher checks)
   const int U = K / 16;
   const __amdgpu_buffer_rsrc_t brsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<h16_t*>(w), 0, w_bytes, 0x00020000);
 
-  // this thread's pieces: A row (tid / PPR) + 16 r, part tid % PPR; B block
-  // (tid + 256 r) / 64 = (32-column block nbl, k16 step s), lane (tid % 64)
-  uint4 sa[IPT], sb[IPT];
-  // Only the lane-dependent parts of the addresses live in VGPRs; the piece
-  // index r and the chunk go into the scalar offset.
+  // this thread's pieces: A row (tid / PPR) + 32 r, part tid % PPR; B block
+  // (n32 block r of the tile, k16 step `wave` of the chunk), lane (tid % 64)
+  uint4 sa[2][IPT], sb[2][IPT];
   const int avoff = ((tid / PPR) * lda + (tid % PPR) * 8) * 2;
   const int bvoff = lane * 16;
   // The last row tile is shifted back to end at row M (M >= 256), so every
@@ -1549,40 +1556,39 @@ __global__ __launch_bounds__(256) void gemm1x1_kernel(const h16_t* __restrict__ 
     const long long m0 = (long long)(tile / nN) * 256;
     return m0 + 256 <= M ? m0 : M - 256;
   };
-  auto issue = [&](int tile, int ch) {
+  auto issue = [&](uint4 (&ra)[IPT], uint4 (&rb)[IPT], int tile, int ch) {
     const long long m0 = tile_m0(tile);
     const int bn = tile % nN;
     const __amdgpu_buffer_rsrc_t arsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<h16_t*>(x + m0 * lda), 0, 256 * lda * 2, 0x00020000);
 #pragma unroll
     for (int r = 0; r < IPT; ++r)
-      sa[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            arsrc, avoff, (16 * r * lda + ch * kG1K) * 2, 0));
+      ra[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            arsrc, avoff, (32 * r * lda + ch * kS1K) * 2, 0));
 #pragma unroll
     for (int r = 0; r < IPT; ++r) {
-      // block (wave + 4r): 32-column block r / 2, k16 step wave + 4 (r % 2)
-      const int nb = bn * 8 + r / 2, u = ch * CS + wave + 4 * (r % 2);
-      sb[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(brsrc, bvoff, (nb * U + u) * 1024, 0));
+      const int nb = bn * 8 + r, u = ch * CS + wave;
+      rb[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(brsrc, bvoff, (nb * U + u) * 1024, 0));
     }
   };
-  const int aloff = (tid / PPR) * kG1ARow + (tid % PPR) * 16;
-  const int bloff = wave * 1024 + lane * 16;
-  auto commit = [&]() {
+  // LDS buffer b: A rows at b * kS1Buf, B blocks (n32 block nb, k16 step s at
+  // (nb * CS + s) * 1024) after them
+  const int aloff = (tid / PPR) * kS1ARow + (tid % PPR) * 16;
+  const int bloff = 256 * kS1ARow + wave * 1024 + lane * 16;
+  auto commit = [&](const uint4 (&ra)[IPT], const uint4 (&rb)[IPT], int buf) {
+    unsigned char* base = g1s + buf * kS1Buf;
 #pragma unroll
     for (int r = 0; r < IPT; ++r) {
-      *reinterpret_cast<uint4*>(As + aloff + 16 * r * kG1ARow) = sa[r];
-      *reinterpret_cast<uint4*>(Bs + bloff + r * 4096) = sb[r];
+      *reinterpret_cast<uint4*>(base + aloff + 32 * r * kS1ARow) = ra[r];
+      *reinterpret_cast<uint4*>(base + bloff + r * CS * 1024) = rb[r];
     }
   };
   int abase[MI], bbase[NJ];
 #pragma unroll
-  for (int i = 0; i < MI; ++i) abase[i] = (wm * 128 + 32 * i + lrow) * kG1ARow + kpart * 16;
+  for (int i = 0; i < MI; ++i) abase[i] = (wm * 128 + 32 * i + lrow) * kS1ARow + kpart * 16;
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) bbase[j] = (wn * 4 + j) * CS * 1024 + lane * 16;
+  for (int j = 0; j < NJ; ++j) bbase[j] = 256 * kS1ARow + (wn * 4 + j) * CS * 1024 + lane * 16;
 
-  issue(seq.at(0), 0);
-  commit();
-  __syncthreads();
   f32x16_t acc[MI][NJ];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
@@ -1591,115 +1597,136 @@ __global__ __launch_bounds__(256) void gemm1x1_kernel(const h16_t* __restrict__ 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
+  // Chunk g + 1 and g + 2 of the stream after chunk ch of tile cur (next
+  // tile nxt; tile < 0: past the end).  nch is even, so every tile's chunks
+  // alternate parity 0, 1, ... and the last one has parity 1.
+  auto ahead = [&](int cur, int nxt, int ch, int d, int& tile, int& c) {
+    tile = ch + d < nch ? cur : nxt;
+    c = ch + d < nch ? ch + d : ch + d - nch;
+  };
+  {
+    int t1, c1;
+    ahead(seq.at(0), seq.at(1), 0, 1, t1, c1);
+    issue(sa[0], sb[0], seq.at(0), 0);
+    issue(sa[1], sb[1], t1 >= 0 ? t1 : seq.at(0), t1 >= 0 ? c1 : 0);
+    commit(sa[0], sb[0], 0);
+  }
+  __syncthreads();
+
+  // Chunk ch of tile cur with register set / LDS buffer parity P (a
+  // compile-time value, so the staging sets stay in registers).
+  auto chunk = [&](auto parity, int cur, int nxt, int ch) {
+    constexpr int P = decltype(parity)::value;
+    int t1, c1, t2, c2;
+    ahead(cur, nxt, ch, 1, t1, c1);
+    ahead(cur, nxt, ch, 2, t2, c2);
+    // unconditional (past the end of the stream it reloads this chunk,
+    // unused), so the set's previous values need not live on
+    issue(sa[P], sb[P], t2 >= 0 ? t2 : cur, t2 >= 0 ? c2 : ch);
+    __builtin_amdgcn_sched_barrier(0);
+    const unsigned char* buf = g1s + P * kS1Buf;
+    f16x8_t ap[2][MI], bp[2][NJ];
+#pragma unroll
+    for (int i = 0; i < MI; ++i) ap[0][i] = *reinterpret_cast<const f16x8_t*>(buf + abase[i]);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) bp[0][j] = *reinterpret_cast<const f16x8_t*>(buf + bbase[j]);
+#pragma unroll
+    for (int s = 0; s < CS; ++s) {
+      if (s + 1 < CS) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+          ap[(s + 1) & 1][i] = *reinterpret_cast<const f16x8_t*>(buf + abase[i] + (s + 1) * 32);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          bp[(s + 1) & 1][j] = *reinterpret_cast<const f16x8_t*>(buf + bbase[j] + (s + 1) * 1024);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bp[s & 1][j], ap[s & 1][i], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // chunk g + 1 (issued two chunks ago) into the other buffer, whose last
+    // reader (chunk g - 1) finished before the previous barrier; the barrier
+    // makes it visible and ends every wave's reads of this buffer
+    if (t1 >= 0) commit(sa[P ^ 1], sb[P ^ 1], P ^ 1);
+    __syncthreads();
+  };
+
   for (int k = 0;; ++k) {
     const int cur = seq.at(k);
     if (cur < 0) break;
     const int nxt = seq.at(k + 1);
-    for (int ch = 0; ch < nch; ++ch) {
-      const bool last = ch + 1 == nch;
-      const bool more = !last || nxt >= 0;  // uniform
-      if (more) issue(last ? nxt : cur, last ? 0 : ch + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      f16x8_t ap[2][MI], bp[2][NJ];
+    for (int ch = 0; ch < nch; ch += 2) {
+      chunk(std::integral_constant<int, 0>{}, cur, nxt, ch);
+      chunk(std::integral_constant<int, 1>{}, cur, nxt, ch + 1);
+    }
+    // epilogue through the A rows of buffer 1 (the tile's last chunk): lane
+    // (kpart, lrow) of block (i, j) holds row 32i + lrow of the wave's rows
+    // and channels 32j + 8g + 4*kpart + r (accumulator 4g + r); per 32 rows
+    // and 64 channels the runs go straight from the accumulators into fp32
+    // LDS rows, then eight channels per lane get the bias, fp16 and a
+    // 16-byte store.
+    constexpr int SROW = 64 * 4 + 16, LPR = 8, RPI = 8;
+    static_assert(4 * 32 * SROW <= 256 * kS1ARow, "staging fits in a buffer's A rows");
+    unsigned char* st = g1s + kS1Buf + wave * 32 * SROW;
+    const long long m0 = tile_m0(cur);
+    const int n0 = (cur % nN) * 256 + wn * 128;
 #pragma unroll
-      for (int i = 0; i < MI; ++i) ap[0][i] = *reinterpret_cast<const f16x8_t*>(As + abase[i]);
+    for (int i = 0; i < MI; ++i) {
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) bp[0][j] = *reinterpret_cast<const f16x8_t*>(Bs + bbase[j]);
+      for (int jh = 0; jh < NJ / 2; ++jh) {
 #pragma unroll
-      for (int s = 0; s < CS; ++s) {
-        if (s + 1 < CS) {
+        for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-          for (int i = 0; i < MI; ++i)
-            ap[(s + 1) & 1][i] = *reinterpret_cast<const f16x8_t*>(As + abase[i] + (s + 1) * 32);
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x16_t& c = acc[i][jh * 2 + jj];
+            f32x4_t v = {c[4 * g4], c[4 * g4 + 1], c[4 * g4 + 2], c[4 * g4 + 3]};
+            *reinterpret_cast<f32x4_t*>(st + lrow * SROW + (32 * jj + 8 * g4 + 4 * kpart) * 4) = v;
+          }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the block is in LDS
+        __builtin_amdgcn_wave_barrier();
+        const int ncol = n0 + jh * 64 + (lane % LPR) * 8;
+        float bv[8];
 #pragma unroll
-          for (int j = 0; j < NJ; ++j)
-            bp[(s + 1) & 1][j] = *reinterpret_cast<const f16x8_t*>(Bs + bbase[j] + (s + 1) * 1024);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        for (int q = 0; q < 8; ++q) bv[q] = 0.0f;
+        if (bias) {
+          const f32x4_t b0 = *reinterpret_cast<const f32x4_t*>(bias + ncol);
+          const f32x4_t b1 = *reinterpret_cast<const f32x4_t*>(bias + ncol + 4);
 #pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-          for (int j = 0; j < NJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bp[s & 1][j], ap[s & 1][i], acc[i][j], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      __syncthreads();  // every wave is done reading this chunk
-      if (last) {
-        // epilogue through the A region: lane (kpart, lrow) of block (i, j)
-        // holds row 32i + lrow of the wave's rows and channels
-        // 32j + 8g + 4*kpart + r (accumulator 4g + r); per 32 rows and 64
-        // channels the runs go straight from the accumulators into fp32 LDS
-        // rows, then eight channels per lane get the bias, fp16 and a
-        // 16-byte store.
-        constexpr int SROW = 64 * 4 + 16, LPR = 8, RPI = 8;
-        static_assert(4 * 32 * SROW <= 256 * kG1ARow, "staging fits in the A region");
-        unsigned char* st = As + wave * 32 * SROW;
-        const long long m0 = tile_m0(cur);
-        const int n0 = (cur % nN) * 256 + wn * 128;
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-#pragma unroll
-          for (int jh = 0; jh < NJ / 2; ++jh) {
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-              for (int g4 = 0; g4 < 4; ++g4) {
-                const f32x16_t& c = acc[i][jh * 2 + jj];
-                f32x4_t v = {c[4 * g4], c[4 * g4 + 1], c[4 * g4 + 2], c[4 * g4 + 3]};
-                *reinterpret_cast<f32x4_t*>(st + lrow * SROW + (32 * jj + 8 * g4 + 4 * kpart) * 4) = v;
-              }
-            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the block is in LDS
-            __builtin_amdgcn_wave_barrier();
-            const int ncol = n0 + jh * 64 + (lane % LPR) * 8;
-            float bv[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) bv[q] = 0.0f;
-            if (bias) {
-              const f32x4_t b0 = *reinterpret_cast<const f32x4_t*>(bias + ncol);
-              const f32x4_t b1 = *reinterpret_cast<const f32x4_t*>(bias + ncol + 4);
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                bv[q] = b0[q];
-                bv[4 + q] = b1[q];
-              }
-            }
-#pragma unroll
-            for (int rr = 0; rr < 32 / RPI; ++rr) {
-              const int r = rr * RPI + lane / LPR;
-              const float* row = reinterpret_cast<const float*>(st + r * SROW) + (lane % LPR) * 8;
-              const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(row);
-              const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(row + 4);
-              const long long m = m0 + wm * 128 + 32 * i + r;
-              {
-                const float v8[8] = {lo[0] + bv[0], lo[1] + bv[1], lo[2] + bv[2], lo[3] + bv[3],
-                                     hi[0] + bv[4], hi[1] + bv[5], hi[2] + bv[6], hi[3] + bv[7]};
-                *reinterpret_cast<uint4*>(out + m * ldo + ncol) = pack8h(v8);
-              }
-            }
-            __builtin_amdgcn_s_waitcnt(0xc07f);  // this round's reads before the next round's writes
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_sched_barrier(0);
+          for (int q = 0; q < 4; ++q) {
+            bv[q] = b0[q];
+            bv[4 + q] = b1[q];
           }
         }
 #pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-          for (int j = 0; j < NJ; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-        __syncthreads();  // the staging rows are free again
+        for (int rr = 0; rr < 32 / RPI; ++rr) {
+          const int r = rr * RPI + lane / LPR;
+          const float* row = reinterpret_cast<const float*>(st + r * SROW) + (lane % LPR) * 8;
+          const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(row);
+          const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(row + 4);
+          const long long m = m0 + wm * 128 + 32 * i + r;
+          const float v8[8] = {lo[0] + bv[0], lo[1] + bv[1], lo[2] + bv[2], lo[3] + bv[3],
+                               hi[0] + bv[4], hi[1] + bv[5], hi[2] + bv[6], hi[3] + bv[7]};
+          *reinterpret_cast<uint4*>(out + m * ldo + ncol) = pack8h(v8);
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // this round's reads before the next round's writes
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (more) commit();
-      __syncthreads();
     }
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    __syncthreads();  // the staging rows are read before the next tile's chunk 1 lands here
   }
 }
 
-// Frames: tile t of the whole grid is frame t / (row tiles x column tiles);
-// A, B, the output and the residual of frame f start f times their strides
-// further.  The epilogue (EPI, a GemmEpi) is chosen at compile time.  The
-// last row tile of a frame is shifted back to end at row M; the rows it
-// shares with the tile before are stored by that tile only.
 template <int EPI>
 __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs ga) {
   constexpr int MI = 4, NJ = 4, CS = kG1K / 16, PPR = kG1K * 2 / 16, IPT = 16;
@@ -1978,7 +2005,8 @@ hipError_t launch_gemm_nt(const GemmArgs& g, int epi, hipStream_t stream) {
 hipError_t launch_gemm1x1(const h16_t* x, long long M, int lda, int K, const h16_t* w, long long w_bytes, int N,
                           const float* bias, h16_t* out, int ldo, hipStream_t stream) {
   if (g_dry_run) return hipSuccess;
-  if (!x || !w || !out || M < 256 || N % 256 || K % kG1K || K > 4096 || lda % 8 || lda < K || ldo % 8 || ldo < N ||
+  if (!x || !w || !out || M < 256 || N % 256 || K % (2 * kS1K) || K > 4096 || lda % 8 || lda < K ||
+      ldo % 8 || ldo < N ||
       w_bytes <= 0 || w_bytes > 0x7fffffffLL || (long long)256 * lda * 2 > 0x7fffffffLL)
     return hipErrorInvalidValue;
   const long long tiles = (M + 255) / 256 * (N / 256);
@@ -1986,7 +2014,7 @@ hipError_t launch_gemm1x1(const h16_t* x, long long M, int lda, int K, const h16
   static bool attr = false;
   if (!attr) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm1x1_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kG1Lds);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kS1Lds);
     if (e != hipSuccess) return e;
     attr = true;
   }
@@ -1995,7 +2023,7 @@ hipError_t launch_gemm1x1(const h16_t* x, long long M, int lda, int K, const h16
   if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   const long long grid = tiles < ncu ? tiles : ncu;
-  hipLaunchKernelGGL(gemm1x1_kernel, dim3((unsigned)grid), dim3(256), kG1Lds, stream, x, M, lda, K, w, (int)w_bytes,
+  hipLaunchKernelGGL(gemm1x1_kernel, dim3((unsigned)grid), dim3(256), kS1Lds, stream, x, M, lda, K, w, (int)w_bytes,
                      N, bias, out, ldo);
   return hipGetLastError();
 }
