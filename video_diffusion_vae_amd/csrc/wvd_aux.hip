@@ -80,34 +80,66 @@ __global__ __launch_bounds__(256) void rms_stats_kernel(const h16_t* __restrict_
   }
 }
 
-// y = SiLU(x * rs * gamma) for the F frames of a pass, rs from the voxel's
-// channel norm exactly as rms_stats_kernel computes it (same lane split and
-// butterfly).  Used where a norm-SiLU input feeds a conv with few output
-// channels (the head), so every voxel is normalised once instead of once per
+// Sum of v over aligned groups of G lanes (G a power of two <= 64), the
+// same value, added in the same order, in every lane of a group: DPP steps
+// pair lanes within rows of 16 (xor 1, xor 2, then mirrored halves of 8 and
+// of 16), cross-lane permutes take the rows of 32 and 64.
+__device__ __forceinline__ float dpp_f32(float a, int ctrl) {
+  const int x = __builtin_bit_cast(int, a);
+  switch (ctrl) {
+    case 0: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));
+    case 1: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));
+    case 2: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false));
+    default: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false));
+  }
+}
+
+__device__ __forceinline__ float lane_group_sum(float v, int G) {
+  if (G >= 2) v += dpp_f32(v, 0);   // quad_perm [1,0,3,2]
+  if (G >= 4) v += dpp_f32(v, 1);   // quad_perm [2,3,0,1]
+  if (G >= 8) v += dpp_f32(v, 2);   // row_half_mirror
+  if (G >= 16) v += dpp_f32(v, 3);  // row_mirror
+  if (G >= 32) v += __shfl_xor(v, 16, 64);
+  if (G >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+// y = SiLU(x * rs * gamma) (ACT) or x * rs * gamma for the F frames of a
+// pass, rs from the voxel's channel norm exactly as rms_stats_kernel computes
+// it (same lane split; the DPP butterfly adds the same two partials at every
+// level as its shuffles, so the sums are identical).  Used where a norm-SiLU
+// input feeds a conv with few output channels (the head) and for the
+// attention's norm, so every voxel is normalised once instead of once per
 // halo that contains it.  The arithmetic per element is the conv prologue's.
+template <bool ACT>
 __global__ __launch_bounds__(256) void norm_silu_kernel(const h16_t* __restrict__ x, long long x_fstride, int lda,
                                                         int C, int F, int HW, int G,
                                                         const float* __restrict__ gamma, h16_t* __restrict__ y,
-                                                        long long y_fstride, int ldy, int act) {
+                                                        long long y_fstride, int ldy) {
   const int lane = threadIdx.x & 63;
   const int sub = lane % G;
   const int vox_per_wave = 64 / G;
-  const long long gw = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-  const long long nw = ((long long)gridDim.x * blockDim.x) >> 6;
-  const long long nvox = (long long)F * HW;
+  const int gw = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int nw = (gridDim.x * blockDim.x) >> 6;
+  const int nvox = F * HW;  // (the launcher checks the range)
   const bool second = sub + G < (C >> 3);
-  const long long step = (long long)vox_per_wave * kStatsU;
-  for (long long base = gw * step; base < nvox; base += nw * step) {
+  const int step = vox_per_wave * kStatsU;
+  float gm[2][8];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) gm[q][k] = q == 0 || second ? gamma[(sub + q * G) * 8 + k] : 0.0f;
+  for (int base = gw * step; base < nvox; base += nw * step) {
     uint4 r[kStatsU][2];
-    long long fr[kStatsU], pix[kStatsU];
+    int fr[kStatsU], pix[kStatsU];
     bool ok[kStatsU];
 #pragma unroll
     for (int u = 0; u < kStatsU; ++u) {
-      const long long vv = base + (long long)u * vox_per_wave + lane / G;
+      const int vv = base + u * vox_per_wave + lane / G;
       ok[u] = vv < nvox;
       fr[u] = ok[u] ? vv / HW : 0;
       pix[u] = ok[u] ? vv % HW : 0;
-      const h16_t* p = x + fr[u] * x_fstride + pix[u] * lda;
+      const h16_t* p = x + fr[u] * x_fstride + (long long)pix[u] * lda;
       r[u][0] = make_uint4(0, 0, 0, 0);
       r[u][1] = make_uint4(0, 0, 0, 0);
       if (ok[u]) {
@@ -127,10 +159,10 @@ __global__ __launch_bounds__(256) void norm_silu_kernel(const h16_t* __restrict_
         for (int k = 0; k < 8; ++k) t = fmaf(f[k], f[k], t);
         ss += t;
       }
-      for (int off = 1; off < G; off <<= 1) ss += __shfl_xor(ss, off, 64);
+      ss = lane_group_sum(ss, G);
       const float sc = 1.0f / fmaxf(sqrtf(ss), kNormEps);
       if (!ok[u]) continue;
-      h16_t* o = y + fr[u] * y_fstride + pix[u] * ldy;
+      h16_t* o = y + fr[u] * y_fstride + (long long)pix[u] * ldy;
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         if (q == 1 && !second) break;
@@ -139,8 +171,8 @@ __global__ __launch_bounds__(256) void norm_silu_kernel(const h16_t* __restrict_
         unpack8h(r[u][q], f);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const float t = f[k] * sc * gamma[g8 + k];
-          f[k] = act ? silu_hw(t) : t;
+          const float t = f[k] * sc * gm[q][k];
+          f[k] = ACT ? silu_hw(t) : t;
         }
         *reinterpret_cast<uint4*>(o + g8) = pack8h(f);
       }
@@ -564,30 +596,6 @@ __global__ void prep_wino_frag_kernel(const void* __restrict__ w, int dtype, int
     }
     out[e] = (h16_t)f2h(v);
   }
-}
-
-// Sum of v over aligned groups of G lanes (G a power of two <= 64), the
-// same value, added in the same order, in every lane of a group: DPP steps
-// pair lanes within rows of 16 (xor 1, xor 2, then mirrored halves of 8 and
-// of 16), cross-lane permutes take the rows of 32 and 64.
-__device__ __forceinline__ float dpp_f32(float a, int ctrl) {
-  const int x = __builtin_bit_cast(int, a);
-  switch (ctrl) {
-    case 0: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));
-    case 1: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));
-    case 2: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false));
-    default: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false));
-  }
-}
-
-__device__ __forceinline__ float lane_group_sum(float v, int G) {
-  if (G >= 2) v += dpp_f32(v, 0);   // quad_perm [1,0,3,2]
-  if (G >= 4) v += dpp_f32(v, 1);   // quad_perm [2,3,0,1]
-  if (G >= 8) v += dpp_f32(v, 2);   // row_half_mirror
-  if (G >= 16) v += dpp_f32(v, 3);  // row_mirror
-  if (G >= 32) v += __shfl_xor(v, 16, 64);
-  if (G >= 64) v += __shfl_xor(v, 32, 64);
-  return v;
 }
 
 // Zeros that the transforms read in place of columns outside a row (no
@@ -1046,9 +1054,14 @@ hipError_t launch_norm_silu(const h16_t* x, long long x_fstride, int lda, int C,
   while (G < 64 && G * 2 <= C / 8) G *= 2;
   if (C % 8 || C / 8 > 2 * G || C > 1024) return hipErrorInvalidValue;
   const long long nvox = (long long)F * HW;
+  if (nvox >= (1LL << 30)) return hipErrorInvalidValue;  // the kernel counts voxels in 32 bits
   const long long waves = (nvox + (64 / G) * kStatsU - 1) / ((64 / G) * kStatsU);
-  hipLaunchKernelGGL(norm_silu_kernel, dim3(grid_for(waves * 64, 256, 16384)), dim3(256), 0, s, x, x_fstride, lda, C,
-                     F, HW, G, gamma, y, y_fstride, ldy, act ? 1 : 0);
+  if (act)
+    hipLaunchKernelGGL(norm_silu_kernel<true>, dim3(grid_for(waves * 64, 256, 16384)), dim3(256), 0, s, x, x_fstride,
+                       lda, C, F, HW, G, gamma, y, y_fstride, ldy);
+  else
+    hipLaunchKernelGGL(norm_silu_kernel<false>, dim3(grid_for(waves * 64, 256, 16384)), dim3(256), 0, s, x, x_fstride,
+                       lda, C, F, HW, G, gamma, y, y_fstride, ldy);
   return hipGetLastError();
 }
 
