@@ -1186,19 +1186,19 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
         constexpr int NLS = IPT;
         constexpr int LAG = 8 - NLS;
         static_assert(NLS >= 1 && LAG >= 3, "phase halo items land inside a chunk");
-        const int py = geo.ph >> 1, px = geo.ph & 1;
-        auto toff = [&](int u) {
-          const int tap = u >> 1;
-          return ((py + (tap >> 1)) * HX + (px + (tap & 1))) * ROWB + (u & 1) * 32;
-        };
+        // the phase's (py, px) offset goes into the row bases once per chunk,
+        // so each step's tap offset is an instruction immediate
+        const int phoff = ((geo.ph >> 1) * HX + (geo.ph & 1)) * ROWB;
+        const unsigned char* hph = hsrc + phoff;
         uint4 hr[IPT];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           f16x8_t av[MI];
           {
-            const int o = toff(u);
+            const int tap = u >> 1;
+            const int o = ((tap >> 1) * HX + (tap & 1)) * ROWB + (u & 1) * 32;
 #pragma unroll
-            for (int i = 0; i < MI; ++i) av[i] = *reinterpret_cast<const f16x8_t*>(hsrc + g.abase[i] + o);
+            for (int i = 0; i < MI; ++i) av[i] = *reinterpret_cast<const f16x8_t*>(hph + g.abase[i] + o);
           }
           {
             const int is = u - LAG, il = u;
@@ -1488,8 +1488,8 @@ Variant conv_variant(const ConvArgs& a) {
     v.bn = 256;
     v.nw = 8;
   } else if (v.mode == 1 && a.Cout <= 32) {
-    // narrow raw 3x3x3 (the head): eight waves of 32 x 32, one MFMA per
-    // k16 step each, all sharing one B fragment stream
+    // narrow raw 3x3x3 (the head): one n32 block (the generic kernel runs it
+    // as eight waves of 32 x 32, the persistent one as four of 64 x 32)
     v.bn = 32;
     v.nw = 8;
   } else {
@@ -2135,7 +2135,10 @@ hipError_t launch_conv(const ConvArgs& a, hipStream_t stream) {
       if (a.TF == 4 && a.TW == 4) return launch_persist_impl<256, 2, 4, PRO_RAW, 4, 4, 4>(a, stream);
       return launch_persist_impl<256, 2, 4, PRO_RAW, 4>(a, stream);
     }
-    if (v.bn == 32) return launch_persist_impl<32, 1, 1, PRO_RAW>(a, stream);
+    // the head (N = 32): 4 waves of 64 x 32, so each weight fragment feeds
+    // two MFMAs (its one n32 block is the same for every wave, and eight
+    // waves of 32 x 32 fetched every fragment eight times from L2)
+    if (v.bn == 32) return launch_persist_impl<32, 1, 1, PRO_RAW, 4>(a, stream);
     if (pro == PRO_NORM_SILU) return launch_persist_impl<256, 2, 1, PRO_NORM_SILU, 4>(a, stream);
     return launch_persist_impl<256, 4, 1, PRO_RAW>(a, stream);
   }
