@@ -24,7 +24,7 @@ namespace {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
-enum ItemKind { K_CONV = 0, K_PHASE = 1, K_VEC = 2, K_WINO = 3, K_CONV_PART = 4 };
+enum ItemKind { K_CONV = 0, K_PHASE = 1, K_VEC = 2, K_WINO = 3, K_CONV_PART = 4, K_S2D = 5 };
 
 // A 3x3x3 norm-SiLU conv runs in Winograd form (F(kWinoM,3) along x: input
 // transform, kWinoN xi-plane GEMMs on the persistent kernel, output transform)
@@ -303,13 +303,23 @@ Layout make_layout_enc(int c, int h, int w) {
   Layout L;
   L.encoder = true;
   const int c4 = 4 * c;
-  add_conv(L, c, 12, 27, 16, &L.conv_in_w, &L.conv_in_b);  // 12 patch channels, padded to 16
+  // 12 patch channels, padded to 32: one 32-channel chunk, so conv_in runs on
+  // the specialised 3x3x3 kernel (16-channel chunks would take the generic one)
+  add_conv(L, c, 12, 27, kEncInC, &L.conv_in_w, &L.conv_in_b);
   int prev = c;
   for (int s = 0; s < 4; ++s) {
     const int cs = enc_width(c, s);
     L.down[s][0] = add_rb(L, prev, cs);
     L.down[s][1] = add_rb(L, cs, cs);
-    if (s < 3) add_conv(L, cs, cs, 9, cs, &L.dc_w[s], &L.dc_b[s]);
+    if (s < 3) {
+      // the stride-2 down-conv runs in space-to-depth form: 2x2 taps over
+      // the four phase images (4 cs input channels)
+      add_conv(L, cs, cs, 9, cs, &L.dc_w[s], &L.dc_b[s]);
+      Item& it = L.items[L.dc_w[s]];
+      it.kind = K_S2D;
+      it.taps = 4;
+      it.bytes = prep_frag_bytes(cs, 4 * cs, 4);
+    }
     if (s == 1 || s == 2) {
       const int k = s - 1;
       add_conv(L, cs, cs, 3, cs, &L.td_w[k][0], &L.td_b[k]);
@@ -341,7 +351,8 @@ Layout make_layout_enc(int c, int h, int w) {
     off = align_up(off + it.bytes);
   }
   L.zero_off = off;
-  L.zero_len = std::max(kMaxCin, lpad_of(h * w));
+  // (the space-to-depth down-convs read 4 x their width per voxel)
+  L.zero_len = std::max({kMaxCin, lpad_of(h * w), 4 * enc_width(c, 2)});
   off = align_up(off + (size_t)L.zero_len * 2);
   L.total = off;
   return L;
@@ -363,7 +374,7 @@ int enc_ring_down(int s, int k, int cv) { return E_DOWN_BASE + 4 * s + 2 * k + c
 
 // Channels and level (0: h x w, ..., 3: 8h x 8w) of encoder ring id.
 RingInfo enc_ring_info(int c, int id) {
-  if (id == E_CONV_IN) return {16, 3};
+  if (id == E_CONV_IN) return {kEncInC, 3};
   if (id < E_TD_BASE) {
     const int r = id - E_DOWN_BASE, s = r / 4, k = (r / 2) % 2, cv = r % 2;
     const int cin = (k == 0 && cv == 0) ? (s == 0 ? c : enc_width(c, s - 1)) : enc_width(c, s);
@@ -382,7 +393,7 @@ Work make_work_enc(int c, int h, int w, int P) {
   const long long res[4] = {r0, 4 * r0, 16 * r0, 64 * r0};
   const long long c4 = 4 * c, c2 = 2 * c;
   const long long F0 = P, F1 = 2LL * P, F2 = 4LL * P;
-  const long long act = std::max({F2 * res[3] * std::max<long long>(c, 16), F2 * res[2] * c2, F2 * res[1] * c2,
+  const long long act = std::max({F2 * res[3] * std::max<long long>(c, kEncInC), F2 * res[2] * c2, F2 * res[1] * c2,
                                   F1 * res[1] * c4, F1 * res[0] * c4, F0 * res[0] * c4});
   const long long L = r0, Lp = lpad_of((int)r0);
   size_t off = 0;
@@ -1125,6 +1136,8 @@ int prepare_plan(int c, int h, int w, const Layout& L, const void* const* weight
                                 static_cast<h16_t*>(dst), s);
     else if (it.kind == K_PHASE)
       e = launch_prep_phase_frag(src, weight_dtype, it.cout, static_cast<h16_t*>(dst), s);
+    else if (it.kind == K_S2D)
+      e = launch_prep_s2d_frag(src, weight_dtype, it.cout, static_cast<h16_t*>(dst), s);
     else
       e = launch_prep_vec(src, weight_dtype, it.n, it.scale, static_cast<float*>(dst), s);
   }
@@ -1331,14 +1344,20 @@ int decode_impl(wvd_plan* plan, const void* z, int z_dtype, int T, int t_begin, 
 
 // Spatial down-conv (R14): Conv2d 3x3, stride 2, zero pad 1, per frame:
 // x [F][2H][2W][C] -> y [F][H][W][Cout].
-Act down_conv(Ctx& cx, int s, const Act& x, h16_t* ybuf) {
+Act down_conv(Ctx& cx, int s, const Act& x, h16_t* ybuf, h16_t* sbuf) {
+  // 3x3 stride-2 conv (pad 1) in space-to-depth form: x's four phase images
+  // side by side in channels (into sbuf), then a 2x2 conv over them at offsets
+  // -1, 0 on the phase-tap kernel with one phase and a plain store.
   const Layout& L = cx.plan->L;
   Act y{ybuf, x.C, x.F, x.H / 2, x.W / 2};
+  Act z{sbuf, 4 * x.C, x.F, y.H, y.W};
+  cx.what = "space_to_depth";
+  cx.run(4, 0, [&] { return launch_space_to_depth(x.p, x.fstride(), x.C, x.F, x.H, x.W, z.p, cx.st); });
   ConvArgs a = args_init();
-  a.seg[0] = seg_basic(x.p, x.fstride(), x.C, x.C, cx.prep<h16_t>(L.dc_w[s]), x.C, 0, 1, KS_3x3,
+  a.seg[0] = seg_basic(z.p, z.fstride(), z.C, z.C, cx.prep<h16_t>(L.dc_w[s]), z.C, 0, 1, KS_PHASE,
                        cx.wbytes(L.dc_w[s]));
-  a.seg[0].stride = 2;
   a.nseg = 1;
+  a.nphase = 1;
   a.Cout = x.C;
   a.bias = cx.prep<float>(L.dc_b[s]);
   a.out = y.p;
@@ -1418,15 +1437,15 @@ int encode_impl(wvd_plan* plan, const void* video, int v_dtype, int T, int frame
     const int F2 = first ? 4 * F0 - 3 : 4 * F0;
     const int g2 = vb, g1 = first ? 0 : 2 * t0 - 1, g0 = t0;
     const int nh2 = std::min(2, g2), nh1 = std::min(2, g1), nh0 = std::min(2, g0);
-    // 2x2 patchify into 16 channels (12 + zero pad), then conv_in 12 -> c.
-    Act zt{Y, 16, F2, 8 * h, 8 * w};
+    // 2x2 patchify into kEncInC channels (12 + zero pad), then conv_in 12 -> c.
+    Act zt{Y, kEncInC, F2, 8 * h, 8 * w};
     cx.what = "patchify";
     cx.run(4, 0, [&] { return launch_patchify(video, v_dtype, Tv, vb, F2, 8 * h, 8 * w, Y, cx.st); });
     Act x{X, c, F2, 8 * h, 8 * w};
     {
       h16_t* ring = cx.ring(E_CONV_IN);
       ConvArgs a = args_init();
-      a.seg[0] = seg_basic(zt.p, zt.fstride(), 16, 16, cx.prep<h16_t>(L.conv_in_w), 16, 0, 3, KS_3x3,
+      a.seg[0] = seg_basic(zt.p, zt.fstride(), kEncInC, kEncInC, cx.prep<h16_t>(L.conv_in_w), kEncInC, 0, 3, KS_3x3,
                            cx.wbytes(L.conv_in_w));
       a.seg[0].ring = ring;
       a.seg[0].n_hist = nh2;
@@ -1444,16 +1463,16 @@ int encode_impl(wvd_plan* plan, const void* video, int v_dtype, int T, int frame
     // Stage 0 (8h x 8w, c), down to 4h x 4w.
     x = resblock(cx, L.down[0][0], x, Hb, nullptr, enc_ring_down(0, 0, 0), enc_ring_down(0, 0, 1), nh2);
     x = resblock(cx, L.down[0][1], x, Hb, nullptr, enc_ring_down(0, 1, 0), enc_ring_down(0, 1, 1), nh2);
-    x = down_conv(cx, 0, x, Y);
+    x = down_conv(cx, 0, x, Y, Hb);
     // Stage 1 (4h x 4w, c -> 2c), down to 2h x 2w, frames 4T-3 -> 2T-1.
     x = resblock(cx, L.down[1][0], x, Hb, X, enc_ring_down(1, 0, 0), enc_ring_down(1, 0, 1), nh2);
     x = resblock(cx, L.down[1][1], x, Hb, nullptr, enc_ring_down(1, 1, 0), enc_ring_down(1, 1, 1), nh2);
-    x = down_conv(cx, 1, x, Y);
+    x = down_conv(cx, 1, x, Y, Hb);
     x = time_down(cx, 0, x, first, X, first ? 0 : std::min(2, 2 * t0 - 2));
     // Stage 2 (2h x 2w, 2c -> 4c), down to h x w, frames 2T-1 -> T.
     x = resblock(cx, L.down[2][0], x, Hb, Y, enc_ring_down(2, 0, 0), enc_ring_down(2, 0, 1), nh1);
     x = resblock(cx, L.down[2][1], x, Hb, nullptr, enc_ring_down(2, 1, 0), enc_ring_down(2, 1, 1), nh1);
-    x = down_conv(cx, 2, x, X);
+    x = down_conv(cx, 2, x, X, Hb);
     x = time_down(cx, 1, x, first, Y, first ? 0 : std::min(2, t0 - 1));
     // Stage 3 (h x w, 4c), then the mid block.
     x = resblock(cx, L.down[3][0], x, Hb, nullptr, enc_ring_down(3, 0, 0), enc_ring_down(3, 0, 1), nh0);

@@ -337,9 +337,12 @@ __global__ __launch_bounds__(256) void patchify_kernel(const void* __restrict__ 
       }
 #pragma unroll
     for (int k = 12; k < 16; ++k) c[k] = 0.0f;
-    uint4* dst = reinterpret_cast<uint4*>(out + e * 16);
+    static_assert(kEncInC == 32, "12 patch channels and 20 zeros");
+    uint4* dst = reinterpret_cast<uint4*>(out + e * kEncInC);
     dst[0] = pack8h(c);
     dst[1] = pack8h(c + 8);
+    dst[2] = make_uint4(0, 0, 0, 0);
+    dst[3] = make_uint4(0, 0, 0, 0);
   }
 }
 
@@ -458,6 +461,59 @@ __global__ void prep_phase_frag_kernel(const void* __restrict__ w, int dtype, in
         for (int kx = kx0; kx <= kx1; ++kx) s += load_in(w, wp + ky * 3 + kx, dtype);
     }
     out[e] = (h16_t)f2h(s);
+  }
+}
+
+// Weights of a 3x3 stride-2 conv (pad 1) for its space-to-depth form: the
+// input's four phase images (py, px) = (row, column parity) side by side in
+// channels, block b = 2 py + px holding input channels [b C, (b + 1) C), and
+// a 2x2 conv over them at offsets -1, 0.  Along each axis, offset -1 reaches
+// only the odd phase (kernel tap 0); offset 0 reaches the even phase (tap 1)
+// and the odd one (tap 2).  Seven of the sixteen (tap, block) pairs are zero.
+// Fragment order with tap = 2 a + b (a, b: offset + 1 in rows and columns).
+__global__ void prep_s2d_frag_kernel(const void* __restrict__ w, int dtype, int C, h16_t* __restrict__ out) {
+  const int NB = (C + 127) / 128 * 4, U = 4 * C / 16;
+  const long long n = (long long)NB * U * 4 * 512;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+       e += (long long)gridDim.x * blockDim.x) {
+    const int j = (int)(e & 7);
+    const int l = (int)((e >> 3) & 63);
+    const long long blk = e >> 9;
+    const int t4 = (int)(blk % 4);
+    const int u = (int)((blk / 4) % U);
+    const int nb = (int)(blk / (4LL * U));
+    const int o = nb * 32 + (l & 31);
+    const int i4 = u * 16 + (l >> 5) * 8 + j;  // channel of the space-to-depth input
+    const int b = i4 / C, c = i4 % C;
+    const int py = b >> 1, px = b & 1, ta = t4 >> 1, tb = t4 & 1;
+    const int ky = ta == 0 ? (py == 1 ? 0 : -1) : (py == 0 ? 1 : 2);
+    const int kx = tb == 0 ? (px == 1 ? 0 : -1) : (px == 0 ? 1 : 2);
+    float v = 0.0f;
+    if (o < C && ky >= 0 && kx >= 0) v = load_in(w, ((long long)o * C + c) * 9 + ky * 3 + kx, dtype);
+    out[e] = (h16_t)f2h(v);
+  }
+}
+
+// Space-to-depth: y[f][Y][X][(2 py + px) C + c] = x[f][2Y + py][2X + px][c]
+// (H and W even), 16 bytes per thread.
+__global__ __launch_bounds__(256) void space_to_depth_kernel(const h16_t* __restrict__ x, long long x_fstride,
+                                                             int C, int F, int H, int W, h16_t* __restrict__ y) {
+  const int C8 = C / 8, H2 = H / 2, W2 = W / 2;
+  const long long n = (long long)F * H2 * W2 * 4 * C8;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+       e += (long long)gridDim.x * blockDim.x) {
+    const int g = (int)(e % C8);
+    long long r = e / C8;
+    const int b = (int)(r % 4);
+    r /= 4;
+    const int X = (int)(r % W2);
+    r /= W2;
+    const int Y = (int)(r % H2);
+    const int f = (int)(r / H2);
+    const int py = b >> 1, px = b & 1;
+    const uint4 v =
+        *reinterpret_cast<const uint4*>(x + f * x_fstride + ((long long)(2 * Y + py) * W + 2 * X + px) * C + g * 8);
+    *reinterpret_cast<uint4*>(y + e * 8) = v;
   }
 }
 
@@ -1162,6 +1218,25 @@ hipError_t launch_prep_frag_part(const void* w, int dtype, int cout, int cin_src
   const long long n = (long long)prep_frag_bytes(cout, cin_pad, taps) / 2;
   hipLaunchKernelGGL(prep_frag_kernel, dim3(grid_for(n)), dim3(256), 0, s, w, dtype, cout, cin_src, cin_off, cin,
                      taps, cin_pad, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep_s2d_frag(const void* w, int dtype, int C, h16_t* out, hipStream_t s) {
+  if (g_dry_run) return hipSuccess;
+  if (C % 8) return hipErrorInvalidValue;
+  const long long n = (long long)prep_frag_bytes(C, 4 * C, 4) / 2;
+  hipLaunchKernelGGL(prep_s2d_frag_kernel, dim3(grid_for(n)), dim3(256), 0, s, w, dtype, C, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_space_to_depth(const h16_t* x, long long x_fstride, int C, int F, int H, int W, h16_t* y,
+                                 hipStream_t s) {
+  if (g_dry_run) return hipSuccess;
+  if (!x || !y || C % 8 || H % 2 || W % 2 || F < 1 || x_fstride < (long long)H * W * C) return hipErrorInvalidValue;
+  const long long n = (long long)F * (H / 2) * (W / 2) * 4 * (C / 8);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(space_to_depth_kernel, dim3(grid_for(n, 256, 65536)), dim3(256), 0, s, x, x_fstride, C, F, H, W,
+                     y);
   return hipGetLastError();
 }
 

@@ -1287,7 +1287,10 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
               } else {
 #pragma unroll
                 for (int k = 0; k < 8; ++k) v8[k] = v8[k] * a.scale + bv[k];
-                const long long op = (long long)(2 * y + (geo.ph >> 1)) * (2 * a.W) + (2 * x + (geo.ph & 1));
+                // phase (py, px) of the 2x output, or (one phase) the plain grid
+                const long long op = a.epi == EPI_PHASE
+                                         ? (long long)(2 * y + (geo.ph >> 1)) * (2 * a.W) + (2 * x + (geo.ph & 1))
+                                         : (long long)y * a.W + x;
                 o = static_cast<h16_t*>(a.out) + f * a.out_fstride + op * a.ldo;
               }
               *reinterpret_cast<uint4*>(o + ncol) = pack8h(v8);
@@ -1473,7 +1476,10 @@ Variant conv_variant(const ConvArgs& a) {
   const bool k333 = g.KT == 3 && g.KS == 3 && a.TF == kTF333 && a.TH == kTH333 && v.bk == 32 && a.nphase == 1 &&
                     g.wfrag && (a.Cout > 32 ? (g.prologue == PRO_NORM_SILU || g.prologue == PRO_RAW)
                                             : (g.prologue == PRO_RAW && a.nseg == 1));
-  const bool kph = g.KT == 1 && g.KS == 2 && a.nphase == 4 && a.TF == 1 && a.TH == 16 && a.Cout > 32 &&
+  // phase taps: the up-conv's four output phases, or one phase with a plain
+  // store (a stride-2 conv in space-to-depth form)
+  const bool kph = g.KT == 1 && g.KS == 2 && (a.nphase == 4 || (a.nphase == 1 && a.epi == EPI_H16)) &&
+                   a.TF == 1 && a.TH == 16 && a.Cout > 32 &&
                    v.bk == 32 && a.nseg == 1 && g.wfrag && g.prologue == PRO_RAW;
   const bool kt3 = g.KT == 3 && g.KS == 1 && a.nphase == 1 && a.TF == kTF333 && a.TH == kTH333 && v.bk == 32 &&
                    a.nseg == 1 && g.wfrag && g.prologue == PRO_RAW && a.Cout % 256 == 0 && a.epi == EPI_TIME;
@@ -2036,7 +2042,8 @@ bool conv_persistent(const ConvArgs& a) {
   if (v.bn == 32) return v.mode == 1 && a.epi == EPI_VIDEO && a.seg[0].prologue == PRO_RAW;
   if (v.mode == 3) return a.epi == EPI_TIME;
   if (v.mode == 4) return a.epi == EPI_WINO;
-  return a.epi == (v.mode == 2 ? EPI_PHASE : EPI_H16) || (v.mode == 1 && a.epi == EPI_VIDEO);
+  if (v.mode == 2) return a.epi == EPI_PHASE || (a.nphase == 1 && a.epi == EPI_H16);
+  return a.epi == EPI_H16 || (v.mode == 1 && a.epi == EPI_VIDEO);
 }
 
 bool conv_is_333(const ConvArgs& a) { return conv_variant(a).mode == 1; }
@@ -2082,15 +2089,17 @@ const char* conv_check(const ConvArgs& a) {
     if (!g.x || !g.w) return "null operand";
     if (g.KT != 1 && g.KT != 3) return "KT must be 1 or 3";
     if (g.KS < KS_1x1 || g.KS > KS_3x1) return "unknown spatial tap code";
-    if (g.KS == KS_PHASE && a.nphase != 4) return "phase taps need 4 phases";
+    if (g.KS == KS_PHASE && !(a.nphase == 4 || (a.nphase == 1 && a.epi == EPI_H16)))
+      return "phase taps need 4 phases (or one, with a plain store)";
+    if (a.epi == EPI_PHASE && (g.KS != KS_PHASE || a.nphase != 4)) return "the phase store needs 4 phases";
     if (g.KS == KS_3x1 && a.nphase != kWinoN) return "Winograd taps need one phase per xi plane";
     if (a.nphase != 1 && g.KS != KS_PHASE && g.KS != KS_3x1) return "phases need phase or Winograd taps";
     if (g.KS == KS_3x1 && (a.epi != EPI_WINO || conv_variant(a).mode != 4))
       return "3x1 taps run only as the Winograd-domain GEMM";
     if ((a.epi == EPI_WINO) != (g.KS == KS_3x1)) return "EPI_WINO needs the 3x1 taps";
-    if ((a.epi == EPI_WINO || a.epi == EPI_PHASE) && a.nhv_max * (bk * 2 + 16) < kSwapEpiBytes)
+    if ((a.epi == EPI_WINO || g.KS == KS_PHASE) && a.nhv_max * (bk * 2 + 16) < kSwapEpiBytes)
       return "halo buffer below the epilogue's staging rows";
-    if (a.epi == EPI_PHASE && a.res) return "the up-conv epilogue adds no residual";
+    if (g.KS == KS_PHASE && a.res) return "the phase-tap epilogue adds no residual";
     if (a.epi == EPI_WINO && (a.bias || a.res || a.scale != 1.0f))
       return "the Winograd-domain GEMM stores plain products (no bias, residual or scale)";
     if (nhv > a.nhv_max) return "halo larger than nhv_max";

@@ -13,6 +13,7 @@ constexpr int kTileW = 16;
 constexpr int kTileM = 256;
 constexpr int kMaxHaloItemsPerTap = 4;  // 16-byte halo items per thread per tap
 constexpr int kMaxCin = 1024;           // largest norm input width kept in LDS
+constexpr int kEncInC = 32;             // encoder input channels: 12 patch channels + zero padding
 constexpr int kWinoTF = 2;              // frames per tile of the Winograd-domain GEMM
 constexpr int kWinoM = 6;               // Winograd F(m,3) along x: output columns per group
 constexpr int kWinoN = kWinoM + 2;      // transformed planes (xi) per group
@@ -188,14 +189,20 @@ hipError_t launch_prep_frag(const void* w, int dtype, int cout, int cin, int tap
 hipError_t launch_prep_frag_part(const void* w, int dtype, int cout, int cin_src, int cin_off, int cin, int taps,
                                  int cin_pad, h16_t* out, hipStream_t s);
 // Encoder input: video [3][T][2H][2W] (bf16 or fp32; NCTHW without the batch)
-// frames t0..t0+F-1 -> channels-last fp16 [F][H][W][16], channel 4k+2dy+dx =
-// pixel (2Y+dy, 2X+dx) of colour k (the inverse of the 2x2 pixel shuffle),
-// channels 12..15 zero.
+// frames t0..t0+F-1 -> channels-last fp16 [F][H][W][kEncInC], channel
+// 4k+2dy+dx = pixel (2Y+dy, 2X+dx) of colour k (the inverse of the 2x2 pixel
+// shuffle), channels 12..kEncInC-1 zero.
 hipError_t launch_patchify(const void* video, int dtype, int T, int t0, int F, int H, int W, h16_t* out,
                            hipStream_t s);
 // Up-conv phase weights in the same fragment order with taps = 16
 // (phase * 4 + 2x2 tap).
 hipError_t launch_prep_phase_frag(const void* w, int dtype, int C, h16_t* out, hipStream_t s);
+// Weights of a 3x3 stride-2 conv for its space-to-depth form (C -> C over 4C
+// input channels, 2x2 taps at offsets -1, 0; fragment order, tap = 2a + b).
+hipError_t launch_prep_s2d_frag(const void* w, int dtype, int C, h16_t* out, hipStream_t s);
+// x [F][H][W][C] -> y [F][H/2][W/2][4C], block 2 py + px = x[2Y+py][2X+px].
+hipError_t launch_space_to_depth(const h16_t* x, long long x_fstride, int C, int F, int H, int W, h16_t* y,
+                                 hipStream_t s);
 // Winograd F(kWinoM,3) weights of a 3x3x3 conv along x: for each (dt, dy)
 // the three x taps g become V = G g (fp32, rounded once to fp16), in
 // fragment order with taps = kWinoN * 9 (xi * 9 + dt * 3 + dy).
