@@ -1506,12 +1506,6 @@ Variant conv_variant(const ConvArgs& a) {
 }
 
 // ---------------------------------------------------------------------------
-// Batched NT GEMM tiles (gemm_nt_kernel below): 256 x 256 tiles in K chunks of
-// kG1K channels, one chunk of loads in flight.
-constexpr int kG1K = 128;               // K channels per chunk
-constexpr int kG1ARow = kG1K * 2 + 16;  // staged A row bytes (+16 pad: conflict-free fragment reads)
-constexpr int kG1Lds = 256 * kG1ARow + 256 * kG1K * 2;
-
 // 1x1 convolution as a plain GEMM, out[m][n] = sum_k x[m][k] w[n][k] + bias[n]
 // (the shortcut of a width-changing block).  It streams its activations from
 // HBM once, so it is organised for that: one persistent workgroup per CU walks
@@ -1735,11 +1729,9 @@ __global__ __launch_bounds__(256) void gemm1x1_kernel(const h16_t* __restrict__ 
 
 template <int EPI>
 __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs ga) {
-  constexpr int MI = 4, NJ = 4, CS = kG1K / 16, PPR = kG1K * 2 / 16, IPT = 16;
-  static_assert(PPR == 16 && IPT == 16 && CS == 8, "16 A pieces (16 rows apart) and 16 B blocks per thread");
+  constexpr int MI = 4, NJ = 4, CS = kS1K / 16, PPR = kS1K * 2 / 16, IPT = 8;
+  static_assert(PPR == 8 && CS == 4, "8 A pieces (32 rows apart) and 8 B blocks per thread");
   extern __shared__ __align__(16) unsigned char g1s[];
-  unsigned char* As = g1s;
-  unsigned char* Bs = g1s + 256 * kG1ARow;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -1751,14 +1743,13 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs ga) {
   const int tpf = (int)(nMt * nN);  // tiles per frame
   const TileSeq seq = tile_seq(tpf * ga.nF);
   if (seq.at(0) < 0) return;
-  const int nch = K / kG1K;
+  const int nch = K / kS1K;  // even (the check requires K % 128 == 0)
   const int U = K / 16;
 
-  // this thread's pieces: A row (tid / PPR) + 16 r, part tid % PPR; B block
-  // (tid + 256 r) / 64 = (32-column block nbl, k16 step s), lane (tid % 64)
-  uint4 sa[IPT], sb[IPT];
-  // Only the lane-dependent parts of the addresses live in VGPRs; the piece
-  // index r and the chunk go into the scalar offset.
+  // The shortcut GEMM's pipeline (gemm1x1_kernel) with frames as a batch
+  // dimension: this thread's pieces are A row (tid / PPR) + 32 r, part
+  // tid % PPR, and B block (n32 block r of the tile, k16 step `wave`).
+  uint4 sa[2][IPT], sb[2][IPT];
   const int avoff = ((tid / PPR) * lda + (tid % PPR) * 8) * 2;
   const int bvoff = lane * 16;
   // The last row tile is shifted back to end at row M (M >= 256), so every
@@ -1768,7 +1759,7 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs ga) {
     const long long m0 = (long long)((tile % tpf) / nN) * 256;
     return m0 + 256 <= M ? m0 : M - 256;
   };
-  auto issue = [&](int tile, int ch) {
+  auto issue = [&](uint4 (&ra)[IPT], uint4 (&rb)[IPT], int tile, int ch) {
     const int f = tile / tpf;
     const long long m0 = tile_m0(tile);
     const int bn = (tile % tpf) % nN;
@@ -1778,33 +1769,30 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs ga) {
         const_cast<h16_t*>(ga.w + f * ga.w_fs), 0, (int)ga.w_bytes, 0x00020000);
 #pragma unroll
     for (int r = 0; r < IPT; ++r)
-      sa[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            arsrc, avoff, (16 * r * lda + ch * kG1K) * 2, 0));
+      ra[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            arsrc, avoff, (32 * r * lda + ch * kS1K) * 2, 0));
 #pragma unroll
     for (int r = 0; r < IPT; ++r) {
-      // block (wave + 4r): 32-column block r / 2, k16 step wave + 4 (r % 2)
-      const int nb = bn * 8 + r / 2, u = ch * CS + wave + 4 * (r % 2);
-      sb[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(brsrc, bvoff, (nb * U + u) * 1024, 0));
+      const int nb = bn * 8 + r, u = ch * CS + wave;
+      rb[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(brsrc, bvoff, (nb * U + u) * 1024, 0));
     }
   };
-  const int aloff = (tid / PPR) * kG1ARow + (tid % PPR) * 16;
-  const int bloff = wave * 1024 + lane * 16;
-  auto commit = [&]() {
+  const int aloff = (tid / PPR) * kS1ARow + (tid % PPR) * 16;
+  const int bloff = 256 * kS1ARow + wave * 1024 + lane * 16;
+  auto commit = [&](const uint4 (&ra)[IPT], const uint4 (&rb)[IPT], int buf) {
+    unsigned char* base = g1s + buf * kS1Buf;
 #pragma unroll
     for (int r = 0; r < IPT; ++r) {
-      *reinterpret_cast<uint4*>(As + aloff + 16 * r * kG1ARow) = sa[r];
-      *reinterpret_cast<uint4*>(Bs + bloff + r * 4096) = sb[r];
+      *reinterpret_cast<uint4*>(base + aloff + 32 * r * kS1ARow) = ra[r];
+      *reinterpret_cast<uint4*>(base + bloff + r * CS * 1024) = rb[r];
     }
   };
   int abase[MI], bbase[NJ];
 #pragma unroll
-  for (int i = 0; i < MI; ++i) abase[i] = (wm * 128 + 32 * i + lrow) * kG1ARow + kpart * 16;
+  for (int i = 0; i < MI; ++i) abase[i] = (wm * 128 + 32 * i + lrow) * kS1ARow + kpart * 16;
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) bbase[j] = (wn * 4 + j) * CS * 1024 + lane * 16;
+  for (int j = 0; j < NJ; ++j) bbase[j] = 256 * kS1ARow + (wn * 4 + j) * CS * 1024 + lane * 16;
 
-  issue(seq.at(0), 0);
-  commit();
-  __syncthreads();
   f32x16_t acc[MI][NJ];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
@@ -1813,160 +1801,185 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs ga) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
+  // chunk g + d (d <= 2 < nch) after chunk ch of tile cur (next tile nxt;
+  // tile < 0: past the end)
+  auto ahead = [&](int cur, int nxt, int ch, int d, int& tile, int& c) {
+    tile = ch + d < nch ? cur : nxt;
+    c = ch + d < nch ? ch + d : ch + d - nch;
+  };
+  {
+    int t1, c1;
+    ahead(seq.at(0), seq.at(1), 0, 1, t1, c1);
+    issue(sa[0], sb[0], seq.at(0), 0);
+    issue(sa[1], sb[1], t1 >= 0 ? t1 : seq.at(0), t1 >= 0 ? c1 : 0);
+    commit(sa[0], sb[0], 0);
+  }
+  __syncthreads();
+
+  auto chunk = [&](auto parity, int cur, int nxt, int ch) {
+    constexpr int P = decltype(parity)::value;
+    int t1, c1, t2, c2;
+    ahead(cur, nxt, ch, 1, t1, c1);
+    ahead(cur, nxt, ch, 2, t2, c2);
+    // unconditional (past the end it reloads this chunk, unused)
+    issue(sa[P], sb[P], t2 >= 0 ? t2 : cur, t2 >= 0 ? c2 : ch);
+    __builtin_amdgcn_sched_barrier(0);
+    const unsigned char* buf = g1s + P * kS1Buf;
+    f16x8_t ap[2][MI], bp[2][NJ];
+#pragma unroll
+    for (int i = 0; i < MI; ++i) ap[0][i] = *reinterpret_cast<const f16x8_t*>(buf + abase[i]);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) bp[0][j] = *reinterpret_cast<const f16x8_t*>(buf + bbase[j]);
+#pragma unroll
+    for (int s = 0; s < CS; ++s) {
+      if (s + 1 < CS) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+          ap[(s + 1) & 1][i] = *reinterpret_cast<const f16x8_t*>(buf + abase[i] + (s + 1) * 32);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          bp[(s + 1) & 1][j] = *reinterpret_cast<const f16x8_t*>(buf + bbase[j] + (s + 1) * 1024);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bp[s & 1][j], ap[s & 1][i], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // chunk g + 1 (issued two chunks ago) into the other buffer; the barrier
+    // makes it visible and ends every wave's reads of this buffer
+    if (t1 >= 0) commit(sa[P ^ 1], sb[P ^ 1], P ^ 1);
+    __syncthreads();
+  };
+
   for (int k = 0;; ++k) {
     const int cur = seq.at(k);
     if (cur < 0) break;
     const int nxt = seq.at(k + 1);
-    for (int ch = 0; ch < nch; ++ch) {
-      const bool last = ch + 1 == nch;
-      const bool more = !last || nxt >= 0;  // uniform
-      if (more) issue(last ? nxt : cur, last ? 0 : ch + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      f16x8_t ap[2][MI], bp[2][NJ];
+    for (int ch = 0; ch < nch; ch += 2) {
+      chunk(std::integral_constant<int, 0>{}, cur, nxt, ch);
+      chunk(std::integral_constant<int, 1>{}, cur, nxt, ch + 1);
+    }
+    {
+    // lane (kpart, lrow) of block (i, j) holds row 32i + lrow of the
+    // wave's rows and columns 32j + 8g + 4*kpart + r (accumulator 4g + r)
+    const int f = cur / tpf;
+    const long long m0 = tile_m0(cur);
+    // rows below mown belong to the previous row tile (the last tile is
+    // shifted back): only their owner stores them, so an in-place
+    // residual is read and written once per row
+    const long long mown = (long long)((cur % tpf) / nN) * 256;
+    const int ct = (cur % tpf) % nN;  // column tile
+    const int n0 = ct * 256 + wn * 128;
+    // Every epilogue goes through buffer 1's A rows (the tile's last chunk): per 32 rows and 64
+    // columns the accumulator runs go straight into fp32 LDS rows; then
+    // each lane takes eight columns of one row (eight lanes per row):
+    //   G_H16: bias (and residual), fp16, a 16-byte store;
+    //   G_STATS: the row's max and sum of e^(v - max) over those 64
+    //     columns (a reduction over the eight lanes), one float2;
+    //   G_PROB: e^(v - M) / S with the row's (M, 1/S), fp16, a store.
+    constexpr int SROW = 64 * 4 + 16, LPR = 8, RPI = 8;
+    static_assert(4 * 32 * SROW <= 256 * kS1ARow, "staging fits in a buffer's A rows");
+    unsigned char* st = g1s + kS1Buf + wave * 32 * SROW;
+    const float scale = ga.scale;
+    // per-tile row bases (uniform): row m of the tile's frame is row
+    // m - m0 + (tile base), so the loops below need 32-bit offsets only
+    h16_t* const outb = EPI == G_STATS ? nullptr : ga.out + f * ga.o_fs + m0 * ga.ldo;
+    const h16_t* const resb = EPI == G_H16 && ga.res ? ga.res + f * ga.r_fs + m0 * ga.ldr : nullptr;
+    const float* const mib = EPI == G_PROB ? ga.mi + (f * M + m0) * 2 : nullptr;
+    float* const stb = EPI == G_STATS ? ga.stats + (f * M + m0) * (N / 64) * 2 : nullptr;
+    const int mskip = (int)(mown - m0);  // tile rows below this belong to the previous tile
 #pragma unroll
-      for (int i = 0; i < MI; ++i) ap[0][i] = *reinterpret_cast<const f16x8_t*>(As + abase[i]);
+    for (int i = 0; i < MI; ++i) {
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) bp[0][j] = *reinterpret_cast<const f16x8_t*>(Bs + bbase[j]);
+      for (int jh = 0; jh < NJ / 2; ++jh) {
 #pragma unroll
-      for (int s = 0; s < CS; ++s) {
-        if (s + 1 < CS) {
+        for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-          for (int i = 0; i < MI; ++i)
-            ap[(s + 1) & 1][i] = *reinterpret_cast<const f16x8_t*>(As + abase[i] + (s + 1) * 32);
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x16_t& c = acc[i][jh * 2 + jj];
+            f32x4_t v = {c[4 * g4], c[4 * g4 + 1], c[4 * g4 + 2], c[4 * g4 + 3]};
+            *reinterpret_cast<f32x4_t*>(st + lrow * SROW + (32 * jj + 8 * g4 + 4 * kpart) * 4) = v;
+          }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the block is in LDS
+        __builtin_amdgcn_wave_barrier();
+        const int ncol = n0 + jh * 64 + (lane % LPR) * 8;
+        float bv[8];
 #pragma unroll
-          for (int j = 0; j < NJ; ++j)
-            bp[(s + 1) & 1][j] = *reinterpret_cast<const f16x8_t*>(Bs + bbase[j] + (s + 1) * 1024);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        for (int q = 0; q < 8; ++q) bv[q] = 0.0f;
+        if (EPI == G_H16 && ga.bias) {
+          const f32x4_t b0 = *reinterpret_cast<const f32x4_t*>(ga.bias + ncol);
+          const f32x4_t b1 = *reinterpret_cast<const f32x4_t*>(ga.bias + ncol + 4);
 #pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-          for (int j = 0; j < NJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bp[s & 1][j], ap[s & 1][i], acc[i][j], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      __syncthreads();  // every wave is done reading this chunk
-      if (last) {
-        // lane (kpart, lrow) of block (i, j) holds row 32i + lrow of the
-        // wave's rows and columns 32j + 8g + 4*kpart + r (accumulator 4g + r)
-        const int f = cur / tpf;
-        const long long m0 = tile_m0(cur);
-        // rows below mown belong to the previous row tile (the last tile is
-        // shifted back): only their owner stores them, so an in-place
-        // residual is read and written once per row
-        const long long mown = (long long)((cur % tpf) / nN) * 256;
-        const int ct = (cur % tpf) % nN;  // column tile
-        const int n0 = ct * 256 + wn * 128;
-        // Every epilogue goes through the A region: per 32 rows and 64
-        // columns the accumulator runs go straight into fp32 LDS rows; then
-        // each lane takes eight columns of one row (eight lanes per row):
-        //   G_H16: bias (and residual), fp16, a 16-byte store;
-        //   G_STATS: the row's max and sum of e^(v - max) over those 64
-        //     columns (a reduction over the eight lanes), one float2;
-        //   G_PROB: e^(v - M) / S with the row's (M, 1/S), fp16, a store.
-        constexpr int SROW = 64 * 4 + 16, LPR = 8, RPI = 8;
-        static_assert(4 * 32 * SROW <= 256 * kG1ARow, "staging fits in the A region");
-        unsigned char* st = As + wave * 32 * SROW;
-        const float scale = ga.scale;
-        // per-tile row bases (uniform): row m of the tile's frame is row
-        // m - m0 + (tile base), so the loops below need 32-bit offsets only
-        h16_t* const outb = EPI == G_STATS ? nullptr : ga.out + f * ga.o_fs + m0 * ga.ldo;
-        const h16_t* const resb = EPI == G_H16 && ga.res ? ga.res + f * ga.r_fs + m0 * ga.ldr : nullptr;
-        const float* const mib = EPI == G_PROB ? ga.mi + (f * M + m0) * 2 : nullptr;
-        float* const stb = EPI == G_STATS ? ga.stats + (f * M + m0) * (N / 64) * 2 : nullptr;
-        const int mskip = (int)(mown - m0);  // tile rows below this belong to the previous tile
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-#pragma unroll
-          for (int jh = 0; jh < NJ / 2; ++jh) {
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-              for (int g4 = 0; g4 < 4; ++g4) {
-                const f32x16_t& c = acc[i][jh * 2 + jj];
-                f32x4_t v = {c[4 * g4], c[4 * g4 + 1], c[4 * g4 + 2], c[4 * g4 + 3]};
-                *reinterpret_cast<f32x4_t*>(st + lrow * SROW + (32 * jj + 8 * g4 + 4 * kpart) * 4) = v;
-              }
-            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the block is in LDS
-            __builtin_amdgcn_wave_barrier();
-            const int ncol = n0 + jh * 64 + (lane % LPR) * 8;
-            float bv[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) bv[q] = 0.0f;
-            if (EPI == G_H16 && ga.bias) {
-              const f32x4_t b0 = *reinterpret_cast<const f32x4_t*>(ga.bias + ncol);
-              const f32x4_t b1 = *reinterpret_cast<const f32x4_t*>(ga.bias + ncol + 4);
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                bv[q] = b0[q];
-                bv[4 + q] = b1[q];
-              }
-            }
-#pragma unroll 1
-            for (int rr = 0; rr < 32 / RPI; ++rr) {
-              const int r = rr * RPI + lane / LPR;
-              const float* row = reinterpret_cast<const float*>(st + r * SROW) + (lane % LPR) * 8;
-              const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(row);
-              const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(row + 4);
-              const int mt = wm * 128 + 32 * i + r;  // row within the tile
-              float v8[8] = {lo[0] * scale + bv[0], lo[1] * scale + bv[1], lo[2] * scale + bv[2],
-                             lo[3] * scale + bv[3], hi[0] * scale + bv[4], hi[1] * scale + bv[5],
-                             hi[2] * scale + bv[6], hi[3] * scale + bv[7]};
-              if constexpr (EPI == G_STATS) {
-                float mx = -INFINITY;
-#pragma unroll
-                for (int q = 0; q < 8; ++q)
-                  if (ncol + q < ga.n_valid) mx = fmaxf(mx, v8[q]);
-                mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
-                mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
-                mx = fmaxf(mx, __shfl_xor(mx, 4, 64));
-                float sm = 0.0f;
-#pragma unroll
-                for (int q = 0; q < 8; ++q)
-                  if (ncol + q < ga.n_valid) sm += exp_hw(v8[q] - mx);
-                sm += __shfl_xor(sm, 1, 64);
-                sm += __shfl_xor(sm, 2, 64);
-                sm += __shfl_xor(sm, 4, 64);
-                if (lane % LPR == 0 && mt >= mskip)
-                  *reinterpret_cast<float2*>(stb + (mt * (N / 64) + ct * 4 + wn * 2 + jh) * 2) = make_float2(mx, sm);
-              } else {
-                if (mt < mskip) continue;
-                if constexpr (EPI == G_PROB) {
-                  const float2 ms = *reinterpret_cast<const float2*>(mib + mt * 2);
-#pragma unroll
-                  for (int q = 0; q < 8; ++q) v8[q] = ncol + q < ga.n_valid ? exp_hw(v8[q] - ms.x) * ms.y : 0.0f;
-                } else if (resb) {
-                  float rv[8];
-                  unpack8h(*reinterpret_cast<const uint4*>(resb + mt * ga.ldr + ncol), rv);
-#pragma unroll
-                  for (int q = 0; q < 8; ++q) v8[q] += rv[q];
-                }
-                *reinterpret_cast<uint4*>(outb + mt * ga.ldo + ncol) = pack8h(v8);
-              }
-            }
-            __builtin_amdgcn_s_waitcnt(0xc07f);  // this round's reads before the next round's writes
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_sched_barrier(0);
+          for (int q = 0; q < 4; ++q) {
+            bv[q] = b0[q];
+            bv[4 + q] = b1[q];
           }
         }
+#pragma unroll 1
+        for (int rr = 0; rr < 32 / RPI; ++rr) {
+          const int r = rr * RPI + lane / LPR;
+          const float* row = reinterpret_cast<const float*>(st + r * SROW) + (lane % LPR) * 8;
+          const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(row);
+          const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(row + 4);
+          const int mt = wm * 128 + 32 * i + r;  // row within the tile
+          float v8[8] = {lo[0] * scale + bv[0], lo[1] * scale + bv[1], lo[2] * scale + bv[2],
+                         lo[3] * scale + bv[3], hi[0] * scale + bv[4], hi[1] * scale + bv[5],
+                         hi[2] * scale + bv[6], hi[3] * scale + bv[7]};
+          if constexpr (EPI == G_STATS) {
+            float mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < MI; ++i)
+            for (int q = 0; q < 8; ++q)
+              if (ncol + q < ga.n_valid) mx = fmaxf(mx, v8[q]);
+            mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 4, 64));
+            float sm = 0.0f;
 #pragma unroll
-          for (int j = 0; j < NJ; ++j)
+            for (int q = 0; q < 8; ++q)
+              if (ncol + q < ga.n_valid) sm += exp_hw(v8[q] - mx);
+            sm += __shfl_xor(sm, 1, 64);
+            sm += __shfl_xor(sm, 2, 64);
+            sm += __shfl_xor(sm, 4, 64);
+            if (lane % LPR == 0 && mt >= mskip)
+              *reinterpret_cast<float2*>(stb + (mt * (N / 64) + ct * 4 + wn * 2 + jh) * 2) = make_float2(mx, sm);
+          } else {
+            if (mt < mskip) continue;
+            if constexpr (EPI == G_PROB) {
+              const float2 ms = *reinterpret_cast<const float2*>(mib + mt * 2);
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-        __syncthreads();  // the staging rows are free again
+              for (int q = 0; q < 8; ++q) v8[q] = ncol + q < ga.n_valid ? exp_hw(v8[q] - ms.x) * ms.y : 0.0f;
+            } else if (resb) {
+              float rv[8];
+              unpack8h(*reinterpret_cast<const uint4*>(resb + mt * ga.ldr + ncol), rv);
+#pragma unroll
+              for (int q = 0; q < 8; ++q) v8[q] += rv[q];
+            }
+            *reinterpret_cast<uint4*>(outb + mt * ga.ldo + ncol) = pack8h(v8);
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // this round's reads before the next round's writes
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (more) commit();
-      __syncthreads();
     }
+    }
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    __syncthreads();  // the staging rows are read before the next tile's chunk 1 lands here
   }
 }
 
 }  // namespace
 
 const char* gemm_nt_check(const GemmArgs& g, int epi) {
-  if (!g.x || !g.w || g.M < 256 || g.N % 256 || g.K % kG1K || g.K > 4096 || g.lda % 8 || g.lda < g.K)
+  if (!g.x || !g.w || g.M < 256 || g.N % 256 || g.K % (2 * kS1K) || g.K > 4096 || g.lda % 8 || g.lda < g.K)
     return "A / B shapes";
   if (g.w_bytes <= 0 || g.w_bytes > 0x7fffffffLL || (long long)256 * g.lda * 2 > 0x7fffffffLL) return "B bytes";
   if (g.nF < 1 || (g.nF > 1 && (g.a_fs < 0 || g.w_fs < 0 || g.o_fs < 0 || g.r_fs < 0))) return "frames";
@@ -1989,7 +2002,7 @@ hipError_t launch_gemm_nt(const GemmArgs& g, int epi, hipStream_t stream) {
                                       : reinterpret_cast<const void*>(gemm_nt_kernel<G_H16>);
   static bool attr[3] = {false, false, false};
   if (!attr[epi]) {
-    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, kG1Lds);
+    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, kS1Lds);
     if (e != hipSuccess) return e;
     attr[epi] = true;
   }
@@ -2000,11 +2013,11 @@ hipError_t launch_gemm_nt(const GemmArgs& g, int epi, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const long long grid = tiles < ncu ? tiles : ncu;
   if (epi == G_STATS)
-    hipLaunchKernelGGL(gemm_nt_kernel<G_STATS>, dim3((unsigned)grid), dim3(256), kG1Lds, stream, g);
+    hipLaunchKernelGGL(gemm_nt_kernel<G_STATS>, dim3((unsigned)grid), dim3(256), kS1Lds, stream, g);
   else if (epi == G_PROB)
-    hipLaunchKernelGGL(gemm_nt_kernel<G_PROB>, dim3((unsigned)grid), dim3(256), kG1Lds, stream, g);
+    hipLaunchKernelGGL(gemm_nt_kernel<G_PROB>, dim3((unsigned)grid), dim3(256), kS1Lds, stream, g);
   else
-    hipLaunchKernelGGL(gemm_nt_kernel<G_H16>, dim3((unsigned)grid), dim3(256), kG1Lds, stream, g);
+    hipLaunchKernelGGL(gemm_nt_kernel<G_H16>, dim3((unsigned)grid), dim3(256), kS1Lds, stream, g);
   return hipGetLastError();
 }
 
