@@ -1224,9 +1224,73 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
     const int nn = seq.at(k + 2);
     if (nn >= 0) build_tables(k & 1, nn);
 
-    if constexpr (SWAPPED) {
-      // ---- epilogue of the swapped-operand loops (Winograd-domain GEMM,
-      // up-conv phases): lane (kpart, lrow) of block (i, j) holds position
+    if constexpr (WINO && NW == 4) {
+      // ---- epilogue of the Winograd-domain GEMM (plain fp16 products): lane
+      // (kpart, lrow) of block (i, j) holds position 32i + lrow of the wave's
+      // rows and channels 32j + 8g + 4*kpart + r (accumulator 4g + r).  Per
+      // 32-row block the wave packs its accumulators to fp16 and writes them
+      // as 8-byte runs into its own LDS rows (128 channels + 16 bytes of pad;
+      // rows 16..31 swap the two halves of every 16-byte piece, so the 32
+      // lanes of a write pass cover all 64 banks once), waits once, reads
+      // 8 rows x 16 pieces (four rows per read, one 16-byte piece per lane),
+      // waits once and stores the 16-byte pieces along the output rows.  The
+      // stores go through a buffer resource at the tile's first output
+      // element; positions outside the grid get an offset past its range, so
+      // the hardware drops them and no lane branches.
+      constexpr int EROWB = 128 * 2 + 16;
+      static_assert(WN == 128 && NJ == 4 && NW * 32 * EROWB <= kSwapEpiBytes, "staged rows fit in one halo buffer");
+      unsigned char* st = smem + ((gc - 1) & 1) * halo_bytes + wave * 32 * EROWB;
+      const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+          static_cast<h16_t*>(a.out) + geo.ph * a.out_pstride + geo.f0 * a.out_fstride +
+              ((long long)geo.y0 * a.W + geo.x0) * a.ldo + geo.n0 + wave_n * WN,
+          0, 0x7fffffff, 0x00020000);
+      const int lf = a.F - geo.f0, ly = a.H - geo.y0, lx = a.W - geo.x0;
+      const unsigned ofs = (unsigned)a.out_fstride, ors_row = (unsigned)a.W * (unsigned)a.ldo;
+      const int rsel = lrow >> 4;  // this lane's write rows: halves swapped
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int gp = 0; gp < 2; ++gp) {
+            const f32x16_t& c = acc[i][j];
+            float v8[8];
+            // read each accumulator where it is used (the compiler would
+            // otherwise copy all of them out of the AGPRs at the loop exit)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v8[e]) : "a"(c[8 * gp + e]));
+            const uint4 pk = pack8h(v8);  // channels 32j + 16gp + 4kpart + (0..3, 8..11)
+            unsigned char* rowp = st + lrow * EROWB + (4 * j + 2 * gp) * 16;
+            *reinterpret_cast<uint2*>(rowp + 8 * (kpart ^ rsel)) = make_uint2(pk.x, pk.y);
+            *reinterpret_cast<uint2*>(rowp + 16 + 8 * (kpart ^ rsel)) = make_uint2(pk.z, pk.w);
+          }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the block is in LDS
+        __builtin_amdgcn_wave_barrier();
+        uint4 pv[8];
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+          const uint4 q = *reinterpret_cast<const uint4*>(st + (rr * 4 + lane / 16) * EROWB + (lane % 16) * 16);
+          pv[rr] = rr < 4 ? q : make_uint4(q.z, q.w, q.x, q.y);  // rows 16..31: halves back in order
+        }
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+          const int m = wave_m * WM + 32 * i + rr * 4 + lane / 16;
+          const int tx = m & (TW - 1), t2 = m / TW;
+          const int dy = t2 % TH, df = t2 / TH;
+          const unsigned off = (unsigned)df * ofs + (unsigned)dy * ors_row + (unsigned)tx * (unsigned)a.ldo +
+                               (unsigned)(lane % 16) * 8u;
+          const bool ok = df < lf && dy < ly && tx < lx;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, pv[rr]), ors, ok ? off * 2u : 0x80000000u,
+                                                 0, 0);
+        }
+        // the next block's writes reuse these rows: this block's reads first
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else if constexpr (SWAPPED) {
+      // ---- epilogue of the swapped-operand loops (Winograd-domain GEMM on
+      // 8 waves, up-conv phases): lane (kpart, lrow) of block (i, j) holds position
       // 32i + lrow of the wave's rows and channels 32j + 8g + 4*kpart + r
       // (accumulator 4g + r).  Per 32 positions and SCH channels the wave
       // writes the runs of four straight from the accumulators into its own
@@ -2115,6 +2179,9 @@ const char* conv_check(const ConvArgs& a) {
     if (g.KS == KS_PHASE && a.res) return "the phase-tap epilogue adds no residual";
     if (a.epi == EPI_WINO && (a.bias || a.res || a.scale != 1.0f))
       return "the Winograd-domain GEMM stores plain products (no bias, residual or scale)";
+    if (a.epi == EPI_WINO && (a.out_fstride < (long long)a.H * a.W * a.ldo ||
+                              2LL * a.TF * a.out_fstride + 16 > 0x7fffffffLL))
+      return "a Winograd product tile must span less than 2^31 bytes (32-bit store offsets)";
     if (nhv > a.nhv_max) return "halo larger than nhv_max";
     if ((g.KT == 3 && g.KS == 3 && a.TF == kTF333 && a.TH == kTH333 &&
          ((kNHV333 * (bk / 8) + 511) / 512) * 512 / (bk / 8) > a.nhv_max))
