@@ -660,9 +660,12 @@ int tf_for(int KT, int F) {
 // power: deeper tiles in t and y load fewer halo rows per output.  The choice
 // minimises rounds of tiles over the CUs times (1 + 0.1 x halo rows per
 // output), which also keeps the 20- and 39-column-group levels from mostly
-// empty wide tiles.
+// empty wide tiles.  A tile of 128 output channels takes half the time of
+// one of 256 at about 1.15 times the cost per multiply-add (each A fragment
+// feeds two MFMAs instead of four); it wins where 256-channel tiles would
+// leave much of a last round idle (the 44x78 level: 384 tiles, 1.5 rounds).
 struct WinoShape {
-  int TF, TW;
+  int TF, TW, bn;
 };
 
 WinoShape wino_tile_shape(int F, int H, int WQ, int Cout) {
@@ -675,15 +678,18 @@ WinoShape wino_tile_shape(int F, int H, int WQ, int Cout) {
     else
       slots = 256;
   }
-  static const WinoShape cand[] = {{2, 16}, {2, 8}, {4, 8}, {4, 4}, {8, 4}};
+  static const WinoShape cand[] = {{2, 16, 256}, {2, 8, 256}, {4, 8, 256}, {4, 4, 256}, {8, 4, 256},
+                                   {2, 16, 128}, {2, 8, 128}, {4, 8, 128}, {4, 4, 128}, {8, 4, 128}};
   WinoShape best = cand[0];
   double best_cost = 1e300;
   for (const WinoShape& c : cand) {
+    if (Cout % c.bn) continue;
     const int th = kTileM / c.TW / c.TF;
     const long long tiles = (long long)((WQ + c.TW - 1) / c.TW) * ((H + th - 1) / th) * ((F + c.TF - 1) / c.TF) *
-                            kWinoN * ((Cout + 255) / 256);
+                            kWinoN * (Cout / c.bn);
     const double halo = (double)(c.TF + 2) * (th + 2) / (c.TF * th);
-    const double cost = (double)((tiles + slots - 1) / slots) * (1.0 + 0.1 * halo);
+    const double per_tile = c.bn == 256 ? 1.0 : 0.5 * 1.15;
+    const double cost = (double)((tiles + slots - 1) / slots) * per_tile * (1.0 + 0.1 * halo);
     if (cost < best_cost) {
       best_cost = cost;
       best = c;
@@ -724,6 +730,7 @@ void wino_gemm(Ctx& cx, const Act& x, int nh, int w_item, int Cout) {
   a.epi = EPI_WINO;
   const WinoShape ts = wino_tile_shape(x.F, x.H, W2, Cout);
   set_grid(a, x.F, x.H, W2, ts.TF, ts.TW);
+  a.bn = ts.bn;
   conv(cx, a, 0);
 }
 

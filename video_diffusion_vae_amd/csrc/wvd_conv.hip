@@ -1224,7 +1224,7 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
     const int nn = seq.at(k + 2);
     if (nn >= 0) build_tables(k & 1, nn);
 
-    if constexpr (WINO && NW == 4) {
+    if constexpr (WINO && NW == 4 && BN == 256) {
       // ---- epilogue of the Winograd-domain GEMM (plain fp16 products): lane
       // (kpart, lrow) of block (i, j) holds position 32i + lrow of the wave's
       // rows and channels 32j + 8g + 4*kpart + r (accumulator 4g + r).  Per
@@ -1290,7 +1290,7 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
       }
     } else if constexpr (SWAPPED) {
       // ---- epilogue of the swapped-operand loops (Winograd-domain GEMM on
-      // 8 waves, up-conv phases): lane (kpart, lrow) of block (i, j) holds position
+      // 128-channel tiles, up-conv phases): lane (kpart, lrow) of block (i, j) holds position
       // 32i + lrow of the wave's rows and channels 32j + 8g + 4*kpart + r
       // (accumulator 4g + r).  Per 32 positions and SCH channels the wave
       // writes the runs of four straight from the accumulators into its own
@@ -2179,6 +2179,8 @@ const char* conv_check(const ConvArgs& a) {
     if (g.KS == KS_PHASE && a.res) return "the phase-tap epilogue adds no residual";
     if (a.epi == EPI_WINO && (a.bias || a.res || a.scale != 1.0f))
       return "the Winograd-domain GEMM stores plain products (no bias, residual or scale)";
+    if (a.bn != 0 && (a.epi != EPI_WINO || (a.bn != 128 && a.bn != 256) || a.Cout % a.bn))
+      return "a tile width of 128 or 256 channels (dividing Cout) is the Winograd GEMM's choice";
     if (a.epi == EPI_WINO && (a.out_fstride < (long long)a.H * a.W * a.ldo ||
                               2LL * a.TF * a.out_fstride + 16 > 0x7fffffffLL))
       return "a Winograd product tile must span less than 2^31 bytes (32-bit store offsets)";
@@ -2217,7 +2219,14 @@ hipError_t launch_conv(const ConvArgs& a, hipStream_t stream) {
     const int pro = a.seg[0].prologue;
     if (v.mode == 2) return launch_persist_impl<256, 4, 2, PRO_RAW>(a, stream);
     if (v.mode == 3) return launch_persist_impl<256, 4, 3, PRO_RAW>(a, stream);
-    if (v.mode == 4) {  // one instantiation per Winograd tile shape (TF frames x TW column groups)
+    if (v.mode == 4) {  // one instantiation per Winograd tile shape (TF frames x TW column groups) and width
+      if (a.bn == 128) {
+        if (a.TF == 2 && a.TW == 8) return launch_persist_impl<128, 2, 4, PRO_RAW, 4, 8, 2>(a, stream);
+        if (a.TF == 4 && a.TW == 8) return launch_persist_impl<128, 2, 4, PRO_RAW, 4, 8, 4>(a, stream);
+        if (a.TF == 8 && a.TW == 4) return launch_persist_impl<128, 2, 4, PRO_RAW, 4, 4, 8>(a, stream);
+        if (a.TF == 4 && a.TW == 4) return launch_persist_impl<128, 2, 4, PRO_RAW, 4, 4, 4>(a, stream);
+        return launch_persist_impl<128, 2, 4, PRO_RAW, 4>(a, stream);
+      }
       if (a.TF == 2 && a.TW == 8) return launch_persist_impl<256, 2, 4, PRO_RAW, 4, 8, 2>(a, stream);
       if (a.TF == 4 && a.TW == 8) return launch_persist_impl<256, 2, 4, PRO_RAW, 4, 8, 4>(a, stream);
       if (a.TF == 8 && a.TW == 4) return launch_persist_impl<256, 2, 4, PRO_RAW, 4, 4, 8>(a, stream);

@@ -89,6 +89,7 @@ struct ConvArgs {
   int out_base;             // EPI_TIME frame base; EPI_VIDEO first frame index
   int video_T;              // EPI_VIDEO total frames of the video
   int nhv_max;              // halo rows per LDS buffer (>= every segment's item rows)
+  int bn;                   // Winograd-domain GEMM: output channels per tile, 256 (or 0) or 128
   const h16_t* zero_row;    // zero_len fp16 zeros: source of padding voxels
   int zero_len;             // >= every segment's Cin
 };
