@@ -24,7 +24,7 @@ namespace {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
-enum ItemKind { K_CONV = 0, K_PHASE = 1, K_VEC = 2, K_WINO = 3, K_CONV_PART = 4, K_S2D = 5 };
+enum ItemKind { K_CONV = 0, K_PHASE = 1, K_VEC = 2, K_WINO = 3, K_CONV_PART = 4, K_S2D = 5, K_HEADX = 6 };
 
 // A 3x3x3 norm-SiLU conv runs in Winograd form (F(kWinoM,3) along x: input
 // transform, kWinoN xi-plane GEMMs on the persistent kernel, output transform)
@@ -147,6 +147,11 @@ Layout make_layout(int c, int h, int w, bool deep = false) {
   }
   L.head_norm = add_vec(L, c, std::sqrt((float)c));
   add_conv(L, 12, c, 27, c, &L.head_w, &L.head_b);
+  if (c % 32 == 0) {  // the x taps in the output columns (the head's packed form)
+    Item& it = L.items[L.head_w];
+    it.kind = K_HEADX;
+    it.bytes = prep_frag_bytes(64, c, 9);
+  }
   size_t off = 0;
   for (auto& it : L.items) {
     it.off = off;
@@ -1145,6 +1150,8 @@ int prepare_plan(int c, int h, int w, const Layout& L, const void* const* weight
       e = launch_prep_phase_frag(src, weight_dtype, it.cout, static_cast<h16_t*>(dst), s);
     else if (it.kind == K_S2D)
       e = launch_prep_s2d_frag(src, weight_dtype, it.cout, static_cast<h16_t*>(dst), s);
+    else if (it.kind == K_HEADX)
+      e = launch_prep_headx_frag(src, weight_dtype, it.cin, static_cast<h16_t*>(dst), s);
     else
       e = launch_prep_vec(src, weight_dtype, it.n, it.scale, static_cast<float*>(dst), s);
   }
@@ -1324,18 +1331,27 @@ int decode_impl(wvd_plan* plan, const void* z, int z_dtype, int T, int t_begin, 
                                 yn.fstride(), yn.C, cx.st);
       });
       ConvArgs a = args_init();
-      a.seg[0] = seg_basic(yn.p, yn.fstride(), yn.C, yn.C, cx.prep<h16_t>(L.head_w), yn.C, (long long)12 * yn.C, 3, 3,
-                           cx.wbytes(L.head_w));
+      // Packed form (widths a multiple of 32): nine (t, y) taps over the
+      // input columns, the three x taps as output columns 12 dx + co, tiles
+      // of 4 frames x 4 rows x 16 columns making 14 output columns each.
+      const bool packed = L.items[L.head_w].kind == K_HEADX;
+      a.seg[0] = seg_basic(yn.p, yn.fstride(), yn.C, yn.C, cx.prep<h16_t>(L.head_w), yn.C, (long long)12 * yn.C, 3,
+                           packed ? KS_3x1 : KS_3x3, cx.wbytes(L.head_w));
       a.seg[0].ring = ring;
       a.seg[0].n_hist = nh2;
       a.nseg = 1;
-      a.Cout = 12;
+      a.Cout = packed ? 64 : 12;
       a.bias = cx.prep<float>(L.head_b);
       a.out = out;
       a.epi = EPI_VIDEO;
       a.out_base = (int)(g2 - vbase);
       a.video_T = VT;
-      set_grid(a, x.F, x.H, x.W, tf_for(3, x.F));
+      if (packed) {
+        set_grid(a, x.F, x.H, x.W, 4, 16);
+        a.tiles_x = (x.W + 13) / 14;
+      } else {
+        set_grid(a, x.F, x.H, x.W, tf_for(3, x.F));
+      }
       conv(cx, a, 0);
       ring_update(cx, ring, yn);
     }

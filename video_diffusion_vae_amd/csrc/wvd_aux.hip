@@ -429,6 +429,30 @@ __global__ void prep_frag_kernel(const void* __restrict__ w, int dtype, int cout
   }
 }
 
+// The head's 3x3x3 conv (12 output channels) with its three x taps moved
+// into the output columns: column n = 12 dx + co (n < 36; the rest zero) of
+// the (dt, dy) tap t = 3 dt + dy holds w[co][i][3 t + dx], so a GEMM over the
+// nine (t, y) taps gives, per input column x, the partial sums
+// P[x][12 dx + co] that the epilogue combines as out[x] = sum over dx of
+// P[x + dx - 1][12 dx + co].  Fragment order with taps = 9 and 128 columns.
+__global__ void prep_headx_frag_kernel(const void* __restrict__ w, int dtype, int cin, h16_t* __restrict__ out) {
+  const int NB = 4, U = cin / 16;
+  const long long n = (long long)NB * U * 9 * 512;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+       e += (long long)gridDim.x * blockDim.x) {
+    const int j = (int)(e & 7);
+    const int l = (int)((e >> 3) & 63);
+    const long long blk = e >> 9;
+    const int t = (int)(blk % 9);
+    const int u = (int)((blk / 9) % U);
+    const int nb = (int)(blk / (9LL * U));
+    const int o = nb * 32 + (l & 31);
+    const int i = u * 16 + (l >> 5) * 8 + j;
+    out[e] = o < 36 ? (h16_t)f2h(load_in(w, ((long long)(o % 12) * cin + i) * 27 + t * 3 + o / 12, dtype))
+                    : (h16_t)0;
+  }
+}
+
 // Phase form of nearest-2x upsampling followed by a 3x3 conv (pad 1): output
 // pixel (2i+py, 2j+px) is a 2x2 conv of the low-resolution input at rows
 // i+py-1+a, cols j+px-1+b (a, b in {0,1}) whose weights are sums of the 3x3
@@ -1223,6 +1247,14 @@ hipError_t launch_prep_frag_part(const void* w, int dtype, int cout, int cin_src
   const long long n = (long long)prep_frag_bytes(cout, cin_pad, taps) / 2;
   hipLaunchKernelGGL(prep_frag_kernel, dim3(grid_for(n)), dim3(256), 0, s, w, dtype, cout, cin_src, cin_off, cin,
                      taps, cin_pad, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep_headx_frag(const void* w, int dtype, int cin, h16_t* out, hipStream_t s) {
+  if (g_dry_run) return hipSuccess;
+  if (cin < 32 || cin % 32) return hipErrorInvalidValue;
+  const long long n = (long long)prep_frag_bytes(64, cin, 9) / 2;
+  hipLaunchKernelGGL(prep_headx_frag_kernel, dim3(grid_for(n)), dim3(256), 0, s, w, dtype, cin, out);
   return hipGetLastError();
 }
 

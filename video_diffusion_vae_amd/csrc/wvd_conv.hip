@@ -805,8 +805,12 @@ struct TileGeo {
 
 template <int BN, int MODE, int TW = kTileW, int TF4 = kTFWino>
 __device__ __forceinline__ TileGeo tile_geo(const ConvArgs& a, int logical) {
-  constexpr int TF = MODE == 2 ? 1 : (MODE == 4 ? TF4 : kTF333);
-  constexpr int TH = MODE == 2 ? 16 : (MODE == 4 ? kTileM / TW / TF4 : kTH333);
+  constexpr bool TYX = MODE == 4 || MODE == 5;  // (t, y) taps over whole columns
+  constexpr int TF = MODE == 2 ? 1 : (TYX ? TF4 : kTF333);
+  constexpr int TH = MODE == 2 ? 16 : (TYX ? kTileM / TW / TF4 : kTH333);
+  // the head's tiles overlap: columns x0 .. x0 + TW - 1 make outputs x0 + 1 ..
+  // x0 + TW - 2, so tile tx starts at column (TW - 2) tx - 1
+  constexpr int XSTEP = MODE == 5 ? TW - 2 : TW, XOFF = MODE == 5 ? -1 : 0;
   // Output positions vary fastest: the tiles running together on an XCD
   // share one (phase, channel block) of weights in its L2 and neighbouring
   // halos (interleaving the phases made them stream one weight set per phase).
@@ -823,7 +827,7 @@ __device__ __forceinline__ TileGeo tile_geo(const ConvArgs& a, int logical) {
   } else {  // temporal taps: frames fastest, so the tiles that share their
             // history frames run together and read them from one L2
     t.f0 = (mt % a.tiles_f) * TF;
-    t.x0 = ((mt / a.tiles_f) % a.tiles_x) * TW;
+    t.x0 = ((mt / a.tiles_f) % a.tiles_x) * XSTEP + XOFF;
     t.y0 = (mt / (a.tiles_f * a.tiles_x)) * TH;
   }
   t.n0 = nt * BN;
@@ -848,21 +852,24 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
   constexpr bool NORM = PRO0 == PRO_NORM || PRO0 == PRO_NORM_SILU;
   constexpr bool ACT = PRO0 == PRO_NORM_SILU;
   constexpr bool KT3 = MODE == 3;   // 3x1x1 temporal conv (time_conv)
-  constexpr bool WINO = MODE == 4;  // Winograd-domain 3x3x1 (t, y) GEMM, one xi per phase
+  // Winograd-domain 3x3x1 (t, y) GEMM, one xi per phase; the same loop runs
+  // the head (MODE 5: input columns, the x taps in the output columns)
+  constexpr bool HEADX = MODE == 5;
+  constexpr bool WINO = MODE == 4 || HEADX;
   // the Winograd and phase loops pass B as the MFMA's first operand: rows of
   // the product are output channels, columns output positions
   constexpr bool SWAPPED = WINO || MODE == 2;
-  constexpr int TW = MODE == 4 ? TWW : kTileW;  // tile columns (Winograd: column groups)
-  static_assert(MODE == 4 || (TWW == kTileW && TFW == kTFWino), "tile shape choice is the Winograd GEMM's");
-  constexpr int TF = MODE == 2 ? 1 : (MODE == 4 ? TFW : kTF333);
-  constexpr int TH = MODE == 2 ? 16 : (MODE == 4 ? kTileM / TW / TFW : kTH333);
+  constexpr int TW = WINO ? TWW : kTileW;  // tile columns (Winograd: column groups)
+  static_assert(WINO || (TWW == kTileW && TFW == kTFWino), "tile shape choice is the Winograd GEMM's");
+  constexpr int TF = MODE == 2 ? 1 : (WINO ? TFW : kTF333);
+  constexpr int TH = MODE == 2 ? 16 : (WINO ? kTileM / TW / TFW : kTH333);
   constexpr int KT = MODE == 2 ? 1 : 3;
   constexpr int HSX = KT3 || WINO ? 0 : 1;  // spatial halo along x
   constexpr int HSY = KT3 ? 0 : 1;          // and along y
   constexpr int HX = TW + 2 * HSX, HY = TH + 2 * HSY, HF = TF + KT - 1;
   constexpr int NHV = HF * HY * HX;
   constexpr int NTAPS = K333 ? 27 : (KT3 ? 3 : (WINO ? 9 : 4));
-  static_assert(MODE >= 1 && MODE <= 4, "specialised tap sets only");
+  static_assert(MODE >= 1 && MODE <= 5, "specialised tap sets only");
   static_assert(WN % 32 == 0 && MI >= 1, "wave tile");
 
   extern __shared__ __align__(16) unsigned char smem[];
@@ -1224,7 +1231,56 @@ __global__ __launch_bounds__(NW * 64) void conv_persist(ConvArgs a) {
     const int nn = seq.at(k + 2);
     if (nn >= 0) build_tables(k & 1, nn);
 
-    if constexpr (WINO && NW == 4 && BN == 256) {
+    if constexpr (HEADX) {
+      // ---- epilogue of the head: the partial sums P[m][12 dx + co] of the
+      // tile's TW columns (one extra on each side of its TW - 2 outputs) go to
+      // LDS (fp32, 40 of the 64 columns: 36 used); output column x of a row is
+      // P[x - 1][co] + P[x][12 + co] + P[x + 1][24 + co] + bias, clamped and
+      // stored as a bf16 pair of one video row (co = 4k + 2 dy + (0, 1):
+      // colour k, row 2y + dy, pixels 2x and 2x + 1).  A row of TW positions
+      // lies inside one wave's 32-row block, so each wave combines its own.
+      static_assert(BN == 64 && NJ == 2 && WN == 64 && WM == 64 && MI == 2 && TW == 16, "head tile");
+      constexpr int PROW = 44;                        // staged row: 40 floats + pad (conflict-free)
+      constexpr int NROW = WM / TW;                   // rows of TW positions per wave
+      constexpr int NITEM = NROW * 6 * (TW - 2);      // (row, colour and video row, output column)
+      static_assert(NW * WM * PROW * 4 <= kHeadXEpiBytes, "staged rows fit in one halo buffer");
+      float* ep = reinterpret_cast<float*>(smem + ((gc - 1) & 1) * halo_bytes) + wave * WM * PROW;
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            if (j == 1 && g4 > 0) continue;  // columns 40..63: zero weights
+            const f32x16_t& c = acc[i][j];
+            f32x4_t v = {c[4 * g4], c[4 * g4 + 1], c[4 * g4 + 2], c[4 * g4 + 3]};
+            *reinterpret_cast<f32x4_t*>(ep + (32 * i + lrow) * PROW + 32 * j + 8 * g4 + 4 * kpart) = v;
+          }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the rows are in LDS
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int rnd = 0; rnd < (NITEM + 63) / 64; ++rnd) {
+        const int q = rnd * 64 + lane;
+        const int ox = q % (TW - 2), t6 = q / (TW - 2);
+        const int pr = t6 % 6, row = t6 / 6;  // pr = 2k + dy
+        const int t2 = wave_m * NROW + row;   // (frame, row) of the tile
+        const int f = geo.f0 + t2 / TH, y = geo.y0 + t2 % TH, x = geo.x0 + 1 + ox;
+        if (q < NITEM && f < a.F && y < a.H && x < a.W) {
+          const float* pp = ep + (row * TW + ox) * PROW + 2 * pr;
+          const float2 p0 = *reinterpret_cast<const float2*>(pp);
+          const float2 p1 = *reinterpret_cast<const float2*>(pp + PROW + 12);
+          const float2 p2 = *reinterpret_cast<const float2*>(pp + 2 * PROW + 24);
+          const int n = 2 * pr;
+          const float v0 = clamp_unit((p0.x + p1.x + p2.x) * a.scale + (a.bias ? a.bias[n] : 0.0f));
+          const float v1 = clamp_unit((p0.y + p1.y + p2.y) * a.scale + (a.bias ? a.bias[n + 1] : 0.0f));
+          const long long r2 = ((long long)(pr >> 1) * a.video_T + a.out_base + f) * (2 * a.H) + 2 * y + (pr & 1);
+          *reinterpret_cast<uint32_t*>(static_cast<bf16_t*>(a.out) + r2 * (2 * a.W) + 2 * x) =
+              f2bf(v0) | (f2bf(v1) << 16);
+        }
+      }
+      // the next tile's halo stores reuse this buffer after the tile barrier
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+    } else if constexpr (WINO && NW == 4 && BN == 256) {
       // ---- epilogue of the Winograd-domain GEMM (plain fp16 products): lane
       // (kpart, lrow) of block (i, j) holds position 32i + lrow of the wave's
       // rows and channels 32j + 8g + 4*kpart + r (accumulator 4g + r).  Per
@@ -1551,10 +1607,18 @@ Variant conv_variant(const ConvArgs& a) {
                      a.TF * a.TH * a.TW == kTileM &&
                      v.bk == 32 && a.nseg == 1 && g.wfrag && g.prologue == PRO_RAW && a.Cout % 256 == 0 &&
                      a.epi == EPI_WINO;
+  // the head with its x taps in the output columns: (t, y) taps over 16
+  // input columns per tile row, 64 output columns (36 used)
+  const bool khead = g.KT == 3 && g.KS == KS_3x1 && a.nphase == 1 && a.TF == 4 && a.TW == 16 && a.TH == 4 &&
+                     a.Cout == 64 && v.bk == 32 && a.nseg == 1 && g.wfrag && g.prologue == PRO_RAW &&
+                     a.epi == EPI_VIDEO;
   const bool shortcut_ok = a.nseg == 1 || (a.seg[1].KT == 1 && a.seg[1].KS == 1 && a.seg[1].prologue == PRO_RAW &&
                                             a.seg[1].wfrag && a.seg[1].Cin % 32 == 0);
-  v.mode = k333 ? 1 : (kph ? 2 : (kt3 ? 3 : (kwino ? 4 : 0)));
-  if (v.mode != 0 && a.Cout % 256 == 0 && shortcut_ok) {
+  v.mode = k333 ? 1 : (kph ? 2 : (kt3 ? 3 : (kwino ? 4 : (khead ? 5 : 0))));
+  if (v.mode == 5) {
+    v.bn = 64;
+    v.nw = 8;
+  } else if (v.mode != 0 && a.Cout % 256 == 0 && shortcut_ok) {
     v.bn = 256;
     v.nw = 8;
   } else if (v.mode == 1 && a.Cout <= 32) {
@@ -2119,6 +2183,7 @@ bool conv_persistent(const ConvArgs& a) {
   if (v.bn == 32) return v.mode == 1 && a.epi == EPI_VIDEO && a.seg[0].prologue == PRO_RAW;
   if (v.mode == 3) return a.epi == EPI_TIME;
   if (v.mode == 4) return a.epi == EPI_WINO;
+  if (v.mode == 5) return true;
   if (v.mode == 2) return a.epi == EPI_PHASE || (a.nphase == 1 && a.epi == EPI_H16);
   return a.epi == EPI_H16 || (v.mode == 1 && a.epi == EPI_VIDEO);
 }
@@ -2147,7 +2212,13 @@ size_t conv_lds_bytes(const ConvArgs& a) {
 
 const char* conv_check(const ConvArgs& a) {
   if (a.nseg < 1 || a.nseg > 2) return "segment count";
-  if (a.seg[0].KS == KS_3x1 ? !wino_tile_shape_ok(a.TF, a.TW) : a.TW != kTileW) return "unsupported tile shape";
+  // the head with its x taps in the output columns (3x1 taps, video store)
+  const bool headx = a.seg[0].KS == KS_3x1 && a.epi == EPI_VIDEO;
+  if (headx ? (a.TF != 4 || a.TW != 16) : (a.seg[0].KS == KS_3x1 ? !wino_tile_shape_ok(a.TF, a.TW) : a.TW != kTileW))
+    return "unsupported tile shape";
+  if (headx && (a.Cout != 64 || a.nphase != 1 || a.tiles_x != (a.W + 13) / 14 || a.nseg != 1 ||
+                a.nhv_max * (32 * 2 + 16) < kHeadXEpiBytes || conv_variant(a).mode != 5))
+    return "the head's packed form: 64 columns, one phase, tiles of 14 output columns, staging rows";
   if (a.TF < 1 || a.TF * a.TH * a.TW != kTileM) return "tile TF*TH*TW != 256";
   if (a.F < 1 || a.H < 1 || a.W < 1 || a.Cout < 1) return "empty output grid";
   if (a.nphase != 1 && a.nphase != 4 && a.nphase != kWinoN) return "phase count";
@@ -2169,11 +2240,11 @@ const char* conv_check(const ConvArgs& a) {
     if (g.KS == KS_PHASE && !(a.nphase == 4 || (a.nphase == 1 && a.epi == EPI_H16)))
       return "phase taps need 4 phases (or one, with a plain store)";
     if (a.epi == EPI_PHASE && (g.KS != KS_PHASE || a.nphase != 4)) return "the phase store needs 4 phases";
-    if (g.KS == KS_3x1 && a.nphase != kWinoN) return "Winograd taps need one phase per xi plane";
+    if (g.KS == KS_3x1 && !headx && a.nphase != kWinoN) return "Winograd taps need one phase per xi plane";
     if (a.nphase != 1 && g.KS != KS_PHASE && g.KS != KS_3x1) return "phases need phase or Winograd taps";
-    if (g.KS == KS_3x1 && (a.epi != EPI_WINO || conv_variant(a).mode != 4))
-      return "3x1 taps run only as the Winograd-domain GEMM";
-    if ((a.epi == EPI_WINO) != (g.KS == KS_3x1)) return "EPI_WINO needs the 3x1 taps";
+    if (g.KS == KS_3x1 && !headx && (a.epi != EPI_WINO || conv_variant(a).mode != 4))
+      return "3x1 taps run only as the Winograd-domain GEMM or the head";
+    if (a.epi == EPI_WINO && g.KS != KS_3x1) return "EPI_WINO needs the 3x1 taps";
     if ((a.epi == EPI_WINO || g.KS == KS_PHASE) && a.nhv_max * (bk * 2 + 16) < kSwapEpiBytes)
       return "halo buffer below the epilogue's staging rows";
     if (g.KS == KS_PHASE && a.res) return "the phase-tap epilogue adds no residual";
@@ -2205,7 +2276,8 @@ const char* conv_check(const ConvArgs& a) {
       return "the specialised kernels take only a 1x1x1 second segment";
     if (s > 0 && g.KS != KS_1x1) return "second segment must have 1x1 spatial taps";
   }
-  if (a.epi == EPI_VIDEO && a.Cout != 12) return "the video epilogue takes the head's 12 channels";
+  if (a.epi == EPI_VIDEO && a.Cout != (headx ? 64 : 12))
+    return "the video epilogue takes the head's 12 channels (64 packed columns)";
   if (a.epi == EPI_LATENT && (conv_persistent(a) || a.video_T < 1 || a.out_base < 0 || a.out_base + a.F > a.video_T))
     return "latent epilogue: generic kernel, frames inside the clip";
   if (!a.out || !a.zero_row) return "null output or zero row";
@@ -2219,6 +2291,7 @@ hipError_t launch_conv(const ConvArgs& a, hipStream_t stream) {
     const int pro = a.seg[0].prologue;
     if (v.mode == 2) return launch_persist_impl<256, 4, 2, PRO_RAW>(a, stream);
     if (v.mode == 3) return launch_persist_impl<256, 4, 3, PRO_RAW>(a, stream);
+    if (v.mode == 5) return launch_persist_impl<64, 1, 5, PRO_RAW, 4, 16, 4>(a, stream);
     if (v.mode == 4) {  // one instantiation per Winograd tile shape (TF frames x TW column groups) and width
       if (a.bn == 128) {
         if (a.TF == 2 && a.TW == 8) return launch_persist_impl<128, 2, 4, PRO_RAW, 4, 8, 2>(a, stream);

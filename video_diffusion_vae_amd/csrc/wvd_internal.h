@@ -22,6 +22,9 @@ constexpr int kWinoInRun = 4;           // column groups per thread of the input
 // 8 waves x 32 positions x (32 fp32 channels + 16 bytes of pad), or 4 waves
 // x 32 x (64 channels + pad), whichever is larger.
 constexpr int kSwapEpiBytes = 8 * 32 * (32 * 4 + 16);
+// The head's epilogue (x taps in the output columns) stages 256 rows of 44
+// fp32 partial sums in one halo buffer.
+constexpr int kHeadXEpiBytes = 256 * 44 * 4;
 
 enum Prologue { PRO_RAW = 0, PRO_NORM = 1, PRO_NORM_SILU = 2 };
 enum Epilogue {
@@ -201,6 +204,10 @@ hipError_t launch_prep_phase_frag(const void* w, int dtype, int C, h16_t* out, h
 // Weights of a 3x3 stride-2 conv for its space-to-depth form (C -> C over 4C
 // input channels, 2x2 taps at offsets -1, 0; fragment order, tap = 2a + b).
 hipError_t launch_prep_s2d_frag(const void* w, int dtype, int C, h16_t* out, hipStream_t s);
+// The head's 12 x cin x 27 weights with the x taps in the output columns
+// (column 12 dx + co of (dt, dy) tap 3 dt + dy; 64 columns, 36 used) in
+// fragment order, prep_frag_bytes(64, cin, 9) bytes; cin a multiple of 32.
+hipError_t launch_prep_headx_frag(const void* w, int dtype, int cin, h16_t* out, hipStream_t s);
 // x [F][H][W][C] -> y [F][H/2][W/2][4C], block 2 py + px = x[2Y+py][2X+px].
 hipError_t launch_space_to_depth(const h16_t* x, long long x_fstride, int C, int F, int H, int W, h16_t* y,
                                  hipStream_t s);
