@@ -169,7 +169,7 @@ Layout make_layout(int c, int h, int w, bool deep = false) {
 // Workspace carve-up for a given maximum number of latent frames per pass.
 struct Work {
   size_t X, H, Y, zt, zp, rs, qkv, S, Pm, Vt, O;
-  size_t kf, vf, st, mi;     // attention on the batched GEMM: K, V^T fragments, score statistics
+  size_t kf, vf, st;         // attention on the batched GEMM: K, V^T fragments, score statistics
   size_t U, M;               // Winograd input planes and products
   std::vector<size_t> ring;  // 24 rings: offsets inside the ring block
   size_t rings;              // ring block offset in the workspace (npos: caller-owned state)
@@ -217,7 +217,7 @@ RingInfo ring_info(int c, int nrb, int id) {
 int lpad_of(int L) { return (L + 31) / 32 * 32; }
 
 // The mid attention runs on the batched 256 x 256 GEMM (scores never stored:
-// a statistics pass, then a probability pass) when a frame has at least 256
+// a score pass, then an in-place softmax of its output) when a frame has at least 256
 // tokens and the width is a multiple of 256; smaller shapes use the generic
 // conv kernel with stored fp32 scores.
 bool attn_fast(int C, long long L) { return L >= 256 && C % 256 == 0; }
@@ -237,7 +237,6 @@ void take_attention(Work& W, Take& take, long long F, long long L, long long C) 
   W.kf = take(fast ? (size_t)F * Np * C * 2 : 0);
   W.vf = take(fast ? (size_t)F * Np * C * 2 : 0);
   W.st = take(fast ? (size_t)F * L * (Np / 64) * 8 : 0);
-  W.mi = take(fast ? (size_t)F * L * 8 : 0);
 }
 
 Work make_work(int c, int h, int w, int P, bool rings_in_workspace = true, int nrb = 2) {
@@ -895,13 +894,13 @@ GemmArgs gemm_args() {
 
 // Per-frame single-head attention on the batched 256 x 256 GEMM:
 //   xn = RMSNorm(x); qkv = xn Wqkv^T + b;
-//   per frame, with K and V^T in fragment order: the score pass computes,
-//   per query and group of 64 keys, the maximum and the sum of e^(s - max)
-//   of s = q.k / sqrt(C); a reduction gives each query's maximum M and
-//   1 / sum; the probability pass recomputes the scores and stores
-//   P = e^(s - M) / sum in fp16 (zero for the padding keys);
-//   O = P V; x += O Wp^T + bp.
-// The fp32 scores are never stored.
+//   per frame, with K and V^T in fragment order: the score pass computes
+//   s = q.k / sqrt(C) and, per query and group g of 64 keys, the maximum
+//   m_g; it stores e^(s - m_g) in fp16 (zero for the padding keys) and
+//   (m_g, sum of e^(s - m_g)); a per-query pass takes the maximum M and the
+//   sum S over the groups and scales the group's values by e^(m_g - M) / S,
+//   which gives P = softmax(s) in place; O = P V; x += O Wp^T + bp.
+// The fp32 scores are never stored, and each score is computed once.
 void attention_fast(Ctx& cx, const Act& x) {
   const Layout& L = cx.plan->L;
   const int C = x.C, Lt = x.H * x.W;
@@ -912,7 +911,6 @@ void attention_fast(Ctx& cx, const Act& x) {
   h16_t* kf = cx.wsp<h16_t>(cx.W->kf);
   h16_t* vf = cx.wsp<h16_t>(cx.W->vf);
   float* st = cx.wsp<float>(cx.W->st);
-  float* mi = cx.wsp<float>(cx.W->mi);
   const long long rows = (long long)x.F * Lt;
   cx.rs_tensor = nullptr;
   cx.what = "attention norm";
@@ -949,18 +947,13 @@ void attention_fast(Ctx& cx, const Act& x) {
   g.w_fs = Np * C;
   g.n_valid = Lt;
   g.stats = st;
-  const double score_flops = 2.0 * x.F * Lt * Np * C;
-  cx.what = "attention scores (statistics)";
-  cx.run(2, score_flops, [&] { return launch_gemm_nt(g, G_STATS, cx.st); });
-  cx.what = "attention statistics";
-  cx.run(4, 0, [&] { return launch_attn_stats(st, rows, (int)(Np / 64), mi, cx.st); });
-  g.stats = nullptr;
-  g.mi = mi;
   g.out = P;
   g.ldo = (int)Np;
   g.o_fs = Lt * Np;
-  cx.what = "attention scores (probabilities)";
-  cx.run(2, score_flops, [&] { return launch_gemm_nt(g, G_PROB, cx.st); });
+  cx.what = "attention scores";
+  cx.run(2, 2.0 * x.F * Lt * Np * C, [&] { return launch_gemm_nt(g, G_STATS, cx.st); });
+  cx.what = "attention softmax";
+  cx.run(4, 0, [&] { return launch_attn_rescale(P, st, rows, (int)Np, cx.st); });
   g = gemm_args();
   g.x = P;
   g.M = Lt;

@@ -299,20 +299,39 @@ __global__ __launch_bounds__(256) void attn_frag_kernel(const h16_t* __restrict_
   }
 }
 
-// Per query row: the maximum M and 1 / sum of e^(s - M) over its keys, from
-// the nst partial (maximum, sum of e^(s - partial maximum)) pairs the score
-// pass wrote for groups of 128 keys.
-__global__ __launch_bounds__(256) void attn_stats_kernel(const float2* __restrict__ st, long long rows, int nst,
-                                                         float2* __restrict__ mi) {
-  for (long long r = (long long)blockIdx.x * blockDim.x + threadIdx.x; r < rows;
-       r += (long long)gridDim.x * blockDim.x) {
-    const float2* p = st + r * nst;
-    float m = -INFINITY;
-    for (int t = 0; t < nst; ++t) m = fmaxf(m, p[t].x);
-    float l = 0.0f;
-    for (int t = 0; t < nst; ++t)
-      if (p[t].y > 0.0f) l += p[t].y * exp_hw(p[t].x - m);
-    mi[r] = make_float2(m, 1.0f / l);
+// One wave per score row r: the row's maximum M over the partial maxima
+// m_g of its groups of 64 keys, S = sum_g l_g e^(m_g - M) from the groups'
+// (m_g, l_g), then each fp16 value e^(s - m_g) of group g is scaled by
+// e^(m_g - M) / S in place.  A group whose keys are all padding has l_g = 0
+// and scale 0 (its values are zero already).
+__global__ __launch_bounds__(256) void attn_rescale_kernel(h16_t* __restrict__ P, const float2* __restrict__ st,
+                                                           long long rows, int np) {
+  const int lane = threadIdx.x & 63;
+  const long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int nst = np / 64;
+  const float2* sr = st + r * nst;
+  float m = -INFINITY;
+  for (int g = lane; g < nst; g += 64) m = fmaxf(m, sr[g].x);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+  float l = 0.0f;
+  for (int g = lane; g < nst; g += 64) {
+    const float2 p = sr[g];
+    if (p.y > 0.0f) l += p.y * exp_hw(p.x - m);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) l += __shfl_xor(l, d, 64);
+  const float inv = 1.0f / l;
+  uint4* row = reinterpret_cast<uint4*>(P + r * np);
+  for (int q = lane; q < np / 8; q += 64) {
+    const float2 p = sr[q >> 3];
+    const float f = p.y > 0.0f ? exp_hw(p.x - m) * inv : 0.0f;
+    float v[8];
+    unpack8h(row[q], v);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] *= f;
+    row[q] = pack8h(v);
   }
 }
 
@@ -1182,11 +1201,11 @@ hipError_t launch_attn_frag(const h16_t* qkv, int F, int L, int C, int Np, h16_t
   return hipGetLastError();
 }
 
-hipError_t launch_attn_stats(const float* st, long long rows, int nst, float* mi, hipStream_t s) {
+hipError_t launch_attn_rescale(h16_t* P, const float* st, long long rows, int np, hipStream_t s) {
+  if (rows < 1 || np < 64 || np % 64) return hipErrorInvalidValue;
   if (g_dry_run) return hipSuccess;
-  if (rows < 1 || nst < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_stats_kernel, dim3(grid_for(rows)), dim3(256), 0, s, reinterpret_cast<const float2*>(st),
-                     rows, nst, reinterpret_cast<float2*>(mi));
+  hipLaunchKernelGGL(attn_rescale_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, P,
+                     reinterpret_cast<const float2*>(st), rows, np);
   return hipGetLastError();
 }
 

@@ -2005,18 +2005,17 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs ga) {
     // columns the accumulator runs go straight into fp32 LDS rows; then
     // each lane takes eight columns of one row (eight lanes per row):
     //   G_H16: bias (and residual), fp16, a 16-byte store;
-    //   G_STATS: the row's max and sum of e^(v - max) over those 64
-    //     columns (a reduction over the eight lanes), one float2;
-    //   G_PROB: e^(v - M) / S with the row's (M, 1/S), fp16, a store.
+    //   G_STATS: the row's max m over those 64 columns (a reduction over
+    //     the eight lanes), e^(v - m) as fp16 with a 16-byte store, and
+    //     (m, sum of e^(v - m)) as one float2.
     constexpr int SROW = 64 * 4 + 16, LPR = 8, RPI = 8;
     static_assert(4 * 32 * SROW <= 256 * kS1ARow, "staging fits in a buffer's A rows");
     unsigned char* st = g1s + kS1Buf + wave * 32 * SROW;
     const float scale = ga.scale;
     // per-tile row bases (uniform): row m of the tile's frame is row
     // m - m0 + (tile base), so the loops below need 32-bit offsets only
-    h16_t* const outb = EPI == G_STATS ? nullptr : ga.out + f * ga.o_fs + m0 * ga.ldo;
+    h16_t* const outb = ga.out + f * ga.o_fs + m0 * ga.ldo;
     const h16_t* const resb = EPI == G_H16 && ga.res ? ga.res + f * ga.r_fs + m0 * ga.ldr : nullptr;
-    const float* const mib = EPI == G_PROB ? ga.mi + (f * M + m0) * 2 : nullptr;
     float* const stb = EPI == G_STATS ? ga.stats + (f * M + m0) * (N / 64) * 2 : nullptr;
     const int mskip = (int)(mown - m0);  // tile rows below this belong to the previous tile
 #pragma unroll
@@ -2066,20 +2065,20 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs ga) {
             mx = fmaxf(mx, __shfl_xor(mx, 4, 64));
             float sm = 0.0f;
 #pragma unroll
-            for (int q = 0; q < 8; ++q)
-              if (ncol + q < ga.n_valid) sm += exp_hw(v8[q] - mx);
+            for (int q = 0; q < 8; ++q) {
+              v8[q] = ncol + q < ga.n_valid ? exp_hw(v8[q] - mx) : 0.0f;
+              sm += v8[q];
+            }
             sm += __shfl_xor(sm, 1, 64);
             sm += __shfl_xor(sm, 2, 64);
             sm += __shfl_xor(sm, 4, 64);
-            if (lane % LPR == 0 && mt >= mskip)
+            if (mt < mskip) continue;
+            if (lane % LPR == 0)
               *reinterpret_cast<float2*>(stb + (mt * (N / 64) + ct * 4 + wn * 2 + jh) * 2) = make_float2(mx, sm);
+            *reinterpret_cast<uint4*>(outb + mt * ga.ldo + ncol) = pack8h(v8);
           } else {
             if (mt < mskip) continue;
-            if constexpr (EPI == G_PROB) {
-              const float2 ms = *reinterpret_cast<const float2*>(mib + mt * 2);
-#pragma unroll
-              for (int q = 0; q < 8; ++q) v8[q] = ncol + q < ga.n_valid ? exp_hw(v8[q] - ms.x) * ms.y : 0.0f;
-            } else if (resb) {
+            if (resb) {
               float rv[8];
               unpack8h(*reinterpret_cast<const uint4*>(resb + mt * ga.ldr + ncol), rv);
 #pragma unroll
@@ -2107,28 +2106,24 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs ga) {
 }  // namespace
 
 const char* gemm_nt_check(const GemmArgs& g, int epi) {
+  if (epi != G_H16 && epi != G_STATS) return "epilogue";
   if (!g.x || !g.w || g.M < 256 || g.N % 256 || g.K % (2 * kS1K) || g.K > 4096 || g.lda % 8 || g.lda < g.K)
     return "A / B shapes";
   if (g.w_bytes <= 0 || g.w_bytes > 0x7fffffffLL || (long long)256 * g.lda * 2 > 0x7fffffffLL) return "B bytes";
   if (g.nF < 1 || (g.nF > 1 && (g.a_fs < 0 || g.w_fs < 0 || g.o_fs < 0 || g.r_fs < 0))) return "frames";
   if ((long long)(g.M + 255) / 256 * (g.N / 256) * g.nF > 0x7fffffffLL) return "tile count";
-  if (epi == G_STATS) {
-    if (!g.stats || g.n_valid < 1 || g.n_valid > g.N) return "statistics operands";
-  } else {
-    if (!g.out || g.ldo % 8 || g.ldo < g.N) return "output";
-    if (g.res && (g.ldr % 8 || g.ldr < g.N || epi != G_H16)) return "residual";
-    if (epi == G_PROB && (!g.mi || g.n_valid < 1 || g.n_valid > g.N || g.bias)) return "probability operands";
-  }
+  if (!g.out || g.ldo % 8 || g.ldo < g.N) return "output";
+  if (g.res && (g.ldr % 8 || g.ldr < g.N || epi != G_H16)) return "residual";
+  if (epi == G_STATS && (!g.stats || g.n_valid < 1 || g.n_valid > g.N || g.bias)) return "statistics operands";
   return nullptr;
 }
 
 hipError_t launch_gemm_nt(const GemmArgs& g, int epi, hipStream_t stream) {
   if (g_dry_run) return gemm_nt_check(g, epi) ? hipErrorInvalidValue : hipSuccess;
   if (gemm_nt_check(g, epi)) return hipErrorInvalidValue;
-  const void* kern = epi == G_STATS   ? reinterpret_cast<const void*>(gemm_nt_kernel<G_STATS>)
-                     : epi == G_PROB  ? reinterpret_cast<const void*>(gemm_nt_kernel<G_PROB>)
-                                      : reinterpret_cast<const void*>(gemm_nt_kernel<G_H16>);
-  static bool attr[3] = {false, false, false};
+  const void* kern = epi == G_STATS ? reinterpret_cast<const void*>(gemm_nt_kernel<G_STATS>)
+                                    : reinterpret_cast<const void*>(gemm_nt_kernel<G_H16>);
+  static bool attr[2] = {false, false};
   if (!attr[epi]) {
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, kS1Lds);
     if (e != hipSuccess) return e;
@@ -2142,8 +2137,6 @@ hipError_t launch_gemm_nt(const GemmArgs& g, int epi, hipStream_t stream) {
   const long long grid = tiles < ncu ? tiles : ncu;
   if (epi == G_STATS)
     hipLaunchKernelGGL(gemm_nt_kernel<G_STATS>, dim3((unsigned)grid), dim3(256), kS1Lds, stream, g);
-  else if (epi == G_PROB)
-    hipLaunchKernelGGL(gemm_nt_kernel<G_PROB>, dim3((unsigned)grid), dim3(256), kS1Lds, stream, g);
   else
     hipLaunchKernelGGL(gemm_nt_kernel<G_H16>, dim3((unsigned)grid), dim3(256), kS1Lds, stream, g);
   return hipGetLastError();

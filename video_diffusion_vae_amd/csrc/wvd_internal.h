@@ -132,19 +132,22 @@ hipError_t launch_norm_silu(const h16_t* x, long long x_fstride, int lda, int C,
 // Attention operands of F frames of qkv [F][L][3C] in fragment order (Np keys,
 // a multiple of 256, zero past L): kf [F][Np x C], vf [F][C x Np].
 hipError_t launch_attn_frag(const h16_t* qkv, int F, int L, int C, int Np, h16_t* kf, h16_t* vf, hipStream_t s);
-// mi[r] = (M, 1 / sum e^(s - M)) of each score row r from its nst partial
-// (max, sum of e^(s - max)) pairs st[r][0..nst) (float2 as two floats).
-hipError_t launch_attn_stats(const float* st, long long rows, int nst, float* mi, hipStream_t s);
+// Softmax of the score rows from the score pass's output: row r of
+// P[rows][np] (fp16) holds e^(s - m_g) for its columns in group g of 64 and
+// st[r][g] = (m_g, sum of those e^(s - m_g)) (float2 as two floats, np / 64
+// groups).  With the row's maximum M = max m_g and sum S = sum_g
+// st.y e^(m_g - M), every value becomes e^(s - m_g) e^(m_g - M) / S in place.
+hipError_t launch_attn_rescale(h16_t* P, const float* st, long long rows, int np, hipStream_t s);
 
 // Batched NT GEMM on fragment-order B (the persistent 256 x 256 kernel of
 // the 1x1 shortcut): for frames f < nF, out[f][m][n] = epilogue of
 // sum_k x[f][m][k] w[f][n][k], M rows (>= 256) per frame, K a multiple of
 // 128, N of 256.
 enum GemmEpi {
-  G_H16 = 0,    // fp16 out = acc * scale + bias (+ res, which may alias out)
-  G_STATS = 1,  // no out: per row and group of 64 columns, (max, sum of e^(v - max)) of v = acc * scale
-                // over the columns < n_valid, into stats [f][M][N / 64] (float2)
-  G_PROB = 2    // fp16 out = e^(acc * scale - M) / S with (M, 1/S) = mi[f][m] (float2); 0 for columns >= n_valid
+  G_H16 = 0,   // fp16 out = acc * scale + bias (+ res, which may alias out)
+  G_STATS = 1  // per row and group g of 64 columns, of v = acc * scale over the columns < n_valid:
+               // m_g = max v and the fp16 out = e^(v - m_g) (0 for columns >= n_valid), and
+               // (m_g, sum of e^(v - m_g)) into stats [f][M][N / 64] (float2)
 };
 struct GemmArgs {
   const h16_t* x;
@@ -163,7 +166,6 @@ struct GemmArgs {
   long long a_fs, w_fs, o_fs, r_fs;  // per-frame strides (elements)
   int n_valid;
   float* stats;
-  const float* mi;
 };
 hipError_t launch_gemm_nt(const GemmArgs& g, int epi, hipStream_t stream);
 hipError_t launch_ring_update(h16_t* ring, const h16_t* x, long long x_fstride, int lda, int C,
