@@ -738,14 +738,18 @@ void wino_gemm(Ctx& cx, const Act& x, int nh, int w_item, int Cout) {
   conv(cx, a, 0);
 }
 
+// act_gamma >= 0: out receives SiLU(RMSNorm(v) * gamma) of the conv output v
+// instead of v (and no norm statistics).
 void wino_out(Ctx& cx, const Act& x, int b_item, int Cout, const Act& out, const h16_t* res, long long res_fstride,
-              int ldr) {
+              int ldr, int act_gamma = -1) {
   cx.what = "wino_out";
   cx.run(5, 0, [&] {
     return launch_wino_out(cx.wsp<h16_t>(cx.W->M), Cout, x.F, x.H, x.W, b_item >= 0 ? cx.prep<float>(b_item) : nullptr,
-                           res, res_fstride, ldr, out.p, out.fstride(), out.C, cx.wsp<float>(cx.W->rs), cx.st);
+                           res, res_fstride, ldr, out.p, out.fstride(), out.C,
+                           act_gamma >= 0 ? nullptr : cx.wsp<float>(cx.W->rs),
+                           act_gamma >= 0 ? cx.prep<float>(act_gamma) : nullptr, cx.st);
   });
-  cx.rs_tensor = out.p;
+  cx.rs_tensor = act_gamma >= 0 ? nullptr : out.p;
   cx.rs_frames = x.F;
 }
 
@@ -777,8 +781,21 @@ ConvArgs conv333(Ctx& cx, const Act& x, h16_t* ring, int nh, int gamma_item, int
   return a;
 }
 
-// ResBlock: x -> x (in place) when widths match, else x -> out.
-Act resblock(Ctx& cx, const RB& rb, const Act& x, h16_t* hbuf, h16_t* obuf, int ring1, int ring2, int nh) {
+// True where resblock() can hand out SiLU(RMSNorm(output) * gamma) in
+// place of its output (conv2 in Winograd form with the residual in place).
+bool resblock_can_activate(const RB& rb) { return rb.wino1 && rb.wino2 && wino_mid_ok(rb.cout) && rb.cin == rb.cout; }
+
+// ResBlock: x -> x (in place) when widths match, else x -> out.  With
+// act_gamma >= 0 (only where resblock_can_activate) the block's output is
+// replaced by SiLU(RMSNorm(output) * gamma), for a consumer that needs only
+// that (the head).
+Act resblock(Ctx& cx, const RB& rb, const Act& x, h16_t* hbuf, h16_t* obuf, int ring1, int ring2, int nh,
+             int act_gamma = -1) {
+  if (act_gamma >= 0 && !resblock_can_activate(rb)) {
+    cx.what = "resblock activation";
+    cx.run(0, 0, [] { return hipErrorInvalidValue; });
+    return x;
+  }
   h16_t* r1 = cx.ring(ring1);
   h16_t* r2 = cx.ring(ring2);
   if (!rb.wino1) stats(cx, x, r1, nh);  // the Winograd input transform computes its own
@@ -828,7 +845,7 @@ Act resblock(Ctx& cx, const RB& rb, const Act& x, h16_t* hbuf, h16_t* obuf, int 
   auto conv2_wino = [&](int b_item, const h16_t* res, long long res_fstride, int ldr) {
     if (fused) {
       wino_gemm(cx, h, nh, rb.conv2w, rb.cout);
-      wino_out(cx, h, b_item, rb.cout, out, res, res_fstride, ldr);
+      wino_out(cx, h, b_item, rb.cout, out, res, res_fstride, ldr, act_gamma);
     } else {
       conv_wino(cx, h, r2, nh, rb.norm2, rb.conv2w, b_item, rb.cout, out, res, res_fstride, ldr);
     }
@@ -1292,10 +1309,13 @@ int decode_impl(wvd_plan* plan, const void* z, int z_dtype, int T, int t_begin, 
     attention(cx, x);
     x = resblock(cx, L.mid1, x, Hb, nullptr, R_MID1_1, R_MID1_2, nh0);
     const int nrb = L.nrb;
+    // The last ResBlock hands the head its normalised input directly (in
+    // place of the block output, which nothing else reads) where it can.
+    const bool head_fused = resblock_can_activate(L.up[3][nrb - 1]);
     auto stage = [&](int s, int nh) {  // the stage's ResBlocks; the first may change the width
       for (int k = 0; k < nrb; ++k)
         x = resblock(cx, L.up[s][k], x, Hb, k == 0 && s >= 2 ? Y : nullptr, ring_up(nrb, s, k, 0),
-                     ring_up(nrb, s, k, 1), nh);
+                     ring_up(nrb, s, k, 1), nh, s == 3 && k == nrb - 1 && head_fused ? L.head_norm : -1);
     };
     // Stage 0 (h x w), time_conv, up-conv to 2h x 2w.
     stage(0, nh0);
@@ -1313,16 +1333,19 @@ int decode_impl(wvd_plan* plan, const void* z, int z_dtype, int T, int t_begin, 
     // Head: RMSNorm + SiLU + conv c -> 12, pixel shuffle, clamp, NCTHW video.
     // With only 12 output channels the conv's halo staging would normalise
     // each voxel many times per output; the normalised input is written once
-    // instead (into the free H buffer), and the head's history ring holds
-    // normalised frames.
+    // instead: by the last ResBlock's output transform (head_fused), else by
+    // a norm-SiLU pass into the free H buffer.  The head's history ring
+    // holds normalised frames.
     {
       h16_t* ring = cx.ring(ring_head(L.nrb));
-      Act yn{Hb, x.C, x.F, x.H, x.W};
-      cx.what = "norm_silu";
-      cx.run(3, 0, [&] {
-        return launch_norm_silu(x.p, x.fstride(), x.C, x.C, x.F, x.H * x.W, cx.prep<float>(L.head_norm), yn.p,
-                                yn.fstride(), yn.C, cx.st);
-      });
+      Act yn{head_fused ? x.p : Hb, x.C, x.F, x.H, x.W};
+      if (!head_fused) {
+        cx.what = "norm_silu";
+        cx.run(3, 0, [&] {
+          return launch_norm_silu(x.p, x.fstride(), x.C, x.C, x.F, x.H * x.W, cx.prep<float>(L.head_norm), yn.p,
+                                  yn.fstride(), yn.C, cx.st);
+        });
+      }
       ConvArgs a = args_init();
       // Packed form (widths a multiple of 32): nine (t, y) taps over the
       // input columns, the three x taps as output columns 12 dx + co, tiles

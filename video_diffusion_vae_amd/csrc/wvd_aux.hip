@@ -1030,11 +1030,16 @@ __global__ __launch_bounds__(256) void wino_mid_kernel(const h16_t* __restrict__
 // kernel also writes the norm statistics of the group's output voxels,
 // summed over the rounded fp16 outputs in exactly rms_stats_kernel's order
 // (lane sums in group order, then the same butterfly), so a voxel's
-// statistic does not depend on which kernel computed it.
+// statistic does not depend on which kernel computed it.  ACT: the stored
+// value is instead SiLU(v / ||v|| * gamma) of the rounded fp16 output v, with
+// norm_silu_kernel's arithmetic (same sums, scale and products), for a
+// consumer that reads only the activated tensor (the head).
+template <bool ACT>
 __global__ __launch_bounds__(256) void wino_out_kernel(const h16_t* __restrict__ M, int Cout, int F, int H, int W,
                                                        int WQ, int G, const float* __restrict__ bias,
                                                        const h16_t* res, long long res_fstride, int ldr, h16_t* out,
-                                                       long long out_fstride, int ldo, float* __restrict__ rs) {
+                                                       long long out_fstride, int ldo, float* __restrict__ rs,
+                                                       const float* __restrict__ gamma) {
   constexpr int WM = kWinoM, NX = Wino<WM>::N;
   const int lane = threadIdx.x & 63;
   const int sub = lane % G;
@@ -1044,6 +1049,11 @@ __global__ __launch_bounds__(256) void wino_out_kernel(const h16_t* __restrict__
   const int grp_per_wave = 64 / G;
   const long long gw = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const long long nw = ((long long)gridDim.x * blockDim.x) >> 6;
+  float gm[2][8];
+#pragma unroll
+  for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) gm[q2][k] = ACT && sub + q2 * G < G8 ? gamma[(sub + q2 * G) * 8 + k] : 0.0f;
   for (long long base = gw * grp_per_wave; base < ngrp; base += nw * grp_per_wave) {
     const long long pr = base + lane / G;
     const bool ok = pr < ngrp;
@@ -1056,6 +1066,7 @@ __global__ __launch_bounds__(256) void wino_out_kernel(const h16_t* __restrict__
     float ss[WM];
 #pragma unroll
     for (int e2 = 0; e2 < WM; ++e2) ss[e2] = 0.0f;
+    uint4 hv[2][WM];  // ACT: the rounded outputs, activated once their norms are known
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) {
       const int g = sub + q2 * G;
@@ -1098,7 +1109,10 @@ __global__ __launch_bounds__(256) void wino_out_kernel(const h16_t* __restrict__
 #pragma unroll
         for (int c = 0; c < 8; ++c) v[c] = o[e2][c] + b[c] + r8[c];
         const uint4 packed = pack8h(v);
-        *reinterpret_cast<uint4*>(out + f * out_fstride + (pix0 + e2) * ldo + g * 8) = packed;
+        if constexpr (ACT)
+          hv[q2][e2] = packed;
+        else
+          *reinterpret_cast<uint4*>(out + f * out_fstride + (pix0 + e2) * ldo + g * 8) = packed;
         float h[8];
         unpack8h(packed, h);
         float t = 0.0f;
@@ -1107,12 +1121,25 @@ __global__ __launch_bounds__(256) void wino_out_kernel(const h16_t* __restrict__
         ss[e2] += t;
       }
     }
-    if (rs) {
+    if (ACT || rs) {
 #pragma unroll
       for (int e2 = 0; e2 < WM; ++e2) {
         float v = ss[e2];
         for (int off = 1; off < G; off <<= 1) v += __shfl_xor(v, off, 64);
-        if (ok && sub == 0 && e2 < nout) rs[(long long)(f + 2) * H * W + pix0 + e2] = 1.0f / fmaxf(sqrtf(v), kNormEps);
+        const float sc = 1.0f / fmaxf(sqrtf(v), kNormEps);
+        if (rs && ok && sub == 0 && e2 < nout) rs[(long long)(f + 2) * H * W + pix0 + e2] = sc;
+        if constexpr (ACT) {
+#pragma unroll
+          for (int q2 = 0; q2 < 2; ++q2) {
+            const int g = sub + q2 * G;
+            if (!ok || g >= G8 || e2 >= nout) continue;
+            float a[8];
+            unpack8h(hv[q2][e2], a);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) a[k] = silu_hw(a[k] * sc * gm[q2][k]);
+            *reinterpret_cast<uint4*>(out + f * out_fstride + (pix0 + e2) * ldo + g * 8) = pack8h(a);
+          }
+        }
       }
     }
   }
@@ -1354,16 +1381,20 @@ hipError_t launch_wino_mid(const h16_t* M, const float* bias, int C, int F, int 
 
 hipError_t launch_wino_out(const h16_t* M, int Cout, int F, int H, int W, const float* bias, const h16_t* res,
                            long long res_fstride, int ldr, h16_t* out, long long out_fstride, int ldo, float* rs,
-                           hipStream_t s) {
+                           const float* act_gamma, hipStream_t s) {
+  if (Cout % 8 || ldo % 8 || (res && ldr % 8) || Cout > 1024 || (act_gamma && rs)) return hipErrorInvalidValue;
   if (g_dry_run) return hipSuccess;
-  if (Cout % 8 || ldo % 8 || (res && ldr % 8) || Cout > 1024) return hipErrorInvalidValue;
   int G = 1;
   while (G < 64 && G * 2 <= Cout / 8) G *= 2;
   const int WQ = (W + kWinoM - 1) / kWinoM;
   const long long ngrp = (long long)F * H * WQ;
   const long long waves = (ngrp + (64 / G) - 1) / (64 / G);
-  hipLaunchKernelGGL(wino_out_kernel, dim3(grid_for(waves * 64, 256, 65536)), dim3(256), 0, s, M, Cout, F, H, W, WQ, G,
-                     bias, res, res_fstride, ldr, out, out_fstride, ldo, rs);
+  if (act_gamma)
+    hipLaunchKernelGGL(wino_out_kernel<true>, dim3(grid_for(waves * 64, 256, 65536)), dim3(256), 0, s, M, Cout, F, H,
+                       W, WQ, G, bias, res, res_fstride, ldr, out, out_fstride, ldo, rs, act_gamma);
+  else
+    hipLaunchKernelGGL(wino_out_kernel<false>, dim3(grid_for(waves * 64, 256, 65536)), dim3(256), 0, s, M, Cout, F, H,
+                       W, WQ, G, bias, res, res_fstride, ldr, out, out_fstride, ldo, rs, nullptr);
   return hipGetLastError();
 }
 

@@ -237,10 +237,12 @@ hipError_t launch_wino_mid(const h16_t* M, const float* bias, int C, int F, int 
 // Output transform: out[f][row][mq + j] = (A^T M)[j] + bias (+ res), with
 // M = [kWinoN][F][H][WQ][Cout] fp16; out may alias res.
 // With rs != null also writes rs[2+f][row][col] = 1/||out voxel|| exactly as
-// launch_rms_stats would for these frames.
+// launch_rms_stats would for these frames.  With act_gamma != null (and no
+// rs) it stores SiLU(v / ||v|| * act_gamma) of each rounded output voxel v
+// instead, bit for bit as launch_norm_silu would from the stored v.
 hipError_t launch_wino_out(const h16_t* M, int Cout, int F, int H, int W, const float* bias, const h16_t* res,
                            long long res_fstride, int ldr, h16_t* out, long long out_fstride, int ldo, float* rs,
-                           hipStream_t s);
+                           const float* act_gamma, hipStream_t s);
 hipError_t launch_prep_vec(const void* v, int dtype, int n, float scale, float* out, hipStream_t s);
 // out[i] = a[i] + b[i] in fp32 (the two biases of a block with a shortcut).
 hipError_t launch_prep_vec_add(const void* a, const void* b, int dtype, int n, float* out, hipStream_t s);
