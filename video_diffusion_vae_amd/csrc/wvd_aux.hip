@@ -1033,8 +1033,10 @@ __global__ __launch_bounds__(256) void wino_mid_kernel(const h16_t* __restrict__
 // statistic does not depend on which kernel computed it.  ACT: the stored
 // value is instead SiLU(v / ||v|| * gamma) of the rounded fp16 output v, with
 // norm_silu_kernel's arithmetic (same sums, scale and products), for a
-// consumer that reads only the activated tensor (the head).
-template <bool ACT>
+// consumer that reads only the activated tensor (the head).  NG: channel
+// groups per lane (2 only where Cout / 8 > G, i.e. Cout = 1024), a
+// compile-time bound so the narrower launches hold one group's registers.
+template <bool ACT, int NG>
 __global__ __launch_bounds__(256) void wino_out_kernel(const h16_t* __restrict__ M, int Cout, int F, int H, int W,
                                                        int WQ, int G, const float* __restrict__ bias,
                                                        const h16_t* res, long long res_fstride, int ldr, h16_t* out,
@@ -1049,9 +1051,9 @@ __global__ __launch_bounds__(256) void wino_out_kernel(const h16_t* __restrict__
   const int grp_per_wave = 64 / G;
   const long long gw = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const long long nw = ((long long)gridDim.x * blockDim.x) >> 6;
-  float gm[2][8];
+  float gm[NG][8];
 #pragma unroll
-  for (int q2 = 0; q2 < 2; ++q2)
+  for (int q2 = 0; q2 < NG; ++q2)
 #pragma unroll
     for (int k = 0; k < 8; ++k) gm[q2][k] = ACT && sub + q2 * G < G8 ? gamma[(sub + q2 * G) * 8 + k] : 0.0f;
   for (long long base = gw * grp_per_wave; base < ngrp; base += nw * grp_per_wave) {
@@ -1066,9 +1068,9 @@ __global__ __launch_bounds__(256) void wino_out_kernel(const h16_t* __restrict__
     float ss[WM];
 #pragma unroll
     for (int e2 = 0; e2 < WM; ++e2) ss[e2] = 0.0f;
-    uint4 hv[2][WM];  // ACT: the rounded outputs, activated once their norms are known
+    uint4 hv[NG][WM];  // ACT: the rounded outputs, activated once their norms are known
 #pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2) {
+    for (int q2 = 0; q2 < NG; ++q2) {
       const int g = sub + q2 * G;
       if (!ok || g >= G8) continue;
       const h16_t* src = M + (((long long)f * H + row) * WQ + q) * Cout + g * 8;
@@ -1109,19 +1111,28 @@ __global__ __launch_bounds__(256) void wino_out_kernel(const h16_t* __restrict__
 #pragma unroll
         for (int c = 0; c < 8; ++c) v[c] = o[e2][c] + b[c] + r8[c];
         const uint4 packed = pack8h(v);
-        if constexpr (ACT)
+        h16_t* const dst = out + f * out_fstride + (pix0 + e2) * ldo + g * 8;
+        if constexpr (ACT && NG == 2)
           hv[q2][e2] = packed;
-        else
-          *reinterpret_cast<uint4*>(out + f * out_fstride + (pix0 + e2) * ldo + g * 8) = packed;
+        else if constexpr (!ACT)
+          *reinterpret_cast<uint4*>(dst) = packed;
         float h[8];
         unpack8h(packed, h);
         float t = 0.0f;
 #pragma unroll
         for (int k = 0; k < 8; ++k) t = fmaf(h[k], h[k], t);
         ss[e2] += t;
+        if constexpr (ACT && NG == 1) {
+          // one channel group per lane: the column's sum is complete here
+          // (the group's G lanes share q, so they all reach this point)
+          const float sc = 1.0f / fmaxf(sqrtf(lane_group_sum(ss[e2], G)), kNormEps);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) h[k] = silu_hw(h[k] * sc * gm[0][k]);
+          *reinterpret_cast<uint4*>(dst) = pack8h(h);
+        }
       }
     }
-    if (ACT || rs) {
+    if (ACT ? NG == 2 : rs != nullptr) {
 #pragma unroll
       for (int e2 = 0; e2 < WM; ++e2) {
         float v = ss[e2];
@@ -1130,7 +1141,7 @@ __global__ __launch_bounds__(256) void wino_out_kernel(const h16_t* __restrict__
         if (rs && ok && sub == 0 && e2 < nout) rs[(long long)(f + 2) * H * W + pix0 + e2] = sc;
         if constexpr (ACT) {
 #pragma unroll
-          for (int q2 = 0; q2 < 2; ++q2) {
+          for (int q2 = 0; q2 < NG; ++q2) {
             const int g = sub + q2 * G;
             if (!ok || g >= G8 || e2 >= nout) continue;
             float a[8];
@@ -1389,12 +1400,22 @@ hipError_t launch_wino_out(const h16_t* M, int Cout, int F, int H, int W, const 
   const int WQ = (W + kWinoM - 1) / kWinoM;
   const long long ngrp = (long long)F * H * WQ;
   const long long waves = (ngrp + (64 / G) - 1) / (64 / G);
-  if (act_gamma)
-    hipLaunchKernelGGL(wino_out_kernel<true>, dim3(grid_for(waves * 64, 256, 65536)), dim3(256), 0, s, M, Cout, F, H,
-                       W, WQ, G, bias, res, res_fstride, ldr, out, out_fstride, ldo, rs, act_gamma);
-  else
-    hipLaunchKernelGGL(wino_out_kernel<false>, dim3(grid_for(waves * 64, 256, 65536)), dim3(256), 0, s, M, Cout, F, H,
-                       W, WQ, G, bias, res, res_fstride, ldr, out, out_fstride, ldo, rs, nullptr);
+  const dim3 grid(grid_for(waves * 64, 256, 65536));
+  if (Cout / 8 > G) {  // two channel groups per lane
+    if (act_gamma)
+      hipLaunchKernelGGL((wino_out_kernel<true, 2>), grid, dim3(256), 0, s, M, Cout, F, H, W, WQ, G, bias, res,
+                         res_fstride, ldr, out, out_fstride, ldo, rs, act_gamma);
+    else
+      hipLaunchKernelGGL((wino_out_kernel<false, 2>), grid, dim3(256), 0, s, M, Cout, F, H, W, WQ, G, bias, res,
+                         res_fstride, ldr, out, out_fstride, ldo, rs, nullptr);
+  } else {
+    if (act_gamma)
+      hipLaunchKernelGGL((wino_out_kernel<true, 1>), grid, dim3(256), 0, s, M, Cout, F, H, W, WQ, G, bias, res,
+                         res_fstride, ldr, out, out_fstride, ldo, rs, act_gamma);
+    else
+      hipLaunchKernelGGL((wino_out_kernel<false, 1>), grid, dim3(256), 0, s, M, Cout, F, H, W, WQ, G, bias, res,
+                         res_fstride, ldr, out, out_fstride, ldo, rs, nullptr);
+  }
   return hipGetLastError();
 }
 
