@@ -174,7 +174,7 @@ __global__ __launch_bounds__(256) void norm_silu_kernel(const h16_t* __restrict_
           const float t = f[k] * sc * gm[q][k];
           f[k] = ACT ? silu_hw(t) : t;
         }
-        *reinterpret_cast<uint4*>(o + g8) = pack8h(f);
+        *reinterpret_cast<uint4*>(o + g8) = pack8h_int(f);
       }
     }
   }
@@ -1110,7 +1110,7 @@ __global__ __launch_bounds__(256) void wino_out_kernel(const h16_t* __restrict__
         unpack8h(rr[e2], r8);
 #pragma unroll
         for (int c = 0; c < 8; ++c) v[c] = o[e2][c] + b[c] + r8[c];
-        const uint4 packed = pack8h(v);
+        const uint4 packed = pack8h_int(v);
         h16_t* const dst = out + f * out_fstride + (pix0 + e2) * ldo + g * 8;
         if constexpr (ACT && NG == 2)
           hv[q2][e2] = packed;
@@ -1128,7 +1128,7 @@ __global__ __launch_bounds__(256) void wino_out_kernel(const h16_t* __restrict__
           const float sc = 1.0f / fmaxf(sqrtf(lane_group_sum(ss[e2], G)), kNormEps);
 #pragma unroll
           for (int k = 0; k < 8; ++k) h[k] = silu_hw(h[k] * sc * gm[0][k]);
-          *reinterpret_cast<uint4*>(dst) = pack8h(h);
+          *reinterpret_cast<uint4*>(dst) = pack8h_int(h);
         }
       }
     }
@@ -1148,7 +1148,7 @@ __global__ __launch_bounds__(256) void wino_out_kernel(const h16_t* __restrict__
             unpack8h(hv[q2][e2], a);
 #pragma unroll
             for (int k = 0; k < 8; ++k) a[k] = silu_hw(a[k] * sc * gm[q2][k]);
-            *reinterpret_cast<uint4*>(out + f * out_fstride + (pix0 + e2) * ldo + g * 8) = pack8h(a);
+            *reinterpret_cast<uint4*>(out + f * out_fstride + (pix0 + e2) * ldo + g * 8) = pack8h_int(a);
           }
         }
       }

@@ -67,10 +67,21 @@ __device__ __noinline__ uint32_t f2h_out_of_range(float f) {
   return r;
 }
 
+// |f| <= 65504, false for a NaN (one compare with an abs modifier).
+__device__ __forceinline__ bool in_f16_range(float f) { return __builtin_fabsf(f) <= kF16Max; }
+
+// max(|a|, |b|, |c|) that propagates a NaN (IEEE 754-2019 maximum: one
+// v_maximum3_f32 with abs modifiers), so !(result <= 65504) tests all three
+// values against the fp16 range and for NaN at once.
+__device__ __forceinline__ float max3_abs_nan(float a, float b, float c) {
+  return __builtin_elementwise_maximum(
+      __builtin_elementwise_maximum(__builtin_fabsf(a), __builtin_fabsf(b)), __builtin_fabsf(c));
+}
+
 // fp32 -> fp16, round to nearest even.  A finite value beyond +-65504
 // saturates there and a NaN stays NaN; either one sets the range flags.
 __device__ __forceinline__ uint32_t f2h(float f) {
-  return abs_bits(f) <= kF16MaxBits ? h16_bits(f) : f2h_out_of_range(f);
+  return in_f16_range(f) ? h16_bits(f) : f2h_out_of_range(f);
 }
 
 // Norm scale 1 / max(||v||, 1e-12) of a channel sum of squares ss >= 0, as
@@ -117,7 +128,8 @@ __device__ __noinline__ uint4 pack8h_out_of_range(float f0, float f1, float f2, 
 // branches, and then the rare path recomputes the whole result.
 __device__ __forceinline__ uint32_t pack2h(float lo, float hi) {
   uint32_t r = h16x2_bits(lo, hi);
-  if (max(abs_bits(lo), abs_bits(hi)) > kF16MaxBits) r = pack2h_out_of_range(lo, hi);
+  if (!(__builtin_elementwise_maximum(__builtin_fabsf(lo), __builtin_fabsf(hi)) <= kF16Max))
+    r = pack2h_out_of_range(lo, hi);
   return r;
 }
 
@@ -129,8 +141,23 @@ __device__ __forceinline__ void unpack8h(const uint4& v, float* f) {
   f[6] = h2f(v.w & 0xffffu); f[7] = h2f(v.w >> 16);
 }
 
-// Eight values at once: one range test for all eight on the common path.
+// Eight values at once: one range test for all eight on the common path
+// (four NaN-propagating maxima of the magnitudes and one compare).
 __device__ __forceinline__ uint4 pack8h(const float* f) {
+  const float m = max3_abs_nan(
+      f[6], f[7], __builtin_elementwise_maximum(max3_abs_nan(f[0], f[1], f[2]), max3_abs_nan(f[3], f[4], f[5])));
+  uint4 r = make_uint4(h16x2_bits(f[0], f[1]), h16x2_bits(f[2], f[3]), h16x2_bits(f[4], f[5]),
+                       h16x2_bits(f[6], f[7]));
+  if (!(m <= kF16Max)) r = pack8h_out_of_range(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
+  return r;
+}
+
+// pack8h with the range test on the magnitudes' bit patterns (an AND and an
+// unsigned maximum per value): the same result and flags, more instructions,
+// but fewer registers live where the values are produced and stored one
+// group at a time (wino_out_kernel keeps three waves per SIMD with it and
+// drops to two with pack8h; norm_silu_kernel keeps five).
+__device__ __forceinline__ uint4 pack8h_int(const float* f) {
   uint32_t m = 0;
 #pragma unroll
   for (int k = 0; k < 8; ++k) m = max(m, abs_bits(f[k]));
