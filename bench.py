@@ -29,7 +29,8 @@ if ROOT not in sys.path:
 
 MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 MFMA
 HBM_PEAK_GBS = 8000.0
-CONV_SRC = os.path.join(ROOT, "video_diffusion_vae_amd", "csrc", "wvd_conv.hip")
+# The dominant kernel's sources: its file and the device helpers it inlines.
+CONV_SRCS = [os.path.join(ROOT, "video_diffusion_vae_amd", "csrc", n) for n in ("wvd_conv.hip", "wvd_common.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv3x3x3_main_c256_T49_704x1248_traffic.json")
 # Direct 3x3x3 multiply-adds per Winograd-domain multiply-add: F(6,3) along x
 # replaces 6 outputs x 27 taps by 8 planes x 9 (t, y) taps.  Reported only as
@@ -40,8 +41,11 @@ WINO_DIRECT_PER_EXECUTED = (6 * 27) / (8 * 9)
 
 def conv_src_hash() -> str:
     import hashlib
-    with open(CONV_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for p in CONV_SRCS:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic():
