@@ -30,6 +30,13 @@ enum ItemKind { K_CONV = 0, K_PHASE = 1, K_VEC = 2, K_WINO = 3, K_CONV_PART = 4,
 // transform, kWinoN xi-plane GEMMs on the persistent kernel, output transform)
 // when its widths suit the 256-wide persistent tiles and 32-channel chunks.
 bool wino_ok(int cin, int cout) { return cin % 32 == 0 && cout % 256 == 0; }
+// conv1 in Winograd form (wino_ok(cin, cout)), conv2 too (wino_ok(cout,
+// cout), and a width-changing block's shortcut suits the 1x1 GEMM: K a
+// multiple of 64).
+bool rb_wino2(int cin, int cout) { return wino_ok(cout, cout) && (cin == cout || cin % 64 == 0); }
+// Both convs of a ResBlock in Winograd form, conv1's output transform fused
+// with conv2's input transform (wino_mid).
+bool rb_fused(int cin, int cout) { return wino_ok(cin, cout) && rb_wino2(cin, cout) && wino_mid_ok(cout); }
 
 // One canonical weight tensor and where its prepared form lives.
 struct Item {
@@ -105,9 +112,7 @@ RB add_rb(Layout& L, int cin, int cout) {
     it.bytes = prep_frag_bytes(it.cout, it.cin_pad, it.taps);
   };
   r.wino1 = wino_ok(cin, cout);
-  // a width-changing block's conv2 runs in Winograd form too when its
-  // shortcut suits the 1x1 GEMM (K a multiple of 64)
-  r.wino2 = wino_ok(cout, cout) && (cin == cout || cin % 64 == 0);
+  r.wino2 = rb_wino2(cin, cout);
   if (r.wino1) to_wino(r.conv1w);
   if (r.wino2) to_wino(r.conv2w);
   return r;
@@ -169,6 +174,7 @@ Layout make_layout(int c, int h, int w, bool deep = false) {
 // Workspace carve-up for a given maximum number of latent frames per pass.
 struct Work {
   size_t X, H, Y, zt, zp, rs, qkv, S, Pm, Vt, O;
+  size_t H_bytes;            // capacity of H (checked before every write into it)
   size_t kf, vf, st;         // attention on the batched GEMM: K, V^T fragments, score statistics
   size_t U, M;               // Winograd input planes and products
   std::vector<size_t> ring;  // 24 rings: offsets inside the ring block
@@ -254,7 +260,24 @@ Work make_work(int c, int h, int w, int P, bool rings_in_workspace = true, int n
     return o;
   };
   W.X = take(act * 2);
-  W.H = take(act * 2);
+  // H holds a ResBlock's conv1 output h.  Where both convs run fused in
+  // Winograd form (the output transform of conv1 feeds conv2's input
+  // transform directly), h is stored only for the history ring, and into H
+  // only by a one-frame pass; other blocks store all the pass's frames.  The
+  // head's normalised input goes to H where the last ResBlock cannot write
+  // it.  Levels 0..3 hold widths 4c, 4c, 4c -> 2c -> 2c, 2c -> c -> c.
+  {
+    const long long fl[4] = {F0, F1, F2, F2};
+    const long long blk[6][3] = {{0, c4, c4}, {1, c4, c4}, {2, c4, c2}, {2, c2, c2}, {3, c2, c}, {3, c, c}};
+    long long hsz = 0;
+    for (const auto& b : blk) {
+      const bool fused = rb_fused((int)b[1], (int)b[2]);
+      hsz = std::max(hsz, (fused ? 1 : fl[b[0]]) * res[b[0]] * b[2]);
+    }
+    if (!rb_fused(c, c)) hsz = std::max(hsz, F2 * res[3] * c);
+    W.H_bytes = (size_t)hsz * 2;
+    W.H = take(W.H_bytes);
+  }
   W.Y = take(act * 2);
   W.zt = take((size_t)F0 * r0 * 64 * 2);
   W.zp = take((size_t)F0 * r0 * 64 * 2);  // latents after the deep variant's 1x1x1 conv
@@ -407,7 +430,8 @@ Work make_work_enc(int c, int h, int w, int P) {
     return o;
   };
   W.X = take(act * 2);
-  W.H = take(act * 2);
+  W.H_bytes = (size_t)act * 2;
+  W.H = take(W.H_bytes);
   W.Y = take(act * 2);
   W.zt = W.zp = take(0);
   W.rs = take((size_t)(F2 + 2) * res[3] * 4);
@@ -519,6 +543,13 @@ struct Ctx {
       plan->pool.push_back(e);
     }
     return plan->pool[plan->pool_used++];
+  }
+  // A host-side check failed: no launch; the decode returns WVD_EHIP with
+  // the reason in wvd_last_error.
+  void fail(const char* why) {
+    if (err != hipSuccess) return;
+    err = hipErrorInvalidValue;
+    set_error(why, err);
   }
   template <typename F>
   void run(int cls, double flops, F&& fn) {
@@ -792,8 +823,7 @@ bool resblock_can_activate(const RB& rb) { return rb.wino1 && rb.wino2 && wino_m
 Act resblock(Ctx& cx, const RB& rb, const Act& x, h16_t* hbuf, h16_t* obuf, int ring1, int ring2, int nh,
              int act_gamma = -1) {
   if (act_gamma >= 0 && !resblock_can_activate(rb)) {
-    cx.what = "resblock activation";
-    cx.run(0, 0, [] { return hipErrorInvalidValue; });
+    cx.fail("resblock activation");
     return x;
   }
   h16_t* r1 = cx.ring(ring1);
@@ -801,6 +831,14 @@ Act resblock(Ctx& cx, const RB& rb, const Act& x, h16_t* hbuf, h16_t* obuf, int 
   if (!rb.wino1) stats(cx, x, r1, nh);  // the Winograd input transform computes its own
   Act h{hbuf, rb.cout, x.F, x.H, x.W};
   const bool fused = rb.wino1 && rb.wino2 && wino_mid_ok(rb.cout);
+  {
+    // frames of h stored into hbuf (fused blocks: only a one-frame pass's)
+    const long long hf = fused ? (x.F >= 2 ? 0 : x.F) : x.F;
+    if ((size_t)hf * x.H * x.W * rb.cout * 2 > cx.W->H_bytes) {
+      cx.fail("resblock: conv1 output beyond the H buffer");
+      return x;
+    }
+  }
   if (fused) {
     // conv1's products go straight into conv2's input planes: h is stored
     // only for the frames the next pass reads as history (its ring)
@@ -1339,6 +1377,7 @@ int decode_impl(wvd_plan* plan, const void* z, int z_dtype, int T, int t_begin, 
     {
       h16_t* ring = cx.ring(ring_head(L.nrb));
       Act yn{head_fused ? x.p : Hb, x.C, x.F, x.H, x.W};
+      if (!head_fused && (size_t)x.F * x.H * x.W * x.C * 2 > W.H_bytes) cx.fail("head: input beyond the H buffer");
       if (!head_fused) {
         cx.what = "norm_silu";
         cx.run(3, 0, [&] {
