@@ -174,7 +174,7 @@ Layout make_layout(int c, int h, int w, bool deep = false) {
 // Workspace carve-up for a given maximum number of latent frames per pass.
 struct Work {
   size_t X, H, Y, zt, zp, rs, qkv, S, Pm, Vt, O;
-  size_t H_bytes;            // capacity of H (checked before every write into it)
+  size_t X_bytes, H_bytes, Y_bytes;  // capacities of X, H, Y (checked before every write into them)
   size_t kf, vf, st;         // attention on the batched GEMM: K, V^T fragments, score statistics
   size_t U, M;               // Winograd input planes and products
   std::vector<size_t> ring;  // 24 rings: offsets inside the ring block
@@ -251,7 +251,6 @@ Work make_work(int c, int h, int w, int P, bool rings_in_workspace = true, int n
   const long long res[4] = {r0, 4 * r0, 16 * r0, 64 * r0};
   const long long c4 = 4 * c, c2 = 2 * c;
   const long long F0 = P, F1 = 2LL * P, F2 = 4LL * P;
-  long long act = std::max({F0 * r0 * c4, F1 * res[1] * c4, F2 * res[2] * c4, F2 * res[3] * c2});
   const long long L = r0, Lp = lpad_of((int)r0);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -259,7 +258,9 @@ Work make_work(int c, int h, int w, int P, bool rings_in_workspace = true, int n
     off = align_up(off + bytes);
     return o;
   };
-  W.X = take(act * 2);
+  // X: conv_in's output and the up-convs' (the widest: level 3 at 2c).
+  W.X_bytes = (size_t)std::max({F0 * r0 * c4, F1 * res[1] * c4, F2 * res[2] * c4, F2 * res[3] * c2}) * 2;
+  W.X = take(W.X_bytes);
   // H holds a ResBlock's conv1 output h.  Where both convs run fused in
   // Winograd form (the output transform of conv1 feeds conv2's input
   // transform directly), h is stored only for the history ring, and into H
@@ -278,7 +279,10 @@ Work make_work(int c, int h, int w, int P, bool rings_in_workspace = true, int n
     W.H_bytes = (size_t)hsz * 2;
     W.H = take(W.H_bytes);
   }
-  W.Y = take(act * 2);
+  // Y: the time_convs' outputs and the width-changing ResBlocks' (4c -> 2c
+  // at level 2, 2c -> c at level 3).
+  W.Y_bytes = (size_t)std::max({F1 * r0 * c4, F2 * res[1] * c4, F2 * res[2] * c2, F2 * res[3] * c}) * 2;
+  W.Y = take(W.Y_bytes);
   W.zt = take((size_t)F0 * r0 * 64 * 2);
   W.zp = take((size_t)F0 * r0 * 64 * 2);  // latents after the deep variant's 1x1x1 conv
   W.rs = take((size_t)(F2 + 2) * res[3] * 4);
@@ -429,10 +433,10 @@ Work make_work_enc(int c, int h, int w, int P) {
     off = align_up(off + bytes);
     return o;
   };
-  W.X = take(act * 2);
-  W.H_bytes = (size_t)act * 2;
+  W.X_bytes = W.H_bytes = W.Y_bytes = (size_t)act * 2;
+  W.X = take(W.X_bytes);
   W.H = take(W.H_bytes);
-  W.Y = take(act * 2);
+  W.Y = take(W.Y_bytes);
   W.zt = W.zp = take(0);
   W.rs = take((size_t)(F2 + 2) * res[3] * 4);
   W.qkv = take((size_t)F0 * L * 3 * c4 * 2);
@@ -550,6 +554,15 @@ struct Ctx {
     if (err != hipSuccess) return;
     err = hipErrorInvalidValue;
     set_error(why, err);
+  }
+  // A write of `bytes` starting at p: where p is the start of the X, H or Y
+  // buffer, the write must fit in that buffer's capacity.
+  void check_fits(const void* p, size_t bytes, const char* what) {
+    const size_t cap = p == wsp<unsigned char>(W->X)   ? W->X_bytes
+                       : p == wsp<unsigned char>(W->H) ? W->H_bytes
+                       : p == wsp<unsigned char>(W->Y) ? W->Y_bytes
+                                                       : ~(size_t)0;
+    if (bytes > cap) fail(what);
   }
   template <typename F>
   void run(int cls, double flops, F&& fn) {
@@ -834,10 +847,10 @@ Act resblock(Ctx& cx, const RB& rb, const Act& x, h16_t* hbuf, h16_t* obuf, int 
   {
     // frames of h stored into hbuf (fused blocks: only a one-frame pass's)
     const long long hf = fused ? (x.F >= 2 ? 0 : x.F) : x.F;
-    if ((size_t)hf * x.H * x.W * rb.cout * 2 > cx.W->H_bytes) {
-      cx.fail("resblock: conv1 output beyond the H buffer");
-      return x;
-    }
+    cx.check_fits(hbuf, (size_t)hf * x.H * x.W * rb.cout * 2, "resblock: conv1 output beyond its buffer");
+    if (rb.cin != rb.cout)
+      cx.check_fits(obuf, (size_t)x.F * x.H * x.W * rb.cout * 2, "resblock: output beyond its buffer");
+    if (cx.err != hipSuccess) return x;
   }
   if (fused) {
     // conv1's products go straight into conv2's input planes: h is stored
@@ -1126,6 +1139,7 @@ Act time_upsample(Ctx& cx, int s, const Act& x, int g, h16_t* ybuf, int ring_id)
   h16_t* ring = cx.ring(ring_id);
   const bool first = g == 0;
   Act y{ybuf, x.C, first ? 2 * x.F - 1 : 2 * x.F, x.H, x.W};
+  cx.check_fits(ybuf, (size_t)y.F * y.fstride() * 2, "time_conv: output beyond its buffer");
   if (first) {
     cx.run(4, 0, [&] { return launch_copy16(y.p, x.p, (size_t)x.fstride() * 2, cx.st); });
   }
@@ -1155,6 +1169,7 @@ Act time_upsample(Ctx& cx, int s, const Act& x, int g, h16_t* ybuf, int ring_id)
 Act up_conv(Ctx& cx, int s, const Act& x, h16_t* ybuf) {
   const Layout& L = cx.plan->L;
   Act y{ybuf, x.C, x.F, 2 * x.H, 2 * x.W};
+  cx.check_fits(ybuf, (size_t)y.F * y.fstride() * 2, "up-conv: output beyond its buffer");
   ConvArgs a = args_init();
   a.seg[0] = seg_basic(x.p, x.fstride(), x.C, x.C, cx.prep<h16_t>(L.upc_w[s]), x.C, (long long)x.C * x.C, 1, 2,
                        cx.wbytes(L.upc_w[s]));
@@ -1377,7 +1392,7 @@ int decode_impl(wvd_plan* plan, const void* z, int z_dtype, int T, int t_begin, 
     {
       h16_t* ring = cx.ring(ring_head(L.nrb));
       Act yn{head_fused ? x.p : Hb, x.C, x.F, x.H, x.W};
-      if (!head_fused && (size_t)x.F * x.H * x.W * x.C * 2 > W.H_bytes) cx.fail("head: input beyond the H buffer");
+      if (!head_fused) cx.check_fits(Hb, (size_t)x.F * x.H * x.W * x.C * 2, "head: input beyond its buffer");
       if (!head_fused) {
         cx.what = "norm_silu";
         cx.run(3, 0, [&] {
