@@ -70,6 +70,12 @@ def test_workspace_fits_288GB_at_the_largest_sweep_point(dry):
     try:
         sizes = {P: wvd.wvd_workspace_bytes(plan, 121, P) for P in (2, 4, 8, 16)}
         assert sizes[2] < sizes[4] < sizes[8] < sizes[16] < 200e9
+        # X, H and Y are sized by what each holds (H: the fused Winograd
+        # blocks keep conv1's output only in the history ring; Y: at most the
+        # level-3 activation at width c), not three copies of the widest
+        # activation: 51.6 GiB at P=16 and 14.9 GiB at P=4, against 70.8 and
+        # 19.8 GiB with three widest buffers
+        assert sizes[16] < 56 * 2**30 and sizes[4] < 16 * 2**30
     finally:
         wvd.wvd_destroy(plan)
 
