@@ -251,7 +251,7 @@ Work make_work(int c, int h, int w, int P, bool rings_in_workspace = true, int n
   const long long res[4] = {r0, 4 * r0, 16 * r0, 64 * r0};
   const long long c4 = 4 * c, c2 = 2 * c;
   const long long F0 = P, F1 = 2LL * P, F2 = 4LL * P;
-  const long long L = r0, Lp = lpad_of((int)r0);
+  const long long L = r0;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -426,7 +426,7 @@ Work make_work_enc(int c, int h, int w, int P) {
   const long long F0 = P, F1 = 2LL * P, F2 = 4LL * P;
   const long long act = std::max({F2 * res[3] * std::max<long long>(c, kEncInC), F2 * res[2] * c2, F2 * res[1] * c2,
                                   F1 * res[1] * c4, F1 * res[0] * c4, F0 * res[0] * c4});
-  const long long L = r0, Lp = lpad_of((int)r0);
+  const long long L = r0;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -571,13 +571,13 @@ struct Ctx {
     if (plan->profile) {
       e0 = ev();
       e1 = ev();
-      if (e0) hipEventRecord(e0, st);
+      // a pair whose first record fails is not timed
+      if (e0 && hipEventRecord(e0, st) != hipSuccess) e0 = nullptr;
     }
     err = fn();
     if (err != hipSuccess) set_error(what, err);
     ++plan->launches;
-    if (plan->profile && e0 && e1) {
-      hipEventRecord(e1, st);
+    if (plan->profile && e0 && e1 && hipEventRecord(e1, st) == hipSuccess) {
       plan->recs.push_back({cls, flops, e0, e1});
     }
   }
@@ -1756,7 +1756,7 @@ long long wvd_last_launch_count(const wvd_plan* plan) { return plan_ok(plan) ? p
 
 void wvd_destroy(wvd_plan* plan) {
   if (!plan_ok(plan)) return;
-  for (hipEvent_t e : plan->pool) hipEventDestroy(e);
+  for (hipEvent_t e : plan->pool) (void)hipEventDestroy(e);
   plan->magic = 0;
   delete plan;
 }

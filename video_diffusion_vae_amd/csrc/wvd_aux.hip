@@ -560,62 +560,14 @@ __global__ __launch_bounds__(256) void space_to_depth_kernel(const h16_t* __rest
   }
 }
 
-// Winograd F(m,3) along x (Lavin and Gray's minimal filtering; m = 2 with
-// interpolation points 0, 1, -1, infinity, m = 4 with 0, 1, -1, 2, -2,
-// infinity).  m outputs x[mq .. mq+m-1] of a 3-tap correlation (pad 1) come
-// from the n = m + 2 inputs d_k = x[mq-1+k]:
+// Winograd F(m,3) along x (Lavin and Gray's minimal filtering): m outputs
+// x[mq .. mq+m-1] of a 3-tap correlation (pad 1) come from the n = m + 2
+// inputs d_k = x[mq-1+k]:
 //   U = B^T d (input transform),  V = G g (weight transform),
 //   M = sum over channels and (t, y) taps of U * V,  y = A^T M.
+// The kernels run m = kWinoM = 6.
 template <int WM>
 struct Wino;
-
-template <>
-struct Wino<2> {
-  static constexpr int N = 4;
-  __device__ static void weights(float g0, float g1, float g2, float* v) {
-    v[0] = g0;
-    v[1] = 0.5f * (g0 + g1 + g2);
-    v[2] = 0.5f * (g0 - g1 + g2);
-    v[3] = g2;
-  }
-  __device__ static void input(const float* d, float* u) {
-    u[0] = d[0] - d[2];
-    u[1] = d[1] + d[2];
-    u[2] = d[2] - d[1];
-    u[3] = d[1] - d[3];
-  }
-  __device__ static void output(const float* m, float* o) {
-    o[0] = m[0] + m[1] + m[2];
-    o[1] = m[1] - m[2] - m[3];
-  }
-};
-
-template <>
-struct Wino<4> {
-  static constexpr int N = 6;
-  __device__ static void weights(float g0, float g1, float g2, float* v) {
-    v[0] = 0.25f * g0;
-    v[1] = -(g0 + g1 + g2) / 6.0f;
-    v[2] = -(g0 - g1 + g2) / 6.0f;
-    v[3] = g0 / 24.0f + g1 / 12.0f + g2 / 6.0f;
-    v[4] = g0 / 24.0f - g1 / 12.0f + g2 / 6.0f;
-    v[5] = g2;
-  }
-  __device__ static void input(const float* d, float* u) {
-    u[0] = 4.0f * d[0] - 5.0f * d[2] + d[4];
-    u[1] = -4.0f * d[1] - 4.0f * d[2] + d[3] + d[4];
-    u[2] = 4.0f * d[1] - 4.0f * d[2] - d[3] + d[4];
-    u[3] = -2.0f * d[1] - d[2] + 2.0f * d[3] + d[4];
-    u[4] = 2.0f * d[1] - d[2] - 2.0f * d[3] + d[4];
-    u[5] = 4.0f * d[1] - 5.0f * d[3] + d[5];
-  }
-  __device__ static void output(const float* m, float* o) {
-    o[0] = m[0] + m[1] + m[2] + m[3] + m[4];
-    o[1] = m[1] - m[2] + 2.0f * m[3] - 2.0f * m[4];
-    o[2] = m[1] + m[2] + 4.0f * m[3] + 4.0f * m[4];
-    o[3] = m[1] - m[2] + 8.0f * m[3] - 8.0f * m[4] + m[5];
-  }
-};
 
 // F(6,3): interpolation points 0, 1, -1, 1/2, -1/2, 2, -2 and infinity
 // (Toom-Cook).  Eight inputs d_k = x[6q-1+k] give six outputs x[6q..6q+5].

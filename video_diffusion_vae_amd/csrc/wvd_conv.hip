@@ -54,7 +54,6 @@ constexpr int kWinoLag = 3;     // Winograd GEMM: taps between a halo item's loa
 // Tile of the Winograd-domain GEMM: 2 frames x 8 rows x 16 column groups
 // (halo 4 x 10 x 16 rows; a 4 x 4 x 16 tile has fewer halo rows but measured slower).
 constexpr int kTFWino = kWinoTF;
-constexpr int kTHWino = kTileM / kTileW / kTFWino;
 }  // namespace
 // Tile shapes (frames x column groups) the Winograd-domain GEMM is built for;
 // rows = 256 / (TF * TW).  Deeper tiles in t and y cut the halo per output.
